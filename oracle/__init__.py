@@ -1,0 +1,146 @@
+"""Reference GEMM oracle -- TEST INFRASTRUCTURE ONLY.
+
+A plain fp64 CPU evaluation of ``C = alpha * (A x B) + beta * C0`` (the
+definition that opens "GEMM Worklog I: Naive to Tiled" and that "A GEMM
+Kernel, Step by Step" states as its one-call problem).  The arithmetic lives
+in ``gemm_ref.c`` (plain C, OpenMP over rows); this module only builds it with
+gcc and marshals numpy arrays.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+and never imports it.
+
+Arrays are 2-D numpy arrays whose last axis is contiguous; their row stride
+(in elements) is passed as the leading dimension, so views into padded
+buffers work unchanged.  fp32 operands are ``numpy.float32``; bf16 operands
+are ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gemm_ref.c")
+_LIB = os.path.join(_HERE, "libgemm_ref.so")
+
+# -O2 without fast-math; contraction off so every operation is a plain IEEE op.
+BUILD_CMD = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+             "-ffp-contract=off", "-fno-fast-math", "-o", _LIB, _SRC]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library; returns its path."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = BUILD_CMD[:-3] + ["-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    # The mutation tests point this at a deliberately broken build of the
+    # same source to show that the pins catch it.
+    path = os.environ.get("GEMM_ORACLE_LIB") or _LIB
+    if path == _LIB and not os.path.exists(_LIB):
+        build(force=True)
+    lib = ctypes.CDLL(path)
+    i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+    sig = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64]
+    for name in ("gemm_ref_f32in", "gemm_ref_bf16in",
+                 "gemm_absbound_f32in", "gemm_absbound_bf16in"):
+        fn = getattr(lib, name)
+        fn.argtypes = sig
+        fn.restype = None
+    lib.gemm_ref_num_threads.argtypes = []
+    lib.gemm_ref_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ld(x: np.ndarray, what: str) -> int:
+    if x.ndim != 2:
+        raise ValueError(f"{what} must be 2-D")
+    if x.size == 0:
+        return max(x.shape[1], 1)
+    if x.shape[1] > 1 and x.strides[1] != x.itemsize:
+        raise ValueError(f"{what}: last axis must be contiguous")
+    if x.strides[0] % x.itemsize:
+        raise ValueError(f"{what}: row stride not a multiple of the element size")
+    return max(x.strides[0] // x.itemsize, 1)
+
+
+def _ptr(x: np.ndarray) -> int:
+    return x.__array_interface__["data"][0]
+
+
+def _run(kind: str, A, B, alpha, beta, C0):
+    if A.dtype == np.float32 and B.dtype == np.float32:
+        suffix = "f32in"
+    elif A.dtype == np.uint16 and B.dtype == np.uint16:
+        suffix = "bf16in"
+    else:
+        raise TypeError("operands must both be float32 or both uint16 (bf16 bits)")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {A.shape} x {B.shape}")
+    lda, ldb = _ld(A, "A"), _ld(B, "B")
+    if C0 is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C0")
+        c0p, ldc0 = None, max(N, 1)
+    else:
+        if C0.dtype != np.float32 or C0.shape != (M, N):
+            raise ValueError("C0 must be float32 of shape (M, N)")
+        c0p, ldc0 = _ptr(C0), _ld(C0, "C0")
+    out = np.empty((M, N), dtype=np.float64)
+    fn = getattr(_load(), f"gemm_{kind}_{suffix}")
+    fn(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta),
+       c0p, ldc0, _ptr(out), max(N, 1))
+    return out
+
+
+def gemm_ref(A, B, alpha=1.0, beta=0.0, C0=None) -> np.ndarray:
+    """fp64 ``alpha * A @ B + beta * C0`` over the exact input values.
+
+    The beta term is left out (C0 not read) when ``beta == 0``.
+    """
+    return _run("ref", A, B, alpha, beta, C0)
+
+
+def gemm_absbound(A, B, alpha=1.0, beta=0.0, C0=None) -> np.ndarray:
+    """fp64 ``|alpha| * |A| @ |B| + |beta| * |C0|`` -- the error-ratio denominator."""
+    return _run("absbound", A, B, alpha, beta, C0)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().gemm_ref_num_threads())
+
+
+def error_ratio(C_gpu: np.ndarray, C_ref: np.ndarray, D: np.ndarray) -> float:
+    """``max |C_gpu - C_ref| / D``; where ``D == 0`` the two must be equal.
+
+    Returns ``inf`` when any entry is NaN/Inf on one side only or differs
+    where the denominator is zero.
+    """
+    C_gpu = np.asarray(C_gpu, dtype=np.float64)
+    err = np.abs(C_gpu - C_ref)
+    if not np.all(np.isfinite(err)):
+        return float("inf")
+    zero = D == 0
+    if np.any(err[zero] != 0):
+        return float("inf")
+    if not np.any(~zero):
+        return 0.0
+    return float(np.max(err[~zero] / D[~zero]))

@@ -1,0 +1,193 @@
+/*
+ * Reference GEMM oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, deliberately obvious CPU implementation of the operation the
+ * pages define:
+ *
+ *     C = alpha * (A x B) + beta * C0,   A is M x K, B is K x N, C is M x N
+ *
+ * ("GEMM Worklog I: Naive to Tiled", opening formula; "A GEMM Kernel, Step by
+ * Step", section "The ladder we are climbing", which states the problem as
+ * one call C <- alpha*A*B + beta*C).  Entry (i, j) is the dot product of row
+ * i of A with column j of B, exactly as the naive kernel of the first page
+ * computes it (section 1, "The Naive CUDA Kernel"), scaled by alpha, plus
+ * beta times the old entry.
+ *
+ * Precision: every input element is widened exactly to double (fp32 -> fp64
+ * is exact; a bf16 bit pattern shifted left by 16 is an exact fp32 value,
+ * hence exact in fp64).  Each product of two such values is exact in fp64
+ * (24 + 24 significand bits <= 53), so the only rounding is the fp64
+ * accumulation over k, which runs in ascending k for every entry.
+ *
+ * Loop order: the i-k-j nest below adds the terms of each entry C[i][j] in
+ * the same order (k = 0, 1, ..., K-1) as the textbook i-j-k dot product;
+ * only the traversal of independent entries differs, so the result is
+ * bitwise the same as the triple loop.  Rows are independent and are spread
+ * over OpenMP threads; nothing is blocked, fused or reordered within an
+ * entry.
+ *
+ * Conventions where the pages are silent (each is listed in the design
+ * notes): row-major storage with explicit leading dimensions
+ * (A[i*lda+k], B[k*ldb+j], C[i*ldc+j]); when beta == 0 the beta*C0 term is
+ * omitted entirely, so C0 is never read and NaN/Inf in it cannot propagate;
+ * K == 0 gives an empty sum (0).
+ *
+ * This library shares no code, header or constant with the HIP path.  Only
+ * the tests, the smoke check and the benchmark's CPU-baseline leg may load
+ * it.
+ */
+#include <stdint.h>
+#include <string.h>
+
+static double widen_bf16(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* out[i*ldo + j] = alpha * sum_k A[i][k] * B[k][j]  (+ beta * C0[i][j] when beta != 0) */
+void gemm_ref_f32in(int64_t M, int64_t N, int64_t K, double alpha,
+                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                    double beta, const float *C0, int64_t ldc0,
+                    double *out, int64_t ldo)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        for (int64_t j = 0; j < N; ++j)
+            row[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)A[i * lda + k];
+            const float *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j)
+                row[j] += a * (double)brow[j];
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * row[j];
+            if (beta != 0.0)
+                v += beta * (double)C0[i * ldc0 + j];
+            row[j] = v;
+        }
+    }
+}
+
+/* Same definition with bf16 operands (raw bit patterns), fp32 C0. */
+void gemm_ref_bf16in(int64_t M, int64_t N, int64_t K, double alpha,
+                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                     double beta, const float *C0, int64_t ldc0,
+                     double *out, int64_t ldo)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        for (int64_t j = 0; j < N; ++j)
+            row[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = widen_bf16(A[i * lda + k]);
+            const uint16_t *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j)
+                row[j] += a * widen_bf16(brow[j]);
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * row[j];
+            if (beta != 0.0)
+                v += beta * (double)C0[i * ldc0 + j];
+            row[j] = v;
+        }
+    }
+}
+
+/*
+ * Error-bound denominator for the acceptance test:
+ *     D[i][j] = |alpha| * sum_k |A[i][k]| * |B[k][j]|  (+ |beta| * |C0[i][j]| when beta != 0)
+ * A floating-point evaluation of the GEMM in any summation order has error
+ * bounded by a small multiple of the unit roundoff times this sum (standard
+ * forward error bound of an inner product), so |C_gpu - C_ref| / D is the
+ * scale-free error measure.
+ */
+void gemm_absbound_f32in(int64_t M, int64_t N, int64_t K, double alpha,
+                         const float *A, int64_t lda, const float *B, int64_t ldb,
+                         double beta, const float *C0, int64_t ldc0,
+                         double *out, int64_t ldo)
+{
+    const double aa = alpha < 0 ? -alpha : alpha;
+    const double ab = beta < 0 ? -beta : beta;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        for (int64_t j = 0; j < N; ++j)
+            row[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = (double)A[i * lda + k];
+            if (a < 0) a = -a;
+            const float *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) {
+                double b = (double)brow[j];
+                row[j] += a * (b < 0 ? -b : b);
+            }
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double v = aa * row[j];
+            if (beta != 0.0) {
+                double c = (double)C0[i * ldc0 + j];
+                v += ab * (c < 0 ? -c : c);
+            }
+            row[j] = v;
+        }
+    }
+}
+
+void gemm_absbound_bf16in(int64_t M, int64_t N, int64_t K, double alpha,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          double beta, const float *C0, int64_t ldc0,
+                          double *out, int64_t ldo)
+{
+    const double aa = alpha < 0 ? -alpha : alpha;
+    const double ab = beta < 0 ? -beta : beta;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        for (int64_t j = 0; j < N; ++j)
+            row[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = widen_bf16(A[i * lda + k]);
+            if (a < 0) a = -a;
+            const uint16_t *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) {
+                double b = widen_bf16(brow[j]);
+                row[j] += a * (b < 0 ? -b : b);
+            }
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double v = aa * row[j];
+            if (beta != 0.0) {
+                double c = (double)C0[i * ldc0 + j];
+                v += ab * (c < 0 ? -c : c);
+            }
+            row[j] = v;
+        }
+    }
+}
+
+/* Threads OpenMP will use for the loops above (reported next to timings). */
+int gemm_ref_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,398 @@
+"""Pins for the fp64 CPU oracle.
+
+The oracle computes C = alpha*(A x B) + beta*C0 (the defining formula of "GEMM
+Worklog I: Naive to Tiled" and the one-call problem of "A GEMM Kernel, Step by
+Step").  Nothing here re-types that formula: each test checks the oracle
+against something fixed independently of it -- a closed form for a special
+operand (identity, permutation, all-ones, rank one), exact rational brute
+force, a library routine (torch's fp64 matmul), algebraic invariants, or the
+bf16 format definition.  A planted mistake in the oracle (dropped term, wrong
+sign, wrong index, transposed operand, ignored leading dimension) fails at
+least one of them; tests/test_oracle_mutants.py proves that by building such
+mutants.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+U = 2.0 ** -53  # fp64 unit roundoff
+
+
+def rand32(rng, shape, lo=-1.0, hi=1.0):
+    return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def padded(x: np.ndarray, extra: int, fill=np.nan) -> np.ndarray:
+    """View of x inside a wider buffer whose padding columns hold ``fill``."""
+    rows, cols = x.shape
+    buf = np.full((rows, cols + extra), fill, dtype=x.dtype)
+    buf[:, :cols] = x
+    return buf[:, :cols]
+
+
+def exact_gemm(A, B, alpha, beta, C0):
+    """Exact rational value of every entry (tiny shapes only)."""
+    M, K = A.shape
+    N = B.shape[1]
+    fa, fb = Fraction(float(alpha)), Fraction(float(beta))
+    out = np.empty((M, N), dtype=object)
+    bnd = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            sa = Fraction(0)
+            for k in range(K):
+                p = Fraction(float(A[i, k])) * Fraction(float(B[k, j]))
+                s += p
+                sa += abs(p)
+            v = fa * s
+            d = abs(fa) * sa
+            if beta != 0.0:
+                c = Fraction(float(C0[i, j]))
+                v += fb * c
+                d += abs(fb) * abs(c)
+            out[i, j] = v
+            bnd[i, j] = d
+    return out, bnd
+
+
+SHAPES_TINY = [(1, 1, 1), (1, 5, 3), (7, 1, 4), (3, 4, 1), (8, 8, 8), (5, 3, 7), (2, 6, 5), (4, 4, 0)]
+SCALARS = [(1.0, 0.0), (2.0, -1.0), (-0.75, 0.5), (0.0, 1.5), (1.0, 1.0)]
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("M", [1, 5, 33])
+@pytest.mark.parametrize("alpha,beta", SCALARS)
+def test_identity_left(M, alpha, beta):
+    """A = I gives C = alpha*B + beta*C0: one exact product per entry, then the scalars."""
+    rng = np.random.default_rng(10 + M)
+    N = 19
+    A = np.eye(M, dtype=np.float32)
+    B = rand32(rng, (M, N))
+    C0 = rand32(rng, (M, N))
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    want = alpha * B.astype(np.float64)
+    if beta != 0.0:
+        want = want + beta * C0.astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("alpha,beta", SCALARS)
+def test_identity_right(alpha, beta):
+    """B = I gives C = alpha*A + beta*C0."""
+    rng = np.random.default_rng(3)
+    M, K = 23, 17
+    A = rand32(rng, (M, K))
+    B = np.eye(K, dtype=np.float32)
+    C0 = rand32(rng, (M, K))
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    want = alpha * A.astype(np.float64)
+    if beta != 0.0:
+        want = want + beta * C0.astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_permutation_left_selects_rows_of_B():
+    """A = row-selection matrix: row i of C is row perm[i] of B (scaled)."""
+    rng = np.random.default_rng(4)
+    M, K, N = 13, 29, 11
+    perm = rng.integers(0, K, size=M)
+    A = np.zeros((M, K), dtype=np.float32)
+    A[np.arange(M), perm] = 1.0
+    B = rand32(rng, (K, N))
+    C0 = rand32(rng, (M, N))
+    got = oracle.gemm_ref(A, B, 2.0, -1.0, C0)
+    want = 2.0 * B[perm].astype(np.float64) - C0.astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_permutation_right_selects_columns_of_A():
+    """B = column-selection matrix: column j of C is column q[j] of A."""
+    rng = np.random.default_rng(5)
+    M, K, N = 9, 21, 14
+    q = rng.permutation(K)[:N]
+    B = np.zeros((K, N), dtype=np.float32)
+    B[q, np.arange(N)] = 1.0
+    A = rand32(rng, (M, K))
+    got = oracle.gemm_ref(A, B, 0.5, 0.0)
+    want = 0.5 * A[:, q].astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("M,N,K", [(3, 5, 7), (16, 8, 1000), (1, 1, 4097)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (2.0, -1.0), (-3.0, 0.25)])
+def test_all_ones(M, N, K, alpha, beta):
+    """All-ones A and B: every entry is alpha*K + beta*C0 exactly."""
+    rng = np.random.default_rng(M * 7 + K)
+    A = np.ones((M, K), dtype=np.float32)
+    B = np.ones((K, N), dtype=np.float32)
+    C0 = rand32(rng, (M, N))
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    want = np.full((M, N), alpha * K, dtype=np.float64)
+    if beta != 0.0:
+        want = want + beta * C0.astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("alpha,beta", SCALARS)
+def test_rank_one(alpha, beta):
+    """K = 1: C is the scaled outer product of the single column and row."""
+    rng = np.random.default_rng(6)
+    M, N = 17, 12
+    A = rand32(rng, (M, 1))
+    B = rand32(rng, (1, N))
+    C0 = rand32(rng, (M, N))
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    want = alpha * np.multiply.outer(A[:, 0].astype(np.float64), B[0].astype(np.float64))
+    if beta != 0.0:
+        want = want + beta * C0.astype(np.float64)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_k_zero_is_empty_sum():
+    """K = 0: the sum is empty, C = beta*C0 (or 0)."""
+    C0 = np.arange(12, dtype=np.float32).reshape(3, 4)
+    A = np.zeros((3, 0), dtype=np.float32)
+    B = np.zeros((0, 4), dtype=np.float32)
+    np.testing.assert_array_equal(oracle.gemm_ref(A, B, 2.0, 0.5, C0), 0.5 * C0.astype(np.float64))
+    np.testing.assert_array_equal(oracle.gemm_ref(A, B, 2.0, 0.0, C0), np.zeros((3, 4)))
+
+
+# ----------------------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("shape", SHAPES_TINY)
+@pytest.mark.parametrize("alpha,beta", SCALARS)
+def test_bruteforce_dyadic_exact(shape, alpha, beta):
+    """Small dyadic operands: every partial sum is exact, so the oracle must equal
+    the exact rational result computed term by term."""
+    M, N, K = shape
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    A = (rng.integers(-8, 9, size=(M, K)) / 4.0).astype(np.float32)
+    B = (rng.integers(-8, 9, size=(K, N)) / 8.0).astype(np.float32)
+    C0 = (rng.integers(-8, 9, size=(M, N)) / 2.0).astype(np.float32)
+    exact, _ = exact_gemm(A, B, alpha, beta, C0)
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    want = np.array([[float(v) for v in row] for row in exact], dtype=np.float64).reshape(M, N)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("shape", SHAPES_TINY)
+@pytest.mark.parametrize("alpha,beta", SCALARS)
+def test_bruteforce_random_within_fp64_bound(shape, alpha, beta):
+    """Random fp32 operands: the oracle sits within (K+2)*u*D of the exact value,
+    the forward error bound of an fp64 inner product of exact terms."""
+    M, N, K = shape
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    A, B, C0 = rand32(rng, (M, K)), rand32(rng, (K, N)), rand32(rng, (M, N))
+    exact, bnd = exact_gemm(A, B, alpha, beta, C0)
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    for i in range(M):
+        for j in range(N):
+            err = abs(Fraction(float(got[i, j])) - exact[i, j])
+            assert err <= Fraction(K + 2) * Fraction(U) * bnd[i, j], (i, j)
+
+
+# ----------------------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("M,N,K", [(64, 96, 200), (300, 200, 500), (1, 257, 129), (33, 1, 65)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (2.0, -1.0), (1.0, 0.5)])
+def test_matches_torch_float64_matmul(M, N, K, alpha, beta):
+    """torch's double-precision matmul (a BLAS dgemm) agrees within 2*(K+2)*u*D."""
+    rng = np.random.default_rng(M + N + K)
+    A, B, C0 = rand32(rng, (M, K)), rand32(rng, (K, N)), rand32(rng, (M, N))
+    got = oracle.gemm_ref(A, B, alpha, beta, C0)
+    t = alpha * (torch.from_numpy(A).double() @ torch.from_numpy(B).double())
+    if beta != 0.0:
+        t = t + beta * torch.from_numpy(C0).double()
+    D = oracle.gemm_absbound(A, B, alpha, beta, C0)
+    assert np.all(np.abs(got - t.numpy()) <= 2 * (K + 2) * U * D)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def test_transpose_invariant():
+    """(A B)^T = B^T A^T term by term, in the same k order, so bitwise."""
+    rng = np.random.default_rng(7)
+    M, N, K = 37, 23, 51
+    A, B, C0 = rand32(rng, (M, K)), rand32(rng, (K, N)), rand32(rng, (M, N))
+    C = oracle.gemm_ref(A, B, 1.5, -0.5, C0)
+    Ct = oracle.gemm_ref(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), 1.5, -0.5,
+                         np.ascontiguousarray(C0.T))
+    np.testing.assert_array_equal(C, Ct.T)
+
+
+def test_not_symmetric_in_operands():
+    """Swapping A and B (square case) changes the answer: guards against an
+    oracle that accidentally computes B A or A^T B."""
+    rng = np.random.default_rng(8)
+    A, B = rand32(rng, (8, 8)), rand32(rng, (8, 8))
+    assert not np.allclose(oracle.gemm_ref(A, B), oracle.gemm_ref(B, A))
+    assert not np.allclose(oracle.gemm_ref(A, B), oracle.gemm_ref(np.ascontiguousarray(A.T), B))
+
+
+@pytest.mark.parametrize("p", [-3, 1, 5])
+def test_alpha_power_of_two_scales_exactly(p):
+    rng = np.random.default_rng(9)
+    A, B = rand32(rng, (11, 30)), rand32(rng, (30, 13))
+    np.testing.assert_array_equal(oracle.gemm_ref(A, B, 2.0 ** p), (2.0 ** p) * oracle.gemm_ref(A, B, 1.0))
+
+
+def test_alpha_sign_flips():
+    rng = np.random.default_rng(19)
+    A, B = rand32(rng, (11, 30)), rand32(rng, (30, 13))
+    np.testing.assert_array_equal(oracle.gemm_ref(A, B, -1.0), -oracle.gemm_ref(A, B, 1.0))
+
+
+def test_beta_term_is_linear_in_C0():
+    """C(beta, C0) - C(0) = beta*C0 up to one rounding per entry."""
+    rng = np.random.default_rng(20)
+    A, B, C0 = rand32(rng, (9, 40)), rand32(rng, (40, 7)), rand32(rng, (9, 7))
+    diff = oracle.gemm_ref(A, B, 1.0, 0.75, C0) - oracle.gemm_ref(A, B, 1.0, 0.0)
+    D = oracle.gemm_absbound(A, B, 1.0, 0.75, C0)
+    assert np.all(np.abs(diff - 0.75 * C0.astype(np.float64)) <= 4 * U * D)
+
+
+def test_k_split_additivity():
+    """A B = A[:, :k] B[:k] + A[:, k:] B[k:] within fp64 rounding."""
+    rng = np.random.default_rng(11)
+    M, N, K, k1 = 19, 17, 90, 37
+    A, B = rand32(rng, (M, K)), rand32(rng, (K, N))
+    full = oracle.gemm_ref(A, B)
+    part = (oracle.gemm_ref(np.ascontiguousarray(A[:, :k1]), np.ascontiguousarray(B[:k1]))
+            + oracle.gemm_ref(np.ascontiguousarray(A[:, k1:]), np.ascontiguousarray(B[k1:])))
+    D = oracle.gemm_absbound(A, B)
+    assert np.all(np.abs(full - part) <= 2 * (K + 2) * U * D)
+    assert not np.array_equal(oracle.gemm_ref(np.ascontiguousarray(A[:, :k1]),
+                                              np.ascontiguousarray(B[:k1])), full)
+
+
+# ----------------------------------------------------------------------------- conventions
+
+def test_beta_zero_does_not_read_C0():
+    """beta == 0 leaves the C0 term out entirely, so NaN in C0 cannot appear."""
+    rng = np.random.default_rng(12)
+    A, B = rand32(rng, (6, 9)), rand32(rng, (9, 5))
+    C0 = np.full((6, 5), np.nan, dtype=np.float32)
+    got = oracle.gemm_ref(A, B, 1.0, 0.0, C0)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(got, oracle.gemm_ref(A, B, 1.0, 0.0, None))
+
+
+def test_beta_nonzero_propagates_nan_per_entry():
+    rng = np.random.default_rng(13)
+    A, B = rand32(rng, (6, 9)), rand32(rng, (9, 5))
+    C0 = rand32(rng, (6, 5))
+    C0[2, 3] = np.nan
+    got = oracle.gemm_ref(A, B, 1.0, 1.0, C0)
+    assert np.isnan(got[2, 3])
+    assert np.isfinite(np.delete(got.ravel(), 2 * 5 + 3)).all()
+
+
+@pytest.mark.parametrize("pa,pb,pc", [(3, 0, 0), (0, 5, 0), (0, 0, 7), (1, 2, 3)])
+def test_leading_dimensions_honoured(pa, pb, pc):
+    """Views into NaN-padded buffers give the same result as packed copies."""
+    rng = np.random.default_rng(14)
+    M, N, K = 10, 12, 9
+    A, B, C0 = rand32(rng, (M, K)), rand32(rng, (K, N)), rand32(rng, (M, N))
+    want = oracle.gemm_ref(A, B, 2.0, -1.0, C0)
+    got = oracle.gemm_ref(padded(A, pa), padded(B, pb), 2.0, -1.0, padded(C0, pc))
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- bf16 operands
+
+BF16_BITS = {
+    0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0x3F81: 1.0 + 2.0 ** -7,
+    0x3E80: 0.25, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,   # largest finite bf16
+    0x0080: 2.0 ** -126,                                    # smallest normal
+    0x0001: 2.0 ** -133,                                    # smallest subnormal
+    0x8000: -0.0, 0x4049: 3.140625,
+}
+
+
+@pytest.mark.parametrize("bits,value", sorted(BF16_BITS.items()))
+def test_bf16_widening_follows_format(bits, value):
+    """A 1x1x1 product with B = 1.0 returns the operand's value as the bf16
+    format defines it (sign, 8-bit exponent, 7-bit fraction)."""
+    A = np.array([[bits]], dtype=np.uint16)
+    one = np.array([[0x3F80]], dtype=np.uint16)
+    got = oracle.gemm_ref(A, one)[0, 0]
+    assert got == value   # -0.0 sums to +0.0 from the empty-sum start; equal as values
+    got_b = oracle.gemm_ref(one, A)[0, 0]
+    assert got_b == value
+
+
+def test_bf16_matches_f32_path_on_same_values():
+    """bf16 operands widened by the format give the same fp64 result as the same
+    values handed over as fp32 (torch's bf16 -> fp32 conversion is exact)."""
+    g = torch.Generator().manual_seed(15)
+    A = torch.randn(21, 44, generator=g).to(torch.bfloat16)
+    B = torch.randn(44, 18, generator=g).to(torch.bfloat16)
+    C0 = torch.randn(21, 18, generator=g)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    got = oracle.gemm_ref(bits(A), bits(B), 1.0, 0.5, C0.numpy())
+    want = oracle.gemm_ref(A.float().numpy(), B.float().numpy(), 1.0, 0.5, C0.numpy())
+    np.testing.assert_array_equal(got, want)
+    Db = oracle.gemm_absbound(bits(A), bits(B), 1.0, 0.5, C0.numpy())
+    Df = oracle.gemm_absbound(A.float().numpy(), B.float().numpy(), 1.0, 0.5, C0.numpy())
+    np.testing.assert_array_equal(Db, Df)
+
+
+def test_bf16_identity():
+    g = torch.Generator().manual_seed(16)
+    B = torch.randn(8, 9, generator=g).to(torch.bfloat16)
+    I = torch.eye(8).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.gemm_ref(bits(I), bits(B), 3.0),
+                                  3.0 * B.double().numpy())
+
+
+# ----------------------------------------------------------------------------- denominator
+
+def test_absbound_all_ones():
+    C0 = np.array([[-2.0, 3.0]], dtype=np.float32)
+    A = -np.ones((1, 5), dtype=np.float32)
+    B = np.ones((5, 2), dtype=np.float32)
+    np.testing.assert_array_equal(oracle.gemm_absbound(A, B, -2.0, -0.5, C0),
+                                  np.array([[10.0 + 1.0, 10.0 + 1.5]]))
+
+
+def test_absbound_identity_and_sign_invariance():
+    rng = np.random.default_rng(17)
+    B, C0 = rand32(rng, (6, 4)), rand32(rng, (6, 4))
+    I = np.eye(6, dtype=np.float32)
+    D = oracle.gemm_absbound(I, B, -2.0, 0.5, C0)
+    np.testing.assert_array_equal(D, 2.0 * np.abs(B.astype(np.float64)) + 0.5 * np.abs(C0.astype(np.float64)))
+    A, C1 = rand32(rng, (5, 6)), rand32(rng, (5, 4))
+    np.testing.assert_array_equal(oracle.gemm_absbound(A, B, 1.0, 0.5, C1),
+                                  oracle.gemm_absbound(-A, B, -1.0, -0.5, -C1))
+
+
+def test_absbound_dominates_result_and_equals_gemm_of_abs():
+    """|C| <= D by the triangle inequality, and D is the GEMM of the absolute values."""
+    rng = np.random.default_rng(18)
+    A, B, C0 = rand32(rng, (12, 33)), rand32(rng, (33, 10)), rand32(rng, (12, 10))
+    C = oracle.gemm_ref(A, B, -1.5, 0.25, C0)
+    D = oracle.gemm_absbound(A, B, -1.5, 0.25, C0)
+    assert np.all(np.abs(C) <= D * (1 + 64 * U))
+    np.testing.assert_array_equal(D, oracle.gemm_ref(np.abs(A), np.abs(B), 1.5, 0.25, np.abs(C0)))
+
+
+# ----------------------------------------------------------------------------- acceptance measure
+
+def test_error_ratio_measure():
+    ref = np.array([[1.0, 0.0, -2.0]])
+    D = np.array([[2.0, 0.0, 4.0]])
+    assert oracle.error_ratio(np.array([[1.0, 0.0, -2.0]]), ref, D) == 0.0
+    assert oracle.error_ratio(np.array([[1.5, 0.0, -2.0]]), ref, D) == 0.25
+    assert oracle.error_ratio(np.array([[1.0, 1e-30, -2.0]]), ref, D) == float("inf")
+    assert oracle.error_ratio(np.array([[np.nan, 0.0, -2.0]]), ref, D) == float("inf")
+
+
+def test_oracle_uses_threads():
+    assert oracle.num_threads() >= 1

@@ -1,0 +1,127 @@
+"""Seeded synthetic GEMM inputs shared by the tests, the smoke check and the
+benchmark.
+
+This module only draws random numbers; it holds none of the GEMM arithmetic.
+Both the HIP library and the CPU oracle consume the same host arrays it
+returns, so the generator's own rounding cannot break parity.
+
+Recipe (fixed, so that every run sees the same bytes):
+
+* ``g = torch.Generator('cpu').manual_seed(seed)`` for each workload.
+* Draw order A, then B, then C0.  C0 is always drawn, even when ``beta == 0``,
+  so the sequence does not depend on beta.
+* ``uniform``: ``torch.empty(shape).uniform_(-1, 1, generator=g)``.
+* ``normal``: ``torch.randn(shape, generator=g)``.
+* bf16 operands: the fp32 draw rounded to bf16 with ``.to(torch.bfloat16)``
+  (round to nearest even); C0 stays fp32.
+
+The shapes are the square and ragged problems the pages measure on (4092 and
+4096 cubes on page 1 and page 3), a small cube, a ragged shape that is a
+multiple of no tile size, a decode-like M = 16 shape (the bandwidth-bound
+case the second page warns about) and a large bf16 cube.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32" or "bf16f32" (bf16 operands, fp32 accumulate and output)
+    M: int
+    N: int
+    K: int
+    alpha: float
+    beta: float
+    dist: str           # "uniform" (U[-1, 1]) or "normal" (N(0, 1))
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def elt_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Bytes the operation must move: read A and B (and C0 if beta != 0), write C."""
+        ab = (self.M * self.K + self.K * self.N) * self.elt_bytes
+        c = self.M * self.N * 4
+        return ab + c * (2 if self.beta != 0.0 else 1)
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("f32_256", "f32", 256, 256, 256, 1.0, 0.0, "uniform", 0),
+        Workload("f32_4092_beta", "f32", 4092, 4092, 4092, 1.0, 0.5, "uniform", 1),
+        Workload("f32_4096", "f32", 4096, 4096, 4096, 1.0, 0.0, "normal", 2),
+        Workload("f32_1000x3000x777", "f32", 1000, 3000, 777, 2.0, -1.0, "uniform", 3),
+        Workload("f32_16x8192x8192", "f32", 16, 8192, 8192, 1.0, 0.0, "uniform", 3),
+        Workload("bf16f32_8192", "bf16f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 4),
+    ]
+}
+
+
+def _draw(shape, dist: str, g: torch.Generator) -> torch.Tensor:
+    if dist == "uniform":
+        return torch.empty(shape, dtype=torch.float32).uniform_(-1.0, 1.0, generator=g)
+    if dist == "normal":
+        return torch.randn(shape, dtype=torch.float32, generator=g)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def make_inputs(w: Workload):
+    """Host tensors (A, B, C0) for a workload.
+
+    A and B are float32 for ``f32`` workloads and bfloat16 for ``bf16f32``;
+    C0 is always float32 of shape (M, N).
+    """
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    A = _draw((w.M, w.K), w.dist, g)
+    B = _draw((w.K, w.N), w.dist, g)
+    C0 = _draw((w.M, w.N), w.dist, g)
+    if w.dtype == "bf16f32":
+        A = A.to(torch.bfloat16)
+        B = B.to(torch.bfloat16)
+    return A, B, C0
+
+
+def make_integer_inputs(M: int, N: int, K: int, seed: int, lo: int = -4, hi: int = 4,
+                        dtype: str = "f32"):
+    """Small-integer operands (exact in fp32 and bf16) and an integer C0.
+
+    With |entries| <= 4 every partial sum stays an integer below 2**24 for
+    K < 2**20, so any summation order gives the same exact result.
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    A = torch.randint(lo, hi + 1, (M, K), generator=g).to(torch.float32)
+    B = torch.randint(lo, hi + 1, (K, N), generator=g).to(torch.float32)
+    C0 = torch.randint(lo, hi + 1, (M, N), generator=g).to(torch.float32)
+    if dtype == "bf16f32":
+        A = A.to(torch.bfloat16)
+        B = B.to(torch.bfloat16)
+    return A, B, C0
+
+
+def make_random_inputs(M: int, N: int, K: int, seed: int, dist: str = "uniform",
+                       dtype: str = "f32"):
+    """Random operands of an arbitrary shape with the same draw order."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    A = _draw((M, K), dist, g)
+    B = _draw((K, N), dist, g)
+    C0 = _draw((M, N), dist, g)
+    if dtype == "bf16f32":
+        A = A.to(torch.bfloat16)
+        B = B.to(torch.bfloat16)
+    return A, B, C0
+
+
+def bf16_bits(t: torch.Tensor):
+    """uint16 numpy view of a bfloat16 tensor's bit patterns (for the oracle)."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view("uint16")
