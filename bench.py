@@ -1,0 +1,196 @@
+"""Throughput of libgemm on one MI355X.
+
+One step is one pass of the whole hot path over synthetic, seeded inputs
+already resident in HBM:
+
+  * fp32 GEMM, M = N = K = 4096 (alpha 1, beta 0, N(0,1), seed 2)  -- tiled MFMA path
+  * bf16-operand / fp32-accumulate GEMM, M = N = K = 8192 (alpha 1, beta 0,
+    N(0,1) rounded to bf16, seed 4)                                   -- tiled MFMA path
+  * fp32 GEMM, M = 16, N = K = 8192 (alpha 1, beta 0, U[-1,1], seed 3) -- skinny streaming path
+
+``value`` is the step's total arithmetic (2*M*N*K summed over the three
+calls) divided by the wall time of the timed steps, in GFLOP/s.  Each launch
+is also bracketed by HIP events on the stream it runs on, giving every
+kernel's average duration; ``roofline`` reports the kernel with the largest
+share of the step against its own roof (fp32 or bf16 matrix peak, or HBM
+bandwidth for the skinny path) and ``parts`` reports all three.
+
+The skinny call cycles through three copies of B (3 x 268 MB) so every call
+streams B from HBM rather than from the 256 MB last-level cache.
+
+``cpu_baseline`` times the CPU oracle (fp64, OpenMP) on a bounded sample of
+the same step: all 4096 rows of the fp32 problem, the first 1024 rows of the
+bf16 problem and the whole skinny problem.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GFLOP/s (2MNK/t) fp32 4096^3 + bf16 8192^3, % of MI355X MFMA peak"
+PEAK_TFLOPS = {"f32": 157.3, "bf16f32": 2500.0}
+PEAK_HBM_GBS = 8000.0
+STEP = ["f32_4096", "bf16f32_8192", "f32_16x8192x8192"]
+SKINNY_COPIES = 3
+CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 1024, "f32_16x8192x8192": 16}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=STEP, default=None, help="time a single workload of the step")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file of measured HBM bytes per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library is single-GPU (no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_gemm_f32_amd as tg
+    from tiled_gemm_f32_amd import _lib
+    from tiled_gemm_f32_amd.workloads import WORKLOADS, make_inputs
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from tiled_gemm_f32_amd import build as hip_build
+        hip_build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = [args.only] if args.only else STEP
+
+    # Inputs resident in HBM before timing.
+    calls = []
+    for name in names:
+        w = WORKLOADS[name]
+        A, B, C0 = make_inputs(w)
+        Ad, C = A.to(dev), C0.to(dev)
+        copies = SKINNY_COPIES if w.M <= 16 else 1
+        Bs = [B.to(dev) for _ in range(copies)]
+        calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "i": 0, "durs": []})
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def launch(c, record):
+        w = c["w"]
+        B = c["B"][c["i"] % len(c["B"])]
+        c["i"] += 1
+        fn = tg.gemm_f32 if w.dtype == "f32" else tg.gemm_bf16f32
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        st = fn(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                c["C"].data_ptr(), w.N, sh)
+        if st != tg.GEMM_OK:
+            raise tg.GemmError(st, w.name)
+        if record:
+            e1.record(stream)
+            c["durs"].append((e0, e1))
+
+    for _ in range(args.warmup):
+        for c in calls:
+            launch(c, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for c in calls:
+            launch(c, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    flops_step = sum(c["w"].flops for c in calls)
+    value = flops_step * args.steps / elapsed / 1e9
+    parts = {}
+    for c in calls:
+        w = c["w"]
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in c["durs"]) / len(c["durs"])
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
+        plan = tg.gemm_plan_query(0 if w.dtype == "f32" else 1, w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K,
+                                  c["B"][0].data_ptr(), w.N, w.beta, c["C"].data_ptr(), w.N)[1]
+        kname = tg.gemm_kernel_query(plan["kernel_id"])["name"]
+        bound = "hbm" if w.M <= 16 else "mfma"
+        parts[w.name] = {
+            "kernel": kname, "ms": round(ms, 5), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+            "bound": bound,
+            "frac": round(gbs / PEAK_HBM_GBS if bound == "hbm" else tflops / PEAK_TFLOPS[w.dtype], 4),
+            "flops": w.flops, "algorithmic_bytes": w.algorithmic_bytes,
+        }
+
+    def roofline_of(name):
+        p = parts[name]
+        w = WORKLOADS[name]
+        if p["bound"] == "hbm":
+            achieved, peak, unit = p["gbs"], PEAK_HBM_GBS, "GB/s"
+        else:
+            achieved, peak, unit = p["tflops"], PEAK_TFLOPS[w.dtype], "TFLOP/s"
+        return {"kernel": p["kernel"], "workload": name, "bound": p["bound"], "achieved": achieved, "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None}
+
+    dominant = max(parts, key=lambda n: parts[n]["ms"])
+    roof = roofline_of(dominant)
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("kernel") == roof["kernel"]:
+            roof["traffic"] = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.only:
+        cpu = cpu_baseline(calls)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32+bf16f32", "data": "synthetic",
+        "config": {"workload": " + ".join(names), "parallelism": "single-gpu",
+                   "shapes": {n: [WORKLOADS[n].M, WORKLOADS[n].N, WORKLOADS[n].K] for n in names}},
+        "roofline": roof,
+        "rooflines": [roofline_of(n) for n in parts],
+        "parts": parts,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(calls):
+    """The oracle on a bounded sample of the step, timed on the host cores."""
+    import numpy as np
+    import oracle
+    from tiled_gemm_f32_amd.workloads import bf16_bits, make_inputs
+
+    flops, secs, sample = 0, 0.0, []
+    for c in calls:
+        w = c["w"]
+        rows = min(CPU_SAMPLE_ROWS.get(w.name, w.M), w.M)
+        A, B, C0 = make_inputs(w)
+        a = bf16_bits(A) if w.dtype == "bf16f32" else A.numpy()
+        b = bf16_bits(B) if w.dtype == "bf16f32" else B.numpy()
+        a = np.ascontiguousarray(a[:rows])
+        c0 = np.ascontiguousarray(C0.numpy()[:rows])
+        t0 = time.perf_counter()
+        oracle.gemm_ref(a, b, w.alpha, w.beta, c0)
+        secs += time.perf_counter() - t0
+        flops += 2 * rows * w.N * w.K
+        sample.append(f"{w.name}: rows 0..{rows - 1} of {w.M}")
+    return {"value": round(flops / secs / 1e9, 2), "unit": "GFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(secs, 2), "sample": "; ".join(sample)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * libgemm -- blocked general matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ *     C = alpha * (A x B) + beta * C
+ *
+ * with A of M x K, B of K x N and C of M x N, all row-major.  This is the
+ * operation defined at the opening of "GEMM Worklog I: Naive to Tiled" and
+ * posed as a single call in "A GEMM Kernel, Step by Step" (section "The
+ * ladder we are climbing"); the host launcher shape (sizes, operand pointers,
+ * a stream) follows the "Code" section of "Tiled matrix multiplication",
+ * extended with alpha, beta and leading dimensions.
+ *
+ * Layout.  Element (i, k) of A is A[i*lda + k]; (k, j) of B is B[k*ldb + j];
+ * (i, j) of C is C[i*ldc + j].  Requirements: lda >= max(1, K),
+ * ldb >= max(1, N), ldc >= max(1, N).  Padding between rows is never read
+ * in a way that can reach C (it may hold anything, NaN included).
+ *
+ * Memory.  A, B and C are DEVICE pointers on the current HIP device.  The
+ * caller owns them; the library allocates nothing on these calls and keeps
+ * no state between them ("Tiled matrix multiplication", section "How it
+ * works": no state between calls).  C must not overlap A or B.
+ *
+ * Streams.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL means the default stream) and the call returns without waiting.  The
+ * result is visible after the stream is synchronised.  Calls on one stream
+ * run in order.
+ *
+ * Scalars.  alpha and beta are fp32.  When beta == 0, C is write-only: its
+ * old contents are never read, so NaN/Inf there does not propagate (the BLAS
+ * convention; the pages leave this open).  When K == 0 or alpha == 0, A and
+ * B are not read and C becomes beta * C (or 0).
+ *
+ * Errors.  Every function returns a gemm_status.  Argument checks happen
+ * before any HIP call, so an invalid call has no side effect.
+ * GEMM_ERR_LAUNCH reports a HIP error raised by the kernel launch (the
+ * stream may then be unusable).  No function throws or aborts.
+ */
+#ifndef LIBGEMM_GEMM_H
+#define LIBGEMM_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The library is built with hidden visibility; only these entry points are exported. */
+#define GEMM_API __attribute__((visibility("default")))
+
+typedef enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,  /* negative size, leading dimension too small, NULL or
+                                  misaligned pointer for an operand that is read or written */
+    GEMM_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels index: M, N or K above
+                                  2^31 - 1, or lda / ldb of 2^21 elements or more; or a forced
+                                  kernel that cannot run on these operands */
+    GEMM_ERR_LAUNCH = 3,       /* the HIP runtime reported an error for the launch */
+    GEMM_ERR_DEVICE = 4        /* no usable gfx950 device is current */
+} gemm_status;
+
+/* A hipStream_t, passed through as an opaque pointer; NULL = default stream. */
+typedef void *gemm_stream_t;
+
+/*
+ * fp32 GEMM.  Products and sums are fp32 (matrix-core fp32 multiply-add);
+ * accumulation covers all of K before alpha and beta are applied.
+ * M <= 16 takes the bandwidth-oriented skinny path (the decode-GEMV case of
+ * "Tiled matrix multiplication", section "Avoid when"); every other shape
+ * takes the LDS-tiled MFMA path.
+ */
+GEMM_API gemm_status gemm_f32(int64_t M, int64_t N, int64_t K, float alpha,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float beta, float *C, int64_t ldc,
+                     gemm_stream_t stream);
+
+/*
+ * bf16 operands, fp32 accumulate and fp32 C.  A and B hold bfloat16 bit
+ * patterns (uint16_t).  Each bf16 x bf16 product is exact in fp32; sums are
+ * fp32.  The tensor-core variant of the blocked method ("Tiled matrix
+ * multiplication", section "How it works", tensor-core level).
+ */
+GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha,
+                         const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb,
+                         float beta, float *C, int64_t ldc,
+                         gemm_stream_t stream);
+
+/* Static English text for a status code (never NULL). */
+GEMM_API const char *gemm_status_string(gemm_status status);
+
+/* ------------------------------------------------------------------------
+ * Kernel selection.  The library ships several kernels and picks one per
+ * call from the shape, the alignment and the tile count against the 256
+ * compute units ("A GEMM Kernel, Step by Step", section "Six parameters,
+ * found by search": the library picks among kernels at run time by shape).
+ * The functions below expose that choice so it can be inspected and tested.
+ * ---------------------------------------------------------------------- */
+
+typedef enum gemm_path {
+    GEMM_PATH_NONE = 0,     /* quick return: nothing launched (M == 0 or N == 0) */
+    GEMM_PATH_SCALE = 1,    /* C = beta * C only (K == 0 or alpha == 0) */
+    GEMM_PATH_TILED = 2,    /* LDS-tiled MFMA kernel */
+    GEMM_PATH_SKINNY = 3    /* M <= 16 streaming kernel */
+} gemm_path;
+
+typedef enum gemm_dtype {
+    GEMM_DTYPE_F32 = 0,     /* fp32 operands */
+    GEMM_DTYPE_BF16F32 = 1  /* bf16 operands, fp32 accumulate and output */
+} gemm_dtype;
+
+typedef struct gemm_kernel_info {
+    int32_t id;             /* 1-based; 0 is never a kernel */
+    int32_t dtype;          /* gemm_dtype */
+    int32_t path;           /* gemm_path (TILED or SKINNY) */
+    int32_t tile_m, tile_n, tile_k;  /* workgroup tile (skinny: rows covered, columns, k unroll) */
+    int32_t threads;        /* threads per workgroup */
+    int32_t vec_a, vec_b;   /* elements per global load of A and of B (1 = element loads) */
+    const char *name;       /* static string */
+} gemm_kernel_info;
+
+typedef struct gemm_plan {
+    int32_t path;           /* gemm_path */
+    int32_t kernel_id;      /* kernel chosen (0 for NONE / SCALE) */
+    int64_t grid;           /* workgroups launched (0 for NONE) */
+    int32_t threads;        /* threads per workgroup */
+    int32_t tile_m, tile_n, tile_k;
+    int32_t vec_a, vec_b;
+} gemm_plan;
+
+/* Number of kernels in the table; ids run from 1 to this value. */
+GEMM_API int32_t gemm_kernel_count(void);
+
+/* Description of kernel `id`.  GEMM_ERR_INVALID_ARG for an unknown id or NULL out. */
+GEMM_API gemm_status gemm_kernel_query(int32_t id, gemm_kernel_info *out);
+
+/*
+ * The choice gemm_f32 / gemm_bf16f32 would make for these arguments,
+ * computed on the host without touching the GPU.  Pointers are only
+ * inspected (NULL-ness and alignment), never dereferenced.  force_kernel = 0
+ * lets the library choose; a positive id asks for that kernel and fails with
+ * GEMM_ERR_UNSUPPORTED if it cannot run these operands (wrong dtype, or a
+ * vector width the alignment does not allow).  Returns the same status the
+ * call itself would return before launching.
+ */
+GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
+                            const void *A, int64_t lda, const void *B, int64_t ldb,
+                            float beta, const float *C, int64_t ldc,
+                            int32_t force_kernel, gemm_plan *out);
+
+/* gemm_f32 / gemm_bf16f32 with a forced kernel (force_kernel as above). */
+GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb,
+                        float beta, float *C, int64_t ldc,
+                        int32_t force_kernel, gemm_stream_t stream);
+
+GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
+                            const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                            float beta, float *C, int64_t ldc,
+                            int32_t force_kernel, gemm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_GEMM_H */

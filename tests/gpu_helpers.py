@@ -1,0 +1,93 @@
+"""Helpers for the GPU parity tests: move seeded host inputs to the device,
+call the library through its C ABI, bring C back, and compare with the
+oracle.  Nothing here computes a GEMM."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import tiled_gemm_f32_amd as tg
+from tiled_gemm_f32_amd.workloads import bf16_bits
+
+TOL = {"f32": 2e-6, "bf16f32": 1e-5}
+
+
+def say(msg: str):
+    """Name the case before its GPU step (flushed, so a crash still shows it)."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def host_view(t: torch.Tensor):
+    """numpy operand for the oracle: float32 array or uint16 bf16 bits."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.contiguous().numpy()
+
+
+def padded_device(t: torch.Tensor, pad: int = 0, offset: int = 0, fill=float("nan")):
+    """Device copy of t inside a wider buffer.
+
+    The row stride becomes cols + pad (padding filled with ``fill``) and the
+    view starts ``offset`` elements into the buffer (to exercise unaligned
+    bases).  Returns (view, backing buffer).
+    """
+    rows, cols = t.shape
+    ld = cols + pad
+    buf = torch.full((rows * ld + offset + 1,), fill, dtype=t.dtype, device="cuda")
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :cols]
+    view.copy_(t.to("cuda"))
+    return view, buf
+
+
+def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c_fill=None):
+    """Run the library on host inputs; returns (C as float32 numpy, C device view, C buffer)."""
+    Ad, _a = padded_device(A, pad[0], offset[0])
+    Bd, _b = padded_device(B, pad[1], offset[1])
+    if c_fill is None:
+        Cd, cbuf = padded_device(C0, pad[2], offset[2])
+    else:
+        Cd, cbuf = padded_device(torch.full_like(C0, c_fill), pad[2], offset[2])
+    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel)
+    torch.cuda.synchronize()
+    return Cd.cpu().numpy(), Cd, cbuf
+
+
+def oracle_ref(A, B, C0, alpha, beta):
+    a, b = host_view(A), host_view(B)
+    c0 = C0.numpy()
+    return oracle.gemm_ref(a, b, alpha, beta, c0), oracle.gemm_absbound(a, b, alpha, beta, c0)
+
+
+def ratio(C_gpu, A, B, C0, alpha, beta):
+    ref, D = oracle_ref(A, B, C0, alpha, beta)
+    return oracle.error_ratio(C_gpu, ref, D)
+
+
+def sampled_ratio(C_gpu, A, B, C0, alpha, beta, rows, cols):
+    """Error ratio over whole sampled rows and whole sampled columns of C."""
+    a, b, c0 = host_view(A), host_view(B), C0.numpy()
+    worst = 0.0
+    for i in rows:
+        ref = oracle.gemm_ref(a[i:i + 1], b, alpha, beta, c0[i:i + 1])
+        D = oracle.gemm_absbound(a[i:i + 1], b, alpha, beta, c0[i:i + 1])
+        worst = max(worst, oracle.error_ratio(C_gpu[i:i + 1], ref, D))
+    bc = np.ascontiguousarray(b[:, cols])
+    c0c = np.ascontiguousarray(c0[:, cols])
+    ref = oracle.gemm_ref(a, bc, alpha, beta, c0c)
+    D = oracle.gemm_absbound(a, bc, alpha, beta, c0c)
+    worst = max(worst, oracle.error_ratio(C_gpu[:, cols], ref, D))
+    return worst
+
+
+def boundary_indices(n: int, tiles=(16, 32, 64, 128, 256), extra: int = 8, seed: int = 0):
+    """Indices at tile boundaries (first/last of each tile) plus random ones."""
+    idx = {0, n - 1}
+    for t in tiles:
+        for b in range(t, n, t):
+            if b % 1024 in (0,) or b < 3 * t or b > n - 3 * t:
+                idx.update({b - 1, b})
+    rng = np.random.default_rng(seed)
+    idx.update(rng.integers(0, n, size=extra).tolist())
+    return sorted(i for i in idx if 0 <= i < n)

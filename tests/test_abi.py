@@ -1,0 +1,199 @@
+"""The C ABI on the host: exported symbols, argument validation and kernel
+choice.  Nothing here launches GPU work; validation and planning are plain
+host code, so they run (and are tested) without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_gemm_f32_amd as tg
+from tiled_gemm_f32_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm.h")
+
+F32, BF16 = tg.GEMM_DTYPE_F32, tg.GEMM_DTYPE_BF16F32
+OK, INVALID, UNSUP = tg.GEMM_OK, tg.GEMM_ERR_INVALID_ARG, tg.GEMM_ERR_UNSUPPORTED
+# Fake but well-aligned device addresses: planning only inspects them.
+PA, PB, PC = 0x7f0000000000, 0x7f1000000000, 0x7f2000000000
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"GEMM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def plan(dtype, M, N, K, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, beta=0.0, C=PC, ldc=None, force=0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return tg.gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force)
+
+
+def kernel_ids(**match):
+    return [k["id"] for k in tg.kernels() if all(k[f] == v for f, v in match.items())]
+
+
+# ----------------------------------------------------------------------------- library
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    lib = _lib.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    # Hidden visibility: nothing but the ABI (and runtime glue) leaks out.
+    assert not [s for s in exported if "gemm" in s and s not in names]
+
+
+def test_status_strings():
+    for st in range(5):
+        s = tg.gemm_status_string(st)
+        assert s and s != "unknown status"
+    assert tg.gemm_status_string(99) == "unknown status"
+
+
+def test_kernel_table_is_consistent():
+    ks = tg.kernels()
+    assert len(ks) == tg.gemm_kernel_count() > 0
+    assert [k["id"] for k in ks] == list(range(1, len(ks) + 1))
+    assert len({k["name"] for k in ks}) == len(ks)
+    for k in ks:
+        assert k["dtype"] in (F32, BF16)
+        assert k["path"] in (tg.GEMM_PATH_TILED, tg.GEMM_PATH_SKINNY)
+        assert k["threads"] % 64 == 0 and 64 <= k["threads"] <= 1024
+        if k["path"] == tg.GEMM_PATH_TILED:
+            assert k["tile_m"] % 32 == 0 and k["tile_n"] % 32 == 0
+    with pytest.raises(tg.GemmError):
+        tg.gemm_kernel_query(0)
+    with pytest.raises(tg.GemmError):
+        tg.gemm_kernel_query(len(ks) + 1)
+
+
+# ----------------------------------------------------------------------------- validation
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("kwargs", [
+    dict(M=-1, N=4, K=4), dict(M=4, N=-1, K=4), dict(M=4, N=4, K=-1),
+    dict(M=4, N=4, K=8, lda=7), dict(M=4, N=8, K=4, ldb=7), dict(M=4, N=8, K=4, ldc=7),
+    dict(M=4, N=4, K=0, lda=0), dict(M=4, N=4, K=4, C=0), dict(M=4, N=4, K=4, A=0), dict(M=4, N=4, K=4, B=0),
+    dict(M=4, N=4, K=4, C=PC + 2),
+])
+def test_invalid_arguments_rejected(dtype, kwargs):
+    st, _ = plan(dtype, **kwargs)
+    assert st == INVALID
+
+
+def test_misaligned_element_pointers_rejected():
+    assert plan(F32, 4, 4, 4, A=PA + 2)[0] == INVALID
+    assert plan(BF16, 4, 4, 4, A=PA + 1)[0] == INVALID
+    assert plan(BF16, 4, 4, 4, A=PA + 2)[0] == OK       # 2-byte aligned is enough for bf16
+
+
+def test_operands_not_needed_may_be_null():
+    assert plan(F32, 4, 4, 0, A=0, B=0)[0] == OK        # K == 0: A, B not read
+    assert plan(F32, 4, 4, 4, alpha=0.0, A=0, B=0)[0] == OK
+    assert plan(F32, 0, 4, 4, A=0, B=0, C=0)[0] == OK   # empty C
+
+
+def test_unsupported_sizes():
+    assert plan(F32, 2 ** 31, 4, 4)[0] == UNSUP
+    assert plan(F32, 4, 4, 4, lda=2 ** 21)[0] == UNSUP
+    assert plan(F32, 4, 4, 4, ldb=2 ** 21)[0] == UNSUP
+    assert plan(F32, 4, 4, 4, lda=2 ** 21 - 1)[0] == OK
+
+
+def test_invalid_dtype_and_force():
+    assert plan(7, 4, 4, 4)[0] == INVALID
+    assert plan(F32, 4, 4, 4, force=-1)[0] == INVALID
+    assert plan(F32, 4, 4, 4, force=tg.gemm_kernel_count() + 1)[0] == INVALID
+
+
+def test_argument_errors_return_before_any_device_call():
+    # Invalid calls come back from the real entry points without a GPU.
+    lib = _lib.load()
+    assert tg.gemm_f32(-1, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, 0) == INVALID
+    assert tg.gemm_bf16f32(4, 4, 8, 1.0, PA, 7, PB, 4, 0.0, PC, 4, 0) == INVALID
+    assert tg.gemm_f32_ex(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, -5, 0) == INVALID
+    assert lib is not None
+
+
+# ----------------------------------------------------------------------------- quick returns
+
+def test_quick_return_paths():
+    assert plan(F32, 0, 10, 10)[1]["path"] == tg.GEMM_PATH_NONE
+    assert plan(F32, 10, 0, 10)[1]["path"] == tg.GEMM_PATH_NONE
+    st, p = plan(F32, 10, 10, 0)
+    assert st == OK and p["path"] == tg.GEMM_PATH_SCALE and p["kernel_id"] == 0
+    assert plan(BF16, 10, 10, 10, alpha=0.0)[1]["path"] == tg.GEMM_PATH_SCALE
+
+
+# ----------------------------------------------------------------------------- kernel choice
+
+def test_skinny_path_for_m_up_to_16():
+    for M in (1, 7, 16):
+        st, p = plan(F32, M, 8192, 8192)
+        assert st == OK and p["path"] == tg.GEMM_PATH_SKINNY and p["tile_m"] == 16
+    st, p = plan(F32, 17, 8192, 8192)
+    assert p["path"] == tg.GEMM_PATH_TILED
+    # bf16 has no skinny kernel: small M goes through the tiled kernel.
+    assert plan(BF16, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
+
+
+def test_skinny_decode_shape_fills_the_chip():
+    st, p = plan(F32, 16, 8192, 8192)
+    assert p["grid"] == 256 and p["vec_b"] == 2 and p["tile_n"] == 32
+
+
+def test_skinny_falls_back_when_b_offsets_would_overflow():
+    st, p = plan(F32, 16, 65536, 65536)
+    assert st == OK and p["path"] == tg.GEMM_PATH_TILED
+
+
+@pytest.mark.parametrize("M,N,K,tile,grid", [
+    (4096, 4096, 4096, 256, 256), (4092, 4092, 4092, 256, 256), (256, 256, 256, 64, 16),
+    (1000, 3000, 777, 64, 16 * 47)])
+def test_f32_tile_choice(M, N, K, tile, grid):
+    st, p = plan(F32, M, N, K)
+    assert st == OK and p["path"] == tg.GEMM_PATH_TILED
+    assert (p["tile_m"], p["grid"]) == (tile, grid)
+
+
+def test_bf16_tile_choice():
+    st, p = plan(BF16, 8192, 8192, 8192)
+    assert (p["tile_m"], p["tile_n"], p["grid"], p["vec_a"], p["vec_b"]) == (256, 256, 1024, 8, 8)
+
+
+def test_vector_width_follows_alignment():
+    # K = 777: rows of A are not 16-byte aligned -> element loads for A only.
+    st, p = plan(F32, 1000, 3000, 777)
+    assert (p["vec_a"], p["vec_b"]) == (1, 4)
+    # A base pointer off by 4 bytes.
+    assert plan(F32, 4096, 4096, 4096, A=PA + 4)[1]["vec_a"] == 1
+    # ldb not a multiple of 4.
+    assert plan(F32, 4096, 4094, 4096, ldb=4094)[1]["vec_b"] == 1
+    assert plan(BF16, 8192, 8192, 8188)[1]["vec_a"] == 1
+
+
+def test_forced_kernels():
+    f32_tiled = kernel_ids(dtype=F32, path=tg.GEMM_PATH_TILED)
+    bf16_tiled = kernel_ids(dtype=BF16, path=tg.GEMM_PATH_TILED)
+    skinny = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY)
+    assert f32_tiled and bf16_tiled and skinny
+    for kid in f32_tiled:
+        st, p = plan(F32, 512, 512, 512, force=kid)
+        assert st == OK and p["kernel_id"] == kid
+        assert plan(BF16, 512, 512, 512, force=kid)[0] == UNSUP
+    for kid in skinny:
+        assert plan(F32, 16, 512, 512, force=kid)[0] == OK
+        assert plan(F32, 17, 512, 512, force=kid)[0] == UNSUP
+    # A 4-wide-A kernel cannot take K = 777.
+    wide_a = [k for k in f32_tiled if tg.gemm_kernel_query(k)["vec_a"] == 4]
+    assert all(plan(F32, 1000, 3000, 777, force=k)[0] == UNSUP for k in wide_a)

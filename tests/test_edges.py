@@ -1,0 +1,180 @@
+"""GPU edge cases, checked against the oracle.
+
+Exact-integer mode: operands are small integers (exact in fp32 and bf16) and
+every partial sum is an integer below 2^24, so any summation order gives the
+exact answer and the GPU must equal the oracle bit for bit.  That catches
+indexing, edge and masking mistakes with zero tolerance.  Shapes straddle
+the tile sizes (16, 32, 64, 128, 256) on every side, and every kernel in the
+table is forced through them.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_gemm_f32_amd as tg
+from tiled_gemm_f32_amd.workloads import make_integer_inputs, make_random_inputs
+
+from gpu_helpers import TOL, host_view, ratio, run_gemm, say
+
+pytestmark = pytest.mark.gpu
+
+EDGE = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    allc = list(itertools.product(EDGE, EDGE, EDGE))
+    pick = rng.choice(len(allc), size=count, replace=False)
+    fixed = [(1, 1, 1), (257, 257, 257), (16, 257, 255), (129, 1, 65), (1, 300, 513), (300, 1, 2)]
+    return fixed + [allc[i] for i in pick]
+
+
+def _exact(A, B, C0, alpha, beta):
+    return oracle.gemm_ref(host_view(A), host_view(B), alpha, beta, C0.numpy())
+
+
+def _kernel_ids(dtype, path=None):
+    return [k["id"] for k in tg.kernels() if k["dtype"] == dtype and (path is None or k["path"] == path)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+def test_exact_integer_auto_choice(gpu_available, dtype):
+    for i, (M, N, K) in enumerate(_shapes(7 if dtype == "f32" else 8, 60)):
+        A, B, C0 = make_integer_inputs(M, N, K, seed=i, dtype=dtype)
+        for alpha, beta in [(2.0, -1.0), (1.0, 0.0)]:
+            say(f"[exact] {dtype} auto M={M} N={N} K={K} alpha={alpha} beta={beta} seed={i}")
+            C, _, _ = run_gemm(A, B, C0, alpha, beta)
+            np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, alpha, beta),
+                                          err_msg=f"{dtype} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+def test_exact_integer_every_kernel(gpu_available, dtype):
+    did = tg.GEMM_DTYPE_F32 if dtype == "f32" else tg.GEMM_DTYPE_BF16F32
+    shapes = _shapes(11 if dtype == "f32" else 12, 14)
+    for kid in _kernel_ids(did):
+        info = tg.gemm_kernel_query(kid)
+        for i, (M, N, K) in enumerate(shapes):
+            if info["path"] == tg.GEMM_PATH_SKINNY:
+                M = min(M, 16)
+            A, B, C0 = make_integer_inputs(M, N, K, seed=100 + i, dtype=dtype)
+            st, _ = tg.gemm_plan_query(did, M, N, K, 2.0, 0x1000, K, 0x1000, N, 0.5, 0x1000, N, kid)
+            if st != tg.GEMM_OK:
+                continue    # this kernel's vector width does not fit the shape
+            say(f"[exact] kernel={info['name']} M={M} N={N} K={K} seed={100 + i}")
+            C, _, _ = run_gemm(A, B, C0, 2.0, 0.5, kernel=kid)
+            np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, 2.0, 0.5),
+                                          err_msg=f"{info['name']} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+def test_random_values_every_kernel(gpu_available, dtype):
+    """Full-precision random operands through every kernel on ragged shapes."""
+    did = tg.GEMM_DTYPE_F32 if dtype == "f32" else tg.GEMM_DTYPE_BF16F32
+    for kid in _kernel_ids(did):
+        info = tg.gemm_kernel_query(kid)
+        M = 16 if info["path"] == tg.GEMM_PATH_SKINNY else 300
+        for (N, K) in [(520, 1030), (264, 96)]:
+            A, B, C0 = make_random_inputs(M, N, K, seed=kid, dist="normal", dtype=dtype)
+            st, _ = tg.gemm_plan_query(did, M, N, K, 1.0, 0x1000, K, 0x1000, N, -2.0, 0x1000, N, kid)
+            if st != tg.GEMM_OK:
+                continue
+            say(f"[random] kernel={info['name']} M={M} N={N} K={K} seed={kid}")
+            C, _, _ = run_gemm(A, B, C0, 1.0, -2.0, kernel=kid)
+            r = ratio(C, A, B, C0, 1.0, -2.0)
+            assert r <= TOL[dtype], (info["name"], r)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("M", [5, 16, 200])
+def test_beta_zero_never_reads_C(gpu_available, dtype, M):
+    """beta = 0 with C full of NaN: the result is finite and exact."""
+    A, B, C0 = make_integer_inputs(M, 130, 70, seed=3, dtype=dtype)
+    say(f"[nan-C] {dtype} M={M} N=130 K=70 beta=0")
+    C, _, _ = run_gemm(A, B, C0, 1.0, 0.0, c_fill=float("nan"))
+    assert np.isfinite(C).all()
+    np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, 1.0, 0.0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("M,N,K", [(16, 200, 300), (130, 70, 90), (300, 260, 264)])
+def test_padded_leading_dimensions_with_nan_padding(gpu_available, dtype, M, N, K):
+    """lda/ldb/ldc wider than the matrix; NaN in the padding must not reach C,
+    and C's padding (a guard band) must come back untouched."""
+    A, B, C0 = make_integer_inputs(M, N, K, seed=4, dtype=dtype)
+    for pad in [(3, 5, 7), (8, 8, 8), (1, 0, 2)]:
+        say(f"[padded] {dtype} M={M} N={N} K={K} pad={pad}")
+        C, Cd, cbuf = run_gemm(A, B, C0, 2.0, -1.0, pad=pad)
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, 2.0, -1.0))
+        ldc = N + pad[2]
+        full = cbuf[:M * ldc].view(M, ldc)
+        if pad[2]:
+            assert torch.isnan(full[:, N:]).all(), "guard band of C was written"
+        assert torch.isnan(cbuf[M * ldc:]).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+def test_unaligned_bases_take_element_loads(gpu_available, dtype):
+    A, B, C0 = make_integer_inputs(140, 136, 136, seed=5, dtype=dtype)
+    for off in [(1, 0, 0), (0, 1, 0), (0, 0, 1), (1, 3, 2)]:
+        say(f"[unaligned] {dtype} 140x136x136 offsets={off}")
+        C, _, _ = run_gemm(A, B, C0, 1.0, 1.0, offset=off)
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, 1.0, 1.0))
+
+
+def test_skinny_rows_1_to_16(gpu_available):
+    for M in range(1, 17):
+        A, B, C0 = make_integer_inputs(M, 1000, 999, seed=M)
+        say(f"[skinny] M={M} N=1000 K=999")
+        C, _, _ = run_gemm(A, B, C0, -1.0, 2.0)
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, -1.0, 2.0))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+def test_quick_returns(gpu_available, dtype):
+    torch_dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    C0 = torch.arange(12, dtype=torch.float32).reshape(3, 4).cuda()
+    A = torch.empty(3, 0, dtype=torch_dt, device="cuda")
+    B = torch.empty(0, 4, dtype=torch_dt, device="cuda")
+    say(f"[quick] {dtype} K=0")
+    C = tg.gemm(A, B, C0.clone(), alpha=2.0, beta=0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(C, 0.5 * C0)
+    C = tg.gemm(A, B, torch.full((3, 4), float("nan"), device="cuda"), alpha=2.0, beta=0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(C, torch.zeros(3, 4, device="cuda"))
+    A = torch.full((3, 5), float("nan"), device="cuda").to(torch_dt)
+    B = torch.full((5, 4), float("nan"), device="cuda").to(torch_dt)
+    say(f"[quick] {dtype} alpha=0 with NaN operands")
+    C = tg.gemm(A, B, C0.clone(), alpha=0.0, beta=-1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(C, -C0)
+    Cm = torch.full((0, 4), 1.0, device="cuda")
+    tg.gemm(torch.empty(0, 5, dtype=torch_dt, device="cuda"), B, Cm)
+
+
+def test_errors_surface_as_exceptions(gpu_available):
+    A = torch.ones(4, 4, device="cuda")
+    with pytest.raises(ValueError):
+        tg.gemm(A, A.t(), torch.empty(4, 4, device="cuda"))   # column-major B rejected
+    with pytest.raises(ValueError):
+        tg.gemm(A, A, beta=1.0)
+    st = tg.gemm_f32(4, 4, 4, 1.0, A.data_ptr(), 3, A.data_ptr(), 4, 0.0, A.data_ptr(), 4, 0)
+    assert st == tg.GEMM_ERR_INVALID_ARG
+
+
+def test_nonzero_mean_large_k_within_worst_case_bound(gpu_available):
+    """All-positive operands at K = 4096: no cancellation, so rounding errors
+    do not average out; the result must still satisfy the worst-case bound
+    (K + 2) * 2^-24 that any fp32 summation order obeys."""
+    g = torch.Generator().manual_seed(9)
+    K = 4096
+    A = torch.rand(64, K, generator=g)
+    B = torch.rand(K, 64, generator=g)
+    C0 = torch.rand(64, 64, generator=g)
+    say("[positive] 64x64x4096")
+    C, _, _ = run_gemm(A, B, C0, 1.0, 1.0)
+    assert ratio(C, A, B, C0, 1.0, 1.0) <= (K + 2) * 2.0 ** -24

@@ -1,5 +1,75 @@
 """libgemm for MI355X (gfx950): C = alpha*(A x B) + beta*C on row-major operands.
 
 The computation runs in hand-written HIP kernels inside ``libgemm.so``; this
-package is a thin ctypes binding over its C ABI (``include/gemm.h``).
+package is a thin binding over its C ABI (``include/gemm.h``).  ``gemm_f32``,
+``gemm_bf16f32`` and the other C entry points are re-exported with the same
+names and arguments (integer device pointers and stream handles).
+``gemm(A, B, C, alpha, beta)`` is a convenience over torch tensors that only
+reads shapes, strides and pointers and forwards them.
 """
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401  (re-exported C ABI)
+    EXPORTED, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
+    GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
+    GEMM_PATH_SKINNY, GEMM_PATH_TILED, GemmError, gemm_bf16f32, gemm_bf16f32_ex, gemm_f32,
+    gemm_f32_ex, gemm_kernel_count, gemm_kernel_query, gemm_plan_query, gemm_status_string,
+    load)
+
+__all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_status_string",
+           "gemm_kernel_count", "gemm_kernel_query", "gemm_plan_query", "GemmError", "kernels"]
+
+
+def _ld(t, what: str) -> int:
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D, got shape {tuple(t.shape)}")
+    rows, cols = t.shape
+    if t.numel() == 0:
+        return max(cols, 1)
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} must be row-major (stride(1) == 1); got strides {t.stride()}")
+    return t.stride(0) if rows > 1 else max(cols, 1)
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None):
+    """C = alpha * (A @ B) + beta * C on the current stream; returns C.
+
+    A (M x K) and B (K x N) are CUDA tensors of dtype float32 (fp32 path) or
+    bfloat16 (bf16 operands, fp32 accumulate); C is float32 (M x N),
+    allocated when None (then beta must be 0).  All three must be row-major
+    with unit stride along columns; padded leading dimensions are fine.
+    ``kernel`` forces a kernel id (0 = library choice).
+    """
+    import torch
+
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"A and B must both be float32 or both bfloat16 (got {A.dtype}, {B.dtype})")
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if C.dtype != torch.float32 or tuple(C.shape) != (M, N) or not C.is_cuda:
+        raise ValueError(f"C must be a float32 device tensor of shape {(M, N)}")
+    lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc)
+    with torch.cuda.device(A.device):
+        if A.dtype == torch.float32:
+            st = gemm_f32_ex(*args, kernel, stream)
+        else:
+            st = gemm_bf16f32_ex(*args, kernel, stream)
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm")
+    return C
+
+
+def kernels() -> list:
+    """Descriptions of every kernel in the library's table."""
+    return [gemm_kernel_query(i) for i in range(1, gemm_kernel_count() + 1)]

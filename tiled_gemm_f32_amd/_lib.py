@@ -1,0 +1,127 @@
+"""ctypes binding of libgemm's C ABI (include/gemm.h).
+
+Every function here has the name and argument order of its C counterpart and
+only converts arguments; all computation happens in libgemm.so.  Pointers are
+plain integers (device addresses), streams are integer handles (0 = default
+stream).  Loading fails loudly if the library has not been built: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_ARG = 1
+GEMM_ERR_UNSUPPORTED = 2
+GEMM_ERR_LAUNCH = 3
+GEMM_ERR_DEVICE = 4
+
+GEMM_PATH_NONE = 0
+GEMM_PATH_SCALE = 1
+GEMM_PATH_TILED = 2
+GEMM_PATH_SKINNY = 3
+
+GEMM_DTYPE_F32 = 0
+GEMM_DTYPE_BF16F32 = 1
+
+# Every entry point include/gemm.h declares.
+EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
+            "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex")
+
+
+class KernelInfo(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int32), ("dtype", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
+                ("name", ctypes.c_char_p)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("kernel_id", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("threads", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32)]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gemm_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgemm.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_gemm_f32_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
+    gemm_sig = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64]
+    lib.gemm_f32.argtypes = gemm_sig + [vp]
+    lib.gemm_bf16f32.argtypes = gemm_sig + [vp]
+    lib.gemm_f32_ex.argtypes = gemm_sig + [i32, vp]
+    lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, vp]
+    for fn in (lib.gemm_f32, lib.gemm_bf16f32, lib.gemm_f32_ex, lib.gemm_bf16f32_ex):
+        fn.restype = ctypes.c_int
+    lib.gemm_status_string.argtypes = [ctypes.c_int]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_kernel_count.argtypes = []
+    lib.gemm_kernel_count.restype = i32
+    lib.gemm_kernel_query.argtypes = [i32, ctypes.POINTER(KernelInfo)]
+    lib.gemm_kernel_query.restype = ctypes.c_int
+    lib.gemm_plan_query.argtypes = [i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32,
+                                    ctypes.POINTER(Plan)]
+    lib.gemm_plan_query.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_bf16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_bf16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream=0) -> int:
+    return load().gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream)
+
+
+def gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream=0) -> int:
+    return load().gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream)
+
+
+def gemm_status_string(status: int) -> str:
+    return load().gemm_status_string(status).decode()
+
+
+def gemm_kernel_count() -> int:
+    return int(load().gemm_kernel_count())
+
+
+def gemm_kernel_query(kid: int) -> dict:
+    info = KernelInfo()
+    st = load().gemm_kernel_query(kid, ctypes.byref(info))
+    if st != GEMM_OK:
+        raise GemmError(st, f"gemm_kernel_query({kid})")
+    d = {f: getattr(info, f) for f, _ in KernelInfo._fields_}
+    d["name"] = info.name.decode()
+    return d
+
+
+def gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0):
+    """(status, plan dict) for the choice the library would make."""
+    pl = Plan()
+    st = load().gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel,
+                                ctypes.byref(pl))
+    return st, {f: getattr(pl, f) for f, _ in Plan._fields_}

@@ -1,0 +1,294 @@
+// The C ABI of libgemm: argument validation, kernel choice and launch.
+//
+// Everything up to the launch is plain host arithmetic on the arguments, so
+// a bad call is rejected before any HIP call and the choice can be inspected
+// on a machine without a GPU (gemm_plan_query).  The choice follows the
+// pages' reasoning about tiles and waves ("A GEMM Kernel, Step by Step",
+// sections "The fringe and the last wave" and "Six parameters, found by
+// search"): the largest workgroup tile that still gives every compute unit
+// work, the widest global loads the operands' alignment permits, and a
+// separate streaming kernel for M <= 16.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "gemm.h"
+#include "gemm_kernels.hpp"
+
+namespace {
+
+using gemm::KernelDesc;
+
+constexpr int64_t kMaxDim = 0x7fffffff;   // sizes index with 32-bit integers in the kernels
+// A 256-row fp32 panel then spans at most 256 * (2^21 - 1) * 4 < 2^31 - 1 bytes,
+// so every buffer extent and in-panel offset fits the 31-bit range.
+constexpr int64_t kMaxLd = (int64_t(1) << 21) - 1;
+constexpr int kComputeUnits = 256;
+
+int table_size() {
+    return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount;
+}
+
+const KernelDesc *kernel_by_id(int32_t id) {
+    if (id < 1) return nullptr;
+    int i = id - 1;
+    if (i < gemm::kF32TiledKernelCount) return &gemm::kF32TiledKernels[i];
+    i -= gemm::kF32TiledKernelCount;
+    if (i < gemm::kBf16TiledKernelCount) return &gemm::kBf16TiledKernels[i];
+    i -= gemm::kBf16TiledKernelCount;
+    if (i < gemm::kF32SkinnyKernelCount) return &gemm::kF32SkinnyKernels[i];
+    return nullptr;
+}
+
+int32_t id_of(const KernelDesc *kd) {
+    for (int32_t id = 1; id <= table_size(); ++id)
+        if (kernel_by_id(id) == kd) return id;
+    return 0;
+}
+
+bool aligned(const void *p, uintptr_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Call {
+    int32_t dtype;
+    int64_t M, N, K;
+    float alpha, beta;
+    const void *A, *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+};
+
+gemm_status validate(const Call &c) {
+    if (c.dtype != GEMM_DTYPE_F32 && c.dtype != GEMM_DTYPE_BF16F32) return GEMM_ERR_INVALID_ARG;
+    if (c.M < 0 || c.N < 0 || c.K < 0) return GEMM_ERR_INVALID_ARG;
+    const int64_t min_lda = c.K > 1 ? c.K : 1, min_n = c.N > 1 ? c.N : 1;
+    if (c.lda < min_lda || c.ldb < min_n || c.ldc < min_n) return GEMM_ERR_INVALID_ARG;
+    const uintptr_t esz = c.dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    if (c.M > 0 && c.N > 0) {
+        if (c.C == nullptr || !aligned(c.C, 4)) return GEMM_ERR_INVALID_ARG;
+        if (c.K > 0 && c.alpha != 0.0f) {
+            if (c.A == nullptr || c.B == nullptr || !aligned(c.A, esz) || !aligned(c.B, esz))
+                return GEMM_ERR_INVALID_ARG;
+        }
+    }
+    if (c.M > kMaxDim || c.N > kMaxDim || c.K > kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    if (c.lda > kMaxLd || c.ldb > kMaxLd) return GEMM_ERR_UNSUPPORTED;
+    return GEMM_OK;
+}
+
+// Widest vector loads each operand allows: 16-byte aligned base, leading
+// dimension and extent along the contiguous axis multiples of the width (so
+// a vector is either wholly inside the valid region or wholly outside).
+int max_vec_a(const Call &c) {
+    const int w = c.dtype == GEMM_DTYPE_F32 ? 4 : 8;
+    return (aligned(c.A, 16) && c.lda % w == 0 && c.K % w == 0) ? w : 1;
+}
+bool vec_b_ok(const Call &c, int v) {
+    if (v == 1) return true;
+    const uintptr_t esz = c.dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    return aligned(c.B, esz * v) && c.ldb % v == 0 && c.N % v == 0;
+}
+
+// The skinny kernel addresses B with 32-bit offsets up to (K + 512) rows.
+bool skinny_fits(const Call &c) {
+    return c.M <= 16 && (c.K + 512) * c.ldb * 4 < (int64_t(1) << 31);
+}
+
+bool kernel_runs(const KernelDesc *kd, const Call &c) {
+    if (kd->dtype != c.dtype) return false;
+    if (kd->path == GEMM_PATH_SKINNY && !skinny_fits(c)) return false;
+    if (kd->vec_a > 1 && max_vec_a(c) < kd->vec_a) return false;
+    return vec_b_ok(c, kd->vec_b);
+}
+
+const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c, int tile_m) {
+    for (int i = 0; i < count; ++i)
+        if ((tile_m == 0 || table[i].tile_m == tile_m) && kernel_runs(&table[i], c)) return &table[i];
+    return nullptr;
+}
+
+// Tile choice: the largest square tile whose tile count covers every compute
+// unit at least once; small problems fall through to the smallest tile.
+const KernelDesc *choose(const Call &c) {
+    if (c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
+        if (const KernelDesc *kd = first_match(gemm::kF32SkinnyKernels, gemm::kF32SkinnyKernelCount, c, 0))
+            return kd;
+    }
+    const KernelDesc *table = c.dtype == GEMM_DTYPE_F32 ? gemm::kF32TiledKernels : gemm::kBf16TiledKernels;
+    const int count = c.dtype == GEMM_DTYPE_F32 ? gemm::kF32TiledKernelCount : gemm::kBf16TiledKernelCount;
+    int smallest = 1 << 30;
+    for (int i = 0; i < count; ++i) smallest = table[i].tile_m < smallest ? table[i].tile_m : smallest;
+    for (int tile : {256, 128, 64}) {
+        const int64_t tiles = ceil_div(c.M, tile) * ceil_div(c.N, tile);
+        if (tiles >= kComputeUnits || tile == smallest) {
+            if (const KernelDesc *kd = first_match(table, count, c, tile)) return kd;
+        }
+    }
+    return first_match(table, count, c, 0);
+}
+
+gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc **chosen) {
+    gemm_plan pl;
+    std::memset(&pl, 0, sizeof pl);
+    *chosen = nullptr;
+    gemm_status st = validate(c);
+    if (st != GEMM_OK) return st;
+    if (force < 0 || (force > 0 && kernel_by_id(force) == nullptr)) return GEMM_ERR_INVALID_ARG;
+    if (c.M == 0 || c.N == 0) {
+        pl.path = GEMM_PATH_NONE;
+    } else if (c.K == 0 || c.alpha == 0.0f) {
+        pl.path = GEMM_PATH_SCALE;
+        pl.threads = 256;
+        pl.grid = ceil_div(c.M * c.N, 256) < 4096 ? ceil_div(c.M * c.N, 256) : 4096;
+    } else {
+        const KernelDesc *kd = force > 0 ? kernel_by_id(force) : choose(c);
+        if (kd == nullptr || !kernel_runs(kd, c)) return GEMM_ERR_UNSUPPORTED;
+        pl.path = kd->path;
+        pl.kernel_id = id_of(kd);
+        pl.threads = kd->threads;
+        pl.tile_m = kd->tile_m;
+        pl.tile_n = kd->tile_n;
+        pl.tile_k = kd->tile_k;
+        pl.vec_a = kd->vec_a;
+        pl.vec_b = kd->vec_b;
+        pl.grid = kd->path == GEMM_PATH_SKINNY ? ceil_div(c.N, kd->tile_n)
+                                               : ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n);
+        *chosen = kd;
+    }
+    if (out) *out = pl;
+    return GEMM_OK;
+}
+
+// The current device must be a gfx950; checked once per device and cached.
+std::atomic<int8_t> g_device_ok[64];
+
+gemm_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_DEVICE;
+    if (dev < 64) {
+        const int8_t known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known != 0) return known > 0 ? GEMM_OK : GEMM_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? GEMM_OK : GEMM_ERR_DEVICE;
+}
+
+gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
+    gemm_plan pl;
+    const KernelDesc *kd = nullptr;
+    gemm_status st = plan(c, force, &pl, &kd);
+    if (st != GEMM_OK || pl.path == GEMM_PATH_NONE) return st;
+    st = check_device();
+    if (st != GEMM_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (pl.path == GEMM_PATH_SCALE) {
+        err = gemm::launch_scale_c(c.beta, c.C, (int32_t)c.M, (int32_t)c.N, c.ldc, s);
+    } else {
+        gemm::GemmParams p;
+        p.A = c.A;
+        p.B = c.B;
+        p.C = c.C;
+        p.M = (int32_t)c.M;
+        p.N = (int32_t)c.N;
+        p.K = (int32_t)c.K;
+        p.lda = (int32_t)c.lda;
+        p.ldb = (int32_t)c.ldb;
+        p.ldc = c.ldc;
+        p.alpha = c.alpha;
+        p.beta = c.beta;
+        err = kd->launch(p, s);
+    }
+    return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
+               const void *B, int64_t ldb, float beta, const float *C, int64_t ldc) {
+    Call c;
+    c.dtype = dtype;
+    c.M = M;
+    c.N = N;
+    c.K = K;
+    c.alpha = alpha;
+    c.beta = beta;
+    c.A = A;
+    c.B = B;
+    c.C = const_cast<float *>(C);
+    c.lda = lda;
+    c.ldb = ldb;
+    c.ldc = ldc;
+    return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+GEMM_API gemm_status gemm_f32(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                              const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                              gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), 0, stream);
+}
+
+GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                  int64_t lda, const uint16_t *B, int64_t ldb, float beta, float *C,
+                                  int64_t ldc, gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), 0, stream);
+}
+
+GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                                 const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                                 int32_t force_kernel, gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), force_kernel, stream);
+}
+
+GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                     int64_t lda, const uint16_t *B, int64_t ldb, float beta, float *C,
+                                     int64_t ldc, int32_t force_kernel, gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), force_kernel,
+               stream);
+}
+
+GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
+                                     const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+                                     const float *C, int64_t ldc, int32_t force_kernel, gemm_plan *out) {
+    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+    const KernelDesc *kd = nullptr;
+    return plan(make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), force_kernel, out, &kd);
+}
+
+GEMM_API int32_t gemm_kernel_count(void) { return table_size(); }
+
+GEMM_API gemm_status gemm_kernel_query(int32_t id, gemm_kernel_info *out) {
+    const KernelDesc *kd = kernel_by_id(id);
+    if (kd == nullptr || out == nullptr) return GEMM_ERR_INVALID_ARG;
+    out->id = id;
+    out->dtype = kd->dtype;
+    out->path = kd->path;
+    out->tile_m = kd->tile_m;
+    out->tile_n = kd->tile_n;
+    out->tile_k = kd->tile_k;
+    out->threads = kd->threads;
+    out->vec_a = kd->vec_a;
+    out->vec_b = kd->vec_b;
+    out->name = kd->name;
+    return GEMM_OK;
+}
+
+GEMM_API const char *gemm_status_string(gemm_status status) {
+    switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_ARG: return "invalid argument (size, leading dimension or pointer)";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported problem or kernel for these operands";
+    case GEMM_ERR_LAUNCH: return "HIP kernel launch failed";
+    case GEMM_ERR_DEVICE: return "no usable gfx950 device is current";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Device helpers shared by the libgemm kernels (gfx950 only).
+//
+// Global memory is read through raw buffer loads.  A buffer resource carries
+// a base address and a byte extent; the hardware returns zero for any access
+// at or beyond the extent instead of touching memory.  That gives the
+// zero-filled edge tiles of the blocked method ("GEMM Worklog I", section 3,
+// and the "Code" section of "Tiled matrix multiplication": out-of-range
+// operand elements load as 0) without a branch per element: rows past the
+// end of an operand fall outside the extent, and the few lanes that must be
+// masked inside it (the K tail of A) get an offset that is always outside.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family
+// parts: 32-bit data format, range checked against num_records in bytes.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+
+// Extents are kept below 2^31 bytes, so this offset is always out of range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr uint32_t kMaxExtent = 0x7fffffffu;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)bytes, (int)kBufferWord3);
+}
+
+__device__ __forceinline__ uint32_t clamp_extent(int64_t bytes) {
+    return bytes <= 0 ? 0u : (bytes > (int64_t)kMaxExtent ? kMaxExtent : (uint32_t)bytes);
+}
+
+__device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 load_b64(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t load_b16(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Map a hardware workgroup id to a (tile row, tile column) of C.
+//
+// Two orderings are composed.  (1) The dispatcher hands consecutive
+// workgroup ids to the 8 XCDs in turn, and each XCD has its own L2, so the
+// ids are first regrouped so that each XCD owns a contiguous range of
+// logical tiles.  (2) Logical tiles are then walked in column-major order
+// inside bands of `group_m` tile rows, so the tiles resident together on an
+// XCD share a few A row panels and B column panels in its L2 -- the
+// swizzled block order "Tiled matrix multiplication" recommends for L2
+// reuse ("Complexity and constants").
+__host__ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int tiles_n, int group_m,
+                                                     int &tm, int &tn) {
+    const int total = tiles_m * tiles_n;
+    const int per_xcd = total >> 3;
+    int w = wg;
+    if (wg < (per_xcd << 3)) w = (wg & 7) * per_xcd + (wg >> 3);
+    const int band = group_m * tiles_n;
+    const int g = w / band;
+    const int first = g * group_m;
+    const int rows = tiles_m - first < group_m ? tiles_m - first : group_m;
+    const int r = w - g * band;
+    tm = first + r % rows;
+    tn = r / rows;
+}
+
+}  // namespace gemm

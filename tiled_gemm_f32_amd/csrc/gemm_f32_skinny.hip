@@ -1,0 +1,171 @@
+// fp32 GEMM for skinny problems (M <= 16): the decode-GEMV case that
+// "Tiled matrix multiplication" ("Avoid when") identifies as bandwidth-bound.
+//
+// With at most 16 rows of A, every element of B is used by at most 16
+// multiply-adds, so the job is to stream B from HBM exactly once at full
+// bandwidth while the matrix cores absorb the arithmetic:
+//
+//   * Each workgroup owns a strip of 16*VEC columns of C over the whole of
+//     K, so B is read once in total.  Each lane loads VEC consecutive
+//     columns of one k row (16 lanes cover the strip's row segment), four
+//     k rows per wave instruction.
+//   * The strip's k quads are dealt round-robin to the workgroup's waves,
+//     each keeping UNROLL quads of loads in flight before consuming them, so
+//     thousands of bytes are outstanding per wave.
+//   * v_mfma_f32_16x16x4_f32 takes the 16 rows of A (lane row l%16, k row
+//     l/16) against 16 columns of B; VEC instructions cover the lane's VEC
+//     columns, column c of instruction j being strip column VEC*c + j.
+//     Rows of A at or past M read as zero.
+//   * The waves' partial 16 x (16*VEC) tiles are summed through LDS in a
+//     fixed wave order (deterministic; no atomics) and the alpha/beta
+//     epilogue is applied once per output.
+#include "gemm_device.hpp"
+#include "gemm_kernels.hpp"
+#include "gemm.h"
+
+namespace gemm {
+namespace {
+
+template <int V> struct BVec;
+template <> struct BVec<4> {
+    static __device__ __forceinline__ f32x4 load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(f32x4, load_b128(r, off));
+    }
+};
+template <> struct BVec<2> {
+    static __device__ __forceinline__ f32x2 load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(f32x2, load_b64(r, off));
+    }
+};
+template <> struct BVec<1> {
+    static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, load_b32(r, off));
+    }
+};
+
+template <int V, typename T> __device__ __forceinline__ float comp(const T &v, int j);
+template <> __device__ __forceinline__ float comp<4, f32x4>(const f32x4 &v, int j) { return v[j]; }
+template <> __device__ __forceinline__ float comp<2, f32x2>(const f32x2 &v, int j) { return v[j]; }
+template <> __device__ __forceinline__ float comp<1, float>(const float &v, int) { return v; }
+
+template <int VEC, int WAVES, int UNROLL>
+__global__ void __launch_bounds__(64 * WAVES)
+f32_skinny_kernel(GemmParams p) {
+    constexpr int NW = 16 * VEC;
+    __shared__ float red[WAVES][16][NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * NW;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int kq = lane >> 4;     // k row within a quad
+    const int lc = lane & 15;     // A row for the A operand; column group for B
+
+    // Rows of A at or past M, and rows of B at or past K, fall outside these
+    // extents and read as zero.  The host guarantees (K + 4*WAVES*UNROLL) * ldb
+    // * 4 < 2^31 on this path, so no offset below wraps.
+    const rsrc_t ra = make_rsrc(p.A, clamp_extent(((int64_t)(M - 1) * lda + K) * 4));
+    const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + n0,
+                                clamp_extent(((int64_t)(K - 1) * ldb + (N - n0)) * 4));
+    const uint32_t a_base = (uint32_t)(lc * lda + kq) * 4u;
+    const uint32_t b_base = (uint32_t)(kq * ldb + VEC * lc) * 4u;
+    const uint32_t b_quad = (uint32_t)(4 * ldb) * 4u;
+
+    f32x4 acc[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) acc[j] = f32x4{};
+
+    const int nq = (K + 3) >> 2;
+    for (int q0 = wave; q0 < nq; q0 += WAVES * UNROLL) {
+        float av[UNROLL];
+        decltype(BVec<VEC>::load(rb, 0)) bv[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int q = q0 + u * WAVES;
+            const int k = 4 * q + kq;
+            // k >= K inside a row of A is the next row or padding: force zero.
+            av[u] = __builtin_bit_cast(float, load_b32(ra, k < K ? a_base + (uint32_t)q * 16u : kOutOfRange));
+            bv[u] = BVec<VEC>::load(rb, b_base + (uint32_t)q * b_quad);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], comp<VEC>(bv[u], j), acc[j], 0, 0, 0);
+    }
+
+    // Register r of lane (kq, lc) is row 4*kq + r, column lc of its 16 x 16 block.
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][VEC * lc + j] = acc[j][r];
+    __syncthreads();
+
+    const float alpha = p.alpha, beta = p.beta;
+    for (int idx = tid; idx < 16 * NW; idx += 64 * WAVES) {
+        const int i = idx / NW, j = idx % NW;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w][i][j];
+        const int col = n0 + j;
+        if (i < M && col < N) {
+            float *cp = p.C + (int64_t)i * p.ldc + col;
+            float v = alpha * s;
+            if (beta != 0.0f) v = fmaf(beta, *cp, v);
+            *cp = v;
+        }
+    }
+}
+
+template <int VEC, int WAVES, int UNROLL>
+hipError_t launch_f32_skinny(const GemmParams &p, hipStream_t stream) {
+    const int strips = (p.N + 16 * VEC - 1) / (16 * VEC);
+    GemmParams args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_kernel<VEC, WAVES, UNROLL>),
+                           dim3((unsigned)strips), dim3(64 * WAVES), argv, 0, stream);
+}
+
+__global__ void __launch_bounds__(256)
+scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t i = idx / N, j = idx - i * N;
+        float *cp = C + i * ldc + j;
+        *cp = (beta == 0.0f) ? 0.0f : beta * *cp;
+    }
+}
+
+#define F32_SKINNY(VEC, WAVES, UNROLL)                                                         \
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 16 * VEC, 4 * WAVES * UNROLL, 64 * WAVES, 1, VEC,   \
+     "f32_skinny_mfma16_n" #VEC "_w" #WAVES "_u" #UNROLL, &launch_f32_skinny<VEC, WAVES, UNROLL>}
+
+// Explicit instantiations: the device pass never sees the host-only table.
+template __global__ void f32_skinny_kernel<4, 16, 8>(GemmParams);
+template __global__ void f32_skinny_kernel<2, 16, 8>(GemmParams);
+template __global__ void f32_skinny_kernel<1, 16, 8>(GemmParams);
+
+}  // namespace
+
+#if !defined(__HIP_DEVICE_COMPILE__)
+// The dispatcher takes the first entry the operands allow.  2-wide loads come
+// first: their 32-column strips give one workgroup per compute unit at
+// N = 8192, where 4-wide strips would leave half the chip idle.
+const KernelDesc kF32SkinnyKernels[] = {
+    F32_SKINNY(2, 16, 8),
+    F32_SKINNY(4, 16, 8),
+    F32_SKINNY(1, 16, 8),
+};
+const int kF32SkinnyKernelCount = sizeof(kF32SkinnyKernels) / sizeof(kF32SkinnyKernels[0]);
+
+hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, hipStream_t stream) {
+    const int64_t total = (int64_t)M * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    void *argv[] = {&beta, &C, &M, &N, &ldc};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&scale_c_kernel), dim3((unsigned)blocks),
+                           dim3(256), argv, 0, stream);
+}
+#endif
+
+}  // namespace gemm

@@ -1,0 +1,50 @@
+// Internal interface between the C ABI (gemm_api.cpp) and the kernel files.
+// Not installed; callers use include/gemm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemm {
+
+// Arguments of one GEMM launch, already validated by the host code:
+// 0 < M, N, K < 2^31, lda and ldb below 2^21 elements (so every in-panel
+// byte offset of a 256-row panel fits the 31-bit buffer extent), pointers
+// aligned to their element size.  A and B are fp32 or bf16 according to
+// the kernel; C is always fp32.
+struct GemmParams {
+    const void *A;
+    const void *B;
+    float *C;
+    int32_t M, N, K;
+    int32_t lda, ldb;
+    int64_t ldc;
+    float alpha, beta;
+};
+
+typedef hipError_t (*LaunchFn)(const GemmParams &p, hipStream_t stream);
+
+// One row of the kernel table.
+struct KernelDesc {
+    int32_t dtype;     // gemm_dtype
+    int32_t path;      // gemm_path
+    int32_t tile_m, tile_n, tile_k;
+    int32_t threads;
+    int32_t vec_a, vec_b;
+    const char *name;
+    LaunchFn launch;
+};
+
+// Tables exported by the kernel files (constant-initialised).
+extern const KernelDesc kF32TiledKernels[];
+extern const int kF32TiledKernelCount;
+extern const KernelDesc kBf16TiledKernels[];
+extern const int kBf16TiledKernelCount;
+extern const KernelDesc kF32SkinnyKernels[];
+extern const int kF32SkinnyKernelCount;
+
+// C = beta * C over an M x N view (beta == 0 writes zeros without reading).
+hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc,
+                          hipStream_t stream);
+
+}  // namespace gemm
