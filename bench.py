@@ -19,7 +19,7 @@ The skinny call cycles through three copies of B (3 x 268 MB) so every call
 streams B from HBM rather than from the 256 MB last-level cache.
 
 ``cpu_baseline`` times the CPU oracle (fp64, OpenMP) on a bounded sample of
-the same step: all 4096 rows of the fp32 problem, the first 1024 rows of the
+the same step: all 4096 rows of the fp32 problem, the first 4096 rows of the
 bf16 problem and the whole skinny problem.
 """
 from __future__ import annotations
@@ -39,7 +39,7 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16f32": 2500.0}
 PEAK_HBM_GBS = 8000.0
 STEP = ["f32_4096", "bf16f32_8192", "f32_16x8192x8192"]
 SKINNY_COPIES = 3
-CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 1024, "f32_16x8192x8192": 16}
+CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
 
 def parse():
@@ -49,9 +49,37 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=STEP, default=None, help="time a single workload of the step")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file of measured HBM bytes per launch of the dominant kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (a plain kernel of known traffic) so hardware "
+                         "byte counters can be scaled against it")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_tiled.hip",
+                  "f32_skinny": "gemm_f32_skinny.hip"}
+
+
+def kernel_source_sha(kernel_name: str):
+    """sha256 of the source file a kernel is built from (to spot stale counter data)."""
+    import hashlib
+    for prefix, src in KERNEL_SOURCES.items():
+        if kernel_name.startswith(prefix):
+            with open(os.path.join(ROOT, "tiled_gemm_f32_amd", "csrc", src), "rb") as f:
+                return hashlib.sha256(f.read()).hexdigest()
+    return None
+
+
+def measured_traffic(kernel_name: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's source changed after the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f).get("kernels", {}).get(kernel_name)
+    if not rec or rec.get("source_sha256") != kernel_source_sha(kernel_name):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def main():
@@ -102,6 +130,14 @@ def main():
             e1.record(stream)
             c["durs"].append((e0, e1))
 
+    if args.copy_calibration:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         for c in calls:
             launch(c, False)
@@ -140,15 +176,11 @@ def main():
         else:
             achieved, peak, unit = p["tflops"], PEAK_TFLOPS[w.dtype], "TFLOP/s"
         return {"kernel": p["kernel"], "workload": name, "bound": p["bound"], "achieved": achieved, "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None}
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(p["kernel"]),
+                "algorithmic_bytes": w.algorithmic_bytes}
 
     dominant = max(parts, key=lambda n: parts[n]["ms"])
     roof = roofline_of(dominant)
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        if tr.get("kernel") == roof["kernel"]:
-            roof["traffic"] = tr.get("bytes_per_launch")
 
     cpu = None
     if not args.no_cpu_baseline and not args.only:

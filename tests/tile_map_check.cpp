@@ -43,6 +43,22 @@ int main() {
         ++cases;
         if (!ok) { std::printf("FAIL big %dx%d\n", b[0], b[1]); ++failures; }
     }
+    // Square-round mapping (falls back to tile_coords off multiples of 16).
+    for (int tm = 1; tm <= 72; tm += (tm < 40 ? 1 : 8)) {
+        for (int tn = 1; tn <= 72; tn += (tn < 40 ? 1 : 8)) {
+            std::vector<int> seen(tm * tn, 0);
+            bool ok = true;
+            for (int w = 0; w < tm * tn; ++w) {
+                int r, c;
+                gemm::tile_coords_square(w, tm, tn, 4, r, c);
+                if (r < 0 || r >= tm || c < 0 || c >= tn) { ok = false; break; }
+                seen[r * tn + c]++;
+            }
+            for (int v : seen) ok = ok && v == 1;
+            ++cases;
+            if (!ok) { std::printf("FAIL square %dx%d\n", tm, tn); ++failures; }
+        }
+    }
     std::printf("%s %d cases\n", failures ? "FAILED" : "OK", cases);
     return failures ? 1 : 0;
 }

@@ -91,9 +91,10 @@ bool vec_b_ok(const Call &c, int v) {
     return aligned(c.B, esz * v) && c.ldb % v == 0 && c.N % v == 0;
 }
 
-// The skinny kernel addresses B with 32-bit offsets up to (K + 512) rows.
+// The skinny kernels address B with 32-bit offsets; their prefetch runs at
+// most 48 * WAVES * UNROLL (<= 1536) rows past K, so K + 2048 rows must fit.
 bool skinny_fits(const Call &c) {
-    return c.M <= 16 && (c.K + 512) * c.ldb * 4 < (int64_t(1) << 31);
+    return c.M <= 16 && (c.K + 2048) * c.ldb * 4 < (int64_t(1) << 31);
 }
 
 bool kernel_runs(const KernelDesc *kd, const Call &c) {
@@ -105,7 +106,8 @@ bool kernel_runs(const KernelDesc *kd, const Call &c) {
 
 const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c, int tile_m) {
     for (int i = 0; i < count; ++i)
-        if ((tile_m == 0 || table[i].tile_m == tile_m) && kernel_runs(&table[i], c)) return &table[i];
+        if ((tile_m == 0 || table[i].tile_m == tile_m) && c.K >= table[i].min_k && kernel_runs(&table[i], c))
+            return &table[i];
     return nullptr;
 }
 

@@ -79,4 +79,29 @@ __host__ __device__ __forceinline__ void tile_coords(int wg, int tiles_m, int ti
     tn = r / rows;
 }
 
+// Map a workgroup id to a tile for grids whose tile counts are multiples of
+// 16 (otherwise fall back to tile_coords).  The 256 workgroups resident at
+// once (one per compute unit) are given one 16 x 16-tile square of C, so the
+// operand panels live in the shared last-level cache at any moment are those
+// of 16 tile rows and 16 tile columns rather than of a whole dimension;
+// squares are visited in a snake so consecutive rounds share half their
+// panels.  Inside a square, hardware id w runs on XCD w % 8, which takes a
+// 4 x 8 block of tiles so its 32 compute units share 4 A panels and 8 B
+// panels in that XCD's L2.
+__host__ __device__ __forceinline__ void tile_coords_square(int wg, int tiles_m, int tiles_n, int group_m,
+                                                            int &tm, int &tn) {
+    if ((tiles_m & 15) || (tiles_n & 15)) {
+        tile_coords(wg, tiles_m, tiles_n, group_m, tm, tn);
+        return;
+    }
+    const int round = wg >> 8, slot = wg & 255;
+    const int squares_n = tiles_n >> 4;
+    const int sq_r = round / squares_n;
+    int sq_c = round - sq_r * squares_n;
+    if (sq_r & 1) sq_c = squares_n - 1 - sq_c;
+    const int xcd = slot & 7, j = slot >> 3;
+    tm = 16 * sq_r + 4 * (xcd & 3) + (j & 3);
+    tn = 16 * sq_c + 8 * (xcd >> 2) + (j >> 2);
+}
+
 }  // namespace gemm

@@ -28,16 +28,19 @@ namespace {
 
 template <int V> struct BVec;
 template <> struct BVec<4> {
+    typedef f32x4 T;
     static __device__ __forceinline__ f32x4 load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(f32x4, load_b128(r, off));
     }
 };
 template <> struct BVec<2> {
+    typedef f32x2 T;
     static __device__ __forceinline__ f32x2 load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(f32x2, load_b64(r, off));
     }
 };
 template <> struct BVec<1> {
+    typedef float T;
     static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(float, load_b32(r, off));
     }
@@ -48,56 +51,93 @@ template <> __device__ __forceinline__ float comp<4, f32x4>(const f32x4 &v, int 
 template <> __device__ __forceinline__ float comp<2, f32x2>(const f32x2 &v, int j) { return v[j]; }
 template <> __device__ __forceinline__ float comp<1, float>(const float &v, int) { return v; }
 
-template <int VEC, int WAVES, int UNROLL>
+template <int VA> struct AVec;
+template <> struct AVec<4> {
+    // 16-byte load of k = 4*kq .. 4*kq+3 of the lane's row (whole vector in or out of range).
+    static __device__ __forceinline__ f32x4 load(rsrc_t r, uint32_t off, int k, int K) {
+        return __builtin_bit_cast(f32x4, load_b128(r, k < K ? off : kOutOfRange));
+    }
+};
+template <> struct AVec<1> {
+    static __device__ __forceinline__ f32x4 load(rsrc_t r, uint32_t off, int k, int K) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(float, load_b32(r, k + j < K ? off + 4u * j : kOutOfRange));
+        return v;
+    }
+};
+
+// One workgroup per 16*VEC-column strip of C.  K is cut into 16-deep blocks,
+// dealt round-robin to the waves.  Inside a block, lane group kq = lane/16
+// owns k = 4*kq .. 4*kq+3 (one 16-byte load of its A row), and MFMA j of the
+// block pairs k = 4*kq + j with B row 4*kq + j.  Blocks are processed in
+// batches of UNROLL; the loads of batch t+1 are issued before batch t is
+// consumed, so each wave always has a batch of loads in flight.
+template <int VEC, int VA, int WAVES, int UNROLL>
 __global__ void __launch_bounds__(64 * WAVES)
 f32_skinny_kernel(GemmParams p) {
     constexpr int NW = 16 * VEC;
+    typedef typename BVec<VEC>::T BT;
     __shared__ float red[WAVES][16][NW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * NW;
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
-    const int kq = lane >> 4;     // k row within a quad
+    const int kq = lane >> 4;     // k group within a 16-deep block
     const int lc = lane & 15;     // A row for the A operand; column group for B
 
     // Rows of A at or past M, and rows of B at or past K, fall outside these
-    // extents and read as zero.  The host guarantees (K + 4*WAVES*UNROLL) * ldb
-    // * 4 < 2^31 on this path, so no offset below wraps.
+    // extents and read as zero.  The prefetch reaches at most 48*WAVES*UNROLL
+    // rows past K and the host guarantees (K + 2048) * ldb * 4 < 2^31 on this
+    // path, so no offset below wraps.
     const rsrc_t ra = make_rsrc(p.A, clamp_extent(((int64_t)(M - 1) * lda + K) * 4));
     const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + n0,
                                 clamp_extent(((int64_t)(K - 1) * ldb + (N - n0)) * 4));
-    const uint32_t a_base = (uint32_t)(lc * lda + kq) * 4u;
-    const uint32_t b_base = (uint32_t)(kq * ldb + VEC * lc) * 4u;
-    const uint32_t b_quad = (uint32_t)(4 * ldb) * 4u;
+    const uint32_t a_base = (uint32_t)(lc * lda + 4 * kq) * 4u;
+    const uint32_t b_base = (uint32_t)(4 * kq * ldb + VEC * lc) * 4u;
+    const uint32_t b_row = (uint32_t)ldb * 4u;
 
     f32x4 acc[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) acc[j] = f32x4{};
 
-    const int nq = (K + 3) >> 2;
-    for (int q0 = wave; q0 < nq; q0 += WAVES * UNROLL) {
-        float av[UNROLL];
-        decltype(BVec<VEC>::load(rb, 0)) bv[UNROLL];
+    f32x4 av[2][UNROLL];
+    BT bv[2][UNROLL][4];
+    auto issue = [&](int set, int blk0) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const int q = q0 + u * WAVES;
-            const int k = 4 * q + kq;
-            // k >= K inside a row of A is the next row or padding: force zero.
-            av[u] = __builtin_bit_cast(float, load_b32(ra, k < K ? a_base + (uint32_t)q * 16u : kOutOfRange));
-            bv[u] = BVec<VEC>::load(rb, b_base + (uint32_t)q * b_quad);
+            const int b = blk0 + u * WAVES;
+            av[set][u] = AVec<VA>::load(ra, a_base + (uint32_t)b * 64u, 16 * b + 4 * kq, K);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[set][u][j] = BVec<VEC>::load(rb, b_base + (uint32_t)(16 * b + j) * b_row);
         }
+    };
+    auto consume = [&](int set) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-            for (int j = 0; j < VEC; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], comp<VEC>(bv[u], j), acc[j], 0, 0, 0);
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[set][u][j], comp<VEC>(bv[set][u][j], c), acc[c], 0, 0, 0);
+    };
+
+    const int nb = (K + 15) >> 4;
+    constexpr int kStride = WAVES * UNROLL;
+    issue(0, wave);
+    for (int blk0 = wave; blk0 < nb; blk0 += 2 * kStride) {
+        issue(1, blk0 + kStride);        // past the end: reads zeros
+        consume(0);
+        issue(0, blk0 + 2 * kStride);
+        consume(1);
     }
 
     // Register r of lane (kq, lc) is row 4*kq + r, column lc of its 16 x 16 block.
 #pragma unroll
-    for (int j = 0; j < VEC; ++j)
+    for (int c = 0; c < VEC; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][VEC * lc + j] = acc[j][r];
+        for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][VEC * lc + c] = acc[c][r];
     __syncthreads();
 
     const float alpha = p.alpha, beta = p.beta;
@@ -116,12 +156,12 @@ f32_skinny_kernel(GemmParams p) {
     }
 }
 
-template <int VEC, int WAVES, int UNROLL>
+template <int VEC, int VA, int WAVES, int UNROLL>
 hipError_t launch_f32_skinny(const GemmParams &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VEC - 1) / (16 * VEC);
     GemmParams args = p;
     void *argv[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_kernel<VEC, WAVES, UNROLL>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_kernel<VEC, VA, WAVES, UNROLL>),
                            dim3((unsigned)strips), dim3(64 * WAVES), argv, 0, stream);
 }
 
@@ -136,26 +176,28 @@ scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc) {
     }
 }
 
-#define F32_SKINNY(VEC, WAVES, UNROLL)                                                         \
-    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 16 * VEC, 4 * WAVES * UNROLL, 64 * WAVES, 1, VEC,   \
-     "f32_skinny_mfma16_n" #VEC "_w" #WAVES "_u" #UNROLL, &launch_f32_skinny<VEC, WAVES, UNROLL>}
+#define F32_SKINNY(VEC, VA, WAVES, UNROLL)                                                     \
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 16 * VEC, 16 * WAVES * UNROLL, 64 * WAVES, VA, VEC,  \
+     "f32_skinny_mfma16_n" #VEC "_a" #VA "_w" #WAVES "_u" #UNROLL,                              \
+     &launch_f32_skinny<VEC, VA, WAVES, UNROLL>}
+#define SKINNY_LIST(X)                                                                          \
+    X(2, 4, 8, 4) X(2, 4, 16, 2) X(4, 4, 16, 2) X(4, 4, 8, 4) X(1, 4, 16, 4)                      \
+    X(2, 1, 8, 4) X(4, 1, 16, 2) X(1, 1, 16, 2)
 
 // Explicit instantiations: the device pass never sees the host-only table.
-template __global__ void f32_skinny_kernel<4, 16, 8>(GemmParams);
-template __global__ void f32_skinny_kernel<2, 16, 8>(GemmParams);
-template __global__ void f32_skinny_kernel<1, 16, 8>(GemmParams);
+#define SKINNY_INSTANTIATE(VEC, VA, WAVES, UNROLL) \
+    template __global__ void f32_skinny_kernel<VEC, VA, WAVES, UNROLL>(GemmParams);
+SKINNY_LIST(SKINNY_INSTANTIATE)
 
 }  // namespace
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 // The dispatcher takes the first entry the operands allow.  2-wide loads come
 // first: their 32-column strips give one workgroup per compute unit at
-// N = 8192, where 4-wide strips would leave half the chip idle.
-const KernelDesc kF32SkinnyKernels[] = {
-    F32_SKINNY(2, 16, 8),
-    F32_SKINNY(4, 16, 8),
-    F32_SKINNY(1, 16, 8),
-};
+// N = 8192, where 4-wide strips would leave half the chip idle; 8 waves with
+// 4 blocks per batch measured fastest on the 16 x 8192 x 8192 shape.
+#define SKINNY_ENTRY(VEC, VA, WAVES, UNROLL) F32_SKINNY(VEC, VA, WAVES, UNROLL),
+const KernelDesc kF32SkinnyKernels[] = {SKINNY_LIST(SKINNY_ENTRY)};
 const int kF32SkinnyKernelCount = sizeof(kF32SkinnyKernels) / sizeof(kF32SkinnyKernels[0]);
 
 hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, hipStream_t stream) {

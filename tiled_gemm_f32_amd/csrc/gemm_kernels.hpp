@@ -33,6 +33,7 @@ struct KernelDesc {
     int32_t vec_a, vec_b;
     const char *name;
     LaunchFn launch;
+    int32_t min_k;     // the automatic choice skips this kernel below this K (0: no limit)
 };
 
 // Tables exported by the kernel files (constant-initialised).
