@@ -16,7 +16,9 @@ share of the step against its own roof (fp32 or bf16 matrix peak, or HBM
 bandwidth for the skinny path) and ``parts`` reports all three.
 
 The skinny call cycles through three copies of B (3 x 268 MB) so every call
-streams B from HBM rather than from the 256 MB last-level cache.
+streams B from HBM rather than from the 256 MB last-level cache, and passes a
+preallocated workspace so the library takes its split-K path (partial sums,
+then a reduce kernel; the event pair brackets both).
 
 ``cpu_baseline`` times the CPU oracle (fp64, OpenMP) on a bounded sample of
 the same step: all 4096 rows of the fp32 problem, the first 4096 rows of the
@@ -109,7 +111,8 @@ def main():
         Ad, C = A.to(dev), C0.to(dev)
         copies = SKINNY_COPIES if w.M <= 16 else 1
         Bs = [B.to(dev) for _ in range(copies)]
-        calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "i": 0, "durs": []})
+        ws = tg.workspace(w.M, w.N, w.K, device=dev) if w.dtype == "f32" else None
+        calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []})
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -122,8 +125,12 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        st = fn(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
-                c["C"].data_ptr(), w.N, sh)
+        if c["ws"] is not None:
+            st = tg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                                c["C"].data_ptr(), w.N, c["ws"].data_ptr(), c["ws"].numel(), sh)
+        else:
+            st = fn(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                    c["C"].data_ptr(), w.N, sh)
         if st != tg.GEMM_OK:
             raise tg.GemmError(st, w.name)
         if record:
@@ -158,7 +165,8 @@ def main():
         tflops = w.flops / (ms * 1e-3) / 1e12
         gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
         plan = tg.gemm_plan_query(0 if w.dtype == "f32" else 1, w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K,
-                                  c["B"][0].data_ptr(), w.N, w.beta, c["C"].data_ptr(), w.N)[1]
+                                  c["B"][0].data_ptr(), w.N, w.beta, c["C"].data_ptr(), w.N, 0,
+                                  c["ws"].numel() if c["ws"] is not None else 0)[1]
         kname = tg.gemm_kernel_query(plan["kernel_id"])["name"]
         bound = "hbm" if w.M <= 16 else "mfma"
         parts[w.name] = {

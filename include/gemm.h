@@ -15,10 +15,11 @@
  * ldb >= max(1, N), ldc >= max(1, N).  Padding between rows is never read
  * in a way that can reach C (it may hold anything, NaN included).
  *
- * Memory.  A, B and C are DEVICE pointers on the current HIP device.  The
- * caller owns them; the library allocates nothing on these calls and keeps
- * no state between them ("Tiled matrix multiplication", section "How it
- * works": no state between calls).  C must not overlap A or B.
+ * Memory.  A, B and C (and a workspace, where one is passed) are DEVICE
+ * pointers on the current HIP device.  The caller owns them; the library
+ * allocates nothing and keeps no state between calls ("Tiled matrix
+ * multiplication", section "How it works": no state between calls).  C must
+ * not overlap A or B.
  *
  * Streams.  Work is enqueued on `stream` (a hipStream_t passed as void*;
  * NULL means the default stream) and the call returns without waiting.  The
@@ -86,6 +87,27 @@ GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha,
                          float beta, float *C, int64_t ldc,
                          gemm_stream_t stream);
 
+/*
+ * Workspace.  For M <= 16 fp32 problems the library can split K across
+ * workgroups and reduce the partial results in a caller-provided device
+ * workspace (the split-K variant of "A GEMM Kernel, Step by Step", section
+ * "What is left").  gemm_workspace_size() returns the bytes that path needs
+ * for this shape (0 when the shape never uses one): `splits` partial M x N
+ * fp32 results, reduced in a fixed order by a second kernel on the same
+ * stream (results are deterministic).  The workspace needs no
+ * initialisation and its contents after a call are unspecified.  Calls
+ * sharing a workspace must be ordered (same stream, or synchronised
+ * streams); overlapping calls on one workspace race.
+ * gemm_f32_ws() is gemm_f32() with a workspace; a NULL or too-small
+ * workspace simply selects the workspace-free kernels.
+ */
+GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K);
+
+GEMM_API gemm_status gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                                 const float *A, int64_t lda, const float *B, int64_t ldb,
+                                 float beta, float *C, int64_t ldc,
+                                 void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
+
 /* Static English text for a status code (never NULL). */
 GEMM_API const char *gemm_status_string(gemm_status status);
 
@@ -101,7 +123,9 @@ typedef enum gemm_path {
     GEMM_PATH_NONE = 0,     /* quick return: nothing launched (M == 0 or N == 0) */
     GEMM_PATH_SCALE = 1,    /* C = beta * C only (K == 0 or alpha == 0) */
     GEMM_PATH_TILED = 2,    /* LDS-tiled MFMA kernel */
-    GEMM_PATH_SKINNY = 3    /* M <= 16 streaming kernel */
+    GEMM_PATH_SKINNY = 3,   /* M <= 16 streaming kernel */
+    GEMM_PATH_SKINNY_SPLITK = 4  /* M <= 16 streaming kernel with K split over workgroups
+                                    (needs the caller's workspace) */
 } gemm_path;
 
 typedef enum gemm_dtype {
@@ -112,7 +136,7 @@ typedef enum gemm_dtype {
 typedef struct gemm_kernel_info {
     int32_t id;             /* 1-based; 0 is never a kernel */
     int32_t dtype;          /* gemm_dtype */
-    int32_t path;           /* gemm_path (TILED or SKINNY) */
+    int32_t path;           /* gemm_path (TILED, SKINNY or SKINNY_SPLITK) */
     int32_t tile_m, tile_n, tile_k;  /* workgroup tile (skinny: rows covered, columns, k unroll) */
     int32_t threads;        /* threads per workgroup */
     int32_t vec_a, vec_b;   /* elements per global load of A and of B (1 = element loads) */
@@ -140,19 +164,22 @@ GEMM_API gemm_status gemm_kernel_query(int32_t id, gemm_kernel_info *out);
  * inspected (NULL-ness and alignment), never dereferenced.  force_kernel = 0
  * lets the library choose; a positive id asks for that kernel and fails with
  * GEMM_ERR_UNSUPPORTED if it cannot run these operands (wrong dtype, or a
- * vector width the alignment does not allow).  Returns the same status the
- * call itself would return before launching.
+ * vector width the alignment does not allow, or a workspace kernel without
+ * enough workspace).  workspace_bytes is the size a call would pass (0 for
+ * none).  Returns the same status the call itself would return before
+ * launching.
  */
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
                             const void *A, int64_t lda, const void *B, int64_t ldb,
                             float beta, const float *C, int64_t ldc,
-                            int32_t force_kernel, gemm_plan *out);
+                            int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out);
 
-/* gemm_f32 / gemm_bf16f32 with a forced kernel (force_kernel as above). */
+/* gemm_f32_ws / gemm_bf16f32 with a forced kernel (force_kernel as above). */
 GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
                         const float *A, int64_t lda, const float *B, int64_t ldb,
                         float beta, float *C, int64_t ldc,
-                        int32_t force_kernel, gemm_stream_t stream);
+                        int32_t force_kernel, void *workspace, int64_t workspace_bytes,
+                        gemm_stream_t stream);
 
 GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
                             const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,

@@ -41,15 +41,25 @@ def padded_device(t: torch.Tensor, pad: int = 0, offset: int = 0, fill=float("na
     return view, buf
 
 
-def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c_fill=None):
-    """Run the library on host inputs; returns (C as float32 numpy, C device view, C buffer)."""
+def needs_workspace(kernel: int) -> bool:
+    return kernel > 0 and tg.gemm_kernel_query(kernel)["path"] == tg.GEMM_PATH_SKINNY_SPLITK
+
+
+def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c_fill=None, ws=None):
+    """Run the library on host inputs; returns (C as float32 numpy, C device view, C buffer).
+
+    A zero-filled workspace is allocated when a workspace kernel is forced
+    and none is given."""
     Ad, _a = padded_device(A, pad[0], offset[0])
     Bd, _b = padded_device(B, pad[1], offset[1])
     if c_fill is None:
         Cd, cbuf = padded_device(C0, pad[2], offset[2])
     else:
         Cd, cbuf = padded_device(torch.full_like(C0, c_fill), pad[2], offset[2])
-    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel)
+    if ws is None and needs_workspace(kernel):
+        M, K = A.shape
+        ws = tg.workspace(M, B.shape[1], K)
+    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel, ws=ws)
     torch.cuda.synchronize()
     return Cd.cpu().numpy(), Cd, cbuf
 

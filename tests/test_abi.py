@@ -26,11 +26,11 @@ def declared_functions():
     return re.findall(r"GEMM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
 
 
-def plan(dtype, M, N, K, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, beta=0.0, C=PC, ldc=None, force=0):
+def plan(dtype, M, N, K, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, beta=0.0, C=PC, ldc=None, force=0, ws=0):
     lda = max(K, 1) if lda is None else lda
     ldb = max(N, 1) if ldb is None else ldb
     ldc = max(N, 1) if ldc is None else ldc
-    return tg.gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force)
+    return tg.gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force, ws)
 
 
 def kernel_ids(**match):
@@ -67,7 +67,7 @@ def test_kernel_table_is_consistent():
     assert len({k["name"] for k in ks}) == len(ks)
     for k in ks:
         assert k["dtype"] in (F32, BF16)
-        assert k["path"] in (tg.GEMM_PATH_TILED, tg.GEMM_PATH_SKINNY)
+        assert k["path"] in (tg.GEMM_PATH_TILED, tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK)
         assert k["threads"] % 64 == 0 and 64 <= k["threads"] <= 1024
         if k["path"] == tg.GEMM_PATH_TILED:
             assert k["tile_m"] % 32 == 0 and k["tile_n"] % 32 == 0
@@ -121,7 +121,9 @@ def test_argument_errors_return_before_any_device_call():
     lib = _lib.load()
     assert tg.gemm_f32(-1, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, 0) == INVALID
     assert tg.gemm_bf16f32(4, 4, 8, 1.0, PA, 7, PB, 4, 0.0, PC, 4, 0) == INVALID
-    assert tg.gemm_f32_ex(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, -5, 0) == INVALID
+    assert tg.gemm_f32_ex(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, -5, 0, 0, 0) == INVALID
+    assert tg.gemm_f32_ws(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, PC + 2, 64, 0) == INVALID   # misaligned ws
+    assert tg.gemm_f32_ws(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, PC, -1, 0) == INVALID
     assert lib is not None
 
 
@@ -197,3 +199,35 @@ def test_forced_kernels():
     # A 4-wide-A kernel cannot take K = 777.
     wide_a = [k for k in f32_tiled if tg.gemm_kernel_query(k)["vec_a"] == 4]
     assert all(plan(F32, 1000, 3000, 777, force=k)[0] == UNSUP for k in wide_a)
+    # Workspace kernels need a workspace of the advertised size.
+    split = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY_SPLITK)
+    assert split
+    need = tg.gemm_workspace_size(F32, 16, 512, 4096)
+    for kid in split:
+        assert plan(F32, 16, 512, 4096, force=kid, ws=need)[0] == OK
+        assert plan(F32, 16, 512, 4096, force=kid, ws=need - 4)[0] == UNSUP
+        assert plan(F32, 16, 512, 4096, force=kid)[0] == UNSUP
+
+
+# ----------------------------------------------------------------------------- workspace path
+
+def test_workspace_size():
+    # 16 x 8192 x 8192: 64 strips of 128 columns, K split in 4 -> 4 partial 16 x 8192 results.
+    assert tg.gemm_workspace_size(F32, 16, 8192, 8192) == 4 * 16 * 8192 * 4
+    assert tg.gemm_workspace_size(F32, 17, 8192, 8192) == 0
+    assert tg.gemm_workspace_size(BF16, 16, 8192, 8192) == 0
+    assert tg.gemm_workspace_size(F32, 16, 8192, 0) == 0
+    # K is not cut into slices shallower than 512: K = 1024 gives 2 slices, K = 1023 one (no workspace).
+    assert tg.gemm_workspace_size(F32, 1, 256, 1024) == 2 * 1 * 256 * 4
+    assert tg.gemm_workspace_size(F32, 1, 256, 1023) == 0
+    # Partials hold M rows: 7 x 1000 with 8 strips and K = 4100 -> 8 slices.
+    assert tg.gemm_workspace_size(F32, 7, 1000, 4100) == 8 * 7 * 1000 * 4
+
+
+def test_workspace_selects_split_k_for_decode_shape():
+    need = tg.gemm_workspace_size(F32, 16, 8192, 8192)
+    st, p = plan(F32, 16, 8192, 8192, ws=need)
+    assert st == OK and p["path"] == tg.GEMM_PATH_SKINNY_SPLITK and p["grid"] == 256 and p["tile_n"] == 128
+    assert plan(F32, 16, 8192, 8192, ws=need - 1)[1]["path"] == tg.GEMM_PATH_SKINNY
+    assert plan(F32, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_SKINNY
+    assert plan(F32, 17, 8192, 8192, ws=need)[1]["path"] == tg.GEMM_PATH_TILED

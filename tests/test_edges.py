@@ -17,7 +17,7 @@ import oracle
 import tiled_gemm_f32_amd as tg
 from tiled_gemm_f32_amd.workloads import make_integer_inputs, make_random_inputs
 
-from gpu_helpers import TOL, host_view, ratio, run_gemm, say
+from gpu_helpers import TOL, host_view, needs_workspace, ratio, run_gemm, say
 
 pytestmark = pytest.mark.gpu
 
@@ -58,10 +58,11 @@ def test_exact_integer_every_kernel(gpu_available, dtype):
     for kid in _kernel_ids(did):
         info = tg.gemm_kernel_query(kid)
         for i, (M, N, K) in enumerate(shapes):
-            if info["path"] == tg.GEMM_PATH_SKINNY:
+            if info["path"] in (tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK):
                 M = min(M, 16)
             A, B, C0 = make_integer_inputs(M, N, K, seed=100 + i, dtype=dtype)
-            st, _ = tg.gemm_plan_query(did, M, N, K, 2.0, 0x1000, K, 0x1000, N, 0.5, 0x1000, N, kid)
+            wsb = tg.gemm_workspace_size(did, M, N, K) if needs_workspace(kid) else 0
+            st, _ = tg.gemm_plan_query(did, M, N, K, 2.0, 0x1000, K, 0x1000, N, 0.5, 0x1000, N, kid, wsb)
             if st != tg.GEMM_OK:
                 continue    # this kernel's vector width does not fit the shape
             say(f"[exact] kernel={info['name']} M={M} N={N} K={K} seed={100 + i}")
@@ -76,10 +77,11 @@ def test_random_values_every_kernel(gpu_available, dtype):
     did = tg.GEMM_DTYPE_F32 if dtype == "f32" else tg.GEMM_DTYPE_BF16F32
     for kid in _kernel_ids(did):
         info = tg.gemm_kernel_query(kid)
-        M = 16 if info["path"] == tg.GEMM_PATH_SKINNY else 300
+        M = 16 if info["path"] in (tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK) else 300
         for (N, K) in [(520, 1030), (264, 96)]:
             A, B, C0 = make_random_inputs(M, N, K, seed=kid, dist="normal", dtype=dtype)
-            st, _ = tg.gemm_plan_query(did, M, N, K, 1.0, 0x1000, K, 0x1000, N, -2.0, 0x1000, N, kid)
+            wsb = tg.gemm_workspace_size(did, M, N, K) if needs_workspace(kid) else 0
+            st, _ = tg.gemm_plan_query(did, M, N, K, 1.0, 0x1000, K, 0x1000, N, -2.0, 0x1000, N, kid, wsb)
             if st != tg.GEMM_OK:
                 continue
             say(f"[random] kernel={info['name']} M={M} N={N} K={K} seed={kid}")
@@ -178,3 +180,38 @@ def test_nonzero_mean_large_k_within_worst_case_bound(gpu_available):
     say("[positive] 64x64x4096")
     C, _, _ = run_gemm(A, B, C0, 1.0, 1.0)
     assert ratio(C, A, B, C0, 1.0, 1.0) <= (K + 2) * 2.0 ** -24
+
+
+SPLIT_SHAPES = [(16, 8192, 8192), (1, 256, 1024), (7, 1000, 4100), (16, 136, 5000), (3, 4096, 2048),
+                (16, 520, 1030), (12, 128, 1200)]
+
+
+def test_split_k_skinny_exact_and_reusable_workspace(gpu_available):
+    """The split-K path with one shared workspace: every row count 1..16 and
+    ragged N and K, called back to back with different shapes (and so
+    different split counts), must equal the oracle exactly each time.  The
+    workspace starts out as NaN bytes: its contents on entry must not matter."""
+    ws = tg.workspace(16, 8192, 8192)          # largest of the shapes below
+    ws.fill_(0xFF)
+    for i, (M, N, K) in enumerate(SPLIT_SHAPES + [(m, 640, 2304) for m in range(1, 17)]):
+        assert tg.gemm_workspace_size(tg.GEMM_DTYPE_F32, M, N, K) <= ws.numel()
+        A, B, C0 = make_integer_inputs(M, N, K, seed=200 + i)
+        st, pl = tg.gemm_plan_query(tg.GEMM_DTYPE_F32, M, N, K, -1.0, 0x1000, K, 0x1000, N, 2.0, 0x1000, N, 0,
+                                    ws.numel())
+        assert pl["path"] == tg.GEMM_PATH_SKINNY_SPLITK, (M, N, K, pl)
+        say(f"[split-k] M={M} N={N} K={K} grid={pl['grid']} seed={200 + i}")
+        C, _, _ = run_gemm(A, B, C0, -1.0, 2.0, ws=ws)
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, -1.0, 2.0),
+                                      err_msg=f"split-k {M}x{N}x{K}")
+
+
+def test_split_k_skinny_deterministic(gpu_available):
+    from tiled_gemm_f32_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["f32_16x8192x8192"]
+    A, B, C0 = make_inputs(w)
+    Ad, Bd = A.cuda(), B.cuda()
+    ws = tg.workspace(w.M, w.N, w.K)
+    say("[split-k determinism] 16x8192x8192 x20")
+    outs = [tg.gemm(Ad, Bd, ws=ws) for _ in range(20)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])

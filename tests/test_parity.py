@@ -37,6 +37,19 @@ def test_workload_full_matrix(gpu_available, name):
     assert r <= TOL[w.dtype], r
 
 
+def test_skinny_workspace_path_full_matrix(gpu_available):
+    """The 16 x 8192 x 8192 workload through the split-K workspace path (the
+    configuration the benchmark times), every entry checked."""
+    w = WORKLOADS["f32_16x8192x8192"]
+    A, B, C0 = make_inputs(w)
+    ws = tg.workspace(w.M, w.N, w.K)
+    say(f"[parity] {w.name} via workspace ({ws.numel()} bytes)")
+    C, _, _ = run_gemm(A, B, C0, w.alpha, w.beta, ws=ws)
+    r = ratio(C, A, B, C0, w.alpha, w.beta)
+    say(f"[parity] {w.name} split-k ratio={r:.3e}")
+    assert r <= TOL["f32"], r
+
+
 def test_bf16_8192_sampled(gpu_available):
     w = WORKLOADS["bf16f32_8192"]
     A, B, C0 = make_inputs(w)

@@ -12,12 +12,13 @@ from __future__ import annotations
 from ._lib import (  # noqa: F401  (re-exported C ABI)
     EXPORTED, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
-    GEMM_PATH_SKINNY, GEMM_PATH_TILED, GemmError, gemm_bf16f32, gemm_bf16f32_ex, gemm_f32,
-    gemm_f32_ex, gemm_kernel_count, gemm_kernel_query, gemm_plan_query, gemm_status_string,
-    load)
+    GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
+    gemm_bf16f32_ex, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
+    gemm_plan_query, gemm_status_string, gemm_workspace_size, load)
 
-__all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_status_string",
-           "gemm_kernel_count", "gemm_kernel_query", "gemm_plan_query", "GemmError", "kernels"]
+__all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws",
+           "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
+           "gemm_plan_query", "GemmError", "kernels", "workspace"]
 
 
 def _ld(t, what: str) -> int:
@@ -31,14 +32,24 @@ def _ld(t, what: str) -> int:
     return t.stride(0) if rows > 1 else max(cols, 1)
 
 
-def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None):
+def workspace(M: int, N: int, K: int, device=None):
+    """An uninitialised uint8 device tensor large enough for the fp32 workspace path (or None)."""
+    import torch
+    n = gemm_workspace_size(GEMM_DTYPE_F32, M, N, K)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None, ws=None):
     """C = alpha * (A @ B) + beta * C on the current stream; returns C.
 
     A (M x K) and B (K x N) are CUDA tensors of dtype float32 (fp32 path) or
     bfloat16 (bf16 operands, fp32 accumulate); C is float32 (M x N),
     allocated when None (then beta must be 0).  All three must be row-major
     with unit stride along columns; padded leading dimensions are fine.
-    ``kernel`` forces a kernel id (0 = library choice).
+    ``kernel`` forces a kernel id (0 = library choice).  ``ws`` is an optional
+    device workspace tensor (see ``workspace()``) for the fp32 split-K path.
     """
     import torch
 
@@ -62,7 +73,8 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc)
     with torch.cuda.device(A.device):
         if A.dtype == torch.float32:
-            st = gemm_f32_ex(*args, kernel, stream)
+            wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
+            st = gemm_f32_ex(*args, kernel, wp, wb, stream)
         else:
             st = gemm_bf16f32_ex(*args, kernel, stream)
     if st != GEMM_OK:

@@ -24,13 +24,15 @@ GEMM_PATH_NONE = 0
 GEMM_PATH_SCALE = 1
 GEMM_PATH_TILED = 2
 GEMM_PATH_SKINNY = 3
+GEMM_PATH_SKINNY_SPLITK = 4
 
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16F32 = 1
 
 # Every entry point include/gemm.h declares.
 EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
-            "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex")
+            "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
+            "gemm_workspace_size", "gemm_f32_ws")
 
 
 class KernelInfo(ctypes.Structure):
@@ -68,17 +70,20 @@ def load() -> ctypes.CDLL:
     gemm_sig = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64]
     lib.gemm_f32.argtypes = gemm_sig + [vp]
     lib.gemm_bf16f32.argtypes = gemm_sig + [vp]
-    lib.gemm_f32_ex.argtypes = gemm_sig + [i32, vp]
+    lib.gemm_f32_ex.argtypes = gemm_sig + [i32, vp, i64, vp]
     lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, vp]
-    for fn in (lib.gemm_f32, lib.gemm_bf16f32, lib.gemm_f32_ex, lib.gemm_bf16f32_ex):
+    lib.gemm_f32_ws.argtypes = gemm_sig + [vp, i64, vp]
+    for fn in (lib.gemm_f32, lib.gemm_bf16f32, lib.gemm_f32_ex, lib.gemm_bf16f32_ex, lib.gemm_f32_ws):
         fn.restype = ctypes.c_int
+    lib.gemm_workspace_size.argtypes = [i32, i64, i64, i64]
+    lib.gemm_workspace_size.restype = i64
     lib.gemm_status_string.argtypes = [ctypes.c_int]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_kernel_count.argtypes = []
     lib.gemm_kernel_count.restype = i32
     lib.gemm_kernel_query.argtypes = [i32, ctypes.POINTER(KernelInfo)]
     lib.gemm_kernel_query.restype = ctypes.c_int
-    lib.gemm_plan_query.argtypes = [i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32,
+    lib.gemm_plan_query.argtypes = [i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32, i64,
                                     ctypes.POINTER(Plan)]
     lib.gemm_plan_query.restype = ctypes.c_int
     _lib = lib
@@ -93,8 +98,18 @@ def gemm_bf16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
     return load().gemm_bf16f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
-def gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream=0) -> int:
-    return load().gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream)
+def gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream=0) -> int:
+    return load().gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream)
+
+
+def gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace=0, workspace_bytes=0,
+                stream=0) -> int:
+    return load().gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace,
+                              workspace_bytes, stream)
+
+
+def gemm_workspace_size(dtype, M, N, K) -> int:
+    return int(load().gemm_workspace_size(dtype, M, N, K))
 
 
 def gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream=0) -> int:
@@ -119,9 +134,9 @@ def gemm_kernel_query(kid: int) -> dict:
     return d
 
 
-def gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0):
+def gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0, workspace_bytes=0):
     """(status, plan dict) for the choice the library would make."""
     pl = Plan()
     st = load().gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel,
-                                ctypes.byref(pl))
+                                workspace_bytes, ctypes.byref(pl))
     return st, {f: getattr(pl, f) for f, _ in Plan._fields_}

@@ -27,7 +27,8 @@ constexpr int64_t kMaxLd = (int64_t(1) << 21) - 1;
 constexpr int kComputeUnits = 256;
 
 int table_size() {
-    return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount;
+    return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
+           gemm::kF32SplitKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -38,6 +39,8 @@ const KernelDesc *kernel_by_id(int32_t id) {
     if (i < gemm::kBf16TiledKernelCount) return &gemm::kBf16TiledKernels[i];
     i -= gemm::kBf16TiledKernelCount;
     if (i < gemm::kF32SkinnyKernelCount) return &gemm::kF32SkinnyKernels[i];
+    i -= gemm::kF32SkinnyKernelCount;
+    if (i < gemm::kF32SplitKernelCount) return &gemm::kF32SplitKernels[i];
     return nullptr;
 }
 
@@ -58,6 +61,8 @@ struct Call {
     const void *A, *B;
     float *C;
     int64_t lda, ldb, ldc;
+    void *ws;
+    int64_t ws_bytes;
 };
 
 gemm_status validate(const Call &c) {
@@ -65,6 +70,7 @@ gemm_status validate(const Call &c) {
     if (c.M < 0 || c.N < 0 || c.K < 0) return GEMM_ERR_INVALID_ARG;
     const int64_t min_lda = c.K > 1 ? c.K : 1, min_n = c.N > 1 ? c.N : 1;
     if (c.lda < min_lda || c.ldb < min_n || c.ldc < min_n) return GEMM_ERR_INVALID_ARG;
+    if (c.ws_bytes < 0 || (c.ws != nullptr && !aligned(c.ws, 4))) return GEMM_ERR_INVALID_ARG;
     const uintptr_t esz = c.dtype == GEMM_DTYPE_F32 ? 4 : 2;
     if (c.M > 0 && c.N > 0) {
         if (c.C == nullptr || !aligned(c.C, 4)) return GEMM_ERR_INVALID_ARG;
@@ -97,9 +103,18 @@ bool skinny_fits(const Call &c) {
     return c.M <= 16 && (c.K + 2048) * c.ldb * 4 < (int64_t(1) << 31);
 }
 
+int64_t split_workspace_bytes(const Call &c, const KernelDesc *kd) {
+    const int64_t strips = ceil_div(c.N, kd->tile_n);
+    return gemm::skinny_workspace_bytes((int)strips, (int)c.M, (int)c.N, (int)c.K);
+}
+
 bool kernel_runs(const KernelDesc *kd, const Call &c) {
     if (kd->dtype != c.dtype) return false;
-    if (kd->path == GEMM_PATH_SKINNY && !skinny_fits(c)) return false;
+    if ((kd->path == GEMM_PATH_SKINNY || kd->path == GEMM_PATH_SKINNY_SPLITK) && !skinny_fits(c)) return false;
+    if (kd->path == GEMM_PATH_SKINNY_SPLITK) {
+        const int64_t need = split_workspace_bytes(c, kd);
+        if (need > 0 && (c.ws == nullptr || c.ws_bytes < need)) return false;
+    }
     if (kd->vec_a > 1 && max_vec_a(c) < kd->vec_a) return false;
     return vec_b_ok(c, kd->vec_b);
 }
@@ -114,6 +129,11 @@ const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c,
 // Tile choice: the largest square tile whose tile count covers every compute
 // unit at least once; small problems fall through to the smallest tile.
 const KernelDesc *choose(const Call &c) {
+    // The split-K kernels pay off only where K is actually split.
+    if (c.dtype == GEMM_DTYPE_F32 && skinny_fits(c) && c.ws != nullptr) {
+        const KernelDesc *kd = first_match(gemm::kF32SplitKernels, gemm::kF32SplitKernelCount, c, 0);
+        if (kd != nullptr && split_workspace_bytes(c, kd) > 0) return kd;
+    }
     if (c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kF32SkinnyKernels, gemm::kF32SkinnyKernelCount, c, 0))
             return kd;
@@ -155,8 +175,14 @@ gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc 
         pl.tile_k = kd->tile_k;
         pl.vec_a = kd->vec_a;
         pl.vec_b = kd->vec_b;
-        pl.grid = kd->path == GEMM_PATH_SKINNY ? ceil_div(c.N, kd->tile_n)
-                                               : ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n);
+        if (kd->path == GEMM_PATH_SKINNY) {
+            pl.grid = ceil_div(c.N, kd->tile_n);
+        } else if (kd->path == GEMM_PATH_SKINNY_SPLITK) {
+            const int64_t strips = ceil_div(c.N, kd->tile_n);
+            pl.grid = strips * gemm::skinny_splits((int)strips, (int)c.K);
+        } else {
+            pl.grid = ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n);
+        }
         *chosen = kd;
     }
     if (out) *out = pl;
@@ -204,14 +230,17 @@ gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
         p.ldc = c.ldc;
         p.alpha = c.alpha;
         p.beta = c.beta;
-        err = kd->launch(p, s);
+        err = kd->launch_ws ? kd->launch_ws(p, c.ws, s) : kd->launch(p, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
-               const void *B, int64_t ldb, float beta, const float *C, int64_t ldc) {
+               const void *B, int64_t ldb, float beta, const float *C, int64_t ldc, void *ws = nullptr,
+               int64_t ws_bytes = 0) {
     Call c;
+    c.ws = ws;
+    c.ws_bytes = ws ? ws_bytes : 0;
     c.dtype = dtype;
     c.M = M;
     c.N = N;
@@ -243,10 +272,31 @@ GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha, 
     return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), 0, stream);
 }
 
+GEMM_API gemm_status gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                                 const float *B, int64_t ldb, float beta, float *C, int64_t ldc, void *workspace,
+                                 int64_t workspace_bytes, gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes),
+               0, stream);
+}
+
 GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                                  const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
-                                 int32_t force_kernel, gemm_stream_t stream) {
-    return run(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), force_kernel, stream);
+                                 int32_t force_kernel, void *workspace, int64_t workspace_bytes,
+                                 gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes),
+               force_kernel, stream);
+}
+
+GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K) {
+    if (dtype != GEMM_DTYPE_F32 || M <= 0 || M > 16 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+        return 0;
+    int64_t need = 0;
+    for (int i = 0; i < gemm::kF32SplitKernelCount; ++i) {
+        const int64_t strips = ceil_div(N, gemm::kF32SplitKernels[i].tile_n);
+        const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);
+        need = b > need ? b : need;
+    }
+    return need;
 }
 
 GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
@@ -258,10 +308,14 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
 
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
                                      const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
-                                     const float *C, int64_t ldc, int32_t force_kernel, gemm_plan *out) {
+                                     const float *C, int64_t ldc, int32_t force_kernel, int64_t workspace_bytes,
+                                     gemm_plan *out) {
     if (out == nullptr) return GEMM_ERR_INVALID_ARG;
     const KernelDesc *kd = nullptr;
-    return plan(make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), force_kernel, out, &kd);
+    // Planning never touches the workspace; a non-null stand-in marks that one is passed.
+    void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
+    return plan(make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes), force_kernel,
+                out, &kd);
 }
 
 GEMM_API int32_t gemm_kernel_count(void) { return table_size(); }

@@ -156,6 +156,140 @@ f32_skinny_kernel(GemmParams p) {
     }
 }
 
+// Split-K variant for a caller-provided workspace.  Workgroup (strip, split)
+// covers 64*CG columns (each lane loads 16 bytes of a k row; CG column groups
+// of 64 give 256*CG contiguous bytes per row) over one of `splits` equal
+// ranges of K, so B rows are read in long runs and each workgroup reads only
+// its own K range of A.  The waves' partial tiles are summed in LDS and the
+// workgroup stores its M x 64*CG partial to the workspace; a second kernel
+// (splitk_reduce_kernel) adds the `splits` partials in split order -- the
+// same order every time, so results are deterministic -- and applies alpha
+// and beta.  The kernel boundary orders the two, so no device-scope fence or
+// counter is needed (a fence per workgroup costs more than the reduction).
+// With splits == 1 the workgroup applies the epilogue itself.
+template <int CG, int VA, int WAVES, int UNROLL>
+__global__ void __launch_bounds__(64 * WAVES)
+f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) {
+    constexpr int NW = 64 * CG;
+    __shared__ float red[WAVES][16][NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int strip = blockIdx.x, split = blockIdx.y;
+    const int n0 = strip * NW;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int kbeg = split * kchunk;
+    const int kend = min(K, kbeg + kchunk);
+    const int kq = lane >> 4, lc = lane & 15;
+
+    // Extents end at this split's last row, so prefetch past kend reads zeros.
+    const rsrc_t ra = make_rsrc(static_cast<const float *>(p.A) + kbeg,
+                                clamp_extent(((int64_t)(M - 1) * lda + (kend - kbeg)) * 4));
+    const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + (int64_t)kbeg * ldb + n0,
+                                clamp_extent(((int64_t)(kend - kbeg - 1) * ldb + (N - n0)) * 4));
+    const uint32_t a_base = (uint32_t)(lc * lda + 4 * kq) * 4u;
+    const uint32_t b_base = (uint32_t)(4 * kq * ldb + 4 * lc) * 4u;
+    const uint32_t b_row = (uint32_t)ldb * 4u;
+    const int kspan = kend - kbeg;
+
+    f32x4 acc[CG][4];
+#pragma unroll
+    for (int g = 0; g < CG; ++g)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[g][c] = f32x4{};
+
+    f32x4 av[2][UNROLL];
+    f32x4 bv[2][UNROLL][4][CG];
+    auto issue = [&](int set, int blk0) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int b = blk0 + u * WAVES;
+            av[set][u] = AVec<VA>::load(ra, a_base + (uint32_t)b * 64u, 16 * b + 4 * kq, kspan);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < CG; ++g)
+                    bv[set][u][j][g] = BVec<4>::load(rb, b_base + (uint32_t)(16 * b + j) * b_row + 256u * g);
+        }
+    };
+    auto consume = [&](int set) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < CG; ++g)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[g][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[set][u][j], bv[set][u][j][g][c],
+                                                                         acc[g][c], 0, 0, 0);
+    };
+
+    const int nb = (kspan + 15) >> 4;
+    constexpr int kStride = WAVES * UNROLL;
+    issue(0, wave);
+    for (int blk0 = wave; blk0 < nb; blk0 += 2 * kStride) {
+        issue(1, blk0 + kStride);
+        consume(0);
+        issue(0, blk0 + 2 * kStride);
+        consume(1);
+    }
+
+    // Register r of lane (kq, lc) in column group g, instruction c is row
+    // 4*kq + r, strip column 64*g + 4*lc + c.
+#pragma unroll
+    for (int g = 0; g < CG; ++g)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][64 * g + 4 * lc + c] = acc[g][c][r];
+    __syncthreads();
+
+    const float alpha = p.alpha, beta = p.beta;
+    if (splits == 1) {
+        for (int idx = tid; idx < 16 * NW; idx += 64 * WAVES) {
+            const int i = idx / NW, j = idx % NW;
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) s += red[w][i][j];
+            const int col = n0 + j;
+            if (i < M && col < N) {
+                float *cp = p.C + (int64_t)i * p.ldc + col;
+                float v = alpha * s;
+                if (beta != 0.0f) v = fmaf(beta, *cp, v);
+                *cp = v;
+            }
+        }
+        return;
+    }
+
+    // Partial of this split -> workspace [split][M][N].
+    float *mine = partials + (int64_t)split * M * N;
+    for (int idx = tid; idx < 16 * NW; idx += 64 * WAVES) {
+        const int i = idx / NW, j = idx % NW;
+        if (i >= M || n0 + j >= N) continue;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w][i][j];
+        mine[(int64_t)i * N + n0 + j] = s;
+    }
+}
+
+// C = alpha * (sum over splits, in split order) + beta * C, one thread per
+// output (consecutive threads along a row of C).
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(GemmParams p, const float *partials, int splits) {
+    const int64_t total = (int64_t)p.M * p.N;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    float s = partials[idx];
+    for (int t = 1; t < splits; ++t) s += partials[(int64_t)t * total + idx];
+    const int64_t i = idx / p.N, j = idx - i * p.N;
+    float *cp = p.C + i * p.ldc + j;
+    float v = p.alpha * s;
+    if (p.beta != 0.0f) v = fmaf(p.beta, *cp, v);
+    *cp = v;
+}
+
 template <int VEC, int VA, int WAVES, int UNROLL>
 hipError_t launch_f32_skinny(const GemmParams &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VEC - 1) / (16 * VEC);
@@ -163,6 +297,24 @@ hipError_t launch_f32_skinny(const GemmParams &p, hipStream_t stream) {
     void *argv[] = {&args};
     return hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_kernel<VEC, VA, WAVES, UNROLL>),
                            dim3((unsigned)strips), dim3(64 * WAVES), argv, 0, stream);
+}
+
+template <int CG, int VA, int WAVES, int UNROLL>
+hipError_t launch_f32_skinny_splitk(const GemmParams &p, void *workspace, hipStream_t stream) {
+    const int strips = (p.N + 64 * CG - 1) / (64 * CG);
+    int splits = skinny_splits(strips, p.K);
+    int kchunk = ((p.K + splits - 1) / splits + 15) / 16 * 16;
+    float *partials = static_cast<float *>(workspace);
+    GemmParams args = p;
+    void *argv[] = {&args, &partials, &splits, &kchunk};
+    hipError_t err =
+        hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_splitk_kernel<CG, VA, WAVES, UNROLL>),
+                        dim3((unsigned)strips, (unsigned)splits), dim3(64 * WAVES), argv, 0, stream);
+    if (err != hipSuccess || splits == 1) return err;
+    const int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
+    void *rargv[] = {&args, &partials, &splits};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel), dim3((unsigned)blocks),
+                           dim3(256), rargv, 0, stream);
 }
 
 __global__ void __launch_bounds__(256)
@@ -184,6 +336,9 @@ scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc) {
     X(2, 4, 8, 4) X(2, 4, 16, 2) X(4, 4, 16, 2) X(4, 4, 8, 4) X(1, 4, 16, 4)                      \
     X(2, 1, 8, 4) X(4, 1, 16, 2) X(1, 1, 16, 2)
 
+template __global__ void f32_skinny_splitk_kernel<2, 4, 8, 2>(GemmParams, float *, int, int);
+template __global__ void f32_skinny_splitk_kernel<2, 1, 8, 2>(GemmParams, float *, int, int);
+
 // Explicit instantiations: the device pass never sees the host-only table.
 #define SKINNY_INSTANTIATE(VEC, VA, WAVES, UNROLL) \
     template __global__ void f32_skinny_kernel<VEC, VA, WAVES, UNROLL>(GemmParams);
@@ -199,6 +354,16 @@ SKINNY_LIST(SKINNY_INSTANTIATE)
 #define SKINNY_ENTRY(VEC, VA, WAVES, UNROLL) F32_SKINNY(VEC, VA, WAVES, UNROLL),
 const KernelDesc kF32SkinnyKernels[] = {SKINNY_LIST(SKINNY_ENTRY)};
 const int kF32SkinnyKernelCount = sizeof(kF32SkinnyKernels) / sizeof(kF32SkinnyKernels[0]);
+
+// Split-K skinny kernels (need the caller's workspace).  tile_n is the strip
+// width; tile_k the K depth one batch of all waves covers.
+const KernelDesc kF32SplitKernels[] = {
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 2, 512, 4, 4, "f32_skinny_splitk_n128_a4_w8_u2",
+     nullptr, 0, &launch_f32_skinny_splitk<2, 4, 8, 2>},
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 2, 512, 1, 4, "f32_skinny_splitk_n128_a1_w8_u2",
+     nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 2>},
+};
+const int kF32SplitKernelCount = sizeof(kF32SplitKernels) / sizeof(kF32SplitKernels[0]);
 
 hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, hipStream_t stream) {
     const int64_t total = (int64_t)M * N;

@@ -23,6 +23,7 @@ struct GemmParams {
 };
 
 typedef hipError_t (*LaunchFn)(const GemmParams &p, hipStream_t stream);
+typedef hipError_t (*LaunchWsFn)(const GemmParams &p, void *workspace, hipStream_t stream);
 
 // One row of the kernel table.
 struct KernelDesc {
@@ -34,7 +35,23 @@ struct KernelDesc {
     const char *name;
     LaunchFn launch;
     int32_t min_k;     // the automatic choice skips this kernel below this K (0: no limit)
+    LaunchWsFn launch_ws;  // set instead of `launch` for kernels that need the caller's workspace
 };
+
+// Split-K skinny kernel sizing, shared by its launcher and the workspace query:
+// double the number of K slices (at most 8, each at least 512 deep) until
+// strips * slices covers the 256 compute units.
+inline int skinny_splits(int strips, int K) {
+    int s = 1;
+    while (s < 8 && strips * s < 256 && K / (2 * s) >= 512) s *= 2;
+    return s;
+}
+// Workspace of the split-K skinny path: `splits` partial M x N fp32
+// results, split-major.  One split needs none (the kernel finishes C itself).
+inline int64_t skinny_workspace_bytes(int strips, int M, int N, int K) {
+    const int s = skinny_splits(strips, K);
+    return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
 
 // Tables exported by the kernel files (constant-initialised).
 extern const KernelDesc kF32TiledKernels[];
@@ -43,6 +60,8 @@ extern const KernelDesc kBf16TiledKernels[];
 extern const int kBf16TiledKernelCount;
 extern const KernelDesc kF32SkinnyKernels[];
 extern const int kF32SkinnyKernelCount;
+extern const KernelDesc kF32SplitKernels[];
+extern const int kF32SplitKernelCount;
 
 // C = beta * C over an M x N view (beta == 0 writes zeros without reading).
 hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc,
