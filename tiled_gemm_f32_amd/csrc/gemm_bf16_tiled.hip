@@ -467,7 +467,7 @@ hipError_t launch_bf16_pipe(const GemmParams &p, hipStream_t stream) {
 // has been consumed, so each load has NS-1 slices of MFMA work to arrive
 // (the multi-buffered pipelining of "What is left", carried to NS stages).
 //
-//   A slice: [256 rows][4 chunks of 16 B], chunk ^= ((row >> 1) ^ (row >> 3)) & 3.
+//   A slice: [256 rows][4 chunks of 16 B], chunk ^= (row >> 2) & 3.
 //     Fragment reads are 16-byte ds_read_b128 (k contiguous per row).
 //   B slice: 8 blocks of 32 columns, each [32 k][64 B] (row-major as in HBM),
 //     16-byte chunk ^= 2 * ((k >> 1) & 1).  Fragments come from the
@@ -475,8 +475,13 @@ hipError_t launch_bf16_pipe(const GemmParams &p, hipStream_t stream) {
 //     points at k row k0 + s/4, columns c0 + 4*(s%4) .. +3, and lane j
 //     receives column c0 + j of rows k0 .. k0+3 -- the B operand layout of
 //     the matrix instruction, with no register transpose.
-// Both layouts are bank-conflict free for every read and (contiguous) DMA
-// write, in both 32- and 64-bank views of the LDS.
+// Bank behaviour, as measured with the LDS conflict counters on gfx950: a
+// ds_read_b128 is served in two halves of 32 lanes, each costing as many
+// cycles as its most-loaded 4-byte bank (64 banks, 256-byte period), and
+// some lane pairings cost extra beyond that model (the earlier swizzle
+// ((row >> 1) ^ (row >> 3)) & 3, conflict-free on paper, measured twice the
+// cycles).  (row >> 2) & 3 measured conflict-free, as did the B reads and the
+// contiguous DMA writes.
 // ---------------------------------------------------------------------------
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -485,7 +490,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= n, lgkmcnt = 0, expcnt unconstrained.
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
-__device__ __forceinline__ int ring_swz_a(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int ring_swz_a(int row) { return (row >> 2) & 3; }
 
 template <int NS, int GROUP_M>
 __global__ void __launch_bounds__(256)
@@ -529,26 +534,26 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int lcb = (lane & 3) ^ (2 * ((rb >> 1) & 1));
         b_goff[j] = (uint32_t)(rb * ldb + 32 * nb + 8 * lcb) * 2u;
     }
-    auto issue = [&](int kt, int stage) {
+    // Resources of slice kt.  Rebased per slice: rows past M / past K fall
+    // outside the extents; a chunk at or past K in a valid row of A gets 2^31
+    // added to its offset.
+    auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
-        // Rebased per slice: rows past M / past K fall outside the extents; a
-        // chunk at or past K in a valid row of A gets 2^31 added to its offset.
-        const rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda + k0,
-                                    clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
-        const rsrc_t rb = make_rsrc(B + (int64_t)k0 * ldb + n0,
-                                    clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t poison = (uint32_t)(a_kc[j] >= K - k0) << 31;
+        ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
+        rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
+    };
+    // DMA instruction j (0..7) of slice kt into `stage`: j < 4 fills A block
+    // 4*wave + j, j >= 4 fills B block 4*wave + j - 4.
+    auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
+        if (j < 4) {
+            const uint32_t poison = (uint32_t)(a_kc[j] >= K - kt * BK) << 31;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16, a_goff[j] + poison, 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + j) * 1024), 16, b_goff[j], 0, 0, 0);
+                rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + j - 4) * 1024), 16, b_goff[j - 4], 0, 0, 0);
+        }
     };
-
     // Fragment read bases (bytes within a slice).
     const int h = lane >> 5, l32 = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
@@ -563,11 +568,17 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                                         8 * (j16 & 1));
 
     bf16x8 fa[2][4], fb[2][4];
-    auto read_frags = [&](int stage, int s, int set) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            char *base = stage_base(stage);
+    // Fragment read slot r (0..7) of half s of the slice in `stage` into
+    // register set `set`, in the order the next MFMA block consumes them:
+    // A0, B0, B1, B2, B3, A1, A2, A3 (one ds_read_b128, or two
+    // ds_read_b64_tr_b16 for a B fragment).
+    auto read_slot = [&](int stage, int s, int set, int r) {
+        char *base = stage_base(stage);
+        if (r == 0 || r >= 5) {
+            const int f = r == 0 ? 0 : r - 4;
             fa[set][f] = *reinterpret_cast<const bf16x8 *>(base + fa_base[s] + 2048 * f);
+        } else {
+            const int f = r - 1;
             const int boff = fb_base + 2048 * f + 1024 * s;
             const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + boff));
             const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + boff + 256));
@@ -583,34 +594,58 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // second, so it accumulates the transposed tile (C^T = B^T A^T): each
     // lane then holds runs of 4 consecutive columns of one row of C, which
     // the epilogue writes with 16-byte stores.
-    auto mfmas = [&](int set) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+    auto mma = [&](int set, int t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
     };
 
-    // Slice kt lives in stage kt % NS.  Before the barrier of slice kt, slice
-    // kt+1 must have landed: the loads issued after it belong to slices
-    // kt+2 .. kt+NS-1, 8 per lane each.
+    // Slice kt lives in stage kt % NS.  Each slice is two blocks of 16
+    // MFMAs.  Block 1 multiplies the first k half (register set 0) while the
+    // second half is read into set 1; then every wave waits for slice kt+1
+    // to land and for all reads of stage kt % NS to finish (barrier), and
+    // block 2 multiplies set 1 while refilling that stage with slice kt+NS
+    // and reading the first half of slice kt+1 into set 0.  The other
+    // instructions are placed one per MFMA and pinned there with
+    // sched_barrier, so the matrix pipe never waits on an LDS read that was
+    // issued just before it.  Before the barrier of slice kt the only loads
+    // allowed in flight are those of slices kt+2 .. kt+NS-1, 8 per lane each.
     const int nk = (K + BK - 1) / BK;
+    {
+        rsrc_t ra, rb;
 #pragma unroll
-    for (int st = 0; st < NS; ++st) issue(st, st);
+        for (int st = 0; st < NS; ++st) {
+            slice_rsrc(st, ra, rb);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dma(st, st, ra, rb, j);
+        }
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 1)));
     __builtin_amdgcn_s_barrier();
-    read_frags(0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) read_slot(0, 0, 0, r);
     for (int kb = 0; kb < nk; kb += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int kt = kb + u;
-            read_frags(u, 1, 1);
-            mfmas(0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                mma(0, t);
+                if (t < 8) read_slot(u, 1, 1, t);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 2)));
             __builtin_amdgcn_s_barrier();
-            issue(kt + NS, u);     // refill the stage just consumed (zeros past the end)
-            read_frags((u + 1) % NS, 0, 0);
-            mfmas(1);
+            rsrc_t ra, rb;
+            slice_rsrc(kt + NS, ra, rb);      // zeros past the end
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                mma(1, t);
+                if (t & 1) read_slot((u + 1) % NS, 0, 0, t >> 1);
+                else dma(kt + NS, u, ra, rb, t >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -696,10 +731,10 @@ template __global__ void bf16_tiled_kernel<128, 128, 64, 2, 2, 1, 1, 8>(GemmPara
 // The table holds host function pointers, so it exists only in the host pass.
 #if !defined(__HIP_DEVICE_COMPILE__)
 const KernelDesc kBf16TiledKernels[] = {
-    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_ring5",
-     &launch_bf16_ring<5, 4>, 1024},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
      &launch_bf16_ring<4, 4>, 1024},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_ring5",
+     &launch_bf16_ring<5, 4>, 1024},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_pipe",
      &launch_bf16_pipe<4>},
     BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
