@@ -483,12 +483,7 @@ hipError_t launch_bf16_pipe(const GemmParams &p, hipStream_t stream) {
 // cycles).  (row >> 2) & 3 measured conflict-free, as did the B reads and the
 // contiguous DMA writes.
 // ---------------------------------------------------------------------------
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt <= n, lgkmcnt = 0, expcnt unconstrained.
-constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
 
 __device__ __forceinline__ int ring_swz_a(int row) { return (row >> 2) & 3; }
 

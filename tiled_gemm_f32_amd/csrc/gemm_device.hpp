@@ -104,4 +104,13 @@ __host__ __device__ __forceinline__ void tile_coords_square(int wg, int tiles_m,
     tn = 16 * sq_c + 8 * (xcd >> 2) + (j >> 2);
 }
 
+
+// LDS pointer types for the direct-to-LDS buffer loads and transposing reads.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= n, lgkmcnt = 0, expcnt unconstrained.
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
+
 }  // namespace gemm

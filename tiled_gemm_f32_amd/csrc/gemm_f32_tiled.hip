@@ -210,6 +210,206 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }
 }
 
+// Ring form for 16-byte-aligned operands: the 256 x 256 tile, 16-deep k
+// slices and 4 waves of the kernel above, with three changes that remove its
+// stalls (each slice is 128 matrix instructions per wave, so a few hundred
+// idle cycles per slice are several percent):
+//   * Panels go straight from HBM into an LDS ring of NS slices with
+//     buffer_load ... lds (lane i of a wave instruction lands at the LDS base
+//     + 16*i), so no registers stage them and no LDS stores are issued.  Slice
+//     kt+NS is requested as soon as slice kt has been consumed ("What is
+//     left": asynchronous copies and multi-buffering).
+//       A slice: [256 rows][4 chunks of 16 B] (k contiguous), chunk ^= (row >> 2) & 3;
+//       B slice: [16 k rows][256 columns], as in HBM.
+//   * Column j of the wave's 32 x 32 fragment fn stands for column 4*j + fn
+//     of its 128-column block, so a lane's four B values of a k pair are
+//     four consecutive floats (one 16-byte read) and its results for a row
+//     are four consecutive columns of C (one 16-byte store).
+//   * Each slice is 8 steps of 16 MFMAs (one k pair per step).  The B values
+//     of step s+1 are read during step s; after step 5 every wave waits for
+//     slice kt+1 to land and for the reads of this stage to finish
+//     (barrier), then steps 6 and 7 run while the stage is refilled and the
+//     next slice's A fragments and first B values are read.  The other
+//     instructions are pinned between MFMAs with sched_barrier.
+// Loads complete in issue order: before the barrier of slice kt the only
+// loads allowed in flight are the 8*(NS-2) of the slices after kt+1.
+template <int NS, int GROUP_M>
+__global__ void __launch_bounds__(256)
+f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    static_assert(NS % 2 == 0, "the two A-fragment register sets alternate with the stage");
+    constexpr int BM = 256, BN = 256, BK = 16, kSteps = 8;
+    constexpr int kA = BM * BK * 4;     // 16 KB of A per slice
+    constexpr int kB = BK * BN * 4;     // 16 KB of B per slice
+    constexpr int kStage = kA + kB;
+    // One array per stage: with distinct objects the compiler can tell that
+    // fragment reads of one stage do not depend on loads still landing in
+    // another.
+    __shared__ __attribute__((aligned(1024))) char st0[kStage], st1[kStage], st2[kStage], st3[kStage];
+    auto stage_base = [&](int st) -> char * { return st == 0 ? st0 : st == 1 ? st1 : st == 2 ? st2 : st3; };
+    static_assert(NS <= 4, "four stage arrays");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, GROUP_M, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const float *A = static_cast<const float *>(p.A);
+    const float *B = static_cast<const float *>(p.B);
+    const int a_rows = min(BM, M - m0);
+
+    // Load instruction j of this wave: j < 4 fills A block 4*wave + j (rows
+    // 16*blk .. +15; lane -> row 16*blk + lane/4, physical chunk lane%4);
+    // j >= 4 fills B row 4*wave + j - 4 (lane -> columns 4*lane .. +3).
+    uint32_t a_goff[4], b_goff[4];
+    int a_kc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 16 * (4 * wave + j) + (lane >> 2);
+        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+        a_kc[j] = 4 * lc;
+        a_goff[j] = (uint32_t)(row * lda + 4 * lc) * 4u;
+        b_goff[j] = (uint32_t)((4 * wave + j) * ldb + 4 * lane) * 4u;
+    }
+    // Resources of slice kt, rebased per slice: rows past M / past K fall
+    // outside the extents; a chunk at or past K in a valid row of A gets 2^31
+    // added to its offset.
+    auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
+        const int k0 = kt * BK;
+        ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 4));
+        rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
+    };
+    auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
+        if (j < 4) {
+            const uint32_t poison = (uint32_t)(a_kc[j] >= K - kt * BK) << 31;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16, a_goff[j] + poison, 0, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + j - 4) * 1024), 16, b_goff[j - 4], 0, 0, 0);
+        }
+    };
+
+    const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    // A fragment (fm, q): row wm*128 + 32*fm + l32, k = 8h + 4q .. +3.
+    // B values of step s: row 8h + s, columns wn*128 + 4*l32 .. +3.
+    uint32_t fa_off[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) fa_off[q] = (uint32_t)((wm * 128 + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
+    const uint32_t fb_off = (uint32_t)(kA + 8 * h * 1024 + (wn * 128 + 4 * l32) * 4);
+
+    f32x4 af[2][4][2];
+    f32x4 bv[kSteps];
+    auto read_a = [&](int stage, int set, int fm) {
+        const char *base = stage_base(stage);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) af[set][fm][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[q] + 2048 * fm);
+    };
+    auto read_b = [&](int stage, int s) {
+        bv[s] = *reinterpret_cast<const f32x4 *>(stage_base(stage) + fb_off + 1024 * s);
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    // MFMA t (0..15) of step s: fragment (t/4, t%4); lane half h supplies
+    // k = s (h = 0) or 8 + s (h = 1) of the slice for both operands.
+    auto mma = [&](int set, int s, int t) {
+        const int fm = t >> 2, fn = t & 3;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][fm][s >> 2][s & 3], bv[s][fn], acc[fm][fn], 0, 0, 0);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    {
+        rsrc_t ra, rb;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            slice_rsrc(st, ra, rb);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dma(st, st, ra, rb, j);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 1)));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) read_a(0, 0, fm);
+    read_b(0, 0);
+    for (int kb = 0; kb < nk; kb += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int kt = kb + u, set = u & 1, nxt = (u + 1) % NS;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 6; ++s) {
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    mma(set, s, t);
+                    if (t == 0) read_b(u, s + 1);
+                    if (s == 5 && t == 1) read_b(u, 7);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 2)));
+            __builtin_amdgcn_s_barrier();
+            rsrc_t ra, rb;
+            slice_rsrc(kt + NS, ra, rb);     // zeros past the end
+            __builtin_amdgcn_sched_barrier(0);
+            // Steps 6 and 7 with 8 loads and 5 fragment reads between them.
+#pragma unroll
+            for (int q = 0; q < 32; ++q) {
+                mma(set, 6 + (q >> 4), q & 15);
+                if ((q & 1) == 0 && q < 16) dma(kt + NS, u, ra, rb, q >> 1);
+                if ((q & 1) == 1 && q < 8) read_a(nxt, set ^ 1, q >> 1);
+                if (q == 9) read_b(nxt, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+    // Epilogue.  Register r of lane (h, l32) in fragment (fm, fn) is row
+    // 32*fm + 8*(r/4) + 4*h + r%4 of the wave tile, column 4*l32 + fn; N is a
+    // multiple of 4 on this path, so each run of 4 columns is wholly inside
+    // or outside C.
+    const float alpha = p.alpha, beta = p.beta;
+    const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
+    const int col = n0 + wn * 128 + 4 * l32;
+    if (col < N) {
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 128 + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row >= M) continue;
+                float *cp = p.C + (int64_t)row * p.ldc + col;
+                f32x4 v = {alpha * acc[fm][0][r], alpha * acc[fm][1][r], alpha * acc[fm][2][r], alpha * acc[fm][3][r]};
+                if (vec_c) {
+                    if (beta != 0.0f) {
+                        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cp);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c0[e], v[e]);
+                    }
+                    *reinterpret_cast<f32x4 *>(cp) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cp[e] = (beta != 0.0f) ? fmaf(beta, cp[e], v[e]) : v[e];
+                }
+            }
+        }
+    }
+}
+
+template <int NS, int GROUP_M>
+hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M>),
+                           dim3((unsigned)(tiles_m * tiles_n)), dim3(256), argv, 0, stream);
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
 hipError_t launch_f32_tiled(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
@@ -226,6 +426,7 @@ hipError_t launch_f32_tiled(const GemmParams &p, hipStream_t stream) {
 
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
+template __global__ void f32_ring_kernel<4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 1, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 1, 4, 4>(GemmParams, int, int);
@@ -246,6 +447,8 @@ template __global__ void f32_tiled_kernel<64, 64, 16, 2, 2, 1, 1, 8>(GemmParams,
 // Order matters: the dispatcher takes the first kernel of the chosen tile
 // shape whose vector widths the operands allow, so wider loads come first.
 const KernelDesc kF32TiledKernels[] = {
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_ring4",
+     &launch_f32_ring<4, 4>},
     F32_TILED(256, 256, 16, 2, 2, 4, 4, 4),
     F32_TILED(256, 256, 16, 2, 2, 4, 1, 4),
     F32_TILED(256, 256, 16, 2, 2, 1, 4, 4),
