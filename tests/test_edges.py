@@ -71,6 +71,26 @@ def test_exact_integer_every_kernel(gpu_available, dtype):
                                           err_msg=f"{info['name']} {M}x{N}x{K}")
 
 
+def test_f32_ring_ragged_multi_wave(gpu_available):
+    """The fp32 ring kernel on a problem with more tiles than compute units:
+    4100 x 4300 gives 17 x 17 = 289 tiles of 256 x 256 (two waves, ragged
+    last tiles) and K = 1100 gives 69 k slices of 16 (the last one
+    partial; the ring runs on to a multiple of its depth with zero slices).
+    Integer data: the result must equal the oracle exactly, with beta on and
+    off, and with a C whose rows are not 16-byte aligned (scalar stores)."""
+    M, N, K = 4100, 4300, 1100
+    A, B, C0 = make_integer_inputs(M, N, K, seed=301)
+    ring = [k for k in _kernel_ids(tg.GEMM_DTYPE_F32) if "ring" in tg.gemm_kernel_query(k)["name"]]
+    assert ring
+    for kid in ring:
+        name = tg.gemm_kernel_query(kid)["name"]
+        for alpha, beta, pad in [(2.0, 0.5, 0), (1.0, 0.0, 0), (-1.0, 1.0, 1)]:
+            say(f"[ring multi-tile] kernel={name} M={M} N={N} K={K} alpha={alpha} beta={beta} c_pad={pad} seed=301")
+            C, _, _ = run_gemm(A, B, C0, alpha, beta, kernel=kid, pad=(0, 0, pad))
+            np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, alpha, beta),
+                                          err_msg=f"{name} alpha={alpha} beta={beta} c_pad={pad}")
+
+
 def test_bf16_ring_ragged_multi_wave(gpu_available):
     """The ring kernels on a problem with more tiles than compute units:
     4100 x 4296 gives 17 x 17 = 289 tiles of 256 x 256 (two waves, ragged

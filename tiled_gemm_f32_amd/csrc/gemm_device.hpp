@@ -50,6 +50,20 @@ __device__ __forceinline__ u32x2 load_b64(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+// Non-temporal ("nt" cache-policy bit) variants for data read exactly once.
+// Streaming such data through the caches with the normal policy displaces
+// whatever else they hold; in particular a large C just written by a
+// previous kernel then gets written back to HBM while this kernel runs.
+constexpr int kCpolNonTemporal = 2;
+__device__ __forceinline__ u32x4 load_b128_nt(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNonTemporal));
+}
+__device__ __forceinline__ u32x2 load_b64_nt(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolNonTemporal));
+}
+__device__ __forceinline__ uint32_t load_b32_nt(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCpolNonTemporal);
+}
 __device__ __forceinline__ uint16_t load_b16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }

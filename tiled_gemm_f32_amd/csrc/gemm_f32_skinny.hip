@@ -26,23 +26,24 @@
 namespace gemm {
 namespace {
 
+// B is streamed exactly once: non-temporal loads.
 template <int V> struct BVec;
 template <> struct BVec<4> {
     typedef f32x4 T;
     static __device__ __forceinline__ f32x4 load(rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(f32x4, load_b128(r, off));
+        return __builtin_bit_cast(f32x4, load_b128_nt(r, off));
     }
 };
 template <> struct BVec<2> {
     typedef f32x2 T;
     static __device__ __forceinline__ f32x2 load(rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(f32x2, load_b64(r, off));
+        return __builtin_bit_cast(f32x2, load_b64_nt(r, off));
     }
 };
 template <> struct BVec<1> {
     typedef float T;
     static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(float, load_b32(r, off));
+        return __builtin_bit_cast(float, load_b32_nt(r, off));
     }
 };
 
