@@ -337,8 +337,8 @@ scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc) {
     X(2, 4, 8, 4) X(2, 4, 16, 2) X(4, 4, 16, 2) X(4, 4, 8, 4) X(1, 4, 16, 4)                      \
     X(2, 1, 8, 4) X(4, 1, 16, 2) X(1, 1, 16, 2)
 
-template __global__ void f32_skinny_splitk_kernel<2, 4, 8, 2>(GemmParams, float *, int, int);
-template __global__ void f32_skinny_splitk_kernel<2, 1, 8, 2>(GemmParams, float *, int, int);
+template __global__ void f32_skinny_splitk_kernel<2, 4, 8, 1>(GemmParams, float *, int, int);
+template __global__ void f32_skinny_splitk_kernel<2, 1, 8, 1>(GemmParams, float *, int, int);
 
 // Explicit instantiations: the device pass never sees the host-only table.
 #define SKINNY_INSTANTIATE(VEC, VA, WAVES, UNROLL) \
@@ -359,10 +359,10 @@ const int kF32SkinnyKernelCount = sizeof(kF32SkinnyKernels) / sizeof(kF32SkinnyK
 // Split-K skinny kernels (need the caller's workspace).  tile_n is the strip
 // width; tile_k the K depth one batch of all waves covers.
 const KernelDesc kF32SplitKernels[] = {
-    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 2, 512, 4, 4, "f32_skinny_splitk_n128_a4_w8_u2",
-     nullptr, 0, &launch_f32_skinny_splitk<2, 4, 8, 2>},
-    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 2, 512, 1, 4, "f32_skinny_splitk_n128_a1_w8_u2",
-     nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 2>},
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 1, 512, 4, 4, "f32_skinny_splitk_n128_a4_w8_u1",
+     nullptr, 0, &launch_f32_skinny_splitk<2, 4, 8, 1>},
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 1, 512, 1, 4, "f32_skinny_splitk_n128_a1_w8_u1",
+     nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 1>},
 };
 const int kF32SplitKernelCount = sizeof(kF32SplitKernels) / sizeof(kF32SplitKernels[0]);
 
