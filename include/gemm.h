@@ -88,17 +88,24 @@ GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha,
                          gemm_stream_t stream);
 
 /*
- * Workspace.  For M <= 16 fp32 problems the library can split K across
- * workgroups and reduce the partial results in a caller-provided device
- * workspace (the split-K variant of "A GEMM Kernel, Step by Step", section
- * "What is left").  gemm_workspace_size() returns the bytes that path needs
- * for this shape (0 when the shape never uses one): `splits` partial M x N
- * fp32 results, reduced in a fixed order by a second kernel on the same
- * stream (results are deterministic).  The workspace needs no
- * initialisation and its contents after a call are unspecified.  Calls
- * sharing a workspace must be ordered (same stream, or synchronised
- * streams); overlapping calls on one workspace race.
- * gemm_f32_ws() is gemm_f32() with a workspace; a NULL or too-small
+ * Workspace.  Two paths split K across workgroups and reduce the partial
+ * results in a caller-provided device workspace (the split-K variant of
+ * "Tiled matrix multiplication", section "Variants and alternatives", and of
+ * "A GEMM Kernel, Step by Step", section "What is left"):
+ *   - fp32 with M <= 16: the skinny streaming kernel, split into up to 8
+ *     k ranges of at least 512;
+ *   - any tiled problem (fp32 or bf16) with fewer 256 x 256 output tiles
+ *     than compute units: the tiled kernel, split into up to 16 k ranges of
+ *     at least 1024, when the split grid fills at least three quarters of
+ *     the compute units.
+ * gemm_workspace_size() returns the largest workspace either path can use
+ * for this shape (0 when none applies): `splits` partial M x N fp32
+ * results, reduced in split order by a second kernel on the same stream
+ * (results are deterministic).  The workspace needs no initialisation and
+ * its contents after a call are unspecified.  Calls sharing a workspace
+ * must be ordered (same stream, or synchronised streams); overlapping calls
+ * on one workspace race.  gemm_f32_ws() and gemm_bf16f32_ws() are
+ * gemm_f32() and gemm_bf16f32() with a workspace; a NULL or too-small
  * workspace simply selects the workspace-free kernels.
  */
 GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K);
@@ -107,6 +114,11 @@ GEMM_API gemm_status gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
                                  const float *A, int64_t lda, const float *B, int64_t ldb,
                                  float beta, float *C, int64_t ldc,
                                  void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
+
+GEMM_API gemm_status gemm_bf16f32_ws(int64_t M, int64_t N, int64_t K, float alpha,
+                                    const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                                    float beta, float *C, int64_t ldc,
+                                    void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
 
 /* Static English text for a status code (never NULL). */
 GEMM_API const char *gemm_status_string(gemm_status status);
@@ -150,6 +162,7 @@ typedef struct gemm_plan {
     int32_t threads;        /* threads per workgroup */
     int32_t tile_m, tile_n, tile_k;
     int32_t vec_a, vec_b;
+    int32_t splits;         /* k ranges of a tiled K split (1: none; 0 for NONE / SCALE) */
 } gemm_plan;
 
 /* Number of kernels in the table; ids run from 1 to this value. */
@@ -174,7 +187,7 @@ GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_
                             float beta, const float *C, int64_t ldc,
                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out);
 
-/* gemm_f32_ws / gemm_bf16f32 with a forced kernel (force_kernel as above). */
+/* gemm_f32_ws / gemm_bf16f32_ws with a forced kernel (force_kernel as above). */
 GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
                         const float *A, int64_t lda, const float *B, int64_t ldb,
                         float beta, float *C, int64_t ldc,
@@ -184,7 +197,8 @@ GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
 GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
                             const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                             float beta, float *C, int64_t ldc,
-                            int32_t force_kernel, gemm_stream_t stream);
+                            int32_t force_kernel, void *workspace, int64_t workspace_bytes,
+                            gemm_stream_t stream);
 
 #ifdef __cplusplus
 }

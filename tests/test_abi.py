@@ -212,22 +212,82 @@ def test_forced_kernels():
 # ----------------------------------------------------------------------------- workspace path
 
 def test_workspace_size():
-    # 16 x 8192 x 8192: 64 strips of 128 columns, K split in 4 -> 4 partial 16 x 8192 results.
-    assert tg.gemm_workspace_size(F32, 16, 8192, 8192) == 4 * 16 * 8192 * 4
-    assert tg.gemm_workspace_size(F32, 17, 8192, 8192) == 0
-    assert tg.gemm_workspace_size(BF16, 16, 8192, 8192) == 0
+    MiB = 1 << 20
+    # 16 x 8192 x 8192 fp32: the skinny split needs 4 slices x 16 x 8192 fp32 (2 MiB); the tiled
+    # split of 32 tiles of 256 x 256 into 8 slices of 1024 needs 8 x 16 x 8192 fp32 (4 MiB).
+    # The larger of the two is returned.
+    assert tg.gemm_workspace_size(F32, 16, 8192, 8192) == 8 * 16 * 8192 * 4 == 4 * MiB
+    assert tg.gemm_workspace_size(BF16, 16, 8192, 8192) == 8 * 16 * 8192 * 4
+    assert tg.gemm_workspace_size(F32, 17, 8192, 8192) == 8 * 17 * 8192 * 4
     assert tg.gemm_workspace_size(F32, 16, 8192, 0) == 0
-    # K is not cut into slices shallower than 512: K = 1024 gives 2 slices, K = 1023 one (no workspace).
+    # Skinny slices are at least 512 deep, tiled ones at least 1024: K = 1024 gives 2 skinny
+    # slices and no tiled split; K = 1023 neither.
     assert tg.gemm_workspace_size(F32, 1, 256, 1024) == 2 * 1 * 256 * 4
     assert tg.gemm_workspace_size(F32, 1, 256, 1023) == 0
-    # Partials hold M rows: 7 x 1000 with 8 strips and K = 4100 -> 8 slices.
+    # Partials hold M rows: 7 x 1000 with 8 strips and K = 4100 -> 8 skinny slices (the tiled
+    # split of its 4 tiles would take 4 slices of 1088).
     assert tg.gemm_workspace_size(F32, 7, 1000, 4100) == 8 * 7 * 1000 * 4
+    # Tiled split: 1024 x 1024 x 16384 has 16 tiles -> 16 slices of 1024.
+    assert tg.gemm_workspace_size(F32, 1024, 1024, 16384) == 16 * 1024 * 1024 * 4
+    assert tg.gemm_workspace_size(BF16, 1024, 1024, 16384) == 16 * 1024 * 1024 * 4
+    # Enough tiles already (4096^3: 256 tiles): no split, no workspace.
+    assert tg.gemm_workspace_size(F32, 4096, 4096, 4096) == 0
+    assert tg.gemm_workspace_size(BF16, 8192, 8192, 8192) == 0
+    assert tg.gemm_workspace_size(2, 16, 16, 16) == 0
 
 
 def test_workspace_selects_split_k_for_decode_shape():
     need = tg.gemm_workspace_size(F32, 16, 8192, 8192)
+    skinny_need = 4 * 16 * 8192 * 4
     st, p = plan(F32, 16, 8192, 8192, ws=need)
     assert st == OK and p["path"] == tg.GEMM_PATH_SKINNY_SPLITK and p["grid"] == 256 and p["tile_n"] == 128
-    assert plan(F32, 16, 8192, 8192, ws=need - 1)[1]["path"] == tg.GEMM_PATH_SKINNY
+    assert p["splits"] == 1
+    assert plan(F32, 16, 8192, 8192, ws=skinny_need)[1]["path"] == tg.GEMM_PATH_SKINNY_SPLITK
+    assert plan(F32, 16, 8192, 8192, ws=skinny_need - 1)[1]["path"] == tg.GEMM_PATH_SKINNY
     assert plan(F32, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_SKINNY
-    assert plan(F32, 17, 8192, 8192, ws=need)[1]["path"] == tg.GEMM_PATH_TILED
+
+
+def test_workspace_tiled_k_split_plan():
+    """Few output tiles and a deep K: with a workspace the 256 x 256 kernel is
+    split along K so that tiles x slices fills the compute units."""
+    for dt in (F32, BF16):
+        need = tg.gemm_workspace_size(dt, 1024, 1024, 16384)
+        st, p = plan(dt, 1024, 1024, 16384, ws=need)
+        assert st == OK and p["path"] == tg.GEMM_PATH_TILED and p["tile_m"] == 256
+        assert p["splits"] == 16 and p["grid"] == 16 * 16
+        # No workspace: smaller tiles, unsplit (fp32 has 64 x 64 kernels, 256 tiles; bf16's
+        # smallest tile is 128 x 128, 64 tiles).  Too small a workspace for the 16-way
+        # 256 x 256 split: the 128 x 128 kernel split 4 ways (16 MiB) fills the chip.
+        st, p = plan(dt, 1024, 1024, 16384)
+        assert st == OK and p["splits"] == 1
+        assert (p["tile_m"], p["grid"]) == ((64, 256) if dt == F32 else (128, 64))
+        st, p = plan(dt, 1024, 1024, 16384, ws=need - 4)
+        assert st == OK and (p["tile_m"], p["splits"], p["grid"]) == (128, 4, 256)
+        # 17 x 8192 x 8192 (not skinny): a 256-row tile would be 93% padding; no tile size
+        # wastes under a quarter, so the usual choice (the smallest tile) is split instead.
+        need = tg.gemm_workspace_size(dt, 17, 8192, 8192)
+        st, p = plan(dt, 17, 8192, 8192, ws=need)
+        assert st == OK
+        assert (p["tile_m"], p["splits"], p["grid"]) == ((64, 2, 256) if dt == F32 else (128, 4, 256))
+        # 100 x 4096 x 8192: 128-row tiles waste 22% -> 32 tiles x 8 slices.
+        st, p = plan(dt, 100, 4096, 8192, ws=tg.gemm_workspace_size(dt, 100, 4096, 8192))
+        assert st == OK and (p["tile_m"], p["splits"], p["grid"]) == (128, 8, 256)
+    # A 256 x 256 split that would fill under three quarters of the compute units is not
+    # preferred over smaller tiles: 512 x 1024 has 8 such tiles (8 x 16 = 128 workgroups);
+    # the 128 x 128 kernel (32 tiles) split in 8 is taken instead.
+    for dt, tile, splits in ((F32, 128, 8), (BF16, 128, 8)):
+        need = tg.gemm_workspace_size(dt, 512, 1024, 16384)
+        st, p = plan(dt, 512, 1024, 16384, ws=need)
+        assert st == OK and (p["tile_m"], p["splits"], p["grid"]) == (tile, splits, 256)
+    # Slices are whole multiples of 64 deep: 256 x 512 x 4100 on 64 x 64 tiles (32 tiles)
+    # -> 4 slices of 1088 (the last one 836).
+    st, p = plan(F32, 256, 512, 4100, ws=tg.gemm_workspace_size(F32, 256, 512, 4100))
+    assert st == OK and p["tile_m"] == 64 and p["splits"] == 4 and p["grid"] == 128
+    # No split where K is shallow or the problem already fills the chip.
+    assert plan(F32, 1024, 1024, 1500, ws=1 << 30)[1]["splits"] == 1
+    assert plan(F32, 4096, 4096, 4096, ws=1 << 30)[1]["splits"] == 1
+    # Quick-return paths report no split.
+    assert plan(F32, 0, 16, 16, ws=1 << 30)[1]["splits"] == 0
+    assert plan(F32, 16, 16, 0, ws=1 << 30)[1]["splits"] == 0
+
+

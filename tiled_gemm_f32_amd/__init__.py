@@ -13,10 +13,10 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
     EXPORTED, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
-    gemm_bf16f32_ex, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
+    gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
     gemm_plan_query, gemm_status_string, gemm_workspace_size, load)
 
-__all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws",
+__all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
            "gemm_plan_query", "GemmError", "kernels", "workspace"]
 
@@ -32,10 +32,11 @@ def _ld(t, what: str) -> int:
     return t.stride(0) if rows > 1 else max(cols, 1)
 
 
-def workspace(M: int, N: int, K: int, device=None):
-    """An uninitialised uint8 device tensor large enough for the fp32 workspace path (or None)."""
+def workspace(M: int, N: int, K: int, device=None, dtype: int = GEMM_DTYPE_F32):
+    """An uninitialised uint8 device tensor large enough for the split-K
+    workspace paths of this shape and operand type (or None when none applies)."""
     import torch
-    n = gemm_workspace_size(GEMM_DTYPE_F32, M, N, K)
+    n = gemm_workspace_size(dtype, M, N, K)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
@@ -49,7 +50,7 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     allocated when None (then beta must be 0).  All three must be row-major
     with unit stride along columns; padded leading dimensions are fine.
     ``kernel`` forces a kernel id (0 = library choice).  ``ws`` is an optional
-    device workspace tensor (see ``workspace()``) for the fp32 split-K path.
+    device workspace tensor (see ``workspace()``) for the split-K paths.
     """
     import torch
 
@@ -72,11 +73,11 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
         stream = torch.cuda.current_stream(A.device).cuda_stream
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc)
     with torch.cuda.device(A.device):
+        wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
         if A.dtype == torch.float32:
-            wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
             st = gemm_f32_ex(*args, kernel, wp, wb, stream)
         else:
-            st = gemm_bf16f32_ex(*args, kernel, stream)
+            st = gemm_bf16f32_ex(*args, kernel, wp, wb, stream)
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
     return C

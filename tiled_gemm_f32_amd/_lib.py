@@ -32,7 +32,7 @@ GEMM_DTYPE_BF16F32 = 1
 # Every entry point include/gemm.h declares.
 EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
-            "gemm_workspace_size", "gemm_f32_ws")
+            "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws")
 
 
 class KernelInfo(ctypes.Structure):
@@ -45,7 +45,8 @@ class KernelInfo(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("kernel_id", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("threads", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("tile_k", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32)]
+                ("tile_k", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
+                ("splits", ctypes.c_int32)]
 
 
 class GemmError(RuntimeError):
@@ -71,9 +72,11 @@ def load() -> ctypes.CDLL:
     lib.gemm_f32.argtypes = gemm_sig + [vp]
     lib.gemm_bf16f32.argtypes = gemm_sig + [vp]
     lib.gemm_f32_ex.argtypes = gemm_sig + [i32, vp, i64, vp]
-    lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, vp]
+    lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, vp, i64, vp]
     lib.gemm_f32_ws.argtypes = gemm_sig + [vp, i64, vp]
-    for fn in (lib.gemm_f32, lib.gemm_bf16f32, lib.gemm_f32_ex, lib.gemm_bf16f32_ex, lib.gemm_f32_ws):
+    lib.gemm_bf16f32_ws.argtypes = gemm_sig + [vp, i64, vp]
+    for fn in (lib.gemm_f32, lib.gemm_bf16f32, lib.gemm_f32_ex, lib.gemm_bf16f32_ex, lib.gemm_f32_ws,
+               lib.gemm_bf16f32_ws):
         fn.restype = ctypes.c_int
     lib.gemm_workspace_size.argtypes = [i32, i64, i64, i64]
     lib.gemm_workspace_size.restype = i64
@@ -112,8 +115,15 @@ def gemm_workspace_size(dtype, M, N, K) -> int:
     return int(load().gemm_workspace_size(dtype, M, N, K))
 
 
-def gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream=0) -> int:
-    return load().gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, stream)
+def gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace=0, workspace_bytes=0,
+                    stream=0) -> int:
+    return load().gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace,
+                                  workspace_bytes, stream)
+
+
+def gemm_bf16f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream=0) -> int:
+    return load().gemm_bf16f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes,
+                                  stream)
 
 
 def gemm_status_string(status: int) -> str:

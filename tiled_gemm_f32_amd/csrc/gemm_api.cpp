@@ -119,6 +119,45 @@ bool kernel_runs(const KernelDesc *kd, const Call &c) {
     return vec_b_ok(c, kd->vec_b);
 }
 
+// K split of the tiled kernels ("Tiled matrix multiplication", "Variants and
+// alternatives"; "A GEMM Kernel, Step by Step", "What is left"): when a
+// problem has fewer output tiles than compute units and a deep K, the k
+// range is cut into up to kMaxKSplits slices of at least kMinSplitDepth
+// (whole multiples of kSplitAlign, which keeps every slice's operand bases
+// 16-byte aligned); each slice's partial product goes to the caller's
+// workspace and a reduce kernel adds them in order.
+constexpr int kMaxKSplits = 16;
+constexpr int64_t kMinSplitDepth = 1024;
+constexpr int64_t kSplitAlign = 64;
+
+struct KSplit {
+    int splits;        // 1: no split
+    int32_t kchunk;    // k depth of each slice (the last one may be shorter)
+    int64_t bytes;     // workspace: splits partial M x N fp32 products
+};
+
+KSplit tiled_ksplit(const Call &c, int tile_m, int tile_n) {
+    KSplit r{1, 0, 0};
+    const int64_t tiles = ceil_div(c.M, tile_m) * ceil_div(c.N, tile_n);
+    int s = 1;
+    while (s < kMaxKSplits && tiles * s * 2 <= kComputeUnits && c.K / (2 * s) >= kMinSplitDepth) s *= 2;
+    if (s == 1) return r;
+    const int64_t chunk = ceil_div(ceil_div(c.K, s), kSplitAlign) * kSplitAlign;
+    r.splits = (int)ceil_div(c.K, chunk);
+    if (r.splits < 2) return KSplit{1, 0, 0};
+    r.kchunk = (int32_t)chunk;
+    r.bytes = (int64_t)r.splits * c.M * c.N * 4;
+    return r;
+}
+
+// The split a tiled kernel takes for this call: none without a workspace
+// large enough for it.
+KSplit call_ksplit(const Call &c, const KernelDesc *kd) {
+    if (kd->path != GEMM_PATH_TILED || c.ws == nullptr) return KSplit{1, 0, 0};
+    const KSplit r = tiled_ksplit(c, kd->tile_m, kd->tile_n);
+    return r.splits > 1 && c.ws_bytes >= r.bytes ? r : KSplit{1, 0, 0};
+}
+
 const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c, int tile_m) {
     for (int i = 0; i < count; ++i)
         if ((tile_m == 0 || table[i].tile_m == tile_m) && c.K >= table[i].min_k && kernel_runs(&table[i], c))
@@ -140,6 +179,22 @@ const KernelDesc *choose(const Call &c) {
     }
     const KernelDesc *table = c.dtype == GEMM_DTYPE_F32 ? gemm::kF32TiledKernels : gemm::kBf16TiledKernels;
     const int count = c.dtype == GEMM_DTYPE_F32 ? gemm::kF32TiledKernelCount : gemm::kBf16TiledKernelCount;
+    // With a workspace: the largest tile that wastes at most a quarter of
+    // its padded M x N ("The fringe and the last wave": tile quantisation)
+    // and whose grid of tiles x K slices fills at least three quarters of the
+    // compute units.  Padding costs the fp32 kernels 8x more time than the
+    // bf16 ones (their matrix rate is 8x lower), so thin problems go to small
+    // tiles even when a large tile would have enough slices.
+    if (c.ws != nullptr) {
+        for (int tile : {256, 128, 64}) {
+            const KernelDesc *kd = first_match(table, count, c, tile);
+            if (kd == nullptr) continue;
+            const int64_t pm = ceil_div(c.M, tile) * tile, pn = ceil_div(c.N, tile) * tile;
+            const KSplit ks = call_ksplit(c, kd);
+            const int64_t groups = (pm / tile) * (pn / tile) * ks.splits;
+            if (4 * c.M * c.N >= 3 * pm * pn && 4 * groups >= 3 * kComputeUnits) return kd;
+        }
+    }
     int smallest = 1 << 30;
     for (int i = 0; i < count; ++i) smallest = table[i].tile_m < smallest ? table[i].tile_m : smallest;
     for (int tile : {256, 128, 64}) {
@@ -181,8 +236,10 @@ gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc 
             const int64_t strips = ceil_div(c.N, kd->tile_n);
             pl.grid = strips * gemm::skinny_splits((int)strips, (int)c.K);
         } else {
-            pl.grid = ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n);
+            pl.splits = call_ksplit(c, kd).splits;
+            pl.grid = ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n) * pl.splits;
         }
+        if (pl.splits == 0) pl.splits = 1;
         *chosen = kd;
     }
     if (out) *out = pl;
@@ -230,7 +287,17 @@ gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
         p.ldc = c.ldc;
         p.alpha = c.alpha;
         p.beta = c.beta;
-        err = kd->launch_ws ? kd->launch_ws(p, c.ws, s) : kd->launch(p, s);
+        p.kchunk = 0;
+        p.partials = nullptr;
+        const KSplit ks = call_ksplit(c, kd);
+        if (ks.splits > 1) {
+            p.kchunk = ks.kchunk;
+            p.partials = static_cast<float *>(c.ws);
+            err = kd->launch(p, s);
+            if (err == hipSuccess) err = gemm::launch_splitk_reduce(p, s);
+        } else {
+            err = kd->launch_ws ? kd->launch_ws(p, c.ws, s) : kd->launch(p, s);
+        }
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -279,6 +346,14 @@ GEMM_API gemm_status gemm_f32_ws(int64_t M, int64_t N, int64_t K, float alpha, c
                0, stream);
 }
 
+GEMM_API gemm_status gemm_bf16f32_ws(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                     int64_t lda, const uint16_t *B, int64_t ldb, float beta, float *C,
+                                     int64_t ldc, void *workspace, int64_t workspace_bytes, gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                         workspace_bytes),
+               0, stream);
+}
+
 GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                                  const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
                                  int32_t force_kernel, void *workspace, int64_t workspace_bytes,
@@ -288,9 +363,17 @@ GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, c
 }
 
 GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K) {
-    if (dtype != GEMM_DTYPE_F32 || M <= 0 || M > 16 || N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim)
+    if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16F32) || M <= 0 || N <= 0 || K <= 0 ||
+        M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return 0;
     int64_t need = 0;
+    // Tiled K split: the largest tile gives the most slices.
+    Call c = make_call(dtype, M, N, K, 1.0f, nullptr, K, nullptr, N, 0.0f, nullptr, N);
+    for (int tile : {256, 128, 64}) {
+        const KSplit ks = tiled_ksplit(c, tile, tile);
+        need = ks.bytes > need ? ks.bytes : need;
+    }
+    if (dtype != GEMM_DTYPE_F32 || M > 16) return need;
     for (int i = 0; i < gemm::kF32SplitKernelCount; ++i) {
         const int64_t strips = ceil_div(N, gemm::kF32SplitKernels[i].tile_n);
         const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);
@@ -301,9 +384,11 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
 
 GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
                                      int64_t lda, const uint16_t *B, int64_t ldb, float beta, float *C,
-                                     int64_t ldc, int32_t force_kernel, gemm_stream_t stream) {
-    return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc), force_kernel,
-               stream);
+                                     int64_t ldc, int32_t force_kernel, void *workspace, int64_t workspace_bytes,
+                                     gemm_stream_t stream) {
+    return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                         workspace_bytes),
+               force_kernel, stream);
 }
 
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,

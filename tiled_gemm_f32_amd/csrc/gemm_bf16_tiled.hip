@@ -62,6 +62,7 @@ __device__ __forceinline__ int swz(int row, int ch) { return ch ^ (row & 7) ^ ((
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
 __global__ void __launch_bounds__(64 * WM * WN)
 bf16_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint16_t>(p);
     typedef Bf16Tiled<BM, BN, BK, WM, WN> Cfg;
 
     __shared__ __attribute__((aligned(16))) u32x4 lds_a[2][BM * Cfg::kChunks];
@@ -289,6 +290,7 @@ constexpr uint32_t kSelOdd = 0x07060302u;    // high halves of (x, y) -> (x.hi, 
 template <int GROUP_M>
 __global__ void __launch_bounds__(256)
 bf16_pipe_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint16_t>(p);
     constexpr int BM = 256, BN = 256, BK = 64;
     constexpr int kABuf = BM * BK * 2;          // bytes of one A panel (32 KB)
     constexpr int kBBuf = BN * BK * 2;          // bytes of one B panel (32 KB)
@@ -451,7 +453,7 @@ hipError_t launch_bf16_pipe(const GemmParams &p, hipStream_t stream) {
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_pipe_kernel<GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(256), argv, 0, stream);
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -490,6 +492,7 @@ __device__ __forceinline__ int ring_swz_a(int row) { return (row >> 2) & 3; }
 template <int NS, int GROUP_M>
 __global__ void __launch_bounds__(256)
 bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint16_t>(p);
     constexpr int BM = 256, BN = 256, BK = 32;
     constexpr int kA = BM * BK * 2;     // 16 KB of A per slice
     constexpr int kB = BN * BK * 2;     // 16 KB of B per slice
@@ -690,7 +693,7 @@ hipError_t launch_bf16_ring(const GemmParams &p, hipStream_t stream) {
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(256), argv, 0, stream);
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
@@ -699,7 +702,7 @@ hipError_t launch_bf16_tiled(const GemmParams &p, hipStream_t stream) {
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_tiled_kernel<BM, BN, BK, WM, WN, VA, VB, GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), argv, 0, stream);
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(64 * WM * WN), argv, 0, stream);
 }
 
 #define BF16_TILED(BM, BN, BK, WM, WN, VA, VB, G)                                             \

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_kernels.hpp"
+
 namespace gemm {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -126,5 +128,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= n, lgkmcnt = 0, expcnt unconstrained.
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | (((n >> 4) & 3) << 14); }
+
+
+// Rebase a workgroup of a K-split grid (gridDim.y > 1) onto its k range and
+// its partial-product slot; see GemmParams::kchunk.  T is the operand type.
+template <typename T>
+__device__ __forceinline__ void apply_k_split(GemmParams &p) {
+    if (p.kchunk <= 0) return;
+    const int kb = (int)blockIdx.y * p.kchunk;
+    p.A = static_cast<const T *>(p.A) + kb;
+    p.B = static_cast<const T *>(p.B) + (int64_t)kb * p.ldb;
+    p.K = min(p.K - kb, p.kchunk);
+    p.C = p.partials + (int64_t)blockIdx.y * p.M * p.N;
+    p.ldc = p.N;
+    p.alpha = 1.0f;
+    p.beta = 0.0f;
+}
 
 }  // namespace gemm

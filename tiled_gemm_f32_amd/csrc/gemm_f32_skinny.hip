@@ -291,6 +291,14 @@ splitk_reduce_kernel(GemmParams p, const float *partials, int splits) {
     *cp = v;
 }
 
+hipError_t launch_reduce(const GemmParams &p, const float *partials, int splits, hipStream_t stream) {
+    GemmParams args = p;
+    const int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
+    void *argv[] = {&args, (void *)&partials, &splits};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel), dim3((unsigned)blocks),
+                           dim3(256), argv, 0, stream);
+}
+
 template <int VEC, int VA, int WAVES, int UNROLL>
 hipError_t launch_f32_skinny(const GemmParams &p, hipStream_t stream) {
     const int strips = (p.N + 16 * VEC - 1) / (16 * VEC);
@@ -312,10 +320,7 @@ hipError_t launch_f32_skinny_splitk(const GemmParams &p, void *workspace, hipStr
         hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_splitk_kernel<CG, VA, WAVES, UNROLL>),
                         dim3((unsigned)strips, (unsigned)splits), dim3(64 * WAVES), argv, 0, stream);
     if (err != hipSuccess || splits == 1) return err;
-    const int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
-    void *rargv[] = {&args, &partials, &splits};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel), dim3((unsigned)blocks),
-                           dim3(256), rargv, 0, stream);
+    return launch_reduce(p, partials, splits, stream);
 }
 
 __global__ void __launch_bounds__(256)
@@ -365,6 +370,10 @@ const KernelDesc kF32SplitKernels[] = {
      nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 1>},
 };
 const int kF32SplitKernelCount = sizeof(kF32SplitKernels) / sizeof(kF32SplitKernels[0]);
+
+hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t stream) {
+    return launch_reduce(p, p.partials, k_splits(p), stream);
+}
 
 hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, hipStream_t stream) {
     const int64_t total = (int64_t)M * N;

@@ -71,6 +71,7 @@ struct F32Tiled {
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
 __global__ void __launch_bounds__(64 * WM * WN)
 f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<float>(p);
     typedef F32Tiled<BM, BN, BK, WM, WN, VA, VB, GROUP_M> Cfg;
     typedef F32Chunk<VA> CA;
     typedef F32Chunk<VB> CB;
@@ -236,6 +237,7 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
 template <int NS, int GROUP_M>
 __global__ void __launch_bounds__(256)
 f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<float>(p);
     static_assert(NS % 2 == 0, "the two A-fragment register sets alternate with the stage");
     constexpr int BM = 256, BN = 256, BK = 16, kSteps = 8;
     constexpr int kA = BM * BK * 4;     // 16 KB of A per slice
@@ -407,7 +409,7 @@ hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(256), argv, 0, stream);
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
@@ -416,7 +418,7 @@ hipError_t launch_f32_tiled(const GemmParams &p, hipStream_t stream) {
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     return hipLaunchKernel(reinterpret_cast<const void *>(&f32_tiled_kernel<BM, BN, BK, WM, WN, VA, VB, GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WM * WN), argv, 0, stream);
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(64 * WM * WN), argv, 0, stream);
 }
 
 #define F32_TILED(BM, BN, BK, WM, WN, VA, VB, G)                                              \

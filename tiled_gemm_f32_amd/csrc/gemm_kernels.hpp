@@ -20,9 +20,21 @@ struct GemmParams {
     int32_t lda, ldb;
     int64_t ldc;
     float alpha, beta;
+    // K split (0: none).  With kchunk > 0 the tiled kernels run on a grid of
+    // (tiles, ceil(K / kchunk)) workgroups; row y of the grid multiplies the
+    // k range [y*kchunk, min(K, (y+1)*kchunk)) and stores that partial product
+    // (alpha 1, beta 0) to partials + y*M*N with leading dimension N.
+    int32_t kchunk;
+    float *partials;
 };
 
+inline int k_splits(const GemmParams &p) { return p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1; }
+
 typedef hipError_t (*LaunchFn)(const GemmParams &p, hipStream_t stream);
+
+// C = alpha * (sum of the k_splits(p) partial products, in split order) +
+// beta * C, for the tiled kernels' K split (defined with the skinny kernels).
+hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t stream);
 typedef hipError_t (*LaunchWsFn)(const GemmParams &p, void *workspace, hipStream_t stream);
 
 // One row of the kernel table.
