@@ -200,6 +200,39 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
                             int32_t force_kernel, void *workspace, int64_t workspace_bytes,
                             gemm_stream_t stream);
 
+/*
+ * Per-shape tuning ("A GEMM Kernel, Step by Step", section "Six parameters,
+ * found by search": the best tile configuration for a shape is not
+ * derivable, so it is found by timing the candidates).
+ *
+ * gemm_autotune() times, on the caller's buffers and stream, every kernel
+ * that can run this call (reps calls each after one untimed call, with and
+ * without a K split when a workspace is given) and records the fastest in a
+ * process-wide table keyed by dtype, M, N, K, the operands' widest vector
+ * width and whether a workspace is passed.  It blocks until the timings are
+ * done.  C is used as scratch: its contents afterwards are unspecified (with
+ * beta != 0 every timed call updates it), so make the real call afterwards.
+ * `out` receives the plan that calls of this kind now take.  reps: 1..1000.
+ * Later calls with no forced kernel (and gemm_plan_query) use a recorded
+ * choice whenever it can run the call; otherwise the built-in rules choose.
+ * The table is guarded by a mutex; autotuning concurrently with calls on
+ * other threads is safe, though the timings then include their load.
+ *
+ * gemm_tuning_save() writes the table as text, one line per entry, naming
+ * kernels (not ids); gemm_tuning_load() adds the entries of such a file
+ * (entries naming unknown kernels are skipped) and returns how many it
+ * added, or -1 if the file cannot be read or parsed.
+ */
+GEMM_API gemm_status gemm_autotune(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
+                                   const void *A, int64_t lda, const void *B, int64_t ldb,
+                                   float beta, float *C, int64_t ldc,
+                                   void *workspace, int64_t workspace_bytes, int32_t reps,
+                                   gemm_stream_t stream, gemm_plan *out);
+GEMM_API int32_t gemm_tuning_count(void);
+GEMM_API void gemm_tuning_clear(void);
+GEMM_API gemm_status gemm_tuning_save(const char *path);
+GEMM_API int32_t gemm_tuning_load(const char *path);
+
 #ifdef __cplusplus
 }
 #endif

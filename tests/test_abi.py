@@ -291,3 +291,75 @@ def test_workspace_tiled_k_split_plan():
     assert plan(F32, 16, 16, 0, ws=1 << 30)[1]["splits"] == 0
 
 
+
+
+# ----------------------------------------------------------------------------- tuning table
+
+def _kid(name):
+    return [k["id"] for k in tg.kernels() if k["name"] == name][0]
+
+
+def test_tuning_table_load_save_and_plan(tmp_path):
+    """A tuning table written as text steers the automatic choice for its key
+    (dtype, shape, alignment class, workspace presence) and only that key."""
+    tg.gemm_tuning_clear()
+    assert tg.gemm_tuning_count() == 0
+    f = tmp_path / "table.txt"
+    f.write_text("# comment\n"
+                 "0 1024 1024 1024 4 4 0 f32_mfma32_128x128x16_w2x2_a4b4 0 0.5\n"
+                 "1 2048 2048 8192 8 8 1 bf16_mfma32_128x128x64_w2x2_a8b8 0 0.1\n"
+                 "0 512 512 512 4 4 0 no_such_kernel 0 0.1\n")
+    assert tg.gemm_tuning_load(str(f)) == 2          # the unknown kernel is skipped
+    assert tg.gemm_tuning_count() == 2
+    st, p = plan(F32, 1024, 1024, 1024)
+    assert st == OK and p["kernel_id"] == _kid("f32_mfma32_128x128x16_w2x2_a4b4")
+    # Another alignment class (A not 16-byte aligned) or shape: the built-in choice.
+    assert plan(F32, 1024, 1024, 1024, A=PA + 4)[1]["kernel_id"] != _kid("f32_mfma32_128x128x16_w2x2_a4b4")
+    assert plan(F32, 1024, 1024, 1032)[1]["kernel_id"] != _kid("f32_mfma32_128x128x16_w2x2_a4b4")
+    # A recorded "no split" is honoured even with a workspace large enough for one.
+    st, p = plan(BF16, 2048, 2048, 8192, ws=1 << 30)
+    assert st == OK and p["kernel_id"] == _kid("bf16_mfma32_128x128x64_w2x2_a8b8") and p["splits"] == 1
+    st, p = plan(BF16, 2048, 2048, 8192)              # no workspace: another key
+    assert p["kernel_id"] != _kid("bf16_mfma32_128x128x64_w2x2_a8b8") or p["splits"] == 1
+    # Forced kernels ignore the table.
+    other = _kid("f32_mfma32_64x64x16_w2x2_a4b4")
+    assert plan(F32, 1024, 1024, 1024, force=other)[1]["kernel_id"] == other
+    # Save and reload round trip.
+    out = tmp_path / "saved.txt"
+    assert tg.gemm_tuning_save(str(out)) == OK
+    lines = [l for l in out.read_text().splitlines() if not l.startswith("#")]
+    assert len(lines) == 2 and all(len(l.split()) == 10 for l in lines)
+    tg.gemm_tuning_clear()
+    assert tg.gemm_tuning_count() == 0
+    assert tg.gemm_tuning_load(str(out)) == 2
+    assert plan(F32, 1024, 1024, 1024)[1]["kernel_id"] == _kid("f32_mfma32_128x128x16_w2x2_a4b4")
+    tg.gemm_tuning_clear()
+
+
+def test_tuning_table_entry_that_cannot_run_is_ignored(tmp_path):
+    """A recorded kernel that cannot run the call (here a split-K kernel
+    recorded under the no-workspace key) is ignored: the built-in rules choose."""
+    tg.gemm_tuning_clear()
+    f = tmp_path / "t.txt"
+    f.write_text("0 16 8192 8192 4 4 0 f32_skinny_splitk_n128_a4_w8_u1 0 0.04\n")
+    assert tg.gemm_tuning_load(str(f)) == 1
+    st, p = plan(F32, 16, 8192, 8192)
+    assert st == OK and p["path"] == tg.GEMM_PATH_SKINNY
+    tg.gemm_tuning_clear()
+
+
+def test_tuning_load_errors(tmp_path):
+    tg.gemm_tuning_clear()
+    assert tg.gemm_tuning_load(str(tmp_path / "missing.txt")) == -1
+    bad = tmp_path / "bad.txt"
+    bad.write_text("0 16 16\n")
+    assert tg.gemm_tuning_load(str(bad)) == -1
+    assert tg.gemm_tuning_count() == 0
+    assert tg.gemm_tuning_save(str(tmp_path / "no_dir" / "x.txt")) == tg.GEMM_ERR_INVALID_ARG
+    # Autotune validates its arguments before touching a device.
+    st, _ = tg.gemm_autotune(F32, 64, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 0)
+    assert st == tg.GEMM_ERR_INVALID_ARG                 # reps must be 1..1000
+    st, _ = tg.gemm_autotune(F32, -1, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 5)
+    assert st == tg.GEMM_ERR_INVALID_ARG
+    st, p = tg.gemm_autotune(F32, 0, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 5)
+    assert st == OK and p["path"] == tg.GEMM_PATH_NONE   # nothing to tune, no device needed

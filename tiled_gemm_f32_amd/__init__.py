@@ -14,11 +14,13 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
     gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
-    gemm_plan_query, gemm_status_string, gemm_workspace_size, load)
+    gemm_plan_query, gemm_status_string, gemm_workspace_size, gemm_autotune, gemm_tuning_count, gemm_tuning_clear,
+    gemm_tuning_save, gemm_tuning_load, load)
 
 __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
-           "gemm_plan_query", "GemmError", "kernels", "workspace"]
+           "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune", "gemm_tuning_count",
+           "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load"]
 
 
 def _ld(t, what: str) -> int:
@@ -81,6 +83,24 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
     return C
+
+
+def autotune(A, B, C, alpha: float = 1.0, beta: float = 0.0, ws=None, reps: int = 5, stream=None) -> dict:
+    """Time every kernel that can run this call and record the fastest for
+    calls of the same kind; returns the plan they now take.  C is scratch."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    dt = GEMM_DTYPE_F32 if A.dtype == torch.float32 else GEMM_DTYPE_BF16F32
+    wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    with torch.cuda.device(A.device):
+        st, pl = gemm_autotune(dt, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"),
+                               float(beta), C.data_ptr(), _ld(C, "C"), wp, wb, reps, stream)
+    if st != GEMM_OK:
+        raise GemmError(st, "autotune")
+    return pl
 
 
 def kernels() -> list:

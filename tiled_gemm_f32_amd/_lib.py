@@ -32,7 +32,8 @@ GEMM_DTYPE_BF16F32 = 1
 # Every entry point include/gemm.h declares.
 EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
-            "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws")
+            "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws", "gemm_autotune", "gemm_tuning_count",
+            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load")
 
 
 class KernelInfo(ctypes.Structure):
@@ -89,6 +90,17 @@ def load() -> ctypes.CDLL:
     lib.gemm_plan_query.argtypes = [i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32, i64,
                                     ctypes.POINTER(Plan)]
     lib.gemm_plan_query.restype = ctypes.c_int
+    lib.gemm_autotune.argtypes = [i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp, i64, i32, vp,
+                                  ctypes.POINTER(Plan)]
+    lib.gemm_autotune.restype = ctypes.c_int
+    lib.gemm_tuning_count.argtypes = []
+    lib.gemm_tuning_count.restype = i32
+    lib.gemm_tuning_clear.argtypes = []
+    lib.gemm_tuning_clear.restype = None
+    lib.gemm_tuning_save.argtypes = [ctypes.c_char_p]
+    lib.gemm_tuning_save.restype = ctypes.c_int
+    lib.gemm_tuning_load.argtypes = [ctypes.c_char_p]
+    lib.gemm_tuning_load.restype = i32
     _lib = lib
     return lib
 
@@ -150,3 +162,28 @@ def gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_k
     st = load().gemm_plan_query(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel,
                                 workspace_bytes, ctypes.byref(pl))
     return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
+
+
+def gemm_autotune(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=0, workspace_bytes=0, reps=5,
+                  stream=0):
+    """(status, plan dict) after timing every candidate; C is scratch."""
+    pl = Plan()
+    st = load().gemm_autotune(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, reps,
+                              stream, ctypes.byref(pl))
+    return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
+
+
+def gemm_tuning_count() -> int:
+    return int(load().gemm_tuning_count())
+
+
+def gemm_tuning_clear() -> None:
+    load().gemm_tuning_clear()
+
+
+def gemm_tuning_save(path: str) -> int:
+    return load().gemm_tuning_save(path.encode())
+
+
+def gemm_tuning_load(path: str) -> int:
+    return int(load().gemm_tuning_load(path.encode()))

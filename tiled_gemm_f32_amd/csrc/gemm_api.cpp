@@ -11,7 +11,12 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
 
 #include "gemm.h"
 #include "gemm_kernels.hpp"
@@ -206,10 +211,58 @@ const KernelDesc *choose(const Call &c) {
     return first_match(table, count, c, 0);
 }
 
-gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc **chosen) {
+// Per-shape tuning ("A GEMM Kernel, Step by Step", "Six parameters, found by
+// search": the best kernel for a shape is found by timing the candidates).
+// gemm_autotune() times every kernel that can run a call, with and without a
+// K split, and records the fastest here; calls of the same dtype, shape,
+// operand alignment class and workspace presence then take that choice
+// whenever it still fits the call.
+struct TuneKey {
+    int32_t dtype;
+    int64_t M, N, K;
+    int32_t vec_a, vec_b;    // widest vector loads A and B allow
+    int32_t has_ws;
+    bool operator<(const TuneKey &o) const {
+        return std::tie(dtype, M, N, K, vec_a, vec_b, has_ws) <
+               std::tie(o.dtype, o.M, o.N, o.K, o.vec_a, o.vec_b, o.has_ws);
+    }
+};
+struct TuneEntry {
+    int32_t kernel_id;
+    int32_t split;           // 1: K split allowed (when the workspace suffices); 0: never
+    float ms;                // measured time per call
+};
+std::mutex g_tune_mu;
+std::map<TuneKey, TuneEntry> g_tuned;
+
+int max_vec_b(const Call &c) {
+    const int w = c.dtype == GEMM_DTYPE_F32 ? 4 : 8;
+    return vec_b_ok(c, w) ? w : 1;
+}
+
+TuneKey tune_key(const Call &c) {
+    return TuneKey{c.dtype, c.M, c.N, c.K, max_vec_a(c), max_vec_b(c), c.ws != nullptr ? 1 : 0};
+}
+
+// A tuned choice for this call, if one was recorded and still fits it.
+bool tuned_choice(const Call &c, const KernelDesc **kd, bool *allow_split) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    auto it = g_tuned.find(tune_key(c));
+    if (it == g_tuned.end()) return false;
+    const KernelDesc *k = kernel_by_id(it->second.kernel_id);
+    if (k == nullptr || !kernel_runs(k, c)) return false;
+    *kd = k;
+    *allow_split = it->second.split != 0;
+    return true;
+}
+
+// The plan of a call: the kernel (forced, tuned or chosen) and its K split.
+gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc **chosen, KSplit *split,
+                 bool use_tuned = true, bool allow_split = true) {
     gemm_plan pl;
     std::memset(&pl, 0, sizeof pl);
     *chosen = nullptr;
+    *split = KSplit{1, 0, 0};
     gemm_status st = validate(c);
     if (st != GEMM_OK) return st;
     if (force < 0 || (force > 0 && kernel_by_id(force) == nullptr)) return GEMM_ERR_INVALID_ARG;
@@ -220,7 +273,12 @@ gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc 
         pl.threads = 256;
         pl.grid = ceil_div(c.M * c.N, 256) < 4096 ? ceil_div(c.M * c.N, 256) : 4096;
     } else {
-        const KernelDesc *kd = force > 0 ? kernel_by_id(force) : choose(c);
+        const KernelDesc *kd = nullptr;
+        if (force > 0) {
+            kd = kernel_by_id(force);
+        } else if (!(use_tuned && tuned_choice(c, &kd, &allow_split))) {
+            kd = choose(c);
+        }
         if (kd == nullptr || !kernel_runs(kd, c)) return GEMM_ERR_UNSUPPORTED;
         pl.path = kd->path;
         pl.kernel_id = id_of(kd);
@@ -236,7 +294,8 @@ gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc 
             const int64_t strips = ceil_div(c.N, kd->tile_n);
             pl.grid = strips * gemm::skinny_splits((int)strips, (int)c.K);
         } else {
-            pl.splits = call_ksplit(c, kd).splits;
+            if (allow_split) *split = call_ksplit(c, kd);
+            pl.splits = split->splits;
             pl.grid = ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n) * pl.splits;
         }
         if (pl.splits == 0) pl.splits = 1;
@@ -263,14 +322,20 @@ gemm_status check_device() {
     return ok ? GEMM_OK : GEMM_ERR_DEVICE;
 }
 
+gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, const KSplit &ks, hipStream_t s);
+
 gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
     gemm_plan pl;
     const KernelDesc *kd = nullptr;
-    gemm_status st = plan(c, force, &pl, &kd);
+    KSplit ks;
+    gemm_status st = plan(c, force, &pl, &kd, &ks);
     if (st != GEMM_OK || pl.path == GEMM_PATH_NONE) return st;
     st = check_device();
     if (st != GEMM_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return launch(c, pl, kd, ks, static_cast<hipStream_t>(stream));
+}
+
+gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, const KSplit &ks, hipStream_t s) {
     hipError_t err;
     if (pl.path == GEMM_PATH_SCALE) {
         err = gemm::launch_scale_c(c.beta, c.C, (int32_t)c.M, (int32_t)c.N, c.ldc, s);
@@ -289,7 +354,6 @@ gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
         p.beta = c.beta;
         p.kchunk = 0;
         p.partials = nullptr;
-        const KSplit ks = call_ksplit(c, kd);
         if (ks.splits > 1) {
             p.kchunk = ks.kchunk;
             p.partials = static_cast<float *>(c.ws);
@@ -300,6 +364,65 @@ gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
         }
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+// Mean time of `reps` calls of one candidate (after one untimed call), by
+// HIP events on the call's stream.  GEMM_ERR_UNSUPPORTED if it cannot run.
+gemm_status time_candidate(const Call &c, const KernelDesc *kd, bool allow_split, int reps, hipStream_t s,
+                           float *ms, bool *split_used) {
+    gemm_plan pl;
+    const KernelDesc *k = nullptr;
+    KSplit ks;
+    gemm_status st = plan(c, id_of(kd), &pl, &k, &ks, false, allow_split);
+    if (st != GEMM_OK) return st;
+    *split_used = ks.splits > 1;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return GEMM_ERR_LAUNCH;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return GEMM_ERR_LAUNCH;
+    }
+    st = launch(c, pl, k, ks, s);
+    if (st == GEMM_OK && hipEventRecord(e0, s) != hipSuccess) st = GEMM_ERR_LAUNCH;
+    for (int r = 0; st == GEMM_OK && r < reps; ++r) st = launch(c, pl, k, ks, s);
+    if (st == GEMM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess))
+        st = GEMM_ERR_LAUNCH;
+    float total = 0.0f;
+    if (st == GEMM_OK && hipEventElapsedTime(&total, e0, e1) != hipSuccess) st = GEMM_ERR_LAUNCH;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    *ms = total / (float)reps;
+    return st;
+}
+
+gemm_status autotune(const Call &c, int reps, hipStream_t s, gemm_plan *out) {
+    if (reps < 1 || reps > 1000 || out == nullptr) return GEMM_ERR_INVALID_ARG;
+    const KernelDesc *kd = nullptr;
+    KSplit ks;
+    gemm_status st = plan(c, 0, out, &kd, &ks, false);
+    if (st != GEMM_OK || out->path == GEMM_PATH_NONE || out->path == GEMM_PATH_SCALE) return st;
+    st = check_device();
+    if (st != GEMM_OK) return st;
+    TuneEntry best{0, 0, 0.0f};
+    for (int32_t id = 1; id <= table_size(); ++id) {
+        const KernelDesc *cand = kernel_by_id(id);
+        if (cand->dtype != c.dtype || !kernel_runs(cand, c)) continue;
+        for (int split = 0; split < 2; ++split) {
+            float ms = 0.0f;
+            bool used = false;
+            st = time_candidate(c, cand, split == 1, reps, s, &ms, &used);
+            if (st == GEMM_ERR_UNSUPPORTED) break;
+            if (st != GEMM_OK) return st;
+            if (split == 1 && !used) break;            // no split possible: same as the first timing
+            if (best.kernel_id == 0 || ms < best.ms) best = TuneEntry{id, split, ms};
+        }
+    }
+    if (best.kernel_id == 0) return GEMM_ERR_UNSUPPORTED;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        g_tuned[tune_key(c)] = best;
+    }
+    return plan(c, 0, out, &kd, &ks);
 }
 
 Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, const void *A, int64_t lda,
@@ -399,8 +522,82 @@ GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_
     const KernelDesc *kd = nullptr;
     // Planning never touches the workspace; a non-null stand-in marks that one is passed.
     void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
+    KSplit ks;
     return plan(make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes), force_kernel,
-                out, &kd);
+                out, &kd, &ks);
+}
+
+GEMM_API gemm_status gemm_autotune(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+                                   int64_t lda, const void *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                                   void *workspace, int64_t workspace_bytes, int32_t reps, gemm_stream_t stream,
+                                   gemm_plan *out) {
+    return autotune(make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes),
+                    reps, static_cast<hipStream_t>(stream), out);
+}
+
+GEMM_API int32_t gemm_tuning_count(void) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    return (int32_t)g_tuned.size();
+}
+
+GEMM_API void gemm_tuning_clear(void) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tuned.clear();
+}
+
+// One line per entry: dtype M N K vec_a vec_b has_workspace kernel_name split ms.
+// Kernels are named, not numbered, so a table survives a reordered kernel list.
+GEMM_API gemm_status gemm_tuning_save(const char *path) {
+    if (path == nullptr) return GEMM_ERR_INVALID_ARG;
+    std::FILE *f = std::fopen(path, "w");
+    if (f == nullptr) return GEMM_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    bool ok = std::fprintf(f, "# libgemm tuning table v1: dtype M N K vec_a vec_b has_ws kernel split ms\n") > 0;
+    for (const auto &kv : g_tuned) {
+        const TuneKey &k = kv.first;
+        const KernelDesc *kd = kernel_by_id(kv.second.kernel_id);
+        ok = ok && kd != nullptr &&
+             std::fprintf(f, "%d %lld %lld %lld %d %d %d %s %d %.6f\n", k.dtype, (long long)k.M, (long long)k.N,
+                          (long long)k.K, k.vec_a, k.vec_b, k.has_ws, kd->name, kv.second.split,
+                          (double)kv.second.ms) > 0;
+    }
+    ok = (std::fclose(f) == 0) && ok;
+    return ok ? GEMM_OK : GEMM_ERR_INVALID_ARG;
+}
+
+GEMM_API int32_t gemm_tuning_load(const char *path) {
+    if (path == nullptr) return -1;
+    std::FILE *f = std::fopen(path, "r");
+    if (f == nullptr) return -1;
+    std::vector<std::pair<TuneKey, TuneEntry>> rows;
+    char line[512];
+    bool ok = true;
+    while (ok && std::fgets(line, sizeof line, f) != nullptr) {
+        if (line[0] == '#' || line[0] == '\n') continue;
+        TuneKey k;
+        long long M, N, K;
+        char name[128];
+        int split;
+        double ms;
+        if (std::sscanf(line, "%d %lld %lld %lld %d %d %d %127s %d %lf", &k.dtype, &M, &N, &K, &k.vec_a, &k.vec_b,
+                        &k.has_ws, name, &split, &ms) != 10) {
+            ok = false;
+            break;
+        }
+        k.M = M;
+        k.N = N;
+        k.K = K;
+        int32_t id = 0;
+        for (int32_t i = 1; i <= table_size(); ++i)
+            if (std::strcmp(kernel_by_id(i)->name, name) == 0) id = i;
+        if (id == 0 || kernel_by_id(id)->dtype != k.dtype) continue;     // unknown or mismatched kernel: skip
+        rows.push_back({k, TuneEntry{id, split != 0 ? 1 : 0, (float)ms}});
+    }
+    std::fclose(f);
+    if (!ok) return -1;
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    for (const auto &r : rows) g_tuned[r.first] = r.second;
+    return (int32_t)rows.size();
 }
 
 GEMM_API int32_t gemm_kernel_count(void) { return table_size(); }
