@@ -65,13 +65,23 @@ KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_
                   "f32_skinny": "gemm_f32_skinny.hip"}
 
 
+# Headers every kernel source includes: a change there changes the kernels too.
+KERNEL_HEADERS = [os.path.join("tiled_gemm_f32_amd", "csrc", "gemm_device.hpp"),
+                  os.path.join("tiled_gemm_f32_amd", "csrc", "gemm_kernels.hpp"),
+                  os.path.join("include", "gemm.h")]
+
+
 def kernel_source_sha(kernel_name: str):
-    """sha256 of the source file a kernel is built from (to spot stale counter data)."""
+    """sha256 over the source file a kernel is built from and the shared
+    headers it includes (to spot stale counter data)."""
     import hashlib
     for prefix, src in KERNEL_SOURCES.items():
         if kernel_name.startswith(prefix):
-            with open(os.path.join(ROOT, "tiled_gemm_f32_amd", "csrc", src), "rb") as f:
-                return hashlib.sha256(f.read()).hexdigest()
+            h = hashlib.sha256()
+            for path in [os.path.join("tiled_gemm_f32_amd", "csrc", src)] + KERNEL_HEADERS:
+                with open(os.path.join(ROOT, path), "rb") as f:
+                    h.update(f.read())
+            return h.hexdigest()
     return None
 
 

@@ -187,18 +187,63 @@ GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_
                             float beta, const float *C, int64_t ldc,
                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out);
 
-/* gemm_f32_ws / gemm_bf16f32_ws with a forced kernel (force_kernel as above). */
+/*
+ * Fused epilogue ("Tiled matrix multiplication", section "Implementation
+ * notes": bias, activation and scaling are applied while the tile is still
+ * in registers, which saves a full read and write of C; "Efficiency",
+ * epilogue fusion).  With an epilogue the call computes
+ *
+ *     C[i][j] = act(alpha * (A x B)[i][j] + beta * C0[i][j] + bias[j])
+ *
+ * bias: N floats (4-byte aligned device memory, read only), or NULL for no
+ * bias.  activation: GEMM_ACT_NONE, GEMM_ACT_RELU (max(x, 0), NaN stays
+ * NaN) or GEMM_ACT_GELU (x * Phi(x) with the normal CDF, erf form).  The
+ * quick returns apply too: K == 0 or alpha == 0 gives act(beta*C0 + bias),
+ * with C0 not read when beta == 0.  A NULL descriptor is the plain call.
+ * Workspace arguments are those of gemm_f32_ws / gemm_bf16f32_ws (a K split
+ * applies the epilogue once, in its reduce step).
+ * Errors: GEMM_ERR_INVALID_ARG for an unknown activation or a misaligned
+ * bias, besides those of the plain call.
+ */
+typedef enum gemm_activation {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1,
+    GEMM_ACT_GELU = 2
+} gemm_activation;
+
+typedef struct gemm_epilogue {
+    const float *bias;       /* N floats or NULL */
+    int32_t activation;      /* gemm_activation */
+} gemm_epilogue;
+
+GEMM_API gemm_status gemm_f32_epi(int64_t M, int64_t N, int64_t K, float alpha,
+                                  const float *A, int64_t lda, const float *B, int64_t ldb,
+                                  float beta, float *C, int64_t ldc, const gemm_epilogue *epilogue,
+                                  void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
+
+GEMM_API gemm_status gemm_bf16f32_epi(int64_t M, int64_t N, int64_t K, float alpha,
+                                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                                      float beta, float *C, int64_t ldc, const gemm_epilogue *epilogue,
+                                      void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
+
+/*
+ * gemm_f32_epi / gemm_bf16f32_epi with a forced kernel (force_kernel as in
+ * gemm_plan_query; 0 lets the library choose), for tests and tuning.  A NULL
+ * epilogue is the plain call, so with one these are gemm_f32_ws /
+ * gemm_bf16f32_ws with a forced kernel.
+ */
 GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
                         const float *A, int64_t lda, const float *B, int64_t ldb,
                         float beta, float *C, int64_t ldc,
-                        int32_t force_kernel, void *workspace, int64_t workspace_bytes,
-                        gemm_stream_t stream);
+                        int32_t force_kernel, const gemm_epilogue *epilogue,
+                        void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
 
 GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha,
                             const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                             float beta, float *C, int64_t ldc,
-                            int32_t force_kernel, void *workspace, int64_t workspace_bytes,
-                            gemm_stream_t stream);
+                            int32_t force_kernel, const gemm_epilogue *epilogue,
+                            void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
+
 
 /*
  * Per-shape tuning ("A GEMM Kernel, Step by Step", section "Six parameters,

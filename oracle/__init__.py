@@ -28,8 +28,13 @@ _SRC = os.path.join(_HERE, "gemm_ref.c")
 _LIB = os.path.join(_HERE, "libgemm_ref.so")
 
 # -O2 without fast-math; contraction off so every operation is a plain IEEE op.
-BUILD_CMD = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-             "-ffp-contract=off", "-fno-fast-math", "-o", _LIB, _SRC]
+BUILD_FLAGS = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-ffp-contract=off", "-fno-fast-math"]
+
+
+def build_cmd(out: str, src: str) -> list:
+    """The gcc command that builds `src` into the shared library `out`."""
+    return BUILD_FLAGS + ["-o", out, src, "-lm"]
 
 _lib = None
 
@@ -38,8 +43,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle shared library; returns its path."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        cmd = BUILD_CMD[:-3] + ["-o", tmp, _SRC]
-        subprocess.run(cmd, check=True)
+        subprocess.run(build_cmd(tmp, _SRC), check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -61,6 +65,8 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = None
+    lib.epilogue_ref.argtypes = [i64, i64, vp, i64, vp, ctypes.c_int]
+    lib.epilogue_ref.restype = None
     lib.gemm_ref_num_threads.argtypes = []
     lib.gemm_ref_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -121,6 +127,36 @@ def gemm_ref(A, B, alpha=1.0, beta=0.0, C0=None) -> np.ndarray:
 def gemm_absbound(A, B, alpha=1.0, beta=0.0, C0=None) -> np.ndarray:
     """fp64 ``|alpha| * |A| @ |B| + |beta| * |C0|`` -- the error-ratio denominator."""
     return _run("absbound", A, B, alpha, beta, C0)
+
+
+# The oracle's own names for the activations (see epilogue_ref in gemm_ref.c).
+ACTIVATIONS = {"none": 0, "relu": 1, "gelu": 2}
+
+
+def epilogue_ref(Z, bias=None, activation="none") -> np.ndarray:
+    """fp64 ``act(Z + bias)`` with the bias broadcast along rows.
+
+    ``Z`` is a finished GEMM result (any float array, M x N); ``bias`` is
+    None or N float32 values; ``activation`` is "none", "relu" (max(z, 0),
+    NaN kept) or "gelu" (z * Phi(z), erf form).  Returns a new array.
+    """
+    out = np.array(Z, dtype=np.float64, order="C", copy=True)
+    if out.ndim != 2:
+        raise ValueError("Z must be 2-D")
+    M, N = out.shape
+    bp = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError(f"bias must hold {N} values")
+        bp = _ptr(bias)
+    _load().epilogue_ref(M, N, _ptr(out), max(N, 1), bp, ACTIVATIONS[activation])
+    return out
+
+
+def gemm_epilogue_ref(A, B, alpha=1.0, beta=0.0, C0=None, bias=None, activation="none") -> np.ndarray:
+    """fp64 ``act(alpha * A @ B + beta * C0 + bias)``: gemm_ref, then epilogue_ref."""
+    return epilogue_ref(gemm_ref(A, B, alpha, beta, C0), bias, activation)
 
 
 def num_threads() -> int:

@@ -36,6 +36,7 @@
  * the tests, the smoke check and the benchmark's CPU-baseline leg may load
  * it.
  */
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -171,6 +172,42 @@ void gemm_absbound_bf16in(int64_t M, int64_t N, int64_t K, double alpha,
                 v += ab * (c < 0 ? -c : c);
             }
             row[j] = v;
+        }
+    }
+}
+
+/*
+ * Fused epilogue, applied to a finished GEMM result Z (M x N, fp64, row
+ * stride ldz) in place:
+ *
+ *     Z[i][j] <- act(Z[i][j] + bias[j])
+ *
+ * ("Tiled matrix multiplication", sections "Efficiency" and "Implementation
+ * notes": bias and activation are applied to the GEMM result while it is
+ * still in registers.)  The pages name the operations but define neither
+ * activation; the readings taken are the usual ones:
+ *   act == 0  identity;
+ *   act == 1  ReLU, max(z, 0); a NaN compares false and is kept;
+ *   act == 2  GELU, z * Phi(z) with Phi the standard normal CDF, written
+ *             through the error function: Phi(z) = (1 + erf(z / sqrt 2)) / 2,
+ *             using the C library's double erf.
+ * bias is NULL (no bias) or N floats, widened exactly to double.
+ */
+void epilogue_ref(int64_t M, int64_t N, double *Z, int64_t ldz, const float *bias, int act)
+{
+    const double inv_sqrt2 = 1.0 / sqrt(2.0);
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double z = Z[i * ldz + j];
+            if (bias != NULL)
+                z += (double)bias[j];
+            if (act == 1) {
+                if (z < 0.0)
+                    z = 0.0;
+            } else if (act == 2) {
+                z = 0.5 * z * (1.0 + erf(z * inv_sqrt2));
+            }
+            Z[i * ldz + j] = z;
         }
     }
 }

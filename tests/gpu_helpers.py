@@ -45,11 +45,13 @@ def needs_workspace(kernel: int) -> bool:
     return kernel > 0 and tg.gemm_kernel_query(kernel)["path"] == tg.GEMM_PATH_SKINNY_SPLITK
 
 
-def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c_fill=None, ws=None):
+def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c_fill=None, ws=None,
+             bias=None, activation=None):
     """Run the library on host inputs; returns (C as float32 numpy, C device view, C buffer).
 
     A zero-filled workspace is allocated when a workspace kernel is forced
-    and none is given."""
+    and none is given.  bias (host float32, N values) and activation are
+    passed to the fused epilogue."""
     Ad, _a = padded_device(A, pad[0], offset[0])
     Bd, _b = padded_device(B, pad[1], offset[1])
     if c_fill is None:
@@ -59,7 +61,8 @@ def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c
     if ws is None and needs_workspace(kernel):
         M, K = A.shape
         ws = tg.workspace(M, B.shape[1], K)
-    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel, ws=ws)
+    bd = bias.to("cuda") if bias is not None else None
+    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel, ws=ws, bias=bd, activation=activation)
     torch.cuda.synchronize()
     return Cd.cpu().numpy(), Cd, cbuf
 

@@ -121,10 +121,35 @@ def test_argument_errors_return_before_any_device_call():
     lib = _lib.load()
     assert tg.gemm_f32(-1, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, 0) == INVALID
     assert tg.gemm_bf16f32(4, 4, 8, 1.0, PA, 7, PB, 4, 0.0, PC, 4, 0) == INVALID
-    assert tg.gemm_f32_ex(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, -5, 0, 0, 0) == INVALID
+    assert tg.gemm_f32_ex(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, -5, None, 0, 0, 0) == INVALID
     assert tg.gemm_f32_ws(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, PC + 2, 64, 0) == INVALID   # misaligned ws
     assert tg.gemm_f32_ws(4, 4, 4, 1.0, PA, 4, PB, 4, 0.0, PC, 4, PC, -1, 0) == INVALID
     assert lib is not None
+
+
+def test_epilogue_argument_errors():
+    """An unknown activation or a bias not 4-byte aligned is rejected on the
+    host; a NULL descriptor and a well-formed one are accepted (M == 0 is a
+    no-op, so nothing reaches the device)."""
+    for fn, a, b in ((tg.gemm_f32_epi, PA, PB), (tg.gemm_bf16f32_epi, PA, PB)):
+        args = (4, 8, 8, 1.0, a, 8, b, 8, 0.0, PC, 8)
+        for act in (-1, 3, 99):
+            assert fn(*args, tg.Epilogue(None, act), 0, 0, 0) == INVALID, act
+        assert fn(*args, tg.Epilogue(PC + 2, tg.GEMM_ACT_RELU), 0, 0, 0) == INVALID
+        empty = (0,) + args[1:]
+        assert fn(*empty, None, 0, 0, 0) == OK
+        for act in (tg.GEMM_ACT_NONE, tg.GEMM_ACT_RELU, tg.GEMM_ACT_GELU):
+            assert fn(*empty, tg.Epilogue(PC, act), 0, 0, 0) == OK
+    assert tg.gemm_f32_ex(4, 8, 8, 1.0, PA, 8, PB, 8, 0.0, PC, 8, 0, tg.Epilogue(None, 5), 0, 0, 0) == INVALID
+    assert tg.gemm_bf16f32_ex(4, 8, 8, 1.0, PA, 8, PB, 8, 0.0, PC, 8, 0, (PC + 1, 0), 0, 0, 0) == INVALID
+
+
+def test_activation_codes_match_header():
+    with open(HEADER) as f:
+        text = f.read()
+    for name in ("GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU"):
+        m = re.search(rf"{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(tg, name), name
 
 
 # ----------------------------------------------------------------------------- quick returns

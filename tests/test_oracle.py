@@ -383,6 +383,107 @@ def test_absbound_dominates_result_and_equals_gemm_of_abs():
     np.testing.assert_array_equal(D, oracle.gemm_ref(np.abs(A), np.abs(B), 1.5, 0.25, np.abs(C0)))
 
 
+# ----------------------------------------------------------------------------- fused epilogue
+# act(Z + bias) on a finished GEMM result ("Tiled matrix multiplication",
+# "Efficiency" and "Implementation notes").  ReLU and GELU are pinned by
+# closed forms, normal-table values, the identity Phi(x) + Phi(-x) = 1 and
+# scipy's normal CDF (the Cephes ndtr, code independent of the C library's
+# erf that the oracle calls).
+
+PHI_1 = 0.8413447460685429          # standard normal CDF at 1 (normal tables)
+Z975 = 1.959963984540054            # the 97.5% quantile of the standard normal
+
+
+def test_epilogue_none_is_identity():
+    Z = np.array([[-3.0, -0.0, 0.0, 2.5, np.inf, -np.inf, np.nan]])
+    out = oracle.epilogue_ref(Z)
+    np.testing.assert_array_equal(out, Z)
+    assert np.signbit(out[0, 1]) and not np.signbit(out[0, 2])
+
+
+def test_relu_closed_forms():
+    Z = np.array([[-3.0, -1e-300, 0.0, 2.5, 1e300, np.inf, -np.inf, np.nan]])
+    out = oracle.epilogue_ref(Z, activation="relu")
+    np.testing.assert_array_equal(out, [[0.0, 0.0, 0.0, 2.5, 1e300, np.inf, 0.0, np.nan]])
+
+
+def test_relu_splits_into_positive_and_negative_parts():
+    rng = np.random.default_rng(40)
+    x = rng.normal(size=(7, 9))
+    pos = oracle.epilogue_ref(x, activation="relu")
+    neg = oracle.epilogue_ref(-x, activation="relu")
+    np.testing.assert_array_equal(pos - neg, x)            # x = x+ - x-
+    np.testing.assert_array_equal(pos * neg, np.zeros_like(x))
+    assert np.all(pos >= 0)
+
+
+def test_gelu_table_values():
+    Z = np.array([[0.0, 1.0, -1.0, Z975, -Z975, 10.0]])
+    out = oracle.epilogue_ref(Z, activation="gelu")[0]
+    assert out[0] == 0.0
+    assert abs(out[1] - PHI_1) <= 4 * U
+    assert abs(out[2] - (-(1.0 - PHI_1))) <= 4 * U
+    assert abs(out[3] - Z975 * 0.975) <= 8 * U
+    assert abs(out[4] - (-Z975 * 0.025)) <= 8 * U
+    assert out[5] == 10.0                                   # 1 - Phi(10) < 1e-23
+
+
+def test_gelu_odd_part_is_identity():
+    """gelu(x) - gelu(-x) = x (Phi(x) + Phi(-x) = 1), and gelu(x) + gelu(-x) = x*(2*Phi(x) - 1) >= 0."""
+    rng = np.random.default_rng(41)
+    x = rng.normal(scale=3.0, size=(11, 13))
+    g = oracle.epilogue_ref(x, activation="gelu")
+    gm = oracle.epilogue_ref(-x, activation="gelu")
+    np.testing.assert_allclose(g - gm, x, rtol=4 * U, atol=4 * U)
+    assert np.all(g + gm >= -4 * U)
+
+
+def test_gelu_matches_scipy_normal_cdf():
+    """The erf form 1 + erf(x/sqrt 2) cancels in the left tail, so the
+    agreement is absolute, a few ulps of |x|, not relative."""
+    from scipy.special import ndtr
+    x = np.linspace(-8.0, 8.0, 321).reshape(3, 107)
+    g = oracle.epilogue_ref(x, activation="gelu")
+    assert np.all(np.abs(g - x * ndtr(x)) <= 8 * U * np.abs(x))
+    right = x > 0.5
+    np.testing.assert_allclose(g[right], (x * ndtr(x))[right], rtol=1e-14)
+
+
+def test_gelu_tails_and_special_values():
+    out = oracle.epilogue_ref(np.array([[-10.0, 40.0, np.inf, np.nan]]), activation="gelu")[0]
+    assert -1e-20 < out[0] <= 0.0                         # 1 + erf(-10/sqrt 2) rounds to 0
+    assert out[1] == 40.0 and out[2] == np.inf and np.isnan(out[3])
+
+
+def test_bias_is_indexed_by_column():
+    bias = np.float32([1.0, -2.0, 3.5, 0.25, -0.125])
+    out = oracle.epilogue_ref(np.zeros((7, 5)), bias)
+    np.testing.assert_array_equal(out, np.tile(bias.astype(np.float64), (7, 1)))
+
+
+def test_bias_with_identity_operand():
+    """act(I @ B + bias) with small integers: B + bias exactly, then the activation."""
+    rng = np.random.default_rng(42)
+    B = rng.integers(-5, 6, size=(6, 9)).astype(np.float32)
+    bias = rng.integers(-3, 4, size=9).astype(np.float32)
+    eye = np.eye(6, dtype=np.float32)
+    np.testing.assert_array_equal(oracle.gemm_epilogue_ref(eye, B, bias=bias), B + bias)
+    np.testing.assert_array_equal(oracle.gemm_epilogue_ref(eye, B, bias=bias, activation="relu"),
+                                  np.maximum(B + bias, 0.0))
+    np.testing.assert_array_equal(oracle.gemm_epilogue_ref(eye, B, 2.0, 0.0, None, bias),
+                                  2.0 * B.astype(np.float64) + bias)
+
+
+def test_activation_applies_after_beta_and_bias():
+    """relu(1*1 + 1*(-3) + 1.5) = relu(-0.5) = 0; the activation taken before
+    the beta term would give 1 - 3 + 1.5, before the bias -2 + 1.5."""
+    one = np.float32([[1.0]])
+    out = oracle.gemm_epilogue_ref(one, one, 1.0, 1.0, np.float32([[-3.0]]), np.float32([1.5]), "relu")
+    assert out[0, 0] == 0.0
+    out = oracle.gemm_epilogue_ref(one, one, 1.0, 1.0, np.float32([[-3.0]]), np.float32([2.5]), "relu")
+    assert out[0, 0] == 0.5
+
+
 # ----------------------------------------------------------------------------- acceptance measure
 
 def test_error_ratio_measure():

@@ -47,6 +47,15 @@ MUTANTS = [
     ("absbound_abs_of_B_dropped", [("row[j] += a * (b < 0 ? -b : b);", "row[j] += a * b;", 0)]),
     ("absbound_beta_dropped", [("v += ab * (c < 0 ? -c : c);", "(void)c;", 0)]),
     ("absbound_alpha_signed", [("double v = aa * row[j];", "double v = alpha * row[j];", 0)]),
+    ("epilogue_bias_dropped", [("z += (double)bias[j];", "(void)bias;", 0)]),
+    ("epilogue_bias_row_index", [("z += (double)bias[j];", "z += (double)bias[i % N];", 0)]),
+    ("epilogue_bias_after_activation", [("z += (double)bias[j];", "(void)0;", 0),
+                                        ("Z[i * ldz + j] = z;", "Z[i * ldz + j] = z + (bias ? (double)bias[j] : 0.0);",
+                                         0)]),
+    ("relu_inverted", [("if (z < 0.0)", "if (z > 0.0)", 0)]),
+    ("gelu_sqrt2_dropped", [("erf(z * inv_sqrt2)", "erf(z)", 0)]),
+    ("gelu_half_dropped", [("z = 0.5 * z * (1.0 + erf", "z = z * (1.0 + erf", 0)]),
+    ("gelu_erf_sign", [("(1.0 + erf(", "(1.0 - erf(", 0)]),
 ]
 
 
@@ -68,7 +77,7 @@ def _run_mutant(name, edits, workdir):
     so_path = os.path.join(workdir, f"lib_{name}.so")
     with open(c_path, "w") as f:
         f.write(src)
-    cmd = [a for a in oracle.BUILD_CMD[:-3]] + ["-o", so_path, c_path]
+    cmd = oracle.build_cmd(so_path, c_path)
     subprocess.run(cmd, check=True, capture_output=True)
     env = dict(os.environ, GEMM_ORACLE_LIB=so_path, OMP_NUM_THREADS="2")
     proc = subprocess.run(

@@ -17,7 +17,8 @@ def test_tile_mapping_is_a_bijection():
     d = tempfile.mkdtemp(prefix="tilemap_")
     try:
         exe = os.path.join(d, "check")
-        subprocess.run([HIPCC, "-O1", "-std=c++17", "-I", os.path.join(ROOT, "tiled_gemm_f32_amd", "csrc"),
+        subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-std=c++17",
+                        "-I", os.path.join(ROOT, "tiled_gemm_f32_amd", "csrc"), "-I", os.path.join(ROOT, "include"),
                         os.path.join(ROOT, "tests", "tile_map_check.cpp"), "-o", exe],
                        check=True, capture_output=True)
         out = subprocess.run([exe], capture_output=True, text=True, timeout=120)

@@ -10,7 +10,8 @@ reads shapes, strides and pointers and forwards them.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401  (re-exported C ABI)
-    EXPORTED, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
+    EXPORTED, GEMM_ACT_GELU, GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, Epilogue,
+    gemm_bf16f32_epi, gemm_f32_epi, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
     gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
     gemm_tuning_save, gemm_tuning_load, load)
 
 __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
+           "gemm_f32_epi", "gemm_bf16f32_epi", "Epilogue", "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
            "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune", "gemm_tuning_count",
            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load"]
@@ -44,8 +46,12 @@ def workspace(M: int, N: int, K: int, device=None, dtype: int = GEMM_DTYPE_F32):
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
 
 
-def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None, ws=None):
-    """C = alpha * (A @ B) + beta * C on the current stream; returns C.
+_ACTIVATIONS = {None: GEMM_ACT_NONE, "none": GEMM_ACT_NONE, "relu": GEMM_ACT_RELU, "gelu": GEMM_ACT_GELU}
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None, ws=None,
+         bias=None, activation=None):
+    """C = act(alpha * (A @ B) + beta * C + bias) on the current stream; returns C.
 
     A (M x K) and B (K x N) are CUDA tensors of dtype float32 (fp32 path) or
     bfloat16 (bf16 operands, fp32 accumulate); C is float32 (M x N),
@@ -53,6 +59,9 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     with unit stride along columns; padded leading dimensions are fine.
     ``kernel`` forces a kernel id (0 = library choice).  ``ws`` is an optional
     device workspace tensor (see ``workspace()``) for the split-K paths.
+    ``bias`` is an optional float32 device tensor of N elements added to every
+    row; ``activation`` is None, "relu", "gelu" or a GEMM_ACT_* value.  Both
+    are applied inside the kernels' epilogue.
     """
     import torch
 
@@ -73,13 +82,20 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
+    act = _ACTIVATIONS[activation] if activation is None or isinstance(activation, str) else int(activation)
+    epi = None
+    if bias is not None or act != GEMM_ACT_NONE:
+        if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda or bias.numel() != N
+                                 or not bias.is_contiguous()):
+            raise ValueError(f"bias must be a contiguous float32 device tensor of {N} elements")
+        epi = Epilogue(bias.data_ptr() if bias is not None else None, act)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc)
     with torch.cuda.device(A.device):
         wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
         if A.dtype == torch.float32:
-            st = gemm_f32_ex(*args, kernel, wp, wb, stream)
+            st = gemm_f32_ex(*args, kernel, epi, wp, wb, stream)
         else:
-            st = gemm_bf16f32_ex(*args, kernel, wp, wb, stream)
+            st = gemm_bf16f32_ex(*args, kernel, epi, wp, wb, stream)
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
     return C

@@ -29,11 +29,15 @@ GEMM_PATH_SKINNY_SPLITK = 4
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16F32 = 1
 
+GEMM_ACT_NONE = 0
+GEMM_ACT_RELU = 1
+GEMM_ACT_GELU = 2
+
 # Every entry point include/gemm.h declares.
 EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
             "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws", "gemm_autotune", "gemm_tuning_count",
-            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load")
+            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_f32_epi", "gemm_bf16f32_epi")
 
 
 class KernelInfo(ctypes.Structure):
@@ -48,6 +52,19 @@ class Plan(ctypes.Structure):
                 ("threads", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
                 ("splits", ctypes.c_int32)]
+
+
+class Epilogue(ctypes.Structure):
+    """gemm_epilogue: bias (device pointer to N floats, or 0) and activation."""
+    _fields_ = [("bias", ctypes.c_void_p), ("activation", ctypes.c_int32)]
+
+
+def _epi(epilogue):
+    """None, an Epilogue, or a (bias_ptr, activation) pair -> ctypes argument."""
+    if epilogue is None or isinstance(epilogue, Epilogue):
+        return epilogue
+    bias, act = epilogue
+    return Epilogue(bias or None, act)
 
 
 class GemmError(RuntimeError):
@@ -72,12 +89,15 @@ def load() -> ctypes.CDLL:
     gemm_sig = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64]
     lib.gemm_f32.argtypes = gemm_sig + [vp]
     lib.gemm_bf16f32.argtypes = gemm_sig + [vp]
-    lib.gemm_f32_ex.argtypes = gemm_sig + [i32, vp, i64, vp]
-    lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, vp, i64, vp]
+    epi = ctypes.POINTER(Epilogue)
+    lib.gemm_f32_ex.argtypes = gemm_sig + [i32, epi, vp, i64, vp]
+    lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, epi, vp, i64, vp]
+    lib.gemm_f32_epi.argtypes = gemm_sig + [epi, vp, i64, vp]
+    lib.gemm_bf16f32_epi.argtypes = gemm_sig + [epi, vp, i64, vp]
     lib.gemm_f32_ws.argtypes = gemm_sig + [vp, i64, vp]
     lib.gemm_bf16f32_ws.argtypes = gemm_sig + [vp, i64, vp]
     for fn in (lib.gemm_f32, lib.gemm_bf16f32, lib.gemm_f32_ex, lib.gemm_bf16f32_ex, lib.gemm_f32_ws,
-               lib.gemm_bf16f32_ws):
+               lib.gemm_bf16f32_ws, lib.gemm_f32_epi, lib.gemm_bf16f32_epi):
         fn.restype = ctypes.c_int
     lib.gemm_workspace_size.argtypes = [i32, i64, i64, i64]
     lib.gemm_workspace_size.restype = i64
@@ -117,20 +137,32 @@ def gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspa
     return load().gemm_f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream)
 
 
-def gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace=0, workspace_bytes=0,
-                stream=0) -> int:
-    return load().gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace,
-                              workspace_bytes, stream)
+def gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, epilogue=None, workspace=0,
+                workspace_bytes=0, stream=0) -> int:
+    return load().gemm_f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, _epi(epilogue),
+                              workspace, workspace_bytes, stream)
+
+
+def gemm_f32_epi(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, epilogue, workspace=0, workspace_bytes=0,
+                 stream=0) -> int:
+    return load().gemm_f32_epi(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, _epi(epilogue), workspace,
+                               workspace_bytes, stream)
 
 
 def gemm_workspace_size(dtype, M, N, K) -> int:
     return int(load().gemm_workspace_size(dtype, M, N, K))
 
 
-def gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace=0, workspace_bytes=0,
-                    stream=0) -> int:
-    return load().gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, workspace,
-                                  workspace_bytes, stream)
+def gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, epilogue=None, workspace=0,
+                    workspace_bytes=0, stream=0) -> int:
+    return load().gemm_bf16f32_ex(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, _epi(epilogue),
+                                  workspace, workspace_bytes, stream)
+
+
+def gemm_bf16f32_epi(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, epilogue, workspace=0, workspace_bytes=0,
+                     stream=0) -> int:
+    return load().gemm_bf16f32_epi(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, _epi(epilogue), workspace,
+                                   workspace_bytes, stream)
 
 
 def gemm_bf16f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream=0) -> int:

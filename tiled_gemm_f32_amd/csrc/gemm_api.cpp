@@ -68,6 +68,8 @@ struct Call {
     int64_t lda, ldb, ldc;
     void *ws;
     int64_t ws_bytes;
+    const float *bias;     // fused epilogue (null: none)
+    int32_t act;           // gemm_activation
 };
 
 gemm_status validate(const Call &c) {
@@ -76,6 +78,8 @@ gemm_status validate(const Call &c) {
     const int64_t min_lda = c.K > 1 ? c.K : 1, min_n = c.N > 1 ? c.N : 1;
     if (c.lda < min_lda || c.ldb < min_n || c.ldc < min_n) return GEMM_ERR_INVALID_ARG;
     if (c.ws_bytes < 0 || (c.ws != nullptr && !aligned(c.ws, 4))) return GEMM_ERR_INVALID_ARG;
+    if (c.act < GEMM_ACT_NONE || c.act > GEMM_ACT_GELU) return GEMM_ERR_INVALID_ARG;
+    if (c.bias != nullptr && !aligned(c.bias, 4)) return GEMM_ERR_INVALID_ARG;
     const uintptr_t esz = c.dtype == GEMM_DTYPE_F32 ? 4 : 2;
     if (c.M > 0 && c.N > 0) {
         if (c.C == nullptr || !aligned(c.C, 4)) return GEMM_ERR_INVALID_ARG;
@@ -338,7 +342,7 @@ gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
 gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, const KSplit &ks, hipStream_t s) {
     hipError_t err;
     if (pl.path == GEMM_PATH_SCALE) {
-        err = gemm::launch_scale_c(c.beta, c.C, (int32_t)c.M, (int32_t)c.N, c.ldc, s);
+        err = gemm::launch_scale_c(c.beta, c.C, (int32_t)c.M, (int32_t)c.N, c.ldc, c.bias, c.act, s);
     } else {
         gemm::GemmParams p;
         p.A = c.A;
@@ -354,6 +358,8 @@ gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, con
         p.beta = c.beta;
         p.kchunk = 0;
         p.partials = nullptr;
+        p.bias = c.bias;
+        p.act = c.act;
         if (ks.splits > 1) {
             p.kchunk = ks.kchunk;
             p.partials = static_cast<float *>(c.ws);
@@ -431,6 +437,8 @@ Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, cons
     Call c;
     c.ws = ws;
     c.ws_bytes = ws ? ws_bytes : 0;
+    c.bias = nullptr;
+    c.act = GEMM_ACT_NONE;
     c.dtype = dtype;
     c.M = M;
     c.N = N;
@@ -477,12 +485,48 @@ GEMM_API gemm_status gemm_bf16f32_ws(int64_t M, int64_t N, int64_t K, float alph
                0, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Calls with a fused epilogue; a NULL descriptor is the plain call.
+gemm_status run_epi(Call c, const gemm_epilogue *epi, int32_t force, gemm_stream_t stream) {
+    if (epi != nullptr) {
+        c.bias = epi->bias;
+        c.act = epi->activation;
+    }
+    return run(c, force, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+GEMM_API gemm_status gemm_f32_epi(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
+                                  const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
+                                  const gemm_epilogue *epilogue, void *workspace, int64_t workspace_bytes,
+                                  gemm_stream_t stream) {
+    return run_epi(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                             workspace_bytes),
+                   epilogue, 0, stream);
+}
+
+GEMM_API gemm_status gemm_bf16f32_epi(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
+                                      int64_t lda, const uint16_t *B, int64_t ldb, float beta, float *C,
+                                      int64_t ldc, const gemm_epilogue *epilogue, void *workspace,
+                                      int64_t workspace_bytes, gemm_stream_t stream) {
+    return run_epi(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                             workspace_bytes),
+                   epilogue, 0, stream);
+}
+
 GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const float *A, int64_t lda,
                                  const float *B, int64_t ldb, float beta, float *C, int64_t ldc,
-                                 int32_t force_kernel, void *workspace, int64_t workspace_bytes,
-                                 gemm_stream_t stream) {
-    return run(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes),
-               force_kernel, stream);
+                                 int32_t force_kernel, const gemm_epilogue *epilogue, void *workspace,
+                                 int64_t workspace_bytes, gemm_stream_t stream) {
+    return run_epi(make_call(GEMM_DTYPE_F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                             workspace_bytes),
+                   epilogue, force_kernel, stream);
 }
 
 GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K) {
@@ -507,11 +551,11 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
 
 GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alpha, const uint16_t *A,
                                      int64_t lda, const uint16_t *B, int64_t ldb, float beta, float *C,
-                                     int64_t ldc, int32_t force_kernel, void *workspace, int64_t workspace_bytes,
-                                     gemm_stream_t stream) {
-    return run(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
-                         workspace_bytes),
-               force_kernel, stream);
+                                     int64_t ldc, int32_t force_kernel, const gemm_epilogue *epilogue,
+                                     void *workspace, int64_t workspace_bytes, gemm_stream_t stream) {
+    return run_epi(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                             workspace_bytes),
+                   epilogue, force_kernel, stream);
 }
 
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,

@@ -261,7 +261,7 @@ bf16_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
                     float *cp = p.C + (int64_t)row * p.ldc + col;
                     float v = alpha * acc[fm][fn][r];
                     if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                    *cp = v;
+                    *cp = epilogue_value(v, col, p.bias, p.act);
                 }
             }
         }
@@ -440,7 +440,7 @@ bf16_pipe_kernel(GemmParams p, int tiles_m, int tiles_n) {
                     float *cp = p.C + (int64_t)row * p.ldc + col;
                     float v = alpha * acc[fm][fn][r];
                     if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                    *cp = v;
+                    *cp = epilogue_value(v, col, p.bias, p.act);
                 }
             }
         }
@@ -651,40 +651,48 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // Epilogue.  Register 4g + t of lane (h, l32) in fragment (fm, fn) is
     // C[row m0 + wm*128 + 32*fm + l32][column n0 + wn*128 + 32*fn + 8*g + 4*h + t].
     // N is a multiple of 8 on this path, so each run of 4 columns is wholly
-    // inside or outside C; 16-byte accesses need C 16-byte aligned and ldc % 4 == 0.
+    // inside or outside C; 16-byte accesses need C 16-byte aligned and
+    // ldc % 4 == 0.  The branch on the activation is taken once for the whole
+    // tile, so each case is one fully unrolled pass and the accumulators stay
+    // in registers.
     const float alpha = p.alpha, beta = p.beta;
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
-#pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-        const int row = m0 + wm * 128 + 32 * fm + l32;
-        if (row >= M) continue;
-        float *crow = p.C + (int64_t)row * p.ldc;
+    with_activation(p.act, [&](auto act) {
+        using Act = decltype(act);
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
                 if (col >= N) continue;
-                f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
-                           alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
-                if (vec_c) {
-                    f32x4 *cp = reinterpret_cast<f32x4 *>(crow + col);
+                float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+#pragma unroll
+                for (int t = 0; t < 4; ++t) b[t] = p.bias != nullptr ? p.bias[col + t] : -0.0f;
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) {
+                    const int row = m0 + wm * 128 + 32 * fm + l32;
+                    if (row >= M) continue;
+                    float *cp = p.C + (int64_t)row * p.ldc + col;
+                    f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
+                               alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
                     if (beta != 0.0f) {
-                        const f32x4 c0 = *cp;
+                        const f32x4 c0 =
+                            vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
                     }
-                    *cp = v;
-                } else {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        float *cp = crow + col + t;
-                        crow[col + t] = (beta != 0.0f) ? fmaf(beta, *cp, v[t]) : v[t];
+                    for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
+                    if (vec_c) {
+                        *reinterpret_cast<f32x4 *>(cp) = v;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) cp[t] = v[t];
                     }
                 }
             }
         }
-    }
+    });
 }
 
 template <int NS, int GROUP_M>

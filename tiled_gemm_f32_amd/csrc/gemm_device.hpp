@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm.h"
 #include "gemm_kernels.hpp"
 
 namespace gemm {
@@ -143,6 +144,56 @@ __device__ __forceinline__ void apply_k_split(GemmParams &p) {
     p.ldc = p.N;
     p.alpha = 1.0f;
     p.beta = 0.0f;
+    p.bias = nullptr;          // the reduce applies the epilogue once
+    p.act = 0;
+}
+
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (a rational function of t = 1 / (1 + p|x|) times exp(-x^2); the
+// formula's error is at most 1.5e-7), evaluated inline: the library erff is
+// a function call, and a call inside an epilogue forces the accumulator
+// registers out to scratch memory.
+__device__ __forceinline__ float erf_inline(float x) {
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));       // 1 ulp reciprocal
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    // exp(-x^2) = 2^(-x^2 * log2(e)); the hardware exp2 is accurate to 1 ulp.
+    return copysignf(1.0f - poly * __builtin_amdgcn_exp2f(-ax * ax * 1.44269504088896341f), x);
+}
+
+// The fused epilogue's activations ("Tiled matrix multiplication",
+// "Implementation notes": bias and activation are applied while the tile is
+// still in registers).  ReLU keeps NaN; GELU is the erf form,
+// x * Phi(x) = x * (1 + erf(x / sqrt(2))) / 2, evaluated as written.  They
+// are types so that a kernel holding a large accumulator tile can branch once
+// on the activation and run one small loop body per case: a per-element
+// branch makes the fully unrolled epilogue too large to unroll, and a loop
+// over the accumulators with a run-time index puts them in scratch memory.
+struct ActNone {
+    __device__ static float apply(float v) { return v; }
+};
+struct ActRelu {
+    __device__ static float apply(float v) { return v < 0.0f ? 0.0f : v; }
+};
+struct ActGelu {
+    __device__ static float apply(float v) { return 0.5f * v * (1.0f + erf_inline(v * 0.70710678118654752f)); }
+};
+
+template <typename F>
+__device__ __forceinline__ void with_activation(int act, F &&f) {
+    if (act == GEMM_ACT_GELU) f(ActGelu{});
+    else if (act == GEMM_ACT_RELU) f(ActRelu{});
+    else f(ActNone{});
+}
+
+// The fused epilogue on one output value already holding
+// alpha * acc + beta * C0: add the column's bias, then the activation.
+__device__ __forceinline__ float epilogue_value(float v, int64_t col, const float *bias, int act) {
+    if (bias != nullptr) v += bias[col];
+    if (act == GEMM_ACT_RELU) v = ActRelu::apply(v);
+    else if (act == GEMM_ACT_GELU) v = ActGelu::apply(v);
+    return v;
 }
 
 }  // namespace gemm

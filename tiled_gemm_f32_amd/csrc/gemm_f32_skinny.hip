@@ -152,7 +152,7 @@ f32_skinny_kernel(GemmParams p) {
             float *cp = p.C + (int64_t)i * p.ldc + col;
             float v = alpha * s;
             if (beta != 0.0f) v = fmaf(beta, *cp, v);
-            *cp = v;
+            *cp = epilogue_value(v, col, p.bias, p.act);
         }
     }
 }
@@ -257,7 +257,7 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
                 float *cp = p.C + (int64_t)i * p.ldc + col;
                 float v = alpha * s;
                 if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                *cp = v;
+                *cp = epilogue_value(v, col, p.bias, p.act);
             }
         }
         return;
@@ -288,7 +288,7 @@ splitk_reduce_kernel(GemmParams p, const float *partials, int splits) {
     float *cp = p.C + i * p.ldc + j;
     float v = p.alpha * s;
     if (p.beta != 0.0f) v = fmaf(p.beta, *cp, v);
-    *cp = v;
+    *cp = epilogue_value(v, j, p.bias, p.act);
 }
 
 hipError_t launch_reduce(const GemmParams &p, const float *partials, int splits, hipStream_t stream) {
@@ -324,13 +324,13 @@ hipError_t launch_f32_skinny_splitk(const GemmParams &p, void *workspace, hipStr
 }
 
 __global__ void __launch_bounds__(256)
-scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc) {
+scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act) {
     const int64_t total = (int64_t)M * N;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
         const int64_t i = idx / N, j = idx - i * N;
         float *cp = C + i * ldc + j;
-        *cp = (beta == 0.0f) ? 0.0f : beta * *cp;
+        *cp = epilogue_value((beta == 0.0f) ? 0.0f : beta * *cp, j, bias, act);
     }
 }
 
@@ -375,11 +375,12 @@ hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t stream) {
     return launch_reduce(p, p.partials, k_splits(p), stream);
 }
 
-hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, hipStream_t stream) {
+hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act,
+                          hipStream_t stream) {
     const int64_t total = (int64_t)M * N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    void *argv[] = {&beta, &C, &M, &N, &ldc};
+    void *argv[] = {&beta, &C, &M, &N, &ldc, (void *)&bias, &act};
     return hipLaunchKernel(reinterpret_cast<const void *>(&scale_c_kernel), dim3((unsigned)blocks),
                            dim3(256), argv, 0, stream);
 }

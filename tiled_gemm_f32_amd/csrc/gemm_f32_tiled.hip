@@ -204,7 +204,7 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
                     float *cp = p.C + (int64_t)row * p.ldc + col;
                     float v = alpha * acc[fm][fn][r];
                     if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                    *cp = v;
+                    *cp = epilogue_value(v, col, p.bias, p.act);
                 }
             }
         }
@@ -374,11 +374,18 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // Epilogue.  Register r of lane (h, l32) in fragment (fm, fn) is row
     // 32*fm + 8*(r/4) + 4*h + r%4 of the wave tile, column 4*l32 + fn; N is a
     // multiple of 4 on this path, so each run of 4 columns is wholly inside
-    // or outside C.
+    // or outside C.  The branch on the activation is taken once for the whole
+    // tile, so each case is one fully unrolled pass and the accumulators stay
+    // in registers.
     const float alpha = p.alpha, beta = p.beta;
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
     const int col = n0 + wn * 128 + 4 * l32;
-    if (col < N) {
+    if (col >= N) return;
+    float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[e] = p.bias != nullptr ? p.bias[col + e] : -0.0f;
+    with_activation(p.act, [&](auto act) {
+        using Act = decltype(act);
 #pragma unroll
         for (int fm = 0; fm < 4; ++fm) {
 #pragma unroll
@@ -387,20 +394,22 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                 if (row >= M) continue;
                 float *cp = p.C + (int64_t)row * p.ldc + col;
                 f32x4 v = {alpha * acc[fm][0][r], alpha * acc[fm][1][r], alpha * acc[fm][2][r], alpha * acc[fm][3][r]};
-                if (vec_c) {
-                    if (beta != 0.0f) {
-                        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cp);
+                if (beta != 0.0f) {
+                    const f32x4 c0 = vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c0[e], v[e]);
-                    }
+                    for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c0[e], v[e]);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = Act::apply(v[e] + b[e]);
+                if (vec_c) {
                     *reinterpret_cast<f32x4 *>(cp) = v;
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) cp[e] = (beta != 0.0f) ? fmaf(beta, cp[e], v[e]) : v[e];
+                    for (int e = 0; e < 4; ++e) cp[e] = v[e];
                 }
             }
         }
-    }
+    });
 }
 
 template <int NS, int GROUP_M>

@@ -26,6 +26,10 @@ struct GemmParams {
     // (alpha 1, beta 0) to partials + y*M*N with leading dimension N.
     int32_t kchunk;
     float *partials;
+    // Fused epilogue: C = act(alpha * acc + beta * C0 + bias[column]); bias
+    // may be null, act is a gemm_activation.
+    const float *bias;
+    int32_t act;
 };
 
 inline int k_splits(const GemmParams &p) { return p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1; }
@@ -76,7 +80,7 @@ extern const KernelDesc kF32SplitKernels[];
 extern const int kF32SplitKernelCount;
 
 // C = beta * C over an M x N view (beta == 0 writes zeros without reading).
-hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc,
+hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act,
                           hipStream_t stream);
 
 }  // namespace gemm

@@ -108,6 +108,14 @@ def make_integer_inputs(M: int, N: int, K: int, seed: int, lo: int = -4, hi: int
     return A, B, C0
 
 
+def make_bias(N: int, seed: int, dist: str = "normal", integer: bool = False):
+    """A float32 bias vector of N values (seeded; small integers if asked)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    if integer:
+        return torch.randint(-4, 5, (N,), generator=g).to(torch.float32)
+    return _draw((N,), dist, g)
+
+
 def make_random_inputs(M: int, N: int, K: int, seed: int, dist: str = "uniform",
                        dtype: str = "f32"):
     """Random operands of an arbitrary shape with the same draw order."""
