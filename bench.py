@@ -37,12 +37,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "GFLOP/s (2MNK/t) fp32 4096^3 + bf16 8192^3, % of MI355X MFMA peak"
-PEAK_TFLOPS = {"f32": 157.3, "bf16f32": 2500.0}
+PEAK_TFLOPS = {"f32": 157.3, "bf16f32": 2500.0, "fp8f32": 5000.0}
 PEAK_HBM_GBS = 8000.0
 # The skinny call runs after the fp32 GEMM (64 MB of C written) rather than
 # right after the bf16 GEMM, whose 256 MB of freshly written C would still be
 # draining from the last-level cache to HBM while the skinny kernel streams B.
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
+# Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
+EXTRA = ["fp8f32_8192_nt"]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -52,7 +54,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=STEP, default=None, help="time a single workload of the step")
+    ap.add_argument("--only", choices=STEP + EXTRA, default=None,
+                    help="time a single workload (of the step, or one of the extra ones)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (a plain kernel of known traffic) so hardware "
@@ -62,7 +65,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_tiled.hip",
-                  "f32_skinny": "gemm_f32_skinny.hip"}
+                  "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip"}
 
 
 # Headers every kernel source includes: a change there changes the kernels too.
@@ -97,6 +100,14 @@ def measured_traffic(kernel_name: str):
     return rec.get("bytes_per_launch")
 
 
+def _to_device(t, dev):
+    """Host tensor to the device; fp8 moves as bytes (no fp8 kernel involved)."""
+    import torch
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).to(dev).view(torch.float8_e4m3fn)
+    return t.to(dev)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -121,14 +132,19 @@ def main():
     for name in names:
         w = WORKLOADS[name]
         A, B, C0 = make_inputs(w)
-        Ad, C = A.to(dev), C0.to(dev)
+        Ad, C = _to_device(A, dev), C0.to(dev)
         copies = SKINNY_COPIES if w.M <= 16 else 1
-        Bs = [B.to(dev) for _ in range(copies)]
+        Bs = [_to_device(B, dev) for _ in range(copies)]
         ws = tg.workspace(w.M, w.N, w.K, device=dev) if w.dtype == "f32" else None
         calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []})
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
+
+    DTYPES = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32, "fp8f32": tg.GEMM_DTYPE_FP8F32}
+
+    def ldb_of(w):
+        return w.K if w.op_b == "T" else w.N
 
     def launch(c, record):
         w = c["w"]
@@ -138,7 +154,11 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        if c["ws"] is not None:
+        if w.dtype == "fp8f32":
+            st = tg.gemm_general(DTYPES[w.dtype], tg.GEMM_OP_N, tg.GEMM_OP_T if w.op_b == "T" else tg.GEMM_OP_N,
+                                 w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), ldb_of(w), w.beta,
+                                 c["C"].data_ptr(), w.N, 0, None, 0, 0, sh)
+        elif c["ws"] is not None:
             st = tg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
                                 c["C"].data_ptr(), w.N, c["ws"].data_ptr(), c["ws"].numel(), sh)
         else:
@@ -177,9 +197,11 @@ def main():
         ms = sum(e0.elapsed_time(e1) for e0, e1 in c["durs"]) / len(c["durs"])
         tflops = w.flops / (ms * 1e-3) / 1e12
         gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
-        plan = tg.gemm_plan_query(0 if w.dtype == "f32" else 1, w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K,
-                                  c["B"][0].data_ptr(), w.N, w.beta, c["C"].data_ptr(), w.N, 0,
-                                  c["ws"].numel() if c["ws"] is not None else 0)[1]
+        plan = tg.gemm_plan_query_general(DTYPES[w.dtype], tg.GEMM_OP_N,
+                                          tg.GEMM_OP_T if w.op_b == "T" else tg.GEMM_OP_N, w.M, w.N, w.K, w.alpha,
+                                          c["A"].data_ptr(), w.K, c["B"][0].data_ptr(), ldb_of(w), w.beta,
+                                          c["C"].data_ptr(), w.N, 0,
+                                          c["ws"].numel() if c["ws"] is not None else 0)[1]
         kname = tg.gemm_kernel_query(plan["kernel_id"])["name"]
         bound = "hbm" if w.M <= 16 else "mfma"
         parts[w.name] = {
@@ -207,10 +229,12 @@ def main():
     if not args.no_cpu_baseline and not args.only:
         cpu = cpu_baseline(calls)
 
+    dtypes = "+".join(d for d in ("f32", "bf16f32", "fp8f32") if any(c["w"].dtype == d for c in calls))
+    metric = METRIC if args.only not in EXTRA else f"GFLOP/s (2MNK/t) {args.only}, % of MI355X MFMA peak"
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32+bf16f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": dtypes, "data": "synthetic",
         "config": {"workload": " + ".join(names), "parallelism": "single-gpu",
                    "shapes": {n: [WORKLOADS[n].M, WORKLOADS[n].N, WORKLOADS[n].K] for n in names}},
         "roofline": roof,

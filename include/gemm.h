@@ -142,8 +142,24 @@ typedef enum gemm_path {
 
 typedef enum gemm_dtype {
     GEMM_DTYPE_F32 = 0,     /* fp32 operands */
-    GEMM_DTYPE_BF16F32 = 1  /* bf16 operands, fp32 accumulate and output */
+    GEMM_DTYPE_BF16F32 = 1, /* bf16 operands, fp32 accumulate and output */
+    GEMM_DTYPE_FP8F32 = 2   /* fp8 operands (OCP E4M3, one byte each), fp32 accumulate and
+                               output; gemm_general only */
 } gemm_dtype;
+
+/*
+ * Operand layouts (gemm_general).  GEMM_OP_N: the operand is stored as
+ * defined above (A: M x K, element (i, k) at A[i*lda + k]; B: K x N,
+ * element (k, j) at B[k*ldb + j]).  GEMM_OP_T: it is stored transposed
+ * (A: K x M, element (i, k) at A[k*lda + i], lda >= max(1, M); B: N x K,
+ * element (k, j) at B[j*ldb + k], ldb >= max(1, K)).  The pages show the
+ * untransposed layout only; the transposed ones are the usual weight
+ * layouts (B as N x K).
+ */
+typedef enum gemm_op {
+    GEMM_OP_N = 0,
+    GEMM_OP_T = 1
+} gemm_op;
 
 typedef struct gemm_kernel_info {
     int32_t id;             /* 1-based; 0 is never a kernel */
@@ -153,6 +169,7 @@ typedef struct gemm_kernel_info {
     int32_t threads;        /* threads per workgroup */
     int32_t vec_a, vec_b;   /* elements per global load of A and of B (1 = element loads) */
     const char *name;       /* static string */
+    int32_t layouts;        /* bit 2*op_a + op_b set for every operand layout it runs */
 } gemm_kernel_info;
 
 typedef struct gemm_plan {
@@ -246,6 +263,40 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
 
 
 /*
+ * The general call: any operand type (gemm_dtype) and either layout of each
+ * operand (gemm_op), with the optional fused epilogue, workspace and forced
+ * kernel of gemm_f32_ex.  A and B point to fp32, bf16 (uint16_t) or fp8
+ * E4M3 (uint8_t) elements as dtype says; C is fp32.  Every combination runs:
+ * untransposed fp32 and bf16 take the kernels above; fp8 with A untransposed
+ * and B transposed (GEMM_OP_N, GEMM_OP_T) takes the fp8 matrix-core kernel
+ * when A, B, lda, ldb and K are multiples of 16 bytes; the rest take a
+ * general kernel that loads elements one by one and multiplies in fp32.
+ *
+ * fp8 accuracy.  Products of two E4M3 values are exact; the fp8 matrix core
+ * sums each run of 8 consecutive k with truncation below 2^-13 of the run's
+ * largest product, then adds the runs in fp32, so its error is at most
+ * about 2^-10 * |alpha| * sum over runs of the largest |product| plus the
+ * usual fp32 accumulation error.  Per-tensor scales fold into alpha.
+ * Errors: GEMM_ERR_INVALID_ARG for an unknown dtype or op, besides those of
+ * gemm_f32_ex.  A call with op_a == op_b == GEMM_OP_N and dtype fp32 or bf16
+ * is exactly gemm_f32_ex / gemm_bf16f32_ex.
+ */
+GEMM_API gemm_status gemm_general(int32_t dtype, int32_t op_a, int32_t op_b,
+                                  int64_t M, int64_t N, int64_t K, float alpha,
+                                  const void *A, int64_t lda, const void *B, int64_t ldb,
+                                  float beta, float *C, int64_t ldc,
+                                  int32_t force_kernel, const gemm_epilogue *epilogue,
+                                  void *workspace, int64_t workspace_bytes, gemm_stream_t stream);
+
+/* gemm_plan_query with operand layouts: the plan gemm_general would take. */
+GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_t op_b,
+                                             int64_t M, int64_t N, int64_t K, float alpha,
+                                             const void *A, int64_t lda, const void *B, int64_t ldb,
+                                             float beta, const float *C, int64_t ldc,
+                                             int32_t force_kernel, int64_t workspace_bytes,
+                                             gemm_plan *out);
+
+/*
  * Per-shape tuning ("A GEMM Kernel, Step by Step", section "Six parameters,
  * found by search": the best tile configuration for a shape is not
  * derivable, so it is found by timing the candidates).
@@ -260,6 +311,8 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  * `out` receives the plan that calls of this kind now take.  reps: 1..1000.
  * Later calls with no forced kernel (and gemm_plan_query) use a recorded
  * choice whenever it can run the call; otherwise the built-in rules choose.
+ * Tuning covers untransposed operands; gemm_general calls with a transposed
+ * operand always take the built-in rules.
  * The table is guarded by a mutex; autotuning concurrently with calls on
  * other threads is safe, though the timings then include their load.
  *

@@ -13,7 +13,12 @@ and never imports it.
 Arrays are 2-D numpy arrays whose last axis is contiguous; their row stride
 (in elements) is passed as the leading dimension, so views into padded
 buffers work unchanged.  fp32 operands are ``numpy.float32``; bf16 operands
-are ``numpy.uint16`` bit patterns.
+are ``numpy.uint16`` bit patterns; fp8 operands (OCP E4M3) are
+``numpy.uint8`` bytes.
+
+Operand layouts: ``op_a="T"`` means the array passed as A holds A
+transposed (K x M), ``op_b="T"`` that B holds B transposed (N x K).  The
+oracle then multiplies the transposes, taken as plain copies.
 """
 from __future__ import annotations
 
@@ -60,11 +65,13 @@ def _load():
     lib = ctypes.CDLL(path)
     i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     sig = [i64, i64, i64, dbl, vp, i64, vp, i64, dbl, vp, i64, vp, i64]
-    for name in ("gemm_ref_f32in", "gemm_ref_bf16in",
-                 "gemm_absbound_f32in", "gemm_absbound_bf16in"):
+    for name in ("gemm_ref_f32in", "gemm_ref_bf16in", "gemm_ref_fp8in",
+                 "gemm_absbound_f32in", "gemm_absbound_bf16in", "gemm_absbound_fp8in"):
         fn = getattr(lib, name)
         fn.argtypes = sig
         fn.restype = None
+    lib.gemm_groupmax_fp8in.argtypes = [i64, i64, i64, dbl, vp, i64, vp, i64, vp, i64]
+    lib.gemm_groupmax_fp8in.restype = None
     lib.epilogue_ref.argtypes = [i64, i64, vp, i64, vp, ctypes.c_int]
     lib.epilogue_ref.restype = None
     lib.gemm_ref_num_threads.argtypes = []
@@ -89,13 +96,25 @@ def _ptr(x: np.ndarray) -> int:
     return x.__array_interface__["data"][0]
 
 
-def _run(kind: str, A, B, alpha, beta, C0):
-    if A.dtype == np.float32 and B.dtype == np.float32:
-        suffix = "f32in"
-    elif A.dtype == np.uint16 and B.dtype == np.uint16:
-        suffix = "bf16in"
-    else:
-        raise TypeError("operands must both be float32 or both uint16 (bf16 bits)")
+_SUFFIX = {np.dtype(np.float32): "f32in", np.dtype(np.uint16): "bf16in", np.dtype(np.uint8): "fp8in"}
+
+
+def _oriented(A, B, op_a, op_b):
+    """A as M x K and B as K x N (copies of the transposes where asked)."""
+    if op_a not in ("N", "T") or op_b not in ("N", "T"):
+        raise ValueError("op_a and op_b are 'N' or 'T'")
+    if op_a == "T":
+        A = np.ascontiguousarray(A.T)
+    if op_b == "T":
+        B = np.ascontiguousarray(B.T)
+    return A, B
+
+
+def _run(kind: str, A, B, alpha, beta, C0, op_a="N", op_b="N"):
+    if A.dtype != B.dtype or A.dtype not in _SUFFIX:
+        raise TypeError("operands must both be float32, uint16 (bf16 bits) or uint8 (fp8 E4M3 bytes)")
+    suffix = _SUFFIX[A.dtype]
+    A, B = _oriented(A, B, op_a, op_b)
     M, K = A.shape
     K2, N = B.shape
     if K2 != K:
@@ -116,17 +135,35 @@ def _run(kind: str, A, B, alpha, beta, C0):
     return out
 
 
-def gemm_ref(A, B, alpha=1.0, beta=0.0, C0=None) -> np.ndarray:
-    """fp64 ``alpha * A @ B + beta * C0`` over the exact input values.
+def gemm_ref(A, B, alpha=1.0, beta=0.0, C0=None, op_a="N", op_b="N") -> np.ndarray:
+    """fp64 ``alpha * op(A) @ op(B) + beta * C0`` over the exact input values.
 
     The beta term is left out (C0 not read) when ``beta == 0``.
     """
-    return _run("ref", A, B, alpha, beta, C0)
+    return _run("ref", A, B, alpha, beta, C0, op_a, op_b)
 
 
-def gemm_absbound(A, B, alpha=1.0, beta=0.0, C0=None) -> np.ndarray:
-    """fp64 ``|alpha| * |A| @ |B| + |beta| * |C0|`` -- the error-ratio denominator."""
-    return _run("absbound", A, B, alpha, beta, C0)
+def gemm_absbound(A, B, alpha=1.0, beta=0.0, C0=None, op_a="N", op_b="N") -> np.ndarray:
+    """fp64 ``|alpha| * |op(A)| @ |op(B)| + |beta| * |C0|`` -- the error-ratio denominator."""
+    return _run("absbound", A, B, alpha, beta, C0, op_a, op_b)
+
+
+def gemm_groupmax(A, B, alpha=1.0, op_a="N", op_b="N") -> np.ndarray:
+    """fp8 operands only: ``|alpha| * sum over runs q of 8 consecutive k of
+    max_k |op(A)[i][k] * op(B)[k][j]|`` (runs start at k = 0, the last may be
+    short) -- the scale of the truncation a matrix unit that sums each run of
+    8 products at a fixed precision below the run's largest can make."""
+    if A.dtype != np.uint8 or B.dtype != np.uint8:
+        raise TypeError("gemm_groupmax takes fp8 (uint8) operands")
+    A, B = _oriented(A, B, op_a, op_b)
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {A.shape} x {B.shape}")
+    out = np.empty((M, N), dtype=np.float64)
+    _load().gemm_groupmax_fp8in(M, N, K, float(alpha), _ptr(A), _ld(A, "A"), _ptr(B), _ld(B, "B"),
+                                _ptr(out), max(N, 1))
+    return out
 
 
 # The oracle's own names for the activations (see epilogue_ref in gemm_ref.c).
@@ -154,9 +191,10 @@ def epilogue_ref(Z, bias=None, activation="none") -> np.ndarray:
     return out
 
 
-def gemm_epilogue_ref(A, B, alpha=1.0, beta=0.0, C0=None, bias=None, activation="none") -> np.ndarray:
-    """fp64 ``act(alpha * A @ B + beta * C0 + bias)``: gemm_ref, then epilogue_ref."""
-    return epilogue_ref(gemm_ref(A, B, alpha, beta, C0), bias, activation)
+def gemm_epilogue_ref(A, B, alpha=1.0, beta=0.0, C0=None, bias=None, activation="none", op_a="N",
+                      op_b="N") -> np.ndarray:
+    """fp64 ``act(alpha * op(A) @ op(B) + beta * C0 + bias)``: gemm_ref, then epilogue_ref."""
+    return epilogue_ref(gemm_ref(A, B, alpha, beta, C0, op_a, op_b), bias, activation)
 
 
 def num_threads() -> int:

@@ -38,6 +38,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 static double widen_bf16(uint16_t bits)
@@ -173,6 +174,125 @@ void gemm_absbound_bf16in(int64_t M, int64_t N, int64_t K, double alpha,
             }
             row[j] = v;
         }
+    }
+}
+
+/*
+ * fp8 operands: the OCP 8-bit floating-point format E4M3 (the variant with
+ * no infinities), raw bytes.  Bit 7 is the sign, bits 6..3 the exponent with
+ * bias 7, bits 2..0 the mantissa.  Exponent field 0 is subnormal, m * 2^-9;
+ * exponent 15 with mantissa 7 is NaN; every other code is finite (the
+ * largest is 448).  Every value is exact in double, and so is every product
+ * of two of them.
+ */
+static double widen_e4m3(uint8_t bits)
+{
+    const int e = (bits >> 3) & 15, m = bits & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(8.0 + m, e - 10);          /* (1 + m/8) * 2^(e-7) */
+    return (bits & 0x80) ? -v : v;
+}
+
+/* The GEMM definition with fp8 E4M3 operands (raw bytes), fp32 C0. */
+void gemm_ref_fp8in(int64_t M, int64_t N, int64_t K, double alpha,
+                    const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                    double beta, const float *C0, int64_t ldc0,
+                    double *out, int64_t ldo)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        for (int64_t j = 0; j < N; ++j)
+            row[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = widen_e4m3(A[i * lda + k]);
+            const uint8_t *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j)
+                row[j] += a * widen_e4m3(brow[j]);
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * row[j];
+            if (beta != 0.0)
+                v += beta * (double)C0[i * ldc0 + j];
+            row[j] = v;
+        }
+    }
+}
+
+/* The error-ratio denominator (as above) with fp8 operands. */
+void gemm_absbound_fp8in(int64_t M, int64_t N, int64_t K, double alpha,
+                         const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                         double beta, const float *C0, int64_t ldc0,
+                         double *out, int64_t ldo)
+{
+    const double aa = alpha < 0 ? -alpha : alpha;
+    const double ab = beta < 0 ? -beta : beta;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        for (int64_t j = 0; j < N; ++j)
+            row[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = fabs(widen_e4m3(A[i * lda + k]));
+            const uint8_t *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j)
+                row[j] += a * fabs(widen_e4m3(brow[j]));
+        }
+        for (int64_t j = 0; j < N; ++j) {
+            double v = aa * row[j];
+            if (beta != 0.0)
+                v += ab * fabs((double)C0[i * ldc0 + j]);
+            row[j] = v;
+        }
+    }
+}
+
+/*
+ * Group-maximum bound for fp8 products summed in runs of 8:
+ *     G[i][j] = |alpha| * sum over q of max_{8q <= k < min(8q+8, K)} |A[i][k] * B[k][j]|
+ * A sum that aligns each run of 8 consecutive products to the run's largest
+ * and keeps a fixed number of bits below it loses less than one unit of the
+ * last kept bit per product; this sum of run maxima scales that loss.
+ */
+void gemm_groupmax_fp8in(int64_t M, int64_t N, int64_t K, double alpha,
+                         const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
+                         double *out, int64_t ldo)
+{
+    const double aa = alpha < 0 ? -alpha : alpha;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *row = out + i * ldo;
+        double *run = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        for (int64_t j = 0; j < N; ++j) {
+            row[j] = 0.0;
+            run[j] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = fabs(widen_e4m3(A[i * lda + k]));
+            const uint8_t *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) {
+                const double p = a * fabs(widen_e4m3(brow[j]));
+                if (p > run[j])
+                    run[j] = p;
+            }
+            if (k % 8 == 7 || k == K - 1) {
+                for (int64_t j = 0; j < N; ++j) {
+                    row[j] += run[j];
+                    run[j] = 0.0;
+                }
+            }
+        }
+        for (int64_t j = 0; j < N; ++j)
+            row[j] *= aa;
+        free(run);
     }
 }
 

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import tiled_gemm_f32_amd as tg
-from tiled_gemm_f32_amd.workloads import bf16_bits
+from tiled_gemm_f32_amd.workloads import bf16_bits, fp8_bytes
 
 TOL = {"f32": 2e-6, "bf16f32": 1e-5}
 
@@ -20,9 +20,11 @@ def say(msg: str):
 
 
 def host_view(t: torch.Tensor):
-    """numpy operand for the oracle: float32 array or uint16 bf16 bits."""
+    """numpy operand for the oracle: float32 array, uint16 bf16 bits or uint8 fp8 bytes."""
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)
+    if t.dtype == torch.float8_e4m3fn:
+        return fp8_bytes(t)
     return t.contiguous().numpy()
 
 
@@ -33,6 +35,10 @@ def padded_device(t: torch.Tensor, pad: int = 0, offset: int = 0, fill=float("na
     view starts ``offset`` elements into the buffer (to exercise unaligned
     bases).  Returns (view, backing buffer).
     """
+    if t.dtype == torch.float8_e4m3fn:
+        # Bytes only (no fp8 arithmetic on the device); padding is the NaN code.
+        view, buf = padded_device(t.view(torch.uint8), pad, offset, fill=0x7F)
+        return view.view(torch.float8_e4m3fn), buf
     rows, cols = t.shape
     ld = cols + pad
     buf = torch.full((rows * ld + offset + 1,), fill, dtype=t.dtype, device="cuda")
@@ -46,7 +52,7 @@ def needs_workspace(kernel: int) -> bool:
 
 
 def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c_fill=None, ws=None,
-             bias=None, activation=None):
+             bias=None, activation=None, op_a="N", op_b="N"):
     """Run the library on host inputs; returns (C as float32 numpy, C device view, C buffer).
 
     A zero-filled workspace is allocated when a workspace kernel is forced
@@ -62,7 +68,8 @@ def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c
         M, K = A.shape
         ws = tg.workspace(M, B.shape[1], K)
     bd = bias.to("cuda") if bias is not None else None
-    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel, ws=ws, bias=bd, activation=activation)
+    tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel, ws=ws, bias=bd, activation=activation, op_a=op_a,
+            op_b=op_b)
     torch.cuda.synchronize()
     return Cd.cpu().numpy(), Cd, cbuf
 

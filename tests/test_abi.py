@@ -14,7 +14,8 @@ from tiled_gemm_f32_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gemm.h")
 
-F32, BF16 = tg.GEMM_DTYPE_F32, tg.GEMM_DTYPE_BF16F32
+F32, BF16, FP8 = tg.GEMM_DTYPE_F32, tg.GEMM_DTYPE_BF16F32, tg.GEMM_DTYPE_FP8F32
+N_, T_ = tg.GEMM_OP_N, tg.GEMM_OP_T
 OK, INVALID, UNSUP = tg.GEMM_OK, tg.GEMM_ERR_INVALID_ARG, tg.GEMM_ERR_UNSUPPORTED
 # Fake but well-aligned device addresses: planning only inspects them.
 PA, PB, PC = 0x7f0000000000, 0x7f1000000000, 0x7f2000000000
@@ -66,8 +67,9 @@ def test_kernel_table_is_consistent():
     assert [k["id"] for k in ks] == list(range(1, len(ks) + 1))
     assert len({k["name"] for k in ks}) == len(ks)
     for k in ks:
-        assert k["dtype"] in (F32, BF16)
+        assert k["dtype"] in (F32, BF16, FP8)
         assert k["path"] in (tg.GEMM_PATH_TILED, tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK)
+        assert 1 <= k["layouts"] <= 15
         assert k["threads"] % 64 == 0 and 64 <= k["threads"] <= 1024
         if k["path"] == tg.GEMM_PATH_TILED:
             assert k["tile_m"] % 32 == 0 and k["tile_n"] % 32 == 0
@@ -388,3 +390,102 @@ def test_tuning_load_errors(tmp_path):
     assert st == tg.GEMM_ERR_INVALID_ARG
     st, p = tg.gemm_autotune(F32, 0, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 5)
     assert st == OK and p["path"] == tg.GEMM_PATH_NONE   # nothing to tune, no device needed
+
+
+# ----------------------------------------------------------------------------- operand layouts and fp8
+
+def gplan(dtype, op_a, op_b, M, N, K, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, beta=0.0, C=PC, ldc=None,
+          force=0, ws=0):
+    lda = max(K if op_a == N_ else M, 1) if lda is None else lda
+    ldb = max(N if op_b == N_ else K, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return tg.gemm_plan_query_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force, ws)
+
+
+def kname(pl):
+    return tg.gemm_kernel_query(pl["kernel_id"])["name"]
+
+
+def test_every_dtype_and_layout_has_a_kernel():
+    ks = tg.kernels()
+    for dt in (F32, BF16, FP8):
+        for bit in range(4):
+            assert any(k["dtype"] == dt and (k["layouts"] >> bit) & 1 for k in ks), (dt, bit)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, FP8])
+def test_general_validation(dtype):
+    assert gplan(dtype, 2, N_, 4, 4, 4)[0] == INVALID
+    assert gplan(dtype, N_, -1, 4, 4, 4)[0] == INVALID
+    # op_a = T: A is K x M, lda >= M; op_b = T: B is N x K, ldb >= K.
+    assert gplan(dtype, T_, N_, 8, 4, 4, lda=4)[0] == INVALID
+    assert gplan(dtype, T_, N_, 8, 4, 4, lda=8)[0] == OK
+    assert gplan(dtype, N_, T_, 4, 8, 6, ldb=5)[0] == INVALID
+    assert gplan(dtype, N_, T_, 4, 8, 6, ldb=6)[0] == OK
+    assert gplan(7, N_, N_, 4, 4, 4)[0] == INVALID
+
+
+def test_general_nn_matches_plain_query():
+    for dt in (F32, BF16):
+        for (M, N, K) in [(4096, 4096, 4096), (1000, 3000, 777), (16, 8192, 8192), (300, 260, 264)]:
+            a = plan(dt, M, N, K)
+            b = gplan(dt, N_, N_, M, N, K)
+            assert a == b, (dt, M, N, K)
+
+
+def test_fp8_nt_takes_the_ring_kernel():
+    st, pl = gplan(FP8, N_, T_, 8192, 8192, 8192)
+    assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4", pl
+    assert pl["grid"] == 32 * 32 and pl["splits"] == 1
+
+
+@pytest.mark.parametrize("why", ["K", "lda", "ldb", "A", "B"])
+def test_fp8_nt_unaligned_falls_back_to_general(why):
+    kw = dict(M=512, N=512, K=1024)
+    if why == "K":
+        kw["K"] = 1000
+    elif why == "lda":
+        kw["lda"] = 1032 - 4
+    elif why == "ldb":
+        kw["ldb"] = 1024 + 8
+    elif why == "A":
+        kw["A"] = PA + 8
+    else:
+        kw["B"] = PB + 4
+    st, pl = gplan(FP8, N_, T_, **kw)
+    assert st == OK and kname(pl) == "fp8_general_128x128x16", (why, pl)
+
+
+@pytest.mark.parametrize("dtype,prefix", [(F32, "f32"), (BF16, "bf16"), (FP8, "fp8")])
+@pytest.mark.parametrize("ops", [(N_, T_), (T_, N_), (T_, T_), (N_, N_)])
+def test_layouts_without_a_fast_kernel_take_general(dtype, prefix, ops):
+    st, pl = gplan(dtype, ops[0], ops[1], 1000, 3000, 777)
+    assert st == OK
+    fast = (dtype in (F32, BF16) and ops == (N_, N_))
+    if fast:
+        assert "general" not in kname(pl)
+    elif not (dtype == FP8 and ops == (N_, T_)):
+        assert kname(pl) == f"{prefix}_general_128x128x16", pl
+
+
+def test_forcing_a_kernel_checks_its_layout():
+    ring = [k["id"] for k in tg.kernels() if k["name"] == "fp8_mfma32_256x256x64_w2x2_nt_ring4"][0]
+    assert gplan(FP8, N_, N_, 512, 512, 512, force=ring)[0] == UNSUP
+    assert gplan(FP8, N_, T_, 512, 512, 512, force=ring)[0] == OK
+    f32_ring = [k["id"] for k in tg.kernels() if k["name"] == "f32_mfma32_256x256x16_w2x2_a4b4_ring4"][0]
+    assert gplan(F32, T_, N_, 512, 512, 512, force=f32_ring)[0] == UNSUP
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, FP8])
+@pytest.mark.parametrize("ops", [(N_, T_), (T_, N_), (T_, T_)])
+def test_transposed_layouts_split_k(dtype, ops):
+    M, N, K = 256, 512, 6000
+    ws = tg.gemm_workspace_size(dtype, M, N, K)
+    assert ws > 0
+    st, pl = gplan(dtype, ops[0], ops[1], M, N, K, ws=ws)
+    assert st == OK and pl["splits"] > 1, pl
+
+
+def test_fp8_workspace_size():
+    assert tg.gemm_workspace_size(FP8, 256, 512, 6000) == tg.gemm_workspace_size(BF16, 256, 512, 6000) > 0
+    assert tg.gemm_workspace_size(FP8, 16, 8192, 8192) > 0

@@ -1,0 +1,232 @@
+"""GPU parity of gemm_general: transposed operand layouts for every operand
+type, and fp8 (OCP E4M3) operands.
+
+Transposed operands are the stored transposes of seeded M x K / K x N
+draws; the oracle multiplies the transposes of what it is given.
+
+Tolerances:
+* fp32 and bf16: the error ratio of the untransposed paths (2e-6, 1e-5).
+* fp8, every kernel:
+      |C - ref| <= 7 * 2^-13 * G + (2e-6 + 2^-24) * D
+  G is the oracle's group-maximum sum (|alpha| times, over each run of 8
+  consecutive k, the largest |product|) and D the error-ratio denominator.
+  The fp8 matrix instruction sums each run of 8 products after truncating
+  them below 2^-13 of the run's largest power of two (measured on gfx950
+  with in-bounds probes), so each of the other 7 products of a run loses
+  less than 2^-13 of the run maximum; runs, slices and C0 are then added in
+  fp32, bounded like the fp32 path.  The general kernel multiplies fp8
+  values exactly in fp32 and meets the same bound with room to spare.
+* Integer operands (|v| <= 4) give exact products, exact run sums (the
+  smallest nonzero product is at most 4 bits below the largest) and sums
+  below 2^24, so every kernel must match the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_gemm_f32_amd as tg
+from tiled_gemm_f32_amd.workloads import make_bias, make_integer_inputs, make_random_inputs
+
+from gpu_helpers import TOL, host_view, run_gemm, say
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32, "fp8f32": tg.GEMM_DTYPE_FP8F32}
+OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+U32 = 2.0 ** -24
+RUN_TRUNC = 7 * 2.0 ** -13
+FP8_RING = "fp8_mfma32_256x256x64_w2x2_nt_ring4"
+
+
+def stored(A, B, op_a, op_b):
+    """The operands as stored for the layout: transposed copies where asked."""
+    return (A.t().contiguous() if op_a == "T" else A), (B.t().contiguous() if op_b == "T" else B)
+
+
+def ref_of(As, Bs, C0, alpha, beta, op_a, op_b):
+    return oracle.gemm_ref(host_view(As), host_view(Bs), alpha, beta, C0.numpy(), op_a, op_b)
+
+
+def check(C, As, Bs, C0, alpha, beta, op_a, op_b, dtype, bias=None, act="none"):
+    """Assert the tolerance above; returns the worst err / allowance."""
+    a, b, c0 = host_view(As), host_view(Bs), C0.numpy()
+    bias_np = bias.numpy() if bias is not None else None
+    ref = oracle.gemm_epilogue_ref(a, b, alpha, beta, c0, bias_np, act, op_a, op_b)
+    D = oracle.gemm_absbound(a, b, alpha, beta, c0, op_a, op_b)
+    if bias_np is not None:
+        D = D + np.abs(bias_np.astype(np.float64))
+    if dtype == "fp8f32":
+        allow = RUN_TRUNC * oracle.gemm_groupmax(a, b, alpha, op_a, op_b) + (2e-6 + U32) * D
+    else:
+        allow = (TOL[dtype] + U32) * D
+    if act == "gelu":
+        z = oracle.gemm_epilogue_ref(a, b, alpha, beta, c0, bias_np, "none", op_a, op_b)
+        allow = 1.13 * allow + 6e-7 * np.abs(z)
+    err = np.abs(np.asarray(C, np.float64) - ref)
+    assert np.all(np.isfinite(err)), "non-finite difference"
+    bad = err > allow
+    assert not np.any(bad), f"{int(bad.sum())} elements out of bound; worst excess {float(np.max(err - allow)):.3e}"
+    nz = allow > 0
+    return float(np.max(err[nz] / allow[nz])) if np.any(nz) else 0.0
+
+
+def kernels_for(dtype, op_a, op_b):
+    bit = 2 * (op_a == "T") + (op_b == "T")
+    return [k for k in tg.kernels() if k["dtype"] == DT[dtype] and (k["layouts"] >> bit) & 1
+            and k["path"] == tg.GEMM_PATH_TILED]
+
+
+def runnable(dtype, op_a, op_b, M, N, K, kid, ws_bytes=0):
+    lda = K if op_a == "N" else M
+    ldb = N if op_b == "N" else K
+    st, pl = tg.gemm_plan_query_general(DT[dtype], 0 if op_a == "N" else 1, 0 if op_b == "N" else 1, M, N, K, 1.0,
+                                        0x1000, lda, 0x1000, ldb, 0.5, 0x1000, N, kid, ws_bytes)
+    return st == tg.GEMM_OK, pl
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32", "fp8f32"])
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+def test_every_kernel_every_layout_exact(gpu_available, dtype, ops):
+    """Integer data through every kernel that runs the layout: bit-exact."""
+    op_a, op_b = ops
+    M, N, K = 300, 264, 208          # ragged tiles; K a multiple of 16 so the fp8 ring runs too
+    A, B, C0 = make_integer_inputs(M, N, K, seed=700, dtype=dtype)
+    As, Bs = stored(A, B, op_a, op_b)
+    ref = ref_of(As, Bs, C0, 2.0, -1.0, op_a, op_b)
+    ran = 0
+    for k in kernels_for(dtype, op_a, op_b):
+        ok, _ = runnable(dtype, op_a, op_b, M, N, K, k["id"])
+        if not ok:
+            continue
+        say(f"[layout exact] {dtype} op_a={op_a} op_b={op_b} kernel={k['name']} M={M} N={N} K={K} seed=700")
+        C, _, _ = run_gemm(As, Bs, C0, 2.0, -1.0, kernel=k["id"], op_a=op_a, op_b=op_b)
+        np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=k["name"])
+        ran += 1
+    assert ran >= 1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32", "fp8f32"])
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+def test_every_kernel_every_layout_random(gpu_available, dtype, ops):
+    op_a, op_b = ops
+    M, N, K = 520, 390, 1040
+    A, B, C0 = make_random_inputs(M, N, K, seed=701, dist="normal", dtype=dtype)
+    As, Bs = stored(A, B, op_a, op_b)
+    for k in kernels_for(dtype, op_a, op_b):
+        ok, _ = runnable(dtype, op_a, op_b, M, N, K, k["id"])
+        if not ok:
+            continue
+        say(f"[layout random] {dtype} op_a={op_a} op_b={op_b} kernel={k['name']} M={M} N={N} K={K} seed=701")
+        C, _, _ = run_gemm(As, Bs, C0, 0.75, 0.5, kernel=k["id"], op_a=op_a, op_b=op_b)
+        r = check(C, As, Bs, C0, 0.75, 0.5, op_a, op_b, dtype)
+        say(f"[layout random] worst err/allowance {r:.3e}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32", "fp8f32"])
+@pytest.mark.parametrize("ops", [("N", "T"), ("T", "N"), ("T", "T")], ids=lambda o: o[0] + o[1])
+def test_padded_and_unaligned_transposed(gpu_available, dtype, ops):
+    """Transposed operands inside padded buffers (NaN padding), bases one
+    element off alignment, C padded: the library's own choice."""
+    op_a, op_b = ops
+    M, N, K = 130, 70, 90
+    A, B, C0 = make_integer_inputs(M, N, K, seed=702, dtype=dtype)
+    As, Bs = stored(A, B, op_a, op_b)
+    say(f"[layout padded] {dtype} op_a={op_a} op_b={op_b} M={M} N={N} K={K} pad=(3,5,2) offset=(1,1,0)")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0, 1.0, pad=(3, 5, 2), offset=(1, 1, 0), op_a=op_a, op_b=op_b)
+    np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, 1.0, 1.0, op_a, op_b))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32", "fp8f32"])
+@pytest.mark.parametrize("ops", OPS, ids=lambda o: o[0] + o[1])
+def test_k_split_every_layout(gpu_available, dtype, ops):
+    """The tiled K split rebases k along rows or down columns by layout."""
+    op_a, op_b = ops
+    M, N, K = 256, 512, 6000
+    ws = tg.workspace(M, N, K, dtype=DT[dtype])
+    ws.fill_(0xFF)
+    A, B, C0 = make_integer_inputs(M, N, K, seed=703, dtype=dtype)
+    As, Bs = stored(A, B, op_a, op_b)
+    ok, pl = runnable(dtype, op_a, op_b, M, N, K, 0, ws.numel())
+    assert ok and pl["splits"] > 1, pl
+    say(f"[layout k-split] {dtype} op_a={op_a} op_b={op_b} M={M} N={N} K={K} splits={pl['splits']} "
+        f"kernel={tg.gemm_kernel_query(pl['kernel_id'])['name']}")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0, 0.5, ws=ws, op_a=op_a, op_b=op_b)
+    np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, 1.0, 0.5, op_a, op_b))
+
+
+# ----------------------------------------------------------------------------- the fp8 ring kernel
+
+FP8_SHAPES = [
+    (256, 256, 64),        # one tile, one slice
+    (1000, 1001, 1040),    # ragged M and N (N not a multiple of 4), a partial last slice
+    (33, 2048, 4096),      # thin M
+    (2048, 40, 2048),      # thin N
+    (1024, 1024, 16),      # K smaller than one slice
+]
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_ring_shapes(gpu_available, shape):
+    """The fp8 ring kernel, forced (small problems would otherwise take the
+    smallest tile), on edge shapes."""
+    M, N, K = shape
+    ring = [k["id"] for k in tg.kernels() if k["name"] == FP8_RING][0]
+    ok, _ = runnable("fp8f32", "N", "T", M, N, K, ring)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=710, dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    say(f"[fp8 ring] exact M={M} N={N} K={K} seed=710")
+    C, _, _ = run_gemm(As, Bs, C0, -1.0, 2.0, kernel=ring, op_b="T")
+    np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, -1.0, 2.0, "N", "T"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=711, dist="normal", dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    say(f"[fp8 ring] random M={M} N={N} K={K} seed=711")
+    C, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_b="T")
+    r = check(C, As, Bs, C0, 0.5, 0.25, "N", "T", "fp8f32")
+    say(f"[fp8 ring] worst err/allowance {r:.3e}")
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+def test_fp8_ring_epilogue_and_unaligned_c(gpu_available, act):
+    M, N, K = 520, 777, 512
+    A, B, C0 = make_random_inputs(M, N, K, seed=712, dist="normal", dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    bias = make_bias(N, seed=713)
+    alpha = 1.0 / np.sqrt(K)
+    ring = [k["id"] for k in tg.kernels() if k["name"] == FP8_RING][0]
+    say(f"[fp8 ring] epilogue act={act} M={M} N={N} K={K} c_offset=1")
+    C, _, _ = run_gemm(As, Bs, C0, alpha, -0.5, kernel=ring, offset=(0, 0, 1), bias=bias, activation=act,
+                       op_b="T")
+    check(C, As, Bs, C0, alpha, -0.5, "N", "T", "fp8f32", bias=bias, act=act)
+
+
+def test_fp8_ring_deterministic_and_bench_shape_sampled(gpu_available):
+    """fp8 8192^3 (A x B^T): integer data exact on sampled rows and columns,
+    normal data within the bound; 5 calls give the same bits."""
+    n = 8192
+    A, B, C0 = make_integer_inputs(n, n, n, seed=714, dtype="fp8f32")
+    Bt = B.t().contiguous()
+    Ad = A.view(torch.uint8).cuda().view(torch.float8_e4m3fn)
+    Bd = Bt.view(torch.uint8).cuda().view(torch.float8_e4m3fn)
+    say(f"[fp8 ring] {n}^3 exact sampled, x5 determinism")
+    outs = [tg.gemm(Ad, Bd, op_b="T") for _ in range(5)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    C = outs[0].cpu().numpy()
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 255, 256, n - 1]) | set(rng.integers(0, n, 6).tolist()))
+    cols = sorted(set([0, 255, 256, n - 1]) | set(rng.integers(0, n, 6).tolist()))
+    a, bt = host_view(A), host_view(Bt)
+    np.testing.assert_array_equal(C[rows].astype(np.float64), oracle.gemm_ref(a[rows], bt, op_b="T"))
+    np.testing.assert_array_equal(C[:, cols].astype(np.float64),
+                                  oracle.gemm_ref(a, np.ascontiguousarray(bt[cols]), op_b="T"))
+    A, B, C0 = make_random_inputs(n, n, n, seed=715, dist="normal", dtype="fp8f32")
+    Bt = B.t().contiguous()
+    Ad = A.view(torch.uint8).cuda().view(torch.float8_e4m3fn)
+    Bd = Bt.view(torch.uint8).cuda().view(torch.float8_e4m3fn)
+    say(f"[fp8 ring] {n}^3 normal sampled")
+    C = tg.gemm(Ad, Bd, op_b="T").cpu().numpy()
+    zero = torch.zeros(len(rows), n)
+    check(C[rows], A[rows], Bt, zero, 1.0, 0.0, "N", "T", "fp8f32")
+    check(C[:, cols], A, Bt[cols].contiguous(), torch.zeros(n, len(cols)), 1.0, 0.0, "N", "T", "fp8f32")

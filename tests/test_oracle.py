@@ -383,6 +383,117 @@ def test_absbound_dominates_result_and_equals_gemm_of_abs():
     np.testing.assert_array_equal(D, oracle.gemm_ref(np.abs(A), np.abs(B), 1.5, 0.25, np.abs(C0)))
 
 
+# ----------------------------------------------------------------------------- fp8 (OCP E4M3) operands
+
+# Code -> value from the E4M3 definition (bias 7; exponent field 0 subnormal
+# m * 2^-9; S.1111.111 NaN; no infinities).
+E4M3_TABLE = [(0x00, 0.0), (0x80, -0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+              (0x30, 0.5), (0x38, 1.0), (0x39, 1.125), (0x3F, 1.875), (0x40, 2.0), (0x7E, 448.0),
+              (0xFE, -448.0), (0xB8, -1.0), (0x77, 240.0), (0x7F, np.nan), (0xFF, np.nan)]
+
+
+@pytest.mark.parametrize("code,value", E4M3_TABLE)
+def test_fp8_widening_follows_format(code, value):
+    one = np.uint8([[0x38]])
+    got = oracle.gemm_ref(np.uint8([[code]]), one)[0, 0]
+    if np.isnan(value):
+        assert np.isnan(got)
+    else:
+        assert got == value          # a sum starts at +0, so the sign of -0 is not kept
+
+
+def test_fp8_every_code_matches_torch_decode():
+    """All 256 codes against torch's float8_e4m3fn decode (independent code)."""
+    codes = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    got = oracle.gemm_ref(codes, np.uint8([[0x38]]))[:, 0]
+    ref = torch.from_numpy(codes[:, 0].copy()).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_fp8_matches_f32_path_on_same_values():
+    rng = np.random.default_rng(30)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    A = rng.choice(codes, size=(9, 37)).astype(np.uint8)
+    B = rng.choice(codes, size=(37, 11)).astype(np.uint8)
+    C0 = rand32(rng, (9, 11))
+    to32 = lambda x: torch.from_numpy(x).view(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(oracle.gemm_ref(A, B, -0.5, 2.0, C0),
+                                  oracle.gemm_ref(to32(A), to32(B), -0.5, 2.0, C0))
+    np.testing.assert_array_equal(oracle.gemm_absbound(A, B, -0.5, 2.0, C0),
+                                  oracle.gemm_absbound(to32(A), to32(B), -0.5, 2.0, C0))
+
+
+def test_fp8_identity():
+    rng = np.random.default_rng(31)
+    B = rng.integers(0, 256, size=(6, 7)).astype(np.uint8)
+    B[B == 0x7F] = 0x38
+    B[B == 0xFF] = 0xB8
+    eye = np.where(np.eye(6, dtype=bool), 0x38, 0x00).astype(np.uint8)
+    vals = torch.from_numpy(B).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(oracle.gemm_ref(eye, B, 2.0), 2.0 * vals)
+
+
+@pytest.mark.parametrize("pa,pb,pc", [(3, 0, 0), (0, 5, 0), (0, 0, 7), (1, 2, 3)])
+def test_fp8_leading_dimensions_honoured(pa, pb, pc):
+    """fp8 views into padded buffers (padding bytes 0x7F, NaN) equal packed copies."""
+    rng = np.random.default_rng(34)
+    M, N, K = 10, 12, 9
+    A = rng.integers(0, 0x7E, size=(M, K)).astype(np.uint8)
+    B = rng.integers(0x80, 0xFE, size=(K, N)).astype(np.uint8)
+    C0 = rand32(rng, (M, N))
+    want = oracle.gemm_ref(A, B, 2.0, -1.0, C0)
+    got = oracle.gemm_ref(padded(A, pa, 0x7F), padded(B, pb, 0x7F), 2.0, -1.0, padded(C0, pc))
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(oracle.gemm_groupmax(padded(A, pa, 0x7F), padded(B, pb, 0x7F), 2.0),
+                                  oracle.gemm_groupmax(A, B, 2.0))
+
+
+# ----------------------------------------------------------------------------- operand layouts
+
+@pytest.mark.parametrize("dt", [np.float32, np.uint16, np.uint8])
+def test_transposed_layouts_multiply_the_transpose(dt):
+    """op(X) = X^T: passing A^T with op_a = "T" (and B^T with op_b = "T")
+    gives the plain product; and C^T = B^T A^T swaps the roles."""
+    rng = np.random.default_rng(32)
+    if dt == np.float32:
+        A, B = rand32(rng, (5, 9)), rand32(rng, (9, 4))
+    else:
+        A = rng.integers(0, 0x3F, size=(5, 9)).astype(dt)      # finite, positive codes
+        B = rng.integers(0, 0x3F, size=(9, 4)).astype(dt)
+    ref = oracle.gemm_ref(A, B, 1.5)
+    At, Bt = np.ascontiguousarray(A.T), np.ascontiguousarray(B.T)
+    np.testing.assert_array_equal(oracle.gemm_ref(At, B, 1.5, op_a="T"), ref)
+    np.testing.assert_array_equal(oracle.gemm_ref(A, Bt, 1.5, op_b="T"), ref)
+    np.testing.assert_array_equal(oracle.gemm_ref(At, Bt, 1.5, op_a="T", op_b="T"), ref)
+    np.testing.assert_array_equal(oracle.gemm_ref(B, A, 1.5, op_a="T", op_b="T"), ref.T)
+    with pytest.raises(ValueError):
+        oracle.gemm_ref(A, B, op_a="X")
+
+
+# ----------------------------------------------------------------------------- fp8 group bound
+
+@pytest.mark.parametrize("K", [1, 7, 8, 9, 64, 70])
+def test_groupmax_all_ones_counts_runs(K):
+    ones_a = np.full((3, K), 0x38, np.uint8)
+    ones_b = np.full((K, 5), 0x38, np.uint8)
+    np.testing.assert_array_equal(oracle.gemm_groupmax(ones_a, ones_b, -2.0), np.full((3, 5), 2.0 * -(-K // 8)))
+
+
+def test_groupmax_bruteforce():
+    rng = np.random.default_rng(33)
+    A = rng.integers(0, 0x7E, size=(4, 21)).astype(np.uint8) | (rng.integers(0, 2, size=(4, 21)) << 7).astype(np.uint8)
+    B = rng.integers(0, 0x7E, size=(21, 3)).astype(np.uint8)
+    a = torch.from_numpy(A).view(torch.float8_e4m3fn).double().numpy()
+    b = torch.from_numpy(B).view(torch.float8_e4m3fn).double().numpy()
+    G = oracle.gemm_groupmax(A, B, 0.5)
+    for i in range(4):
+        for j in range(3):
+            expect = sum(max(abs(a[i, k] * b[k, j]) for k in range(q, min(q + 8, 21))) for q in range(0, 21, 8))
+            assert G[i, j] == 0.5 * expect
+    D = oracle.gemm_absbound(A, B, 0.5)
+    assert np.all(G <= D) and np.all(8 * G >= D)
+
+
 # ----------------------------------------------------------------------------- fused epilogue
 # act(Z + bias) on a finished GEMM result ("Tiled matrix multiplication",
 # "Efficiency" and "Implementation notes").  ReLU and GELU are pinned by

@@ -56,6 +56,14 @@ MUTANTS = [
     ("gelu_sqrt2_dropped", [("erf(z * inv_sqrt2)", "erf(z)", 0)]),
     ("gelu_half_dropped", [("z = 0.5 * z * (1.0 + erf", "z = z * (1.0 + erf", 0)]),
     ("gelu_erf_sign", [("(1.0 + erf(", "(1.0 - erf(", 0)]),
+    ("e4m3_bias_wrong", [("v = ldexp(8.0 + m, e - 10);", "v = ldexp(8.0 + m, e - 9);", 0)]),
+    ("e4m3_subnormal_scale", [("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);", 0)]),
+    ("e4m3_nan_missing", [("if (e == 15 && m == 7)\n        v = NAN;", "if (0)\n        v = NAN;", 0)]),
+    ("e4m3_sign_ignored", [("return (bits & 0x80) ? -v : v;", "return v;", 0)]),
+    ("fp8_beta_dropped", [("v += beta * (double)C0[i * ldc0 + j];", "(void)0;", 2)]),
+    ("fp8_B_row_stride_ignored", [("const uint8_t *brow = B + k * ldb;", "const uint8_t *brow = B + k * N;", 0)]),
+    ("groupmax_run_of_7", [("if (k % 8 == 7 || k == K - 1)", "if (k % 7 == 6 || k == K - 1)", 0)]),
+    ("groupmax_sum_not_max", [("if (p > run[j])\n                    run[j] = p;", "run[j] += p;", 0)]),
 ]
 
 

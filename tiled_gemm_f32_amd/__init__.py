@@ -10,8 +10,8 @@ reads shapes, strides and pointers and forwards them.
 from __future__ import annotations
 
 from ._lib import (  # noqa: F401  (re-exported C ABI)
-    EXPORTED, GEMM_ACT_GELU, GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, Epilogue,
-    gemm_bf16f32_epi, gemm_f32_epi, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
+    EXPORTED, GEMM_ACT_GELU, GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, GEMM_DTYPE_FP8F32,
+    GEMM_OP_N, GEMM_OP_T, Epilogue, gemm_bf16f32_epi, gemm_f32_epi, gemm_general, gemm_plan_query_general, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
     gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
 
 __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
            "gemm_f32_epi", "gemm_bf16f32_epi", "Epilogue", "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU",
+           "gemm_general", "gemm_plan_query_general", "GEMM_DTYPE_FP8F32", "GEMM_OP_N", "GEMM_OP_T",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
            "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune", "gemm_tuning_count",
            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load"]
@@ -49,30 +50,47 @@ def workspace(M: int, N: int, K: int, device=None, dtype: int = GEMM_DTYPE_F32):
 _ACTIVATIONS = {None: GEMM_ACT_NONE, "none": GEMM_ACT_NONE, "relu": GEMM_ACT_RELU, "gelu": GEMM_ACT_GELU}
 
 
-def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None, ws=None,
-         bias=None, activation=None):
-    """C = act(alpha * (A @ B) + beta * C + bias) on the current stream; returns C.
+def _dtype_of(t):
+    import torch
+    if t.dtype == torch.float32:
+        return GEMM_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return GEMM_DTYPE_BF16F32
+    if t.dtype == torch.float8_e4m3fn:
+        return GEMM_DTYPE_FP8F32
+    raise TypeError(f"operands must be float32, bfloat16 or float8_e4m3fn (got {t.dtype})")
 
-    A (M x K) and B (K x N) are CUDA tensors of dtype float32 (fp32 path) or
-    bfloat16 (bf16 operands, fp32 accumulate); C is float32 (M x N),
-    allocated when None (then beta must be 0).  All three must be row-major
-    with unit stride along columns; padded leading dimensions are fine.
-    ``kernel`` forces a kernel id (0 = library choice).  ``ws`` is an optional
-    device workspace tensor (see ``workspace()``) for the split-K paths.
-    ``bias`` is an optional float32 device tensor of N elements added to every
-    row; ``activation`` is None, "relu", "gelu" or a GEMM_ACT_* value.  Both
-    are applied inside the kernels' epilogue.
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None, ws=None,
+         bias=None, activation=None, op_a: str = "N", op_b: str = "N"):
+    """C = act(alpha * (op(A) @ op(B)) + beta * C + bias) on the current stream; returns C.
+
+    A and B are CUDA tensors of one dtype: float32 (fp32 path), bfloat16
+    (bf16 operands, fp32 accumulate) or float8_e4m3fn (fp8 operands, fp32
+    accumulate).  ``op_a="T"`` means A is passed transposed (K x M), and
+    ``op_b="T"`` that B is passed transposed (N x K); otherwise A is M x K and
+    B is K x N.  C is float32 (M x N), allocated when None (then beta must be
+    0).  All tensors must be row-major with unit stride along columns; padded
+    leading dimensions are fine.  ``kernel`` forces a kernel id (0 = library
+    choice).  ``ws`` is an optional device workspace tensor (see
+    ``workspace()``) for the split-K paths.  ``bias`` is an optional float32
+    device tensor of N elements added to every row; ``activation`` is None,
+    "relu", "gelu" or a GEMM_ACT_* value.  Both are applied inside the
+    kernels' epilogue.
     """
     import torch
 
-    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError(f"A and B must both be float32 or both bfloat16 (got {A.dtype}, {B.dtype})")
+    if A.dtype != B.dtype:
+        raise TypeError(f"A and B must have one dtype (got {A.dtype}, {B.dtype})")
+    dt = _dtype_of(A)
     if not (A.is_cuda and B.is_cuda):
         raise ValueError("A and B must be device tensors")
-    M, K = A.shape
-    K2, N = B.shape
+    if op_a not in ("N", "T") or op_b not in ("N", "T"):
+        raise ValueError("op_a and op_b are 'N' or 'T'")
+    M, K = A.shape if op_a == "N" else (A.shape[1], A.shape[0])
+    K2, N = B.shape if op_b == "N" else (B.shape[1], B.shape[0])
     if K2 != K:
-        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} x {tuple(B.shape)}")
+        raise ValueError(f"inner dimensions differ: op_a={op_a} {tuple(A.shape)}, op_b={op_b} {tuple(B.shape)}")
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
@@ -90,12 +108,15 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
             raise ValueError(f"bias must be a contiguous float32 device tensor of {N} elements")
         epi = Epilogue(bias.data_ptr() if bias is not None else None, act)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc)
+    ops = (GEMM_OP_N if op_a == "N" else GEMM_OP_T, GEMM_OP_N if op_b == "N" else GEMM_OP_T)
     with torch.cuda.device(A.device):
         wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
-        if A.dtype == torch.float32:
+        if dt == GEMM_DTYPE_F32 and ops == (GEMM_OP_N, GEMM_OP_N):
             st = gemm_f32_ex(*args, kernel, epi, wp, wb, stream)
-        else:
+        elif dt == GEMM_DTYPE_BF16F32 and ops == (GEMM_OP_N, GEMM_OP_N):
             st = gemm_bf16f32_ex(*args, kernel, epi, wp, wb, stream)
+        else:
+            st = gemm_general(dt, ops[0], ops[1], *args, kernel, epi, wp, wb, stream)
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
     return C
@@ -107,7 +128,7 @@ def autotune(A, B, C, alpha: float = 1.0, beta: float = 0.0, ws=None, reps: int 
     import torch
     M, K = A.shape
     N = B.shape[1]
-    dt = GEMM_DTYPE_F32 if A.dtype == torch.float32 else GEMM_DTYPE_BF16F32
+    dt = _dtype_of(A)
     wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream

@@ -28,6 +28,10 @@ GEMM_PATH_SKINNY_SPLITK = 4
 
 GEMM_DTYPE_F32 = 0
 GEMM_DTYPE_BF16F32 = 1
+GEMM_DTYPE_FP8F32 = 2
+
+GEMM_OP_N = 0
+GEMM_OP_T = 1
 
 GEMM_ACT_NONE = 0
 GEMM_ACT_RELU = 1
@@ -37,14 +41,15 @@ GEMM_ACT_GELU = 2
 EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
             "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws", "gemm_autotune", "gemm_tuning_count",
-            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_f32_epi", "gemm_bf16f32_epi")
+            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_f32_epi", "gemm_bf16f32_epi",
+            "gemm_general", "gemm_plan_query_general")
 
 
 class KernelInfo(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int32), ("dtype", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
-                ("name", ctypes.c_char_p)]
+                ("name", ctypes.c_char_p), ("layouts", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -93,6 +98,11 @@ def load() -> ctypes.CDLL:
     lib.gemm_f32_ex.argtypes = gemm_sig + [i32, epi, vp, i64, vp]
     lib.gemm_bf16f32_ex.argtypes = gemm_sig + [i32, epi, vp, i64, vp]
     lib.gemm_f32_epi.argtypes = gemm_sig + [epi, vp, i64, vp]
+    lib.gemm_general.argtypes = [i32, i32, i32] + gemm_sig + [i32, epi, vp, i64, vp]
+    lib.gemm_general.restype = ctypes.c_int
+    lib.gemm_plan_query_general.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32,
+                                            i64, ctypes.POINTER(Plan)]
+    lib.gemm_plan_query_general.restype = ctypes.c_int
     lib.gemm_bf16f32_epi.argtypes = gemm_sig + [epi, vp, i64, vp]
     lib.gemm_f32_ws.argtypes = gemm_sig + [vp, i64, vp]
     lib.gemm_bf16f32_ws.argtypes = gemm_sig + [vp, i64, vp]
@@ -168,6 +178,21 @@ def gemm_bf16f32_epi(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, epilogue, wor
 def gemm_bf16f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream=0) -> int:
     return load().gemm_bf16f32_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes,
                                   stream)
+
+
+def gemm_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0, epilogue=None,
+                 workspace=0, workspace_bytes=0, stream=0) -> int:
+    return load().gemm_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel,
+                               _epi(epilogue), workspace, workspace_bytes, stream)
+
+
+def gemm_plan_query_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0,
+                            workspace_bytes=0):
+    """(status, plan dict) for the choice gemm_general would make."""
+    pl = Plan()
+    st = load().gemm_plan_query_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                        force_kernel, workspace_bytes, ctypes.byref(pl))
+    return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
 
 
 def gemm_status_string(status: int) -> str:

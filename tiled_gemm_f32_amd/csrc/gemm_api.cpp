@@ -33,7 +33,7 @@ constexpr int kComputeUnits = 256;
 
 int table_size() {
     return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
-           gemm::kF32SplitKernelCount;
+           gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -46,6 +46,10 @@ const KernelDesc *kernel_by_id(int32_t id) {
     if (i < gemm::kF32SkinnyKernelCount) return &gemm::kF32SkinnyKernels[i];
     i -= gemm::kF32SkinnyKernelCount;
     if (i < gemm::kF32SplitKernelCount) return &gemm::kF32SplitKernels[i];
+    i -= gemm::kF32SplitKernelCount;
+    if (i < gemm::kFp8TiledKernelCount) return &gemm::kFp8TiledKernels[i];
+    i -= gemm::kFp8TiledKernelCount;
+    if (i < gemm::kGeneralKernelCount) return &gemm::kGeneralKernels[i];
     return nullptr;
 }
 
@@ -61,6 +65,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Call {
     int32_t dtype;
+    int32_t op_a, op_b;    // gemm_op layouts
     int64_t M, N, K;
     float alpha, beta;
     const void *A, *B;
@@ -72,15 +77,26 @@ struct Call {
     int32_t act;           // gemm_activation
 };
 
+int elem_size(int32_t dtype) { return dtype == GEMM_DTYPE_F32 ? 4 : dtype == GEMM_DTYPE_BF16F32 ? 2 : 1; }
+
+// Length of each operand's stored rows (its contiguous dimension).
+int64_t row_len_a(const Call &c) { return c.op_a == GEMM_OP_N ? c.K : c.M; }
+int64_t row_len_b(const Call &c) { return c.op_b == GEMM_OP_N ? c.N : c.K; }
+
 gemm_status validate(const Call &c) {
-    if (c.dtype != GEMM_DTYPE_F32 && c.dtype != GEMM_DTYPE_BF16F32) return GEMM_ERR_INVALID_ARG;
+    if (c.dtype != GEMM_DTYPE_F32 && c.dtype != GEMM_DTYPE_BF16F32 && c.dtype != GEMM_DTYPE_FP8F32)
+        return GEMM_ERR_INVALID_ARG;
+    if ((c.op_a != GEMM_OP_N && c.op_a != GEMM_OP_T) || (c.op_b != GEMM_OP_N && c.op_b != GEMM_OP_T))
+        return GEMM_ERR_INVALID_ARG;
     if (c.M < 0 || c.N < 0 || c.K < 0) return GEMM_ERR_INVALID_ARG;
-    const int64_t min_lda = c.K > 1 ? c.K : 1, min_n = c.N > 1 ? c.N : 1;
-    if (c.lda < min_lda || c.ldb < min_n || c.ldc < min_n) return GEMM_ERR_INVALID_ARG;
+    const int64_t min_lda = row_len_a(c) > 1 ? row_len_a(c) : 1;
+    const int64_t min_ldb = row_len_b(c) > 1 ? row_len_b(c) : 1;
+    const int64_t min_ldc = c.N > 1 ? c.N : 1;
+    if (c.lda < min_lda || c.ldb < min_ldb || c.ldc < min_ldc) return GEMM_ERR_INVALID_ARG;
     if (c.ws_bytes < 0 || (c.ws != nullptr && !aligned(c.ws, 4))) return GEMM_ERR_INVALID_ARG;
     if (c.act < GEMM_ACT_NONE || c.act > GEMM_ACT_GELU) return GEMM_ERR_INVALID_ARG;
     if (c.bias != nullptr && !aligned(c.bias, 4)) return GEMM_ERR_INVALID_ARG;
-    const uintptr_t esz = c.dtype == GEMM_DTYPE_F32 ? 4 : 2;
+    const uintptr_t esz = (uintptr_t)elem_size(c.dtype);
     if (c.M > 0 && c.N > 0) {
         if (c.C == nullptr || !aligned(c.C, 4)) return GEMM_ERR_INVALID_ARG;
         if (c.K > 0 && c.alpha != 0.0f) {
@@ -96,15 +112,14 @@ gemm_status validate(const Call &c) {
 // Widest vector loads each operand allows: 16-byte aligned base, leading
 // dimension and extent along the contiguous axis multiples of the width (so
 // a vector is either wholly inside the valid region or wholly outside).
+bool vec_ok(const void *p, int64_t ld, int64_t row_len, int esz, int v) {
+    return v == 1 || (aligned(p, (uintptr_t)(esz * v)) && ld % v == 0 && row_len % v == 0);
+}
 int max_vec_a(const Call &c) {
-    const int w = c.dtype == GEMM_DTYPE_F32 ? 4 : 8;
-    return (aligned(c.A, 16) && c.lda % w == 0 && c.K % w == 0) ? w : 1;
+    const int esz = elem_size(c.dtype), w = 16 / esz;
+    return vec_ok(c.A, c.lda, row_len_a(c), esz, w) ? w : 1;
 }
-bool vec_b_ok(const Call &c, int v) {
-    if (v == 1) return true;
-    const uintptr_t esz = c.dtype == GEMM_DTYPE_F32 ? 4 : 2;
-    return aligned(c.B, esz * v) && c.ldb % v == 0 && c.N % v == 0;
-}
+bool vec_b_ok(const Call &c, int v) { return vec_ok(c.B, c.ldb, row_len_b(c), elem_size(c.dtype), v); }
 
 // The skinny kernels address B with 32-bit offsets; their prefetch runs at
 // most 48 * WAVES * UNROLL (<= 1536) rows past K, so K + 2048 rows must fit.
@@ -119,6 +134,7 @@ int64_t split_workspace_bytes(const Call &c, const KernelDesc *kd) {
 
 bool kernel_runs(const KernelDesc *kd, const Call &c) {
     if (kd->dtype != c.dtype) return false;
+    if (((kd->layouts >> (2 * c.op_a + c.op_b)) & 1) == 0) return false;
     if ((kd->path == GEMM_PATH_SKINNY || kd->path == GEMM_PATH_SKINNY_SPLITK) && !skinny_fits(c)) return false;
     if (kd->path == GEMM_PATH_SKINNY_SPLITK) {
         const int64_t need = split_workspace_bytes(c, kd);
@@ -174,20 +190,42 @@ const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c,
     return nullptr;
 }
 
+// The tiled kernels of the call's operand type that run its layout, in
+// table order (which is preference order: the general kernels come last).
+struct Candidates {
+    const KernelDesc *k[64];
+    int n = 0;
+};
+Candidates tiled_candidates(const Call &c) {
+    Candidates r;
+    for (int32_t id = 1; id <= table_size() && r.n < 64; ++id) {
+        const KernelDesc *kd = kernel_by_id(id);
+        if (kd->path == GEMM_PATH_TILED && kd->dtype == c.dtype && ((kd->layouts >> (2 * c.op_a + c.op_b)) & 1))
+            r.k[r.n++] = kd;
+    }
+    return r;
+}
+const KernelDesc *first_candidate(const Candidates &cand, const Call &c, int tile_m) {
+    for (int i = 0; i < cand.n; ++i)
+        if ((tile_m == 0 || cand.k[i]->tile_m == tile_m) && c.K >= cand.k[i]->min_k && kernel_runs(cand.k[i], c))
+            return cand.k[i];
+    return nullptr;
+}
+
 // Tile choice: the largest square tile whose tile count covers every compute
 // unit at least once; small problems fall through to the smallest tile.
 const KernelDesc *choose(const Call &c) {
+    const bool plain = c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_N;
     // The split-K kernels pay off only where K is actually split.
-    if (c.dtype == GEMM_DTYPE_F32 && skinny_fits(c) && c.ws != nullptr) {
+    if (plain && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c) && c.ws != nullptr) {
         const KernelDesc *kd = first_match(gemm::kF32SplitKernels, gemm::kF32SplitKernelCount, c, 0);
         if (kd != nullptr && split_workspace_bytes(c, kd) > 0) return kd;
     }
-    if (c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
+    if (plain && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kF32SkinnyKernels, gemm::kF32SkinnyKernelCount, c, 0))
             return kd;
     }
-    const KernelDesc *table = c.dtype == GEMM_DTYPE_F32 ? gemm::kF32TiledKernels : gemm::kBf16TiledKernels;
-    const int count = c.dtype == GEMM_DTYPE_F32 ? gemm::kF32TiledKernelCount : gemm::kBf16TiledKernelCount;
+    const Candidates cand = tiled_candidates(c);
     // With a workspace: the largest tile that wastes at most a quarter of
     // its padded M x N ("The fringe and the last wave": tile quantisation)
     // and whose grid of tiles x K slices fills at least three quarters of the
@@ -196,7 +234,7 @@ const KernelDesc *choose(const Call &c) {
     // tiles even when a large tile would have enough slices.
     if (c.ws != nullptr) {
         for (int tile : {256, 128, 64}) {
-            const KernelDesc *kd = first_match(table, count, c, tile);
+            const KernelDesc *kd = first_candidate(cand, c, tile);
             if (kd == nullptr) continue;
             const int64_t pm = ceil_div(c.M, tile) * tile, pn = ceil_div(c.N, tile) * tile;
             const KSplit ks = call_ksplit(c, kd);
@@ -204,15 +242,17 @@ const KernelDesc *choose(const Call &c) {
             if (4 * c.M * c.N >= 3 * pm * pn && 4 * groups >= 3 * kComputeUnits) return kd;
         }
     }
+    // The smallest tile among the kernels that can run the call.
     int smallest = 1 << 30;
-    for (int i = 0; i < count; ++i) smallest = table[i].tile_m < smallest ? table[i].tile_m : smallest;
+    for (int i = 0; i < cand.n; ++i)
+        if (kernel_runs(cand.k[i], c) && cand.k[i]->tile_m < smallest) smallest = cand.k[i]->tile_m;
     for (int tile : {256, 128, 64}) {
         const int64_t tiles = ceil_div(c.M, tile) * ceil_div(c.N, tile);
         if (tiles >= kComputeUnits || tile == smallest) {
-            if (const KernelDesc *kd = first_match(table, count, c, tile)) return kd;
+            if (const KernelDesc *kd = first_candidate(cand, c, tile)) return kd;
         }
     }
-    return first_match(table, count, c, 0);
+    return first_candidate(cand, c, 0);
 }
 
 // Per-shape tuning ("A GEMM Kernel, Step by Step", "Six parameters, found by
@@ -240,7 +280,7 @@ std::mutex g_tune_mu;
 std::map<TuneKey, TuneEntry> g_tuned;
 
 int max_vec_b(const Call &c) {
-    const int w = c.dtype == GEMM_DTYPE_F32 ? 4 : 8;
+    const int w = 16 / elem_size(c.dtype);
     return vec_b_ok(c, w) ? w : 1;
 }
 
@@ -250,6 +290,7 @@ TuneKey tune_key(const Call &c) {
 
 // A tuned choice for this call, if one was recorded and still fits it.
 bool tuned_choice(const Call &c, const KernelDesc **kd, bool *allow_split) {
+    if (c.op_a != GEMM_OP_N || c.op_b != GEMM_OP_N) return false;     // tuning covers untransposed operands
     std::lock_guard<std::mutex> lock(g_tune_mu);
     auto it = g_tuned.find(tune_key(c));
     if (it == g_tuned.end()) return false;
@@ -356,6 +397,8 @@ gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, con
         p.ldc = c.ldc;
         p.alpha = c.alpha;
         p.beta = c.beta;
+        p.op_a = c.op_a;
+        p.op_b = c.op_b;
         p.kchunk = 0;
         p.partials = nullptr;
         p.bias = c.bias;
@@ -440,6 +483,8 @@ Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, cons
     c.bias = nullptr;
     c.act = GEMM_ACT_NONE;
     c.dtype = dtype;
+    c.op_a = GEMM_OP_N;
+    c.op_b = GEMM_OP_N;
     c.M = M;
     c.N = N;
     c.K = K;
@@ -530,7 +575,8 @@ GEMM_API gemm_status gemm_f32_ex(int64_t M, int64_t N, int64_t K, float alpha, c
 }
 
 GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K) {
-    if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16F32) || M <= 0 || N <= 0 || K <= 0 ||
+    if ((dtype != GEMM_DTYPE_F32 && dtype != GEMM_DTYPE_BF16F32 && dtype != GEMM_DTYPE_FP8F32) || M <= 0 ||
+        N <= 0 || K <= 0 ||
         M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return 0;
     int64_t need = 0;
@@ -556,6 +602,30 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
     return run_epi(make_call(GEMM_DTYPE_BF16F32, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                              workspace_bytes),
                    epilogue, force_kernel, stream);
+}
+
+GEMM_API gemm_status gemm_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N, int64_t K,
+                                  float alpha, const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+                                  float *C, int64_t ldc, int32_t force_kernel, const gemm_epilogue *epilogue,
+                                  void *workspace, int64_t workspace_bytes, gemm_stream_t stream) {
+    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes);
+    c.op_a = op_a;
+    c.op_b = op_b;
+    return run_epi(c, epilogue, force_kernel, stream);
+}
+
+GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                             int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                             int64_t ldb, float beta, const float *C, int64_t ldc,
+                                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out) {
+    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+    const KernelDesc *kd = nullptr;
+    void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
+    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
+    c.op_a = op_a;
+    c.op_b = op_b;
+    KSplit ks;
+    return plan(c, force_kernel, out, &kd, &ks);
 }
 
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
@@ -659,6 +729,7 @@ GEMM_API gemm_status gemm_kernel_query(int32_t id, gemm_kernel_info *out) {
     out->vec_a = kd->vec_a;
     out->vec_b = kd->vec_b;
     out->name = kd->name;
+    out->layouts = kd->layouts;
     return GEMM_OK;
 }
 

@@ -137,8 +137,10 @@ template <typename T>
 __device__ __forceinline__ void apply_k_split(GemmParams &p) {
     if (p.kchunk <= 0) return;
     const int kb = (int)blockIdx.y * p.kchunk;
-    p.A = static_cast<const T *>(p.A) + kb;
-    p.B = static_cast<const T *>(p.B) + (int64_t)kb * p.ldb;
+    // k runs along a row of an untransposed A and a transposed B, down the
+    // columns otherwise.
+    p.A = static_cast<const T *>(p.A) + (p.op_a == GEMM_OP_N ? (int64_t)kb : (int64_t)kb * p.lda);
+    p.B = static_cast<const T *>(p.B) + (p.op_b == GEMM_OP_N ? (int64_t)kb * p.ldb : (int64_t)kb);
     p.K = min(p.K - kb, p.kchunk);
     p.C = p.partials + (int64_t)blockIdx.y * p.M * p.N;
     p.ldc = p.N;

@@ -1,0 +1,234 @@
+// fp8 (OCP E4M3) GEMM on the gfx950 matrix cores, A untransposed (M x K)
+// times B transposed (stored N x K), fp32 accumulate and output.
+//
+// With both operands stored k-contiguous, this is the bf16 ring kernel with
+// both panels handled the way it handles A ("Tiled matrix multiplication",
+// "How it works", at the tensor-core level; "A GEMM Kernel, Step by Step",
+// "What is left": asynchronous copies into a multi-stage ring).  The fp8
+// product instruction v_mfma_f32_32x32x64_f8f6f4 takes 64 k per call, so a
+// 64-byte k slice of a row feeds exactly one instruction per fragment pair:
+// the same bytes and the same 64 matrix cycles per slice as the bf16 kernel,
+// for twice the multiply-adds.
+//
+//   Both slices: [256 rows][4 chunks of 16 B] (k contiguous),
+//     chunk ^= (row >> 2) & 3 (the A layout of the bf16 ring, measured free
+//     of bank conflicts there; the reads below have the same pattern).
+//   Fragments: lane (h, l32) of a 32-row fragment holds bytes 32h .. 32h+31
+//     of its row's slice (k = 32h .. 32h+31), read as two 16-byte ds_read_b128.
+//     The instruction pairs byte b of an A lane with byte b of the B lane of
+//     the same half, whatever its internal k order, so equal placement on
+//     both sides gives the dot product.  It sums each run of 8 bytes (8
+//     consecutive k here) at reduced precision before adding runs in fp32.
+//
+// Schedule, per slice kt (stage kt % NS, register set kt % 2): every wave
+// waits for its own reads of slice kt and for slice kt+1 to land, then a
+// barrier; then 16 matrix instructions on slice kt, each paired with one of
+// the 16 fragment reads of slice kt+1 (into the other register set) and,
+// every other one, with one of the 8 loads that refill stage kt % NS with
+// slice kt + NS.  The pairs are pinned with sched_barrier.
+#include "gemm_device.hpp"
+#include "gemm_kernels.hpp"
+#include "gemm.h"
+
+namespace gemm {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int fp8_swz(int row) { return (row >> 2) & 3; }
+
+template <int NS, int GROUP_M>
+__global__ void __launch_bounds__(256)
+fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint8_t>(p);
+    static_assert(NS == 4, "the stage arrays and the register-set parity assume four stages");
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int kA = BM * BK;          // 16 KB of A per slice
+    constexpr int kB = BN * BK;          // 16 KB of B per slice
+    constexpr int kStage = kA + kB;
+    __shared__ __attribute__((aligned(1024))) char st0[kStage], st1[kStage], st2[kStage], st3[kStage];
+    auto stage_base = [&](int st) -> char * { return st == 0 ? st0 : st == 1 ? st1 : st == 2 ? st2 : st3; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, GROUP_M, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint8_t *A = static_cast<const uint8_t *>(p.A);
+    const uint8_t *B = static_cast<const uint8_t *>(p.B);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+
+    // Load instruction j (0..3) of this wave fills 1 KB block 4*wave + j of a
+    // panel: rows 16*blk .. +15, lane -> row 16*blk + lane/4, physical chunk
+    // lane%4, which holds logical chunk (lane%4) ^ swizzle(row).
+    uint32_t goff_a[4], goff_b[4];
+    int kc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 16 * (4 * wave + j) + (lane >> 2);
+        const int lc = (lane & 3) ^ fp8_swz(row);
+        kc[j] = 16 * lc;
+        goff_a[j] = (uint32_t)(row * lda + 16 * lc);
+        goff_b[j] = (uint32_t)(row * ldb + 16 * lc);
+    }
+    // Resources of slice kt, rebased per slice.  Rows past M (or N) and
+    // slices past K fall outside the extents; a chunk at or past K in a valid
+    // row gets 2^31 added to its offset.
+    auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
+        const int k0 = kt * BK;
+        ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent((int64_t)(a_rows - 1) * lda + (K - k0)));
+        rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent((int64_t)(b_rows - 1) * ldb + (K - k0)));
+    };
+    // Load instruction j (0..7) of slice kt into `stage`: j < 4 fills A block
+    // 4*wave + j, j >= 4 fills B block 4*wave + j - 4.
+    auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
+        const int jj = j & 3;
+        const uint32_t poison = (uint32_t)(kc[jj] >= K - kt * BK) << 31;
+        char *dst = stage_base(stage) + (j < 4 ? 0 : kA) + (4 * wave + jj) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 4 ? ra : rb, (lds_void *)dst, 16,
+                                                 (j < 4 ? goff_a[jj] : goff_b[jj]) + poison, 0, 0, 0);
+    };
+    // Fragment reads: lane (h, l32) of fragment f reads row 32*f + l32 of the
+    // wave's 128-row block, logical chunks 2h and 2h+1.
+    const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int sw = fp8_swz(l32);
+    const uint32_t ch0 = 16 * ((2 * h) ^ sw), ch1 = 16 * ((2 * h + 1) ^ sw);
+    const uint32_t fa_row = (uint32_t)((wm * 128 + l32) * BK);
+    const uint32_t fb_row = (uint32_t)(kA + (wn * 128 + l32) * BK);
+
+    i32x8 fa[2][4], fb[2][4];
+    // Read r (0..15) of the slice in `stage` into register set `set`: reads
+    // 0..7 are the two halves of A fragments 0..3, reads 8..15 of B's.
+    auto read_slot = [&](int stage, int set, int r) {
+        const char *base = stage_base(stage);
+        const int f = (r >> 1) & 3;
+        const uint32_t off = (r < 8 ? fa_row : fb_row) + 32 * BK * f + ((r & 1) ? ch1 : ch0);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + off);
+        i32x8 &dst = r < 8 ? fa[set][f] : fb[set][f];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * (r & 1) + e] = (int)v[e];
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    // B^T as the first operand and A^T as the second, as in the bf16 ring:
+    // each lane then holds runs of 4 consecutive columns of one row of C.
+    auto mma = [&](int set, int t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0, 0,
+                                                                     0, 0);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    {
+        rsrc_t ra, rb;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            slice_rsrc(st, ra, rb);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dma(st, st, ra, rb, j);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 1)));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read_slot(0, 0, r);
+    for (int kb = 0; kb < nk; kb += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int kt = kb + u;
+            // This wave's reads of slice kt are done and slice kt+1 has
+            // landed; after the barrier, for every wave.
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 2)));
+            __builtin_amdgcn_s_barrier();
+            rsrc_t ra, rb;
+            slice_rsrc(kt + NS, ra, rb);      // zeros past the end
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                mma(u & 1, t);
+                read_slot((u + 1) % NS, (u + 1) & 1, t);
+                if ((t & 1) == 0) dma(kt + NS, u, ra, rb, t >> 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+
+    // Epilogue.  Register 4g + t of lane (h, l32) in fragment (fm, fn) is
+    // C[row m0 + wm*128 + 32*fm + l32][column n0 + wn*128 + 32*fn + 8*g + 4*h + t].
+    // A run of 4 columns may straddle N (no constraint on N here): such runs,
+    // and C without 16-byte alignment, take element accesses.  One branch on
+    // the activation for the whole tile keeps the accumulators in registers.
+    const float alpha = p.alpha, beta = p.beta;
+    const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
+    with_activation(p.act, [&](auto act) {
+        using Act = decltype(act);
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
+                if (col >= N) continue;
+                const bool whole = vec_c && col + 4 <= N;
+                float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+#pragma unroll
+                for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col + t < N) ? p.bias[col + t] : -0.0f;
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) {
+                    const int row = m0 + wm * 128 + 32 * fm + l32;
+                    if (row >= M) continue;
+                    float *cp = p.C + (int64_t)row * p.ldc + col;
+                    f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
+                               alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
+                    if (whole) {
+                        if (beta != 0.0f) {
+                            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cp);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
+                        }
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
+                        *reinterpret_cast<f32x4 *>(cp) = v;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            if (col + t >= N) continue;
+                            float x = v[t];
+                            if (beta != 0.0f) x = fmaf(beta, cp[t], x);
+                            cp[t] = Act::apply(x + b[t]);
+                        }
+                    }
+                }
+            }
+        }
+    });
+}
+
+template <int NS, int GROUP_M>
+hipError_t launch_fp8_ring(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M>),
+                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
+}
+
+template __global__ void fp8_ring_kernel<4, 4>(GemmParams, int, int);
+
+}  // namespace
+
+#if !defined(__HIP_DEVICE_COMPILE__)
+// vec_a = vec_b = 16: A, B, lda, ldb and K multiples of 16 bytes.
+const KernelDesc kFp8TiledKernels[] = {
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_nt_ring4",
+     &launch_fp8_ring<4, 4>, 0, nullptr, kLayoutNT},
+};
+const int kFp8TiledKernelCount = sizeof(kFp8TiledKernels) / sizeof(kFp8TiledKernels[0]);
+#endif
+
+}  // namespace gemm

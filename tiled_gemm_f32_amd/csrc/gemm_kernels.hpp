@@ -10,8 +10,9 @@ namespace gemm {
 // Arguments of one GEMM launch, already validated by the host code:
 // 0 < M, N, K < 2^31, lda and ldb below 2^21 elements (so every in-panel
 // byte offset of a 256-row panel fits the 31-bit buffer extent), pointers
-// aligned to their element size.  A and B are fp32 or bf16 according to
-// the kernel; C is always fp32.
+// aligned to their element size.  A and B are fp32, bf16 or fp8 according
+// to the kernel; C is always fp32.  op_a / op_b are gemm_op layouts; a
+// kernel runs only the layouts its table row lists.
 struct GemmParams {
     const void *A;
     const void *B;
@@ -20,6 +21,7 @@ struct GemmParams {
     int32_t lda, ldb;
     int64_t ldc;
     float alpha, beta;
+    int32_t op_a, op_b;
     // K split (0: none).  With kchunk > 0 the tiled kernels run on a grid of
     // (tiles, ceil(K / kchunk)) workgroups; row y of the grid multiplies the
     // k range [y*kchunk, min(K, (y+1)*kchunk)) and stores that partial product
@@ -35,6 +37,9 @@ struct GemmParams {
 inline int k_splits(const GemmParams &p) { return p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1; }
 
 typedef hipError_t (*LaunchFn)(const GemmParams &p, hipStream_t stream);
+
+// Operand layouts a kernel runs: bit 2*op_a + op_b.
+constexpr int32_t kLayoutNN = 1, kLayoutNT = 2, kLayoutTN = 4, kLayoutTT = 8, kLayoutAll = 15;
 
 // C = alpha * (sum of the k_splits(p) partial products, in split order) +
 // beta * C, for the tiled kernels' K split (defined with the skinny kernels).
@@ -52,6 +57,7 @@ struct KernelDesc {
     LaunchFn launch;
     int32_t min_k;     // the automatic choice skips this kernel below this K (0: no limit)
     LaunchWsFn launch_ws;  // set instead of `launch` for kernels that need the caller's workspace
+    int32_t layouts = kLayoutNN;
 };
 
 // Split-K skinny kernel sizing, shared by its launcher and the workspace query:
@@ -78,6 +84,10 @@ extern const KernelDesc kF32SkinnyKernels[];
 extern const int kF32SkinnyKernelCount;
 extern const KernelDesc kF32SplitKernels[];
 extern const int kF32SplitKernelCount;
+extern const KernelDesc kFp8TiledKernels[];
+extern const int kFp8TiledKernelCount;
+extern const KernelDesc kGeneralKernels[];
+extern const int kGeneralKernelCount;
 
 // C = beta * C over an M x N view (beta == 0 writes zeros without reading).
 hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act,

@@ -13,7 +13,10 @@ Recipe (fixed, so that every run sees the same bytes):
 * ``uniform``: ``torch.empty(shape).uniform_(-1, 1, generator=g)``.
 * ``normal``: ``torch.randn(shape, generator=g)``.
 * bf16 operands: the fp32 draw rounded to bf16 with ``.to(torch.bfloat16)``
-  (round to nearest even); C0 stays fp32.
+  (round to nearest even); C0 stays fp32.  fp8 operands likewise with
+  ``.to(torch.float8_e4m3fn)`` (OCP E4M3, round to nearest even).
+* A transposed operand (``op_b == "T"``) is drawn in its defining shape
+  (K x N) and then stored transposed.
 
 The shapes are the square and ragged problems the pages measure on (4092 and
 4096 cubes on page 1 and page 3), a small cube, a ragged shape that is a
@@ -30,7 +33,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str          # "f32" or "bf16f32" (bf16 operands, fp32 accumulate and output)
+    dtype: str          # "f32", "bf16f32" or "fp8f32" (bf16 / fp8 E4M3 operands, fp32 accumulate and output)
     M: int
     N: int
     K: int
@@ -38,6 +41,7 @@ class Workload:
     beta: float
     dist: str           # "uniform" (U[-1, 1]) or "normal" (N(0, 1))
     seed: int
+    op_b: str = "N"     # "T": B is stored transposed (N x K)
 
     @property
     def flops(self) -> int:
@@ -45,7 +49,7 @@ class Workload:
 
     @property
     def elt_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16f32": 2, "fp8f32": 1}[self.dtype]
 
     @property
     def algorithmic_bytes(self) -> int:
@@ -63,6 +67,8 @@ WORKLOADS = {
         Workload("f32_1000x3000x777", "f32", 1000, 3000, 777, 2.0, -1.0, "uniform", 3),
         Workload("f32_16x8192x8192", "f32", 16, 8192, 8192, 1.0, 0.0, "uniform", 3),
         Workload("bf16f32_8192", "bf16f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 4),
+        # fp8 operands with B stored N x K, the layout of the fp8 matrix-core kernel.
+        Workload("fp8f32_8192_nt", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 5, "T"),
     ]
 }
 
@@ -78,22 +84,35 @@ def _draw(shape, dist: str, g: torch.Generator) -> torch.Tensor:
 def make_inputs(w: Workload):
     """Host tensors (A, B, C0) for a workload.
 
-    A and B are float32 for ``f32`` workloads and bfloat16 for ``bf16f32``;
-    C0 is always float32 of shape (M, N).
+    A and B are float32 for ``f32`` workloads, bfloat16 for ``bf16f32`` and
+    float8_e4m3fn for ``fp8f32``; B is returned as stored (N x K when
+    ``op_b == "T"``).  C0 is always float32 of shape (M, N).
     """
     g = torch.Generator("cpu").manual_seed(w.seed)
     A = _draw((w.M, w.K), w.dist, g)
     B = _draw((w.K, w.N), w.dist, g)
     C0 = _draw((w.M, w.N), w.dist, g)
-    if w.dtype == "bf16f32":
-        A = A.to(torch.bfloat16)
-        B = B.to(torch.bfloat16)
+    A, B = _operand_type(A, w.dtype), _operand_type(B, w.dtype)
+    if w.op_b == "T":
+        B = B.t().contiguous()
     return A, B, C0
+
+
+def _operand_type(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    """fp32 draws rounded (nearest even) to the operand type: "f32", "bf16f32"
+    or "fp8f32" (OCP E4M3; N(0,1) and small-integer draws stay far inside its
+    finite range)."""
+    if dtype == "bf16f32":
+        return x.to(torch.bfloat16)
+    if dtype == "fp8f32":
+        return x.to(torch.float8_e4m3fn)
+    assert dtype == "f32", dtype
+    return x
 
 
 def make_integer_inputs(M: int, N: int, K: int, seed: int, lo: int = -4, hi: int = 4,
                         dtype: str = "f32"):
-    """Small-integer operands (exact in fp32 and bf16) and an integer C0.
+    """Small-integer operands (exact in fp32, bf16 and fp8 E4M3) and an integer C0.
 
     With |entries| <= 4 every partial sum stays an integer below 2**24 for
     K < 2**20, so any summation order gives the same exact result.
@@ -102,10 +121,7 @@ def make_integer_inputs(M: int, N: int, K: int, seed: int, lo: int = -4, hi: int
     A = torch.randint(lo, hi + 1, (M, K), generator=g).to(torch.float32)
     B = torch.randint(lo, hi + 1, (K, N), generator=g).to(torch.float32)
     C0 = torch.randint(lo, hi + 1, (M, N), generator=g).to(torch.float32)
-    if dtype == "bf16f32":
-        A = A.to(torch.bfloat16)
-        B = B.to(torch.bfloat16)
-    return A, B, C0
+    return _operand_type(A, dtype), _operand_type(B, dtype), C0
 
 
 def make_bias(N: int, seed: int, dist: str = "normal", integer: bool = False):
@@ -123,13 +139,16 @@ def make_random_inputs(M: int, N: int, K: int, seed: int, dist: str = "uniform",
     A = _draw((M, K), dist, g)
     B = _draw((K, N), dist, g)
     C0 = _draw((M, N), dist, g)
-    if dtype == "bf16f32":
-        A = A.to(torch.bfloat16)
-        B = B.to(torch.bfloat16)
-    return A, B, C0
+    return _operand_type(A, dtype), _operand_type(B, dtype), C0
 
 
 def bf16_bits(t: torch.Tensor):
     """uint16 numpy view of a bfloat16 tensor's bit patterns (for the oracle)."""
     assert t.dtype == torch.bfloat16
     return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def fp8_bytes(t: torch.Tensor):
+    """uint8 numpy view of a float8_e4m3fn tensor's bytes (for the oracle)."""
+    assert t.dtype == torch.float8_e4m3fn
+    return t.contiguous().view(torch.uint8).numpy()
