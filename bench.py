@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0
 # draining from the last-level cache to HBM while the skinny kernel streams B.
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 # Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
-EXTRA = ["fp8f32_8192_nt"]
+EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt"]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -154,7 +154,7 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        if w.dtype == "fp8f32":
+        if w.dtype == "fp8f32" or w.op_b == "T":
             st = tg.gemm_general(DTYPES[w.dtype], tg.GEMM_OP_N, tg.GEMM_OP_T if w.op_b == "T" else tg.GEMM_OP_N,
                                  w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), ldb_of(w), w.beta,
                                  c["C"].data_ptr(), w.N, 0, None, 0, 0, sh)

@@ -433,10 +433,17 @@ def test_general_nn_matches_plain_query():
             assert a == b, (dt, M, N, K)
 
 
-def test_fp8_nt_takes_the_ring_kernel():
+def test_nt_takes_the_ring_kernels():
     st, pl = gplan(FP8, N_, T_, 8192, 8192, 8192)
     assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4", pl
     assert pl["grid"] == 32 * 32 and pl["splits"] == 1
+    st, pl = gplan(BF16, N_, T_, 8192, 8192, 8192)
+    assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", pl
+    # The bf16 B^T ring needs only 16-byte rows of B^T: N is free.
+    st, pl = gplan(BF16, N_, T_, 1000, 1001, 1040)
+    assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", pl
+    st, pl = gplan(BF16, N_, T_, 1000, 1001, 1044)
+    assert st == OK and kname(pl) == "bf16_general_128x128x16", pl
 
 
 @pytest.mark.parametrize("why", ["K", "lda", "ldb", "A", "B"])
@@ -459,12 +466,12 @@ def test_fp8_nt_unaligned_falls_back_to_general(why):
 @pytest.mark.parametrize("dtype,prefix", [(F32, "f32"), (BF16, "bf16"), (FP8, "fp8")])
 @pytest.mark.parametrize("ops", [(N_, T_), (T_, N_), (T_, T_), (N_, N_)])
 def test_layouts_without_a_fast_kernel_take_general(dtype, prefix, ops):
-    st, pl = gplan(dtype, ops[0], ops[1], 1000, 3000, 777)
+    st, pl = gplan(dtype, ops[0], ops[1], 1000, 3000, 784)      # K a multiple of 16: fast kernels can run
     assert st == OK
-    fast = (dtype in (F32, BF16) and ops == (N_, N_))
+    fast = (dtype in (F32, BF16) and ops == (N_, N_)) or (dtype in (BF16, FP8) and ops == (N_, T_))
     if fast:
-        assert "general" not in kname(pl)
-    elif not (dtype == FP8 and ops == (N_, T_)):
+        assert "general" not in kname(pl), pl
+    else:
         assert kname(pl) == f"{prefix}_general_128x128x16", pl
 
 

@@ -74,7 +74,8 @@ def _exact_epilogue(A, B, C0, alpha, beta, bias, act):
 
 
 def _kernels(did):
-    return [k["id"] for k in tg.kernels() if k["dtype"] == did]
+    """Kernels of this operand type that run untransposed operands."""
+    return [k["id"] for k in tg.kernels() if k["dtype"] == did and k["layouts"] & 1]
 
 
 def _skinny(kid):

@@ -37,6 +37,7 @@ OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
 U32 = 2.0 ** -24
 RUN_TRUNC = 7 * 2.0 ** -13
 FP8_RING = "fp8_mfma32_256x256x64_w2x2_nt_ring4"
+BF16_NT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4"
 
 
 def stored(A, B, op_a, op_b):
@@ -155,7 +156,7 @@ def test_k_split_every_layout(gpu_available, dtype, ops):
     np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, 1.0, 0.5, op_a, op_b))
 
 
-# ----------------------------------------------------------------------------- the fp8 ring kernel
+# ----------------------------------------------------------------------------- the A x B^T ring kernels
 
 FP8_SHAPES = [
     (256, 256, 64),        # one tile, one slice
@@ -166,39 +167,42 @@ FP8_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("dtype,ring_name", [("fp8f32", FP8_RING), ("bf16f32", BF16_NT_RING)], ids=["fp8", "bf16"])
 @pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_fp8_ring_shapes(gpu_available, shape):
-    """The fp8 ring kernel, forced (small problems would otherwise take the
-    smallest tile), on edge shapes."""
+def test_nt_ring_shapes(gpu_available, dtype, ring_name, shape):
+    """The A x B^T ring kernels, forced (small problems would otherwise take
+    the smallest tile), on edge shapes."""
     M, N, K = shape
-    ring = [k["id"] for k in tg.kernels() if k["name"] == FP8_RING][0]
-    ok, _ = runnable("fp8f32", "N", "T", M, N, K, ring)
+    ring = [k["id"] for k in tg.kernels() if k["name"] == ring_name][0]
+    ok, _ = runnable(dtype, "N", "T", M, N, K, ring)
     assert ok
-    A, B, C0 = make_integer_inputs(M, N, K, seed=710, dtype="fp8f32")
+    A, B, C0 = make_integer_inputs(M, N, K, seed=710, dtype=dtype)
     As, Bs = stored(A, B, "N", "T")
-    say(f"[fp8 ring] exact M={M} N={N} K={K} seed=710")
+    say(f"[nt ring] {ring_name} exact M={M} N={N} K={K} seed=710")
     C, _, _ = run_gemm(As, Bs, C0, -1.0, 2.0, kernel=ring, op_b="T")
     np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, -1.0, 2.0, "N", "T"))
-    A, B, C0 = make_random_inputs(M, N, K, seed=711, dist="normal", dtype="fp8f32")
+    A, B, C0 = make_random_inputs(M, N, K, seed=711, dist="normal", dtype=dtype)
     As, Bs = stored(A, B, "N", "T")
-    say(f"[fp8 ring] random M={M} N={N} K={K} seed=711")
+    say(f"[nt ring] {ring_name} random M={M} N={N} K={K} seed=711")
     C, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_b="T")
-    r = check(C, As, Bs, C0, 0.5, 0.25, "N", "T", "fp8f32")
-    say(f"[fp8 ring] worst err/allowance {r:.3e}")
+    r = check(C, As, Bs, C0, 0.5, 0.25, "N", "T", dtype)
+    say(f"[nt ring] worst err/allowance {r:.3e}")
 
 
+@pytest.mark.parametrize("dtype,ring_name", [("fp8f32", FP8_RING), ("bf16f32", BF16_NT_RING)], ids=["fp8", "bf16"])
 @pytest.mark.parametrize("act", ["relu", "gelu"])
-def test_fp8_ring_epilogue_and_unaligned_c(gpu_available, act):
+@pytest.mark.parametrize("c_offset", [0, 1])
+def test_nt_ring_epilogue_and_c_alignment(gpu_available, dtype, ring_name, act, c_offset):
     M, N, K = 520, 777, 512
-    A, B, C0 = make_random_inputs(M, N, K, seed=712, dist="normal", dtype="fp8f32")
+    A, B, C0 = make_random_inputs(M, N, K, seed=712, dist="normal", dtype=dtype)
     As, Bs = stored(A, B, "N", "T")
     bias = make_bias(N, seed=713)
     alpha = 1.0 / np.sqrt(K)
-    ring = [k["id"] for k in tg.kernels() if k["name"] == FP8_RING][0]
-    say(f"[fp8 ring] epilogue act={act} M={M} N={N} K={K} c_offset=1")
-    C, _, _ = run_gemm(As, Bs, C0, alpha, -0.5, kernel=ring, offset=(0, 0, 1), bias=bias, activation=act,
+    ring = [k["id"] for k in tg.kernels() if k["name"] == ring_name][0]
+    say(f"[nt ring] {ring_name} epilogue act={act} M={M} N={N} K={K} c_offset={c_offset}")
+    C, _, _ = run_gemm(As, Bs, C0, alpha, -0.5, kernel=ring, offset=(0, 0, c_offset), bias=bias, activation=act,
                        op_b="T")
-    check(C, As, Bs, C0, alpha, -0.5, "N", "T", "fp8f32", bias=bias, act=act)
+    check(C, As, Bs, C0, alpha, -0.5, "N", "T", dtype, bias=bias, act=act)
 
 
 def test_fp8_ring_deterministic_and_bench_shape_sampled(gpu_available):

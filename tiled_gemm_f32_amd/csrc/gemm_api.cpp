@@ -191,16 +191,17 @@ const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c,
 }
 
 // The tiled kernels of the call's operand type that run its layout, in
-// table order (which is preference order: the general kernels come last).
+// table order (which is preference order), fallback kernels or not.
 struct Candidates {
     const KernelDesc *k[64];
     int n = 0;
 };
-Candidates tiled_candidates(const Call &c) {
+Candidates tiled_candidates(const Call &c, bool fallback) {
     Candidates r;
     for (int32_t id = 1; id <= table_size() && r.n < 64; ++id) {
         const KernelDesc *kd = kernel_by_id(id);
-        if (kd->path == GEMM_PATH_TILED && kd->dtype == c.dtype && ((kd->layouts >> (2 * c.op_a + c.op_b)) & 1))
+        if (kd->path == GEMM_PATH_TILED && kd->dtype == c.dtype && kd->fallback == fallback &&
+            ((kd->layouts >> (2 * c.op_a + c.op_b)) & 1))
             r.k[r.n++] = kd;
     }
     return r;
@@ -212,8 +213,14 @@ const KernelDesc *first_candidate(const Candidates &cand, const Call &c, int til
     return nullptr;
 }
 
+// Tile choice among kernels of one class (see below).
+const KernelDesc *choose_tiled(const Call &c, const Candidates &cand);
+
 // Tile choice: the largest square tile whose tile count covers every compute
-// unit at least once; small problems fall through to the smallest tile.
+// unit at least once; small problems fall through to the smallest tile.  The
+// rule compares kernels of like speed, so it runs over the regular kernels
+// first and over the fallback (general) kernels only when none of those runs
+// the call.
 const KernelDesc *choose(const Call &c) {
     const bool plain = c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_N;
     // The split-K kernels pay off only where K is actually split.
@@ -225,7 +232,11 @@ const KernelDesc *choose(const Call &c) {
         if (const KernelDesc *kd = first_match(gemm::kF32SkinnyKernels, gemm::kF32SkinnyKernelCount, c, 0))
             return kd;
     }
-    const Candidates cand = tiled_candidates(c);
+    if (const KernelDesc *kd = choose_tiled(c, tiled_candidates(c, false))) return kd;
+    return choose_tiled(c, tiled_candidates(c, true));
+}
+
+const KernelDesc *choose_tiled(const Call &c, const Candidates &cand) {
     // With a workspace: the largest tile that wastes at most a quarter of
     // its padded M x N ("The fringe and the last wave": tile quantisation)
     // and whose grid of tiles x K slices fills at least three quarters of the

@@ -489,7 +489,10 @@ hipError_t launch_bf16_pipe(const GemmParams &p, hipStream_t stream) {
 
 __device__ __forceinline__ int ring_swz_a(int row) { return (row >> 2) & 3; }
 
-template <int NS, int GROUP_M>
+// BT: B is stored transposed (N x K, k contiguous), so its slices take the A
+// layout, loads and fragment reads above, and N needs no alignment: runs of
+// C columns that straddle N are stored element by element.
+template <int NS, int GROUP_M, bool BT>
 __global__ void __launch_bounds__(256)
 bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint16_t>(p);
@@ -514,7 +517,7 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
-    const int a_rows = min(BM, M - m0);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
 
     // DMA instruction j of this wave fills 1 KB block 4*wave + j of each panel.
     //   A block: rows 16*blk .. +15; lane -> row 16*blk + lane/4, physical chunk lane%4.
@@ -528,9 +531,14 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int lca = (lane & 3) ^ ring_swz_a(ra);
         a_kc[j] = 8 * lca;
         a_goff[j] = (uint32_t)(ra * lda + 8 * lca) * 2u;
-        const int nb = blk >> 1, rb = 16 * (blk & 1) + (lane >> 2);
-        const int lcb = (lane & 3) ^ (2 * ((rb >> 1) & 1));
-        b_goff[j] = (uint32_t)(rb * ldb + 32 * nb + 8 * lcb) * 2u;
+        if (BT) {
+            // Rows of B^T (columns of B) laid out as A's rows; same chunk k as A.
+            b_goff[j] = (uint32_t)(ra * ldb + 8 * lca) * 2u;
+        } else {
+            const int nb = blk >> 1, rb = 16 * (blk & 1) + (lane >> 2);
+            const int lcb = (lane & 3) ^ (2 * ((rb >> 1) & 1));
+            b_goff[j] = (uint32_t)(rb * ldb + 32 * nb + 8 * lcb) * 2u;
+        }
     }
     // Resources of slice kt.  Rebased per slice: rows past M / past K fall
     // outside the extents; a chunk at or past K in a valid row of A gets 2^31
@@ -538,7 +546,10 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
         ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
-        rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
+        if (BT)
+            rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 2));
+        else
+            rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
     };
     // DMA instruction j (0..7) of slice kt into `stage`: j < 4 fills A block
     // 4*wave + j, j >= 4 fills B block 4*wave + j - 4.
@@ -548,8 +559,11 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16, a_goff[j] + poison, 0, 0, 0);
         } else {
+            // B^T chunks past K in a valid row would read the next row: poison them as A's.
+            const uint32_t poison = BT ? (uint32_t)(a_kc[j - 4] >= K - kt * BK) << 31 : 0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + j - 4) * 1024), 16, b_goff[j - 4], 0, 0, 0);
+                rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + j - 4) * 1024), 16, b_goff[j - 4] + poison,
+                0, 0, 0);
         }
     };
     // Fragment read bases (bytes within a slice).
@@ -564,6 +578,10 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int bch = 2 * (q & 1) + ((j16 & 3) >> 1);
     const uint32_t fb_base = (uint32_t)(kA + wn * 4 * 2048 + brow * 64 + 16 * (bch ^ (2 * ((brow >> 1) & 1))) +
                                         8 * (j16 & 1));
+    uint32_t fbt_base[2];   // BT: B^T fragment reads, the A pattern in the B half of the stage
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        fbt_base[s] = (uint32_t)(kA + (wn * 128 + l32) * 64 + 16 * ((2 * s + h) ^ ring_swz_a(l32)));
 
     bf16x8 fa[2][4], fb[2][4];
     // Fragment read slot r (0..7) of half s of the slice in `stage` into
@@ -575,6 +593,9 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         if (r == 0 || r >= 5) {
             const int f = r == 0 ? 0 : r - 4;
             fa[set][f] = *reinterpret_cast<const bf16x8 *>(base + fa_base[s] + 2048 * f);
+        } else if (BT) {
+            const int f = r - 1;
+            fb[set][f] = *reinterpret_cast<const bf16x8 *>(base + fbt_base[s] + 2048 * f);
         } else {
             const int f = r - 1;
             const int boff = fb_base + 2048 * f + 1024 * s;
@@ -650,8 +671,9 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
 
     // Epilogue.  Register 4g + t of lane (h, l32) in fragment (fm, fn) is
     // C[row m0 + wm*128 + 32*fm + l32][column n0 + wn*128 + 32*fn + 8*g + 4*h + t].
-    // N is a multiple of 8 on this path, so each run of 4 columns is wholly
-    // inside or outside C; 16-byte accesses need C 16-byte aligned and
+    // Untransposed, N is a multiple of 8, so each run of 4 columns is wholly
+    // inside or outside C; with B^T a run may straddle N and is then stored
+    // element by element.  16-byte accesses need C 16-byte aligned and
     // ldc % 4 == 0.  The branch on the activation is taken once for the whole
     // tile, so each case is one fully unrolled pass and the accumulators stay
     // in registers.
@@ -665,9 +687,11 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
             for (int g = 0; g < 4; ++g) {
                 const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
                 if (col >= N) continue;
+                const bool whole = vec_c && (!BT || col + 4 <= N);
                 float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
 #pragma unroll
-                for (int t = 0; t < 4; ++t) b[t] = p.bias != nullptr ? p.bias[col + t] : -0.0f;
+                for (int t = 0; t < 4; ++t)
+                    b[t] = (p.bias != nullptr && (!BT || col + t < N)) ? p.bias[col + t] : -0.0f;
 #pragma unroll
                 for (int fm = 0; fm < 4; ++fm) {
                     const int row = m0 + wm * 128 + 32 * fm + l32;
@@ -675,19 +699,38 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                     float *cp = p.C + (int64_t)row * p.ldc + col;
                     f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
                                alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
-                    if (beta != 0.0f) {
-                        const f32x4 c0 =
-                            vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
+                    if (!BT) {
+                        if (beta != 0.0f) {
+                            const f32x4 c0 =
+                                vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
-                    }
+                            for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
+                        }
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
-                    if (vec_c) {
+                        for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
+                        if (vec_c) {
+                            *reinterpret_cast<f32x4 *>(cp) = v;
+                        } else {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) cp[t] = v[t];
+                        }
+                    } else if (whole) {
+                        if (beta != 0.0f) {
+                            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cp);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
+                        }
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
                         *reinterpret_cast<f32x4 *>(cp) = v;
                     } else {
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) cp[t] = v[t];
+                        for (int t = 0; t < 4; ++t) {
+                            if (col + t >= N) continue;
+                            float x = v[t];
+                            if (beta != 0.0f) x = fmaf(beta, cp[t], x);
+                            cp[t] = Act::apply(x + b[t]);
+                        }
                     }
                 }
             }
@@ -695,12 +738,12 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     });
 }
 
-template <int NS, int GROUP_M>
+template <int NS, int GROUP_M, bool BT = false>
 hipError_t launch_bf16_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT>),
                            dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
@@ -721,8 +764,9 @@ hipError_t launch_bf16_tiled(const GemmParams &p, hipStream_t stream) {
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
 template __global__ void bf16_pipe_kernel<4>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<5, 4>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<5, 4, false>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 8, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 1, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 1, 8, 4>(GemmParams, int, int);
@@ -743,6 +787,9 @@ const KernelDesc kBf16TiledKernels[] = {
      &launch_bf16_ring<5, 4>, 1024},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_pipe",
      &launch_bf16_pipe<4>},
+    // B stored N x K: the only fast kernel for that layout, so no K minimum.
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4",
+     &launch_bf16_ring<4, 4, true>, 0, nullptr, kLayoutNT},
     BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
     BF16_TILED(256, 256, 64, 2, 2, 8, 1, 4),
     BF16_TILED(256, 256, 64, 2, 2, 1, 8, 4),

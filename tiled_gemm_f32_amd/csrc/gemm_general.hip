@@ -234,11 +234,11 @@ GENERAL_INSTANCES(GEMM_DTYPE_FP8F32)
 // kernel runs its operands.
 const KernelDesc kGeneralKernels[] = {
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, kBM, kBN, kBK, kThreads, 1, 1, "f32_general_128x128x16",
-     &launch_general<GEMM_DTYPE_F32>, 0, nullptr, kLayoutAll},
+     &launch_general<GEMM_DTYPE_F32>, 0, nullptr, kLayoutAll, true},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, kBM, kBN, kBK, kThreads, 1, 1, "bf16_general_128x128x16",
-     &launch_general<GEMM_DTYPE_BF16F32>, 0, nullptr, kLayoutAll},
+     &launch_general<GEMM_DTYPE_BF16F32>, 0, nullptr, kLayoutAll, true},
     {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, kBM, kBN, kBK, kThreads, 1, 1, "fp8_general_128x128x16",
-     &launch_general<GEMM_DTYPE_FP8F32>, 0, nullptr, kLayoutAll},
+     &launch_general<GEMM_DTYPE_FP8F32>, 0, nullptr, kLayoutAll, true},
 };
 const int kGeneralKernelCount = sizeof(kGeneralKernels) / sizeof(kGeneralKernels[0]);
 #endif

@@ -58,6 +58,7 @@ struct KernelDesc {
     int32_t min_k;     // the automatic choice skips this kernel below this K (0: no limit)
     LaunchWsFn launch_ws;  // set instead of `launch` for kernels that need the caller's workspace
     int32_t layouts = kLayoutNN;
+    bool fallback = false;     // chosen only when no other kernel runs the call
 };
 
 // Split-K skinny kernel sizing, shared by its launcher and the workspace query:

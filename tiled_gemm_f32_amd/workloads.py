@@ -69,6 +69,7 @@ WORKLOADS = {
         Workload("bf16f32_8192", "bf16f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 4),
         # fp8 operands with B stored N x K, the layout of the fp8 matrix-core kernel.
         Workload("fp8f32_8192_nt", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 5, "T"),
+        Workload("bf16f32_8192_nt", "bf16f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 6, "T"),
     ]
 }
 
