@@ -88,20 +88,25 @@ GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha,
                          gemm_stream_t stream);
 
 /*
- * Workspace.  Two paths split K across workgroups and reduce the partial
+ * Workspace.  These paths split K across workgroups and reduce the partial
  * results in a caller-provided device workspace (the split-K variant of
  * "Tiled matrix multiplication", section "Variants and alternatives", and of
  * "A GEMM Kernel, Step by Step", section "What is left"):
  *   - fp32 with M <= 16: the skinny streaming kernel, split into up to 8
  *     k ranges of at least 512;
- *   - any tiled problem (fp32 or bf16) with fewer 256 x 256 output tiles
- *     than compute units: the tiled kernel, split into up to 16 k ranges of
- *     at least 1024, when the split grid fills at least three quarters of
- *     the compute units.
- * gemm_workspace_size() returns the largest workspace either path can use
- * for this shape (0 when none applies): `splits` partial M x N fp32
- * results, reduced in split order by a second kernel on the same stream
- * (results are deterministic).  The workspace needs no initialisation and
+ *   - any tiled problem with fewer output tiles than compute units: the
+ *     tiled kernel, split into up to 16 k ranges of at least 1024, when the
+ *     split grid fills at least three quarters of the compute units;
+ *   - a tiled problem whose tile count is just over a multiple of the 256
+ *     compute units (a last wave at most half full; "The fringe and the last
+ *     wave", and the aim of Stream-K in "Variants and alternatives"): the
+ *     top rows of tiles run first in whole waves, then the leftover bottom
+ *     rows run K-split, spreading their work over the otherwise idle
+ *     compute units (gemm_plan.split_row gives the boundary).
+ * gemm_workspace_size() returns the largest workspace any path can use
+ * for this shape (0 when none applies): `splits` partial fp32 results for
+ * the rows split, reduced in split order by a further kernel on the same
+ * stream (results are deterministic).  The workspace needs no initialisation and
  * its contents after a call are unspecified.  Calls sharing a workspace
  * must be ordered (same stream, or synchronised streams); overlapping calls
  * on one workspace race.  gemm_f32_ws() and gemm_bf16f32_ws() are
@@ -180,6 +185,8 @@ typedef struct gemm_plan {
     int32_t tile_m, tile_n, tile_k;
     int32_t vec_a, vec_b;
     int32_t splits;         /* k ranges of a tiled K split (1: none; 0 for NONE / SCALE) */
+    int64_t split_row;      /* first row of C that the K split covers: rows above it run first,
+                               unsplit, in whole waves of tiles (0: the split, if any, covers all) */
 } gemm_plan;
 
 /* Number of kernels in the table; ids run from 1 to this value. */

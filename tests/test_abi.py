@@ -496,3 +496,36 @@ def test_transposed_layouts_split_k(dtype, ops):
 def test_fp8_workspace_size():
     assert tg.gemm_workspace_size(FP8, 256, 512, 6000) == tg.gemm_workspace_size(BF16, 256, 512, 6000) > 0
     assert tg.gemm_workspace_size(FP8, 16, 8192, 8192) > 0
+
+
+# ----------------------------------------------------------------------------- last-wave split
+
+def test_wave_tail_plan():
+    """272 tiles of 256 = one full wave + 16: the top 4096 rows run as one
+    wave and the last tile row runs K-split."""
+    ws = tg.gemm_workspace_size(F32, 4352, 4096, 4096)
+    st, pl = plan(F32, 4352, 4096, 4096, ws=ws)
+    assert st == OK and pl["tile_m"] == 256 and pl["split_row"] == 4096 and pl["splits"] >= 2, pl
+    assert pl["grid"] == 256 + 16 * pl["splits"]
+    assert ws >= pl["splits"] * 256 * 4096 * 4
+    # No workspace, or one too small: the plain plan.
+    assert plan(F32, 4352, 4096, 4096)[1]["split_row"] == 0
+    assert plan(F32, 4352, 4096, 4096, ws=1024)[1]["split_row"] == 0
+
+
+def test_wave_tail_only_for_a_mostly_empty_last_wave():
+    ws = 1 << 32
+    assert plan(F32, 4096, 4096, 4096, ws=ws)[1]["split_row"] == 0           # exactly one wave
+    assert plan(F32, 4096 + 256 * 13, 4096, 4096, ws=ws)[1]["split_row"] == 0  # 464 tiles: last wave 81% full
+    assert plan(F32, 4352, 4096, 1024, ws=ws)[1]["split_row"] == 0           # K too shallow to split
+    st, pl = plan(BF16, 8448, 8192, 8192, ws=ws)
+    assert st == OK and pl["split_row"] == 8192 and pl["splits"] >= 2, pl
+
+
+@pytest.mark.parametrize("dtype,ops", [(F32, (T_, N_)), (BF16, (N_, T_)), (FP8, (N_, T_))])
+def test_wave_tail_other_layouts(dtype, ops):
+    M = 4352 if dtype != F32 else 2176          # the fp32 transposed call takes 128-tile kernels
+    N = 4096 if dtype != F32 else 2048
+    ws = tg.gemm_workspace_size(dtype, M, N, 4096)
+    st, pl = gplan(dtype, ops[0], ops[1], M, N, 4096, ws=ws)
+    assert st == OK and pl["split_row"] > 0 and pl["splits"] >= 2, pl

@@ -56,7 +56,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("kernel_id", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("threads", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
-                ("splits", ctypes.c_int32)]
+                ("splits", ctypes.c_int32), ("split_row", ctypes.c_int64)]
 
 
 class Epilogue(ctypes.Structure):

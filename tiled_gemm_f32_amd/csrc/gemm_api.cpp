@@ -158,7 +158,10 @@ constexpr int64_t kSplitAlign = 64;
 struct KSplit {
     int splits;        // 1: no split
     int32_t kchunk;    // k depth of each slice (the last one may be shorter)
-    int64_t bytes;     // workspace: splits partial M x N fp32 products
+    int64_t bytes;     // workspace: splits partial products of the split rows
+    // Rows [0, m_top) run first without a split (whole waves of tiles); the
+    // split covers rows [m_top, M).  0: the split covers the whole call.
+    int64_t m_top = 0;
 };
 
 KSplit tiled_ksplit(const Call &c, int tile_m, int tile_n) {
@@ -175,11 +178,41 @@ KSplit tiled_ksplit(const Call &c, int tile_m, int tile_n) {
     return r;
 }
 
+// The last, mostly empty wave ("A GEMM Kernel, Step by Step", "The fringe
+// and the last wave"; the goal of Stream-K in "Tiled matrix
+// multiplication", "Variants and alternatives": give every compute unit an
+// equal share of the multiply-adds).  When the tile count is just over a
+// multiple of the compute units, the top rows of tiles that fill whole waves
+// run as usual and the few tile rows left over run as a separate K-split
+// problem, whose slices spread their multiply-adds over the compute units
+// that would otherwise idle.  Estimated in full-tile times: taken when it
+// saves at least half of one.
+KSplit wave_tail(const Call &c, int tile) {
+    const KSplit none{1, 0, 0};
+    const int64_t tiles_m = ceil_div(c.M, tile), tiles_n = ceil_div(c.N, tile);
+    const int64_t T = tiles_m * tiles_n, waves = T / kComputeUnits, r = T % kComputeUnits;
+    if (waves == 0 || r == 0 || 2 * r > kComputeUnits) return none;
+    const int64_t dm = waves * kComputeUnits / tiles_n;       // tile rows in whole waves
+    if (dm <= 0 || dm >= tiles_m) return none;
+    Call bot = c;
+    bot.M = c.M - dm * tile;
+    KSplit ks = tiled_ksplit(bot, tile, tile);
+    if (ks.splits < 2) return none;
+    const int64_t bot_tiles = (tiles_m - dm) * tiles_n;
+    const double plain = (double)ceil_div(T, kComputeUnits);
+    const double split = (double)ceil_div(dm * tiles_n, kComputeUnits) +
+                         (double)ceil_div(bot_tiles * ks.splits, kComputeUnits) / ks.splits;
+    if (split > plain - 0.5) return none;
+    ks.m_top = dm * tile;
+    return ks;
+}
+
 // The split a tiled kernel takes for this call: none without a workspace
 // large enough for it.
 KSplit call_ksplit(const Call &c, const KernelDesc *kd) {
     if (kd->path != GEMM_PATH_TILED || c.ws == nullptr) return KSplit{1, 0, 0};
-    const KSplit r = tiled_ksplit(c, kd->tile_m, kd->tile_n);
+    KSplit r = tiled_ksplit(c, kd->tile_m, kd->tile_n);
+    if (r.splits < 2) r = wave_tail(c, kd->tile_m);
     return r.splits > 1 && c.ws_bytes >= r.bytes ? r : KSplit{1, 0, 0};
 }
 
@@ -352,7 +385,10 @@ gemm_status plan(const Call &c, int32_t force, gemm_plan *out, const KernelDesc 
         } else {
             if (allow_split) *split = call_ksplit(c, kd);
             pl.splits = split->splits;
-            pl.grid = ceil_div(c.M, kd->tile_m) * ceil_div(c.N, kd->tile_n) * pl.splits;
+            pl.split_row = split->m_top;
+            const int64_t tiles_n = ceil_div(c.N, kd->tile_n);
+            pl.grid = ceil_div(split->m_top, kd->tile_m) * tiles_n +
+                      ceil_div(c.M - split->m_top, kd->tile_m) * tiles_n * pl.splits;
         }
         if (pl.splits == 0) pl.splits = 1;
         *chosen = kd;
@@ -414,7 +450,22 @@ gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, con
         p.partials = nullptr;
         p.bias = c.bias;
         p.act = c.act;
-        if (ks.splits > 1) {
+        if (ks.splits > 1 && ks.m_top > 0) {
+            // Whole waves of the top rows, then the K-split bottom rows (A's
+            // rows are its columns when it is stored transposed).
+            gemm::GemmParams top = p;
+            top.M = (int32_t)ks.m_top;
+            err = kd->launch(top, s);
+            const int64_t esz = elem_size(c.dtype);
+            const int64_t a_off = (c.op_a == GEMM_OP_N ? ks.m_top * c.lda : ks.m_top) * esz;
+            p.A = static_cast<const char *>(c.A) + a_off;
+            p.C = c.C + ks.m_top * c.ldc;
+            p.M = (int32_t)(c.M - ks.m_top);
+            p.kchunk = ks.kchunk;
+            p.partials = static_cast<float *>(c.ws);
+            if (err == hipSuccess) err = kd->launch(p, s);
+            if (err == hipSuccess) err = gemm::launch_splitk_reduce(p, s);
+        } else if (ks.splits > 1) {
             p.kchunk = ks.kchunk;
             p.partials = static_cast<float *>(c.ws);
             err = kd->launch(p, s);
@@ -596,6 +647,8 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
     for (int tile : {256, 128, 64}) {
         const KSplit ks = tiled_ksplit(c, tile, tile);
         need = ks.bytes > need ? ks.bytes : need;
+        const KSplit tail = wave_tail(c, tile);
+        need = tail.bytes > need ? tail.bytes : need;
     }
     if (dtype != GEMM_DTYPE_F32 || M > 16) return need;
     for (int i = 0; i < gemm::kF32SplitKernelCount; ++i) {
