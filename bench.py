@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0
 # draining from the last-level cache to HBM while the skinny kernel streams B.
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 # Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
-EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt"]
+EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn"]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -146,6 +146,12 @@ def main():
     def ldb_of(w):
         return w.K if w.op_b == "T" else w.N
 
+    def lda_of(w):
+        return w.M if w.op_a == "T" else w.K
+
+    def ops_of(w):
+        return (tg.GEMM_OP_T if w.op_a == "T" else tg.GEMM_OP_N, tg.GEMM_OP_T if w.op_b == "T" else tg.GEMM_OP_N)
+
     def launch(c, record):
         w = c["w"]
         B = c["B"][c["i"] % len(c["B"])]
@@ -154,10 +160,9 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        if w.dtype == "fp8f32" or w.op_b == "T":
-            st = tg.gemm_general(DTYPES[w.dtype], tg.GEMM_OP_N, tg.GEMM_OP_T if w.op_b == "T" else tg.GEMM_OP_N,
-                                 w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), ldb_of(w), w.beta,
-                                 c["C"].data_ptr(), w.N, 0, None, 0, 0, sh)
+        if w.dtype == "fp8f32" or w.op_b == "T" or w.op_a == "T":
+            st = tg.gemm_general(DTYPES[w.dtype], *ops_of(w), w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), lda_of(w),
+                                 B.data_ptr(), ldb_of(w), w.beta, c["C"].data_ptr(), w.N, 0, None, 0, 0, sh)
         elif c["ws"] is not None:
             st = tg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
                                 c["C"].data_ptr(), w.N, c["ws"].data_ptr(), c["ws"].numel(), sh)
@@ -197,9 +202,8 @@ def main():
         ms = sum(e0.elapsed_time(e1) for e0, e1 in c["durs"]) / len(c["durs"])
         tflops = w.flops / (ms * 1e-3) / 1e12
         gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
-        plan = tg.gemm_plan_query_general(DTYPES[w.dtype], tg.GEMM_OP_N,
-                                          tg.GEMM_OP_T if w.op_b == "T" else tg.GEMM_OP_N, w.M, w.N, w.K, w.alpha,
-                                          c["A"].data_ptr(), w.K, c["B"][0].data_ptr(), ldb_of(w), w.beta,
+        plan = tg.gemm_plan_query_general(DTYPES[w.dtype], *ops_of(w), w.M, w.N, w.K, w.alpha,
+                                          c["A"].data_ptr(), lda_of(w), c["B"][0].data_ptr(), ldb_of(w), w.beta,
                                           c["C"].data_ptr(), w.N, 0,
                                           c["ws"].numel() if c["ws"] is not None else 0)[1]
         kname = tg.gemm_kernel_query(plan["kernel_id"])["name"]

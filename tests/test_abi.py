@@ -468,7 +468,7 @@ def test_fp8_nt_unaligned_falls_back_to_general(why):
 def test_layouts_without_a_fast_kernel_take_general(dtype, prefix, ops):
     st, pl = gplan(dtype, ops[0], ops[1], 1000, 3000, 784)      # K a multiple of 16: fast kernels can run
     assert st == OK
-    fast = (dtype in (F32, BF16) and ops == (N_, N_)) or (dtype in (BF16, FP8) and ops == (N_, T_))
+    fast = (dtype in (F32, BF16) and ops == (N_, N_)) or (dtype == FP8 and ops == (N_, T_)) or dtype == BF16
     if fast:
         assert "general" not in kname(pl), pl
     else:
@@ -529,3 +529,13 @@ def test_wave_tail_other_layouts(dtype, ops):
     ws = tg.gemm_workspace_size(dtype, M, N, 4096)
     st, pl = gplan(dtype, ops[0], ops[1], M, N, 4096, ws=ws)
     assert st == OK and pl["split_row"] > 0 and pl["splits"] >= 2, pl
+
+
+@pytest.mark.parametrize("ops,name", [((N_, T_), "nt"), ((T_, N_), "tn"), ((T_, T_), "tt")])
+def test_bf16_transposed_layouts_take_their_rings(ops, name):
+    st, pl = gplan(BF16, ops[0], ops[1], 8192, 8192, 8192)
+    assert st == OK and kname(pl) == f"bf16_mfma32_256x256x32_w2x2_a8b8_{name}_ring4", pl
+    # A^T rows are M long: M not a multiple of 8 leaves only the general kernel.
+    if ops[0] == T_:
+        st, pl = gplan(BF16, ops[0], ops[1], 8196, 8192, 8192)
+        assert st == OK and kname(pl) == "bf16_general_128x128x16", pl

@@ -38,6 +38,11 @@ U32 = 2.0 ** -24
 RUN_TRUNC = 7 * 2.0 ** -13
 FP8_RING = "fp8_mfma32_256x256x64_w2x2_nt_ring4"
 BF16_NT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4"
+BF16_TN_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4"
+BF16_TT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4"
+# (dtype, kernel, op_a, op_b) of every ring kernel for a transposed layout
+T_RINGS = [("fp8f32", FP8_RING, "N", "T"), ("bf16f32", BF16_NT_RING, "N", "T"),
+           ("bf16f32", BF16_TN_RING, "T", "N"), ("bf16f32", BF16_TT_RING, "T", "T")]
 
 
 def stored(A, B, op_a, op_b):
@@ -167,42 +172,56 @@ FP8_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("dtype,ring_name", [("fp8f32", FP8_RING), ("bf16f32", BF16_NT_RING)], ids=["fp8", "bf16"])
-@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_nt_ring_shapes(gpu_available, dtype, ring_name, shape):
-    """The A x B^T ring kernels, forced (small problems would otherwise take
-    the smallest tile), on edge shapes."""
+def ring_shape(shape, op_a, op_b):
+    """Adjust an edge shape to what a ring kernel for this layout needs: the
+    stored rows of A and B are whole 16-byte chunks (M is A^T's row length,
+    N is an untransposed B's)."""
     M, N, K = shape
+    if op_a == "T":
+        M = -(-M // 8) * 8
+    if op_b == "N":
+        N = -(-N // 8) * 8
+    return M, N, K
+
+
+@pytest.mark.parametrize("ring_case", T_RINGS, ids=lambda c: c[1])
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_transposed_ring_shapes(gpu_available, ring_case, shape):
+    """The ring kernels for transposed layouts, forced (small problems would
+    otherwise take the smallest tile), on edge shapes."""
+    dtype, ring_name, op_a, op_b = ring_case
+    M, N, K = ring_shape(shape, op_a, op_b)
     ring = [k["id"] for k in tg.kernels() if k["name"] == ring_name][0]
-    ok, _ = runnable(dtype, "N", "T", M, N, K, ring)
+    ok, _ = runnable(dtype, op_a, op_b, M, N, K, ring)
     assert ok
     A, B, C0 = make_integer_inputs(M, N, K, seed=710, dtype=dtype)
-    As, Bs = stored(A, B, "N", "T")
-    say(f"[nt ring] {ring_name} exact M={M} N={N} K={K} seed=710")
-    C, _, _ = run_gemm(As, Bs, C0, -1.0, 2.0, kernel=ring, op_b="T")
-    np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, -1.0, 2.0, "N", "T"))
+    As, Bs = stored(A, B, op_a, op_b)
+    say(f"[t ring] {ring_name} exact M={M} N={N} K={K} seed=710")
+    C, _, _ = run_gemm(As, Bs, C0, -1.0, 2.0, kernel=ring, op_a=op_a, op_b=op_b)
+    np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, -1.0, 2.0, op_a, op_b))
     A, B, C0 = make_random_inputs(M, N, K, seed=711, dist="normal", dtype=dtype)
-    As, Bs = stored(A, B, "N", "T")
-    say(f"[nt ring] {ring_name} random M={M} N={N} K={K} seed=711")
-    C, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_b="T")
-    r = check(C, As, Bs, C0, 0.5, 0.25, "N", "T", dtype)
-    say(f"[nt ring] worst err/allowance {r:.3e}")
+    As, Bs = stored(A, B, op_a, op_b)
+    say(f"[t ring] {ring_name} random M={M} N={N} K={K} seed=711")
+    C, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_a=op_a, op_b=op_b)
+    r = check(C, As, Bs, C0, 0.5, 0.25, op_a, op_b, dtype)
+    say(f"[t ring] worst err/allowance {r:.3e}")
 
 
-@pytest.mark.parametrize("dtype,ring_name", [("fp8f32", FP8_RING), ("bf16f32", BF16_NT_RING)], ids=["fp8", "bf16"])
+@pytest.mark.parametrize("ring_case", T_RINGS, ids=lambda c: c[1])
 @pytest.mark.parametrize("act", ["relu", "gelu"])
 @pytest.mark.parametrize("c_offset", [0, 1])
-def test_nt_ring_epilogue_and_c_alignment(gpu_available, dtype, ring_name, act, c_offset):
-    M, N, K = 520, 777, 512
+def test_transposed_ring_epilogue_and_c_alignment(gpu_available, ring_case, act, c_offset):
+    dtype, ring_name, op_a, op_b = ring_case
+    M, N, K = ring_shape((520, 777, 512), op_a, op_b)
     A, B, C0 = make_random_inputs(M, N, K, seed=712, dist="normal", dtype=dtype)
-    As, Bs = stored(A, B, "N", "T")
+    As, Bs = stored(A, B, op_a, op_b)
     bias = make_bias(N, seed=713)
     alpha = 1.0 / np.sqrt(K)
     ring = [k["id"] for k in tg.kernels() if k["name"] == ring_name][0]
-    say(f"[nt ring] {ring_name} epilogue act={act} M={M} N={N} K={K} c_offset={c_offset}")
+    say(f"[t ring] {ring_name} epilogue act={act} M={M} N={N} K={K} c_offset={c_offset}")
     C, _, _ = run_gemm(As, Bs, C0, alpha, -0.5, kernel=ring, offset=(0, 0, c_offset), bias=bias, activation=act,
-                       op_b="T")
-    check(C, As, Bs, C0, alpha, -0.5, "N", "T", dtype, bias=bias, act=act)
+                       op_a=op_a, op_b=op_b)
+    check(C, As, Bs, C0, alpha, -0.5, op_a, op_b, dtype, bias=bias, act=act)
 
 
 def test_fp8_ring_deterministic_and_bench_shape_sampled(gpu_available):

@@ -492,7 +492,11 @@ __device__ __forceinline__ int ring_swz_a(int row) { return (row >> 2) & 3; }
 // BT: B is stored transposed (N x K, k contiguous), so its slices take the A
 // layout, loads and fragment reads above, and N needs no alignment: runs of
 // C columns that straddle N are stored element by element.
-template <int NS, int GROUP_M, bool BT>
+// AT: A is stored transposed (K x M, m contiguous), the shape of an
+// untransposed B, so its slices take the B layout, loads and transposing
+// reads above.  The reads deliver each lane's k values in the same order as
+// the 16-byte reads do, so either form of A pairs with either form of B.
+template <int NS, int GROUP_M, bool BT, bool AT>
 __global__ void __launch_bounds__(256)
 bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint16_t>(p);
@@ -531,6 +535,12 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int lca = (lane & 3) ^ ring_swz_a(ra);
         a_kc[j] = 8 * lca;
         a_goff[j] = (uint32_t)(ra * lda + 8 * lca) * 2u;
+        if (AT) {
+            // Rows of A^T (k rows, m contiguous) laid out as an untransposed B.
+            const int mb = blk >> 1, rk = 16 * (blk & 1) + (lane >> 2);
+            const int lck = (lane & 3) ^ (2 * ((rk >> 1) & 1));
+            a_goff[j] = (uint32_t)(rk * lda + 32 * mb + 8 * lck) * 2u;
+        }
         if (BT) {
             // Rows of B^T (columns of B) laid out as A's rows; same chunk k as A.
             b_goff[j] = (uint32_t)(ra * ldb + 8 * lca) * 2u;
@@ -545,7 +555,10 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // added to its offset.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
-        ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
+        if (AT)
+            ra = make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent(((int64_t)(K - k0 - 1) * lda + (M - m0)) * 2));
+        else
+            ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
         if (BT)
             rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 2));
         else
@@ -555,7 +568,8 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // 4*wave + j, j >= 4 fills B block 4*wave + j - 4.
     auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
         if (j < 4) {
-            const uint32_t poison = (uint32_t)(a_kc[j] >= K - kt * BK) << 31;
+            // (A^T rows past K already fall outside the extent.)
+            const uint32_t poison = AT ? 0u : (uint32_t)(a_kc[j] >= K - kt * BK) << 31;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16, a_goff[j] + poison, 0, 0, 0);
         } else {
@@ -578,6 +592,9 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int bch = 2 * (q & 1) + ((j16 & 3) >> 1);
     const uint32_t fb_base = (uint32_t)(kA + wn * 4 * 2048 + brow * 64 + 16 * (bch ^ (2 * ((brow >> 1) & 1))) +
                                         8 * (j16 & 1));
+    // AT: A^T fragment reads, the transposing pattern of B in the A half of the stage.
+    const uint32_t fat_base = (uint32_t)(wm * 4 * 2048 + brow * 64 + 16 * (bch ^ (2 * ((brow >> 1) & 1))) +
+                                         8 * (j16 & 1));
     uint32_t fbt_base[2];   // BT: B^T fragment reads, the A pattern in the B half of the stage
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -590,7 +607,13 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // ds_read_b64_tr_b16 for a B fragment).
     auto read_slot = [&](int stage, int s, int set, int r) {
         char *base = stage_base(stage);
-        if (r == 0 || r >= 5) {
+        if ((r == 0 || r >= 5) && AT) {
+            const int f = r == 0 ? 0 : r - 4;
+            const int aoff = fat_base + 2048 * f + 1024 * s;
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + aoff));
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + aoff + 256));
+            fa[set][f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else if (r == 0 || r >= 5) {
             const int f = r == 0 ? 0 : r - 4;
             fa[set][f] = *reinterpret_cast<const bf16x8 *>(base + fa_base[s] + 2048 * f);
         } else if (BT) {
@@ -738,12 +761,12 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     });
 }
 
-template <int NS, int GROUP_M, bool BT = false>
+template <int NS, int GROUP_M, bool BT = false, bool AT = false>
 hipError_t launch_bf16_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT, AT>),
                            dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
@@ -764,9 +787,11 @@ hipError_t launch_bf16_tiled(const GemmParams &p, hipStream_t stream) {
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
 template __global__ void bf16_pipe_kernel<4>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4, false>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<5, 4, false>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4, true>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, false>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<5, 4, false, false>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, false>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, true>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, true>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 8, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 1, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 1, 8, 4>(GemmParams, int, int);
@@ -787,9 +812,14 @@ const KernelDesc kBf16TiledKernels[] = {
      &launch_bf16_ring<5, 4>, 1024},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_pipe",
      &launch_bf16_pipe<4>},
-    // B stored N x K: the only fast kernel for that layout, so no K minimum.
+    // Transposed layouts: the only fast kernels for them, so no K minimum.
+    // vec_a / vec_b = 8: the stored rows of A and B are 16-byte multiples.
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4",
-     &launch_bf16_ring<4, 4, true>, 0, nullptr, kLayoutNT},
+     &launch_bf16_ring<4, 4, true, false>, 0, nullptr, kLayoutNT},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
+     &launch_bf16_ring<4, 4, false, true>, 0, nullptr, kLayoutTN},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4",
+     &launch_bf16_ring<4, 4, true, true>, 0, nullptr, kLayoutTT},
     BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
     BF16_TILED(256, 256, 64, 2, 2, 8, 1, 4),
     BF16_TILED(256, 256, 64, 2, 2, 1, 8, 4),

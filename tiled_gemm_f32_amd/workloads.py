@@ -15,8 +15,8 @@ Recipe (fixed, so that every run sees the same bytes):
 * bf16 operands: the fp32 draw rounded to bf16 with ``.to(torch.bfloat16)``
   (round to nearest even); C0 stays fp32.  fp8 operands likewise with
   ``.to(torch.float8_e4m3fn)`` (OCP E4M3, round to nearest even).
-* A transposed operand (``op_b == "T"``) is drawn in its defining shape
-  (K x N) and then stored transposed.
+* A transposed operand (``op_a`` or ``op_b == "T"``) is drawn in its
+  defining shape (M x K or K x N) and then stored transposed.
 
 The shapes are the square and ragged problems the pages measure on (4092 and
 4096 cubes on page 1 and page 3), a small cube, a ragged shape that is a
@@ -42,6 +42,7 @@ class Workload:
     dist: str           # "uniform" (U[-1, 1]) or "normal" (N(0, 1))
     seed: int
     op_b: str = "N"     # "T": B is stored transposed (N x K)
+    op_a: str = "N"     # "T": A is stored transposed (K x M)
 
     @property
     def flops(self) -> int:
@@ -70,6 +71,7 @@ WORKLOADS = {
         # fp8 operands with B stored N x K, the layout of the fp8 matrix-core kernel.
         Workload("fp8f32_8192_nt", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 5, "T"),
         Workload("bf16f32_8192_nt", "bf16f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 6, "T"),
+        Workload("bf16f32_8192_tn", "bf16f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 7, "N", "T"),
     ]
 }
 
@@ -96,6 +98,8 @@ def make_inputs(w: Workload):
     A, B = _operand_type(A, w.dtype), _operand_type(B, w.dtype)
     if w.op_b == "T":
         B = B.t().contiguous()
+    if w.op_a == "T":
+        A = A.t().contiguous()
     return A, B, C0
 
 
