@@ -44,7 +44,7 @@ PEAK_HBM_GBS = 8000.0
 # draining from the last-level cache to HBM while the skinny kernel streams B.
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 # Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
-EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn"]
+EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x8192x8192"]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -135,7 +135,10 @@ def main():
         Ad, C = _to_device(A, dev), C0.to(dev)
         copies = SKINNY_COPIES if w.M <= 16 else 1
         Bs = [_to_device(B, dev) for _ in range(copies)]
-        ws = tg.workspace(w.M, w.N, w.K, device=dev) if w.dtype == "f32" else None
+        ws = None
+        if w.dtype == "f32" or (w.dtype == "bf16f32" and w.M <= 16):
+            ws = tg.workspace(w.M, w.N, w.K, device=dev, dtype=tg.GEMM_DTYPE_F32 if w.dtype == "f32" else
+                              tg.GEMM_DTYPE_BF16F32)
         calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []})
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -164,8 +167,9 @@ def main():
             st = tg.gemm_general(DTYPES[w.dtype], *ops_of(w), w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), lda_of(w),
                                  B.data_ptr(), ldb_of(w), w.beta, c["C"].data_ptr(), w.N, 0, None, 0, 0, sh)
         elif c["ws"] is not None:
-            st = tg.gemm_f32_ws(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
-                                c["C"].data_ptr(), w.N, c["ws"].data_ptr(), c["ws"].numel(), sh)
+            fws = tg.gemm_f32_ws if w.dtype == "f32" else tg.gemm_bf16f32_ws
+            st = fws(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
+                     c["C"].data_ptr(), w.N, c["ws"].data_ptr(), c["ws"].numel(), sh)
         else:
             st = fn(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
                     c["C"].data_ptr(), w.N, sh)

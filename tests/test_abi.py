@@ -539,3 +539,23 @@ def test_bf16_transposed_layouts_take_their_rings(ops, name):
     if ops[0] == T_:
         st, pl = gplan(BF16, ops[0], ops[1], 8196, 8192, 8192)
         assert st == OK and kname(pl) == "bf16_general_128x128x16", pl
+
+
+# ----------------------------------------------------------------------------- bf16 skinny
+
+def test_bf16_skinny_with_workspace():
+    for M in (1, 7, 16):
+        ws = tg.gemm_workspace_size(BF16, M, 8192, 8192)
+        assert ws >= 4 * M * 8192 * 4               # at least 4 splits of M x N fp32 partials
+        st, pl = plan(BF16, M, 8192, 8192, ws=ws)
+        assert st == OK and pl["path"] == tg.GEMM_PATH_SKINNY_SPLITK and pl["grid"] == 64 * 4, pl
+        assert kname(pl) == "bf16_skinny_lds_n128_w4_s4"
+    # A not 16-byte aligned: the tiled kernels.
+    st, pl = plan(BF16, 16, 8192, 8192, A=PA + 2, ws=1 << 30)
+    assert st == OK and pl["path"] == tg.GEMM_PATH_TILED, pl
+    # Without a workspace a split is impossible: the tiled path, unless no split is needed.
+    assert plan(BF16, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
+    assert plan(BF16, 16, 32768, 8192)[1]["path"] == tg.GEMM_PATH_SKINNY_SPLITK
+    # B rows must be whole 16-byte chunks; M = 17 is not skinny.
+    assert plan(BF16, 16, 8196, 8192, ws=1 << 30)[1]["path"] == tg.GEMM_PATH_TILED
+    assert plan(BF16, 17, 8192, 8192, ws=1 << 30)[1]["path"] == tg.GEMM_PATH_TILED

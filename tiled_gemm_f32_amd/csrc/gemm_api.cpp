@@ -33,7 +33,8 @@ constexpr int kComputeUnits = 256;
 
 int table_size() {
     return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
-           gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount;
+           gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount +
+           gemm::kBf16SplitKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -50,6 +51,8 @@ const KernelDesc *kernel_by_id(int32_t id) {
     if (i < gemm::kFp8TiledKernelCount) return &gemm::kFp8TiledKernels[i];
     i -= gemm::kFp8TiledKernelCount;
     if (i < gemm::kGeneralKernelCount) return &gemm::kGeneralKernels[i];
+    i -= gemm::kGeneralKernelCount;
+    if (i < gemm::kBf16SplitKernelCount) return &gemm::kBf16SplitKernels[i];
     return nullptr;
 }
 
@@ -263,6 +266,12 @@ const KernelDesc *choose(const Call &c) {
     }
     if (plain && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kF32SkinnyKernels, gemm::kF32SkinnyKernelCount, c, 0))
+            return kd;
+    }
+    // bf16 weights with M <= 16: the streaming kernel, split over K when the
+    // caller's workspace allows (it needs one only when it splits).
+    if (plain && c.dtype == GEMM_DTYPE_BF16F32 && skinny_fits(c)) {
+        if (const KernelDesc *kd = first_match(gemm::kBf16SplitKernels, gemm::kBf16SplitKernelCount, c, 0))
             return kd;
     }
     if (const KernelDesc *kd = choose_tiled(c, tiled_candidates(c, false))) return kd;
@@ -650,9 +659,11 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
         const KSplit tail = wave_tail(c, tile);
         need = tail.bytes > need ? tail.bytes : need;
     }
-    if (dtype != GEMM_DTYPE_F32 || M > 16) return need;
-    for (int i = 0; i < gemm::kF32SplitKernelCount; ++i) {
-        const int64_t strips = ceil_div(N, gemm::kF32SplitKernels[i].tile_n);
+    if (M > 16 || dtype == GEMM_DTYPE_FP8F32) return need;
+    const gemm::KernelDesc *skinny = dtype == GEMM_DTYPE_F32 ? gemm::kF32SplitKernels : gemm::kBf16SplitKernels;
+    const int count = dtype == GEMM_DTYPE_F32 ? gemm::kF32SplitKernelCount : gemm::kBf16SplitKernelCount;
+    for (int i = 0; i < count; ++i) {
+        const int64_t strips = ceil_div(N, skinny[i].tile_n);
         const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);
         need = b > need ? b : need;
     }
