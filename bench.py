@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--only", choices=STEP + EXTRA, default=None,
                     help="time a single workload (of the step, or one of the extra ones)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--observe-clocks", type=float, default=6.0,
+                    help="after the timed steps, keep running the step this many seconds while amd-smi samples "
+                         "the GFX clocks and socket power (0: off)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (a plain kernel of known traffic) so hardware "
                          "byte counters can be scaled against it")
@@ -98,6 +101,68 @@ def measured_traffic(kernel_name: str):
     if not rec or rec.get("source_sha256") != kernel_source_sha(kernel_name):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _amd_smi_sample(exe):
+    """(socket power W, [GFX clock MHz per XCD]) from one amd-smi metric call, or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run([exe, "metric", "-g", "0", "--clock", "--power"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    power = re.search(r"SOCKET_POWER:\s*(\d+(?:\.\d+)?)\s*W", out)
+    clocks, in_gfx = [], False
+    for line in out.splitlines():
+        if re.match(r"^\s*GFX_\d+:\s*$", line):
+            in_gfx = True
+            continue
+        m = re.match(r"^\s*CLK:\s*(\d+)\s*MHz", line)
+        if m and in_gfx:
+            clocks.append(int(m.group(1)))
+        in_gfx = False if m else in_gfx
+    if power is None or not clocks:
+        return None
+    return float(power.group(1)), clocks
+
+
+def observe_clocks(run_step, seconds):
+    """Run the step for `seconds` while a thread samples amd-smi; median GFX
+    clock (mean over XCDs) and socket power, or None when unavailable."""
+    import shutil
+    import statistics
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None or seconds <= 0:
+        return None
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        stop.wait(0.5)                   # let the clocks settle on the load first
+        while not stop.is_set():
+            s = _amd_smi_sample(exe)
+            if s is not None:
+                samples.append(s)
+            stop.wait(0.25)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            run_step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    mean_clk = [sum(c) / len(c) for _, c in samples]
+    return {"gfx_mhz_median": round(statistics.median(mean_clk)), "gfx_mhz_min": min(min(c) for _, c in samples),
+            "gfx_mhz_max": max(max(c) for _, c in samples),
+            "socket_power_w_median": round(statistics.median(p for p, _ in samples)), "samples": len(samples),
+            "seconds": seconds, "tool": "amd-smi metric --clock --power"}
 
 
 def _to_device(t, dev):
@@ -233,6 +298,12 @@ def main():
     dominant = max(parts, key=lambda n: parts[n]["ms"])
     roof = roofline_of(dominant)
 
+    def one_step():
+        for c in calls:
+            launch(c, False)
+
+    observed = observe_clocks(one_step, args.observe_clocks)
+
     cpu = None
     if not args.no_cpu_baseline and not args.only:
         cpu = cpu_baseline(calls)
@@ -248,6 +319,7 @@ def main():
         "roofline": roof,
         "rooflines": [roofline_of(n) for n in parts],
         "parts": parts,
+        "observed_clocks": observed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
