@@ -68,7 +68,8 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_tiled.hip",
-                  "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip"}
+                  "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip",
+                  "bf16_skinny": "gemm_bf16_skinny.hip"}
 
 
 # Headers every kernel source includes: a change there changes the kernels too.
