@@ -214,7 +214,7 @@ def test_vector_width_follows_alignment():
 def test_forced_kernels():
     f32_tiled = kernel_ids(dtype=F32, path=tg.GEMM_PATH_TILED)
     bf16_tiled = kernel_ids(dtype=BF16, path=tg.GEMM_PATH_TILED)
-    skinny = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY)
+    skinny = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY, layouts=1)
     assert f32_tiled and bf16_tiled and skinny
     for kid in f32_tiled:
         st, p = plan(F32, 512, 512, 512, force=kid)
@@ -227,7 +227,7 @@ def test_forced_kernels():
     wide_a = [k for k in f32_tiled if tg.gemm_kernel_query(k)["vec_a"] == 4]
     assert all(plan(F32, 1000, 3000, 777, force=k)[0] == UNSUP for k in wide_a)
     # Workspace kernels need a workspace of the advertised size.
-    split = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY_SPLITK)
+    split = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY_SPLITK, layouts=1)
     assert split
     need = tg.gemm_workspace_size(F32, 16, 512, 4096)
     for kid in split:
@@ -559,3 +559,50 @@ def test_bf16_skinny_with_workspace():
     # B rows must be whole 16-byte chunks; M = 17 is not skinny.
     assert plan(BF16, 16, 8196, 8192, ws=1 << 30)[1]["path"] == tg.GEMM_PATH_TILED
     assert plan(BF16, 17, 8192, 8192, ws=1 << 30)[1]["path"] == tg.GEMM_PATH_TILED
+
+
+# ----------------------------------------------------------------------------- skinny, B stored N x K
+
+@pytest.mark.parametrize("dtype,prefix,chunk", [(F32, "f32", 4), (BF16, "bf16", 8)])
+def test_skinny_nt_choice(dtype, prefix, chunk):
+    # 256 strips of 32 columns cover the chip: no split, no workspace needed.
+    for M in (1, 9, 16):
+        st, pl = gplan(dtype, N_, T_, M, 8192, 8192)
+        assert st == OK and kname(pl) == f"{prefix}_skinny_nt_n32_w8_u2", pl
+        assert pl["path"] == tg.GEMM_PATH_SKINNY and pl["grid"] == 256
+    # With a workspace and few strips: K split across workgroups.
+    ws = tg.gemm_workspace_size(dtype, 16, 1024, 8192)
+    assert ws >= 8 * 16 * 1024 * 4
+    st, pl = gplan(dtype, N_, T_, 16, 1024, 8192, ws=ws)
+    assert st == OK and kname(pl) == f"{prefix}_skinny_nt_splitk_n32_w8_u2" and pl["grid"] == 32 * 8, pl
+    # The same shape with the workspace of a call that needs no split: plain.
+    st, pl = gplan(dtype, N_, T_, 16, 8192, 8192, ws=tg.gemm_workspace_size(dtype, 16, 8192, 8192))
+    assert st == OK and kname(pl) == f"{prefix}_skinny_nt_n32_w8_u2", pl
+    # M = 17, rows that are not whole 16-byte chunks, or op_a = T: not the skinny kernel.
+    for kw in (dict(M=17), dict(K=8192 + chunk // 2), dict(ldb=8192 + chunk // 2), dict(B=PB + 4 * (dtype == BF16) + 8)):
+        args = dict(M=16, N=8192, K=8192)
+        args.update(kw)
+        st, pl = gplan(dtype, N_, T_, **args)
+        assert st == OK and "skinny_nt" not in kname(pl), (kw, kname(pl))
+    st, pl = gplan(dtype, T_, T_, 16, 8192, 8192)
+    assert st == OK and "skinny_nt" not in kname(pl)
+
+
+def test_skinny_nt_largest_leading_dimension():
+    # Leading dimensions stop at 2^21 - 1 elements, so 32 rows of B^T (and 16
+    # of A) stay below 2^31 bytes and the kernel's 32-bit offsets always fit.
+    ld = (1 << 21) - 4
+    st, pl = gplan(F32, N_, T_, 16, 64, 8192, lda=ld, ldb=ld)
+    assert st == OK and "skinny_nt" in kname(pl), pl
+    assert gplan(F32, N_, T_, 16, 64, 8192, ldb=(1 << 21) + 4)[0] != OK
+
+
+def test_skinny_nt_forced_needs_its_layout():
+    for k in tg.kernels():
+        if "skinny_nt" not in k["name"]:
+            continue
+        assert k["layouts"] == 2
+        st, _ = plan(k["dtype"], 16, 8192, 8192, force=k["id"], ws=1 << 30)
+        assert st == UNSUP, k["name"]
+        st, _ = gplan(k["dtype"], N_, T_, 16, 8192, 8192, force=k["id"], ws=1 << 30)
+        assert st == OK, k["name"]

@@ -20,7 +20,8 @@ BF16 = tg.GEMM_DTYPE_BF16F32
 
 
 def _skinny_ids():
-    return {k["name"]: k["id"] for k in tg.kernels() if k["dtype"] == BF16 and k["path"] == tg.GEMM_PATH_SKINNY_SPLITK}
+    return {k["name"]: k["id"] for k in tg.kernels() if k["dtype"] == BF16 and k["path"] == tg.GEMM_PATH_SKINNY_SPLITK
+            and k["layouts"] & 1}
 
 
 def _ws(M, N, K):

@@ -34,7 +34,7 @@ constexpr int kComputeUnits = 256;
 int table_size() {
     return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
            gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount +
-           gemm::kBf16SplitKernelCount;
+           gemm::kBf16SplitKernelCount + gemm::kSkinnyNtKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -53,6 +53,8 @@ const KernelDesc *kernel_by_id(int32_t id) {
     if (i < gemm::kGeneralKernelCount) return &gemm::kGeneralKernels[i];
     i -= gemm::kGeneralKernelCount;
     if (i < gemm::kBf16SplitKernelCount) return &gemm::kBf16SplitKernels[i];
+    i -= gemm::kBf16SplitKernelCount;
+    if (i < gemm::kSkinnyNtKernelCount) return &gemm::kSkinnyNtKernels[i];
     return nullptr;
 }
 
@@ -124,10 +126,18 @@ int max_vec_a(const Call &c) {
 }
 bool vec_b_ok(const Call &c, int v) { return vec_ok(c.B, c.ldb, row_len_b(c), elem_size(c.dtype), v); }
 
-// The skinny kernels address B with 32-bit offsets; their prefetch runs at
-// most 48 * WAVES * UNROLL (<= 1536) rows past K, so K + 2048 rows must fit.
+// The skinny kernels address B with 32-bit offsets.  With B stored K x N
+// their prefetch runs at most 48 * WAVES * UNROLL (<= 1536) rows past K, so
+// K + 2048 rows must fit.  With B stored N x K a workgroup's 32 rows of B
+// and the 16 rows of A, each K long, must fit.
 bool skinny_fits(const Call &c) {
-    return c.M <= 16 && (c.K + 2048) * c.ldb * 4 < (int64_t(1) << 31);
+    if (c.M > 16) return false;
+    const int64_t lim = int64_t(1) << 31;
+    if (c.op_b == GEMM_OP_T) {
+        const int64_t esz = elem_size(c.dtype);
+        return (32 * c.ldb + c.K) * esz < lim && (16 * c.lda + c.K) * esz < lim;
+    }
+    return (c.K + 2048) * c.ldb * 4 < lim;
 }
 
 int64_t split_workspace_bytes(const Call &c, const KernelDesc *kd) {
@@ -273,6 +283,21 @@ const KernelDesc *choose(const Call &c) {
     if (plain && c.dtype == GEMM_DTYPE_BF16F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kBf16SplitKernels, gemm::kBf16SplitKernelCount, c, 0))
             return kd;
+    }
+    // M <= 16 with B stored N x K (a linear layer's weights): the streaming
+    // kernel that reads weight rows straight into the matrix instruction,
+    // split over K only where the workspace lets it cover the compute units.
+    if (c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_T && skinny_fits(c)) {
+        for (int i = 0; i < gemm::kSkinnyNtKernelCount; ++i) {
+            const KernelDesc *kd = &gemm::kSkinnyNtKernels[i];
+            if (kd->path == GEMM_PATH_SKINNY_SPLITK && c.ws != nullptr && split_workspace_bytes(c, kd) > 0 &&
+                kernel_runs(kd, c))
+                return kd;
+        }
+        for (int i = 0; i < gemm::kSkinnyNtKernelCount; ++i) {
+            const KernelDesc *kd = &gemm::kSkinnyNtKernels[i];
+            if (kd->path == GEMM_PATH_SKINNY && kernel_runs(kd, c)) return kd;
+        }
     }
     if (const KernelDesc *kd = choose_tiled(c, tiled_candidates(c, false))) return kd;
     return choose_tiled(c, tiled_candidates(c, true));
@@ -664,6 +689,13 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
     const int count = dtype == GEMM_DTYPE_F32 ? gemm::kF32SplitKernelCount : gemm::kBf16SplitKernelCount;
     for (int i = 0; i < count; ++i) {
         const int64_t strips = ceil_div(N, skinny[i].tile_n);
+        const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);
+        need = b > need ? b : need;
+    }
+    for (int i = 0; i < gemm::kSkinnyNtKernelCount; ++i) {
+        const gemm::KernelDesc &kd = gemm::kSkinnyNtKernels[i];
+        if (kd.dtype != dtype || kd.path != GEMM_PATH_SKINNY_SPLITK) continue;
+        const int64_t strips = ceil_div(N, kd.tile_n);
         const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);
         need = b > need ? b : need;
     }

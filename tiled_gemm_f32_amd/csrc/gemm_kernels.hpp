@@ -91,6 +91,8 @@ extern const KernelDesc kGeneralKernels[];
 extern const int kGeneralKernelCount;
 extern const KernelDesc kBf16SplitKernels[];
 extern const int kBf16SplitKernelCount;
+extern const KernelDesc kSkinnyNtKernels[];
+extern const int kSkinnyNtKernelCount;
 
 // C = beta * C over an M x N view (beta == 0 writes zeros without reading).
 hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act,
