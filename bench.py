@@ -45,7 +45,7 @@ PEAK_HBM_GBS = 8000.0
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 # Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
 EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x8192x8192", "bf16f32_16x8192x8192_nt",
-         "f32_16x8192x8192_nt"]
+         "f32_16x8192x8192_nt", "fp8f32_16x8192x8192_nt"]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -70,7 +70,8 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_tiled.hip",
                   "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip",
-                  "bf16_skinny": "gemm_bf16_skinny.hip"}
+                  "bf16_skinny": "gemm_bf16_skinny.hip", "f32_skinny_nt": "gemm_skinny_nt.hip",
+                  "bf16_skinny_nt": "gemm_skinny_nt.hip", "fp8_skinny_nt": "gemm_skinny_nt.hip"}
 
 
 # Headers every kernel source includes: a change there changes the kernels too.
@@ -83,7 +84,8 @@ def kernel_source_sha(kernel_name: str):
     """sha256 over the source file a kernel is built from and the shared
     headers it includes (to spot stale counter data)."""
     import hashlib
-    for prefix, src in KERNEL_SOURCES.items():
+    # The longest matching prefix names the source.
+    for prefix, src in sorted(KERNEL_SOURCES.items(), key=lambda kv: -len(kv[0])):
         if kernel_name.startswith(prefix):
             h = hashlib.sha256()
             for path in [os.path.join("tiled_gemm_f32_amd", "csrc", src)] + KERNEL_HEADERS:

@@ -92,10 +92,10 @@ GEMM_API gemm_status gemm_bf16f32(int64_t M, int64_t N, int64_t K, float alpha,
  * results in a caller-provided device workspace (the split-K variant of
  * "Tiled matrix multiplication", section "Variants and alternatives", and of
  * "A GEMM Kernel, Step by Step", section "What is left"):
- *   - fp32 and bf16 with M <= 16: the skinny streaming kernels, split into
- *     up to 8 k ranges of at least 512 while the strips of C (128 columns,
- *     or 32 with B stored N x K through gemm_general) number fewer than the
- *     256 compute units;
+ *   - M <= 16 (fp32 and bf16; with B stored N x K through gemm_general, fp8
+ *     too): the skinny streaming kernels, split into up to 8 k ranges of at
+ *     least 512 while the strips of C (128 columns, or 32 with B stored
+ *     N x K) number fewer than the 256 compute units;
  *   - any tiled problem with fewer output tiles than compute units: the
  *     tiled kernel, split into up to 16 k ranges of at least 1024, when the
  *     split grid fills at least three quarters of the compute units;
@@ -277,9 +277,9 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  * kernel of gemm_f32_ex.  A and B point to fp32, bf16 (uint16_t) or fp8
  * E4M3 (uint8_t) elements as dtype says; C is fp32.  Every combination runs:
  *   - untransposed fp32 and bf16 take the kernels above;
- *   - fp32 and bf16 with M <= 16, A untransposed and B transposed
- *     (GEMM_OP_N, GEMM_OP_T: B stored N x K, the layout of a linear layer's
- *     weights) take a streaming kernel that loads each weight row straight
+ *   - M <= 16 with A untransposed and B transposed (GEMM_OP_N, GEMM_OP_T:
+ *     B stored N x K, the layout of a linear layer's weights), any operand
+ *     type, takes a streaming kernel that loads each weight row straight
  *     into the matrix instruction, when the rows of A and B are whole
  *     16-byte chunks (aligned bases, K, lda and ldb);
  *   - bf16 with either operand transposed takes the matrix-core kernel for

@@ -67,7 +67,8 @@ def run_gemm(A, B, C0, alpha, beta, kernel=0, pad=(0, 0, 0), offset=(0, 0, 0), c
     if ws is None and needs_workspace(kernel):
         M, K = A.shape if op_a == "N" else A.shape[::-1]
         N = B.shape[1] if op_b == "N" else B.shape[0]
-        dt = {torch.float32: tg.GEMM_DTYPE_F32, torch.bfloat16: tg.GEMM_DTYPE_BF16F32}[A.dtype]
+        dt = {torch.float32: tg.GEMM_DTYPE_F32, torch.bfloat16: tg.GEMM_DTYPE_BF16F32,
+              torch.float8_e4m3fn: tg.GEMM_DTYPE_FP8F32}[A.dtype]
         ws = tg.workspace(M, N, K, dtype=dt)
     bd = bias.to("cuda") if bias is not None else None
     tg.gemm(Ad, Bd, Cd, alpha=alpha, beta=beta, kernel=kernel, ws=ws, bias=bd, activation=activation, op_a=op_a,

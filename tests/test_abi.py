@@ -563,7 +563,7 @@ def test_bf16_skinny_with_workspace():
 
 # ----------------------------------------------------------------------------- skinny, B stored N x K
 
-@pytest.mark.parametrize("dtype,prefix,chunk", [(F32, "f32", 4), (BF16, "bf16", 8)])
+@pytest.mark.parametrize("dtype,prefix,chunk", [(F32, "f32", 4), (BF16, "bf16", 8), (FP8, "fp8", 16)])
 def test_skinny_nt_choice(dtype, prefix, chunk):
     # 256 strips of 32 columns cover the chip: no split, no workspace needed.
     for M in (1, 9, 16):

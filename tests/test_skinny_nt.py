@@ -1,10 +1,13 @@
 """GPU parity of the skinny kernels for B stored N x K (M <= 16, the
-decode-GEMV layout of a linear layer's weights): fp32 and bf16 operands,
-with and without a K split through the workspace.
+decode-GEMV layout of a linear layer's weights): fp32, bf16 and fp8 (OCP
+E4M3) operands, with and without a K split through the workspace.
 
-Integer operands make every sum exact, so results must equal the fp64
-oracle bit for bit; random operands meet the error ratio of the untransposed
-paths (2e-6 fp32, 1e-5 bf16).  Workspaces start full of NaN bit patterns."""
+Integer operands make every sum exact (for fp8 too: products of |v| <= 4
+lie within 2^4 of each other, far inside the matrix unit's 2^-13 run
+truncation), so results must equal the fp64 oracle bit for bit.  Random
+operands meet the error ratio of the untransposed paths (2e-6 fp32, 1e-5
+bf16) and, for fp8, the run-truncation bound of the fp8 kernels.
+Workspaces start full of NaN bit patterns."""
 import numpy as np
 import pytest
 import torch
@@ -14,10 +17,13 @@ import tiled_gemm_f32_amd as tg
 from tiled_gemm_f32_amd.workloads import make_bias, make_integer_inputs, make_random_inputs
 
 from gpu_helpers import TOL, host_view, run_gemm, say
+from test_layouts import check as layout_check
 
 pytestmark = pytest.mark.gpu
 
-DT = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32}
+DT = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32, "fp8f32": tg.GEMM_DTYPE_FP8F32}
+ALL = ["f32", "bf16f32", "fp8f32"]
+ESZ = {"f32": 4, "bf16f32": 2, "fp8f32": 1}
 OP_N, OP_T = tg.GEMM_OP_N, tg.GEMM_OP_T
 
 
@@ -37,6 +43,12 @@ def nbytes(ws):
     return ws.numel() if ws is not None else 0
 
 
+def to_dev(t):
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cuda().view(torch.float8_e4m3fn)
+    return t.cuda()
+
+
 def plan(dtype, M, N, K, kid=0, ws_bytes=0, lda=None, ldb=None):
     return tg.gemm_plan_query_general(DT[dtype], OP_N, OP_T, M, N, K, 1.0, 0x1000, lda or K, 0x1000, ldb or K, 0.5,
                                       0x1000, N, kid, ws_bytes)
@@ -48,7 +60,7 @@ def ref_nt(A, Bt, C0, alpha, beta, bias=None, act="none"):
                                     "N", "T")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("dtype", ALL)
 @pytest.mark.parametrize("M", [1, 5, 16])
 @pytest.mark.parametrize("NK", [(8192, 4096), (1000, 3008), (40, 12288), (33, 64)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_skinny_nt_exact_every_variant(gpu_available, dtype, M, NK):
@@ -67,7 +79,7 @@ def test_skinny_nt_exact_every_variant(gpu_available, dtype, M, NK):
         np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("dtype", ALL)
 @pytest.mark.parametrize("with_ws", [False, True], ids=["no_ws", "ws"])
 def test_skinny_nt_random_full_size(gpu_available, dtype, with_ws):
     """16 x 8192 x 8192 on N(0,1) data, the library's own choice: the error
@@ -81,20 +93,24 @@ def test_skinny_nt_random_full_size(gpu_available, dtype, with_ws):
     assert st == tg.GEMM_OK and "skinny_nt" in name, name
     say(f"[skinny nt] auto {name} M={M} N={N} K={K} random seed=1110 ws={with_ws}")
     C, _, _ = run_gemm(A, Bt, C0, 0.75, 0.5, ws=ws, op_b="T")
-    a, b = host_view(A), host_view(Bt)
-    ref = oracle.gemm_ref(a, b, 0.75, 0.5, C0.numpy(), "N", "T")
-    D = oracle.gemm_absbound(a, b, 0.75, 0.5, C0.numpy(), "N", "T")
-    r = oracle.error_ratio(C, ref, D)
-    say(f"[skinny nt] ratio {r:.3e}")
-    assert r <= TOL[dtype]
-    Ad, Btd = A.cuda(), Bt.cuda()
+    if dtype == "fp8f32":
+        r = layout_check(C, A, Bt, C0, 0.75, 0.5, "N", "T", dtype)
+        say(f"[skinny nt] worst err/allowance {r:.3e}")
+    else:
+        a, b = host_view(A), host_view(Bt)
+        ref = oracle.gemm_ref(a, b, 0.75, 0.5, C0.numpy(), "N", "T")
+        D = oracle.gemm_absbound(a, b, 0.75, 0.5, C0.numpy(), "N", "T")
+        r = oracle.error_ratio(C, ref, D)
+        say(f"[skinny nt] ratio {r:.3e}")
+        assert r <= TOL[dtype]
+    Ad, Btd = to_dev(A), to_dev(Bt)
     outs = [tg.gemm(Ad, Btd, ws=ws, op_b="T") for _ in range(4)]
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
     np.testing.assert_array_equal(outs[0].cpu().numpy(), tg.gemm(Ad, Btd, ws=ws, op_b="T").cpu().numpy())
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("dtype", ALL)
 def test_skinny_nt_split_matches_unsplit(gpu_available, dtype):
     """Few strips and a deep K: the workspace variant splits K across
     workgroups; both variants stay within the bound, and integer data gives
@@ -115,12 +131,12 @@ def test_skinny_nt_split_matches_unsplit(gpu_available, dtype):
     np.testing.assert_array_equal(C1.astype(np.float64), ref_nt(A, Bt, C0, 1.0, 1.0))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("dtype", ALL)
 def test_skinny_nt_padded_rows(gpu_available, dtype):
     """Padded leading dimensions (whole 16-byte chunks of NaN padding) on
     both operands: the padding is never read."""
     M, N, K = 7, 520, 2048
-    chunk = 16 // (4 if dtype == "f32" else 2)
+    chunk = 16 // ESZ[dtype]
     A, B, C0 = make_integer_inputs(M, N, K, seed=1130, dtype=dtype)
     Bt = B.t().contiguous()
     say(f"[skinny nt] padded M={M} N={N} K={K} pad={chunk} seed=1130")
@@ -128,7 +144,7 @@ def test_skinny_nt_padded_rows(gpu_available, dtype):
     np.testing.assert_array_equal(C.astype(np.float64), ref_nt(A, Bt, C0, -1.0, 0.5))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
+@pytest.mark.parametrize("dtype", ALL)
 @pytest.mark.parametrize("act", ["none", "relu", "gelu"])
 def test_skinny_nt_epilogue_random(gpu_available, dtype, act):
     """Every variant with the fused bias and activation on N(0,1) data, to
@@ -145,5 +161,35 @@ def test_skinny_nt_epilogue_random(gpu_available, dtype, act):
     for name, k in nt_kernels(dtype).items():
         say(f"[skinny nt] {name} M={M} N={N} K={K} act={act} random seed=1140")
         C, _, _ = run_gemm(A, Bt, C0, alpha, 0.5, kernel=k["id"], ws=ws, bias=bias, activation=act, op_b="T")
-        r = check_epilogue(C, A, B, C0, alpha, 0.5, bias, act, dtype)
+        if dtype == "fp8f32":
+            r = layout_check(C, A, Bt, C0, alpha, 0.5, "N", "T", dtype, bias=bias, act=act)
+        else:
+            r = check_epilogue(C, A, B, C0, alpha, 0.5, bias, act, dtype)
         say(f"[skinny nt] worst err/allowance {r:.3e}")
+
+
+def test_fp8_adversarial_runs_within_bound(gpu_available):
+    """Every run of 8 consecutive k holds one product of 384 (256 x 1.5)
+    among products of 2^-18 .. 2^-6 with mixed signs, so the matrix unit's
+    truncation below 2^-13 of the run maximum drops most small products:
+    every fp8 kernel for B stored N x K (skinny, ring, general) must stay
+    within the run-truncation bound.  Values are exact E4M3 codes."""
+    M, N, K = 16, 96, 1024
+    rng = np.random.default_rng(1150)
+    k = np.arange(K)
+    big = (k % 8) == ((k // 8) * 3) % 8          # one position per run of 8
+    tiny_a = rng.choice([2.0 ** -9, 2.0 ** -8, 2.0 ** -7, 2.0 ** -6], size=(M, K)) * rng.choice([-1.0, 1.0], size=(M, K))
+    tiny_w = rng.choice([1.0, 0.5, 0.25, 2.0 ** -9], size=(N, K))
+    A = np.where(big[None, :], 256.0, tiny_a).astype(np.float32)
+    Wt = np.where(big[None, :], 1.5, tiny_w).astype(np.float32)
+    A8 = torch.from_numpy(A).to(torch.float8_e4m3fn)
+    W8 = torch.from_numpy(Wt).to(torch.float8_e4m3fn)
+    assert torch.equal(A8.float(), torch.from_numpy(A)) and torch.equal(W8.float(), torch.from_numpy(Wt))
+    C0 = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32))
+    names = ["fp8_skinny_nt_n32_w8_u2", "fp8_mfma32_256x256x64_w2x2_nt_ring4", "fp8_general_128x128x16"]
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    for name in names:
+        say(f"[fp8 adversarial] {name} M={M} N={N} K={K} seed=1150")
+        C, _, _ = run_gemm(A8, W8, C0, 1.0, 1.0, kernel=ids[name], op_b="T")
+        r = layout_check(C, A8, W8, C0, 1.0, 1.0, "N", "T", "fp8f32")
+        say(f"[fp8 adversarial] {name} worst err/allowance {r:.3e}")

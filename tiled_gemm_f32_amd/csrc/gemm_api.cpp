@@ -684,9 +684,11 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
         const KSplit tail = wave_tail(c, tile);
         need = tail.bytes > need ? tail.bytes : need;
     }
-    if (M > 16 || dtype == GEMM_DTYPE_FP8F32) return need;
+    if (M > 16) return need;
     const gemm::KernelDesc *skinny = dtype == GEMM_DTYPE_F32 ? gemm::kF32SplitKernels : gemm::kBf16SplitKernels;
-    const int count = dtype == GEMM_DTYPE_F32 ? gemm::kF32SplitKernelCount : gemm::kBf16SplitKernelCount;
+    const int count = dtype == GEMM_DTYPE_F32   ? gemm::kF32SplitKernelCount
+                      : dtype == GEMM_DTYPE_BF16F32 ? gemm::kBf16SplitKernelCount
+                                                  : 0;
     for (int i = 0; i < count; ++i) {
         const int64_t strips = ceil_div(N, skinny[i].tile_n);
         const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);
