@@ -165,6 +165,7 @@ bool kernel_runs(const KernelDesc *kd, const Call &c) {
 // 16-byte aligned); each slice's partial product goes to the caller's
 // workspace and a reduce kernel adds them in order.
 constexpr int kMaxKSplits = 16;
+static_assert(kMaxKSplits <= gemm::kMaxReduceSplits, "the reduce kernel adds at most kMaxReduceSplits slices");
 constexpr int64_t kMinSplitDepth = 1024;
 constexpr int64_t kSplitAlign = 64;
 

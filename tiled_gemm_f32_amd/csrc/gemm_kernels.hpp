@@ -35,6 +35,8 @@ struct GemmParams {
 };
 
 inline int k_splits(const GemmParams &p) { return p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1; }
+// Most K slices the reduce kernel adds (every split path stays within it).
+constexpr int kMaxReduceSplits = 16;
 
 typedef hipError_t (*LaunchFn)(const GemmParams &p, hipStream_t stream);
 
