@@ -74,6 +74,8 @@ def _load():
     lib.gemm_groupmax_fp8in.restype = None
     lib.epilogue_ref.argtypes = [i64, i64, vp, i64, vp, ctypes.c_int]
     lib.epilogue_ref.restype = None
+    lib.quantize_ref.argtypes = [i64, i64, vp, i64, ctypes.c_int, dbl]
+    lib.quantize_ref.restype = None
     lib.gemm_ref_num_threads.argtypes = []
     lib.gemm_ref_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -195,6 +197,21 @@ def gemm_epilogue_ref(A, B, alpha=1.0, beta=0.0, C0=None, bias=None, activation=
                       op_b="N") -> np.ndarray:
     """fp64 ``act(alpha * op(A) @ op(B) + beta * C0 + bias)``: gemm_ref, then epilogue_ref."""
     return epilogue_ref(gemm_ref(A, B, alpha, beta, C0, op_a, op_b), bias, activation)
+
+
+# The oracle's own names for the output formats (see quantize_ref in gemm_ref.c).
+OUTPUTS = {"bf16": 1, "fp8": 2}
+
+
+def quantize(Z, kind, scale=1.0) -> np.ndarray:
+    """fp64 values of ``Z * scale`` rounded to ``kind`` ("bf16", or "fp8" =
+    OCP E4M3 saturating at +-448), nearest with ties to even.  Returns a new
+    array of the same shape."""
+    out = np.array(Z, dtype=np.float64, order="C", copy=True)
+    flat = out.reshape(1, -1) if out.ndim != 2 else out
+    M, N = flat.shape
+    _load().quantize_ref(M, N, _ptr(flat), max(N, 1), OUTPUTS[kind], float(scale))
+    return out
 
 
 def num_threads() -> int:

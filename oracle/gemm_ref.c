@@ -332,6 +332,83 @@ void epilogue_ref(int64_t M, int64_t N, double *Z, int64_t ldz, const float *bia
     }
 }
 
+/*
+ * Output quantisation, the last fused epilogue step ("Tiled matrix
+ * multiplication", sections "Efficiency" and "Implementation notes": the
+ * result is converted while still in registers, before it is stored).  The
+ * pages name the step but fix no format or rounding; the readings taken:
+ * the value is multiplied by `scale`, then rounded to the nearest value of
+ * the storage format, ties to the even code (IEEE round-to-nearest-even).
+ *
+ *   kind 1: bfloat16, 8 significant bits over fp32's exponent range
+ *           (normal down to 2^-126, subnormal steps of 2^-133).  Past the
+ *           largest finite value the rounding reaches infinity, as IEEE
+ *           rounding does.
+ *   kind 2: OCP E4M3 (see widen_e4m3).  The format has no infinities:
+ *           magnitudes at or past the largest finite value, 448, give +-448
+ *           (saturation).
+ *
+ * NaN stays NaN; the sign of zero is kept.
+ */
+static double quant_bf16(double x)
+{
+    if (isnan(x) || isinf(x) || x == 0.0)
+        return x;
+    const double a = fabs(x);
+    int e;
+    frexp(a, &e);                          /* a = f * 2^e, 0.5 <= f < 1 */
+    int q = e - 8;                         /* spacing of 8-bit significands in this binade */
+    if (q < -133)
+        q = -133;                          /* subnormal spacing */
+    const double ulp = ldexp(1.0, q);
+    const double n = a / ulp;              /* exact: ulp is a power of two */
+    const double fl = floor(n), frac = n - fl;
+    double m = fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) == 1.0))
+        m = fl + 1.0;
+    double r = m * ulp;
+    const double max_finite = ldexp(255.0, 120);   /* (2 - 2^-7) * 2^127 */
+    if (r > max_finite)
+        r = INFINITY;
+    return copysign(r, x);
+}
+
+static double quant_e4m3(double x)
+{
+    if (isnan(x))
+        return x;
+    const double a = fabs(x);
+    double r;
+    if (a >= 448.0) {
+        r = 448.0;
+    } else {
+        /* Codes 0 .. 126 are the non-negative finite values in increasing
+         * order; find the two that bracket a. */
+        int c = 0;
+        while (c < 126 && widen_e4m3((uint8_t)(c + 1)) <= a)
+            ++c;
+        const double lo = widen_e4m3((uint8_t)c), hi = widen_e4m3((uint8_t)(c + 1));
+        if (a - lo < hi - a)
+            r = lo;
+        else if (a - lo > hi - a)
+            r = hi;
+        else
+            r = (c % 2 == 0) ? lo : hi;
+    }
+    return copysign(r, x);
+}
+
+/* Z[i][j] <- quantise(scale * Z[i][j]) for kind 1 (bf16) or 2 (E4M3). */
+void quantize_ref(int64_t M, int64_t N, double *Z, int64_t ldz, int kind, double scale)
+{
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            const double v = scale * Z[i * ldz + j];
+            Z[i * ldz + j] = kind == 1 ? quant_bf16(v) : quant_e4m3(v);
+        }
+    }
+}
+
 /* Threads OpenMP will use for the loops above (reported next to timings). */
 int gemm_ref_num_threads(void)
 {

@@ -608,3 +608,73 @@ def test_error_ratio_measure():
 
 def test_oracle_uses_threads():
     assert oracle.num_threads() >= 1
+
+
+# ----------------------------------------------------------------------------- output quantisation
+
+def _e4m3_values():
+    """The 127 non-negative finite E4M3 values in code order, decoded by the
+    format's definition (exponent bias 7, subnormals m * 2^-9)."""
+    vals = []
+    for c in range(127):
+        e, m = (c >> 3) & 15, c & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def test_quantize_e4m3_round_trips_every_finite_code():
+    v = _e4m3_values()
+    assert v[-1] == 448.0 and np.all(np.diff(v) > 0)
+    both = np.concatenate([v, -v])
+    np.testing.assert_array_equal(oracle.quantize(both, "fp8"), both)
+
+
+def test_quantize_e4m3_ties_go_to_the_even_code():
+    v = _e4m3_values()
+    mid = (v[:-1] + v[1:]) / 2          # exact in fp64
+    even = np.where(np.arange(126) % 2 == 0, v[:-1], v[1:])
+    np.testing.assert_array_equal(oracle.quantize(mid, "fp8"), even)
+    np.testing.assert_array_equal(oracle.quantize(-mid, "fp8"), -even)
+    gap = v[1:] - v[:-1]
+    np.testing.assert_array_equal(oracle.quantize(mid - gap / 8, "fp8"), v[:-1])
+    np.testing.assert_array_equal(oracle.quantize(mid + gap / 8, "fp8"), v[1:])
+
+
+def test_quantize_e4m3_saturates_and_keeps_nan_and_signed_zero():
+    x = np.array([448.0, 449.0, 463.99, 464.0, 1e30, np.inf, -500.0, -np.inf])
+    np.testing.assert_array_equal(oracle.quantize(x, "fp8"), [448, 448, 448, 448, 448, 448, -448, -448])
+    q = oracle.quantize(np.array([np.nan, -0.0, 0.0]), "fp8")
+    assert np.isnan(q[0]) and np.signbit(q[1]) and not np.signbit(q[2])
+
+
+def test_quantize_e4m3_matches_torch_in_range():
+    """torch's own E4M3 conversion (round to nearest even) on fp32 values
+    below 464, past which torch gives NaN where the oracle saturates."""
+    rng = np.random.default_rng(41)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1.0, 30.0, 150.0)]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(oracle.quantize(x.astype(np.float64), "fp8"), t)
+
+
+def test_quantize_bf16_matches_torch():
+    """torch's fp32 -> bfloat16 conversion (round to nearest even) on random
+    fp32 values, exact ties, subnormals and values near the top of the range."""
+    rng = np.random.default_rng(42)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-38, 1e-3, 1.0, 1e20, 1e37)]).astype(np.float32)
+    base = rng.standard_normal(5000).astype(np.float32)
+    base = torch.from_numpy(base).to(torch.bfloat16).float().numpy()
+    ties = (base.view(np.uint32) + np.uint32(0x8000)).view(np.float32)     # exactly half a bf16 step up
+    top = np.array([3.3895e38, 3.39e38, 3.3961e38, 3.4e38, np.finfo(np.float32).max], np.float32)
+    x = np.concatenate([x, ties, -ties, top, -top])
+    t = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(oracle.quantize(x.astype(np.float64), "bf16"), t)
+    q = oracle.quantize(np.array([np.nan, -0.0]), "bf16")
+    assert np.isnan(q[0]) and np.signbit(q[1])
+
+
+def test_quantize_applies_the_scale_first():
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal(1000) * 10
+    for kind in ("bf16", "fp8"):
+        np.testing.assert_array_equal(oracle.quantize(x, kind, scale=0.375), oracle.quantize(x * 0.375, kind))

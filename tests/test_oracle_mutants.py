@@ -64,6 +64,13 @@ MUTANTS = [
     ("fp8_B_row_stride_ignored", [("const uint8_t *brow = B + k * ldb;", "const uint8_t *brow = B + k * N;", 0)]),
     ("groupmax_run_of_7", [("if (k % 8 == 7 || k == K - 1)", "if (k % 7 == 6 || k == K - 1)", 0)]),
     ("groupmax_sum_not_max", [("if (p > run[j])\n                    run[j] = p;", "run[j] += p;", 0)]),
+    ("quant_e4m3_ties_up", [("r = (c % 2 == 0) ? lo : hi;", "r = hi;", 0)]),
+    ("quant_e4m3_no_saturation", [("if (a >= 448.0) {\n        r = 448.0;", "if (a >= 448.0) {\n        r = a;", 0)]),
+    ("quant_e4m3_truncates", [("if (a - lo < hi - a)\n            r = lo;", "if (1)\n            r = lo;", 0)]),
+    ("quant_bf16_ties_up", [("if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) == 1.0))", "if (frac >= 0.5)", 0)]),
+    ("quant_bf16_7_bits", [("int q = e - 8;", "int q = e - 7;", 0)]),
+    ("quant_bf16_no_subnormals", [("q = -133;", "q = -126;", 0)]),
+    ("quant_scale_dropped", [("const double v = scale * Z[i * ldz + j];", "const double v = Z[i * ldz + j];", 0)]),
 ]
 
 
