@@ -177,6 +177,7 @@ typedef struct gemm_kernel_info {
     int32_t vec_a, vec_b;   /* elements per global load of A and of B (1 = element loads) */
     const char *name;       /* static string */
     int32_t layouts;        /* bit 2*op_a + op_b set for every operand layout it runs */
+    int32_t outputs;        /* bit gemm_output set for every output type it writes */
 } gemm_kernel_info;
 
 typedef struct gemm_plan {
@@ -228,8 +229,25 @@ GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_
  * with C0 not read when beta == 0.  A NULL descriptor is the plain call.
  * Workspace arguments are those of gemm_f32_ws / gemm_bf16f32_ws (a K split
  * applies the epilogue once, in its reduce step).
- * Errors: GEMM_ERR_INVALID_ARG for an unknown activation or a misaligned
- * bias, besides those of the plain call.
+ *
+ * Output quantisation (the result converted in registers before it is
+ * stored).  out_type GEMM_OUT_F32 (0) writes C as above.  GEMM_OUT_BF16 and
+ * GEMM_OUT_FP8 write
+ *
+ *     out[i*ldo + j] = round(s * act(alpha * (A x B)[i][j] + beta * C0[i][j] + bias[j]))
+ *
+ * to `out` instead, with s = out_scale (0 is taken as 1), rounding to the
+ * nearest value with ties to even: bfloat16 bit patterns (uint16_t; past the
+ * largest finite value the rounding gives infinity) or OCP E4M3 bytes
+ * (uint8_t; magnitudes from 448 up saturate to +-448, the format having no
+ * infinities).  NaN stays NaN.  C is then not written; it is read as C0
+ * only when beta != 0 and may be NULL otherwise.  out must be aligned to its
+ * element size, ldo >= max(1, N).  A zero-filled descriptor (bias NULL,
+ * activation and out_type 0) is the plain call.
+ * Errors: GEMM_ERR_INVALID_ARG for an unknown activation or output type, a
+ * misaligned bias or output, a NULL output or ldo < N, besides those of the
+ * plain call.  GEMM_ERR_UNSUPPORTED when a forced kernel cannot write the
+ * output type (gemm_kernel_info.outputs).
  */
 typedef enum gemm_activation {
     GEMM_ACT_NONE = 0,
@@ -237,9 +255,19 @@ typedef enum gemm_activation {
     GEMM_ACT_GELU = 2
 } gemm_activation;
 
+typedef enum gemm_output {
+    GEMM_OUT_F32 = 0,        /* fp32, to C */
+    GEMM_OUT_BF16 = 1,       /* bfloat16 bit patterns, to out */
+    GEMM_OUT_FP8 = 2         /* OCP E4M3 bytes, saturating, to out */
+} gemm_output;
+
 typedef struct gemm_epilogue {
     const float *bias;       /* N floats or NULL */
     int32_t activation;      /* gemm_activation */
+    int32_t out_type;        /* gemm_output */
+    void *out;               /* GEMM_OUT_BF16 / GEMM_OUT_FP8: M x N output, row i at out + i*ldo */
+    int64_t ldo;             /* elements between rows of out */
+    float out_scale;         /* multiplies the result before rounding; 0 means 1 */
 } gemm_epilogue;
 
 GEMM_API gemm_status gemm_f32_epi(int64_t M, int64_t N, int64_t K, float alpha,
@@ -313,6 +341,15 @@ GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_
                                              float beta, const float *C, int64_t ldc,
                                              int32_t force_kernel, int64_t workspace_bytes,
                                              gemm_plan *out);
+
+/* gemm_plan_query_general with an epilogue (its output type narrows the
+ * kernels that can run): the plan gemm_general would take with it. */
+GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op_b,
+                                         int64_t M, int64_t N, int64_t K, float alpha,
+                                         const void *A, int64_t lda, const void *B, int64_t ldb,
+                                         float beta, const float *C, int64_t ldc,
+                                         int32_t force_kernel, const gemm_epilogue *epilogue,
+                                         int64_t workspace_bytes, gemm_plan *out);
 
 /*
  * Per-shape tuning ("A GEMM Kernel, Step by Step", section "Six parameters,

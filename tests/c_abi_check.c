@@ -36,6 +36,7 @@ int main(void)
         CHECK(gemm_kernel_query(id, &info) == GEMM_OK, "kernel query");
         CHECK(info.id == id && info.name != NULL && strlen(info.name) > 0, "kernel info");
         CHECK(info.layouts >= 1 && info.layouts <= 15, "kernel layouts");
+        CHECK((info.outputs & 1) && info.outputs <= 7, "kernel outputs (fp32 always)");
     }
     CHECK(gemm_kernel_query(0, &info) == GEMM_ERR_INVALID_ARG, "kernel id 0 rejected");
 
@@ -56,13 +57,33 @@ int main(void)
           GEMM_ERR_INVALID_ARG, "unknown dtype");
     {
         gemm_epilogue epi;
-        epi.bias = NULL;
+        memset(&epi, 0, sizeof epi);
         epi.activation = 7;
         CHECK(gemm_f32_epi(4, 4, 4, 1.0f, (const float *)A, 4, (const float *)B, 4, 0.0f, C, 4, &epi, NULL, 0,
                            NULL) == GEMM_ERR_INVALID_ARG, "unknown activation");
         epi.activation = GEMM_ACT_GELU;
         CHECK(gemm_bf16f32_epi(0, 4, 4, 1.0f, (const uint16_t *)A, 4, (const uint16_t *)B, 4, 0.0f, C, 4, &epi,
                                NULL, 0, NULL) == GEMM_OK, "empty call is a no-op");
+        /* Quantised output: the plan takes a kernel that writes it; a NULL
+         * output, an unknown type or ldo < N is rejected. */
+        epi.activation = GEMM_ACT_NONE;
+        epi.out_type = GEMM_OUT_BF16;
+        epi.out = (void *)(uintptr_t)0x7f3000000000ull;
+        epi.ldo = 4096;
+        CHECK(gemm_plan_query_epi(GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_N, 4096, 4096, 4096, 1.0f, A, 4096, B, 4096,
+                                  0.0f, NULL, 4096, 0, &epi, 0, &plan) == GEMM_OK, "bf16-output plan, C NULL");
+        CHECK(gemm_kernel_query(plan.kernel_id, &info) == GEMM_OK && (info.outputs & (1 << GEMM_OUT_BF16)),
+              "bf16-output kernel");
+        epi.ldo = 4095;
+        CHECK(gemm_plan_query_epi(GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_N, 4096, 4096, 4096, 1.0f, A, 4096, B, 4096,
+                                  0.0f, NULL, 4096, 0, &epi, 0, &plan) == GEMM_ERR_INVALID_ARG, "ldo < N");
+        epi.ldo = 4096;
+        epi.out = NULL;
+        CHECK(gemm_f32_epi(4, 4, 4, 1.0f, (const float *)A, 4, (const float *)B, 4, 0.0f, C, 4, &epi, NULL, 0,
+                           NULL) == GEMM_ERR_INVALID_ARG, "NULL output");
+        epi.out_type = 3;
+        CHECK(gemm_f32_epi(4, 4, 4, 1.0f, (const float *)A, 4, (const float *)B, 4, 0.0f, C, 4, &epi, NULL, 0,
+                           NULL) == GEMM_ERR_INVALID_ARG, "unknown output type");
     }
     CHECK(gemm_workspace_size(GEMM_DTYPE_BF16F32, 256, 512, 6000) > 0, "workspace size");
     CHECK(gemm_workspace_size(GEMM_DTYPE_F32, 4096, 4096, 4096) == 0, "no workspace for a full wave");

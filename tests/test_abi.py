@@ -606,3 +606,69 @@ def test_skinny_nt_forced_needs_its_layout():
         assert st == UNSUP, k["name"]
         st, _ = gplan(k["dtype"], N_, T_, 16, 8192, 8192, force=k["id"], ws=1 << 30)
         assert st == OK, k["name"]
+
+
+# ----------------------------------------------------------------------------- output quantisation
+
+def eplan(dtype, op_a, op_b, M, N, K, out_type, ws=0, force=0, C=PC, beta=0.0, ldo=None, out=0x7f3000000000):
+    lda = K if op_a == N_ else M
+    ldb = N if op_b == N_ else K
+    epi = (0, 0, out_type, out, N if ldo is None else ldo, 0.0)
+    return tg.gemm_plan_query_epi(dtype, op_a, op_b, M, N, K, 1.0, PA, lda, PB, ldb, beta, C, N, force, epi, ws)
+
+
+def test_output_types_of_the_kernels():
+    outs = {k["name"]: k["outputs"] for k in tg.kernels()}
+    assert all(v & 1 for v in outs.values())
+    for name in ("f32_mfma32_256x256x16_w2x2_a4b4_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
+                 "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
+                 "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
+                 "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
+                 "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_nt_n32_w8_u2",
+                 "fp8_skinny_nt_splitk_n32_w8_u2"):
+        assert outs[name] == 7, name
+    assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 1 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 1
+
+
+@pytest.mark.parametrize("out_type", [tg.GEMM_OUT_BF16, tg.GEMM_OUT_FP8])
+def test_output_quantisation_choice(out_type):
+    # The main shapes keep their kernels, and C may be NULL when beta == 0.
+    for dt, M, N, K, name in ((F32, 4096, 4096, 4096, "f32_mfma32_256x256x16_w2x2_a4b4_ring4"),
+                              (BF16, 8192, 8192, 8192, "bf16_mfma32_256x256x32_w2x2_a8b8_ring4")):
+        st, pl = eplan(dt, N_, N_, M, N, K, out_type, C=0)
+        assert st == OK and kname(pl) == name, pl
+    st, pl = eplan(FP8, N_, T_, 8192, 8192, 8192, out_type, C=0)
+    assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4"
+    st, pl = eplan(BF16, N_, T_, 16, 8192, 8192, out_type, C=0)
+    assert st == OK and kname(pl) == "bf16_skinny_nt_n32_w8_u2"
+    # Short K: the kernels preferred there write fp32 only, so the ring
+    # (whose K minimum yields) runs rather than the general fallback.
+    st, pl = eplan(BF16, N_, N_, 4352, 4096, 512, out_type, C=0)
+    assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_ring4", pl
+    assert kname(gplan(BF16, N_, N_, 4352, 4096, 512)[1]) == "bf16_mfma32_256x256x64_w2x2_a8b8_pipe"
+    # fp32 M <= 16 without a workspace: the one-pass skinny kernels write
+    # fp32 only, so the call takes a kernel that can convert.
+    st, pl = eplan(F32, N_, N_, 16, 8192, 8192, out_type)
+    assert st == OK and pl["path"] != tg.GEMM_PATH_SKINNY and (
+        tg.gemm_kernel_query(pl["kernel_id"])["outputs"] >> out_type) & 1, pl
+    st, pl = eplan(F32, N_, N_, 16, 8192, 8192, out_type, ws=tg.gemm_workspace_size(F32, 16, 8192, 8192))
+    assert st == OK and kname(pl) == "f32_skinny_splitk_n128_a4_w8_u1"
+    # A kernel that writes fp32 only cannot be forced.
+    only_f32 = [k["id"] for k in tg.kernels() if k["outputs"] == 1 and k["dtype"] == F32 and k["layouts"] & 1]
+    assert only_f32
+    for kid in only_f32:
+        assert eplan(F32, N_, N_, 16, 512, 512, out_type, force=kid)[0] == UNSUP
+        assert eplan(F32, N_, N_, 16, 512, 512, tg.GEMM_OUT_F32, force=kid)[0] == OK
+
+
+def test_output_quantisation_validation():
+    assert eplan(F32, N_, N_, 64, 64, 64, 3)[0] == INVALID
+    assert eplan(F32, N_, N_, 64, 64, 64, -1)[0] == INVALID
+    assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_BF16, ldo=63)[0] == INVALID
+    assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_BF16, out=0)[0] == INVALID
+    assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_BF16, out=0x7f3000000001)[0] == INVALID   # bf16 needs 2-byte
+    assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_FP8, out=0x7f3000000001)[0] == OK
+    # C is needed as C0 when beta != 0, and always for fp32 output.
+    assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_BF16, C=0, beta=0.5)[0] == INVALID
+    assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_F32, C=0)[0] == INVALID
+    assert eplan(F32, N_, N_, 0, 64, 64, tg.GEMM_OUT_BF16, out=0)[0] == OK       # empty: nothing is written

@@ -11,7 +11,8 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401  (re-exported C ABI)
     EXPORTED, GEMM_ACT_GELU, GEMM_ACT_NONE, GEMM_ACT_RELU, GEMM_DTYPE_BF16F32, GEMM_DTYPE_F32, GEMM_DTYPE_FP8F32,
-    GEMM_OP_N, GEMM_OP_T, Epilogue, gemm_bf16f32_epi, gemm_f32_epi, gemm_general, gemm_plan_query_general, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
+    GEMM_OP_N, GEMM_OP_T, GEMM_OUT_BF16, GEMM_OUT_F32, GEMM_OUT_FP8, Epilogue, gemm_bf16f32_epi, gemm_f32_epi,
+    gemm_general, gemm_plan_query_general, gemm_plan_query_epi, GEMM_ERR_DEVICE, GEMM_ERR_INVALID_ARG,
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
     gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
 
 __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
            "gemm_f32_epi", "gemm_bf16f32_epi", "Epilogue", "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU",
+           "GEMM_OUT_F32", "GEMM_OUT_BF16", "GEMM_OUT_FP8", "gemm_plan_query_epi",
            "gemm_general", "gemm_plan_query_general", "GEMM_DTYPE_FP8F32", "GEMM_OP_N", "GEMM_OP_T",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
            "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune", "gemm_tuning_count",
@@ -62,7 +64,7 @@ def _dtype_of(t):
 
 
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, stream=None, ws=None,
-         bias=None, activation=None, op_a: str = "N", op_b: str = "N"):
+         bias=None, activation=None, op_a: str = "N", op_b: str = "N", out=None, out_scale: float = 1.0):
     """C = act(alpha * (op(A) @ op(B)) + beta * C + bias) on the current stream; returns C.
 
     A and B are CUDA tensors of one dtype: float32 (fp32 path), bfloat16
@@ -76,7 +78,10 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     ``workspace()``) for the split-K paths.  ``bias`` is an optional float32
     device tensor of N elements added to every row; ``activation`` is None,
     "relu", "gelu" or a GEMM_ACT_* value.  Both are applied inside the
-    kernels' epilogue.
+    kernels' epilogue.  ``out`` (optional) is a bfloat16 or float8_e4m3fn
+    device tensor (M x N) that receives ``round(out_scale * result)`` instead
+    of C (nearest-even; fp8 saturates at +-448); C is then only read, as C0,
+    when beta != 0, and ``out`` is returned.
     """
     import torch
 
@@ -91,23 +96,37 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     K2, N = B.shape if op_b == "N" else (B.shape[1], B.shape[0])
     if K2 != K:
         raise ValueError(f"inner dimensions differ: op_a={op_a} {tuple(A.shape)}, op_b={op_b} {tuple(B.shape)}")
+    out_type = GEMM_OUT_F32
+    if out is not None:
+        kinds = {torch.bfloat16: GEMM_OUT_BF16, torch.float8_e4m3fn: GEMM_OUT_FP8}
+        if out.dtype not in kinds or tuple(out.shape) != (M, N) or not out.is_cuda:
+            raise ValueError(f"out must be a bfloat16 or float8_e4m3fn device tensor of shape {(M, N)}")
+        out_type = kinds[out.dtype]
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    if C.dtype != torch.float32 or tuple(C.shape) != (M, N) or not C.is_cuda:
+        if out is None:
+            C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if C is not None and (C.dtype != torch.float32 or tuple(C.shape) != (M, N) or not C.is_cuda):
         raise ValueError(f"C must be a float32 device tensor of shape {(M, N)}")
-    lda, ldb, ldc = _ld(A, "A"), _ld(B, "B"), _ld(C, "C")
+    lda, ldb = _ld(A, "A"), _ld(B, "B")
+    ldc = _ld(C, "C") if C is not None else max(N, 1)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     act = _ACTIVATIONS[activation] if activation is None or isinstance(activation, str) else int(activation)
     epi = None
-    if bias is not None or act != GEMM_ACT_NONE:
+    if bias is not None or act != GEMM_ACT_NONE or out is not None:
         if bias is not None and (bias.dtype != torch.float32 or not bias.is_cuda or bias.numel() != N
                                  or not bias.is_contiguous()):
             raise ValueError(f"bias must be a contiguous float32 device tensor of {N} elements")
-        epi = Epilogue(bias.data_ptr() if bias is not None else None, act)
-    args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc)
+        if out is not None:
+            out_ptr = out.view(torch.uint8).data_ptr() if out_type == GEMM_OUT_FP8 else out.data_ptr()
+            epi = Epilogue(bias.data_ptr() if bias is not None else None, act, out_type, out_ptr,
+                           _ld(out, "out"), float(out_scale))
+        else:
+            epi = Epilogue(bias.data_ptr() if bias is not None else None, act)
+    c_ptr = C.data_ptr() if C is not None else None
+    args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb, float(beta), c_ptr, ldc)
     ops = (GEMM_OP_N if op_a == "N" else GEMM_OP_T, GEMM_OP_N if op_b == "N" else GEMM_OP_T)
     with torch.cuda.device(A.device):
         wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
@@ -119,7 +138,7 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
             st = gemm_general(dt, ops[0], ops[1], *args, kernel, epi, wp, wb, stream)
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
-    return C
+    return out if out is not None else C
 
 
 def autotune(A, B, C, alpha: float = 1.0, beta: float = 0.0, ws=None, reps: int = 5, stream=None) -> dict:

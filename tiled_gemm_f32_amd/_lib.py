@@ -36,20 +36,24 @@ GEMM_OP_T = 1
 GEMM_ACT_NONE = 0
 GEMM_ACT_RELU = 1
 GEMM_ACT_GELU = 2
+# gemm_output
+GEMM_OUT_F32 = 0
+GEMM_OUT_BF16 = 1
+GEMM_OUT_FP8 = 2
 
 # Every entry point include/gemm.h declares.
 EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count",
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
             "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws", "gemm_autotune", "gemm_tuning_count",
             "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_f32_epi", "gemm_bf16f32_epi",
-            "gemm_general", "gemm_plan_query_general")
+            "gemm_general", "gemm_plan_query_general", "gemm_plan_query_epi")
 
 
 class KernelInfo(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int32), ("dtype", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32),
-                ("name", ctypes.c_char_p), ("layouts", ctypes.c_int32)]
+                ("name", ctypes.c_char_p), ("layouts", ctypes.c_int32), ("outputs", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -60,16 +64,20 @@ class Plan(ctypes.Structure):
 
 
 class Epilogue(ctypes.Structure):
-    """gemm_epilogue: bias (device pointer to N floats, or 0) and activation."""
-    _fields_ = [("bias", ctypes.c_void_p), ("activation", ctypes.c_int32)]
+    """gemm_epilogue: bias (device pointer to N floats, or 0), activation, and
+    the output (type, device pointer, leading dimension, scale; type 0 = C)."""
+    _fields_ = [("bias", ctypes.c_void_p), ("activation", ctypes.c_int32), ("out_type", ctypes.c_int32),
+                ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("out_scale", ctypes.c_float)]
 
 
 def _epi(epilogue):
-    """None, an Epilogue, or a (bias_ptr, activation) pair -> ctypes argument."""
+    """None, an Epilogue, or a (bias_ptr, activation[, out_type, out_ptr, ldo, out_scale]) tuple -> ctypes
+    argument."""
     if epilogue is None or isinstance(epilogue, Epilogue):
         return epilogue
-    bias, act = epilogue
-    return Epilogue(bias or None, act)
+    bias, act, *rest = epilogue
+    out_type, out, ldo, scale = (list(rest) + [0, None, 0, 0.0][len(rest):])[:4]
+    return Epilogue(bias or None, act, out_type, out or None, ldo, scale)
 
 
 class GemmError(RuntimeError):
@@ -103,6 +111,9 @@ def load() -> ctypes.CDLL:
     lib.gemm_plan_query_general.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32,
                                             i64, ctypes.POINTER(Plan)]
     lib.gemm_plan_query_general.restype = ctypes.c_int
+    lib.gemm_plan_query_epi.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32, epi,
+                                        i64, ctypes.POINTER(Plan)]
+    lib.gemm_plan_query_epi.restype = ctypes.c_int
     lib.gemm_bf16f32_epi.argtypes = gemm_sig + [epi, vp, i64, vp]
     lib.gemm_f32_ws.argtypes = gemm_sig + [vp, i64, vp]
     lib.gemm_bf16f32_ws.argtypes = gemm_sig + [vp, i64, vp]
@@ -192,6 +203,15 @@ def gemm_plan_query_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, b
     pl = Plan()
     st = load().gemm_plan_query_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                         force_kernel, workspace_bytes, ctypes.byref(pl))
+    return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
+
+
+def gemm_plan_query_epi(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0,
+                        epilogue=None, workspace_bytes=0):
+    """(status, plan dict) for the choice gemm_general would make with this epilogue."""
+    pl = Plan()
+    st = load().gemm_plan_query_epi(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel,
+                                    _epi(epilogue), workspace_bytes, ctypes.byref(pl))
     return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
 
 

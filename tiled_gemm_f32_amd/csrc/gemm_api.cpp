@@ -80,6 +80,10 @@ struct Call {
     int64_t ws_bytes;
     const float *bias;     // fused epilogue (null: none)
     int32_t act;           // gemm_activation
+    int32_t out_type;      // gemm_output
+    void *out;             // bf16 / fp8 output (out_type != GEMM_OUT_F32)
+    int64_t ldo;
+    float out_scale;
 };
 
 int elem_size(int32_t dtype) { return dtype == GEMM_DTYPE_F32 ? 4 : dtype == GEMM_DTYPE_BF16F32 ? 2 : 1; }
@@ -101,9 +105,18 @@ gemm_status validate(const Call &c) {
     if (c.ws_bytes < 0 || (c.ws != nullptr && !aligned(c.ws, 4))) return GEMM_ERR_INVALID_ARG;
     if (c.act < GEMM_ACT_NONE || c.act > GEMM_ACT_GELU) return GEMM_ERR_INVALID_ARG;
     if (c.bias != nullptr && !aligned(c.bias, 4)) return GEMM_ERR_INVALID_ARG;
+    if (c.out_type < GEMM_OUT_F32 || c.out_type > GEMM_OUT_FP8) return GEMM_ERR_INVALID_ARG;
+    if (c.out_type != GEMM_OUT_F32) {
+        const int64_t min_ldo = c.N > 1 ? c.N : 1;
+        if (c.ldo < min_ldo || !aligned(c.out, c.out_type == GEMM_OUT_BF16 ? 2 : 1)) return GEMM_ERR_INVALID_ARG;
+        if (c.out == nullptr && c.M > 0 && c.N > 0) return GEMM_ERR_INVALID_ARG;
+        if (c.ldo > kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    }
+    if (c.C != nullptr && !aligned(c.C, 4)) return GEMM_ERR_INVALID_ARG;
     const uintptr_t esz = (uintptr_t)elem_size(c.dtype);
     if (c.M > 0 && c.N > 0) {
-        if (c.C == nullptr || !aligned(c.C, 4)) return GEMM_ERR_INVALID_ARG;
+        // C is written for fp32 output and read as C0 when beta != 0.
+        if (c.C == nullptr && (c.out_type == GEMM_OUT_F32 || c.beta != 0.0f)) return GEMM_ERR_INVALID_ARG;
         if (c.K > 0 && c.alpha != 0.0f) {
             if (c.A == nullptr || c.B == nullptr || !aligned(c.A, esz) || !aligned(c.B, esz))
                 return GEMM_ERR_INVALID_ARG;
@@ -147,6 +160,7 @@ int64_t split_workspace_bytes(const Call &c, const KernelDesc *kd) {
 
 bool kernel_runs(const KernelDesc *kd, const Call &c) {
     if (kd->dtype != c.dtype) return false;
+    if (((kd->outputs >> c.out_type) & 1) == 0) return false;
     if (((kd->layouts >> (2 * c.op_a + c.op_b)) & 1) == 0) return false;
     if ((kd->path == GEMM_PATH_SKINNY || kd->path == GEMM_PATH_SKINNY_SPLITK) && !skinny_fits(c)) return false;
     if (kd->path == GEMM_PATH_SKINNY_SPLITK) {
@@ -242,6 +256,7 @@ const KernelDesc *first_match(const KernelDesc *table, int count, const Call &c,
 struct Candidates {
     const KernelDesc *k[64];
     int n = 0;
+    bool use_min_k = true;     // honour each kernel's K minimum
 };
 Candidates tiled_candidates(const Call &c, bool fallback) {
     Candidates r;
@@ -255,7 +270,8 @@ Candidates tiled_candidates(const Call &c, bool fallback) {
 }
 const KernelDesc *first_candidate(const Candidates &cand, const Call &c, int tile_m) {
     for (int i = 0; i < cand.n; ++i)
-        if ((tile_m == 0 || cand.k[i]->tile_m == tile_m) && c.K >= cand.k[i]->min_k && kernel_runs(cand.k[i], c))
+        if ((tile_m == 0 || cand.k[i]->tile_m == tile_m) && (!cand.use_min_k || c.K >= cand.k[i]->min_k) &&
+            kernel_runs(cand.k[i], c))
             return cand.k[i];
     return nullptr;
 }
@@ -300,7 +316,13 @@ const KernelDesc *choose(const Call &c) {
             if (kd->path == GEMM_PATH_SKINNY && kernel_runs(kd, c)) return kd;
         }
     }
-    if (const KernelDesc *kd = choose_tiled(c, tiled_candidates(c, false))) return kd;
+    Candidates regular = tiled_candidates(c, false);
+    if (const KernelDesc *kd = choose_tiled(c, regular)) return kd;
+    // A K minimum prefers another regular kernel for short K; where none of
+    // those runs the call (say, an output type they cannot write), the
+    // kernel is still better than a fallback.
+    regular.use_min_k = false;
+    if (const KernelDesc *kd = choose_tiled(c, regular)) return kd;
     return choose_tiled(c, tiled_candidates(c, true));
 }
 
@@ -463,51 +485,55 @@ gemm_status run(const Call &c, int32_t force, gemm_stream_t stream) {
 }
 
 gemm_status launch(const Call &c, const gemm_plan &pl, const KernelDesc *kd, const KSplit &ks, hipStream_t s) {
+    gemm::GemmParams p;
+    p.A = c.A;
+    p.B = c.B;
+    p.C = c.C;
+    p.M = (int32_t)c.M;
+    p.N = (int32_t)c.N;
+    p.K = (int32_t)c.K;
+    p.lda = (int32_t)c.lda;
+    p.ldb = (int32_t)c.ldb;
+    p.ldc = c.ldc;
+    p.alpha = c.alpha;
+    p.beta = c.beta;
+    p.op_a = c.op_a;
+    p.op_b = c.op_b;
+    p.kchunk = 0;
+    p.partials = nullptr;
+    p.bias = c.bias;
+    p.act = c.act;
+    p.out_type = c.out_type;
+    p.out_scale = c.out_scale;
+    p.out = c.out_type == GEMM_OUT_F32 ? static_cast<void *>(c.C) : c.out;
+    p.ldo = c.out_type == GEMM_OUT_F32 ? c.ldc : c.ldo;
     hipError_t err;
     if (pl.path == GEMM_PATH_SCALE) {
-        err = gemm::launch_scale_c(c.beta, c.C, (int32_t)c.M, (int32_t)c.N, c.ldc, c.bias, c.act, s);
+        err = gemm::launch_scale_c(p, s);
+    } else if (ks.splits > 1 && ks.m_top > 0) {
+        // Whole waves of the top rows, then the K-split bottom rows (A's
+        // rows are its columns when it is stored transposed).
+        gemm::GemmParams top = p;
+        top.M = (int32_t)ks.m_top;
+        err = kd->launch(top, s);
+        const int64_t esz = elem_size(c.dtype);
+        const int64_t a_off = (c.op_a == GEMM_OP_N ? ks.m_top * c.lda : ks.m_top) * esz;
+        const int64_t out_esz = c.out_type == GEMM_OUT_F32 ? 4 : c.out_type == GEMM_OUT_BF16 ? 2 : 1;
+        p.A = static_cast<const char *>(c.A) + a_off;
+        if (c.C != nullptr) p.C = c.C + ks.m_top * c.ldc;
+        p.out = static_cast<char *>(p.out) + ks.m_top * p.ldo * out_esz;
+        p.M = (int32_t)(c.M - ks.m_top);
+        p.kchunk = ks.kchunk;
+        p.partials = static_cast<float *>(c.ws);
+        if (err == hipSuccess) err = kd->launch(p, s);
+        if (err == hipSuccess) err = gemm::launch_splitk_reduce(p, s);
+    } else if (ks.splits > 1) {
+        p.kchunk = ks.kchunk;
+        p.partials = static_cast<float *>(c.ws);
+        err = kd->launch(p, s);
+        if (err == hipSuccess) err = gemm::launch_splitk_reduce(p, s);
     } else {
-        gemm::GemmParams p;
-        p.A = c.A;
-        p.B = c.B;
-        p.C = c.C;
-        p.M = (int32_t)c.M;
-        p.N = (int32_t)c.N;
-        p.K = (int32_t)c.K;
-        p.lda = (int32_t)c.lda;
-        p.ldb = (int32_t)c.ldb;
-        p.ldc = c.ldc;
-        p.alpha = c.alpha;
-        p.beta = c.beta;
-        p.op_a = c.op_a;
-        p.op_b = c.op_b;
-        p.kchunk = 0;
-        p.partials = nullptr;
-        p.bias = c.bias;
-        p.act = c.act;
-        if (ks.splits > 1 && ks.m_top > 0) {
-            // Whole waves of the top rows, then the K-split bottom rows (A's
-            // rows are its columns when it is stored transposed).
-            gemm::GemmParams top = p;
-            top.M = (int32_t)ks.m_top;
-            err = kd->launch(top, s);
-            const int64_t esz = elem_size(c.dtype);
-            const int64_t a_off = (c.op_a == GEMM_OP_N ? ks.m_top * c.lda : ks.m_top) * esz;
-            p.A = static_cast<const char *>(c.A) + a_off;
-            p.C = c.C + ks.m_top * c.ldc;
-            p.M = (int32_t)(c.M - ks.m_top);
-            p.kchunk = ks.kchunk;
-            p.partials = static_cast<float *>(c.ws);
-            if (err == hipSuccess) err = kd->launch(p, s);
-            if (err == hipSuccess) err = gemm::launch_splitk_reduce(p, s);
-        } else if (ks.splits > 1) {
-            p.kchunk = ks.kchunk;
-            p.partials = static_cast<float *>(c.ws);
-            err = kd->launch(p, s);
-            if (err == hipSuccess) err = gemm::launch_splitk_reduce(p, s);
-        } else {
-            err = kd->launch_ws ? kd->launch_ws(p, c.ws, s) : kd->launch(p, s);
-        }
+        err = kd->launch_ws ? kd->launch_ws(p, c.ws, s) : kd->launch(p, s);
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -579,6 +605,10 @@ Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, cons
     c.ws_bytes = ws ? ws_bytes : 0;
     c.bias = nullptr;
     c.act = GEMM_ACT_NONE;
+    c.out_type = GEMM_OUT_F32;
+    c.out = nullptr;
+    c.ldo = 0;
+    c.out_scale = 1.0f;
     c.dtype = dtype;
     c.op_a = GEMM_OP_N;
     c.op_b = GEMM_OP_N;
@@ -632,11 +662,18 @@ GEMM_API gemm_status gemm_bf16f32_ws(int64_t M, int64_t N, int64_t K, float alph
 namespace {
 
 // Calls with a fused epilogue; a NULL descriptor is the plain call.
+void apply_epilogue(Call &c, const gemm_epilogue *epi) {
+    if (epi == nullptr) return;
+    c.bias = epi->bias;
+    c.act = epi->activation;
+    c.out_type = epi->out_type;
+    c.out = epi->out;
+    c.ldo = epi->ldo;
+    c.out_scale = epi->out_scale == 0.0f ? 1.0f : epi->out_scale;
+}
+
 gemm_status run_epi(Call c, const gemm_epilogue *epi, int32_t force, gemm_stream_t stream) {
-    if (epi != nullptr) {
-        c.bias = epi->bias;
-        c.act = epi->activation;
-    }
+    apply_epilogue(c, epi);
     return run(c, force, stream);
 }
 
@@ -734,6 +771,21 @@ GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_
     Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
     c.op_a = op_a;
     c.op_b = op_b;
+    KSplit ks;
+    return plan(c, force_kernel, out, &kd, &ks);
+}
+
+GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                         int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                         int64_t ldb, float beta, const float *C, int64_t ldc, int32_t force_kernel,
+                                         const gemm_epilogue *epilogue, int64_t workspace_bytes, gemm_plan *out) {
+    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+    const KernelDesc *kd = nullptr;
+    void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
+    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
+    c.op_a = op_a;
+    c.op_b = op_b;
+    apply_epilogue(c, epilogue);
     KSplit ks;
     return plan(c, force_kernel, out, &kd, &ks);
 }
@@ -839,6 +891,7 @@ GEMM_API gemm_status gemm_kernel_query(int32_t id, gemm_kernel_info *out) {
     out->vec_a = kd->vec_a;
     out->vec_b = kd->vec_b;
     out->name = kd->name;
+    out->outputs = kd->outputs;
     out->layouts = kd->layouts;
     return GEMM_OK;
 }

@@ -172,10 +172,9 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
             for (int w = 0; w < WAVES; ++w) sum += red[w][i][j];
             const int col = n0 + j;
             if (i < M && col < N) {
-                float *cp = p.C + (int64_t)i * p.ldc + col;
                 float v = alpha * sum;
-                if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                *cp = epilogue_value(v, col, p.bias, p.act);
+                if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)i * p.ldc + col], v);
+                store_out_any(p, i, col, epilogue_value(v, col, p.bias, p.act));
             }
         }
         return;
@@ -220,7 +219,7 @@ template __global__ void bf16_skinny_kernel<4, 4>(GemmParams, float *, int, int)
 // aligned); other operands take the tiled kernels.
 const KernelDesc kBf16SplitKernels[] = {
     {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY_SPLITK, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_w4_s4",
-     nullptr, 0, &launch_bf16_skinny<4, 4>},
+     nullptr, 0, &launch_bf16_skinny<4, 4>, kLayoutNN, false, kOutAll},
 };
 const int kBf16SplitKernelCount = sizeof(kBf16SplitKernels) / sizeof(kBf16SplitKernels[0]);
 #endif

@@ -496,7 +496,7 @@ __device__ __forceinline__ int ring_swz_a(int row) { return (row >> 2) & 3; }
 // untransposed B, so its slices take the B layout, loads and transposing
 // reads above.  The reads deliver each lane's k values in the same order as
 // the 16-byte reads do, so either form of A pairs with either form of B.
-template <int NS, int GROUP_M, bool BT, bool AT>
+template <int NS, int GROUP_M, bool BT, bool AT, int OUT>
 __global__ void __launch_bounds__(256)
 bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint16_t>(p);
@@ -704,60 +704,47 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
     with_activation(p.act, [&](auto act) {
         using Act = decltype(act);
+        const bool vec_o = out_vec4<OUT>(p);
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) {
+            for (int fn = 0; fn < 4; ++fn) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
-                if (col >= N) continue;
-                const bool whole = vec_c && (!BT || col + 4 <= N);
-                float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
+                    if (col >= N) continue;
+                    // With B untransposed N is a multiple of 8, so a run of 4
+                    // columns is never cut by N.
+                    const bool whole = !BT || col + 4 <= N;
+                    float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    b[t] = (p.bias != nullptr && (!BT || col + t < N)) ? p.bias[col + t] : -0.0f;
+                    for (int t = 0; t < 4; ++t)
+                        b[t] = (p.bias != nullptr && (!BT || col + t < N)) ? p.bias[col + t] : -0.0f;
 #pragma unroll
-                for (int fm = 0; fm < 4; ++fm) {
-                    const int row = m0 + wm * 128 + 32 * fm + l32;
-                    if (row >= M) continue;
-                    float *cp = p.C + (int64_t)row * p.ldc + col;
-                    f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
-                               alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
-                    if (!BT) {
+                    for (int fm = 0; fm < 4; ++fm) {
+                        const int row = m0 + wm * 128 + 32 * fm + l32;
+                        if (row >= M) continue;
+                        const float *cp = p.C + (int64_t)row * p.ldc + col;
+                        f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
+                                   alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
                         if (beta != 0.0f) {
-                            const f32x4 c0 =
-                                vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
+                            f32x4 c0;
+                            if (whole && vec_c) {
+                                c0 = *reinterpret_cast<const f32x4 *>(cp);
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) c0[t] = col + t < N ? cp[t] : 0.0f;
+                            }
 #pragma unroll
                             for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
                         }
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
-                        if (vec_c) {
-                            *reinterpret_cast<f32x4 *>(cp) = v;
-                        } else {
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) cp[t] = v[t];
-                        }
-                    } else if (whole) {
-                        if (beta != 0.0f) {
-                            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cp);
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
-                        }
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
-                        *reinterpret_cast<f32x4 *>(cp) = v;
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            if (col + t >= N) continue;
-                            float x = v[t];
-                            if (beta != 0.0f) x = fmaf(beta, cp[t], x);
-                            cp[t] = Act::apply(x + b[t]);
-                        }
+                        if (whole)
+                            store_out4<OUT>(p, row, col, v, vec_o);
+                        else
+                            store_out_first<OUT>(p, row, col, v, N - col);
                     }
                 }
             }
-        }
     });
 }
 
@@ -766,8 +753,13 @@ hipError_t launch_bf16_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT, AT>),
-                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
+    const int out = launch_out_type(p);
+    const void *fn =
+        out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT, AT, GEMM_OUT_BF16>)
+        : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT, AT, GEMM_OUT_FP8>)
+                              : reinterpret_cast<const void *>(&bf16_ring_kernel<NS, GROUP_M, BT, AT, GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
@@ -787,11 +779,21 @@ hipError_t launch_bf16_tiled(const GemmParams &p, hipStream_t stream) {
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
 template __global__ void bf16_pipe_kernel<4>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4, false, false>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<5, 4, false, false>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4, true, false>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4, false, true>(GemmParams, int, int);
-template __global__ void bf16_ring_kernel<4, 4, true, true>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, false, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, false, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, false, GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<5, 4, false, false, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<5, 4, false, false, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<5, 4, false, false, GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, false, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, false, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, false, GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, true, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, true, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, false, true, GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, true, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, true, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_ring_kernel<4, 4, true, true, GEMM_OUT_FP8>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 8, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 1, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 1, 8, 4>(GemmParams, int, int);
@@ -807,19 +809,19 @@ template __global__ void bf16_tiled_kernel<128, 128, 64, 2, 2, 1, 1, 8>(GemmPara
 #if !defined(__HIP_DEVICE_COMPILE__)
 const KernelDesc kBf16TiledKernels[] = {
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
-     &launch_bf16_ring<4, 4>, 1024},
+     &launch_bf16_ring<4, 4>, 1024, nullptr, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_ring5",
-     &launch_bf16_ring<5, 4>, 1024},
+     &launch_bf16_ring<5, 4>, 1024, nullptr, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_pipe",
      &launch_bf16_pipe<4>},
     // Transposed layouts: the only fast kernels for them, so no K minimum.
     // vec_a / vec_b = 8: the stored rows of A and B are 16-byte multiples.
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4",
-     &launch_bf16_ring<4, 4, true, false>, 0, nullptr, kLayoutNT},
+     &launch_bf16_ring<4, 4, true, false>, 0, nullptr, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
-     &launch_bf16_ring<4, 4, false, true>, 0, nullptr, kLayoutTN},
+     &launch_bf16_ring<4, 4, false, true>, 0, nullptr, kLayoutTN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4",
-     &launch_bf16_ring<4, 4, true, true>, 0, nullptr, kLayoutTT},
+     &launch_bf16_ring<4, 4, true, true>, 0, nullptr, kLayoutTT, false, kOutAll},
     BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
     BF16_TILED(256, 256, 64, 2, 2, 8, 1, 4),
     BF16_TILED(256, 256, 64, 2, 2, 1, 8, 4),

@@ -148,6 +148,9 @@ __device__ __forceinline__ void apply_k_split(GemmParams &p) {
     p.beta = 0.0f;
     p.bias = nullptr;          // the reduce applies the epilogue once
     p.act = 0;
+    p.out_type = GEMM_OUT_F32;     // partials are fp32, into the workspace
+    p.out = p.C;
+    p.ldo = p.ldc;
 }
 
 // erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
@@ -196,6 +199,109 @@ __device__ __forceinline__ float epilogue_value(float v, int64_t col, const floa
     if (act == GEMM_ACT_RELU) v = ActRelu::apply(v);
     else if (act == GEMM_ACT_GELU) v = ActGelu::apply(v);
     return v;
+}
+
+// ---- Output quantisation (GemmParams::out_type).
+//
+// bfloat16: the upper half of the fp32 pattern after rounding to nearest,
+// ties to even (add 0x7fff plus the lowest kept bit; a carry into the
+// exponent is the correct next binade, and past the largest finite value it
+// gives infinity).  A NaN keeps its sign and upper payload with the quiet
+// bit set.  Written as a select, not a branch: the tile epilogues convert
+// hundreds of values in one unrolled pass.
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x40u;
+    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);
+}
+// OCP E4M3: saturate to +-448 first (both comparisons are false for NaN,
+// which passes through to the NaN code), then the hardware conversion,
+// which rounds to nearest, ties to even.
+__device__ __forceinline__ uint8_t to_e4m3(float x) {
+    x = x > 448.0f ? 448.0f : (x < -448.0f ? -448.0f : x);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xff);
+}
+
+template <int OUT> struct OutType { static constexpr int value = OUT; };
+// Calls f with the output type as a compile-time constant, so an epilogue
+// branches once per tile rather than once per element.
+template <class F> __device__ __forceinline__ void with_output(int out, F &&f) {
+    if (out == GEMM_OUT_BF16) f(OutType<GEMM_OUT_BF16>{});
+    else if (out == GEMM_OUT_FP8) f(OutType<GEMM_OUT_FP8>{});
+    else f(OutType<GEMM_OUT_F32>{});
+}
+
+// One finished value at (row, col) of the output.
+template <int OUT>
+__device__ __forceinline__ void store_out(const GemmParams &p, int64_t row, int64_t col, float v) {
+    if constexpr (OUT == GEMM_OUT_F32)
+        p.C[row * p.ldc + col] = v;
+    else if constexpr (OUT == GEMM_OUT_BF16)
+        static_cast<uint16_t *>(p.out)[row * p.ldo + col] = to_bf16(v * p.out_scale);
+    else
+        static_cast<uint8_t *>(p.out)[row * p.ldo + col] = to_e4m3(v * p.out_scale);
+}
+// The same with the type read at run time (per-element epilogues).
+__device__ __forceinline__ void store_out_any(const GemmParams &p, int64_t row, int64_t col, float v) {
+    if (p.out_type == GEMM_OUT_BF16) store_out<GEMM_OUT_BF16>(p, row, col, v);
+    else if (p.out_type == GEMM_OUT_FP8) store_out<GEMM_OUT_FP8>(p, row, col, v);
+    else store_out<GEMM_OUT_F32>(p, row, col, v);
+}
+
+// Whether four output values of a row starting at a column that is a
+// multiple of 4 form one aligned vector (16, 8 or 4 bytes).
+template <int OUT> __device__ __forceinline__ bool out_vec4(const GemmParams &p) {
+    if constexpr (OUT == GEMM_OUT_F32)
+        return (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
+    else
+        return (reinterpret_cast<uintptr_t>(p.out) & (OUT == GEMM_OUT_BF16 ? 7 : 3)) == 0 && p.ldo % 4 == 0;
+}
+
+// The first n (1..3) of four values of a run cut by the edge of C.
+template <int OUT>
+__device__ __forceinline__ void store_out_first(const GemmParams &p, int64_t row, int64_t col, f32x4 v, int n) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+        if (t < n) store_out<OUT>(p, row, col + t, v[t]);
+}
+
+// Four finished values of row `row`, columns col .. col+3; `vec` as out_vec4.
+template <int OUT>
+__device__ __forceinline__ void store_out4(const GemmParams &p, int64_t row, int64_t col, f32x4 v, bool vec) {
+    if constexpr (OUT == GEMM_OUT_F32) {
+        float *cp = p.C + row * p.ldc + col;
+        if (vec) {
+            *reinterpret_cast<f32x4 *>(cp) = v;
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) cp[t] = v[t];
+        }
+    } else if constexpr (OUT == GEMM_OUT_BF16) {
+        const uint32_t h0 = to_bf16(v[0] * p.out_scale), h1 = to_bf16(v[1] * p.out_scale);
+        const uint32_t h2 = to_bf16(v[2] * p.out_scale), h3 = to_bf16(v[3] * p.out_scale);
+        uint16_t *op = static_cast<uint16_t *>(p.out) + row * p.ldo + col;
+        if (vec) {
+            *reinterpret_cast<u32x2 *>(op) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
+        } else {
+            op[0] = (uint16_t)h0;
+            op[1] = (uint16_t)h1;
+            op[2] = (uint16_t)h2;
+            op[3] = (uint16_t)h3;
+        }
+    } else {
+        const uint32_t b0 = to_e4m3(v[0] * p.out_scale), b1 = to_e4m3(v[1] * p.out_scale);
+        const uint32_t b2 = to_e4m3(v[2] * p.out_scale), b3 = to_e4m3(v[3] * p.out_scale);
+        uint8_t *op = static_cast<uint8_t *>(p.out) + row * p.ldo + col;
+        if (vec) {
+            *reinterpret_cast<uint32_t *>(op) = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        } else {
+            op[0] = (uint8_t)b0;
+            op[1] = (uint8_t)b1;
+            op[2] = (uint8_t)b2;
+            op[3] = (uint8_t)b3;
+        }
+    }
 }
 
 }  // namespace gemm

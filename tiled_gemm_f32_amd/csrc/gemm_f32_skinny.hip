@@ -254,10 +254,9 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
             for (int w = 0; w < WAVES; ++w) s += red[w][i][j];
             const int col = n0 + j;
             if (i < M && col < N) {
-                float *cp = p.C + (int64_t)i * p.ldc + col;
                 float v = alpha * s;
-                if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                *cp = epilogue_value(v, col, p.bias, p.act);
+                if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)i * p.ldc + col], v);
+                store_out_any(p, i, col, epilogue_value(v, col, p.bias, p.act));
             }
         }
         return;
@@ -296,10 +295,9 @@ splitk_reduce_kernel(GemmParams p, const float *partials, int splits) {
     for (int t = 1; t < kMaxReduceSplits; ++t)
         if (t < splits) s += part[t];
     const int64_t i = idx / p.N, j = idx - i * p.N;
-    float *cp = p.C + i * p.ldc + j;
     float v = p.alpha * s;
-    if (p.beta != 0.0f) v = fmaf(p.beta, *cp, v);
-    *cp = epilogue_value(v, j, p.bias, p.act);
+    if (p.beta != 0.0f) v = fmaf(p.beta, p.C[i * p.ldc + j], v);
+    store_out_any(p, i, j, epilogue_value(v, j, p.bias, p.act));
 }
 
 hipError_t launch_reduce(const GemmParams &p, const float *partials, int splits, hipStream_t stream) {
@@ -336,13 +334,13 @@ hipError_t launch_f32_skinny_splitk(const GemmParams &p, void *workspace, hipStr
 }
 
 __global__ void __launch_bounds__(256)
-scale_c_kernel(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act) {
-    const int64_t total = (int64_t)M * N;
+scale_c_kernel(GemmParams p) {
+    const int64_t total = (int64_t)p.M * p.N;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
-        const int64_t i = idx / N, j = idx - i * N;
-        float *cp = C + i * ldc + j;
-        *cp = epilogue_value((beta == 0.0f) ? 0.0f : beta * *cp, j, bias, act);
+        const int64_t i = idx / p.N, j = idx - i * p.N;
+        const float v = p.beta == 0.0f ? 0.0f : p.beta * p.C[i * p.ldc + j];
+        store_out_any(p, i, j, epilogue_value(v, j, p.bias, p.act));
     }
 }
 
@@ -377,9 +375,9 @@ const int kF32SkinnyKernelCount = sizeof(kF32SkinnyKernels) / sizeof(kF32SkinnyK
 // width; tile_k the K depth one batch of all waves covers.
 const KernelDesc kF32SplitKernels[] = {
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 1, 512, 4, 4, "f32_skinny_splitk_n128_a4_w8_u1",
-     nullptr, 0, &launch_f32_skinny_splitk<2, 4, 8, 1>},
+     nullptr, 0, &launch_f32_skinny_splitk<2, 4, 8, 1>, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 1, 512, 1, 4, "f32_skinny_splitk_n128_a1_w8_u1",
-     nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 1>},
+     nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 1>, kLayoutNN, false, kOutAll},
 };
 const int kF32SplitKernelCount = sizeof(kF32SplitKernels) / sizeof(kF32SplitKernels[0]);
 
@@ -387,12 +385,12 @@ hipError_t launch_splitk_reduce(const GemmParams &p, hipStream_t stream) {
     return launch_reduce(p, p.partials, k_splits(p), stream);
 }
 
-hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act,
-                          hipStream_t stream) {
-    const int64_t total = (int64_t)M * N;
+hipError_t launch_scale_c(const GemmParams &p, hipStream_t stream) {
+    const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
-    void *argv[] = {&beta, &C, &M, &N, &ldc, (void *)&bias, &act};
+    GemmParams args = p;
+    void *argv[] = {&args};
     return hipLaunchKernel(reinterpret_cast<const void *>(&scale_c_kernel), dim3((unsigned)blocks),
                            dim3(256), argv, 0, stream);
 }

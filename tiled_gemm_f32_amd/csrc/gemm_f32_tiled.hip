@@ -234,7 +234,7 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
 //     instructions are pinned between MFMAs with sched_barrier.
 // Loads complete in issue order: before the barrier of slice kt the only
 // loads allowed in flight are the 8*(NS-2) of the slices after kt+1.
-template <int NS, int GROUP_M>
+template <int NS, int GROUP_M, int OUT>
 __global__ void __launch_bounds__(256)
 f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<float>(p);
@@ -386,29 +386,27 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     for (int e = 0; e < 4; ++e) b[e] = p.bias != nullptr ? p.bias[col + e] : -0.0f;
     with_activation(p.act, [&](auto act) {
         using Act = decltype(act);
+        const bool vec_o = out_vec4<OUT>(p);
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
+            for (int fm = 0; fm < 4; ++fm) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 128 + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row >= M) continue;
-                float *cp = p.C + (int64_t)row * p.ldc + col;
-                f32x4 v = {alpha * acc[fm][0][r], alpha * acc[fm][1][r], alpha * acc[fm][2][r], alpha * acc[fm][3][r]};
-                if (beta != 0.0f) {
-                    const f32x4 c0 = vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 128 + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (row >= M) continue;
+                    f32x4 v = {alpha * acc[fm][0][r], alpha * acc[fm][1][r], alpha * acc[fm][2][r],
+                               alpha * acc[fm][3][r]};
+                    if (beta != 0.0f) {
+                        const float *cp = p.C + (int64_t)row * p.ldc + col;
+                        const f32x4 c0 =
+                            vec_c ? *reinterpret_cast<const f32x4 *>(cp) : f32x4{cp[0], cp[1], cp[2], cp[3]};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c0[e], v[e]);
-                }
+                        for (int e = 0; e < 4; ++e) v[e] = fmaf(beta, c0[e], v[e]);
+                    }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = Act::apply(v[e] + b[e]);
-                if (vec_c) {
-                    *reinterpret_cast<f32x4 *>(cp) = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cp[e] = v[e];
+                    for (int e = 0; e < 4; ++e) v[e] = Act::apply(v[e] + b[e]);
+                    store_out4<OUT>(p, row, col, v, vec_o);
                 }
             }
-        }
     });
 }
 
@@ -417,8 +415,12 @@ hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8>)
+                                           : reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int VA, int VB, int GROUP_M>
@@ -437,7 +439,9 @@ hipError_t launch_f32_tiled(const GemmParams &p, hipStream_t stream) {
 
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
-template __global__ void f32_ring_kernel<4, 4>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 1, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 1, 4, 4>(GemmParams, int, int);
@@ -459,7 +463,7 @@ template __global__ void f32_tiled_kernel<64, 64, 16, 2, 2, 1, 1, 8>(GemmParams,
 // shape whose vector widths the operands allow, so wider loads come first.
 const KernelDesc kF32TiledKernels[] = {
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_ring4",
-     &launch_f32_ring<4, 4>},
+     &launch_f32_ring<4, 4>, 0, nullptr, kLayoutNN, false, kOutAll},
     F32_TILED(256, 256, 16, 2, 2, 4, 4, 4),
     F32_TILED(256, 256, 16, 2, 2, 4, 1, 4),
     F32_TILED(256, 256, 16, 2, 2, 1, 4, 4),

@@ -37,7 +37,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int fp8_swz(int row) { return (row >> 2) & 3; }
 
-template <int NS, int GROUP_M>
+template <int NS, int GROUP_M, int OUT>
 __global__ void __launch_bounds__(256)
 fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint8_t>(p);
@@ -168,44 +168,44 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
     with_activation(p.act, [&](auto act) {
         using Act = decltype(act);
+        const bool vec_o = out_vec4<OUT>(p);
 #pragma unroll
-        for (int fn = 0; fn < 4; ++fn) {
+            for (int fn = 0; fn < 4; ++fn) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
-                if (col >= N) continue;
-                const bool whole = vec_c && col + 4 <= N;
-                float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
+                    if (col >= N) continue;
+                    const bool whole = col + 4 <= N;
+                    float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
 #pragma unroll
-                for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col + t < N) ? p.bias[col + t] : -0.0f;
+                    for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col + t < N) ? p.bias[col + t] : -0.0f;
 #pragma unroll
-                for (int fm = 0; fm < 4; ++fm) {
-                    const int row = m0 + wm * 128 + 32 * fm + l32;
-                    if (row >= M) continue;
-                    float *cp = p.C + (int64_t)row * p.ldc + col;
-                    f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
-                               alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
-                    if (whole) {
+                    for (int fm = 0; fm < 4; ++fm) {
+                        const int row = m0 + wm * 128 + 32 * fm + l32;
+                        if (row >= M) continue;
+                        const float *cp = p.C + (int64_t)row * p.ldc + col;
+                        f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
+                                   alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
                         if (beta != 0.0f) {
-                            const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cp);
+                            f32x4 c0;
+                            if (whole && vec_c) {
+                                c0 = *reinterpret_cast<const f32x4 *>(cp);
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) c0[t] = col + t < N ? cp[t] : 0.0f;
+                            }
 #pragma unroll
                             for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
                         }
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
-                        *reinterpret_cast<f32x4 *>(cp) = v;
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            if (col + t >= N) continue;
-                            float x = v[t];
-                            if (beta != 0.0f) x = fmaf(beta, cp[t], x);
-                            cp[t] = Act::apply(x + b[t]);
-                        }
+                        if (whole)
+                            store_out4<OUT>(p, row, col, v, vec_o);
+                        else
+                            store_out_first<OUT>(p, row, col, v, N - col);
                     }
                 }
             }
-        }
     });
 }
 
@@ -214,11 +214,17 @@ hipError_t launch_fp8_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M>),
-                           dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8>)
+                                           : reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
 }
 
-template __global__ void fp8_ring_kernel<4, 4>(GemmParams, int, int);
+template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_FP8>(GemmParams, int, int);
 
 }  // namespace
 
@@ -226,7 +232,7 @@ template __global__ void fp8_ring_kernel<4, 4>(GemmParams, int, int);
 // vec_a = vec_b = 16: A, B, lda, ldb and K multiples of 16 bytes.
 const KernelDesc kFp8TiledKernels[] = {
     {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_nt_ring4",
-     &launch_fp8_ring<4, 4>, 0, nullptr, kLayoutNT},
+     &launch_fp8_ring<4, 4>, 0, nullptr, kLayoutNT, false, kOutAll},
 };
 const int kFp8TiledKernelCount = sizeof(kFp8TiledKernels) / sizeof(kFp8TiledKernels[0]);
 #endif

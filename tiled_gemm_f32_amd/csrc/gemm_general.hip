@@ -191,10 +191,9 @@ general_kernel(GemmParams p, int tiles_m, int tiles_n) {
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 64 + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < M) {
-                    float *cp = p.C + (int64_t)row * p.ldc + col;
                     float v = alpha * acc[fm][fn][r];
-                    if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                    *cp = epilogue_value(v, col, p.bias, p.act);
+                    if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)row * p.ldc + col], v);
+                    store_out_any(p, row, col, epilogue_value(v, col, p.bias, p.act));
                 }
             }
         }
@@ -234,11 +233,11 @@ GENERAL_INSTANCES(GEMM_DTYPE_FP8F32)
 // kernel runs its operands.
 const KernelDesc kGeneralKernels[] = {
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, kBM, kBN, kBK, kThreads, 1, 1, "f32_general_128x128x16",
-     &launch_general<GEMM_DTYPE_F32>, 0, nullptr, kLayoutAll, true},
+     &launch_general<GEMM_DTYPE_F32>, 0, nullptr, kLayoutAll, true, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, kBM, kBN, kBK, kThreads, 1, 1, "bf16_general_128x128x16",
-     &launch_general<GEMM_DTYPE_BF16F32>, 0, nullptr, kLayoutAll, true},
+     &launch_general<GEMM_DTYPE_BF16F32>, 0, nullptr, kLayoutAll, true, kOutAll},
     {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, kBM, kBN, kBK, kThreads, 1, 1, "fp8_general_128x128x16",
-     &launch_general<GEMM_DTYPE_FP8F32>, 0, nullptr, kLayoutAll, true},
+     &launch_general<GEMM_DTYPE_FP8F32>, 0, nullptr, kLayoutAll, true, kOutAll},
 };
 const int kGeneralKernelCount = sizeof(kGeneralKernels) / sizeof(kGeneralKernels[0]);
 #endif

@@ -32,9 +32,21 @@ struct GemmParams {
     // may be null, act is a gemm_activation.
     const float *bias;
     int32_t act;
+    // Output (gemm_output).  GEMM_OUT_F32 stores to C (out == C, ldo ==
+    // ldc); the others store round(out_scale * value) to out, bf16 or E4M3,
+    // and leave C unwritten (it is read as C0 when beta != 0).  Kernels run
+    // only the outputs their table row lists.
+    int32_t out_type;
+    float out_scale;
+    void *out;
+    int64_t ldo;
 };
 
 inline int k_splits(const GemmParams &p) { return p.kchunk > 0 ? (p.K + p.kchunk - 1) / p.kchunk : 1; }
+// Output type a launch stores: a K-split slice stores fp32 partials whatever
+// the call's output (the reduce converts); kernels templated on the output
+// type launch the matching instantiation.
+inline int launch_out_type(const GemmParams &p) { return p.kchunk > 0 ? 0 : p.out_type; }
 // Most K slices the reduce kernel adds (every split path stays within it).
 constexpr int kMaxReduceSplits = 16;
 
@@ -42,6 +54,8 @@ typedef hipError_t (*LaunchFn)(const GemmParams &p, hipStream_t stream);
 
 // Operand layouts a kernel runs: bit 2*op_a + op_b.
 constexpr int32_t kLayoutNN = 1, kLayoutNT = 2, kLayoutTN = 4, kLayoutTT = 8, kLayoutAll = 15;
+// Output-type bits (bit gemm_output).
+constexpr int32_t kOutF32 = 1, kOutAll = 7;
 
 // C = alpha * (sum of the k_splits(p) partial products, in split order) +
 // beta * C, for the tiled kernels' K split (defined with the skinny kernels).
@@ -61,6 +75,7 @@ struct KernelDesc {
     LaunchWsFn launch_ws;  // set instead of `launch` for kernels that need the caller's workspace
     int32_t layouts = kLayoutNN;
     bool fallback = false;     // chosen only when no other kernel runs the call
+    int32_t outputs = kOutF32;
 };
 
 // Split-K skinny kernel sizing, shared by its launcher and the workspace query:
@@ -96,8 +111,8 @@ extern const int kBf16SplitKernelCount;
 extern const KernelDesc kSkinnyNtKernels[];
 extern const int kSkinnyNtKernelCount;
 
-// C = beta * C over an M x N view (beta == 0 writes zeros without reading).
-hipError_t launch_scale_c(float beta, float *C, int32_t M, int32_t N, int64_t ldc, const float *bias, int32_t act,
-                          hipStream_t stream);
+// The K == 0 / alpha == 0 result over p's M x N view: act(beta * C + bias)
+// (C not read when beta == 0), stored as p's output type.
+hipError_t launch_scale_c(const GemmParams &p, hipStream_t stream);
 
 }  // namespace gemm

@@ -188,10 +188,9 @@ skinny_nt_kernel(GemmParams p, float *partials, int splits, int kchunk) {
         if (mine != nullptr) {
             mine[(int64_t)i * N + col] = s;
         } else {
-            float *cp = p.C + (int64_t)i * p.ldc + col;
             float v = alpha * s;
-            if (beta != 0.0f) v = fmaf(beta, *cp, v);
-            *cp = epilogue_value(v, col, p.bias, p.act);
+            if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)i * p.ldc + col], v);
+            store_out_any(p, i, col, epilogue_value(v, col, p.bias, p.act));
         }
     }
 }
@@ -246,17 +245,17 @@ template __global__ void skinny_nt_kernel<GEMM_DTYPE_FP8F32, 8, 2>(GemmParams, f
 // workspace (one slice); the split entries need one when they split.
 const KernelDesc kSkinnyNtKernels[] = {
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, kNtCols, 32 * 8 * 2, 512, 4, 4, "f32_skinny_nt_n32_w8_u2",
-     &launch_nt_plain<GEMM_DTYPE_F32, 8, 2>, 0, nullptr, kLayoutNT},
+     &launch_nt_plain<GEMM_DTYPE_F32, 8, 2>, 0, nullptr, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kNtCols, 64 * 8 * 2, 512, 8, 8, "bf16_skinny_nt_n32_w8_u2",
-     &launch_nt_plain<GEMM_DTYPE_BF16F32, 8, 2>, 0, nullptr, kLayoutNT},
+     &launch_nt_plain<GEMM_DTYPE_BF16F32, 8, 2>, 0, nullptr, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 32 * 8 * 2, 512, 4, 4, "f32_skinny_nt_splitk_n32_w8_u2",
-     nullptr, 0, &launch_nt_ws<GEMM_DTYPE_F32, 8, 2>, kLayoutNT},
+     nullptr, 0, &launch_nt_ws<GEMM_DTYPE_F32, 8, 2>, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 64 * 8 * 2, 512, 8, 8,
-     "bf16_skinny_nt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_BF16F32, 8, 2>, kLayoutNT},
+     "bf16_skinny_nt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_BF16F32, 8, 2>, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_FP8F32, GEMM_PATH_SKINNY, 16, kNtCols, 128 * 8 * 2, 512, 16, 16, "fp8_skinny_nt_n32_w8_u2",
-     &launch_nt_plain<GEMM_DTYPE_FP8F32, 8, 2>, 0, nullptr, kLayoutNT},
+     &launch_nt_plain<GEMM_DTYPE_FP8F32, 8, 2>, 0, nullptr, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_FP8F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 128 * 8 * 2, 512, 16, 16,
-     "fp8_skinny_nt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_FP8F32, 8, 2>, kLayoutNT},
+     "fp8_skinny_nt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_FP8F32, 8, 2>, kLayoutNT, false, kOutAll},
 };
 const int kSkinnyNtKernelCount = sizeof(kSkinnyNtKernels) / sizeof(kSkinnyNtKernels[0]);
 #endif
