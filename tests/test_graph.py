@@ -3,8 +3,10 @@
 The library launches only on the caller's stream and allocates nothing,
 and its workspaces need no clearing, so its calls capture like any kernel
 launch.  The captured sequence mixes the paths: a bf16 ring call, a tiled
-K split (partials, then the reduce kernel), an fp32 M = 16 split call and
-an fp8 call with a fused GELU epilogue.  It is replayed several times, with
+K split (partials, then the reduce kernel), an fp32 M = 16 split call, an
+fp8 call with a fused GELU epilogue, a bf16 decode call with weights stored
+N x K split over K into a bf16 output, and the bf16 ring writing a
+saturating fp8 output.  It is replayed several times, with
 eager work and synchronisations between replays, and every replay must
 reproduce the eager results bit for bit (every path is deterministic).
 """
@@ -33,16 +35,26 @@ def test_graph_capture_and_replay(gpu_available):
     B4t = B4.t().contiguous()
     bias = make_bias(768, seed=904).cuda()
     A1, B1, A2, B2, A3, B3, A4, B4t = (_dev(t) for t in (A1, B1, A2, B2, A3, B3, A4, B4t))
+    A5, B5, _ = make_random_inputs(16, 2048, 4096, seed=905, dist="normal", dtype="bf16f32")
+    B5t = _dev(B5.t().contiguous())
+    A5 = _dev(A5)
     ws2 = tg.workspace(256, 512, 6000)
     ws3 = tg.workspace(16, 4096, 8192)
+    ws5 = tg.workspace(16, 2048, 4096, dtype=tg.GEMM_DTYPE_BF16F32)
     outs = [torch.empty(1024, 1024, device="cuda"), torch.empty(256, 512, device="cuda"),
-            torch.empty(16, 4096, device="cuda"), torch.empty(512, 768, device="cuda")]
+            torch.empty(16, 4096, device="cuda"), torch.empty(512, 768, device="cuda"),
+            torch.empty(16, 2048, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(1024, 1024, dtype=torch.float8_e4m3fn, device="cuda")]
 
     def sequence():
         tg.gemm(A1, B1, outs[0])
         tg.gemm(A2, B2, outs[1], ws=ws2)
         tg.gemm(A3, B3, outs[2], ws=ws3)
         tg.gemm(A4, B4t, outs[3], op_b="T", bias=bias, activation="gelu", alpha=0.125)
+        # weights stored N x K, split over K through the workspace, bf16 output
+        tg.gemm(A5, B5t, None, op_b="T", ws=ws5, out=outs[4], out_scale=0.5)
+        # the bf16 ring with a saturating fp8 output
+        tg.gemm(A1, B1, None, out=outs[5], out_scale=0.01)
 
     say("[graph] eager reference")
     sequence()
@@ -62,13 +74,18 @@ def test_graph_capture_and_replay(gpu_available):
         sequence()
     torch.cuda.synchronize()
 
+    def bits(t):
+        return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t.view(torch.int16) \
+            if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
     for rep in range(4):
         for o in outs:
-            o.fill_(float("nan"))          # eager work between replays
+            bits(o).fill_(-1)              # eager work between replays: NaN patterns
         ws2.fill_(0xFF)
+        ws5.fill_(0xFF)
         torch.cuda.synchronize()
         say(f"[graph] replay {rep}")
         graph.replay()
         torch.cuda.synchronize()
         for i, (o, r) in enumerate(zip(outs, ref)):
-            assert torch.equal(o, r), f"replay {rep}, call {i}"
+            assert torch.equal(bits(o), bits(r)), f"replay {rep}, call {i}"
