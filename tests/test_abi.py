@@ -212,8 +212,9 @@ def test_vector_width_follows_alignment():
 
 
 def test_forced_kernels():
-    f32_tiled = kernel_ids(dtype=F32, path=tg.GEMM_PATH_TILED)
-    bf16_tiled = kernel_ids(dtype=BF16, path=tg.GEMM_PATH_TILED)
+    nn = {k["id"] for k in tg.kernels() if k["layouts"] & 1}
+    f32_tiled = [k for k in kernel_ids(dtype=F32, path=tg.GEMM_PATH_TILED) if k in nn]
+    bf16_tiled = [k for k in kernel_ids(dtype=BF16, path=tg.GEMM_PATH_TILED) if k in nn]
     skinny = kernel_ids(dtype=F32, path=tg.GEMM_PATH_SKINNY, layouts=1)
     assert f32_tiled and bf16_tiled and skinny
     for kid in f32_tiled:
@@ -468,7 +469,7 @@ def test_fp8_nt_unaligned_falls_back_to_general(why):
 def test_layouts_without_a_fast_kernel_take_general(dtype, prefix, ops):
     st, pl = gplan(dtype, ops[0], ops[1], 1000, 3000, 784)      # K a multiple of 16: fast kernels can run
     assert st == OK
-    fast = (dtype in (F32, BF16) and ops == (N_, N_)) or (dtype == FP8 and ops == (N_, T_)) or dtype == BF16
+    fast = (dtype in (F32, BF16) and ops == (N_, N_)) or (dtype in (FP8, F32) and ops == (N_, T_)) or dtype == BF16
     if fast:
         assert "general" not in kname(pl), pl
     else:

@@ -234,7 +234,14 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
 //     instructions are pinned between MFMAs with sched_barrier.
 // Loads complete in issue order: before the barrier of slice kt the only
 // loads allowed in flight are the 8*(NS-2) of the slices after kt+1.
-template <int NS, int GROUP_M, int OUT>
+//
+// BT: B is stored N x K (k contiguous along each of its rows), the shape of
+// A.  Its slices then take A's layout, loads and fragment reads (k chunks
+// past K masked the same way), and B's fragment goes in as the matrix
+// instruction's first operand: lane (h, l32) of fragment (fm, fn) then holds
+// runs of 4 consecutive columns of one row of C, as in the bf16 ring.  N is
+// free; runs of columns that straddle N are stored element by element.
+template <int NS, int GROUP_M, int OUT, bool BT>
 __global__ void __launch_bounds__(256)
 f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<float>(p);
@@ -259,10 +266,12 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const float *A = static_cast<const float *>(p.A);
     const float *B = static_cast<const float *>(p.B);
     const int a_rows = min(BM, M - m0);
+    const int b_rows = min(BN, N - n0);     // rows of a B^T slice (BT)
 
     // Load instruction j of this wave: j < 4 fills A block 4*wave + j (rows
     // 16*blk .. +15; lane -> row 16*blk + lane/4, physical chunk lane%4);
-    // j >= 4 fills B row 4*wave + j - 4 (lane -> columns 4*lane .. +3).
+    // j >= 4 fills B row 4*wave + j - 4 (lane -> columns 4*lane .. +3), or
+    // with BT block 4*wave + j - 4 of B^T exactly as for A.
     uint32_t a_goff[4], b_goff[4];
     int a_kc[4];
 #pragma unroll
@@ -271,24 +280,28 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int lc = (lane & 3) ^ ((row >> 2) & 3);
         a_kc[j] = 4 * lc;
         a_goff[j] = (uint32_t)(row * lda + 4 * lc) * 4u;
-        b_goff[j] = (uint32_t)((4 * wave + j) * ldb + 4 * lane) * 4u;
+        b_goff[j] = BT ? (uint32_t)(row * ldb + 4 * lc) * 4u : (uint32_t)((4 * wave + j) * ldb + 4 * lane) * 4u;
     }
-    // Resources of slice kt, rebased per slice: rows past M / past K fall
-    // outside the extents; a chunk at or past K in a valid row of A gets 2^31
-    // added to its offset.
+    // Resources of slice kt, rebased per slice: rows past M / past K (past N
+    // for B^T) fall outside the extents; a chunk at or past K in a valid row
+    // of A (or B^T) gets 2^31 added to its offset.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
         ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 4));
-        rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
+        if (BT)
+            rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 4));
+        else
+            rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
     };
     auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
+        const int jj = j & 3;
+        const uint32_t poison = (uint32_t)(a_kc[jj] >= K - kt * BK) << 31;
         if (j < 4) {
-            const uint32_t poison = (uint32_t)(a_kc[j] >= K - kt * BK) << 31;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16, a_goff[j] + poison, 0, 0, 0);
         } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + j - 4) * 1024), 16, b_goff[j - 4], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + jj) * 1024),
+                                                     16, b_goff[jj] + (BT ? poison : 0u), 0, 0, 0);
         }
     };
 
@@ -296,20 +309,32 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int wm = wave >> 1, wn = wave & 1;
     // A fragment (fm, q): row wm*128 + 32*fm + l32, k = 8h + 4q .. +3.
     // B values of step s: row 8h + s, columns wn*128 + 4*l32 .. +3.
-    uint32_t fa_off[2];
+    uint32_t fa_off[2], fbt_off[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) fa_off[q] = (uint32_t)((wm * 128 + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
+    for (int q = 0; q < 2; ++q) {
+        fa_off[q] = (uint32_t)((wm * 128 + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
+        fbt_off[q] = (uint32_t)(kA + (wn * 128 + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
+    }
     const uint32_t fb_off = (uint32_t)(kA + 8 * h * 1024 + (wn * 128 + 4 * l32) * 4);
 
     f32x4 af[2][4][2];
     f32x4 bv[kSteps];
+    f32x4 bf[BT ? 2 : 1][4][2];    // B^T fragments, like af (BT only)
     auto read_a = [&](int stage, int set, int fm) {
         const char *base = stage_base(stage);
 #pragma unroll
         for (int q = 0; q < 2; ++q) af[set][fm][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[q] + 2048 * fm);
     };
     auto read_b = [&](int stage, int s) {
-        bv[s] = *reinterpret_cast<const f32x4 *>(stage_base(stage) + fb_off + 1024 * s);
+        if constexpr (!BT) bv[s] = *reinterpret_cast<const f32x4 *>(stage_base(stage) + fb_off + 1024 * s);
+    };
+    auto read_bt = [&](int stage, int set, int fn) {
+        if constexpr (BT) {
+            const char *base = stage_base(stage);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                bf[set][fn][q] = *reinterpret_cast<const f32x4 *>(base + fbt_off[q] + 2048 * fn);
+        }
     };
     f32x16 acc[4][4];
 #pragma unroll
@@ -320,7 +345,12 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // k = s (h = 0) or 8 + s (h = 1) of the slice for both operands.
     auto mma = [&](int set, int s, int t) {
         const int fm = t >> 2, fn = t & 3;
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][fm][s >> 2][s & 3], bv[s][fn], acc[fm][fn], 0, 0, 0);
+        if constexpr (BT)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[set][fn][s >> 2][s & 3], af[set][fm][s >> 2][s & 3],
+                                                               acc[fm][fn], 0, 0, 0);
+        else
+            acc[fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][fm][s >> 2][s & 3], bv[s][fn], acc[fm][fn], 0, 0, 0);
     };
 
     const int nk = (K + BK - 1) / BK;
@@ -337,6 +367,8 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) read_a(0, 0, fm);
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) read_bt(0, 0, fn);
     read_b(0, 0);
     for (int kb = 0; kb < nk; kb += NS) {
 #pragma unroll
@@ -364,6 +396,7 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                 mma(set, 6 + (q >> 4), q & 15);
                 if ((q & 1) == 0 && q < 16) dma(kt + NS, u, ra, rb, q >> 1);
                 if ((q & 1) == 1 && q < 8) read_a(nxt, set ^ 1, q >> 1);
+                if (BT && (q & 1) == 1 && q >= 9 && q < 16) read_bt(nxt, set ^ 1, (q - 9) >> 1);
                 if (q == 9) read_b(nxt, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -379,6 +412,53 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // in registers.
     const float alpha = p.alpha, beta = p.beta;
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
+    if constexpr (BT) {
+        // B^T was the first operand: register 4g + t of lane (h, l32) in
+        // fragment (fm, fn) is C[row m0 + wm*128 + 32*fm + l32][column
+        // n0 + wn*128 + 32*fn + 8*g + 4*h + t].
+        with_activation(p.act, [&](auto act) {
+            using Act = decltype(act);
+            const bool vec_o = out_vec4<OUT>(p);
+#pragma unroll
+            for (int fn = 0; fn < 4; ++fn) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * 128 + 32 * fn + 8 * g + 4 * h;
+                    if (col >= N) continue;
+                    const bool whole = col + 4 <= N;
+                    float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col + t < N) ? p.bias[col + t] : -0.0f;
+#pragma unroll
+                    for (int fm = 0; fm < 4; ++fm) {
+                        const int row = m0 + wm * 128 + 32 * fm + l32;
+                        if (row >= M) continue;
+                        const float *cp = p.C + (int64_t)row * p.ldc + col;
+                        f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
+                                   alpha * acc[fm][fn][4 * g + 2], alpha * acc[fm][fn][4 * g + 3]};
+                        if (beta != 0.0f) {
+                            f32x4 c0;
+                            if (whole && vec_c) {
+                                c0 = *reinterpret_cast<const f32x4 *>(cp);
+                            } else {
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) c0[t] = col + t < N ? cp[t] : 0.0f;
+                            }
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
+                        }
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
+                        if (whole)
+                            store_out4<OUT>(p, row, col, v, vec_o);
+                        else
+                            store_out_first<OUT>(p, row, col, v, N - col);
+                    }
+                }
+            }
+        });
+        return;
+    }
     const int col = n0 + wn * 128 + 4 * l32;
     if (col >= N) return;
     float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
@@ -410,15 +490,16 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     });
 }
 
-template <int NS, int GROUP_M>
+template <int NS, int GROUP_M, bool BT = false>
 hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     const int out = launch_out_type(p);
-    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16>)
-                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8>)
-                                           : reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_F32>);
+    const void *fn =
+        out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16, BT>)
+        : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8, BT>)
+                              : reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_F32, BT>);
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
                            stream);
 }
@@ -439,9 +520,12 @@ hipError_t launch_f32_tiled(const GemmParams &p, hipStream_t stream) {
 
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32, false>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16, false>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8, false>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32, true>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16, true>(GemmParams, int, int);
+template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8, true>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 1, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 1, 4, 4>(GemmParams, int, int);
@@ -464,6 +548,9 @@ template __global__ void f32_tiled_kernel<64, 64, 16, 2, 2, 1, 1, 8>(GemmParams,
 const KernelDesc kF32TiledKernels[] = {
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_ring4",
      &launch_f32_ring<4, 4>, 0, nullptr, kLayoutNN, false, kOutAll},
+    // B stored N x K: its rows (and A's) must be whole 16-byte chunks.
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_nt_ring4",
+     &launch_f32_ring<4, 4, true>, 0, nullptr, kLayoutNT, false, kOutAll},
     F32_TILED(256, 256, 16, 2, 2, 4, 4, 4),
     F32_TILED(256, 256, 16, 2, 2, 4, 1, 4),
     F32_TILED(256, 256, 16, 2, 2, 1, 4, 4),
