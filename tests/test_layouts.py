@@ -41,10 +41,12 @@ BF16_NT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4"
 BF16_TN_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4"
 BF16_TT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4"
 F32_NT_RING = "f32_mfma32_256x256x16_w2x2_a4b4_nt_ring4"
+F32_TN_RING = "f32_mfma32_256x256x16_w2x2_a4b4_tn_ring4"
+F32_TT_RING = "f32_mfma32_256x256x16_w2x2_a4b4_tt_ring4"
 # (dtype, kernel, op_a, op_b) of every ring kernel for a transposed layout
 T_RINGS = [("fp8f32", FP8_RING, "N", "T"), ("bf16f32", BF16_NT_RING, "N", "T"),
            ("bf16f32", BF16_TN_RING, "T", "N"), ("bf16f32", BF16_TT_RING, "T", "T"),
-           ("f32", F32_NT_RING, "N", "T")]
+           ("f32", F32_NT_RING, "N", "T"), ("f32", F32_TN_RING, "T", "N"), ("f32", F32_TT_RING, "T", "T")]
 
 
 def stored(A, B, op_a, op_b):

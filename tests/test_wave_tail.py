@@ -26,7 +26,8 @@ CASES = [
     ("bf16f32", "N", "N", 4352, 4096, 2048),
     ("bf16f32", "N", "T", 4352, 4096, 2048),
     ("fp8f32", "N", "T", 4352, 4096, 2048),
-    ("f32", "T", "N", 2176, 2048, 2048),      # 128-tile general kernel
+    ("f32", "T", "N", 4352, 4096, 2048),
+    ("f32", "T", "T", 4352, 4096, 2048),
 ]
 
 

@@ -241,7 +241,14 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
 // instruction's first operand: lane (h, l32) of fragment (fm, fn) then holds
 // runs of 4 consecutive columns of one row of C, as in the bf16 ring.  N is
 // free; runs of columns that straddle N are stored element by element.
-template <int NS, int GROUP_M, int OUT, bool BT>
+//
+// AT: A is stored K x M (m contiguous), the shape of an untransposed B, so
+// its slices take B's layout and loads ([16 k rows][256 m]), and a lane's
+// 16-byte read at row k gives it one value for each of its four A
+// fragments: row i of fragment fm stands for m = 4*i + fm of the wave's
+// 128-row block, as column j of fragment fn stands for n = 4*j + fn.  Only
+// the rows of C the epilogue addresses change.
+template <int NS, int GROUP_M, int OUT, bool BT, bool AT = false>
 __global__ void __launch_bounds__(256)
 f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<float>(p);
@@ -279,7 +286,7 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int row = 16 * (4 * wave + j) + (lane >> 2);
         const int lc = (lane & 3) ^ ((row >> 2) & 3);
         a_kc[j] = 4 * lc;
-        a_goff[j] = (uint32_t)(row * lda + 4 * lc) * 4u;
+        a_goff[j] = AT ? (uint32_t)((4 * wave + j) * lda + 4 * lane) * 4u : (uint32_t)(row * lda + 4 * lc) * 4u;
         b_goff[j] = BT ? (uint32_t)(row * ldb + 4 * lc) * 4u : (uint32_t)((4 * wave + j) * ldb + 4 * lane) * 4u;
     }
     // Resources of slice kt, rebased per slice: rows past M / past K (past N
@@ -287,7 +294,10 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // of A (or B^T) gets 2^31 added to its offset.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
-        ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 4));
+        if (AT)
+            ra = make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent(((int64_t)(K - k0 - 1) * lda + (M - m0)) * 4));
+        else
+            ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 4));
         if (BT)
             rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 4));
         else
@@ -297,8 +307,8 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int jj = j & 3;
         const uint32_t poison = (uint32_t)(a_kc[jj] >= K - kt * BK) << 31;
         if (j < 4) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16, a_goff[j] + poison, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(stage_base(stage) + (4 * wave + j) * 1024), 16,
+                                                     a_goff[j] + (AT ? 0u : poison), 0, 0, 0);
         } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage_base(stage) + kA + (4 * wave + jj) * 1024),
                                                      16, b_goff[jj] + (BT ? poison : 0u), 0, 0, 0);
@@ -316,14 +326,22 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         fbt_off[q] = (uint32_t)(kA + (wn * 128 + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
     }
     const uint32_t fb_off = (uint32_t)(kA + 8 * h * 1024 + (wn * 128 + 4 * l32) * 4);
+    const uint32_t fat_off = (uint32_t)(8 * h * 1024 + (wm * 128 + 4 * l32) * 4);   // A^T values (AT)
 
     f32x4 af[2][4][2];
     f32x4 bv[kSteps];
     f32x4 bf[BT ? 2 : 1][4][2];    // B^T fragments, like af (BT only)
+    f32x4 av[kSteps];              // A^T values of each step, like bv (AT only)
     auto read_a = [&](int stage, int set, int fm) {
-        const char *base = stage_base(stage);
+        if constexpr (!AT) {
+            const char *base = stage_base(stage);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) af[set][fm][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[q] + 2048 * fm);
+            for (int q = 0; q < 2; ++q)
+                af[set][fm][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[q] + 2048 * fm);
+        }
+    };
+    auto read_at = [&](int stage, int s) {
+        if constexpr (AT) av[s] = *reinterpret_cast<const f32x4 *>(stage_base(stage) + fat_off + 1024 * s);
     };
     auto read_b = [&](int stage, int s) {
         if constexpr (!BT) bv[s] = *reinterpret_cast<const f32x4 *>(stage_base(stage) + fb_off + 1024 * s);
@@ -345,12 +363,11 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // k = s (h = 0) or 8 + s (h = 1) of the slice for both operands.
     auto mma = [&](int set, int s, int t) {
         const int fm = t >> 2, fn = t & 3;
+        const float a = AT ? av[s][fm] : af[set][fm][s >> 2][s & 3];
         if constexpr (BT)
-            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[set][fn][s >> 2][s & 3], af[set][fm][s >> 2][s & 3],
-                                                               acc[fm][fn], 0, 0, 0);
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(bf[set][fn][s >> 2][s & 3], a, acc[fm][fn], 0, 0, 0);
         else
-            acc[fm][fn] =
-                __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][fm][s >> 2][s & 3], bv[s][fn], acc[fm][fn], 0, 0, 0);
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv[s][fn], acc[fm][fn], 0, 0, 0);
     };
 
     const int nk = (K + BK - 1) / BK;
@@ -370,6 +387,7 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int fn = 0; fn < 4; ++fn) read_bt(0, 0, fn);
     read_b(0, 0);
+    read_at(0, 0);
     for (int kb = 0; kb < nk; kb += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
@@ -381,7 +399,9 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                 for (int t = 0; t < 16; ++t) {
                     mma(set, s, t);
                     if (t == 0) read_b(u, s + 1);
+                    if (t == 2) read_at(u, s + 1);
                     if (s == 5 && t == 1) read_b(u, 7);
+                    if (s == 5 && t == 3) read_at(u, 7);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -398,6 +418,7 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                 if ((q & 1) == 1 && q < 8) read_a(nxt, set ^ 1, q >> 1);
                 if (BT && (q & 1) == 1 && q >= 9 && q < 16) read_bt(nxt, set ^ 1, (q - 9) >> 1);
                 if (q == 9) read_b(nxt, 0);
+                if (q == 11) read_at(nxt, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -414,8 +435,8 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
     if constexpr (BT) {
         // B^T was the first operand: register 4g + t of lane (h, l32) in
-        // fragment (fm, fn) is C[row m0 + wm*128 + 32*fm + l32][column
-        // n0 + wn*128 + 32*fn + 8*g + 4*h + t].
+        // fragment (fm, fn) is C[row m0 + wm*128 + 32*fm + l32 (with A^T:
+        // 4*l32 + fm)][column n0 + wn*128 + 32*fn + 8*g + 4*h + t].
         with_activation(p.act, [&](auto act) {
             using Act = decltype(act);
             const bool vec_o = out_vec4<OUT>(p);
@@ -431,7 +452,7 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                     for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col + t < N) ? p.bias[col + t] : -0.0f;
 #pragma unroll
                     for (int fm = 0; fm < 4; ++fm) {
-                        const int row = m0 + wm * 128 + 32 * fm + l32;
+                        const int row = AT ? m0 + wm * 128 + 4 * l32 + fm : m0 + wm * 128 + 32 * fm + l32;
                         if (row >= M) continue;
                         const float *cp = p.C + (int64_t)row * p.ldc + col;
                         f32x4 v = {alpha * acc[fm][fn][4 * g], alpha * acc[fm][fn][4 * g + 1],
@@ -471,7 +492,8 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
             for (int fm = 0; fm < 4; ++fm) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int i = 8 * (r >> 2) + 4 * h + (r & 3);     // row of the fragment
+                    const int row = AT ? m0 + wm * 128 + 4 * i + fm : m0 + wm * 128 + 32 * fm + i;
                     if (row >= M) continue;
                     f32x4 v = {alpha * acc[fm][0][r], alpha * acc[fm][1][r], alpha * acc[fm][2][r],
                                alpha * acc[fm][3][r]};
@@ -490,16 +512,16 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     });
 }
 
-template <int NS, int GROUP_M, bool BT = false>
+template <int NS, int GROUP_M, bool BT = false, bool AT = false>
 hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     const int out = launch_out_type(p);
     const void *fn =
-        out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16, BT>)
-        : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8, BT>)
-                              : reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_F32, BT>);
+        out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16, BT, AT>)
+        : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8, BT, AT>)
+                              : reinterpret_cast<const void *>(&f32_ring_kernel<NS, GROUP_M, GEMM_OUT_F32, BT, AT>);
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
                            stream);
 }
@@ -520,12 +542,14 @@ hipError_t launch_f32_tiled(const GemmParams &p, hipStream_t stream) {
 
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32, false>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16, false>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8, false>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32, true>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16, true>(GemmParams, int, int);
-template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8, true>(GemmParams, int, int);
+#define F32_RING_INSTANCES(BT, AT)                                                          \
+    template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_F32, BT, AT>(GemmParams, int, int);  \
+    template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_BF16, BT, AT>(GemmParams, int, int); \
+    template __global__ void f32_ring_kernel<4, 4, GEMM_OUT_FP8, BT, AT>(GemmParams, int, int);
+F32_RING_INSTANCES(false, false)
+F32_RING_INSTANCES(true, false)
+F32_RING_INSTANCES(false, true)
+F32_RING_INSTANCES(true, true)
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 1, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 1, 4, 4>(GemmParams, int, int);
@@ -551,6 +575,12 @@ const KernelDesc kF32TiledKernels[] = {
     // B stored N x K: its rows (and A's) must be whole 16-byte chunks.
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_nt_ring4",
      &launch_f32_ring<4, 4, true>, 0, nullptr, kLayoutNT, false, kOutAll},
+    // A stored K x M (and B either way): the stored rows of A^T (M long) are
+    // 16-byte chunks too.
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_tn_ring4",
+     &launch_f32_ring<4, 4, false, true>, 0, nullptr, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 256, 256, 16, 256, 4, 4, "f32_mfma32_256x256x16_w2x2_a4b4_tt_ring4",
+     &launch_f32_ring<4, 4, true, true>, 0, nullptr, kLayoutTT, false, kOutAll},
     F32_TILED(256, 256, 16, 2, 2, 4, 4, 4),
     F32_TILED(256, 256, 16, 2, 2, 4, 1, 4),
     F32_TILED(256, 256, 16, 2, 2, 1, 4, 4),

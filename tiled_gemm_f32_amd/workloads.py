@@ -77,6 +77,7 @@ WORKLOADS = {
         Workload("f32_16x8192x8192_nt", "f32", 16, 8192, 8192, 1.0, 0.0, "uniform", 10, "T"),
         Workload("fp8f32_16x8192x8192_nt", "fp8f32", 16, 8192, 8192, 1.0, 0.0, "normal", 11, "T"),
         Workload("f32_4096_nt", "f32", 4096, 4096, 4096, 1.0, 0.0, "normal", 12, "T"),
+        Workload("f32_4096_tn", "f32", 4096, 4096, 4096, 1.0, 0.0, "normal", 13, "N", "T"),
     ]
 }
 
