@@ -310,9 +310,9 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  *     type, takes a streaming kernel that loads each weight row straight
  *     into the matrix instruction, when the rows of A and B are whole
  *     16-byte chunks (aligned bases, K, lda and ldb);
- *   - bf16 with either operand transposed takes the matrix-core kernel for
- *     that layout when the transposed operands' rows are whole 16-byte
- *     chunks;
+ *   - fp32 and bf16 with either operand transposed take the matrix-core
+ *     kernel for that layout when the stored rows of A and B are whole
+ *     16-byte chunks;
  *   - fp8 with (GEMM_OP_N, GEMM_OP_T) takes the fp8 matrix-core kernel when
  *     A, B, lda, ldb and K are multiples of 16 bytes;
  *   - the rest take a general kernel that loads elements one by one and
