@@ -627,7 +627,9 @@ def test_output_types_of_the_kernels():
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_nt_n32_w8_u2",
                  "fp8_skinny_nt_splitk_n32_w8_u2"):
         assert outs[name] == 7, name
-    assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 1 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 1
+    assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 7 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 7
+    # Register-staged kernels holding 256 accumulators per lane write fp32 only.
+    assert outs["f32_mfma32_256x256x16_w2x2_a4b4"] == 1 and outs["bf16_mfma32_256x256x64_w2x2_a8b8_pipe"] == 1
 
 
 @pytest.mark.parametrize("out_type", [tg.GEMM_OUT_BF16, tg.GEMM_OUT_FP8])
@@ -641,16 +643,15 @@ def test_output_quantisation_choice(out_type):
     assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4"
     st, pl = eplan(BF16, N_, T_, 16, 8192, 8192, out_type, C=0)
     assert st == OK and kname(pl) == "bf16_skinny_nt_n32_w8_u2"
-    # Short K: the kernels preferred there write fp32 only, so the ring
-    # (whose K minimum yields) runs rather than the general fallback.
+    # Short K: the 256-tile kernels preferred there write fp32 only, so a
+    # regular kernel that writes the type runs, never the general fallback.
     st, pl = eplan(BF16, N_, N_, 4352, 4096, 512, out_type, C=0)
-    assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_ring4", pl
+    info = tg.gemm_kernel_query(pl["kernel_id"])
+    assert st == OK and "general" not in info["name"] and (info["outputs"] >> out_type) & 1, pl
     assert kname(gplan(BF16, N_, N_, 4352, 4096, 512)[1]) == "bf16_mfma32_256x256x64_w2x2_a8b8_pipe"
-    # fp32 M <= 16 without a workspace: the one-pass skinny kernels write
-    # fp32 only, so the call takes a kernel that can convert.
+    # fp32 M <= 16 without a workspace: the one-pass skinny kernel.
     st, pl = eplan(F32, N_, N_, 16, 8192, 8192, out_type)
-    assert st == OK and pl["path"] != tg.GEMM_PATH_SKINNY and (
-        tg.gemm_kernel_query(pl["kernel_id"])["outputs"] >> out_type) & 1, pl
+    assert st == OK and pl["path"] == tg.GEMM_PATH_SKINNY, pl
     st, pl = eplan(F32, N_, N_, 16, 8192, 8192, out_type, ws=tg.gemm_workspace_size(F32, 16, 8192, 8192))
     assert st == OK and kname(pl) == "f32_skinny_splitk_n128_a4_w8_u1"
     # A kernel that writes fp32 only cannot be forced.

@@ -258,10 +258,15 @@ bf16_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * Cfg::kWaveM + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < M) {
-                    float *cp = p.C + (int64_t)row * p.ldc + col;
                     float v = alpha * acc[fm][fn][r];
-                    if (beta != 0.0f) v = fmaf(beta, *cp, v);
-                    *cp = epilogue_value(v, col, p.bias, p.act);
+                    if constexpr (quantising_epilogue(Cfg::kWaveM * Cfg::kWaveN / 64)) {
+                        if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)row * p.ldc + col], v);
+                        store_out_any(p, row, col, epilogue_value(v, col, p.bias, p.act));
+                    } else {
+                        float *cp = p.C + (int64_t)row * p.ldc + col;
+                        if (beta != 0.0f) v = fmaf(beta, *cp, v);
+                        *cp = epilogue_value(v, col, p.bias, p.act);
+                    }
                 }
             }
         }
@@ -774,7 +779,8 @@ hipError_t launch_bf16_tiled(const GemmParams &p, hipStream_t stream) {
 #define BF16_TILED(BM, BN, BK, WM, WN, VA, VB, G)                                             \
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, BM, BN, BK, 64 * WM * WN, VA, VB,                   \
      "bf16_mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_a" #VA "b" #VB,                    \
-     &launch_bf16_tiled<BM, BN, BK, WM, WN, VA, VB, G>}
+     &launch_bf16_tiled<BM, BN, BK, WM, WN, VA, VB, G>, 0, nullptr, kLayoutNN, false,               \
+     quantising_epilogue((BM / WM) * (BN / WN) / 64) ? kOutAll : kOutF32}
 
 // Explicit instantiations: the device pass never sees the host-only table
 // below, so the kernels it needs are named here.

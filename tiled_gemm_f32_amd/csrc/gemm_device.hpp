@@ -249,6 +249,12 @@ __device__ __forceinline__ void store_out_any(const GemmParams &p, int64_t row, 
     else store_out<GEMM_OUT_F32>(p, row, col, v);
 }
 
+// Register-staged kernels whose epilogue holds more than 128 accumulators per
+// lane store fp32 only: a run-time output switch per element (even a
+// rewritten fp32 store) pushes their accumulators to scratch.  Their table
+// rows say so.
+constexpr bool quantising_epilogue(int acc_per_lane) { return acc_per_lane <= 128; }
+
 // Whether four output values of a row starting at a column that is a
 // multiple of 4 form one aligned vector (16, 8 or 4 bytes).
 template <int OUT> __device__ __forceinline__ bool out_vec4(const GemmParams &p) {

@@ -149,10 +149,9 @@ f32_skinny_kernel(GemmParams p) {
         for (int w = 0; w < WAVES; ++w) s += red[w][i][j];
         const int col = n0 + j;
         if (i < M && col < N) {
-            float *cp = p.C + (int64_t)i * p.ldc + col;
             float v = alpha * s;
-            if (beta != 0.0f) v = fmaf(beta, *cp, v);
-            *cp = epilogue_value(v, col, p.bias, p.act);
+            if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)i * p.ldc + col], v);
+            store_out_any(p, i, col, epilogue_value(v, col, p.bias, p.act));
         }
     }
 }
@@ -347,7 +346,7 @@ scale_c_kernel(GemmParams p) {
 #define F32_SKINNY(VEC, VA, WAVES, UNROLL)                                                     \
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 16 * VEC, 16 * WAVES * UNROLL, 64 * WAVES, VA, VEC,  \
      "f32_skinny_mfma16_n" #VEC "_a" #VA "_w" #WAVES "_u" #UNROLL,                              \
-     &launch_f32_skinny<VEC, VA, WAVES, UNROLL>}
+     &launch_f32_skinny<VEC, VA, WAVES, UNROLL>, 0, nullptr, kLayoutNN, false, kOutAll}
 #define SKINNY_LIST(X)                                                                          \
     X(2, 4, 8, 4) X(2, 4, 16, 2) X(4, 4, 16, 2) X(4, 4, 8, 4) X(1, 4, 16, 4)                      \
     X(2, 1, 8, 4) X(4, 1, 16, 2) X(1, 1, 16, 2)
