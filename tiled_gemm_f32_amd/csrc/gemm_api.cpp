@@ -761,20 +761,6 @@ GEMM_API gemm_status gemm_general(int32_t dtype, int32_t op_a, int32_t op_b, int
     return run_epi(c, epilogue, force_kernel, stream);
 }
 
-GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
-                                             int64_t K, float alpha, const void *A, int64_t lda, const void *B,
-                                             int64_t ldb, float beta, const float *C, int64_t ldc,
-                                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out) {
-    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
-    const KernelDesc *kd = nullptr;
-    void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
-    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
-    c.op_a = op_a;
-    c.op_b = op_b;
-    KSplit ks;
-    return plan(c, force_kernel, out, &kd, &ks);
-}
-
 GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
                                          int64_t K, float alpha, const void *A, int64_t lda, const void *B,
                                          int64_t ldb, float beta, const float *C, int64_t ldc, int32_t force_kernel,
@@ -789,6 +775,15 @@ GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op
     KSplit ks;
     return plan(c, force_kernel, out, &kd, &ks);
 }
+
+GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                             int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                             int64_t ldb, float beta, const float *C, int64_t ldc,
+                                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out) {
+    return gemm_plan_query_epi(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, nullptr,
+                               workspace_bytes, out);
+}
+
 
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
                                      const void *A, int64_t lda, const void *B, int64_t ldb, float beta,

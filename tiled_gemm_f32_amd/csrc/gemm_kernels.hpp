@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm.h"
+
 namespace gemm {
 
 // Arguments of one GEMM launch, already validated by the host code:
@@ -46,7 +48,7 @@ inline int k_splits(const GemmParams &p) { return p.kchunk > 0 ? (p.K + p.kchunk
 // Output type a launch stores: a K-split slice stores fp32 partials whatever
 // the call's output (the reduce converts); kernels templated on the output
 // type launch the matching instantiation.
-inline int launch_out_type(const GemmParams &p) { return p.kchunk > 0 ? 0 : p.out_type; }
+inline int launch_out_type(const GemmParams &p) { return p.kchunk > 0 ? GEMM_OUT_F32 : p.out_type; }
 // Most K slices the reduce kernel adds (every split path stays within it).
 constexpr int kMaxReduceSplits = 16;
 
