@@ -45,7 +45,8 @@ PEAK_HBM_GBS = 8000.0
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 # Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
 EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x8192x8192", "bf16f32_16x8192x8192_nt",
-         "f32_16x8192x8192_nt", "fp8f32_16x8192x8192_nt", "f32_4096_nt", "f32_4096_tn"]
+         "f32_16x8192x8192_nt", "fp8f32_16x8192x8192_nt", "f32_4096_nt", "f32_4096_tn",
+         "fp8f32_8192_nn", "fp8f32_8192_tn"]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 

@@ -313,8 +313,9 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  *   - fp32 and bf16 with either operand transposed take the matrix-core
  *     kernel for that layout when the stored rows of A and B are whole
  *     16-byte chunks;
- *   - fp8 with (GEMM_OP_N, GEMM_OP_T) takes the fp8 matrix-core kernel when
- *     A, B, lda, ldb and K are multiples of 16 bytes;
+ *   - fp8 takes the fp8 matrix-core kernel for its layout when the stored
+ *     rows of A and B (K, M or N long) and lda, ldb are whole 16-byte
+ *     chunks on 16-byte aligned bases;
  *   - the rest take a general kernel that loads elements one by one and
  *     multiplies in fp32.
  *

@@ -673,3 +673,17 @@ def test_output_quantisation_validation():
     assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_BF16, C=0, beta=0.5)[0] == INVALID
     assert eplan(F32, N_, N_, 64, 64, 64, tg.GEMM_OUT_F32, C=0)[0] == INVALID
     assert eplan(F32, N_, N_, 0, 64, 64, tg.GEMM_OUT_BF16, out=0)[0] == OK       # empty: nothing is written
+
+
+@pytest.mark.parametrize("ops,name", [((N_, N_), "fp8_mfma32_256x256x64_w2x2_nn_ring4"),
+                                      ((T_, N_), "fp8_mfma32_256x256x64_w2x2_tn_ring4"),
+                                      ((T_, T_), "fp8_mfma32_256x256x64_w2x2_tt_ring4")])
+def test_fp8_other_layouts_take_their_rings(ops, name):
+    st, pl = gplan(FP8, ops[0], ops[1], 8192, 8192, 8192)
+    assert st == OK and kname(pl) == name and pl["grid"] == 32 * 32, pl
+    # Rows of the K x M / K x N operand must be whole 16-byte chunks.
+    bad = dict(M=8192 + 8) if ops[0] == T_ else dict(N=8192 + 8)
+    args = dict(M=8192, N=8192, K=8192)
+    args.update(bad)
+    st, pl = gplan(FP8, ops[0], ops[1], **args)
+    assert st == OK and kname(pl) == "fp8_general_128x128x16", pl

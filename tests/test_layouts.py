@@ -40,13 +40,17 @@ FP8_RING = "fp8_mfma32_256x256x64_w2x2_nt_ring4"
 BF16_NT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4"
 BF16_TN_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4"
 BF16_TT_RING = "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4"
+FP8_NN_RING = "fp8_mfma32_256x256x64_w2x2_nn_ring4"
+FP8_TN_RING = "fp8_mfma32_256x256x64_w2x2_tn_ring4"
+FP8_TT_RING = "fp8_mfma32_256x256x64_w2x2_tt_ring4"
 F32_NT_RING = "f32_mfma32_256x256x16_w2x2_a4b4_nt_ring4"
 F32_TN_RING = "f32_mfma32_256x256x16_w2x2_a4b4_tn_ring4"
 F32_TT_RING = "f32_mfma32_256x256x16_w2x2_a4b4_tt_ring4"
 # (dtype, kernel, op_a, op_b) of every ring kernel for a transposed layout
 T_RINGS = [("fp8f32", FP8_RING, "N", "T"), ("bf16f32", BF16_NT_RING, "N", "T"),
            ("bf16f32", BF16_TN_RING, "T", "N"), ("bf16f32", BF16_TT_RING, "T", "T"),
-           ("f32", F32_NT_RING, "N", "T"), ("f32", F32_TN_RING, "T", "N"), ("f32", F32_TT_RING, "T", "T")]
+           ("f32", F32_NT_RING, "N", "T"), ("f32", F32_TN_RING, "T", "N"), ("f32", F32_TT_RING, "T", "T"),
+           ("fp8f32", FP8_NN_RING, "N", "N"), ("fp8f32", FP8_TN_RING, "T", "N"), ("fp8f32", FP8_TT_RING, "T", "T")]
 
 
 def stored(A, B, op_a, op_b):
@@ -176,15 +180,16 @@ FP8_SHAPES = [
 ]
 
 
-def ring_shape(shape, op_a, op_b):
+def ring_shape(shape, op_a, op_b, dtype="bf16f32"):
     """Adjust an edge shape to what a ring kernel for this layout needs: the
     stored rows of A and B are whole 16-byte chunks (M is A^T's row length,
-    N is an untransposed B's)."""
+    N is an untransposed B's; 16 fp8 or 8 wider elements)."""
     M, N, K = shape
+    step = 16 if dtype == "fp8f32" else 8
     if op_a == "T":
-        M = -(-M // 8) * 8
+        M = -(-M // step) * step
     if op_b == "N":
-        N = -(-N // 8) * 8
+        N = -(-N // step) * step
     return M, N, K
 
 
@@ -194,7 +199,7 @@ def test_transposed_ring_shapes(gpu_available, ring_case, shape):
     """The ring kernels for transposed layouts, forced (small problems would
     otherwise take the smallest tile), on edge shapes."""
     dtype, ring_name, op_a, op_b = ring_case
-    M, N, K = ring_shape(shape, op_a, op_b)
+    M, N, K = ring_shape(shape, op_a, op_b, dtype)
     ring = [k["id"] for k in tg.kernels() if k["name"] == ring_name][0]
     ok, _ = runnable(dtype, op_a, op_b, M, N, K, ring)
     assert ok
@@ -216,7 +221,7 @@ def test_transposed_ring_shapes(gpu_available, ring_case, shape):
 @pytest.mark.parametrize("c_offset", [0, 1])
 def test_transposed_ring_epilogue_and_c_alignment(gpu_available, ring_case, act, c_offset):
     dtype, ring_name, op_a, op_b = ring_case
-    M, N, K = ring_shape((520, 777, 512), op_a, op_b)
+    M, N, K = ring_shape((520, 777, 512), op_a, op_b, dtype)
     A, B, C0 = make_random_inputs(M, N, K, seed=712, dist="normal", dtype=dtype)
     As, Bs = stored(A, B, op_a, op_b)
     bias = make_bias(N, seed=713)

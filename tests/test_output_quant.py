@@ -76,7 +76,7 @@ def runnable(dtype, kind, op_a, op_b, M, N, K, kid, ws_bytes):
 
 
 LAYOUTS = {"f32": [("N", "N"), ("N", "T")], "bf16f32": [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")],
-           "fp8f32": [("N", "T"), ("N", "N")]}
+           "fp8f32": [("N", "T"), ("N", "N"), ("T", "N"), ("T", "T")]}
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])

@@ -1,5 +1,6 @@
-// fp8 (OCP E4M3) GEMM on the gfx950 matrix cores, A untransposed (M x K)
-// times B transposed (stored N x K), fp32 accumulate and output.
+// fp8 (OCP E4M3) GEMM on the gfx950 matrix cores, fp32 accumulate and
+// output; first for A untransposed (M x K) times B transposed (stored N x K),
+// then for every other layout.
 //
 // With both operands stored k-contiguous, this is the bf16 ring kernel with
 // both panels handled the way it handles A ("Tiled matrix multiplication",
@@ -20,6 +21,18 @@
 //     both sides gives the dot product.  It sums each run of 8 bytes (8
 //     consecutive k here) at reduced precision before adding runs in fp32.
 //
+// Operands stored the other way (A as K x M, B as K x N: AKN, BKN) are
+// contiguous along m or n instead of k.  Their slices are [64 k rows][256
+// columns] of bytes, 16-byte chunk c of row k stored at chunk c ^ 2*(k % 8),
+// loaded one whole 256-byte row per 16 lanes.  A fragment is gathered with
+// ds_read_b64_tr_b8, which returns to lane j of a 16-lane group byte j % 8
+// of the 8-byte reads of lanes (j / 8) + {0, 2, 4, 6, 8, 10, 12, 14}
+// (probed): pointing those lanes at rows kb + 0 .. kb + 7 and the two halves
+// of a 16-byte chunk gives each lane 8 consecutive k of one column, and four
+// reads give the 32 consecutive k of the k-contiguous fragment, in the same
+// byte order.  The swizzle puts each half-wave's 16 rows-and-chunks in 16
+// different chunk columns, so the reads are free of bank conflicts.
+//
 // Schedule, per slice kt (stage kt % NS, register set kt % 2): every wave
 // waits for its own reads of slice kt and for slice kt+1 to land, then a
 // barrier; then 16 matrix instructions on slice kt, each paired with one of
@@ -36,8 +49,11 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int fp8_swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int kn_swz(int k) { return 2 * (k & 7); }
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
-template <int NS, int GROUP_M, int OUT>
+template <int NS, int GROUP_M, int OUT, bool AKN = false, bool BKN = false>
 __global__ void __launch_bounds__(256)
 fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint8_t>(p);
@@ -62,6 +78,9 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // Load instruction j (0..3) of this wave fills 1 KB block 4*wave + j of a
     // panel: rows 16*blk .. +15, lane -> row 16*blk + lane/4, physical chunk
     // lane%4, which holds logical chunk (lane%4) ^ swizzle(row).
+    // For a K x (M or N) panel, instruction j fills k rows 4*(4*wave + j) ..
+    // +3: lane -> row 4*(4*wave + j) + lane/16, physical chunk lane%16, which
+    // holds logical chunk (lane%16) ^ kn_swz(row).
     uint32_t goff_a[4], goff_b[4];
     int kc[4];
 #pragma unroll
@@ -69,22 +88,33 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int row = 16 * (4 * wave + j) + (lane >> 2);
         const int lc = (lane & 3) ^ fp8_swz(row);
         kc[j] = 16 * lc;
-        goff_a[j] = (uint32_t)(row * lda + 16 * lc);
-        goff_b[j] = (uint32_t)(row * ldb + 16 * lc);
+        const int kr = 4 * (4 * wave + j) + (lane >> 4);
+        const int cc = (lane & 15) ^ kn_swz(kr);
+        goff_a[j] = AKN ? (uint32_t)(kr * lda + 16 * cc) : (uint32_t)(row * lda + 16 * lc);
+        goff_b[j] = BKN ? (uint32_t)(kr * ldb + 16 * cc) : (uint32_t)(row * ldb + 16 * lc);
     }
     // Resources of slice kt, rebased per slice.  Rows past M (or N) and
     // slices past K fall outside the extents; a chunk at or past K in a valid
     // row gets 2^31 added to its offset.
+    // A K x (M or N) panel's extent ends at its last k row; rows past K and
+    // the last row's columns past M (N) read as zero.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
-        ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent((int64_t)(a_rows - 1) * lda + (K - k0)));
-        rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent((int64_t)(b_rows - 1) * ldb + (K - k0)));
+        if (AKN)
+            ra = make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent((int64_t)(K - k0 - 1) * lda + (M - m0)));
+        else
+            ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent((int64_t)(a_rows - 1) * lda + (K - k0)));
+        if (BKN)
+            rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent((int64_t)(K - k0 - 1) * ldb + (N - n0)));
+        else
+            rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent((int64_t)(b_rows - 1) * ldb + (K - k0)));
     };
     // Load instruction j (0..7) of slice kt into `stage`: j < 4 fills A block
     // 4*wave + j, j >= 4 fills B block 4*wave + j - 4.
     auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
         const int jj = j & 3;
-        const uint32_t poison = (uint32_t)(kc[jj] >= K - kt * BK) << 31;
+        const bool kn = j < 4 ? AKN : BKN;     // k rows past K already fall outside the extent
+        const uint32_t poison = kn ? 0u : (uint32_t)(kc[jj] >= K - kt * BK) << 31;
         char *dst = stage_base(stage) + (j < 4 ? 0 : kA) + (4 * wave + jj) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 4 ? ra : rb, (lds_void *)dst, 16,
                                                  (j < 4 ? goff_a[jj] : goff_b[jj]) + poison, 0, 0, 0);
@@ -98,17 +128,41 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const uint32_t fa_row = (uint32_t)((wm * 128 + l32) * BK);
     const uint32_t fb_row = (uint32_t)(kA + (wn * 128 + l32) * BK);
 
+    // Transposing reads of a K x (M or N) panel: lane s of each 16-lane group
+    // points at k row 32h + 8q + e(s) and the half 8*(s%2) of the 16-byte
+    // chunk holding the group's 16 columns.
+    const int s16 = lane & 15;
+    const int e_src = ((s16 >> 1) & 3) + 4 * (s16 >> 3);
+    auto kn_off = [&](uint32_t region, int wcol, int f, int q) -> uint32_t {
+        const int kr = 32 * h + 8 * q + e_src;
+        const int c = wcol / 16 + 2 * f + (l32 >> 4);
+        return region + (uint32_t)(kr * 256 + 16 * (c ^ kn_swz(kr)) + 8 * (s16 & 1));
+    };
+
     i32x8 fa[2][4], fb[2][4];
-    // Read r (0..15) of the slice in `stage` into register set `set`: reads
-    // 0..7 are the two halves of A fragments 0..3, reads 8..15 of B's.
+    // Read r of the slice in `stage` into register set `set`: the first NRA
+    // are A's (two 16-byte halves, or four transposing 8-byte reads, per
+    // fragment), then B's.
+    constexpr int NRA = AKN ? 16 : 8, NRB = BKN ? 16 : 8, NR = NRA + NRB;
     auto read_slot = [&](int stage, int set, int r) {
         const char *base = stage_base(stage);
-        const int f = (r >> 1) & 3;
-        const uint32_t off = (r < 8 ? fa_row : fb_row) + 32 * BK * f + ((r & 1) ? ch1 : ch0);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(base + off);
-        i32x8 &dst = r < 8 ? fa[set][f] : fb[set][f];
+        const bool is_a = r < NRA;
+        const bool kn = is_a ? AKN : BKN;
+        const int rr = is_a ? r : r - NRA;
+        i32x8 *frags = is_a ? fa[set] : fb[set];
+        if (kn) {
+            const int f = rr >> 2, q = rr & 3;
+            const uint32_t off = is_a ? kn_off(0, wm * 128, f, q) : kn_off(kA, wn * 128, f, q);
+            const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(base + off));
+            frags[f][2 * q] = v[0];
+            frags[f][2 * q + 1] = v[1];
+        } else {
+            const int f = (rr >> 1) & 3;
+            const uint32_t off = (is_a ? fa_row : fb_row) + 32 * BK * f + ((rr & 1) ? ch1 : ch0);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(base + off);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[4 * (r & 1) + e] = (int)v[e];
+            for (int e = 0; e < 4; ++e) frags[f][4 * (rr & 1) + e] = (int)v[e];
+        }
     };
     f32x16 acc[4][4];
 #pragma unroll
@@ -136,7 +190,7 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8 * (NS - 1)));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) read_slot(0, 0, r);
+    for (int r = 0; r < NR; ++r) read_slot(0, 0, r);
     for (int kb = 0; kb < nk; kb += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
@@ -151,7 +205,8 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
                 mma(u & 1, t);
-                read_slot((u + 1) % NS, (u + 1) & 1, t);
+#pragma unroll
+                for (int r = t * NR / 16; r < (t + 1) * NR / 16; ++r) read_slot((u + 1) % NS, (u + 1) & 1, r);
                 if ((t & 1) == 0) dma(kt + NS, u, ra, rb, t >> 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -209,22 +264,28 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     });
 }
 
-template <int NS, int GROUP_M>
+template <int NS, int GROUP_M, bool AKN = false, bool BKN = false>
 hipError_t launch_fp8_ring(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     const int out = launch_out_type(p);
-    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16>)
-                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8>)
-                                           : reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_F32>);
+    const void *fn =
+        out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_BF16, AKN, BKN>)
+        : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_FP8, AKN, BKN>)
+                              : reinterpret_cast<const void *>(&fp8_ring_kernel<NS, GROUP_M, GEMM_OUT_F32, AKN, BKN>);
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
                            stream);
 }
 
-template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_F32>(GemmParams, int, int);
-template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_BF16>(GemmParams, int, int);
-template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_FP8>(GemmParams, int, int);
+#define FP8_RING_INSTANCES(AKN, BKN)                                                             \
+    template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_F32, AKN, BKN>(GemmParams, int, int);  \
+    template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_BF16, AKN, BKN>(GemmParams, int, int); \
+    template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_FP8, AKN, BKN>(GemmParams, int, int);
+FP8_RING_INSTANCES(false, false)
+FP8_RING_INSTANCES(false, true)
+FP8_RING_INSTANCES(true, true)
+FP8_RING_INSTANCES(true, false)
 
 }  // namespace
 
@@ -233,6 +294,14 @@ template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_FP8>(GemmParams, int, in
 const KernelDesc kFp8TiledKernels[] = {
     {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_nt_ring4",
      &launch_fp8_ring<4, 4>, 0, nullptr, kLayoutNT, false, kOutAll},
+    // A or B stored the other way (K x M, K x N): its rows, M or N long, are
+    // whole 16-byte chunks too.
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_nn_ring4",
+     &launch_fp8_ring<4, 4, false, true>, 0, nullptr, kLayoutNN, false, kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_tn_ring4",
+     &launch_fp8_ring<4, 4, true, true>, 0, nullptr, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_tt_ring4",
+     &launch_fp8_ring<4, 4, true, false>, 0, nullptr, kLayoutTT, false, kOutAll},
 };
 const int kFp8TiledKernelCount = sizeof(kFp8TiledKernels) / sizeof(kFp8TiledKernels[0]);
 #endif

@@ -78,6 +78,8 @@ WORKLOADS = {
         Workload("fp8f32_16x8192x8192_nt", "fp8f32", 16, 8192, 8192, 1.0, 0.0, "normal", 11, "T"),
         Workload("f32_4096_nt", "f32", 4096, 4096, 4096, 1.0, 0.0, "normal", 12, "T"),
         Workload("f32_4096_tn", "f32", 4096, 4096, 4096, 1.0, 0.0, "normal", 13, "N", "T"),
+        Workload("fp8f32_8192_nn", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 14),
+        Workload("fp8f32_8192_tn", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 15, "N", "T"),
     ]
 }
 
