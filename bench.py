@@ -197,6 +197,7 @@ def main():
     torch.cuda.set_device(dev)
     names = [args.only] if args.only else STEP
 
+    DTYPES = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32, "fp8f32": tg.GEMM_DTYPE_FP8F32}
     # Inputs resident in HBM before timing.
     calls = []
     for name in names:
@@ -206,15 +207,12 @@ def main():
         copies = SKINNY_COPIES if w.M <= 16 else 1
         Bs = [_to_device(B, dev) for _ in range(copies)]
         ws = None
-        if w.dtype == "f32" or (w.dtype == "bf16f32" and w.M <= 16):
-            ws = tg.workspace(w.M, w.N, w.K, device=dev, dtype=tg.GEMM_DTYPE_F32 if w.dtype == "f32" else
-                              tg.GEMM_DTYPE_BF16F32)
+        if w.dtype == "f32" or w.M <= 16:
+            ws = tg.workspace(w.M, w.N, w.K, device=dev, dtype=DTYPES[w.dtype])
         calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []})
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-
-    DTYPES = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32, "fp8f32": tg.GEMM_DTYPE_FP8F32}
 
     def ldb_of(w):
         return w.K if w.op_b == "T" else w.N
@@ -235,7 +233,9 @@ def main():
             e0.record(stream)
         if w.dtype == "fp8f32" or w.op_b == "T" or w.op_a == "T":
             st = tg.gemm_general(DTYPES[w.dtype], *ops_of(w), w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), lda_of(w),
-                                 B.data_ptr(), ldb_of(w), w.beta, c["C"].data_ptr(), w.N, 0, None, 0, 0, sh)
+                                 B.data_ptr(), ldb_of(w), w.beta, c["C"].data_ptr(), w.N, 0, None,
+                                 c["ws"].data_ptr() if c["ws"] is not None else 0,
+                                 c["ws"].numel() if c["ws"] is not None else 0, sh)
         elif c["ws"] is not None:
             fws = tg.gemm_f32_ws if w.dtype == "f32" else tg.gemm_bf16f32_ws
             st = fws(w.M, w.N, w.K, w.alpha, c["A"].data_ptr(), w.K, B.data_ptr(), w.N, w.beta,
