@@ -20,6 +20,10 @@ streams B from HBM rather than from the 256 MB last-level cache, and passes a
 preallocated workspace so the library takes its split-K path (partial sums,
 then a reduce kernel; the event pair brackets both).
 
+``cold`` times each workload again, call by call, after reading a 1 GiB
+buffer that evicts L2 and the last-level cache, and reports the median and
+the minimum (``--cold-calls``; it does not enter ``value``).
+
 ``cpu_baseline`` times the CPU oracle (fp64, OpenMP) on a bounded sample of
 the same step: all 4096 rows of the fp32 problem, the first 4096 rows of the
 bf16 problem and the whole skinny problem.
@@ -62,6 +66,9 @@ def parse():
     ap.add_argument("--observe-clocks", type=float, default=6.0,
                     help="after the timed steps, keep running the step this many seconds while amd-smi samples "
                          "the GFX clocks and socket power (0: off)")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="after the timed steps, time this many calls of each workload one at a time, each "
+                         "after reading a 1 GiB buffer that evicts L2 and the last-level cache (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (a plain kernel of known traffic) so hardware "
                          "byte counters can be scaled against it")
@@ -300,6 +307,8 @@ def main():
                 "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(p["kernel"]),
                 "algorithmic_bytes": w.algorithmic_bytes}
 
+    cold = cold_timings(calls, launch, args.cold_calls, dev) if args.cold_calls > 0 else None
+
     dominant = max(parts, key=lambda n: parts[n]["ms"])
     roof = roofline_of(dominant)
 
@@ -324,10 +333,43 @@ def main():
         "roofline": roof,
         "rooflines": [roofline_of(n) for n in parts],
         "parts": parts,
+        "cold": cold,
         "observed_clocks": observed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def cold_timings(calls, launch, n, dev):
+    """Each workload's calls timed one by one from cold caches: before every
+    call a 1 GiB buffer is read (a sum), which evicts the XCDs' L2 and the
+    256 MB last-level cache with clean lines, so no write-back lands in the
+    timed call.  Median and minimum of the HIP-event times on the launch
+    stream, after 5 untimed calls."""
+    import statistics
+    import torch
+    scrub = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    out = {}
+    for c in calls:
+        w = c["w"]
+        for _ in range(5):
+            launch(c, False)
+        saved, c["durs"] = c["durs"], []
+        for _ in range(n):
+            scrub.sum()
+            launch(c, True)
+        torch.cuda.synchronize()
+        ts = [e0.elapsed_time(e1) for e0, e1 in c["durs"]]
+        c["durs"] = saved
+        med, lo = statistics.median(ts), min(ts)
+        if w.M <= 16:
+            rate, unit, peak = w.algorithmic_bytes / (med * 1e-3) / 1e9, "GB/s", PEAK_HBM_GBS
+        else:
+            rate, unit, peak = w.flops / (med * 1e-3) / 1e12, "TFLOP/s", PEAK_TFLOPS[w.dtype]
+        out[w.name] = {"calls": n, "median_ms": round(med, 5), "min_ms": round(lo, 5), "rate_at_median": round(rate, 2),
+                       "unit": unit, "frac_at_median": round(rate / peak, 4)}
+    del scrub
+    return out
 
 
 def cpu_baseline(calls):
