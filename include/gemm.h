@@ -360,28 +360,40 @@ GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op
  * gemm_autotune() times, on the caller's buffers and stream, every kernel
  * that can run this call (reps calls each after one untimed call, with and
  * without a K split when a workspace is given) and records the fastest in a
- * process-wide table keyed by dtype, M, N, K, the operands' widest vector
- * width and whether a workspace is passed.  It blocks until the timings are
+ * process-wide table keyed by dtype, layout (op_a, op_b), M, N, K, the
+ * operands' widest vector width and whether a workspace is passed.  It
+ * blocks until the timings are
  * done.  C is used as scratch: its contents afterwards are unspecified (with
  * beta != 0 every timed call updates it), so make the real call afterwards.
  * `out` receives the plan that calls of this kind now take.  reps: 1..1000.
  * Later calls with no forced kernel (and gemm_plan_query) use a recorded
  * choice whenever it can run the call; otherwise the built-in rules choose.
- * Tuning covers untransposed operands; gemm_general calls with a transposed
- * operand always take the built-in rules.
+ * gemm_autotune() tunes untransposed operands; gemm_autotune_general()
+ * takes any operand type and layout with the arguments of gemm_general()
+ * (op_a, op_b as there), and its entries steer gemm_general() calls of the
+ * same kind.
  * The table is guarded by a mutex; autotuning concurrently with calls on
  * other threads is safe, though the timings then include their load.
  *
  * gemm_tuning_save() writes the table as text, one line per entry, naming
- * kernels (not ids); gemm_tuning_load() adds the entries of such a file
- * (entries naming unknown kernels are skipped) and returns how many it
- * added, or -1 if the file cannot be read or parsed.
+ * kernels (not ids): "dtype op_a op_b M N K vec_a vec_b has_ws kernel split
+ * ms" under a "# libgemm tuning table v2" header.  gemm_tuning_load() adds
+ * the entries of such a file (entries naming unknown kernels, or kernels
+ * for another operand type or layout, are skipped) and returns how many it
+ * added, or -1 if the file cannot be read or parsed.  Files without the v2
+ * header are read in the earlier format, without op_a op_b, as untransposed
+ * entries.
  */
 GEMM_API gemm_status gemm_autotune(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
                                    const void *A, int64_t lda, const void *B, int64_t ldb,
                                    float beta, float *C, int64_t ldc,
                                    void *workspace, int64_t workspace_bytes, int32_t reps,
                                    gemm_stream_t stream, gemm_plan *out);
+GEMM_API gemm_status gemm_autotune_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                           int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                           int64_t ldb, float beta, float *C, int64_t ldc, void *workspace,
+                                           int64_t workspace_bytes, int32_t reps, gemm_stream_t stream,
+                                           gemm_plan *out);
 GEMM_API int32_t gemm_tuning_count(void);
 GEMM_API void gemm_tuning_clear(void);
 GEMM_API gemm_status gemm_tuning_save(const char *path);

@@ -89,6 +89,13 @@ int main(void)
     CHECK(gemm_workspace_size(GEMM_DTYPE_F32, 4096, 4096, 4096) == 0, "no workspace for a full wave");
     CHECK(strcmp(gemm_status_string(GEMM_OK), "success") == 0, "status string");
     CHECK(gemm_tuning_count() >= 0, "tuning count");
+    {
+        gemm_plan pl;
+        CHECK(gemm_autotune_general(GEMM_DTYPE_FP8F32, GEMM_OP_N, GEMM_OP_T, 64, 64, 64, 1.0f, A, 64, B, 64, 0.0f, C,
+                                    64, NULL, 0, 0, NULL, &pl) == GEMM_ERR_INVALID_ARG, "autotune reps 0");
+        CHECK(gemm_autotune_general(GEMM_DTYPE_FP8F32, GEMM_OP_N, 2, 64, 64, 64, 1.0f, A, 64, B, 64, 0.0f, C, 64,
+                                    NULL, 0, 5, NULL, &pl) == GEMM_ERR_INVALID_ARG, "autotune bad op");
+    }
 
     printf("OK %d\n", checks);
     return 0;

@@ -356,12 +356,47 @@ def test_tuning_table_load_save_and_plan(tmp_path):
     out = tmp_path / "saved.txt"
     assert tg.gemm_tuning_save(str(out)) == OK
     lines = [l for l in out.read_text().splitlines() if not l.startswith("#")]
-    assert len(lines) == 2 and all(len(l.split()) == 10 for l in lines)
+    assert out.read_text().startswith("# libgemm tuning table v2")
+    assert len(lines) == 2 and all(len(l.split()) == 12 and l.split()[1:3] == ["0", "0"] for l in lines)
     tg.gemm_tuning_clear()
     assert tg.gemm_tuning_count() == 0
     assert tg.gemm_tuning_load(str(out)) == 2
     assert plan(F32, 1024, 1024, 1024)[1]["kernel_id"] == _kid("f32_mfma32_128x128x16_w2x2_a4b4")
     tg.gemm_tuning_clear()
+
+
+def test_tuning_table_layouts(tmp_path):
+    """Format v2 keys entries by layout as well: an entry for A x B^T steers
+    gemm_general calls of that layout only; entries naming a kernel without
+    that layout are skipped; op values other than N/T make the file invalid."""
+    tg.gemm_tuning_clear()
+    f = tmp_path / "v2.txt"
+    f.write_text("# libgemm tuning table v2: dtype op_a op_b M N K vec_a vec_b has_ws kernel split ms\n"
+                 "1 0 1 4096 4096 4096 8 8 0 bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4 0 0.2\n"
+                 "2 1 0 2048 2048 2048 16 16 0 fp8_general_128x128x16 0 0.3\n"
+                 "1 1 1 4096 4096 4096 8 8 0 bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4 0 0.2\n")
+    assert tg.gemm_tuning_load(str(f)) == 2          # the NT ring cannot run T x T: skipped
+    # Untuned built-in choice for the same shape in another layout.
+    base_tn = gplan(BF16, T_, N_, 4096, 4096, 4096)[1]["kernel_id"]
+    nt = _kid("bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4")
+    assert gplan(BF16, N_, T_, 4096, 4096, 4096)[1]["kernel_id"] == nt
+    assert gplan(BF16, T_, N_, 4096, 4096, 4096)[1]["kernel_id"] == base_tn != nt
+    # The fp8 entry overrides the ring for A stored K x M, and for no other layout.
+    gen = _kid("fp8_general_128x128x16")
+    assert gplan(FP8, T_, N_, 2048, 2048, 2048)[1]["kernel_id"] == gen
+    assert gplan(FP8, N_, N_, 2048, 2048, 2048)[1]["kernel_id"] != gen
+    out = tmp_path / "saved.txt"
+    assert tg.gemm_tuning_save(str(out)) == OK
+    tg.gemm_tuning_clear()
+    assert tg.gemm_tuning_load(str(out)) == 2
+    assert gplan(FP8, T_, N_, 2048, 2048, 2048)[1]["kernel_id"] == gen
+    tg.gemm_tuning_clear()
+    bad = tmp_path / "bad_op.txt"
+    bad.write_text("# libgemm tuning table v2\n2 2 0 64 64 64 16 16 0 fp8_general_128x128x16 0 0.3\n")
+    assert tg.gemm_tuning_load(str(bad)) == -1 and tg.gemm_tuning_count() == 0
+    # A v1 line under a v2 header has too few fields.
+    bad.write_text("# libgemm tuning table v2\n0 1024 1024 1024 4 4 0 f32_mfma32_128x128x16_w2x2_a4b4 0 0.5\n")
+    assert tg.gemm_tuning_load(str(bad)) == -1
 
 
 def test_tuning_table_entry_that_cannot_run_is_ignored(tmp_path):
@@ -391,6 +426,14 @@ def test_tuning_load_errors(tmp_path):
     assert st == tg.GEMM_ERR_INVALID_ARG
     st, p = tg.gemm_autotune(F32, 0, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 5)
     assert st == OK and p["path"] == tg.GEMM_PATH_NONE   # nothing to tune, no device needed
+    st, _ = tg.gemm_autotune_general(FP8, N_, T_, 64, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 0)
+    assert st == tg.GEMM_ERR_INVALID_ARG
+    st, _ = tg.gemm_autotune_general(FP8, N_, 2, 64, 64, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 64, 0, 0, 5)
+    assert st == tg.GEMM_ERR_INVALID_ARG
+    st, _ = tg.gemm_autotune_general(FP8, T_, N_, 64, 64, 64, 1.0, PA, 32, PB, 64, 0.0, PC, 64, 0, 0, 5)
+    assert st == tg.GEMM_ERR_INVALID_ARG                 # A stored K x M needs lda >= M
+    st, p = tg.gemm_autotune_general(BF16, T_, T_, 64, 0, 64, 1.0, PA, 64, PB, 64, 0.0, PC, 1, 0, 0, 5)
+    assert st == OK and p["path"] == tg.GEMM_PATH_NONE
 
 
 # ----------------------------------------------------------------------------- operand layouts and fp8

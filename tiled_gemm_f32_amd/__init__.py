@@ -16,15 +16,16 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
     GEMM_ERR_LAUNCH, GEMM_ERR_UNSUPPORTED, GEMM_OK, GEMM_PATH_NONE, GEMM_PATH_SCALE,
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
     gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
-    gemm_plan_query, gemm_status_string, gemm_workspace_size, gemm_autotune, gemm_tuning_count, gemm_tuning_clear,
-    gemm_tuning_save, gemm_tuning_load, load)
+    gemm_plan_query, gemm_status_string, gemm_workspace_size, gemm_autotune, gemm_autotune_general, gemm_tuning_count,
+    gemm_tuning_clear, gemm_tuning_save, gemm_tuning_load, load)
 
 __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
            "gemm_f32_epi", "gemm_bf16f32_epi", "Epilogue", "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU",
            "GEMM_OUT_F32", "GEMM_OUT_BF16", "GEMM_OUT_FP8", "gemm_plan_query_epi",
            "gemm_general", "gemm_plan_query_general", "GEMM_DTYPE_FP8F32", "GEMM_OP_N", "GEMM_OP_T",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
-           "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune", "gemm_tuning_count",
+           "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune",
+           "gemm_autotune_general", "gemm_tuning_count",
            "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load"]
 
 
@@ -141,19 +142,24 @@ def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, kernel: int = 0, s
     return out if out is not None else C
 
 
-def autotune(A, B, C, alpha: float = 1.0, beta: float = 0.0, ws=None, reps: int = 5, stream=None) -> dict:
+def autotune(A, B, C, alpha: float = 1.0, beta: float = 0.0, ws=None, reps: int = 5, stream=None,
+             op_a: str = "N", op_b: str = "N") -> dict:
     """Time every kernel that can run this call and record the fastest for
-    calls of the same kind; returns the plan they now take.  C is scratch."""
+    calls of the same kind; returns the plan they now take.  C is scratch.
+    Operands and ``op_a``/``op_b`` are as in ``gemm``."""
     import torch
-    M, K = A.shape
-    N = B.shape[1]
+    if op_a not in ("N", "T") or op_b not in ("N", "T"):
+        raise ValueError("op_a and op_b are 'N' or 'T'")
+    M, K = A.shape if op_a == "N" else (A.shape[1], A.shape[0])
+    N = B.shape[1] if op_b == "N" else B.shape[0]
     dt = _dtype_of(A)
     wp, wb = (ws.data_ptr(), ws.numel() * ws.element_size()) if ws is not None else (0, 0)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
+    ops = (GEMM_OP_N if op_a == "N" else GEMM_OP_T, GEMM_OP_N if op_b == "N" else GEMM_OP_T)
     with torch.cuda.device(A.device):
-        st, pl = gemm_autotune(dt, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"),
-                               float(beta), C.data_ptr(), _ld(C, "C"), wp, wb, reps, stream)
+        st, pl = gemm_autotune_general(dt, *ops, M, N, K, float(alpha), A.data_ptr(), _ld(A, "A"), B.data_ptr(),
+                                       _ld(B, "B"), float(beta), C.data_ptr(), _ld(C, "C"), wp, wb, reps, stream)
     if st != GEMM_OK:
         raise GemmError(st, "autotune")
     return pl

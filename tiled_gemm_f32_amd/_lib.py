@@ -46,7 +46,7 @@ EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
             "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws", "gemm_autotune", "gemm_tuning_count",
             "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_f32_epi", "gemm_bf16f32_epi",
-            "gemm_general", "gemm_plan_query_general", "gemm_plan_query_epi")
+            "gemm_general", "gemm_plan_query_general", "gemm_plan_query_epi", "gemm_autotune_general")
 
 
 class KernelInfo(ctypes.Structure):
@@ -134,6 +134,9 @@ def load() -> ctypes.CDLL:
     lib.gemm_autotune.argtypes = [i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp, i64, i32, vp,
                                   ctypes.POINTER(Plan)]
     lib.gemm_autotune.restype = ctypes.c_int
+    lib.gemm_autotune_general.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp, i64,
+                                          i32, vp, ctypes.POINTER(Plan)]
+    lib.gemm_autotune_general.restype = ctypes.c_int
     lib.gemm_tuning_count.argtypes = []
     lib.gemm_tuning_count.restype = i32
     lib.gemm_tuning_clear.argtypes = []
@@ -247,6 +250,15 @@ def gemm_autotune(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace
     pl = Plan()
     st = load().gemm_autotune(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, reps,
                               stream, ctypes.byref(pl))
+    return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
+
+
+def gemm_autotune_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=0,
+                          workspace_bytes=0, reps=5, stream=0):
+    """gemm_autotune for any operand type and layout (op_a, op_b as in gemm_general)."""
+    pl = Plan()
+    st = load().gemm_autotune_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                      workspace_bytes, reps, stream, ctypes.byref(pl))
     return st, {f: getattr(pl, f) for f, _ in Plan._fields_}
 
 

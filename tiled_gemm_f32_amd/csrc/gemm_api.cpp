@@ -359,17 +359,18 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand) {
 // Per-shape tuning ("A GEMM Kernel, Step by Step", "Six parameters, found by
 // search": the best kernel for a shape is found by timing the candidates).
 // gemm_autotune() times every kernel that can run a call, with and without a
-// K split, and records the fastest here; calls of the same dtype, shape,
-// operand alignment class and workspace presence then take that choice
-// whenever it still fits the call.
+// K split, and records the fastest here; calls of the same operand type,
+// layout, shape, operand alignment class and workspace presence then take
+// that choice whenever it still fits the call.
 struct TuneKey {
     int32_t dtype;
+    int32_t op_a, op_b;      // GEMM_OP_N or GEMM_OP_T
     int64_t M, N, K;
     int32_t vec_a, vec_b;    // widest vector loads A and B allow
     int32_t has_ws;
     bool operator<(const TuneKey &o) const {
-        return std::tie(dtype, M, N, K, vec_a, vec_b, has_ws) <
-               std::tie(o.dtype, o.M, o.N, o.K, o.vec_a, o.vec_b, o.has_ws);
+        return std::tie(dtype, op_a, op_b, M, N, K, vec_a, vec_b, has_ws) <
+               std::tie(o.dtype, o.op_a, o.op_b, o.M, o.N, o.K, o.vec_a, o.vec_b, o.has_ws);
     }
 };
 struct TuneEntry {
@@ -386,12 +387,11 @@ int max_vec_b(const Call &c) {
 }
 
 TuneKey tune_key(const Call &c) {
-    return TuneKey{c.dtype, c.M, c.N, c.K, max_vec_a(c), max_vec_b(c), c.ws != nullptr ? 1 : 0};
+    return TuneKey{c.dtype, c.op_a, c.op_b, c.M, c.N, c.K, max_vec_a(c), max_vec_b(c), c.ws != nullptr ? 1 : 0};
 }
 
 // A tuned choice for this call, if one was recorded and still fits it.
 bool tuned_choice(const Call &c, const KernelDesc **kd, bool *allow_split) {
-    if (c.op_a != GEMM_OP_N || c.op_b != GEMM_OP_N) return false;     // tuning covers untransposed operands
     std::lock_guard<std::mutex> lock(g_tune_mu);
     auto it = g_tuned.find(tune_key(c));
     if (it == g_tuned.end()) return false;
@@ -806,6 +806,17 @@ GEMM_API gemm_status gemm_autotune(int32_t dtype, int64_t M, int64_t N, int64_t 
                     reps, static_cast<hipStream_t>(stream), out);
 }
 
+GEMM_API gemm_status gemm_autotune_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                           int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                           int64_t ldb, float beta, float *C, int64_t ldc, void *workspace,
+                                           int64_t workspace_bytes, int32_t reps, gemm_stream_t stream,
+                                           gemm_plan *out) {
+    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes);
+    c.op_a = op_a;
+    c.op_b = op_b;
+    return autotune(c, reps, static_cast<hipStream_t>(stream), out);
+}
+
 GEMM_API int32_t gemm_tuning_count(void) {
     std::lock_guard<std::mutex> lock(g_tune_mu);
     return (int32_t)g_tuned.size();
@@ -816,21 +827,24 @@ GEMM_API void gemm_tuning_clear(void) {
     g_tuned.clear();
 }
 
-// One line per entry: dtype M N K vec_a vec_b has_workspace kernel_name split ms.
-// Kernels are named, not numbered, so a table survives a reordered kernel list.
+// One line per entry: dtype op_a op_b M N K vec_a vec_b has_workspace
+// kernel_name split ms (format v2; v1 files, written before layouts were
+// tuned, lack op_a op_b and load as untransposed entries).  Kernels are
+// named, not numbered, so a table survives a reordered kernel list.
 GEMM_API gemm_status gemm_tuning_save(const char *path) {
     if (path == nullptr) return GEMM_ERR_INVALID_ARG;
     std::FILE *f = std::fopen(path, "w");
     if (f == nullptr) return GEMM_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> lock(g_tune_mu);
-    bool ok = std::fprintf(f, "# libgemm tuning table v1: dtype M N K vec_a vec_b has_ws kernel split ms\n") > 0;
+    bool ok =
+        std::fprintf(f, "# libgemm tuning table v2: dtype op_a op_b M N K vec_a vec_b has_ws kernel split ms\n") > 0;
     for (const auto &kv : g_tuned) {
         const TuneKey &k = kv.first;
         const KernelDesc *kd = kernel_by_id(kv.second.kernel_id);
         ok = ok && kd != nullptr &&
-             std::fprintf(f, "%d %lld %lld %lld %d %d %d %s %d %.6f\n", k.dtype, (long long)k.M, (long long)k.N,
-                          (long long)k.K, k.vec_a, k.vec_b, k.has_ws, kd->name, kv.second.split,
-                          (double)kv.second.ms) > 0;
+             std::fprintf(f, "%d %d %d %lld %lld %lld %d %d %d %s %d %.6f\n", k.dtype, k.op_a, k.op_b,
+                          (long long)k.M, (long long)k.N, (long long)k.K, k.vec_a, k.vec_b, k.has_ws, kd->name,
+                          kv.second.split, (double)kv.second.ms) > 0;
     }
     ok = (std::fclose(f) == 0) && ok;
     return ok ? GEMM_OK : GEMM_ERR_INVALID_ARG;
@@ -843,15 +857,23 @@ GEMM_API int32_t gemm_tuning_load(const char *path) {
     std::vector<std::pair<TuneKey, TuneEntry>> rows;
     char line[512];
     bool ok = true;
+    bool v2 = false;
     while (ok && std::fgets(line, sizeof line, f) != nullptr) {
+        if (std::strncmp(line, "# libgemm tuning table v2", 25) == 0) v2 = true;
         if (line[0] == '#' || line[0] == '\n') continue;
         TuneKey k;
         long long M, N, K;
         char name[128];
         int split;
         double ms;
-        if (std::sscanf(line, "%d %lld %lld %lld %d %d %d %127s %d %lf", &k.dtype, &M, &N, &K, &k.vec_a, &k.vec_b,
-                        &k.has_ws, name, &split, &ms) != 10) {
+        k.op_a = k.op_b = GEMM_OP_N;
+        const int got =
+            v2 ? std::sscanf(line, "%d %d %d %lld %lld %lld %d %d %d %127s %d %lf", &k.dtype, &k.op_a, &k.op_b, &M,
+                             &N, &K, &k.vec_a, &k.vec_b, &k.has_ws, name, &split, &ms)
+               : std::sscanf(line, "%d %lld %lld %lld %d %d %d %127s %d %lf", &k.dtype, &M, &N, &K, &k.vec_a,
+                             &k.vec_b, &k.has_ws, name, &split, &ms);
+        if (got != (v2 ? 12 : 10) || (k.op_a != GEMM_OP_N && k.op_a != GEMM_OP_T) ||
+            (k.op_b != GEMM_OP_N && k.op_b != GEMM_OP_T)) {
             ok = false;
             break;
         }
@@ -861,7 +883,10 @@ GEMM_API int32_t gemm_tuning_load(const char *path) {
         int32_t id = 0;
         for (int32_t i = 1; i <= table_size(); ++i)
             if (std::strcmp(kernel_by_id(i)->name, name) == 0) id = i;
-        if (id == 0 || kernel_by_id(id)->dtype != k.dtype) continue;     // unknown or mismatched kernel: skip
+        // An unknown kernel, or one for another operand type or layout: skip.
+        if (id == 0 || kernel_by_id(id)->dtype != k.dtype ||
+            ((kernel_by_id(id)->layouts >> (2 * k.op_a + k.op_b)) & 1) == 0)
+            continue;
         rows.push_back({k, TuneEntry{id, split != 0 ? 1 : 0, (float)ms}});
     }
     std::fclose(f);
