@@ -631,6 +631,30 @@ def test_skinny_nt_choice(dtype, prefix, chunk):
     assert st == OK and "skinny_nt" not in kname(pl)
 
 
+def test_skinny_a_transposed_choice():
+    """fp32 with A stored K x M and M <= 16: the streaming kernels that read
+    A transposed, split over K when a workspace is passed; never for other
+    layouts, M = 17, or K rows of A beyond 2^31 bytes."""
+    for M in (1, 16):
+        st, pl = gplan(F32, T_, N_, M, 8192, 8192)
+        assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4" and pl["grid"] == 256, pl
+    st, pl = gplan(F32, T_, N_, 16, 8192, 8192, ws=tg.gemm_workspace_size(F32, 16, 8192, 8192))
+    assert st == OK and kname(pl) == "f32_skinny_splitk_n128_at_w8_u1" and pl["grid"] == 256, pl
+    assert "_at_" not in kname(plan(F32, 16, 8192, 8192)[1])
+    assert "_at_" not in kname(gplan(F32, T_, N_, 17, 8192, 8192)[1])
+    assert "_at_" not in kname(gplan(F32, T_, T_, 16, 8192, 8192)[1])
+    assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192)[1])
+    K = 1 << 20
+    st, pl = gplan(F32, T_, N_, 16, 64, K, lda=(1 << 9) - 4)       # K * lda * 4 < 2^31
+    assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4", pl
+    st, pl = gplan(F32, T_, N_, 16, 64, K, lda=1 << 9)             # = 2^31
+    assert st == OK and "_at_" not in kname(pl), pl
+    # Forced on untransposed A they refuse, as the untransposed ones do here.
+    for n in ("f32_skinny_mfma16_n2_at_w8_u4", "f32_skinny_splitk_n128_at_w8_u1"):
+        assert plan(F32, 16, 8192, 8192, force=_kid(n), ws=1 << 30)[0] == UNSUP
+    assert gplan(F32, T_, N_, 16, 8192, 8192, force=_kid("f32_skinny_mfma16_n2_a4_w8_u4"))[0] == UNSUP
+
+
 def test_skinny_nt_largest_leading_dimension():
     # Leading dimensions stop at 2^21 - 1 elements, so 32 rows of B^T (and 16
     # of A) stay below 2^31 bytes and the kernel's 32-bit offsets always fit.

@@ -262,3 +262,55 @@ def test_fp8_ring_deterministic_and_bench_shape_sampled(gpu_available):
     zero = torch.zeros(len(rows), n)
     check(C[rows], A[rows], Bt, zero, 1.0, 0.0, "N", "T", "fp8f32")
     check(C[:, cols], A, Bt[cols].contiguous(), torch.zeros(n, len(cols)), 1.0, 0.0, "N", "T", "fp8f32")
+
+
+# ----------------------------------------------------------------------------- decode with A stored K x M
+
+F32_AT_SKINNY = ["f32_skinny_mfma16_n2_at_w8_u4", "f32_skinny_splitk_n128_at_w8_u1"]
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+@pytest.mark.parametrize("NK", [(8192, 4096), (1000, 777), (40, 12288)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_skinny_a_transposed_exact(gpu_available, M, NK):
+    """fp32, M <= 16, A stored K x M: both streaming kernels forced, and the
+    library's choice with and without a workspace, bit-exact on integer data
+    with bias and ReLU; A's leading dimension padded past M once."""
+    N, K = NK
+    A, B, C0 = make_integer_inputs(M, N, K, seed=760 + M, dtype="f32")
+    As = A.t().contiguous()
+    bias = make_bias(N, seed=761, integer=True)
+    ref = oracle.gemm_epilogue_ref(host_view(As), host_view(B), 2.0, -1.0, C0.numpy(), bias.numpy(), "relu", "T", "N")
+    ws = tg.workspace(M, N, K, dtype=tg.GEMM_DTYPE_F32)
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    runs = [(n, ids[n], ws, (0, 0, 0)) for n in F32_AT_SKINNY] + [("auto", 0, None, (0, 0, 0)),
+                                                                   ("auto ws", 0, ws, (0, 0, 0)),
+                                                                   ("auto ws lda+5", 0, ws, (5, 0, 0))]
+    for name, kid, w, pad in runs:
+        say(f"[A^T skinny] {name} M={M} N={N} K={K} pad={pad[0]} seed={760 + M}")
+        C, _, _ = run_gemm(As, B, C0, 2.0, -1.0, kernel=kid, ws=w, bias=bias, activation="relu", op_a="T",
+                           pad=pad)
+        np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
+    st, pl = tg.gemm_plan_query_general(tg.GEMM_DTYPE_F32, 1, 0, M, N, K, 1.0, 0x1000, M, 0x1000, N, 0.0, 0x1000, N,
+                                        0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] in F32_AT_SKINNY
+
+
+@pytest.mark.parametrize("with_ws", [False, True], ids=["no_ws", "ws"])
+def test_skinny_a_transposed_random_full_size(gpu_available, with_ws):
+    """16 x 8192 x 8192 with A stored K x M on U[-1,1] data (the decode
+    workload's distribution): the fp32 error ratio, and the same bits as
+    the call with A stored M x K on the same values."""
+    M, N, K = 16, 8192, 8192
+    A, B, C0 = make_random_inputs(M, N, K, seed=3, dist="uniform")
+    As = A.t().contiguous()
+    ws = tg.workspace(M, N, K, dtype=tg.GEMM_DTYPE_F32) if with_ws else None
+    say(f"[A^T skinny] auto M={M} N={N} K={K} uniform seed=3 ws={with_ws}")
+    C, _, _ = run_gemm(As, B, C0, 1.0, 0.0, ws=ws, op_a="T")
+    ref = oracle.gemm_ref(host_view(As), host_view(B), 1.0, 0.0, C0.numpy(), "T", "N")
+    D = oracle.gemm_absbound(host_view(As), host_view(B), 1.0, 0.0, C0.numpy(), "T", "N")
+    r = oracle.error_ratio(C, ref, D)
+    say(f"[A^T skinny] ratio {r:.3e}")
+    assert r <= TOL["f32"]
+    # Same k pairing and summation order as the untransposed kernel of the same shape.
+    C2, _, _ = run_gemm(A, B, C0, 1.0, 0.0, ws=ws)
+    np.testing.assert_array_equal(C, C2)

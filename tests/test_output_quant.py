@@ -75,7 +75,7 @@ def runnable(dtype, kind, op_a, op_b, M, N, K, kid, ws_bytes):
     return st == tg.GEMM_OK
 
 
-LAYOUTS = {"f32": [("N", "N"), ("N", "T")], "bf16f32": [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")],
+LAYOUTS = {"f32": [("N", "N"), ("N", "T"), ("T", "N")], "bf16f32": [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")],
            "fp8f32": [("N", "T"), ("N", "N"), ("T", "N"), ("T", "T")]}
 
 

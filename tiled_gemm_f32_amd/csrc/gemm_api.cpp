@@ -142,10 +142,13 @@ bool vec_b_ok(const Call &c, int v) { return vec_ok(c.B, c.ldb, row_len_b(c), el
 // The skinny kernels address B with 32-bit offsets.  With B stored K x N
 // their prefetch runs at most 48 * WAVES * UNROLL (<= 1536) rows past K, so
 // K + 2048 rows must fit.  With B stored N x K a workgroup's 32 rows of B
-// and the 16 rows of A, each K long, must fit.
+// and the 16 rows of A, each K long, must fit; with A stored K x M, its K
+// rows.
 bool skinny_fits(const Call &c) {
     if (c.M > 16) return false;
     const int64_t lim = int64_t(1) << 31;
+    // A stored K x M is addressed row by row: K rows of lda elements.
+    if (c.op_a == GEMM_OP_T && c.K * c.lda * elem_size(c.dtype) >= lim) return false;
     if (c.op_b == GEMM_OP_T) {
         const int64_t esz = elem_size(c.dtype);
         return (32 * c.ldb + c.K) * esz < lim && (16 * c.lda + c.K) * esz < lim;
@@ -286,12 +289,15 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand);
 // the call.
 const KernelDesc *choose(const Call &c) {
     const bool plain = c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_N;
-    // The split-K kernels pay off only where K is actually split.
-    if (plain && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c) && c.ws != nullptr) {
+    // fp32 with B stored K x N: the streaming kernels, for A stored either
+    // way (the table's layouts pick the A load).  The split-K kernels pay
+    // off only where K is actually split.
+    const bool b_kn = c.op_b == GEMM_OP_N;
+    if (b_kn && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c) && c.ws != nullptr) {
         const KernelDesc *kd = first_match(gemm::kF32SplitKernels, gemm::kF32SplitKernelCount, c, 0);
         if (kd != nullptr && split_workspace_bytes(c, kd) > 0) return kd;
     }
-    if (plain && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
+    if (b_kn && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kF32SkinnyKernels, gemm::kF32SkinnyKernelCount, c, 0))
             return kd;
     }

@@ -15,7 +15,10 @@
 //   * v_mfma_f32_16x16x4_f32 takes the 16 rows of A (lane row l%16, k row
 //     l/16) against 16 columns of B; VEC instructions cover the lane's VEC
 //     columns, column c of instruction j being strip column VEC*c + j.
-//     Rows of A at or past M read as zero.
+//     Rows of A at or past M read as zero.  A may also be stored K x M
+//     (transposed): its values then come from 4-byte loads of 4 rows of
+//     the stored matrix.  A is 16 x K at most and is re-read from L2 by
+//     every strip, so the narrower loads cost little next to B.
 //   * The waves' partial 16 x (16*VEC) tiles are summed through LDS in a
 //     fixed wave order (deterministic; no atomics) and the alpha/beta
 //     epilogue is applied once per output.
@@ -69,6 +72,28 @@ template <> struct AVec<1> {
     }
 };
 
+// The lane's A values of k block b: row lc, k = 16*b + 4*kq .. +3.  VA = 4
+// or 1: A stored M x K (one 16-byte load, or four 4-byte ones, from
+// a_base + 64*b).  VA = 0: A stored K x M (lda >= M), so the four k are
+// four rows of the stored matrix and each value is one 4-byte load of
+// column lc; a wave instruction reads 4 runs of 16 consecutive floats.
+// Columns at or past M and k at or past K read as zero.
+template <int VA>
+__device__ __forceinline__ f32x4 load_a_quad(rsrc_t r, uint32_t a_base, int b, int kq, int lc, int K, int M,
+                                             int lda) {
+    const int k = 16 * b + 4 * kq;
+    if constexpr (VA == 0) {
+        f32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = __builtin_bit_cast(
+                float, load_b32(r, lc < M && k + j < K ? (uint32_t)((k + j) * lda + lc) * 4u : kOutOfRange));
+        return v;
+    } else {
+        return AVec<VA>::load(r, a_base + (uint32_t)b * 64u, k, K);
+    }
+}
+
 // One workgroup per 16*VEC-column strip of C.  K is cut into 16-deep blocks,
 // dealt round-robin to the waves.  Inside a block, lane group kq = lane/16
 // owns k = 4*kq .. 4*kq+3 (one 16-byte load of its A row), and MFMA j of the
@@ -92,7 +117,7 @@ f32_skinny_kernel(GemmParams p) {
     // extents and read as zero.  The prefetch reaches at most 48*WAVES*UNROLL
     // rows past K and the host guarantees (K + 2048) * ldb * 4 < 2^31 on this
     // path, so no offset below wraps.
-    const rsrc_t ra = make_rsrc(p.A, clamp_extent(((int64_t)(M - 1) * lda + K) * 4));
+    const rsrc_t ra = make_rsrc(p.A, clamp_extent((VA == 0 ? (int64_t)(K - 1) * lda + M : (int64_t)(M - 1) * lda + K) * 4));
     const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + n0,
                                 clamp_extent(((int64_t)(K - 1) * ldb + (N - n0)) * 4));
     const uint32_t a_base = (uint32_t)(lc * lda + 4 * kq) * 4u;
@@ -109,7 +134,7 @@ f32_skinny_kernel(GemmParams p) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int b = blk0 + u * WAVES;
-            av[set][u] = AVec<VA>::load(ra, a_base + (uint32_t)b * 64u, 16 * b + 4 * kq, K);
+            av[set][u] = load_a_quad<VA>(ra, a_base, b, kq, lc, K, M, lda);
 #pragma unroll
             for (int j = 0; j < 4; ++j) bv[set][u][j] = BVec<VEC>::load(rb, b_base + (uint32_t)(16 * b + j) * b_row);
         }
@@ -182,8 +207,10 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
     const int kq = lane >> 4, lc = lane & 15;
 
     // Extents end at this split's last row, so prefetch past kend reads zeros.
-    const rsrc_t ra = make_rsrc(static_cast<const float *>(p.A) + kbeg,
-                                clamp_extent(((int64_t)(M - 1) * lda + (kend - kbeg)) * 4));
+    const rsrc_t ra = VA == 0 ? make_rsrc(static_cast<const float *>(p.A) + (int64_t)kbeg * lda,
+                                          clamp_extent(((int64_t)(kend - kbeg - 1) * lda + M) * 4))
+                              : make_rsrc(static_cast<const float *>(p.A) + kbeg,
+                                          clamp_extent(((int64_t)(M - 1) * lda + (kend - kbeg)) * 4));
     const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + (int64_t)kbeg * ldb + n0,
                                 clamp_extent(((int64_t)(kend - kbeg - 1) * ldb + (N - n0)) * 4));
     const uint32_t a_base = (uint32_t)(lc * lda + 4 * kq) * 4u;
@@ -203,7 +230,7 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int b = blk0 + u * WAVES;
-            av[set][u] = AVec<VA>::load(ra, a_base + (uint32_t)b * 64u, 16 * b + 4 * kq, kspan);
+            av[set][u] = load_a_quad<VA>(ra, a_base, b, kq, lc, kspan, M, lda);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -353,6 +380,8 @@ scale_c_kernel(GemmParams p) {
 
 template __global__ void f32_skinny_splitk_kernel<2, 4, 8, 1>(GemmParams, float *, int, int);
 template __global__ void f32_skinny_splitk_kernel<2, 1, 8, 1>(GemmParams, float *, int, int);
+template __global__ void f32_skinny_splitk_kernel<2, 0, 8, 1>(GemmParams, float *, int, int);
+template __global__ void f32_skinny_kernel<2, 0, 8, 4>(GemmParams);
 
 // Explicit instantiations: the device pass never sees the host-only table.
 #define SKINNY_INSTANTIATE(VEC, VA, WAVES, UNROLL) \
@@ -367,7 +396,13 @@ SKINNY_LIST(SKINNY_INSTANTIATE)
 // N = 8192, where 4-wide strips would leave half the chip idle; 8 waves with
 // 4 blocks per batch measured fastest on the 16 x 8192 x 8192 shape.
 #define SKINNY_ENTRY(VEC, VA, WAVES, UNROLL) F32_SKINNY(VEC, VA, WAVES, UNROLL),
-const KernelDesc kF32SkinnyKernels[] = {SKINNY_LIST(SKINNY_ENTRY)};
+// The last entry reads A stored K x M (A transposed), with the 2-wide B
+// loads and batches of the first.
+const KernelDesc kF32SkinnyKernels[] = {
+    SKINNY_LIST(SKINNY_ENTRY)
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 32, 16 * 8 * 4, 512, 1, 2, "f32_skinny_mfma16_n2_at_w8_u4",
+     &launch_f32_skinny<2, 0, 8, 4>, 0, nullptr, kLayoutTN, false, kOutAll},
+};
 const int kF32SkinnyKernelCount = sizeof(kF32SkinnyKernels) / sizeof(kF32SkinnyKernels[0]);
 
 // Split-K skinny kernels (need the caller's workspace).  tile_n is the strip
@@ -377,6 +412,8 @@ const KernelDesc kF32SplitKernels[] = {
      nullptr, 0, &launch_f32_skinny_splitk<2, 4, 8, 1>, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 1, 512, 1, 4, "f32_skinny_splitk_n128_a1_w8_u1",
      nullptr, 0, &launch_f32_skinny_splitk<2, 1, 8, 1>, kLayoutNN, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, 128, 16 * 8 * 1, 512, 1, 4, "f32_skinny_splitk_n128_at_w8_u1",
+     nullptr, 0, &launch_f32_skinny_splitk<2, 0, 8, 1>, kLayoutTN, false, kOutAll},
 };
 const int kF32SplitKernelCount = sizeof(kF32SplitKernels) / sizeof(kF32SplitKernels[0]);
 
