@@ -172,8 +172,9 @@ def test_skinny_path_for_m_up_to_16():
         assert st == OK and p["path"] == tg.GEMM_PATH_SKINNY and p["tile_m"] == 16
     st, p = plan(F32, 17, 8192, 8192)
     assert p["path"] == tg.GEMM_PATH_TILED
-    # bf16 has no skinny kernel: small M goes through the tiled kernel.
-    assert plan(BF16, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
+    # bf16 without a workspace: its streaming kernel over the whole of K.
+    assert plan(BF16, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_SKINNY
+    assert plan(BF16, 17, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
 
 
 def test_skinny_decode_shape_fills_the_chip():
@@ -596,8 +597,11 @@ def test_bf16_skinny_with_workspace():
     # A not 16-byte aligned: the tiled kernels.
     st, pl = plan(BF16, 16, 8192, 8192, A=PA + 2, ws=1 << 30)
     assert st == OK and pl["path"] == tg.GEMM_PATH_TILED, pl
-    # Without a workspace a split is impossible: the tiled path, unless no split is needed.
-    assert plan(BF16, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
+    # Without a workspace a split is impossible: the same kernel over the whole of K
+    # (one workgroup per 128-column strip), unless no split is needed anyway.
+    st, pl = plan(BF16, 16, 8192, 8192)
+    assert st == OK and kname(pl) == "bf16_skinny_lds_n128_w4_s4_whole_k" and pl["grid"] == 64, pl
+    assert pl["path"] == tg.GEMM_PATH_SKINNY
     assert plan(BF16, 16, 32768, 8192)[1]["path"] == tg.GEMM_PATH_SKINNY_SPLITK
     # B rows must be whole 16-byte chunks; M = 17 is not skinny.
     assert plan(BF16, 16, 8196, 8192, ws=1 << 30)[1]["path"] == tg.GEMM_PATH_TILED
@@ -691,7 +695,7 @@ def test_output_types_of_the_kernels():
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
-                 "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_nt_n32_w8_u2",
+                 "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
                  "fp8_skinny_nt_splitk_n32_w8_u2"):
         assert outs[name] == 7, name
     assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 7 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 7

@@ -20,8 +20,8 @@ BF16 = tg.GEMM_DTYPE_BF16F32
 
 
 def _skinny_ids():
-    return {k["name"]: k["id"] for k in tg.kernels() if k["dtype"] == BF16 and k["path"] == tg.GEMM_PATH_SKINNY_SPLITK
-            and k["layouts"] & 1}
+    return {k["name"]: k["id"] for k in tg.kernels() if k["dtype"] == BF16 and k["layouts"] & 1
+            and k["path"] in (tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK)}
 
 
 def _ws(M, N, K):
@@ -59,6 +59,24 @@ def test_bf16_skinny_random_and_deterministic(gpu_available):
     assert r <= TOL["bf16f32"]
     Ad, Bd = A.cuda(), B.cuda()
     outs = [tg.gemm(Ad, Bd, ws=ws) for _ in range(5)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_bf16_skinny_without_workspace(gpu_available):
+    """16 x 8192 x 8192 without a workspace: the streaming kernel over the
+    whole of K, within the bound and bit-identical to itself on repeats."""
+    M, N, K = 16, 8192, 8192
+    A, B, C0 = make_random_inputs(M, N, K, seed=961, dist="normal", dtype="bf16f32")
+    st, pl = tg.gemm_plan_query(BF16, M, N, K, 1.0, 0x1000, K, 0x1000, N, 0.5, 0x1000, N, 0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] == "bf16_skinny_lds_n128_w4_s4_whole_k"
+    say(f"[bf16 skinny] auto, no workspace M={M} N={N} K={K} random seed=961")
+    C, _, _ = run_gemm(A, B, C0, 1.0, 0.5)
+    r = ratio(C, A, B, C0, 1.0, 0.5)
+    say(f"[bf16 skinny] ratio {r:.3e}")
+    assert r <= TOL["bf16f32"]
+    Ad, Bd = A.cuda(), B.cuda()
+    outs = [tg.gemm(Ad, Bd) for _ in range(3)]
     torch.cuda.synchronize()
     assert all(torch.equal(outs[0], o) for o in outs[1:])
 

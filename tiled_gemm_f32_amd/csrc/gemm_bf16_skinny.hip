@@ -191,10 +191,12 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     }
 }
 
-template <int WAVES, int NSLOT>
+// SPLIT: cut K over workgroups as skinny_splits() suggests (which needs the
+// workspace); otherwise every workgroup covers the whole of K and finishes C.
+template <int WAVES, int NSLOT, bool SPLIT = true>
 hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t stream) {
     const int strips = (p.N + kSkNW - 1) / kSkNW;
-    const int want = skinny_splits(strips, p.K);
+    const int want = SPLIT ? skinny_splits(strips, p.K) : 1;
     int kchunk = ((p.K + want - 1) / want + 15) / 16 * 16;
     int splits = (p.K + kchunk - 1) / kchunk;     // never more than the workspace was sized for
     GemmParams args = p;
@@ -209,6 +211,11 @@ hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t 
     return launch_splitk_reduce(red, stream);
 }
 
+template <int WAVES, int NSLOT>
+hipError_t launch_bf16_skinny_whole_k(const GemmParams &p, hipStream_t stream) {
+    return launch_bf16_skinny<WAVES, NSLOT, false>(p, nullptr, stream);
+}
+
 template __global__ void bf16_skinny_kernel<4, 4>(GemmParams, float *, int, int);
 
 }  // namespace
@@ -220,6 +227,11 @@ template __global__ void bf16_skinny_kernel<4, 4>(GemmParams, float *, int, int)
 const KernelDesc kBf16SplitKernels[] = {
     {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY_SPLITK, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_w4_s4",
      nullptr, 0, &launch_bf16_skinny<4, 4>, kLayoutNN, false, kOutAll},
+    // Without a workspace: one workgroup per strip over the whole of K.  At
+    // N = 8192 that is 64 workgroups, still far ahead of the tiled kernels,
+    // which compute 128 rows for 16 on as many workgroups.
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_w4_s4_whole_k",
+     &launch_bf16_skinny_whole_k<4, 4>, 0, nullptr, kLayoutNN, false, kOutAll},
 };
 const int kBf16SplitKernelCount = sizeof(kBf16SplitKernels) / sizeof(kBf16SplitKernels[0]);
 #endif
