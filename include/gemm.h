@@ -312,7 +312,8 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  *     16-byte chunks (aligned bases, K, lda and ldb);
  *   - fp32 with M <= 16, A transposed and B untransposed (A stored K x M)
  *     takes the fp32 skinny kernels of gemm_f32, which then gather A's
- *     values from the rows of its stored transpose;
+ *     values from the rows of its stored transpose; bf16 does the same when
+ *     M and lda are multiples of 8 and A is 16-byte aligned;
  *   - fp32 and bf16 with either operand transposed take the matrix-core
  *     kernel for that layout when the stored rows of A and B are whole
  *     16-byte chunks;

@@ -647,7 +647,16 @@ def test_skinny_a_transposed_choice():
     assert "_at_" not in kname(plan(F32, 16, 8192, 8192)[1])
     assert "_at_" not in kname(gplan(F32, T_, N_, 17, 8192, 8192)[1])
     assert "_at_" not in kname(gplan(F32, T_, T_, 16, 8192, 8192)[1])
-    assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192)[1])
+    # bf16: the streaming kernel reading A's K rows in 16-byte chunks (M and
+    # lda multiples of 8, A 16-byte aligned), over the whole of K or split.
+    st, pl = gplan(BF16, T_, N_, 16, 8192, 8192, lda=16)
+    assert st == OK and kname(pl) == "bf16_skinny_lds_n128_at_w4_s4_whole_k" and pl["grid"] == 64, pl
+    st, pl = gplan(BF16, T_, N_, 8, 8192, 8192, lda=8, ws=tg.gemm_workspace_size(BF16, 8, 8192, 8192))
+    assert st == OK and kname(pl) == "bf16_skinny_lds_n128_at_w4_s4" and pl["grid"] == 256, pl
+    assert "_at_" not in kname(gplan(BF16, T_, N_, 5, 8192, 8192, lda=8)[1])      # rows of 5: not whole chunks
+    assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=20)[1])
+    assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=16, A=PA + 2)[1])
+    assert "_at_" not in kname(gplan(BF16, N_, N_, 16, 8192, 8192)[1])
     K = 1 << 20
     st, pl = gplan(F32, T_, N_, 16, 64, K, lda=(1 << 9) - 4)       # K * lda * 4 < 2^31
     assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4", pl

@@ -314,3 +314,50 @@ def test_skinny_a_transposed_random_full_size(gpu_available, with_ws):
     # Same k pairing and summation order as the untransposed kernel of the same shape.
     C2, _, _ = run_gemm(A, B, C0, 1.0, 0.0, ws=ws)
     np.testing.assert_array_equal(C, C2)
+
+
+BF16_AT_SKINNY = ["bf16_skinny_lds_n128_at_w4_s4", "bf16_skinny_lds_n128_at_w4_s4_whole_k"]
+
+
+@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("NK", [(8192, 4096), (1000, 3008)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_bf16_skinny_a_transposed_exact(gpu_available, M, NK):
+    """bf16, M of 8 or 16, A stored K x M with its rows padded to 16 elements
+    by NaN (which must never reach C): both streaming kernels forced, and the
+    library's choice with and without a workspace, bit-exact on integer data
+    with bias and ReLU."""
+    N, K = NK
+    A, B, C0 = make_integer_inputs(M, N, K, seed=780 + M, dtype="bf16f32")
+    As = A.t().contiguous()
+    bias = make_bias(N, seed=781, integer=True)
+    ref = oracle.gemm_epilogue_ref(host_view(As), host_view(B), 2.0, -1.0, C0.numpy(), bias.numpy(), "relu", "T", "N")
+    ws = tg.workspace(M, N, K, dtype=tg.GEMM_DTYPE_BF16F32)
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    pad = (16 - M, 0, 0)
+    runs = [(n, ids[n], ws) for n in BF16_AT_SKINNY] + [("auto", 0, None), ("auto ws", 0, ws)]
+    for name, kid, w in runs:
+        say(f"[bf16 A^T skinny] {name} M={M} N={N} K={K} lda=16 seed={780 + M}")
+        C, _, _ = run_gemm(As, B, C0, 2.0, -1.0, kernel=kid, ws=w, bias=bias, activation="relu", op_a="T", pad=pad)
+        np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
+    st, pl = tg.gemm_plan_query_general(tg.GEMM_DTYPE_BF16F32, 1, 0, M, N, K, 1.0, 0x1000, 16, 0x1000, N, 0.0,
+                                        0x1000, N, 0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] in BF16_AT_SKINNY
+
+
+def test_bf16_skinny_a_transposed_random_full_size(gpu_available):
+    """16 x 8192 x 8192, A stored K x M, N(0,1) data with a workspace: the
+    bf16 error ratio, and the same bits as the untransposed call (the same
+    matrix-instruction inputs in the same order)."""
+    M, N, K = 16, 8192, 8192
+    A, B, C0 = make_random_inputs(M, N, K, seed=4, dist="normal", dtype="bf16f32")
+    As = A.t().contiguous()
+    ws = tg.workspace(M, N, K, dtype=tg.GEMM_DTYPE_BF16F32)
+    say(f"[bf16 A^T skinny] auto M={M} N={N} K={K} normal seed=4 ws=True")
+    C, _, _ = run_gemm(As, B, C0, 1.0, 0.5, ws=ws, op_a="T")
+    a, b = host_view(As), host_view(B)
+    r = oracle.error_ratio(C, oracle.gemm_ref(a, b, 1.0, 0.5, C0.numpy(), "T", "N"),
+                           oracle.gemm_absbound(a, b, 1.0, 0.5, C0.numpy(), "T", "N"))
+    say(f"[bf16 A^T skinny] ratio {r:.3e}")
+    assert r <= TOL["bf16f32"]
+    C2, _, _ = run_gemm(A, B, C0, 1.0, 0.5, ws=ws)
+    np.testing.assert_array_equal(C, C2)

@@ -288,9 +288,8 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand);
 // first and over the fallback (general) kernels only when none of those runs
 // the call.
 const KernelDesc *choose(const Call &c) {
-    const bool plain = c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_N;
-    // fp32 with B stored K x N: the streaming kernels, for A stored either
-    // way (the table's layouts pick the A load).  The split-K kernels pay
+    // fp32 and bf16 with B stored K x N: the streaming kernels, for A stored
+    // either way (the table's layouts pick the A load).  The split-K kernels pay
     // off only where K is actually split.
     const bool b_kn = c.op_b == GEMM_OP_N;
     if (b_kn && c.dtype == GEMM_DTYPE_F32 && skinny_fits(c) && c.ws != nullptr) {
@@ -303,7 +302,7 @@ const KernelDesc *choose(const Call &c) {
     }
     // bf16 weights with M <= 16: the streaming kernel, split over K when the
     // caller's workspace allows (it needs one only when it splits).
-    if (plain && c.dtype == GEMM_DTYPE_BF16F32 && skinny_fits(c)) {
+    if (b_kn && c.dtype == GEMM_DTYPE_BF16F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kBf16SplitKernels, gemm::kBf16SplitKernelCount, c, 0))
             return kd;
     }

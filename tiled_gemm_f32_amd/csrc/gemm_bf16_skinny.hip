@@ -47,7 +47,12 @@ constexpr int kSkSlot = kSkB + 16 * kSkKB * 2;   // B, then A's 16 x 32 block (1
 // (q = 0..3, t = 0..7) of one read get (t & 3) + 4 (q & 1) pairs apart.
 __device__ __forceinline__ int sk_swz(int row) { return 2 * ((row & 3) | (((row >> 3) & 1) << 2)); }
 
-template <int WAVES, int NSLOT>
+// AT: A is stored K x M (M and lda multiples of 8).  Its 32 x 16 block of a
+// slot is then 32 rows of 32 bytes (lane -> k row lane/2, half lane%2) and
+// the A operand comes out of the same transposing reads as B's (one
+// 16-column block: lane s gets column m = s).  Columns of the stored block
+// at or past M only reach rows of C that are never written.
+template <int WAVES, int NSLOT, bool AT = false>
 __global__ void __launch_bounds__(64 * WAVES)
 bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     static_assert(NSLOT == 4, "four slot arrays");
@@ -75,7 +80,8 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     // a zero of B times an infinity there would not vanish.
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
-    const rsrc_t ra = make_rsrc(A + kbeg, clamp_extent(((int64_t)(M - 1) * lda + kspan) * 2));
+    const rsrc_t ra = AT ? make_rsrc(A + (int64_t)kbeg * lda, clamp_extent(((int64_t)(kspan - 1) * lda + M) * 2))
+                         : make_rsrc(A + kbeg, clamp_extent(((int64_t)(M - 1) * lda + kspan) * 2));
     const rsrc_t rb =
         make_rsrc(B + (int64_t)kbeg * ldb + n0, clamp_extent(((int64_t)(kspan - 1) * ldb + (N - n0)) * 2));
 
@@ -101,10 +107,18 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
             const int chunk = (col >> 3) ^ sk_swz(row);
             tr_off[h][cb] = (uint32_t)(row * 256 + 16 * chunk + 2 * (col & 7));
         }
-    // A's load: lane -> row lane/4, 16-byte chunk lane%4 (k = 8 (lane%4) ..).
-    const uint32_t a_goff = (uint32_t)((lane >> 2) * lda + 8 * (lane & 3)) * 2u;
-    const int a_kc = 8 * (lane & 3);
+    // A's load: lane -> row lane/4, 16-byte chunk lane%4 (k = 8 (lane%4) ..);
+    // with AT, lane -> k row lane/2, columns 8 (lane%2) .. +7.  a_kc is the
+    // first k the lane's chunk holds.
+    const uint32_t a_goff = AT ? (uint32_t)((lane >> 1) * lda + 8 * (lane & 1)) * 2u
+                               : (uint32_t)((lane >> 2) * lda + 8 * (lane & 3)) * 2u;
+    const int a_kc = AT ? (lane >> 1) : 8 * (lane & 3);
+    const uint32_t a_blk = AT ? (uint32_t)kSkKB * (uint32_t)lda * 2u : (uint32_t)kSkKB * 2u;   // per block
     const uint32_t a_read = (uint32_t)(kSkB + s * 64 + 16 * q);
+    // AT: lane s of group q points at k row 8q + s/4 (+4), columns 4 (s%4) .. +3.
+    uint32_t at_off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) at_off[h] = (uint32_t)(kSkB + (8 * q + (s >> 2) + 4 * h) * 32 + 8 * (s & 3));
 
     const int nb = (kspan + kSkKB - 1) / kSkKB;
     f32x4 acc[8];
@@ -122,11 +136,18 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
                                                      b_goff[i] + boff, 0, 0, 0);
         const uint32_t poison = (uint32_t)(blk * kSkKB + a_kc >= kspan) << 31;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_base(slot) + kSkB), 16,
-                                                 a_goff + (uint32_t)(blk * kSkKB) * 2u + poison, 0, 0, 0);
+                                                 a_goff + (uint32_t)blk * a_blk + poison, 0, 0, 0);
     };
     auto consume = [&](int slot) {
         const char *base = slot_base(slot);
-        const bf16x8 afrag = *reinterpret_cast<const bf16x8 *>(base + a_read);
+        bf16x8 afrag;
+        if constexpr (AT) {
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + at_off[0]));
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + at_off[1]));
+            afrag = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            afrag = *reinterpret_cast<const bf16x8 *>(base + a_read);
+        }
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
             const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + tr_off[0][cb]));
@@ -193,7 +214,7 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
 
 // SPLIT: cut K over workgroups as skinny_splits() suggests (which needs the
 // workspace); otherwise every workgroup covers the whole of K and finishes C.
-template <int WAVES, int NSLOT, bool SPLIT = true>
+template <int WAVES, int NSLOT, bool SPLIT = true, bool AT = false>
 hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t stream) {
     const int strips = (p.N + kSkNW - 1) / kSkNW;
     const int want = SPLIT ? skinny_splits(strips, p.K) : 1;
@@ -202,7 +223,7 @@ hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t 
     GemmParams args = p;
     float *partials = static_cast<float *>(workspace);
     void *argv[] = {&args, &partials, &splits, &kchunk};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&bf16_skinny_kernel<WAVES, NSLOT>),
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&bf16_skinny_kernel<WAVES, NSLOT, AT>),
                                      dim3((unsigned)strips, (unsigned)splits), dim3(64 * WAVES), argv, 0, stream);
     if (err != hipSuccess || splits == 1) return err;
     GemmParams red = p;
@@ -211,12 +232,13 @@ hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t 
     return launch_splitk_reduce(red, stream);
 }
 
-template <int WAVES, int NSLOT>
+template <int WAVES, int NSLOT, bool AT = false>
 hipError_t launch_bf16_skinny_whole_k(const GemmParams &p, hipStream_t stream) {
-    return launch_bf16_skinny<WAVES, NSLOT, false>(p, nullptr, stream);
+    return launch_bf16_skinny<WAVES, NSLOT, false, AT>(p, nullptr, stream);
 }
 
-template __global__ void bf16_skinny_kernel<4, 4>(GemmParams, float *, int, int);
+template __global__ void bf16_skinny_kernel<4, 4, false>(GemmParams, float *, int, int);
+template __global__ void bf16_skinny_kernel<4, 4, true>(GemmParams, float *, int, int);
 
 }  // namespace
 
@@ -232,6 +254,13 @@ const KernelDesc kBf16SplitKernels[] = {
     // which compute 128 rows for 16 on as many workgroups.
     {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_w4_s4_whole_k",
      &launch_bf16_skinny_whole_k<4, 4>, 0, nullptr, kLayoutNN, false, kOutAll},
+    // A stored K x M: its K rows (M long) must be whole 16-byte chunks too,
+    // so M is 8 or 16.  Then the extent of each split's A ends on a chunk
+    // boundary; a 16-byte load that straddled it would read as zero whole.
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY_SPLITK, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_at_w4_s4",
+     nullptr, 0, &launch_bf16_skinny<4, 4, true, true>, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_at_w4_s4_whole_k",
+     &launch_bf16_skinny_whole_k<4, 4, true>, 0, nullptr, kLayoutTN, false, kOutAll},
 };
 const int kBf16SplitKernelCount = sizeof(kBf16SplitKernels) / sizeof(kBf16SplitKernels[0]);
 #endif
