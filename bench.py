@@ -51,6 +51,12 @@ STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x8192x8192", "bf16f32_16x8192x8192_nt",
          "f32_16x8192x8192_nt", "fp8f32_16x8192x8192_nt", "f32_4096_nt", "f32_4096_tn",
          "fp8f32_8192_nn", "fp8f32_8192_tn"]
+# The other configurations of the workload set, timed call by call after the
+# step (they do not enter ``value``): (workload, whether a workspace is passed).
+# The M = 16 shape is timed here through the plain call as well, which has no
+# workspace and so no K split.
+CONFIGS = [("f32_256", True), ("f32_4092_beta", True), ("f32_1000x3000x777", True),
+           ("f32_16x8192x8192", False)]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -69,6 +75,9 @@ def parse():
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="after the timed steps, time this many calls of each workload one at a time, each "
                          "after reading a 1 GiB buffer that evicts L2 and the last-level cache (0: skip)")
+    ap.add_argument("--config-calls", type=int, default=50,
+                    help="after the timed steps, time this many back-to-back calls of each of the other "
+                         "configurations (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (a plain kernel of known traffic) so hardware "
                          "byte counters can be scaled against it")
@@ -206,17 +215,20 @@ def main():
 
     DTYPES = {"f32": tg.GEMM_DTYPE_F32, "bf16f32": tg.GEMM_DTYPE_BF16F32, "fp8f32": tg.GEMM_DTYPE_FP8F32}
     # Inputs resident in HBM before timing.
-    calls = []
-    for name in names:
+    def make_call(name, with_ws=None):
         w = WORKLOADS[name]
         A, B, C0 = make_inputs(w)
         Ad, C = _to_device(A, dev), C0.to(dev)
         copies = SKINNY_COPIES if w.M <= 16 else 1
         Bs = [_to_device(B, dev) for _ in range(copies)]
         ws = None
-        if w.dtype == "f32" or w.M <= 16:
+        if with_ws is None:
+            with_ws = w.dtype == "f32" or w.M <= 16
+        if with_ws:
             ws = tg.workspace(w.M, w.N, w.K, device=dev, dtype=DTYPES[w.dtype])
-        calls.append({"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []})
+        return {"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []}
+
+    calls = [make_call(name) for name in names]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -256,6 +268,13 @@ def main():
             e1.record(stream)
             c["durs"].append((e0, e1))
 
+    def plan_of(c):
+        w = c["w"]
+        return tg.gemm_plan_query_general(DTYPES[w.dtype], *ops_of(w), w.M, w.N, w.K, w.alpha,
+                                          c["A"].data_ptr(), lda_of(w), c["B"][0].data_ptr(), ldb_of(w), w.beta,
+                                          c["C"].data_ptr(), w.N, 0,
+                                          c["ws"].numel() if c["ws"] is not None else 0)[1]
+
     if args.copy_calibration:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -283,11 +302,7 @@ def main():
         ms = sum(e0.elapsed_time(e1) for e0, e1 in c["durs"]) / len(c["durs"])
         tflops = w.flops / (ms * 1e-3) / 1e12
         gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
-        plan = tg.gemm_plan_query_general(DTYPES[w.dtype], *ops_of(w), w.M, w.N, w.K, w.alpha,
-                                          c["A"].data_ptr(), lda_of(w), c["B"][0].data_ptr(), ldb_of(w), w.beta,
-                                          c["C"].data_ptr(), w.N, 0,
-                                          c["ws"].numel() if c["ws"] is not None else 0)[1]
-        kname = tg.gemm_kernel_query(plan["kernel_id"])["name"]
+        kname = tg.gemm_kernel_query(plan_of(c)["kernel_id"])["name"]
         bound = "hbm" if w.M <= 16 else "mfma"
         parts[w.name] = {
             "kernel": kname, "ms": round(ms, 5), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
@@ -308,6 +323,9 @@ def main():
                 "algorithmic_bytes": w.algorithmic_bytes}
 
     cold = cold_timings(calls, launch, args.cold_calls, dev) if args.cold_calls > 0 else None
+    configs = None
+    if args.config_calls > 0 and not args.only:
+        configs = config_timings(make_call, launch, plan_of, args.config_calls)
 
     dominant = max(parts, key=lambda n: parts[n]["ms"])
     roof = roofline_of(dominant)
@@ -334,6 +352,7 @@ def main():
         "rooflines": [roofline_of(n) for n in parts],
         "parts": parts,
         "cold": cold,
+        "configs": configs,
         "observed_clocks": observed,
         "cpu_baseline": cpu,
     }
@@ -370,6 +389,44 @@ def cold_timings(calls, launch, n, dev):
                        "unit": unit, "frac_at_median": round(rate / peak, 4)}
     del scrub
     return out
+
+
+def config_timings(make_call, launch, plan_of, n):
+    """The other configurations, each timed over n back-to-back calls (HIP
+    events per call on the launch stream, after 5 untimed calls): mean time,
+    rate against the call's own roof, and the launch the library chose (tile,
+    K split, workgroups and how many waves of the 256 compute units they
+    make)."""
+    import torch
+    out = {}
+    for name, with_ws in CONFIGS:
+        c = make_call(name, with_ws)
+        w = c["w"]
+        for _ in range(5):
+            launch(c, False)
+        for _ in range(n):
+            launch(c, True)
+        torch.cuda.synchronize()
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in c["durs"]) / len(c["durs"])
+        pl = plan_of(c)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = w.algorithmic_bytes / (ms * 1e-3) / 1e9
+        bound = "hbm" if w.M <= 16 else "mfma"
+        key = name if with_ws or w.M > 16 else name + "_no_workspace"
+        out[key] = {
+            "kernel": tg_kernel_name(pl["kernel_id"]), "workspace": with_ws, "calls": n, "ms": round(ms, 5),
+            "tflops": round(tflops, 2), "gbs": round(gbs, 1), "bound": bound,
+            "frac": round(gbs / PEAK_HBM_GBS if bound == "hbm" else tflops / PEAK_TFLOPS[w.dtype], 4),
+            "tile": [pl["tile_m"], pl["tile_n"]], "k_splits": pl["splits"], "workgroups": pl["grid"],
+            "waves_of_256": round(pl["grid"] / 256, 3), "flops": w.flops, "algorithmic_bytes": w.algorithmic_bytes,
+        }
+        del c
+    return out
+
+
+def tg_kernel_name(kernel_id):
+    import tiled_gemm_f32_amd as tg
+    return tg.gemm_kernel_query(kernel_id)["name"]
 
 
 def cpu_baseline(calls):

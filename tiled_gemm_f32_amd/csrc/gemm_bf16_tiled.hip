@@ -801,9 +801,7 @@ template __global__ void bf16_ring_kernel<4, 4, true, true, GEMM_OUT_F32>(GemmPa
 template __global__ void bf16_ring_kernel<4, 4, true, true, GEMM_OUT_BF16>(GemmParams, int, int);
 template __global__ void bf16_ring_kernel<4, 4, true, true, GEMM_OUT_FP8>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 8, 4>(GemmParams, int, int);
-template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 8, 1, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 1, 8, 4>(GemmParams, int, int);
-template __global__ void bf16_tiled_kernel<256, 256, 64, 2, 2, 1, 1, 4>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<128, 128, 64, 2, 2, 8, 8, 8>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<128, 128, 64, 2, 2, 8, 1, 8>(GemmParams, int, int);
 template __global__ void bf16_tiled_kernel<128, 128, 64, 2, 2, 1, 8, 8>(GemmParams, int, int);
@@ -829,9 +827,10 @@ const KernelDesc kBf16TiledKernels[] = {
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4",
      &launch_bf16_ring<4, 4, true, true>, 0, nullptr, kLayoutTT, false, kOutAll},
     BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
-    BF16_TILED(256, 256, 64, 2, 2, 8, 1, 4),
+    // With B read element by element the 256 x 256 tile does not fit the
+    // registers (its staged B values spill to scratch), so B without 16-byte
+    // rows takes the 128 x 128 tiles below.
     BF16_TILED(256, 256, 64, 2, 2, 1, 8, 4),
-    BF16_TILED(256, 256, 64, 2, 2, 1, 1, 4),
     BF16_TILED(128, 128, 64, 2, 2, 8, 8, 8),
     BF16_TILED(128, 128, 64, 2, 2, 8, 1, 8),
     BF16_TILED(128, 128, 64, 2, 2, 1, 8, 8),

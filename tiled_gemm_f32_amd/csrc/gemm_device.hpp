@@ -203,17 +203,14 @@ __device__ __forceinline__ float epilogue_value(float v, int64_t col, const floa
 
 // ---- Output quantisation (GemmParams::out_type).
 //
-// bfloat16: the upper half of the fp32 pattern after rounding to nearest,
-// ties to even (add 0x7fff plus the lowest kept bit; a carry into the
-// exponent is the correct next binade, and past the largest finite value it
-// gives infinity).  A NaN keeps its sign and upper payload with the quiet
-// bit set.  Written as a select, not a branch: the tile epilogues convert
-// hundreds of values in one unrolled pass.
+// bfloat16: gfx950's fp32 -> bf16 conversion instruction (what a plain
+// conversion to __bf16 compiles to there), which rounds to nearest, ties to
+// even, overflows to infinity and keeps NaN a NaN.  One instruction per value
+// instead of the bit arithmetic of a software rounding: the tile epilogues
+// convert hundreds of values in one unrolled pass, and every extra temporary
+// there competes with the accumulators for registers.
 __device__ __forceinline__ uint16_t to_bf16(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t quiet_nan = (u >> 16) | 0x40u;
-    return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 // OCP E4M3: saturate to +-448 first (both comparisons are false for NaN,
 // which passes through to the NaN code), then the hardware conversion,

@@ -217,13 +217,16 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // Epilogue.  Register 4g + t of lane (h, l32) in fragment (fm, fn) is
     // C[row m0 + wm*128 + 32*fm + l32][column n0 + wn*128 + 32*fn + 8*g + 4*h + t].
     // A run of 4 columns may straddle N (no constraint on N here): such runs,
-    // and C without 16-byte alignment, take element accesses.  One branch on
-    // the activation for the whole tile keeps the accumulators in registers.
+    // and C without 16-byte alignment, take element accesses.  The activation
+    // is a uniform branch per run of 4 values, taken on values already moved
+    // out of the accumulators: with one branch around the whole tile the
+    // compiler copied every accumulator to an architectural register at the
+    // branch and had to put some in scratch memory.
     const float alpha = p.alpha, beta = p.beta;
     const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
-    with_activation(p.act, [&](auto act) {
-        using Act = decltype(act);
+    {
         const bool vec_o = out_vec4<OUT>(p);
+        const int act = p.act;
 #pragma unroll
             for (int fn = 0; fn < 4; ++fn) {
 #pragma unroll
@@ -253,7 +256,14 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                             for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
                         }
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = Act::apply(v[t] + b[t]);
+                        for (int t = 0; t < 4; ++t) v[t] += b[t];
+                        if (act == GEMM_ACT_GELU) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = ActGelu::apply(v[t]);
+                        } else if (act == GEMM_ACT_RELU) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = ActRelu::apply(v[t]);
+                        }
                         if (whole)
                             store_out4<OUT>(p, row, col, v, vec_o);
                         else
@@ -261,7 +271,7 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
                     }
                 }
             }
-    });
+    }
 }
 
 template <int NS, int GROUP_M, bool AKN = false, bool BKN = false>
