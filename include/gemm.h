@@ -56,7 +56,9 @@ typedef enum gemm_status {
                                   2^31 - 1, or lda / ldb of 2^21 elements or more; or a forced
                                   kernel that cannot run on these operands */
     GEMM_ERR_LAUNCH = 3,       /* the HIP runtime reported an error for the launch */
-    GEMM_ERR_DEVICE = 4        /* no usable gfx950 device is current */
+    GEMM_ERR_DEVICE = 4,       /* no usable gfx950 device is current */
+    GEMM_ERR_SCRATCH = 5       /* gemm_general_noalloc: the problem's K split could need more
+                                  scratch than the library's static buffer holds */
 } gemm_status;
 
 /* A hipStream_t, passed through as an opaque pointer; NULL = default stream. */
@@ -346,6 +348,36 @@ GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_
                                              float beta, const float *C, int64_t ldc,
                                              int32_t force_kernel, int64_t workspace_bytes,
                                              gemm_plan *out);
+
+/*
+ * gemm_general for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it).  The
+ * arguments are those of gemm_general without the workspace: the K-split
+ * paths keep their partial products in a static device array that the
+ * library holds, GEMM_STATIC_SCRATCH_BYTES (32 MiB) on each GPU it is called
+ * on, from the first call on that device until the process ends.  The call
+ * allocates nothing itself; the result is the one gemm_general gives with a
+ * workspace of that size.
+ *
+ * Limit: when gemm_workspace_size(dtype, M, N, K) exceeds
+ * GEMM_STATIC_SCRATCH_BYTES the call returns GEMM_ERR_SCRATCH and does
+ * nothing (pass a workspace to gemm_general instead).  Argument errors are
+ * reported first, as by gemm_general.
+ *
+ * Sharing: all calls on one GPU use the same array.  It needs no clearing
+ * (every partial product is written before it is read), but calls that can
+ * overlap on one GPU (different streams not ordered by events, or several
+ * host threads with no ordering) race on it.  Calls on one stream are
+ * ordered and safe.
+ */
+#define GEMM_STATIC_SCRATCH_BYTES ((int64_t)32 << 20)
+
+GEMM_API gemm_status gemm_general_noalloc(int32_t dtype, int32_t op_a, int32_t op_b,
+                                          int64_t M, int64_t N, int64_t K, float alpha,
+                                          const void *A, int64_t lda, const void *B, int64_t ldb,
+                                          float beta, float *C, int64_t ldc,
+                                          int32_t force_kernel, const gemm_epilogue *epilogue,
+                                          gemm_stream_t stream);
 
 /* gemm_plan_query_general with an epilogue (its output type narrows the
  * kernels that can run): the plan gemm_general would take with it. */

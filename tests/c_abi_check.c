@@ -88,6 +88,13 @@ int main(void)
     CHECK(gemm_workspace_size(GEMM_DTYPE_BF16F32, 256, 512, 6000) > 0, "workspace size");
     CHECK(gemm_workspace_size(GEMM_DTYPE_F32, 4096, 4096, 4096) == 0, "no workspace for a full wave");
     CHECK(strcmp(gemm_status_string(GEMM_OK), "success") == 0, "status string");
+    /* The no-allocation entry point checks its arguments, then the scratch
+     * its K split could need, before touching the device. */
+    CHECK(gemm_general_noalloc(GEMM_DTYPE_F32, GEMM_OP_N, GEMM_OP_N, -1, 4, 4, 1.0f, A, 4, B, 4, 0.0f, C, 4, 0,
+                               NULL, NULL) == GEMM_ERR_INVALID_ARG, "noalloc invalid size");
+    CHECK(gemm_general_noalloc(GEMM_DTYPE_BF16F32, GEMM_OP_N, GEMM_OP_N, 2048, 2048, 65536, 1.0f, A, 65536, B, 2048,
+                               0.0f, C, 2048, 0, NULL, NULL) == GEMM_ERR_SCRATCH, "noalloc scratch limit");
+    CHECK(GEMM_STATIC_SCRATCH_BYTES == ((int64_t)32 << 20), "scratch size macro");
     CHECK(gemm_tuning_count() >= 0, "tuning count");
     {
         gemm_plan pl;

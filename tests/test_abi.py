@@ -55,7 +55,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(5):
+    for st in range(6):
         s = tg.gemm_status_string(st)
         assert s and s != "unknown status"
     assert tg.gemm_status_string(99) == "unknown status"
@@ -767,3 +767,35 @@ def test_fp8_other_layouts_take_their_rings(ops, name):
     args.update(bad)
     st, pl = gplan(FP8, ops[0], ops[1], **args)
     assert st == OK and kname(pl) == "fp8_general_128x128x16", pl
+
+
+# ----------------------------------------------------------------------------- no-allocation entry point
+
+def _noalloc(dtype, M, N, K, lda=None, ldb=None, ldc=None, A=PA, B=PB, C=PC, op_a=0, op_b=0):
+    lda = (max(K, 1) if op_a == 0 else max(M, 1)) if lda is None else lda
+    ldb = (max(N, 1) if op_b == 0 else max(K, 1)) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return tg.gemm_general_noalloc(dtype, op_a, op_b, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, ldc, 0, None, 0)
+
+
+def test_noalloc_checks_arguments_before_anything_else():
+    # Invalid arguments are reported as by gemm_general, with no HIP call (no GPU here).
+    assert _noalloc(F32, -1, 4, 4) == tg.GEMM_ERR_INVALID_ARG
+    assert _noalloc(F32, 4, 4, 4, lda=3) == tg.GEMM_ERR_INVALID_ARG
+    assert _noalloc(7, 4, 4, 4) == tg.GEMM_ERR_INVALID_ARG
+    assert _noalloc(F32, 4, 4, 4, A=0) == tg.GEMM_ERR_INVALID_ARG
+    # Empty problems are a no-op.
+    assert _noalloc(F32, 0, 4, 4) == tg.GEMM_OK
+    assert _noalloc(BF16, 4, 0, 4) == tg.GEMM_OK
+
+
+def test_noalloc_rejects_problems_beyond_the_static_scratch():
+    assert tg.GEMM_STATIC_SCRATCH_BYTES == 32 << 20
+    # A 2048 x 2048 bf16 problem with a deep K splits 4 ways: 64 MiB of partial products.
+    need = tg.gemm_workspace_size(BF16, 2048, 2048, 65536)
+    assert need > tg.GEMM_STATIC_SCRATCH_BYTES
+    assert _noalloc(BF16, 2048, 2048, 65536) == tg.GEMM_ERR_SCRATCH
+    assert "static scratch" in tg.gemm_status_string(tg.GEMM_ERR_SCRATCH)
+    # The decode and small-tile splits fit.
+    for dt, M, N, K in [(F32, 16, 8192, 8192), (BF16, 16, 8192, 8192), (BF16, 512, 512, 8192), (F32, 16, 16384, 65536)]:
+        assert 0 < tg.gemm_workspace_size(dt, M, N, K) <= tg.GEMM_STATIC_SCRATCH_BYTES, (dt, M, N, K)

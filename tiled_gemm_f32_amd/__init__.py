@@ -17,7 +17,8 @@ from ._lib import (  # noqa: F401  (re-exported C ABI)
     GEMM_PATH_SKINNY, GEMM_PATH_SKINNY_SPLITK, GEMM_PATH_TILED, GemmError, gemm_bf16f32,
     gemm_bf16f32_ex, gemm_bf16f32_ws, gemm_f32, gemm_f32_ex, gemm_f32_ws, gemm_kernel_count, gemm_kernel_query,
     gemm_plan_query, gemm_status_string, gemm_workspace_size, gemm_autotune, gemm_autotune_general, gemm_tuning_count,
-    gemm_tuning_clear, gemm_tuning_save, gemm_tuning_load, load)
+    gemm_tuning_clear, gemm_tuning_save, gemm_tuning_load, load, gemm_general_noalloc, GEMM_ERR_SCRATCH,
+    GEMM_STATIC_SCRATCH_BYTES)
 
 __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex", "gemm_f32_ws", "gemm_bf16f32_ws",
            "gemm_f32_epi", "gemm_bf16f32_epi", "Epilogue", "GEMM_ACT_NONE", "GEMM_ACT_RELU", "GEMM_ACT_GELU",
@@ -26,7 +27,8 @@ __all__ = ["gemm", "gemm_f32", "gemm_bf16f32", "gemm_f32_ex", "gemm_bf16f32_ex",
            "gemm_workspace_size", "gemm_status_string", "gemm_kernel_count", "gemm_kernel_query",
            "gemm_plan_query", "GemmError", "kernels", "workspace", "autotune", "gemm_autotune",
            "gemm_autotune_general", "gemm_tuning_count",
-           "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load"]
+           "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_general_noalloc",
+           "GEMM_ERR_SCRATCH", "GEMM_STATIC_SCRATCH_BYTES"]
 
 
 def _ld(t, what: str) -> int:

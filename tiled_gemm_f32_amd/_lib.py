@@ -19,6 +19,9 @@ GEMM_ERR_INVALID_ARG = 1
 GEMM_ERR_UNSUPPORTED = 2
 GEMM_ERR_LAUNCH = 3
 GEMM_ERR_DEVICE = 4
+GEMM_ERR_SCRATCH = 5
+# Bytes of the library's static device scratch (gemm_general_noalloc).
+GEMM_STATIC_SCRATCH_BYTES = 32 << 20
 
 GEMM_PATH_NONE = 0
 GEMM_PATH_SCALE = 1
@@ -46,7 +49,8 @@ EXPORTED = ("gemm_f32", "gemm_bf16f32", "gemm_status_string", "gemm_kernel_count
             "gemm_kernel_query", "gemm_plan_query", "gemm_f32_ex", "gemm_bf16f32_ex",
             "gemm_workspace_size", "gemm_f32_ws", "gemm_bf16f32_ws", "gemm_autotune", "gemm_tuning_count",
             "gemm_tuning_clear", "gemm_tuning_save", "gemm_tuning_load", "gemm_f32_epi", "gemm_bf16f32_epi",
-            "gemm_general", "gemm_plan_query_general", "gemm_plan_query_epi", "gemm_autotune_general")
+            "gemm_general", "gemm_plan_query_general", "gemm_plan_query_epi", "gemm_autotune_general",
+            "gemm_general_noalloc")
 
 
 class KernelInfo(ctypes.Structure):
@@ -108,6 +112,8 @@ def load() -> ctypes.CDLL:
     lib.gemm_f32_epi.argtypes = gemm_sig + [epi, vp, i64, vp]
     lib.gemm_general.argtypes = [i32, i32, i32] + gemm_sig + [i32, epi, vp, i64, vp]
     lib.gemm_general.restype = ctypes.c_int
+    lib.gemm_general_noalloc.argtypes = [i32, i32, i32] + gemm_sig + [i32, epi, vp]
+    lib.gemm_general_noalloc.restype = ctypes.c_int
     lib.gemm_plan_query_general.argtypes = [i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, i32,
                                             i64, ctypes.POINTER(Plan)]
     lib.gemm_plan_query_general.restype = ctypes.c_int
@@ -198,6 +204,12 @@ def gemm_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
                  workspace=0, workspace_bytes=0, stream=0) -> int:
     return load().gemm_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel,
                                _epi(epilogue), workspace, workspace_bytes, stream)
+
+
+def gemm_general_noalloc(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0,
+                         epilogue=None, stream=0) -> int:
+    return load().gemm_general_noalloc(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                       force_kernel, _epi(epilogue), stream)
 
 
 def gemm_plan_query_general(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel=0,

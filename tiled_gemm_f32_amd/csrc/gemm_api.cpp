@@ -792,6 +792,33 @@ GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_
 
 GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
                                      const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
+GEMM_API gemm_status gemm_general_noalloc(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                          int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                          int64_t ldb, float beta, float *C, int64_t ldc, int32_t force_kernel,
+                                          const gemm_epilogue *epilogue, gemm_stream_t stream) {
+    static_assert(gemm::kStaticScratchBytes == GEMM_STATIC_SCRATCH_BYTES, "header and library disagree");
+    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    c.op_a = op_a;
+    c.op_b = op_b;
+    apply_epilogue(c, epilogue);
+    // Argument errors first, with no HIP call, exactly as gemm_general.
+    {
+        gemm_plan pl;
+        const KernelDesc *kd = nullptr;
+        KSplit ks;
+        const gemm_status st = plan(c, force_kernel, &pl, &kd, &ks);
+        if (st != GEMM_OK || pl.path == GEMM_PATH_NONE) return st;
+    }
+    if (gemm_workspace_size(dtype, M, N, K) > gemm::kStaticScratchBytes) return GEMM_ERR_SCRATCH;
+    gemm_status st = check_device();
+    if (st != GEMM_OK) return st;
+    void *scratch = nullptr;
+    if (gemm::static_scratch(&scratch) != hipSuccess) return GEMM_ERR_DEVICE;
+    c.ws = scratch;
+    c.ws_bytes = gemm::kStaticScratchBytes;
+    return run(c, force_kernel, stream);
+}
+
                                      const float *C, int64_t ldc, int32_t force_kernel, int64_t workspace_bytes,
                                      gemm_plan *out) {
     if (out == nullptr) return GEMM_ERR_INVALID_ARG;
@@ -933,3 +960,4 @@ GEMM_API const char *gemm_status_string(gemm_status status) {
 }
 
 }  // extern "C"
+    case GEMM_ERR_SCRATCH: return "the problem's K split could need more than the library's static scratch";

@@ -113,6 +113,13 @@ extern const int kBf16SplitKernelCount;
 extern const KernelDesc kSkinnyNtKernels[];
 extern const int kSkinnyNtKernelCount;
 
+// Size of the library's static device scratch (gemm_scratch.hip), the
+// workspace of gemm_general_noalloc.
+constexpr int64_t kStaticScratchBytes = int64_t(32) << 20;
+// Device address of the current device's copy of that scratch (looked up
+// once per device).
+hipError_t static_scratch(void **ptr);
+
 // The K == 0 / alpha == 0 result over p's M x N view: act(beta * C + bias)
 // (C not read when beta == 0), stored as p's output type.
 hipError_t launch_scale_c(const GemmParams &p, hipStream_t stream);
