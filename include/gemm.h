@@ -52,9 +52,9 @@ typedef enum gemm_status {
     GEMM_OK = 0,
     GEMM_ERR_INVALID_ARG = 1,  /* negative size, leading dimension too small, NULL or
                                   misaligned pointer for an operand that is read or written */
-    GEMM_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels index: M, N or K above
-                                  2^31 - 1, or lda / ldb of 2^21 elements or more; or a forced
-                                  kernel that cannot run on these operands */
+    GEMM_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels index: M, N, K, lda or
+                                  ldb above 2^31 - 1; or a forced kernel that cannot run on
+                                  these operands */
     GEMM_ERR_LAUNCH = 3,       /* the HIP runtime reported an error for the launch */
     GEMM_ERR_DEVICE = 4,       /* no usable gfx950 device is current */
     GEMM_ERR_SCRATCH = 5       /* gemm_general_noalloc: the problem's K split could need more

@@ -107,9 +107,41 @@ def test_operands_not_needed_may_be_null():
 
 def test_unsupported_sizes():
     assert plan(F32, 2 ** 31, 4, 4)[0] == UNSUP
-    assert plan(F32, 4, 4, 4, lda=2 ** 21)[0] == UNSUP
-    assert plan(F32, 4, 4, 4, ldb=2 ** 21)[0] == UNSUP
-    assert plan(F32, 4, 4, 4, lda=2 ** 21 - 1)[0] == OK
+    assert plan(F32, 4, 4, 4, lda=2 ** 31)[0] == UNSUP
+    assert plan(F32, 4, 4, 4, ldb=2 ** 31)[0] == UNSUP
+    assert plan(F32, 4, 4, 4, lda=2 ** 31 - 1)[0] == OK
+    assert plan(F32, 4, 4, 4, ldb=2 ** 31 - 1)[0] == OK
+
+
+def test_large_operands_keep_their_fast_kernels():
+    """Buffer offsets are 32-bit per panel or slice, not per operand: weights
+    of 2 GiB and more stay on the streaming kernels, and a leading dimension
+    of 2^21 elements or more on the tiled ones, as long as one panel fits."""
+    # 16 x 65536 x 8192 fp32 and 16 x 131072 x 8192 bf16: B is 2 GiB.
+    st, pl = plan(F32, 16, 65536, 8192)
+    assert st == OK and pl["path"] == tg.GEMM_PATH_SKINNY, kname(pl)
+    st, pl = plan(F32, 16, 65536, 8192, ws=1 << 30)
+    assert st == OK and pl["path"] in (tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK), kname(pl)
+    st, pl = plan(BF16, 16, 131072, 8192)
+    assert st == OK and pl["path"] in (tg.GEMM_PATH_SKINNY, tg.GEMM_PATH_SKINNY_SPLITK), kname(pl)
+    st, pl = gplan(F32, T_, N_, 16, 65536, 8192, lda=16)
+    assert st == OK and pl["path"] == tg.GEMM_PATH_SKINNY, kname(pl)
+    # B with more than 2^21 columns (2.1 GB at K = 256): a ring kernel, whose
+    # B slices are 16 rows deep.
+    st, pl = plan(F32, 64, (1 << 21) + 64, 256)
+    assert st == OK and "general" not in kname(pl) and pl["tile_k"] == 16, kname(pl)
+    st, pl = plan(BF16, 512, (1 << 22) + 64, 256)
+    assert st == OK and "general" not in kname(pl), kname(pl)
+    # A with rows 2^22 floats apart: 256- and 128-row panels would span more
+    # than 2^31 bytes, 64-row ones do not.
+    st, pl = plan(F32, 1024, 1024, 4096, lda=1 << 22)
+    assert st == OK and pl["tile_m"] == 64 and "general" not in kname(pl), kname(pl)
+    # Too far apart for any panel: the general kernel (64-bit element offsets).
+    st, pl = plan(F32, 1024, 1024, 4096, lda=1 << 25)
+    assert st == OK and "general" in kname(pl), kname(pl)
+    # A skinny call whose 16 rows of A span more than 2^31 bytes is not streamed.
+    st, pl = plan(F32, 16, 8192, 4096, lda=1 << 26)
+    assert st == OK and pl["path"] == tg.GEMM_PATH_TILED, kname(pl)
 
 
 def test_invalid_dtype_and_force():
@@ -182,9 +214,13 @@ def test_skinny_decode_shape_fills_the_chip():
     assert p["grid"] == 256 and p["vec_b"] == 2 and p["tile_n"] == 32
 
 
-def test_skinny_falls_back_when_b_offsets_would_overflow():
+def test_skinny_streams_any_size_and_falls_back_only_when_a_batch_overflows():
+    # 16 GiB of B: the streaming kernels rebase B per batch of k rows.
     st, p = plan(F32, 16, 65536, 65536)
-    assert st == OK and p["path"] == tg.GEMM_PATH_TILED
+    assert st == OK and p["path"] == tg.GEMM_PATH_SKINNY
+    # One batch of 512 rows of 2^21 floats spans 4 GiB: not streamed by those.
+    st, p = plan(F32, 16, 1 << 21, 4096)
+    assert st == OK and kname(p) != "f32_skinny_mfma16_n2_a4_w8_u4", kname(p)
 
 
 @pytest.mark.parametrize("M,N,K,tile,grid", [
@@ -658,9 +694,9 @@ def test_skinny_a_transposed_choice():
     assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=16, A=PA + 2)[1])
     assert "_at_" not in kname(gplan(BF16, N_, N_, 16, 8192, 8192)[1])
     K = 1 << 20
-    st, pl = gplan(F32, T_, N_, 16, 64, K, lda=(1 << 9) - 4)       # K * lda * 4 < 2^31
+    st, pl = gplan(F32, T_, N_, 16, 64, K, lda=1 << 9)             # ((K - 1) * lda + M) * 4 < 2^31
     assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4", pl
-    st, pl = gplan(F32, T_, N_, 16, 64, K, lda=1 << 9)             # = 2^31
+    st, pl = gplan(F32, T_, N_, 16, 64, K, lda=(1 << 9) + 4)       # > 2^31
     assert st == OK and "_at_" not in kname(pl), pl
     # Forced on untransposed A they refuse, as the untransposed ones do here.
     for n in ("f32_skinny_mfma16_n2_at_w8_u4", "f32_skinny_splitk_n128_at_w8_u1"):
@@ -669,12 +705,14 @@ def test_skinny_a_transposed_choice():
 
 
 def test_skinny_nt_largest_leading_dimension():
-    # Leading dimensions stop at 2^21 - 1 elements, so 32 rows of B^T (and 16
-    # of A) stay below 2^31 bytes and the kernel's 32-bit offsets always fit.
-    ld = (1 << 21) - 4
+    # A workgroup's 32 rows of B^T and the 16 rows of A must each span less
+    # than 2^31 bytes for the kernel's 32-bit offsets; beyond that another
+    # kernel takes the call.
+    ld = (1 << 24) - 4096
     st, pl = gplan(F32, N_, T_, 16, 64, 8192, lda=ld, ldb=ld)
     assert st == OK and "skinny_nt" in kname(pl), pl
-    assert gplan(F32, N_, T_, 16, 64, 8192, ldb=(1 << 21) + 4)[0] != OK
+    st, pl = gplan(F32, N_, T_, 16, 64, 8192, ldb=(1 << 24) + (1 << 20))
+    assert st == OK and "skinny_nt" not in kname(pl), pl
 
 
 def test_skinny_nt_forced_needs_its_layout():

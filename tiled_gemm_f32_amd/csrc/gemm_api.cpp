@@ -25,10 +25,7 @@ namespace {
 
 using gemm::KernelDesc;
 
-constexpr int64_t kMaxDim = 0x7fffffff;   // sizes index with 32-bit integers in the kernels
-// A 256-row fp32 panel then spans at most 256 * (2^21 - 1) * 4 < 2^31 - 1 bytes,
-// so every buffer extent and in-panel offset fits the 31-bit range.
-constexpr int64_t kMaxLd = (int64_t(1) << 21) - 1;
+constexpr int64_t kMaxDim = 0x7fffffff;   // sizes and leading dimensions index with 32-bit integers in the kernels
 constexpr int kComputeUnits = 256;
 
 int table_size() {
@@ -123,7 +120,7 @@ gemm_status validate(const Call &c) {
         }
     }
     if (c.M > kMaxDim || c.N > kMaxDim || c.K > kMaxDim) return GEMM_ERR_UNSUPPORTED;
-    if (c.lda > kMaxLd || c.ldb > kMaxLd) return GEMM_ERR_UNSUPPORTED;
+    if (c.lda > kMaxDim || c.ldb > kMaxDim) return GEMM_ERR_UNSUPPORTED;
     return GEMM_OK;
 }
 
@@ -139,22 +136,50 @@ int max_vec_a(const Call &c) {
 }
 bool vec_b_ok(const Call &c, int v) { return vec_ok(c.B, c.ldb, row_len_b(c), elem_size(c.dtype), v); }
 
-// The skinny kernels address B with 32-bit offsets.  With B stored K x N
-// their prefetch runs at most 48 * WAVES * UNROLL (<= 1536) rows past K, so
-// K + 2048 rows must fit.  With B stored N x K a workgroup's 32 rows of B
-// and the 16 rows of A, each K long, must fit; with A stored K x M, its K
-// rows.
-bool skinny_fits(const Call &c) {
-    if (c.M > 16) return false;
-    const int64_t lim = int64_t(1) << 31;
-    // A stored K x M is addressed row by row: K rows of lda elements.
-    if (c.op_a == GEMM_OP_T && c.K * c.lda * elem_size(c.dtype) >= lim) return false;
-    if (c.op_b == GEMM_OP_T) {
-        const int64_t esz = elem_size(c.dtype);
-        return (32 * c.ldb + c.K) * esz < lim && (16 * c.lda + c.K) * esz < lim;
-    }
-    return (c.K + 2048) * c.ldb * 4 < lim;
+// Buffer addressing.  The kernels read operands through buffer resources
+// whose byte offsets are 32-bit, with 2^31 reserved to mark a load out of
+// range; each resource starts at a panel or slice of an operand (rebased as
+// the kernel walks K, with 64-bit base arithmetic), so what must stay below
+// 2^31 bytes is the extent of one panel or slice, not the operand:
+//   - a panel of rows read whole (A stored M x K, B stored N x K): the
+//     tile's valid rows, each K long rounded up to the k slice (rows past
+//     them are read as the last valid one);
+//   - a slice of k rows (B stored K x N, A stored K x M): tile_k rows of
+//     the leading dimension, the last of them tile_n (tile_m) long;
+//   - the skinny kernels: B stored K x N in batches of tile_k rows; A (16
+//     rows at most) whole, or with A stored K x M as a K-row panel (fp32)
+//     or per 32-row block (bf16); with B stored N x K, 32 rows of B and the
+//     16 rows of A, each K long.
+// The general kernels index with 64-bit element offsets and take anything.
+constexpr int64_t kMaxResourceBytes = (int64_t(1) << 31) - 1;
+
+bool panel_fits(int64_t rows, int64_t ld, int64_t row_len, int64_t esz) {
+    return rows < 1 || ((rows - 1) * ld + row_len) * esz <= kMaxResourceBytes;
 }
+
+bool operands_fit(const KernelDesc *kd, const Call &c) {
+    if (kd->fallback) return true;
+    const int64_t esz = elem_size(c.dtype);
+    const bool a_n = c.op_a == GEMM_OP_N, b_n = c.op_b == GEMM_OP_N;
+    if (kd->path == GEMM_PATH_SKINNY || kd->path == GEMM_PATH_SKINNY_SPLITK) {
+        if (!b_n) return panel_fits(32, c.ldb, c.K, esz) && panel_fits(16, c.lda, c.K, esz);
+        const bool b_ok = panel_fits(kd->tile_k, c.ldb, kd->tile_n, esz);
+        if (a_n) return b_ok && panel_fits(c.M, c.lda, c.K, esz);
+        const int64_t a_rows = c.dtype == GEMM_DTYPE_F32 ? c.K : kd->tile_k;
+        return b_ok && panel_fits(a_rows, c.lda, c.M, esz);
+    }
+    // Rows read whole are addressed up to K rounded up to the k slice (the
+    // chunks past K get 2^31 added, which must not wrap).
+    const int64_t a_panel = c.M < kd->tile_m ? c.M : kd->tile_m;
+    const int64_t b_panel = c.N < kd->tile_n ? c.N : kd->tile_n;
+    const int64_t k_pad = ceil_div(c.K, kd->tile_k) * kd->tile_k;
+    const bool a_ok = a_n ? panel_fits(a_panel, c.lda, k_pad, esz) : panel_fits(kd->tile_k, c.lda, kd->tile_m, esz);
+    const bool b_ok = b_n ? panel_fits(kd->tile_k, c.ldb, kd->tile_n, esz) : panel_fits(b_panel, c.ldb, k_pad, esz);
+    return a_ok && b_ok;
+}
+
+// The skinny kernels take M <= 16.
+bool skinny_fits(const Call &c) { return c.M <= 16; }
 
 int64_t split_workspace_bytes(const Call &c, const KernelDesc *kd) {
     const int64_t strips = ceil_div(c.N, kd->tile_n);
@@ -166,6 +191,7 @@ bool kernel_runs(const KernelDesc *kd, const Call &c) {
     if (((kd->outputs >> c.out_type) & 1) == 0) return false;
     if (((kd->layouts >> (2 * c.op_a + c.op_b)) & 1) == 0) return false;
     if ((kd->path == GEMM_PATH_SKINNY || kd->path == GEMM_PATH_SKINNY_SPLITK) && !skinny_fits(c)) return false;
+    if (!operands_fit(kd, c)) return false;
     if (kd->path == GEMM_PATH_SKINNY_SPLITK) {
         const int64_t need = split_workspace_bytes(c, kd);
         if (need > 0 && (c.ws == nullptr || c.ws_bytes < need)) return false;
@@ -766,32 +792,6 @@ GEMM_API gemm_status gemm_general(int32_t dtype, int32_t op_a, int32_t op_b, int
     return run_epi(c, epilogue, force_kernel, stream);
 }
 
-GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
-                                         int64_t K, float alpha, const void *A, int64_t lda, const void *B,
-                                         int64_t ldb, float beta, const float *C, int64_t ldc, int32_t force_kernel,
-                                         const gemm_epilogue *epilogue, int64_t workspace_bytes, gemm_plan *out) {
-    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
-    const KernelDesc *kd = nullptr;
-    void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
-    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
-    c.op_a = op_a;
-    c.op_b = op_b;
-    apply_epilogue(c, epilogue);
-    KSplit ks;
-    return plan(c, force_kernel, out, &kd, &ks);
-}
-
-GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
-                                             int64_t K, float alpha, const void *A, int64_t lda, const void *B,
-                                             int64_t ldb, float beta, const float *C, int64_t ldc,
-                                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out) {
-    return gemm_plan_query_epi(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, nullptr,
-                               workspace_bytes, out);
-}
-
-
-GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
-                                     const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
 GEMM_API gemm_status gemm_general_noalloc(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
                                           int64_t K, float alpha, const void *A, int64_t lda, const void *B,
                                           int64_t ldb, float beta, float *C, int64_t ldc, int32_t force_kernel,
@@ -819,6 +819,32 @@ GEMM_API gemm_status gemm_general_noalloc(int32_t dtype, int32_t op_a, int32_t o
     return run(c, force_kernel, stream);
 }
 
+GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                         int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                         int64_t ldb, float beta, const float *C, int64_t ldc, int32_t force_kernel,
+                                         const gemm_epilogue *epilogue, int64_t workspace_bytes, gemm_plan *out) {
+    if (out == nullptr) return GEMM_ERR_INVALID_ARG;
+    const KernelDesc *kd = nullptr;
+    void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
+    Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
+    c.op_a = op_a;
+    c.op_b = op_b;
+    apply_epilogue(c, epilogue);
+    KSplit ks;
+    return plan(c, force_kernel, out, &kd, &ks);
+}
+
+GEMM_API gemm_status gemm_plan_query_general(int32_t dtype, int32_t op_a, int32_t op_b, int64_t M, int64_t N,
+                                             int64_t K, float alpha, const void *A, int64_t lda, const void *B,
+                                             int64_t ldb, float beta, const float *C, int64_t ldc,
+                                             int32_t force_kernel, int64_t workspace_bytes, gemm_plan *out) {
+    return gemm_plan_query_epi(dtype, op_a, op_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, force_kernel, nullptr,
+                               workspace_bytes, out);
+}
+
+
+GEMM_API gemm_status gemm_plan_query(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha,
+                                     const void *A, int64_t lda, const void *B, int64_t ldb, float beta,
                                      const float *C, int64_t ldc, int32_t force_kernel, int64_t workspace_bytes,
                                      gemm_plan *out) {
     if (out == nullptr) return GEMM_ERR_INVALID_ARG;
@@ -955,9 +981,9 @@ GEMM_API const char *gemm_status_string(gemm_status status) {
     case GEMM_ERR_UNSUPPORTED: return "unsupported problem or kernel for these operands";
     case GEMM_ERR_LAUNCH: return "HIP kernel launch failed";
     case GEMM_ERR_DEVICE: return "no usable gfx950 device is current";
+    case GEMM_ERR_SCRATCH: return "the problem's K split could need more than the library's static scratch";
     }
     return "unknown status";
 }
 
 }  // extern "C"
-    case GEMM_ERR_SCRATCH: return "the problem's K split could need more than the library's static scratch";

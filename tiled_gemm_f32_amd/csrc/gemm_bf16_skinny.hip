@@ -74,16 +74,20 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     const int kspan = min(K, kbeg + kchunk) - kbeg;
     const int q = lane >> 4, s = lane & 15;
 
-    // Extents end at the split's last k row (B) and A's last row, so rows of
-    // A past M and B rows past the range read as zero; A chunks past the
-    // range (which hold the next range's k) are forced to zero by offset, as
-    // a zero of B times an infinity there would not vanish.
+    // B (and A stored K x M) are addressed through resources rebased at each
+    // block's first k row, with extents ending at the range's last k row: rows
+    // past the range read as zero, and offsets span one 32-row block whatever
+    // the size of the operand.  A stored M x K has one resource ending after
+    // its last valid element (the host keeps it below 2^31 bytes); its rows
+    // at or past M read row M - 1, which only reaches rows of C that are never
+    // written, and its chunks past the range (which hold the next range's k)
+    // are given an offset outside every extent, as a zero of B times an
+    // infinity there would not vanish.
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
-    const rsrc_t ra = AT ? make_rsrc(A + (int64_t)kbeg * lda, clamp_extent(((int64_t)(kspan - 1) * lda + M) * 2))
-                         : make_rsrc(A + kbeg, clamp_extent(((int64_t)(M - 1) * lda + kspan) * 2));
-    const rsrc_t rb =
-        make_rsrc(B + (int64_t)kbeg * ldb + n0, clamp_extent(((int64_t)(kspan - 1) * ldb + (N - n0)) * 2));
+    const rsrc_t ra_mk = make_rsrc(A + kbeg, clamp_extent(((int64_t)(M - 1) * lda + kspan) * 2));
+    const uint16_t *b_range = B + (int64_t)kbeg * ldb + n0;
+    const uint16_t *a_range = A + (int64_t)kbeg * lda;     // A stored K x M
 
     // Load instruction i (0..7) of a block: rows 4i .. 4i+3; lane -> row
     // 4i + lane/16, physical chunk lane%16 holding logical chunk
@@ -107,13 +111,12 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
             const int chunk = (col >> 3) ^ sk_swz(row);
             tr_off[h][cb] = (uint32_t)(row * 256 + 16 * chunk + 2 * (col & 7));
         }
-    // A's load: lane -> row lane/4, 16-byte chunk lane%4 (k = 8 (lane%4) ..);
-    // with AT, lane -> k row lane/2, columns 8 (lane%2) .. +7.  a_kc is the
-    // first k the lane's chunk holds.
+    // A's load: lane -> row lane/4, 16-byte chunk lane%4 (k = 8 (lane%4) ..,
+    // the first of which is a_kc); with AT, lane -> k row lane/2 of the block,
+    // columns 8 (lane%2) .. +7.
     const uint32_t a_goff = AT ? (uint32_t)((lane >> 1) * lda + 8 * (lane & 1)) * 2u
-                               : (uint32_t)((lane >> 2) * lda + 8 * (lane & 3)) * 2u;
-    const int a_kc = AT ? (lane >> 1) : 8 * (lane & 3);
-    const uint32_t a_blk = AT ? (uint32_t)kSkKB * (uint32_t)lda * 2u : (uint32_t)kSkKB * 2u;   // per block
+                               : panel_off(lane >> 2, M, lda, 8 * (lane & 3), 2);
+    const int a_kc = 8 * (lane & 3);
     const uint32_t a_read = (uint32_t)(kSkB + s * 64 + 16 * q);
     // AT: lane s of group q points at k row 8q + s/4 (+4), columns 4 (s%4) .. +3.
     uint32_t at_off[2];
@@ -128,15 +131,19 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     // Block t of this wave is block wave + t*WAVES of the range; it goes to
     // slot t % NSLOT.  Nine loads per block: 8 of B, then A's.
     auto issue = [&](int t, int slot) {
-        const int blk = wave + t * WAVES;
-        const uint32_t boff = (uint32_t)(blk * kSkKB) * (uint32_t)ldb * 2u;
+        const int k0 = (wave + t * WAVES) * kSkKB;
+        const rsrc_t rb = make_rsrc(b_range + (int64_t)k0 * ldb, clamp_extent(((int64_t)(kspan - k0 - 1) * ldb + (N - n0)) * 2));
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(slot_base(slot) + 1024 * i), 16,
-                                                     b_goff[i] + boff, 0, 0, 0);
-        const uint32_t poison = (uint32_t)(blk * kSkKB + a_kc >= kspan) << 31;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_base(slot) + kSkB), 16,
-                                                 a_goff + (uint32_t)blk * a_blk + poison, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(slot_base(slot) + 1024 * i), 16, b_goff[i], 0, 0,
+                                                     0);
+        if constexpr (AT) {
+            const rsrc_t ra = make_rsrc(a_range + (int64_t)k0 * lda, clamp_extent(((int64_t)(kspan - k0 - 1) * lda + M) * 2));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_base(slot) + kSkB), 16, a_goff, 0, 0, 0);
+        } else {
+            const uint32_t off = k0 + a_kc >= kspan ? kOutOfRange : a_goff + (uint32_t)k0 * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_mk, (lds_void *)(slot_base(slot) + kSkB), 16, off, 0, 0, 0);
+        }
     };
     auto consume = [&](int slot) {
         const char *base = slot_base(slot);

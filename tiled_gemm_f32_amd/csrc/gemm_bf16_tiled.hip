@@ -85,7 +85,7 @@ bf16_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
     for (int i = 0; i < Cfg::kAPer; ++i) {
         const int c = tid + i * Cfg::kThreads;
         const int r = c / Cfg::kChunks, ch = c % Cfg::kChunks;
-        a_off[i] = (uint32_t)(r * lda + ch * 8) * 2u;
+        a_off[i] = panel_off(r, a_rows, lda, ch * 8, 2);
         a_k[i] = ch * 8;
         a_lds[i] = r * Cfg::kChunks + swz(r, ch);
     }
@@ -318,14 +318,15 @@ bf16_pipe_kernel(GemmParams p, int tiles_m, int tiles_n) {
     uint32_t a_off[8], b_off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        a_off[i] = (uint32_t)((a_r0 + 32 * i) * lda + 8 * a_ch) * 2u;
+        a_off[i] = panel_off(a_r0 + 32 * i, a_rows, lda, 8 * a_ch, 2);
         b_off[i] = (uint32_t)((8 * b_kg + i) * ldb + 8 * b_ng) * 2u;
     }
     u32x4 ga[8], gb[8];
     auto fetch = [&](int kt) {
         const int k0 = kt * BK;
-        // Rebased per slice: rows past M and rows past K fall outside the
-        // extents; a chunk at or past K in a valid row is forced out of range.
+        // Rebased per slice: rows past K fall outside the extents, rows past M
+        // read row M - 1, and a chunk at or past K in a row of A is forced out
+        // of range.
         const rsrc_t ra = make_rsrc(A + (int64_t)m0 * lda + k0,
                                     clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
         const rsrc_t rb = make_rsrc(B + (int64_t)k0 * ldb + n0,
@@ -539,7 +540,7 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int ra = 16 * blk + (lane >> 2);
         const int lca = (lane & 3) ^ ring_swz_a(ra);
         a_kc[j] = 8 * lca;
-        a_goff[j] = (uint32_t)(ra * lda + 8 * lca) * 2u;
+        a_goff[j] = panel_off(ra, a_rows, lda, 8 * lca, 2);
         if (AT) {
             // Rows of A^T (k rows, m contiguous) laid out as an untransposed B.
             const int mb = blk >> 1, rk = 16 * (blk & 1) + (lane >> 2);
@@ -548,16 +549,16 @@ bf16_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         }
         if (BT) {
             // Rows of B^T (columns of B) laid out as A's rows; same chunk k as A.
-            b_goff[j] = (uint32_t)(ra * ldb + 8 * lca) * 2u;
+            b_goff[j] = panel_off(ra, b_rows, ldb, 8 * lca, 2);
         } else {
             const int nb = blk >> 1, rb = 16 * (blk & 1) + (lane >> 2);
             const int lcb = (lane & 3) ^ (2 * ((rb >> 1) & 1));
             b_goff[j] = (uint32_t)(rb * ldb + 32 * nb + 8 * lcb) * 2u;
         }
     }
-    // Resources of slice kt.  Rebased per slice: rows past M / past K fall
-    // outside the extents; a chunk at or past K in a valid row of A gets 2^31
-    // added to its offset.
+    // Resources of slice kt.  Rebased per slice: k rows past K fall outside
+    // the extents, rows past M (past N for B^T) read the last valid row, and a
+    // chunk at or past K in a row of A (or B^T) gets 2^31 added to its offset.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
         if (AT)
@@ -826,10 +827,10 @@ const KernelDesc kBf16TiledKernels[] = {
      &launch_bf16_ring<4, 4, false, true>, 0, nullptr, kLayoutTN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4",
      &launch_bf16_ring<4, 4, true, true>, 0, nullptr, kLayoutTT, false, kOutAll},
-    BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
     // With B read element by element the 256 x 256 tile does not fit the
     // registers (its staged B values spill to scratch), so B without 16-byte
     // rows takes the 128 x 128 tiles below.
+    BF16_TILED(256, 256, 64, 2, 2, 8, 8, 4),
     BF16_TILED(256, 256, 64, 2, 2, 1, 8, 4),
     BF16_TILED(128, 128, 64, 2, 2, 8, 8, 8),
     BF16_TILED(128, 128, 64, 2, 2, 8, 1, 8),

@@ -44,6 +44,16 @@ __device__ __forceinline__ uint32_t clamp_extent(int64_t bytes) {
     return bytes <= 0 ? 0u : (bytes > (int64_t)kMaxExtent ? kMaxExtent : (uint32_t)bytes);
 }
 
+// Byte offset of element (row, col) of an operand panel whose buffer
+// resource starts at the panel's first row and ends after its last valid row
+// (`rows` of them, rows >= 1).  A row past the last valid one is read as that
+// row instead: such rows only feed outputs that are never stored, and the
+// clamp keeps every offset inside the panel, whose extent the host checks to
+// be below 2^31 bytes, however large the leading dimension.
+__device__ __forceinline__ uint32_t panel_off(int row, int rows, int ld, int col, int esz) {
+    return (uint32_t)(min(row, rows - 1) * ld + col) * (uint32_t)esz;
+}
+
 __device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }

@@ -107,20 +107,23 @@ f32_skinny_kernel(GemmParams p) {
     typedef typename BVec<VEC>::T BT;
     __shared__ float red[WAVES][16][NW];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n0 = blockIdx.x * NW;
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int kq = lane >> 4;     // k group within a 16-deep block
     const int lc = lane & 15;     // A row for the A operand; column group for B
 
-    // Rows of A at or past M, and rows of B at or past K, fall outside these
-    // extents and read as zero.  The prefetch reaches at most 48*WAVES*UNROLL
-    // rows past K and the host guarantees (K + 2048) * ldb * 4 < 2^31 on this
-    // path, so no offset below wraps.
+    // A's extent ends after its last valid element (the host keeps it below
+    // 2^31 bytes): rows at or past M read row M - 1, which only reaches rows
+    // of C that are never stored, and k at or past K reads as zero.  B is
+    // addressed through a resource rebased at the first k row of each batch
+    // of loads, so offsets span one batch (at most 16*WAVES*UNROLL rows)
+    // whatever the size of B; rows at or past K fall outside it and read as
+    // zero.
     const rsrc_t ra = make_rsrc(p.A, clamp_extent((VA == 0 ? (int64_t)(K - 1) * lda + M : (int64_t)(M - 1) * lda + K) * 4));
-    const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + n0,
-                                clamp_extent(((int64_t)(K - 1) * ldb + (N - n0)) * 4));
-    const uint32_t a_base = (uint32_t)(lc * lda + 4 * kq) * 4u;
+    const float *b_strip = static_cast<const float *>(p.B) + n0;
+    const uint32_t a_base = panel_off(lc, M, lda, 4 * kq, 4);
     const uint32_t b_base = (uint32_t)(4 * kq * ldb + VEC * lc) * 4u;
     const uint32_t b_row = (uint32_t)ldb * 4u;
 
@@ -131,12 +134,15 @@ f32_skinny_kernel(GemmParams p) {
     f32x4 av[2][UNROLL];
     BT bv[2][UNROLL][4];
     auto issue = [&](int set, int blk0) {
+        const int k0 = 16 * blk0;
+        const rsrc_t rb = make_rsrc(b_strip + (int64_t)k0 * ldb, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int b = blk0 + u * WAVES;
             av[set][u] = load_a_quad<VA>(ra, a_base, b, kq, lc, K, M, lda);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bv[set][u][j] = BVec<VEC>::load(rb, b_base + (uint32_t)(16 * b + j) * b_row);
+            for (int j = 0; j < 4; ++j)
+                bv[set][u][j] = BVec<VEC>::load(rb, b_base + (uint32_t)(16 * u * WAVES + j) * b_row);
         }
     };
     auto consume = [&](int set) {
@@ -198,7 +204,8 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
     constexpr int NW = 64 * CG;
     __shared__ float red[WAVES][16][NW];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int strip = blockIdx.x, split = blockIdx.y;
     const int n0 = strip * NW;
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
@@ -206,14 +213,15 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
     const int kend = min(K, kbeg + kchunk);
     const int kq = lane >> 4, lc = lane & 15;
 
-    // Extents end at this split's last row, so prefetch past kend reads zeros.
+    // Extents end at this split's last row, so prefetch past kend reads
+    // zeros; rows of A at or past M read row M - 1.  B's resource is rebased
+    // at each batch's first k row (as in the single-pass kernel).
     const rsrc_t ra = VA == 0 ? make_rsrc(static_cast<const float *>(p.A) + (int64_t)kbeg * lda,
                                           clamp_extent(((int64_t)(kend - kbeg - 1) * lda + M) * 4))
                               : make_rsrc(static_cast<const float *>(p.A) + kbeg,
                                           clamp_extent(((int64_t)(M - 1) * lda + (kend - kbeg)) * 4));
-    const rsrc_t rb = make_rsrc(static_cast<const float *>(p.B) + (int64_t)kbeg * ldb + n0,
-                                clamp_extent(((int64_t)(kend - kbeg - 1) * ldb + (N - n0)) * 4));
-    const uint32_t a_base = (uint32_t)(lc * lda + 4 * kq) * 4u;
+    const float *b_split = static_cast<const float *>(p.B) + (int64_t)kbeg * ldb + n0;
+    const uint32_t a_base = panel_off(lc, M, lda, 4 * kq, 4);
     const uint32_t b_base = (uint32_t)(4 * kq * ldb + 4 * lc) * 4u;
     const uint32_t b_row = (uint32_t)ldb * 4u;
     const int kspan = kend - kbeg;
@@ -227,6 +235,9 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
     f32x4 av[2][UNROLL];
     f32x4 bv[2][UNROLL][4][CG];
     auto issue = [&](int set, int blk0) {
+        const int k0 = 16 * blk0;
+        const rsrc_t rb =
+            make_rsrc(b_split + (int64_t)k0 * ldb, clamp_extent(((int64_t)(kspan - k0 - 1) * ldb + (N - n0)) * 4));
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int b = blk0 + u * WAVES;
@@ -235,7 +246,8 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int g = 0; g < CG; ++g)
-                    bv[set][u][j][g] = BVec<4>::load(rb, b_base + (uint32_t)(16 * b + j) * b_row + 256u * g);
+                    bv[set][u][j][g] =
+                        BVec<4>::load(rb, b_base + (uint32_t)(16 * u * WAVES + j) * b_row + 256u * g);
         }
     };
     auto consume = [&](int set) {

@@ -85,8 +85,8 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
 
-    // A row panel: its extent ends right after the last valid element, so rows
-    // at or past M read as zero.  lda < 2^21 keeps every offset below 2^31.
+    // A row panel: its extent ends right after the last valid element (the
+    // host keeps it below 2^31 bytes); rows at or past M read row M - 1.
     const float *a_panel = static_cast<const float *>(p.A) + (int64_t)m0 * lda;
     const int a_rows = min(BM, M - m0);
     const rsrc_t ra = make_rsrc(a_panel, clamp_extent(((int64_t)(a_rows - 1) * lda + K) * 4));
@@ -97,7 +97,7 @@ f32_tiled_kernel(GemmParams p, int tiles_m, int tiles_n) {
     for (int i = 0; i < Cfg::kAPer; ++i) {
         const int c = tid + i * Cfg::kThreads;
         const int r = c / (BK / VA), kc = (c % (BK / VA)) * VA;
-        a_off[i] = (uint32_t)(r * lda + kc) * 4u;
+        a_off[i] = panel_off(r, a_rows, lda, kc, 4);
         a_k[i] = kc;
         a_lds[i] = r * Cfg::kAStride + kc;
     }
@@ -291,12 +291,12 @@ f32_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int row = 16 * (4 * wave + j) + (lane >> 2);
         const int lc = (lane & 3) ^ ((row >> 2) & 3);
         a_kc[j] = 4 * lc;
-        a_goff[j] = AT ? (uint32_t)((4 * wave + j) * lda + 4 * lane) * 4u : (uint32_t)(row * lda + 4 * lc) * 4u;
-        b_goff[j] = BT ? (uint32_t)(row * ldb + 4 * lc) * 4u : (uint32_t)((4 * wave + j) * ldb + 4 * lane) * 4u;
+        a_goff[j] = AT ? (uint32_t)((4 * wave + j) * lda + 4 * lane) * 4u : panel_off(row, a_rows, lda, 4 * lc, 4);
+        b_goff[j] = BT ? panel_off(row, b_rows, ldb, 4 * lc, 4) : (uint32_t)((4 * wave + j) * ldb + 4 * lane) * 4u;
     }
-    // Resources of slice kt, rebased per slice: rows past M / past K (past N
-    // for B^T) fall outside the extents; a chunk at or past K in a valid row
-    // of A (or B^T) gets 2^31 added to its offset.
+    // Resources of slice kt, rebased per slice: k rows past K fall outside the
+    // extents, rows past M (past N for B^T) read the last valid row, and a
+    // chunk at or past K in a row of A (or B^T) gets 2^31 added to its offset.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
         const int k0 = kt * BK;
         if (AT)

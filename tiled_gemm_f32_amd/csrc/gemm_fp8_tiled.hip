@@ -90,12 +90,12 @@ fp8_ring_kernel(GemmParams p, int tiles_m, int tiles_n) {
         kc[j] = 16 * lc;
         const int kr = 4 * (4 * wave + j) + (lane >> 4);
         const int cc = (lane & 15) ^ kn_swz(kr);
-        goff_a[j] = AKN ? (uint32_t)(kr * lda + 16 * cc) : (uint32_t)(row * lda + 16 * lc);
-        goff_b[j] = BKN ? (uint32_t)(kr * ldb + 16 * cc) : (uint32_t)(row * ldb + 16 * lc);
+        goff_a[j] = AKN ? (uint32_t)(kr * lda + 16 * cc) : panel_off(row, a_rows, lda, 16 * lc, 1);
+        goff_b[j] = BKN ? (uint32_t)(kr * ldb + 16 * cc) : panel_off(row, b_rows, ldb, 16 * lc, 1);
     }
-    // Resources of slice kt, rebased per slice.  Rows past M (or N) and
-    // slices past K fall outside the extents; a chunk at or past K in a valid
-    // row gets 2^31 added to its offset.
+    // Resources of slice kt, rebased per slice.  Slices past K fall outside
+    // the extents, rows past M (or N) read the last valid row, and a chunk at
+    // or past K in a row gets 2^31 added to its offset.
     // A K x (M or N) panel's extent ends at its last k row; rows past K and
     // the last row's columns past M (N) read as zero.
     auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {

@@ -10,9 +10,9 @@
 namespace gemm {
 
 // Arguments of one GEMM launch, already validated by the host code:
-// 0 < M, N, K < 2^31, lda and ldb below 2^21 elements (so every in-panel
-// byte offset of a 256-row panel fits the 31-bit buffer extent), pointers
-// aligned to their element size.  A and B are fp32, bf16 or fp8 according
+// 0 < M, N, K < 2^31, lda and ldb below 2^31 elements, every panel or slice
+// the chosen kernel reads through one buffer resource below 2^31 bytes
+// (gemm_api.cpp, operands_fit), pointers aligned to their element size.  A and B are fp32, bf16 or fp8 according
 // to the kernel; C is always fp32.  op_a / op_b are gemm_op layouts; a
 // kernel runs only the layouts its table row lists.
 struct GemmParams {
