@@ -739,7 +739,7 @@ def test_output_types_of_the_kernels():
     outs = {k["name"]: k["outputs"] for k in tg.kernels()}
     assert all(v & 1 for v in outs.values())
     for name in ("f32_mfma32_256x256x16_w2x2_a4b4_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
-                 "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
+                 "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
@@ -754,7 +754,7 @@ def test_output_types_of_the_kernels():
 def test_output_quantisation_choice(out_type):
     # The main shapes keep their kernels, and C may be NULL when beta == 0.
     for dt, M, N, K, name in ((F32, 4096, 4096, 4096, "f32_mfma32_256x256x16_w2x2_a4b4_ring4"),
-                              (BF16, 8192, 8192, 8192, "bf16_mfma32_256x256x32_w2x2_a8b8_ring4")):
+                              (BF16, 8192, 8192, 8192, "bf16_mfma32_256x256x64_w2x2_a8b8_lines")):
         st, pl = eplan(dt, N_, N_, M, N, K, out_type, C=0)
         assert st == OK and kname(pl) == name, pl
     st, pl = eplan(FP8, N_, T_, 8192, 8192, 8192, out_type, C=0)

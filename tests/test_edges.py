@@ -94,7 +94,8 @@ def test_f32_ring_ragged_multi_wave(gpu_available):
 
 
 def test_bf16_ring_ragged_multi_wave(gpu_available):
-    """The ring kernels on a problem with more tiles than compute units:
+    """The ring kernels (and the line-granular one) on a problem with more
+    tiles than compute units:
     4100 x 4296 gives 17 x 17 = 289 tiles of 256 x 256 (two waves, ragged
     last tiles) and K = 1096 gives 35 k slices, the last one partial.
     Integer data: every ring kernel must equal the oracle exactly, with beta
@@ -102,7 +103,8 @@ def test_bf16_ring_ragged_multi_wave(gpu_available):
     M, N, K = 4100, 4296, 1096
     A, B, C0 = make_integer_inputs(M, N, K, seed=300, dtype="bf16f32")
     refs = {(2.0, 0.5): _exact(A, B, C0, 2.0, 0.5), (1.0, 0.0): _exact(A, B, C0, 1.0, 0.0)}
-    ring = [k for k in _kernel_ids(tg.GEMM_DTYPE_BF16F32) if "ring" in tg.gemm_kernel_query(k)["name"]]
+    ring = [k for k in _kernel_ids(tg.GEMM_DTYPE_BF16F32)
+            if "ring" in tg.gemm_kernel_query(k)["name"] or "lines" in tg.gemm_kernel_query(k)["name"]]
     assert ring
     for kid in ring:
         name = tg.gemm_kernel_query(kid)["name"]

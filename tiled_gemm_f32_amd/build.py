@@ -33,7 +33,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libgemm.so")
 
 SOURCES = ["gemm_api.cpp", "gemm_f32_tiled.hip", "gemm_bf16_tiled.hip", "gemm_f32_skinny.hip", "gemm_fp8_tiled.hip",
-           "gemm_general.hip", "gemm_bf16_skinny.hip", "gemm_skinny_nt.hip", "gemm_scratch.hip"]
+           "gemm_general.hip", "gemm_bf16_skinny.hip", "gemm_skinny_nt.hip", "gemm_scratch.hip",
+           "gemm_bf16_lines.hip"]
 HEADERS = ["gemm_device.hpp", "gemm_kernels.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -164,13 +165,13 @@ def resource_markdown(table: dict) -> str:
            "Per-kernel figures from hipcc's kernel-resource remarks, written by",
            "`python -m tiled_gemm_f32_amd.build --resources profiles/kernel_resources.md`",
            f"({len(rows)} kernels; scratch is bytes per lane, LDS bytes per workgroup).", "",
-           "| source | kernel | VGPR | AGPR | SGPR | scratch | VGPR spill | LDS | waves/SIMD |",
-           "|---|---|---|---|---|---|---|---|---|"]
+           "| source | kernel | VGPR | AGPR | SGPR | scratch | VGPR spill | SGPR spill (to lanes) | LDS | waves/SIMD |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
     for k in rows:
         name = re.sub(r"^void gemm::\(anonymous namespace\)::", "", k["name"])
         name = re.sub(r"\(gemm::GemmParams.*$", "", name)
         out.append(f"| {k['source']} | `{name}` | {k.get('vgprs')} | {k.get('agprs')} | {k.get('sgprs')} | "
-                   f"{k.get('scratch')} | {k.get('vgpr_spill')} | {k.get('lds')} | {k.get('occupancy')} |")
+                   f"{k.get('scratch')} | {k.get('vgpr_spill')} | {k.get('sgpr_spill')} | {k.get('lds')} | {k.get('occupancy')} |")
     return "\n".join(out) + "\n"
 
 

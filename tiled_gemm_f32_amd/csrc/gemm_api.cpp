@@ -31,7 +31,7 @@ constexpr int kComputeUnits = 256;
 int table_size() {
     return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
            gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount +
-           gemm::kBf16SplitKernelCount + gemm::kSkinnyNtKernelCount;
+           gemm::kBf16SplitKernelCount + gemm::kSkinnyNtKernelCount + gemm::kBf16LinesKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -39,6 +39,10 @@ const KernelDesc *kernel_by_id(int32_t id) {
     int i = id - 1;
     if (i < gemm::kF32TiledKernelCount) return &gemm::kF32TiledKernels[i];
     i -= gemm::kF32TiledKernelCount;
+    // The line-granular bf16 kernel comes before the other bf16 kernels: the
+    // automatic choice takes the first kernel of a tile size that runs a call.
+    if (i < gemm::kBf16LinesKernelCount) return &gemm::kBf16LinesKernels[i];
+    i -= gemm::kBf16LinesKernelCount;
     if (i < gemm::kBf16TiledKernelCount) return &gemm::kBf16TiledKernels[i];
     i -= gemm::kBf16TiledKernelCount;
     if (i < gemm::kF32SkinnyKernelCount) return &gemm::kF32SkinnyKernels[i];

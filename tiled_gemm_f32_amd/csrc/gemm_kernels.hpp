@@ -112,6 +112,8 @@ extern const KernelDesc kBf16SplitKernels[];
 extern const int kBf16SplitKernelCount;
 extern const KernelDesc kSkinnyNtKernels[];
 extern const int kSkinnyNtKernelCount;
+extern const KernelDesc kBf16LinesKernels[];
+extern const int kBf16LinesKernelCount;
 
 // Size of the library's static device scratch (gemm_scratch.hip), the
 // workspace of gemm_general_noalloc.
