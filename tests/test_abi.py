@@ -230,6 +230,12 @@ def test_f32_tile_choice(M, N, K, tile, grid):
     st, p = plan(F32, M, N, K)
     assert st == OK and p["path"] == tg.GEMM_PATH_TILED
     assert (p["tile_m"], p["grid"]) == (tile, grid)
+    # A workspace changes the choice only where it buys a K split (or a
+    # larger tile that still fills a whole wave).
+    st, pw = plan(F32, M, N, K, ws=1 << 30)
+    assert st == OK and (pw["splits"] > 1 or pw["grid"] >= 256 or (pw["tile_m"], pw["grid"]) == (tile, grid)), pw
+    if (M, N, K) == (1000, 3000, 777):
+        assert (pw["tile_m"], pw["splits"]) == (64, 1), pw
 
 
 def test_bf16_tile_choice():
