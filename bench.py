@@ -57,6 +57,7 @@ EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x819
 # workspace and so no K split.
 CONFIGS = [("f32_256", True), ("f32_4092_beta", True), ("f32_1000x3000x777", True),
            ("f32_16x8192x8192", False)]
+CONFIG_NAMES = [n for n, _ in CONFIGS if n not in STEP]
 SKINNY_COPIES = 3
 CPU_SAMPLE_ROWS = {"f32_4096": 4096, "bf16f32_8192": 4096, "f32_16x8192x8192": 16}
 
@@ -66,8 +67,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=STEP + EXTRA, default=None,
-                    help="time a single workload (of the step, or one of the extra ones)")
+    ap.add_argument("--only", choices=STEP + EXTRA + CONFIG_NAMES, default=None,
+                    help="time a single workload (of the step, an extra one, or one of the other configurations)")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="with --only: call without a workspace (the plain call; no K split)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--observe-clocks", type=float, default=6.0,
                     help="after the timed steps, keep running the step this many seconds while amd-smi samples "
@@ -229,7 +232,7 @@ def main():
             ws = tg.workspace(w.M, w.N, w.K, device=dev, dtype=DTYPES[w.dtype])
         return {"w": w, "A": Ad, "B": Bs, "C": C, "ws": ws, "i": 0, "durs": []}
 
-    calls = [make_call(name) for name in names]
+    calls = [make_call(name, False if args.no_workspace else None) for name in names]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -342,7 +345,8 @@ def main():
         cpu = cpu_baseline(calls)
 
     dtypes = "+".join(d for d in ("f32", "bf16f32", "fp8f32") if any(c["w"].dtype == d for c in calls))
-    metric = METRIC if args.only not in EXTRA else f"GFLOP/s (2MNK/t) {args.only}, % of MI355X MFMA peak"
+    single = args.only is not None and (args.only not in STEP or args.no_workspace)
+    metric = METRIC if not single else f"GFLOP/s (2MNK/t) {args.only}" + (" (no workspace)" if args.no_workspace else "")
     line = {
         "metric": metric, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
