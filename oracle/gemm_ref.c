@@ -116,8 +116,8 @@ void gemm_absbound_f32in(int64_t M, int64_t N, int64_t K, double alpha,
                          double beta, const float *C0, int64_t ldc0,
                          double *out, int64_t ldo)
 {
-    const double aa = alpha < 0 ? -alpha : alpha;
-    const double ab = beta < 0 ? -beta : beta;
+    const double aa = fabs(alpha);
+    const double ab = fabs(beta);
     int64_t i;
 #pragma omp parallel for schedule(static)
     for (i = 0; i < M; ++i) {
@@ -125,20 +125,15 @@ void gemm_absbound_f32in(int64_t M, int64_t N, int64_t K, double alpha,
         for (int64_t j = 0; j < N; ++j)
             row[j] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double a = (double)A[i * lda + k];
-            if (a < 0) a = -a;
+            const double a = fabs((double)A[i * lda + k]);
             const float *brow = B + k * ldb;
-            for (int64_t j = 0; j < N; ++j) {
-                double b = (double)brow[j];
-                row[j] += a * (b < 0 ? -b : b);
-            }
+            for (int64_t j = 0; j < N; ++j)
+                row[j] += a * fabs((double)brow[j]);
         }
         for (int64_t j = 0; j < N; ++j) {
             double v = aa * row[j];
-            if (beta != 0.0) {
-                double c = (double)C0[i * ldc0 + j];
-                v += ab * (c < 0 ? -c : c);
-            }
+            if (beta != 0.0)
+                v += ab * fabs((double)C0[i * ldc0 + j]);
             row[j] = v;
         }
     }
@@ -149,8 +144,8 @@ void gemm_absbound_bf16in(int64_t M, int64_t N, int64_t K, double alpha,
                           double beta, const float *C0, int64_t ldc0,
                           double *out, int64_t ldo)
 {
-    const double aa = alpha < 0 ? -alpha : alpha;
-    const double ab = beta < 0 ? -beta : beta;
+    const double aa = fabs(alpha);
+    const double ab = fabs(beta);
     int64_t i;
 #pragma omp parallel for schedule(static)
     for (i = 0; i < M; ++i) {
@@ -158,20 +153,15 @@ void gemm_absbound_bf16in(int64_t M, int64_t N, int64_t K, double alpha,
         for (int64_t j = 0; j < N; ++j)
             row[j] = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double a = widen_bf16(A[i * lda + k]);
-            if (a < 0) a = -a;
+            const double a = fabs(widen_bf16(A[i * lda + k]));
             const uint16_t *brow = B + k * ldb;
-            for (int64_t j = 0; j < N; ++j) {
-                double b = widen_bf16(brow[j]);
-                row[j] += a * (b < 0 ? -b : b);
-            }
+            for (int64_t j = 0; j < N; ++j)
+                row[j] += a * fabs(widen_bf16(brow[j]));
         }
         for (int64_t j = 0; j < N; ++j) {
             double v = aa * row[j];
-            if (beta != 0.0) {
-                double c = (double)C0[i * ldc0 + j];
-                v += ab * (c < 0 ? -c : c);
-            }
+            if (beta != 0.0)
+                v += ab * fabs((double)C0[i * ldc0 + j]);
             row[j] = v;
         }
     }
@@ -231,8 +221,8 @@ void gemm_absbound_fp8in(int64_t M, int64_t N, int64_t K, double alpha,
                          double beta, const float *C0, int64_t ldc0,
                          double *out, int64_t ldo)
 {
-    const double aa = alpha < 0 ? -alpha : alpha;
-    const double ab = beta < 0 ? -beta : beta;
+    const double aa = fabs(alpha);
+    const double ab = fabs(beta);
     int64_t i;
 #pragma omp parallel for schedule(static)
     for (i = 0; i < M; ++i) {
@@ -265,7 +255,7 @@ void gemm_groupmax_fp8in(int64_t M, int64_t N, int64_t K, double alpha,
                          const uint8_t *A, int64_t lda, const uint8_t *B, int64_t ldb,
                          double *out, int64_t ldo)
 {
-    const double aa = alpha < 0 ? -alpha : alpha;
+    const double aa = fabs(alpha);
     int64_t i;
 #pragma omp parallel for schedule(static)
     for (i = 0; i < M; ++i) {

@@ -91,14 +91,18 @@ def ratio(C_gpu, A, B, C0, alpha, beta):
 def blocked_ratio(C_gpu, A, B, C0, alpha, beta, rows_per_block=1024):
     """Error ratio over every entry of C, with the oracle run on blocks of
     rows (each block's fp64 reference and bound are all that is held)."""
+    import time
     a, b, c0 = host_view(A), host_view(B), C0.numpy()
     worst = 0.0
+    t0 = time.perf_counter()
     for i in range(0, a.shape[0], rows_per_block):
         j = min(i + rows_per_block, a.shape[0])
         ab, cb = np.ascontiguousarray(a[i:j]), np.ascontiguousarray(c0[i:j])
         ref = oracle.gemm_ref(ab, b, alpha, beta, cb)
         D = oracle.gemm_absbound(ab, b, alpha, beta, cb)
         worst = max(worst, oracle.error_ratio(C_gpu[i:j], ref, D))
+        say(f"[oracle] rows {i}..{j - 1} of {a.shape[0]} checked ({time.perf_counter() - t0:.0f} s, "
+            f"{oracle.num_threads()} threads)")
     return worst
 
 

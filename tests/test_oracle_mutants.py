@@ -44,8 +44,8 @@ MUTANTS = [
     ("bf16_B_transposed", [("const uint16_t *brow = B + k * ldb;", "const uint16_t *brow = B + k;", 0),
                            ("row[j] += a * widen_bf16(brow[j]);", "row[j] += a * widen_bf16(brow[j * ldb]);", 0)]),
     ("bf16_beta_dropped", [("v += beta * (double)C0[i * ldc0 + j];", "(void)0;", 1)]),
-    ("absbound_abs_of_B_dropped", [("row[j] += a * (b < 0 ? -b : b);", "row[j] += a * b;", 0)]),
-    ("absbound_beta_dropped", [("v += ab * (c < 0 ? -c : c);", "(void)c;", 0)]),
+    ("absbound_abs_of_B_dropped", [("row[j] += a * fabs((double)brow[j]);", "row[j] += a * (double)brow[j];", 0)]),
+    ("absbound_beta_dropped", [("v += ab * fabs((double)C0[i * ldc0 + j]);", "(void)ab;", 0)]),
     ("absbound_alpha_signed", [("double v = aa * row[j];", "double v = alpha * row[j];", 0)]),
     ("epilogue_bias_dropped", [("z += (double)bias[j];", "(void)bias;", 0)]),
     ("epilogue_bias_row_index", [("z += (double)bias[j];", "z += (double)bias[i % N];", 0)]),

@@ -50,6 +50,7 @@ def test_skinny_workspace_path_full_matrix(gpu_available):
     assert r <= TOL["f32"], r
 
 
+@pytest.mark.timeout(1200)   # about 2.2 TFLOP of fp64 oracle work on the host cores
 def test_bf16_8192_full_matrix(gpu_available):
     """The bf16 8192 cube in the benchmark's own launch (no workspace, the
     kernel the library picks), every one of the 67M entries of C compared
