@@ -305,6 +305,27 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
         float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
 #pragma unroll
         for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col < N) ? p.bias[col + t] : -0.0f;
+        // C = A x B (alpha 1, beta 0, no bias or activation): each run is
+        // stored as read, and eight runs are read from LDS before any is
+        // stored (3% of the whole 8192^3 call against the general loop
+        // below, whose per-run steps and uniform branches the compiler
+        // keeps in order).
+        if (alpha == 1.0f && beta == 0.0f && p.bias == nullptr && act == GEMM_ACT_NONE) {
+            for (int i0 = 0; i0 < 32; i0 += 8) {
+                f32x4 vv[8];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    const int row = 4 * (i0 + ii) + (lane >> 4);
+                    vv[ii] = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
+                }
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    const int grow = m0 + wm * 128 + 4 * (i0 + ii) + (lane >> 4);
+                    if (grow < M && col < N) store_out4<OUT>(p, grow, col, vv[ii], vec_o);
+                }
+            }
+            continue;
+        }
 #pragma unroll 4
         for (int i = 0; i < 32; ++i) {
             const int row = 4 * i + (lane >> 4);
