@@ -248,30 +248,6 @@ def test_split_k_skinny_exact_and_reusable_workspace(gpu_available):
                                       err_msg=f"split-k {M}x{N}x{K}")
 
 
-def test_split_k_reduce_widths_agree(gpu_available):
-    """The reduce kernel finishes 4 outputs per thread when N is a multiple of
-    4 and the workspace is 16-byte aligned, else 1: a workspace 4 bytes off
-    alignment must give the same bits, on random data (epilogue included)."""
-    M, N, K = 16, 4096, 8192
-    g = torch.Generator().manual_seed(77)
-    A = torch.rand(M, K, generator=g) * 2 - 1
-    B = torch.rand(K, N, generator=g) * 2 - 1
-    C0 = torch.rand(M, N, generator=g) * 2 - 1
-    bias = torch.rand(N, generator=g) * 2 - 1
-    n = tg.gemm_workspace_size(tg.GEMM_DTYPE_F32, M, N, K)
-    ws = torch.empty(n + 16, dtype=torch.uint8, device="cuda")
-    Ad, Bd, biasd = A.cuda(), B.cuda(), bias.cuda()
-    outs = []
-    for off in (0, 4):
-        say(f"[split-k reduce] 16x4096x8192 workspace offset {off}")
-        C = C0.cuda()
-        tg.gemm(Ad, Bd, C, alpha=0.75, beta=-0.5, ws=ws[off:off + n], bias=biasd, activation="gelu")
-        outs.append(C.cpu())
-    assert torch.equal(outs[0], outs[1])
-    st, pl = tg.gemm_plan_query(tg.GEMM_DTYPE_F32, M, N, K, 0.75, 0x1000, K, 0x1000, N, -0.5, 0x1000, N, 0, n)
-    assert pl["path"] == tg.GEMM_PATH_SKINNY_SPLITK and pl["grid"] > (N + 127) // 128   # K is split
-
-
 def test_split_k_skinny_deterministic(gpu_available):
     from tiled_gemm_f32_amd.workloads import WORKLOADS, make_inputs
     w = WORKLOADS["f32_16x8192x8192"]

@@ -312,59 +312,39 @@ f32_skinny_splitk_kernel(GemmParams p, float *partials, int splits, int kchunk) 
     }
 }
 
-// C = alpha * (sum over splits, in split order) + beta * C.  Each thread
-// finishes V consecutive outputs of one row (V = 4 when N is a multiple of 4
-// and the workspace is 16-byte aligned: one 16-byte load per slice; else
-// V = 1).  Every slice is loaded before any is added, so the loads'
-// latencies overlap (added as they arrive, each load waited for the previous
-// sum: 4.2 us for four slices of 16 x 8192); the sum runs in split order
-// either way, so both widths give the same bits.
-template <int V>
+// C = alpha * (sum over splits, in split order) + beta * C, one thread per
+// output (consecutive threads along a row of C).  Every slice is loaded
+// before any is added, so the loads' latencies overlap (added as they
+// arrive, each load waited for the previous sum: 4.2 us for four slices of
+// 16 x 8192); the sum runs in split order either way.
 __global__ void __launch_bounds__(256)
 splitk_reduce_kernel(GemmParams p, const float *partials, int splits) {
-    typedef typename BVec<V>::T VT;
     const int64_t total = (int64_t)p.M * p.N;
-    const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= total) return;
-    VT part[kMaxReduceSplits];
+    float part[kMaxReduceSplits];
 #pragma unroll
     for (int t = 0; t < kMaxReduceSplits; ++t) {
         const float *slice = partials + (int64_t)t * total;     // uniform across the workgroup
-        part[t] = t < splits ? *reinterpret_cast<const VT *>(slice + idx) : VT{};
+        part[t] = t < splits ? slice[idx] : 0.0f;
     }
-    VT s = part[0];
+    float s = part[0];
 #pragma unroll
     for (int t = 1; t < kMaxReduceSplits; ++t)
         if (t < splits) s += part[t];
-    // Row and column in 32-bit arithmetic where the matrix allows it (a
-    // 64-bit division is a long instruction sequence).
-    int64_t i, j;
-    if (total <= INT32_MAX) {
-        const int i32 = (int)idx / p.N;
-        i = i32;
-        j = (int)idx - i32 * p.N;
-    } else {
-        i = idx / p.N;
-        j = idx - i * p.N;
-    }
-#pragma unroll
-    for (int c = 0; c < V; ++c) {
-        float v = p.alpha * comp<V>(s, c);
-        if (p.beta != 0.0f) v = fmaf(p.beta, p.C[i * p.ldc + j + c], v);
-        store_out_any(p, i, j + c, epilogue_value(v, j + c, p.bias, p.act));
-    }
+    const int64_t i = idx / p.N, j = idx - i * p.N;
+    float v = p.alpha * s;
+    if (p.beta != 0.0f) v = fmaf(p.beta, p.C[i * p.ldc + j], v);
+    store_out_any(p, i, j, epilogue_value(v, j, p.bias, p.act));
 }
 
 hipError_t launch_reduce(const GemmParams &p, const float *partials, int splits, hipStream_t stream) {
     if (splits < 1 || splits > kMaxReduceSplits) return hipErrorInvalidValue;
     GemmParams args = p;
-    const bool v4 = p.N % 4 == 0 && (reinterpret_cast<uintptr_t>(partials) & 15) == 0;
-    const int64_t per_block = 256 * (v4 ? 4 : 1);
-    const int64_t blocks = ((int64_t)p.M * p.N + per_block - 1) / per_block;
+    const int64_t blocks = ((int64_t)p.M * p.N + 255) / 256;
     void *argv[] = {&args, (void *)&partials, &splits};
-    const void *fn = v4 ? reinterpret_cast<const void *>(&splitk_reduce_kernel<4>)
-                        : reinterpret_cast<const void *>(&splitk_reduce_kernel<1>);
-    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), argv, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&splitk_reduce_kernel), dim3((unsigned)blocks),
+                           dim3(256), argv, 0, stream);
 }
 
 template <int VEC, int VA, int WAVES, int UNROLL>
@@ -414,8 +394,6 @@ template __global__ void f32_skinny_splitk_kernel<2, 4, 8, 1>(GemmParams, float 
 template __global__ void f32_skinny_splitk_kernel<2, 1, 8, 1>(GemmParams, float *, int, int);
 template __global__ void f32_skinny_splitk_kernel<2, 0, 8, 1>(GemmParams, float *, int, int);
 template __global__ void f32_skinny_kernel<2, 0, 8, 4>(GemmParams);
-template __global__ void splitk_reduce_kernel<1>(GemmParams, const float *, int);
-template __global__ void splitk_reduce_kernel<4>(GemmParams, const float *, int);
 
 // Explicit instantiations: the device pass never sees the host-only table.
 #define SKINNY_INSTANTIATE(VEC, VA, WAVES, UNROLL) \
