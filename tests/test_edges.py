@@ -178,6 +178,28 @@ def test_skinny_rows_1_to_16(gpu_available):
         np.testing.assert_array_equal(C.astype(np.float64), _exact(A, B, C0, -1.0, 2.0))
 
 
+def test_skinny_lds_a_kernel_matches_direct_loads(gpu_available):
+    """The single-pass kernel that stages A through LDS pairs the same k in
+    the same order as the kernel that loads A straight into registers: on
+    random data the two give the same bits, for row counts below 16, K not a
+    multiple of its 512-deep batches (nor of 16) and ragged N; on integer
+    data both equal the oracle."""
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    lds, direct = ids["f32_skinny_mfma16_n2_alds_w8_u4"], ids["f32_skinny_mfma16_n2_a4_w8_u4"]
+    for M, N, K in [(16, 8192, 8192), (1, 1000, 1028), (7, 96, 516), (16, 32, 4), (13, 2050, 3000)]:
+        A, B, C0 = make_random_inputs(M, N, K, seed=M + N + K, dist="uniform")
+        st, pl = tg.gemm_plan_query(tg.GEMM_DTYPE_F32, M, N, K, 1.5, 0x1000, K, 0x1000, N, -0.5, 0x1000, N, 0, 0)
+        assert st == tg.GEMM_OK and pl["kernel_id"] == lds, tg.gemm_kernel_query(pl["kernel_id"])["name"]
+        say(f"[skinny lds A] M={M} N={N} K={K}")
+        C1, _, _ = run_gemm(A, B, C0, 1.5, -0.5, kernel=lds)
+        C2, _, _ = run_gemm(A, B, C0, 1.5, -0.5, kernel=direct)
+        np.testing.assert_array_equal(C1, C2, err_msg=f"{M}x{N}x{K}")
+        assert ratio(C1, A, B, C0, 1.5, -0.5) <= TOL["f32"]
+        Ai, Bi, Ci = make_integer_inputs(M, N, K, seed=M * 7 + K)
+        C, _, _ = run_gemm(Ai, Bi, Ci, -1.0, 2.0, kernel=lds)
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(Ai, Bi, Ci, -1.0, 2.0), err_msg=f"{M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16f32"])
 def test_quick_returns(gpu_available, dtype):
     torch_dt = torch.float32 if dtype == "f32" else torch.bfloat16

@@ -187,6 +187,138 @@ f32_skinny_kernel(GemmParams p) {
     }
 }
 
+// Single pass with A staged through LDS (A stored M x K, 16-byte aligned).
+// The kernel above loads each lane's A values straight from memory: every
+// wave instruction touches 16 rows of A 64 bytes at a time, lda apart, and
+// since every strip re-reads all of A, those loads cost as much as a fifth
+// of the call (the same kernel with A held constant in registers takes
+// 47.6 us against 58.6 us at 16 x 8192 x 8192).  Here the workgroup loads
+// the A chunk of a whole batch (16 rows x 16*WAVES*UNROLL k) with each
+// wave instruction reading 1 KB of one row, stores it to LDS, and every wave
+// reads its fragments from there.  Chunks are loaded two batches ahead into
+// registers, written to one of three LDS buffers one batch ahead, and one
+// barrier per batch orders the writes before the reads (the buffer written
+// in batch t last held chunk t - 2, whose readers have all passed the
+// barrier of batch t - 1).  Blocks, their k pairing and the order of the
+// sums are those of f32_skinny_kernel, so the two give identical bits.
+template <int VEC, int WAVES, int UNROLL>
+__global__ void __launch_bounds__(64 * WAVES)
+f32_skinny_lds_kernel(GemmParams p) {
+    static_assert((16 * 16 * WAVES * UNROLL / 256) % WAVES == 0 && (16 * WAVES * UNROLL) % 256 == 0,
+                  "the A chunk splits into whole 1 KB runs, the same number per wave");
+    constexpr int NW = 16 * VEC;
+    constexpr int kStride = WAVES * UNROLL;          // 16-deep blocks per batch
+    constexpr int KC = 16 * kStride;                 // k per batch
+    constexpr int ROW = KC + 4;                      // floats per LDS row (16-byte pad)
+    constexpr int BUF = 16 * ROW;                    // floats per buffer
+    constexpr int RUNS = KC / 256;                   // 1 KB runs per row (64 lanes x 16 bytes)
+    constexpr int PER_WAVE = 16 * RUNS / WAVES;      // A chunk loads per wave
+    typedef typename BVec<VEC>::T BT;
+    __shared__ float red[WAVES][16][NW];
+    __shared__ __attribute__((aligned(16))) float sa[3 * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * NW;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int kq = lane >> 4, lc = lane & 15;
+
+    const rsrc_t ra = make_rsrc(p.A, clamp_extent(((int64_t)(M - 1) * lda + K) * 4));
+    const float *b_strip = static_cast<const float *>(p.B) + n0;
+    const uint32_t b_base = (uint32_t)(4 * kq * ldb + VEC * lc) * 4u;
+    const uint32_t b_row = (uint32_t)ldb * 4u;
+
+    f32x4 acc[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) acc[j] = f32x4{};
+
+    // A chunk c: load j of this wave is row r = (PER_WAVE*wave + j) / RUNS,
+    // run (PER_WAVE*wave + j) % RUNS, lane l's 16 bytes at k = KC*c + 256*run
+    // + 4l (rows past M read row M - 1, whose products reach no stored row;
+    // k past K reads as zero).
+    f32x4 areg[2][PER_WAVE];
+    auto load_a = [&](int set, int c) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int q = PER_WAVE * wave + j, r = q / RUNS;
+            const int k = KC * c + 256 * (q % RUNS) + 4 * lane;
+            areg[set][j] = __builtin_bit_cast(f32x4, load_b128(ra, k < K ? panel_off(r, M, lda, k, 4) : kOutOfRange));
+        }
+    };
+    auto write_a = [&](int set, int c) {
+        float *buf = sa + (c % 3) * BUF;
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int q = PER_WAVE * wave + j;
+            *reinterpret_cast<f32x4 *>(buf + (q / RUNS) * ROW + 256 * (q % RUNS) + 4 * lane) = areg[set][j];
+        }
+    };
+    BT bv[2][UNROLL][4];
+    auto issue_b = [&](int set, int t) {
+        const int k0 = 16 * (t * kStride + wave);
+        const rsrc_t rb = make_rsrc(b_strip + (int64_t)k0 * ldb, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bv[set][u][j] = BVec<VEC>::load(rb, b_base + (uint32_t)(16 * u * WAVES + j) * b_row);
+    };
+    // Batch t: the lane's A values of block wave + u*WAVES of the chunk (row
+    // lc, k = 4*kq .. 4*kq+3 of the block) against B, as in f32_skinny_kernel.
+    auto consume = [&](int set, int t) {
+        const float *buf = sa + (t % 3) * BUF + lc * ROW + 4 * kq;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const f32x4 av = *reinterpret_cast<const f32x4 *>(buf + 16 * (wave + u * WAVES));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c)
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], comp<VEC>(bv[set][u][j], c), acc[c], 0, 0, 0);
+        }
+    };
+
+    const int nb = (K + 15) >> 4;
+    const int nbat = (nb + kStride - 1) / kStride;
+    load_a(0, 0);
+    load_a(1, 1);
+    issue_b(0, 0);
+    write_a(0, 0);
+    for (int t = 0; t < nbat; t += 2) {
+        issue_b(1, t + 1);               // past the end: reads zeros
+        load_a(0, t + 2);
+        write_a(1, t + 1);
+        __syncthreads();
+        consume(0, t);
+        issue_b(0, t + 2);
+        load_a(1, t + 3);
+        write_a(0, t + 2);
+        __syncthreads();
+        consume(1, t + 1);
+    }
+
+    // Register r of lane (kq, lc) is row 4*kq + r, column lc of its 16 x 16 block.
+#pragma unroll
+    for (int c = 0; c < VEC; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][4 * kq + r][VEC * lc + c] = acc[c][r];
+    __syncthreads();
+
+    const float alpha = p.alpha, beta = p.beta;
+    for (int idx = tid; idx < 16 * NW; idx += 64 * WAVES) {
+        const int i = idx / NW, j = idx % NW;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w][i][j];
+        const int col = n0 + j;
+        if (i < M && col < N) {
+            float v = alpha * s;
+            if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)i * p.ldc + col], v);
+            store_out_any(p, i, col, epilogue_value(v, col, p.bias, p.act));
+        }
+    }
+}
+
 // Split-K variant for a caller-provided workspace.  Workgroup (strip, split)
 // covers 64*CG columns (each lane loads 16 bytes of a k row; CG column groups
 // of 64 give 256*CG contiguous bytes per row) over one of `splits` equal
@@ -356,6 +488,15 @@ hipError_t launch_f32_skinny(const GemmParams &p, hipStream_t stream) {
                            dim3((unsigned)strips), dim3(64 * WAVES), argv, 0, stream);
 }
 
+template <int VEC, int WAVES, int UNROLL>
+hipError_t launch_f32_skinny_lds(const GemmParams &p, hipStream_t stream) {
+    const int strips = (p.N + 16 * VEC - 1) / (16 * VEC);
+    GemmParams args = p;
+    void *argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_skinny_lds_kernel<VEC, WAVES, UNROLL>),
+                           dim3((unsigned)strips), dim3(64 * WAVES), argv, 0, stream);
+}
+
 template <int CG, int VA, int WAVES, int UNROLL>
 hipError_t launch_f32_skinny_splitk(const GemmParams &p, void *workspace, hipStream_t stream) {
     const int strips = (p.N + 64 * CG - 1) / (64 * CG);
@@ -394,6 +535,7 @@ template __global__ void f32_skinny_splitk_kernel<2, 4, 8, 1>(GemmParams, float 
 template __global__ void f32_skinny_splitk_kernel<2, 1, 8, 1>(GemmParams, float *, int, int);
 template __global__ void f32_skinny_splitk_kernel<2, 0, 8, 1>(GemmParams, float *, int, int);
 template __global__ void f32_skinny_kernel<2, 0, 8, 4>(GemmParams);
+template __global__ void f32_skinny_lds_kernel<2, 8, 4>(GemmParams);
 
 // Explicit instantiations: the device pass never sees the host-only table.
 #define SKINNY_INSTANTIATE(VEC, VA, WAVES, UNROLL) \
@@ -411,6 +553,8 @@ SKINNY_LIST(SKINNY_INSTANTIATE)
 // The last entry reads A stored K x M (A transposed), with the 2-wide B
 // loads and batches of the first.
 const KernelDesc kF32SkinnyKernels[] = {
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 32, 16 * 8 * 4, 512, 4, 2, "f32_skinny_mfma16_n2_alds_w8_u4",
+     &launch_f32_skinny_lds<2, 8, 4>, 0, nullptr, kLayoutNN, false, kOutAll},
     SKINNY_LIST(SKINNY_ENTRY)
     {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, 32, 16 * 8 * 4, 512, 1, 2, "f32_skinny_mfma16_n2_at_w8_u4",
      &launch_f32_skinny<2, 0, 8, 4>, 0, nullptr, kLayoutTN, false, kOutAll},
