@@ -6,7 +6,9 @@ launch.  The captured sequence mixes the paths: a bf16 ring call, a tiled
 K split (partials, then the reduce kernel), an fp32 M = 16 split call, an
 fp8 call with a fused GELU epilogue, a bf16 decode call with weights stored
 N x K split over K into a bf16 output, and the bf16 ring writing a
-saturating fp8 output.  It is replayed several times, with
+saturating fp8 output, the whole-line bf16 kernel (4096 x 4096 x 1024),
+and the plain fp32 M = 16 call (A staged through LDS, no workspace).  It
+is replayed several times, with
 eager work and synchronisations between replays, and every replay must
 reproduce the eager results bit for bit (every path is deterministic).
 """
@@ -38,13 +40,21 @@ def test_graph_capture_and_replay(gpu_available):
     A5, B5, _ = make_random_inputs(16, 2048, 4096, seed=905, dist="normal", dtype="bf16f32")
     B5t = _dev(B5.t().contiguous())
     A5 = _dev(A5)
+    A6, B6, _ = make_random_inputs(4096, 4096, 1024, seed=906, dist="normal", dtype="bf16f32")
+    A7, B7, _ = make_random_inputs(16, 4096, 2048, seed=907, dist="normal", dtype="f32")
+    A6, B6, A7, B7 = (_dev(t) for t in (A6, B6, A7, B7))
     ws2 = tg.workspace(256, 512, 6000)
     ws3 = tg.workspace(16, 4096, 8192)
     ws5 = tg.workspace(16, 2048, 4096, dtype=tg.GEMM_DTYPE_BF16F32)
     outs = [torch.empty(1024, 1024, device="cuda"), torch.empty(256, 512, device="cuda"),
             torch.empty(16, 4096, device="cuda"), torch.empty(512, 768, device="cuda"),
             torch.empty(16, 2048, dtype=torch.bfloat16, device="cuda"),
-            torch.empty(1024, 1024, dtype=torch.float8_e4m3fn, device="cuda")]
+            torch.empty(1024, 1024, dtype=torch.float8_e4m3fn, device="cuda"),
+            torch.empty(4096, 4096, device="cuda"), torch.empty(16, 4096, device="cuda")]
+    names = {k["id"]: k["name"] for k in tg.kernels()}
+    for (M, N, K, dt) in [(4096, 4096, 1024, tg.GEMM_DTYPE_BF16F32), (16, 4096, 2048, tg.GEMM_DTYPE_F32)]:
+        st, pl = tg.gemm_plan_query(dt, M, N, K, 1.0, A6.data_ptr(), K, B6.data_ptr(), N, 0.0, A6.data_ptr(), N, 0, 0)
+        assert st == tg.GEMM_OK and ("lines" in names[pl["kernel_id"]] or "alds" in names[pl["kernel_id"]])
 
     def sequence():
         tg.gemm(A1, B1, outs[0])
@@ -55,6 +65,9 @@ def test_graph_capture_and_replay(gpu_available):
         tg.gemm(A5, B5t, None, op_b="T", ws=ws5, out=outs[4], out_scale=0.5)
         # the bf16 ring with a saturating fp8 output
         tg.gemm(A1, B1, None, out=outs[5], out_scale=0.01)
+        # the whole-line bf16 kernel; the plain fp32 M = 16 call
+        tg.gemm(A6, B6, outs[6])
+        tg.gemm(A7, B7, outs[7])
 
     say("[graph] eager reference")
     sequence()
