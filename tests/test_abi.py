@@ -524,10 +524,13 @@ def test_nt_takes_the_ring_kernels():
     st, pl = gplan(FP8, N_, T_, 8192, 8192, 8192)
     assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4", pl
     assert pl["grid"] == 32 * 32 and pl["splits"] == 1
+    # bf16 with B stored N x K: the whole-line kernel from K = 1024, the ring below.
     st, pl = gplan(BF16, N_, T_, 8192, 8192, 8192)
-    assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", pl
-    # The bf16 B^T ring needs only 16-byte rows of B^T: N is free.
+    assert st == OK and kname(pl) == "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines", pl
+    # Both need only 16-byte rows of B^T: N is free.
     st, pl = gplan(BF16, N_, T_, 1000, 1001, 1040)
+    assert st == OK and kname(pl) == "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines", pl
+    st, pl = gplan(BF16, N_, T_, 1000, 1001, 1000)
     assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", pl
     st, pl = gplan(BF16, N_, T_, 1000, 1001, 1044)
     assert st == OK and kname(pl) == "bf16_general_128x128x16", pl
@@ -620,6 +623,9 @@ def test_wave_tail_other_layouts(dtype, ops):
 @pytest.mark.parametrize("ops,name", [((N_, T_), "nt"), ((T_, N_), "tn"), ((T_, T_), "tt")])
 def test_bf16_transposed_layouts_take_their_rings(ops, name):
     st, pl = gplan(BF16, ops[0], ops[1], 8192, 8192, 8192)
+    expect = "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines" if name == "nt" else f"bf16_mfma32_256x256x32_w2x2_a8b8_{name}_ring4"
+    assert st == OK and kname(pl) == expect, pl
+    st, pl = gplan(BF16, ops[0], ops[1], 8192, 8192, 512)      # below the whole-line kernel's K minimum
     assert st == OK and kname(pl) == f"bf16_mfma32_256x256x32_w2x2_a8b8_{name}_ring4", pl
     # A^T rows are M long: M not a multiple of 8 leaves only the general kernel.
     if ops[0] == T_:
@@ -745,7 +751,8 @@ def test_output_types_of_the_kernels():
     outs = {k["name"]: k["outputs"] for k in tg.kernels()}
     assert all(v & 1 for v in outs.values())
     for name in ("f32_mfma32_256x256x16_w2x2_a4b4_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
-                 "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
+                 "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
+                 "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",

@@ -233,6 +233,66 @@ def test_transposed_ring_epilogue_and_c_alignment(gpu_available, ring_case, act,
     check(C, As, Bs, C0, alpha, -0.5, op_a, op_b, dtype, bias=bias, act=act)
 
 
+NT_LINES = "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines"
+NT_LINES_SHAPES = [
+    (256, 256, 1024),      # one tile
+    (1000, 1001, 1040),    # ragged M and N (runs of 4 columns straddle N), a partial last slice
+    (33, 2048, 4096),      # thin M
+    (2048, 40, 2048),      # thin N
+    (4100, 4300, 1096),    # more tiles than compute units, ragged last tiles
+]
+
+
+@pytest.mark.parametrize("shape", NT_LINES_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_nt_lines_kernel(gpu_available, shape):
+    """The whole-line bf16 kernel with B stored N x K, forced: exact on
+    integer data, and on random data the same bits as the B-transposed ring
+    kernel (the same k pairing and summation order per lane)."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    lines, ring = ids[NT_LINES], ids[BF16_NT_RING]
+    ok, _ = runnable("bf16f32", "N", "T", M, N, K, lines)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=720, dtype="bf16f32")
+    As, Bs = stored(A, B, "N", "T")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[nt lines] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=720")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=lines, op_a="N", op_b="T")
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, "N", "T"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=721, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "N", "T")
+    say(f"[nt lines] random M={M} N={N} K={K} seed=721, against the ring")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=lines, op_a="N", op_b="T")
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_a="N", op_b="T")
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, "N", "T", "bf16f32")
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+@pytest.mark.parametrize("c_offset", [0, 1])
+def test_nt_lines_epilogue_and_c_alignment(gpu_available, act, c_offset):
+    M, N, K = 520, 777, 1024
+    A, B, C0 = make_random_inputs(M, N, K, seed=722, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "N", "T")
+    bias = make_bias(N, seed=723)
+    lines = [k["id"] for k in tg.kernels() if k["name"] == NT_LINES][0]
+    say(f"[nt lines] epilogue act={act} M={M} N={N} K={K} c_offset={c_offset}")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0 / np.sqrt(K), -0.5, kernel=lines, offset=(0, 0, c_offset), bias=bias,
+                       activation=act, op_a="N", op_b="T")
+    check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "bf16f32", bias=bias, act=act)
+
+
+def test_nt_lines_is_the_choice_for_weights_stored_n_by_k():
+    """bf16 A x B^T with K >= 1024 and whole 16-byte rows goes to the
+    whole-line kernel; K below 1024 stays on the ring."""
+    st, pl = tg.gemm_plan_query_general(DT["bf16f32"], 0, 1, 8192, 8192, 8192, 1.0, 0x1000, 8192, 0x1000, 8192,
+                                        0.0, 0x1000, 8192, 0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] == NT_LINES
+    st, pl = tg.gemm_plan_query_general(DT["bf16f32"], 0, 1, 8192, 8192, 512, 1.0, 0x1000, 512, 0x1000, 512,
+                                        0.0, 0x1000, 8192, 0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] != NT_LINES
+
+
 def test_fp8_ring_deterministic_and_bench_shape_sampled(gpu_available):
     """fp8 8192^3 (A x B^T): integer data exact on sampled rows and columns,
     normal data within the bound; 5 calls give the same bits."""

@@ -51,7 +51,7 @@ namespace {
 __device__ __forceinline__ int lines_swz_a(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lines_swz_b(int row) { return 4 * ((row >> 1) & 1); }
 
-template <int OUT>
+template <int OUT, bool BT>
 __global__ void __launch_bounds__(256)
 bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint16_t>(p);
@@ -74,7 +74,7 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
-    const int a_rows = min(BM, M - m0);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
 
     // A load j (0..7) of this wave for a pair: rows 8g .. 8g+7 with g = 8*wave
     // + j (lane -> row 8g + lane/8, physical chunk lane%8), landing at
@@ -82,7 +82,7 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // 64*wave ..), k rows 8j .. 8j+7 (lane -> row 8j + lane/8), landing at
     // stage + 4096 wave + 1024 j.
     uint32_t a_goff[8], b_goff[4];
-    int a_kc[8];
+    int a_kc[8], b_kc[4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int row = 8 * (8 * wave + j) + (lane >> 3);
@@ -92,9 +92,21 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int row = 8 * j + (lane >> 3);
-        const int lc = (lane & 7) ^ lines_swz_b(row);
-        b_goff[j] = (uint32_t)(row * ldb + 64 * wave + 8 * lc) * 2u;
+        if (BT) {
+            // B stored N x K: its slice is 256 rows (columns of C) of 64
+            // bytes, laid out as the ring kernel lays out A's slice (chunk
+            // c of row r at c ^ ((r >> 2) & 3)); load j fills rows
+            // 16*(4*wave + j) .. +15 (lane -> row 16*(4*wave + j) + lane/4).
+            const int row = 16 * (4 * wave + j) + (lane >> 2);
+            const int lc = (lane & 3) ^ ((row >> 2) & 3);
+            b_kc[j] = 8 * lc;
+            b_goff[j] = panel_off(row, b_rows, ldb, 8 * lc, 2);
+        } else {
+            const int row = 8 * j + (lane >> 3);
+            const int lc = (lane & 7) ^ lines_swz_b(row);
+            b_kc[j] = 0;
+            b_goff[j] = (uint32_t)(row * ldb + 64 * wave + 8 * lc) * 2u;
+        }
     }
     // Resources: pair P of A (k 64P ..) and slice s of B (k rows 32s ..),
     // rebased per use.  k rows past K fall outside B's extent; A chunks at or
@@ -105,6 +117,8 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     };
     auto rsrc_b = [&](int s) {
         const int k0 = BK * s;
+        if (BT)
+            return make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 2));
         return make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
     };
     auto dma_a = [&](int P, int si, const rsrc_t &ra, int j) {
@@ -113,10 +127,17 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(stage + (8 * wave + j) * 1024), 16,
                                                  a_goff[j] + poison, 0, 0, 0);
     };
-    auto dma_b = [&](int si, const rsrc_t &rb, int j) {
+    auto dma_b = [&](int s, int si, const rsrc_t &rb, int j) {
         char *stage = b_stage(si);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage + 4096 * wave + 1024 * j), 16, b_goff[j], 0,
-                                                 0, 0);
+        if (BT) {
+            // A chunk at or past K in a valid row would read the next row.
+            const uint32_t poison = (uint32_t)(b_kc[j] >= K - BK * s) << 31;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage + 1024 * (4 * wave + j)), 16,
+                                                     b_goff[j] + poison, 0, 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(stage + 4096 * wave + 1024 * j), 16, b_goff[j],
+                                                     0, 0, 0);
+        }
     };
 
     // Fragment reads.  A fragment f, k half s of a slice with pair parity
@@ -136,6 +157,12 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int fp = 0; fp < 2; ++fp)
         fb_off[fp] = (uint32_t)(wn * 2 * 4096 + brow * 128 + 16 * (bx + 4 * (fp ^ bsw)) + 8 * (j16 & 1));
+    // B stored N x K: fragment f, k half s is row wn*128 + 32f + l32 of the
+    // slice, logical chunk 2s + h (16-byte reads, as the ring kernel reads A).
+    uint32_t fbt_off[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+        fbt_off[s2] = (uint32_t)((wn * 128 + l32) * 64 + 16 * ((2 * s2 + h) ^ ((l32 >> 2) & 3)));
 
     bf16x8 fa[2][4], fb[2][4];
     // Read slot r (0..7) of half s of slice (A stage asi, parity par; B stage
@@ -147,6 +174,9 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
             const int f = r == 0 ? 0 : r - 4;
             const int c = (4 * par + 2 * s + h) ^ a_sw;
             fa[set][f] = *reinterpret_cast<const bf16x8 *>(as + fa_row + 4096 * f + 16 * c);
+        } else if (BT) {
+            const int f = r - 1;
+            fb[set][f] = *reinterpret_cast<const bf16x8 *>(bs + fbt_off[s] + 2048 * f);
         } else {
             const int f = r - 1;
             const uint32_t off = fb_off[f & 1] + 4096 * (f >> 1) + 2048 * s;
@@ -186,17 +216,17 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) dma_a(0, 0, ra0, j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma_b(0, rb0, j);
+        for (int j = 0; j < 4; ++j) dma_b(0, 0, rb0, j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma_b(1, rb1, j);
+        for (int j = 0; j < 4; ++j) dma_b(1, 1, rb1, j);
 #pragma unroll
         for (int j = 0; j < 8; ++j) dma_a(1, 1, ra1, j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma_b(2, rb2, j);
+        for (int j = 0; j < 4; ++j) dma_b(2, 2, rb2, j);
         dma_a(2, 2, ra2, 0);
         dma_a(2, 2, ra2, 1);
-        dma_b(3, rb3, 0);
-        dma_b(3, rb3, 1);
+        dma_b(3, 3, rb3, 0);
+        dma_b(3, 3, rb3, 1);
     }
     // Resources carried into the next block: B slice kt + 3 and A pair
     // (kt + 4) / 2, for block 1 of slice kt.
@@ -222,9 +252,9 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
             mma(0, t);
             if (t < 8) read_slot(as, u & 1, bs, 1, 1, t);
             else if (t == 9) dma_a(P1, a1, ra_pend, 2 * q1);
-            else if (t == 11) dma_b(b1, rb_pend, 2);
+            else if (t == 11) dma_b(kt + 3, b1, rb_pend, 2);
             else if (t == 13) dma_a(P1, a1, ra_pend, 2 * q1 + 1);
-            else if (t == 15) dma_b(b1, rb_pend, 3);
+            else if (t == 15) dma_b(kt + 3, b1, rb_pend, 3);
             else if (t == 8) ra_next = rsrc_a(P2);
             else if (t == 10) rb_next = rsrc_b(kt + 4);
             __builtin_amdgcn_sched_barrier(0);
@@ -243,9 +273,9 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
             mma(1, t);
             if (t & 1) read_slot(as_n, (u + 1) & 1, bs_n, 0, 0, t >> 1);
             else if (t == 0) dma_a(P2, a2, ra_next, 2 * q2);
-            else if (t == 2) dma_b(b2, rb_next, 0);
+            else if (t == 2) dma_b(kt + 4, b2, rb_next, 0);
             else if (t == 4) dma_a(P2, a2, ra_next, 2 * q2 + 1);
-            else if (t == 6) dma_b(b2, rb_next, 1);
+            else if (t == 6) dma_b(kt + 4, b2, rb_next, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         rb_pend = rb_next;
@@ -304,7 +334,12 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
         const int col = n0 + wn * 128 + 64 * pass + 4 * cc;
         float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
 #pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col < N) ? p.bias[col + t] : -0.0f;
+        for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && (BT ? col + t < N : col < N)) ? p.bias[col + t] : -0.0f;
+        // With B stored N x K, N is free: a run of 4 columns may straddle
+        // it, and such a run is read and stored element by element.  (With
+        // B stored K x N its rows are whole 16-byte chunks, so N is a
+        // multiple of 8.)
+        const bool whole = !BT || col + 4 <= N;
         // C = A x B (alpha 1, beta 0, no bias or activation): each run is
         // stored as read, and eight runs are read from LDS before any is
         // stored (3% of the whole 8192^3 call against the general loop
@@ -321,7 +356,11 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) {
                     const int grow = m0 + wm * 128 + 4 * (i0 + ii) + (lane >> 4);
-                    if (grow < M && col < N) store_out4<OUT>(p, grow, col, vv[ii], vec_o);
+                    if (grow >= M || col >= N) continue;
+                    if (whole)
+                        store_out4<OUT>(p, grow, col, vv[ii], vec_o);
+                    else
+                        store_out_first<OUT>(p, grow, col, vv[ii], N - col);
                 }
             }
             continue;
@@ -337,11 +376,11 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
             if (beta != 0.0f) {
                 const float *cp = p.C + (int64_t)grow * p.ldc + col;
                 f32x4 c0;
-                if (vec_c) {
+                if (whole && vec_c) {
                     c0 = *reinterpret_cast<const f32x4 *>(cp);
                 } else {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) c0[t] = cp[t];
+                    for (int t = 0; t < 4; ++t) c0[t] = (!BT || col + t < N) ? cp[t] : 0.0f;
                 }
 #pragma unroll
                 for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
@@ -355,33 +394,42 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t) v[t] = ActRelu::apply(v[t]);
             }
-            store_out4<OUT>(p, grow, col, v, vec_o);
+            if (whole)
+                store_out4<OUT>(p, grow, col, v, vec_o);
+            else
+                store_out_first<OUT>(p, grow, col, v, N - col);
         }
     }
 }
 
+template <bool BT>
 hipError_t launch_bf16_lines(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     const int out = launch_out_type(p);
-    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines_kernel<GEMM_OUT_BF16>)
-                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines_kernel<GEMM_OUT_FP8>)
-                                           : reinterpret_cast<const void *>(&bf16_lines_kernel<GEMM_OUT_F32>);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines_kernel<GEMM_OUT_BF16, BT>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines_kernel<GEMM_OUT_FP8, BT>)
+                                           : reinterpret_cast<const void *>(&bf16_lines_kernel<GEMM_OUT_F32, BT>);
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
                            stream);
 }
 
-template __global__ void bf16_lines_kernel<GEMM_OUT_F32>(GemmParams, int, int);
-template __global__ void bf16_lines_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
-template __global__ void bf16_lines_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void bf16_lines_kernel<GEMM_OUT_F32, false>(GemmParams, int, int);
+template __global__ void bf16_lines_kernel<GEMM_OUT_BF16, false>(GemmParams, int, int);
+template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, false>(GemmParams, int, int);
+template __global__ void bf16_lines_kernel<GEMM_OUT_F32, true>(GemmParams, int, int);
+template __global__ void bf16_lines_kernel<GEMM_OUT_BF16, true>(GemmParams, int, int);
+template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, true>(GemmParams, int, int);
 
 }  // namespace
 
 #if !defined(__HIP_DEVICE_COMPILE__)
 const KernelDesc kBf16LinesKernels[] = {
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_lines",
-     &launch_bf16_lines, 1024, nullptr, kLayoutNN, false, kOutAll},
+     &launch_bf16_lines<false>, 1024, nullptr, kLayoutNN, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
+     &launch_bf16_lines<true>, 1024, nullptr, kLayoutNT, false, kOutAll},
 };
 const int kBf16LinesKernelCount = sizeof(kBf16LinesKernels) / sizeof(kBf16LinesKernels[0]);
 #endif
