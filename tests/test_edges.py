@@ -198,6 +198,10 @@ def test_skinny_lds_a_kernel_matches_direct_loads(gpu_available):
         Ai, Bi, Ci = make_integer_inputs(M, N, K, seed=M * 7 + K)
         C, _, _ = run_gemm(Ai, Bi, Ci, -1.0, 2.0, kernel=lds)
         np.testing.assert_array_equal(C.astype(np.float64), _exact(Ai, Bi, Ci, -1.0, 2.0), err_msg=f"{M}x{N}x{K}")
+        # A and B inside wider NaN-padded rows (A's padding a multiple of 4, so
+        # its rows stay 16-byte aligned), C padded by an odd amount.
+        C, _, _ = run_gemm(Ai, Bi, Ci, -1.0, 2.0, kernel=lds, pad=(12, 6, 3))
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(Ai, Bi, Ci, -1.0, 2.0), err_msg=f"padded {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16f32"])

@@ -282,6 +282,21 @@ def test_nt_lines_epilogue_and_c_alignment(gpu_available, act, c_offset):
     check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "bf16f32", bias=bias, act=act)
 
 
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_lines_kernels_padded_operands(gpu_available, op_b):
+    """The whole-line kernels on operands inside wider buffers: A, B and C
+    padded by 8, 24 and 5 elements per row, the padding NaN (it must never
+    reach C), ragged M, N and K; integer data, so the result is exact."""
+    name = NT_LINES if op_b == "T" else "bf16_mfma32_256x256x64_w2x2_a8b8_lines"
+    kid = [k["id"] for k in tg.kernels() if k["name"] == name][0]
+    for M, N, K in [(300, 520 if op_b == "N" else 517, 1096), (1030, 264, 2056)]:
+        A, B, C0 = make_integer_inputs(M, N, K, seed=730 + M, dtype="bf16f32")
+        As, Bs = stored(A, B, "N", op_b)
+        say(f"[lines padded] {name} M={M} N={N} K={K} pad=(8, 24, 5)")
+        C, _, _ = run_gemm(As, Bs, C0, 2.0, -1.0, kernel=kid, pad=(8, 24, 5), op_a="N", op_b=op_b)
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, 2.0, -1.0, "N", op_b))
+
+
 def test_nt_lines_is_the_choice_for_weights_stored_n_by_k():
     """bf16 A x B^T with K >= 1024 and whole 16-byte rows goes to the
     whole-line kernel; K below 1024 stays on the ring."""
