@@ -522,8 +522,10 @@ def test_general_nn_matches_plain_query():
 
 def test_nt_takes_the_ring_kernels():
     st, pl = gplan(FP8, N_, T_, 8192, 8192, 8192)
-    assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4", pl
+    assert st == OK and kname(pl) == "fp8_mfma32_256x256x128_w2x2_nt_lines", pl
     assert pl["grid"] == 32 * 32 and pl["splits"] == 1
+    st, pl = gplan(FP8, N_, T_, 8192, 8192, 512)      # below the whole-line kernel's K minimum
+    assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4", pl
     # bf16 with B stored N x K: the whole-line kernel from K = 1024, the ring below.
     st, pl = gplan(BF16, N_, T_, 8192, 8192, 8192)
     assert st == OK and kname(pl) == "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines", pl
@@ -754,6 +756,7 @@ def test_output_types_of_the_kernels():
                  "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
+                 "fp8_mfma32_256x256x128_w2x2_nt_lines",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
                  "fp8_skinny_nt_splitk_n32_w8_u2"):
@@ -771,7 +774,7 @@ def test_output_quantisation_choice(out_type):
         st, pl = eplan(dt, N_, N_, M, N, K, out_type, C=0)
         assert st == OK and kname(pl) == name, pl
     st, pl = eplan(FP8, N_, T_, 8192, 8192, 8192, out_type, C=0)
-    assert st == OK and kname(pl) == "fp8_mfma32_256x256x64_w2x2_nt_ring4"
+    assert st == OK and kname(pl) == "fp8_mfma32_256x256x128_w2x2_nt_lines"
     st, pl = eplan(BF16, N_, T_, 16, 8192, 8192, out_type, C=0)
     assert st == OK and kname(pl) == "bf16_skinny_nt_n32_w8_u2"
     # Short K: the 256-tile kernels preferred there write fp32 only, so a

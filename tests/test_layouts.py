@@ -282,6 +282,49 @@ def test_nt_lines_epilogue_and_c_alignment(gpu_available, act, c_offset):
     check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "bf16f32", bias=bias, act=act)
 
 
+FP8_LINES = "fp8_mfma32_256x256x128_w2x2_nt_lines"
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 1024), (1000, 1001, 1040), (33, 2048, 4096), (2048, 40, 2048),
+                                   (4100, 4300, 1088), (300, 264, 80)], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_lines_kernel(gpu_available, shape):
+    """The whole-line fp8 kernel (B stored N x K), forced: exact on integer
+    data (K of 80 is one whole pair and a partial one), and on random data
+    the same bits as the fp8 ring (the same byte pairing and run order)."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    lines, ring = ids[FP8_LINES], ids[FP8_RING]
+    ok, _ = runnable("fp8f32", "N", "T", M, N, K, lines)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=740, dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[fp8 lines] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=740")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=lines, op_a="N", op_b="T")
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, "N", "T"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=741, dist="normal", dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    say(f"[fp8 lines] random M={M} N={N} K={K} seed=741, against the ring")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=lines, op_a="N", op_b="T")
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_a="N", op_b="T")
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, "N", "T", "fp8f32")
+
+
+def test_fp8_lines_epilogue_padded(gpu_available):
+    """Bias and GELU with A, B and C inside NaN-padded rows (padding 16, 48
+    and 3 elements), ragged N."""
+    M, N, K = 520, 777, 1024
+    A, B, C0 = make_random_inputs(M, N, K, seed=742, dist="normal", dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    bias = make_bias(N, seed=743)
+    lines = [k["id"] for k in tg.kernels() if k["name"] == FP8_LINES][0]
+    say(f"[fp8 lines] epilogue gelu, padded, M={M} N={N} K={K}")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0 / np.sqrt(K), -0.5, kernel=lines, pad=(16, 48, 3), bias=bias,
+                       activation="gelu", op_a="N", op_b="T")
+    check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "fp8f32", bias=bias, act="gelu")
+
+
 @pytest.mark.parametrize("op_b", ["N", "T"])
 def test_lines_kernels_padded_operands(gpu_available, op_b):
     """The whole-line kernels on operands inside wider buffers: A, B and C

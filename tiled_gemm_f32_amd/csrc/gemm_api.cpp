@@ -31,7 +31,8 @@ constexpr int kComputeUnits = 256;
 int table_size() {
     return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
            gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount +
-           gemm::kBf16SplitKernelCount + gemm::kSkinnyNtKernelCount + gemm::kBf16LinesKernelCount;
+           gemm::kBf16SplitKernelCount + gemm::kSkinnyNtKernelCount + gemm::kBf16LinesKernelCount +
+           gemm::kFp8LinesKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -49,6 +50,9 @@ const KernelDesc *kernel_by_id(int32_t id) {
     i -= gemm::kF32SkinnyKernelCount;
     if (i < gemm::kF32SplitKernelCount) return &gemm::kF32SplitKernels[i];
     i -= gemm::kF32SplitKernelCount;
+    // Likewise the line-granular fp8 kernel before the fp8 rings.
+    if (i < gemm::kFp8LinesKernelCount) return &gemm::kFp8LinesKernels[i];
+    i -= gemm::kFp8LinesKernelCount;
     if (i < gemm::kFp8TiledKernelCount) return &gemm::kFp8TiledKernels[i];
     i -= gemm::kFp8TiledKernelCount;
     if (i < gemm::kGeneralKernelCount) return &gemm::kGeneralKernels[i];

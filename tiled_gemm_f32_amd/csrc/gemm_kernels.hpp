@@ -114,6 +114,8 @@ extern const KernelDesc kSkinnyNtKernels[];
 extern const int kSkinnyNtKernelCount;
 extern const KernelDesc kBf16LinesKernels[];
 extern const int kBf16LinesKernelCount;
+extern const KernelDesc kFp8LinesKernels[];
+extern const int kFp8LinesKernelCount;
 
 // Size of the library's static device scratch (gemm_scratch.hip), the
 // workspace of gemm_general_noalloc.
