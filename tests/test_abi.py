@@ -625,7 +625,8 @@ def test_wave_tail_other_layouts(dtype, ops):
 @pytest.mark.parametrize("ops,name", [((N_, T_), "nt"), ((T_, N_), "tn"), ((T_, T_), "tt")])
 def test_bf16_transposed_layouts_take_their_rings(ops, name):
     st, pl = gplan(BF16, ops[0], ops[1], 8192, 8192, 8192)
-    expect = "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines" if name == "nt" else f"bf16_mfma32_256x256x32_w2x2_a8b8_{name}_ring4"
+    expect = {"nt": "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines", "tn": "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines",
+              "tt": "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4"}[name]
     assert st == OK and kname(pl) == expect, pl
     st, pl = gplan(BF16, ops[0], ops[1], 8192, 8192, 512)      # below the whole-line kernel's K minimum
     assert st == OK and kname(pl) == f"bf16_mfma32_256x256x32_w2x2_a8b8_{name}_ring4", pl
@@ -754,6 +755,7 @@ def test_output_types_of_the_kernels():
     assert all(v & 1 for v in outs.values())
     for name in ("f32_mfma32_256x256x16_w2x2_a4b4_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
                  "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
+                 "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "fp8_mfma32_256x256x128_w2x2_nt_lines",

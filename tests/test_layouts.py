@@ -282,6 +282,50 @@ def test_nt_lines_epilogue_and_c_alignment(gpu_available, act, c_offset):
     check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "bf16f32", bias=bias, act=act)
 
 
+TN_LINES = "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines"
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 1024), (1000, 1000, 1040), (40, 2048, 4096), (2048, 40, 2048),
+                                   (4104, 4296, 1096), (264, 136, 48)], ids=lambda s: "x".join(map(str, s)))
+def test_tn_lines_kernel(gpu_available, shape):
+    """The whole-line bf16 kernel with A stored K x M, forced: exact on
+    integer data (with beta on and off; K of 48 is one slice and a half),
+    and on random data the same bits as the A-transposed ring kernel."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    lines, ring = ids[TN_LINES], ids[BF16_TN_RING]
+    ok, _ = runnable("bf16f32", "T", "N", M, N, K, lines)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=750, dtype="bf16f32")
+    As, Bs = stored(A, B, "T", "N")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[tn lines] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=750")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=lines, op_a="T", op_b="N")
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, "T", "N"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=751, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "T", "N")
+    say(f"[tn lines] random M={M} N={N} K={K} seed=751, against the ring")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=lines, op_a="T", op_b="N")
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=ring, op_a="T", op_b="N")
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, "T", "N", "bf16f32")
+
+
+def test_tn_lines_epilogue_padded(gpu_available):
+    """Bias and GELU with A^T, B and C inside NaN-padded rows (padding 8, 24
+    and 3 elements: A^T's padding reaches only rows of C that are never
+    written)."""
+    M, N, K = 520, 776, 1024
+    A, B, C0 = make_random_inputs(M, N, K, seed=752, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "T", "N")
+    bias = make_bias(N, seed=753)
+    lines = [k["id"] for k in tg.kernels() if k["name"] == TN_LINES][0]
+    say(f"[tn lines] epilogue gelu, padded, M={M} N={N} K={K}")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0 / np.sqrt(K), -0.5, kernel=lines, pad=(8, 24, 3), bias=bias,
+                       activation="gelu", op_a="T", op_b="N")
+    check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "T", "N", "bf16f32", bias=bias, act="gelu")
+
+
 FP8_LINES = "fp8_mfma32_256x256x128_w2x2_nt_lines"
 
 

@@ -51,6 +51,111 @@ namespace {
 __device__ __forceinline__ int lines_swz_a(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lines_swz_b(int row) { return 4 * ((row >> 1) & 1); }
 
+// Epilogue of the whole-line kernels, in two passes of 64 columns per
+// wave.  The wave's 128 x 64 accumulators of a pass are written to its
+// 32 KB of LDS (stage_row(r) points at row r, 256 bytes) in their register
+// layout (register 4g + t of lane (h, l32) in fragment (fm, fn) is row
+// 32fm + l32, column 32*(fn%2) + 8g + 4h + t of the pass; 16-byte chunk c
+// of a row at c ^ (row & 15), for both the accumulator-layout writes and the
+// row-major reads), then read back 4 rows x 64 columns per instruction and
+// finished and stored a row run at a time.  STRADDLE: N is free, and runs
+// of 4 columns that straddle it are read and stored element by element
+// (otherwise N is a multiple of 8).
+template <int OUT, bool STRADDLE, typename RowPtr>
+__device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16 (&acc)[4][4], RowPtr stage_row,
+                                               int m0, int n0, int wm, int wn, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    const int M = p.M, N = p.N;
+    const float alpha = p.alpha, beta = p.beta;
+    const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
+    const bool vec_o = out_vec4<OUT>(p);
+    const int act = p.act;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int fl = 0; fl < 2; ++fl) {
+            const int fn = 2 * pass + fl;
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) {
+                const int row = 32 * fm + l32;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = (8 * fl + 2 * g + h) ^ (row & 15);
+                    const f32x4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
+                                     acc[fm][fn][4 * g + 3]};
+                    *reinterpret_cast<f32x4 *>(stage_row(row) + 16 * c) = v;
+                }
+            }
+        }
+        const int cc = lane & 15;
+        const int col = n0 + wn * 128 + 64 * pass + 4 * cc;
+        float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            b[t] = (p.bias != nullptr && (STRADDLE ? col + t < N : col < N)) ? p.bias[col + t] : -0.0f;
+        const bool whole = !STRADDLE || col + 4 <= N;
+        // C = A x B (alpha 1, beta 0, no bias or activation): each run is
+        // stored as read, and eight runs are read from LDS before any is
+        // stored (3% of the whole 8192^3 call against the general loop
+        // below, whose per-run steps and uniform branches the compiler
+        // keeps in order).
+        if (alpha == 1.0f && beta == 0.0f && p.bias == nullptr && act == GEMM_ACT_NONE) {
+            for (int i0 = 0; i0 < 32; i0 += 8) {
+                f32x4 vv[8];
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    const int row = 4 * (i0 + ii) + (lane >> 4);
+                    vv[ii] = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
+                }
+#pragma unroll
+                for (int ii = 0; ii < 8; ++ii) {
+                    const int grow = m0 + wm * 128 + 4 * (i0 + ii) + (lane >> 4);
+                    if (grow >= M || col >= N) continue;
+                    if (whole)
+                        store_out4<OUT>(p, grow, col, vv[ii], vec_o);
+                    else
+                        store_out_first<OUT>(p, grow, col, vv[ii], N - col);
+                }
+            }
+            continue;
+        }
+#pragma unroll 4
+        for (int i = 0; i < 32; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            f32x4 v = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
+            const int grow = m0 + wm * 128 + row;
+            if (grow >= M || col >= N) continue;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] *= alpha;
+            if (beta != 0.0f) {
+                const float *cp = p.C + (int64_t)grow * p.ldc + col;
+                f32x4 c0;
+                if (whole && vec_c) {
+                    c0 = *reinterpret_cast<const f32x4 *>(cp);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) c0[t] = (!STRADDLE || col + t < N) ? cp[t] : 0.0f;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] += b[t];
+            if (act == GEMM_ACT_GELU) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = ActGelu::apply(v[t]);
+            } else if (act == GEMM_ACT_RELU) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = ActRelu::apply(v[t]);
+            }
+            if (whole)
+                store_out4<OUT>(p, grow, col, v, vec_o);
+            else
+                store_out_first<OUT>(p, grow, col, v, N - col);
+        }
+    }
+}
+
 template <int OUT, bool BT>
 __global__ void __launch_bounds__(256)
 bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
@@ -300,106 +405,218 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __builtin_amdgcn_s_barrier();
 
-    // Epilogue, in two passes of 64 columns per wave.  The wave's 128 x 64
-    // accumulators are written to its 32 KB of LDS in their register layout
-    // (register 4g + t of lane (h, l32) in fragment (fm, fn) is row 32fm +
-    // l32, column 32*(fn%2) + 8g + 4h + t of the pass), then read back 4 rows
-    // x 64 columns per instruction and finished and stored a row run at a time.
+    // Epilogue, in two passes of 64 columns per wave (lines_epilogue): the
+    // wave's 32 KB of LDS is a pair stage for waves 0-2 and two B stages for
+    // wave 3.
     char *stg = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : nullptr;
-    auto stage_row = [&](int row) -> char * {
+    lines_epilogue<OUT, BT>(p, acc, [&](int row) -> char * {
         return stg != nullptr ? stg + row * 256 : (row < 64 ? sb0 : sb1) + (row & 63) * 256;
-    };
-    const float alpha = p.alpha, beta = p.beta;
-    const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
-    const bool vec_o = out_vec4<OUT>(p);
-    const int act = p.act;
+    }, m0, n0, wm, wn, lane);
+}
+
+// A stored K x M (m contiguous; the weight-gradient product X^T dY) times an
+// untransposed B.  A's 32-deep slice then has the shape of B's (32 k rows of
+// 256 columns), so both operands take the B machinery of the kernel above:
+// four 16 KB single-slice stages each, loaded as four 64-column blocks whose
+// rows are whole 128-byte lines, and read with the transposing
+// ds_read_b64_tr_b16 (which gives each lane its k values in the order the
+// 16-byte reads of an untransposed A do, so the bits equal the A^T ring's).
+// Every block of 16 matrix instructions issues two loads of A and two of B,
+// as above, with B's timing for both: slice s's loads 0, 1 in block 2 of
+// slice s - 4 and loads 2, 3 in block 1 of slice s - 3, so the wait of
+// vmcnt(16) at each barrier is unchanged.  128 KB of LDS.
+template <int OUT>
+__global__ void __launch_bounds__(256)
+bf16_lines_tn_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint16_t>(p);
+    constexpr int BM = 256, BN = 256, BK = 32;
+    constexpr int kSlice = BK * 256 * 2;      // 16 KB: 32 k rows x 256 columns
+    constexpr int UNROLL = 4;                 // stage cycle (and twice the register-set cycle)
+    __shared__ __attribute__((aligned(1024))) char sa0[kSlice], sa1[kSlice], sa2[kSlice], sa3[kSlice];
+    __shared__ __attribute__((aligned(1024))) char sb0[kSlice], sb1[kSlice], sb2[kSlice], sb3[kSlice];
+    auto a_stage = [&](int i) -> char * { return i == 0 ? sa0 : i == 1 ? sa1 : i == 2 ? sa2 : sa3; };
+    auto b_stage = [&](int i) -> char * { return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : sb3; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+
+    // Load j (0..3) of a slice, for either operand: block `wave` (columns
+    // 64*wave ..), k rows 8j .. 8j+7 (lane -> row 8j + lane/8, physical chunk
+    // lane%8), landing at stage + 4096 wave + 1024 j.  Columns past M (N)
+    // belong to rows (columns) of C that are never stored.
+    uint32_t a_goff[4], b_goff[4];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int fl = 0; fl < 2; ++fl) {
-            const int fn = 2 * pass + fl;
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) {
-                const int row = 32 * fm + l32;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int c = (8 * fl + 2 * g + h) ^ (row & 15);
-                    const f32x4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
-                                     acc[fm][fn][4 * g + 3]};
-                    *reinterpret_cast<f32x4 *>(stage_row(row) + 16 * c) = v;
-                }
-            }
-        }
-        const int cc = lane & 15;
-        const int col = n0 + wn * 128 + 64 * pass + 4 * cc;
-        float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && (BT ? col + t < N : col < N)) ? p.bias[col + t] : -0.0f;
-        // With B stored N x K, N is free: a run of 4 columns may straddle
-        // it, and such a run is read and stored element by element.  (With
-        // B stored K x N its rows are whole 16-byte chunks, so N is a
-        // multiple of 8.)
-        const bool whole = !BT || col + 4 <= N;
-        // C = A x B (alpha 1, beta 0, no bias or activation): each run is
-        // stored as read, and eight runs are read from LDS before any is
-        // stored (3% of the whole 8192^3 call against the general loop
-        // below, whose per-run steps and uniform branches the compiler
-        // keeps in order).
-        if (alpha == 1.0f && beta == 0.0f && p.bias == nullptr && act == GEMM_ACT_NONE) {
-            for (int i0 = 0; i0 < 32; i0 += 8) {
-                f32x4 vv[8];
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
-                    const int row = 4 * (i0 + ii) + (lane >> 4);
-                    vv[ii] = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
-                }
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
-                    const int grow = m0 + wm * 128 + 4 * (i0 + ii) + (lane >> 4);
-                    if (grow >= M || col >= N) continue;
-                    if (whole)
-                        store_out4<OUT>(p, grow, col, vv[ii], vec_o);
-                    else
-                        store_out_first<OUT>(p, grow, col, vv[ii], N - col);
-                }
-            }
-            continue;
-        }
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-            const int row = 4 * i + (lane >> 4);
-            f32x4 v = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
-            const int grow = m0 + wm * 128 + row;
-            if (grow >= M || col >= N) continue;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] *= alpha;
-            if (beta != 0.0f) {
-                const float *cp = p.C + (int64_t)grow * p.ldc + col;
-                f32x4 c0;
-                if (whole && vec_c) {
-                    c0 = *reinterpret_cast<const f32x4 *>(cp);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) c0[t] = (!BT || col + t < N) ? cp[t] : 0.0f;
-                }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] += b[t];
-            if (act == GEMM_ACT_GELU) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = ActGelu::apply(v[t]);
-            } else if (act == GEMM_ACT_RELU) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = ActRelu::apply(v[t]);
-            }
-            if (whole)
-                store_out4<OUT>(p, grow, col, v, vec_o);
-            else
-                store_out_first<OUT>(p, grow, col, v, N - col);
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * j + (lane >> 3);
+        const int lc = (lane & 7) ^ lines_swz_b(row);
+        a_goff[j] = (uint32_t)(row * lda + 64 * wave + 8 * lc) * 2u;
+        b_goff[j] = (uint32_t)(row * ldb + 64 * wave + 8 * lc) * 2u;
     }
+    // Resources of slice s, rebased per slice; k rows past K fall outside.
+    auto rsrc_a = [&](int s) {
+        const int k0 = BK * s;
+        return make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent(((int64_t)(K - k0 - 1) * lda + (M - m0)) * 2));
+    };
+    auto rsrc_b = [&](int s) {
+        const int k0 = BK * s;
+        return make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
+    };
+    auto dma_a = [&](int si, const rsrc_t &ra, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(a_stage(si) + 4096 * wave + 1024 * j), 16,
+                                                 a_goff[j], 0, 0, 0);
+    };
+    auto dma_b = [&](int si, const rsrc_t &rb, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(b_stage(si) + 4096 * wave + 1024 * j), 16,
+                                                 b_goff[j], 0, 0, 0);
+    };
+
+    // Fragment reads (the transposing pattern of the kernel above, with the
+    // wave's m block for A and its n block for B): fragment f, k half s:
+    // lane (q, j16) points at k row 16s + 8*(q/2) + j16/4 (and 4 rows on for
+    // the second read), columns 32f + 16*(q%2) + 4*(j16%4) .. +3 of the wave's
+    // 128-column block.
+    const int l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int q = lane >> 4, j16 = lane & 15;
+    const int brow = 8 * (q >> 1) + (j16 >> 2);
+    const int bx = 2 * (q & 1) + ((j16 & 3) >> 1);
+    const int bsw = (j16 >> 3) & 1;
+    uint32_t fa_off[2], fb_off[2];
+#pragma unroll
+    for (int fp = 0; fp < 2; ++fp) {
+        const uint32_t in_block = (uint32_t)(brow * 128 + 16 * (bx + 4 * (fp ^ bsw)) + 8 * (j16 & 1));
+        fa_off[fp] = (uint32_t)(wm * 2 * 4096) + in_block;
+        fb_off[fp] = (uint32_t)(wn * 2 * 4096) + in_block;
+    }
+    auto tr_read = [&](const char *stage, uint32_t off) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(stage + off));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(stage + off + 512));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 fa[2][4], fb[2][4];
+    // Read slot r (0..7) of half s of the slice in stage si into register set
+    // `set`, in the order the next block of matrix instructions consumes them:
+    // A0, B0, B1, B2, B3, A1, A2, A3.
+    auto read_slot = [&](int si, int s, int set, int r) {
+        if (r == 0 || r >= 5) {
+            const int f = r == 0 ? 0 : r - 4;
+            fa[set][f] = tr_read(a_stage(si), fa_off[f & 1] + 4096 * (f >> 1) + 2048 * s);
+        } else {
+            const int f = r - 1;
+            fb[set][f] = tr_read(b_stage(si), fb_off[f & 1] + 4096 * (f >> 1) + 2048 * s);
+        }
+    };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    auto mma = [&](int set, int t) {
+        const int i = t >> 2, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+    };
+
+    // Prologue: slices 0..2 whole and loads 0, 1 of slice 3, A before B in
+    // each; slice 0 is followed by 20 loads.
+    const int nk = (K + BK - 1) / BK;
+    {
+        const rsrc_t ra0 = rsrc_a(0), ra1 = rsrc_a(1), ra2 = rsrc_a(2), ra3 = rsrc_a(3);
+        const rsrc_t rb0 = rsrc_b(0), rb1 = rsrc_b(1), rb2 = rsrc_b(2), rb3 = rsrc_b(3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_a(0, ra0, j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_b(0, rb0, j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_a(1, ra1, j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_b(1, rb1, j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_a(2, ra2, j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_b(2, rb2, j);
+        dma_a(3, ra3, 0);
+        dma_a(3, ra3, 1);
+        dma_b(3, rb3, 0);
+        dma_b(3, rb3, 1);
+    }
+    rsrc_t ra_pend = rsrc_a(3), rb_pend = rsrc_b(3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(20));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) read_slot(0, 0, 0, r);
+    auto slice = [&](int u, int kt) {
+        const int st = u % 4, st3 = (u + 3) % 4, st_n = (u + 1) % 4;
+        rsrc_t ra_next, rb_next;
+        // Block 1: the slice's first k half; reads of its second half; loads
+        // 2, 3 of slice kt + 3.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            mma(0, t);
+            if (t < 8) read_slot(st, 1, 1, t);
+            else if (t == 9) dma_a(st3, ra_pend, 2);
+            else if (t == 11) dma_b(st3, rb_pend, 2);
+            else if (t == 13) dma_a(st3, ra_pend, 3);
+            else if (t == 15) dma_b(st3, rb_pend, 3);
+            else if (t == 8) ra_next = rsrc_a(kt + 4);
+            else if (t == 10) rb_next = rsrc_b(kt + 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(16));
+        __builtin_amdgcn_s_barrier();
+        // Block 2: the second k half while the first half of slice kt + 1 is
+        // read; loads 0, 1 of slice kt + 4 into this slice's stages.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            mma(1, t);
+            if (t & 1) read_slot(st_n, 0, 0, t >> 1);
+            else if (t == 0) dma_a(st, ra_next, 0);
+            else if (t == 2) dma_b(st, rb_next, 0);
+            else if (t == 4) dma_a(st, ra_next, 1);
+            else if (t == 6) dma_b(st, rb_next, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ra_pend = ra_next;
+        rb_pend = rb_next;
+    };
+    const int nfull = nk / UNROLL;
+    int kb = 0;
+    for (int it = 0; it < nfull; ++it, kb += UNROLL) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) slice(u, kb + u);
+    }
+    const int rem = nk - kb;
+#pragma unroll
+    for (int u = 0; u < UNROLL - 1; ++u)
+        if (u < rem) slice(u, kb + u);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    // Each wave's 32 KB of staging: two consecutive stages.
+    char *lo = wave == 0 ? sa0 : wave == 1 ? sa2 : wave == 2 ? sb0 : sb2;
+    char *hi = wave == 0 ? sa1 : wave == 1 ? sa3 : wave == 2 ? sb1 : sb3;
+    lines_epilogue<OUT, false>(p, acc, [&](int row) -> char * {
+        return (row < 64 ? lo : hi) + (row & 63) * 256;
+    }, m0, n0, wm, wn, lane);
+}
+
+hipError_t launch_bf16_lines_tn(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines_tn_kernel<GEMM_OUT_BF16>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines_tn_kernel<GEMM_OUT_FP8>)
+                                           : reinterpret_cast<const void *>(&bf16_lines_tn_kernel<GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
 }
 
 template <bool BT>
@@ -421,6 +638,9 @@ template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, false>(GemmParams, int,
 template __global__ void bf16_lines_kernel<GEMM_OUT_F32, true>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_BF16, true>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, true>(GemmParams, int, int);
+template __global__ void bf16_lines_tn_kernel<GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_lines_tn_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_lines_tn_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 
 }  // namespace
 
@@ -430,6 +650,8 @@ const KernelDesc kBf16LinesKernels[] = {
      &launch_bf16_lines<false>, 1024, nullptr, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 64, 256, 8, 8, "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
      &launch_bf16_lines<true>, 1024, nullptr, kLayoutNT, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines",
+     &launch_bf16_lines_tn, 1024, nullptr, kLayoutTN, false, kOutAll},
 };
 const int kBf16LinesKernelCount = sizeof(kBf16LinesKernels) / sizeof(kBf16LinesKernels[0]);
 #endif
