@@ -91,6 +91,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_tiled.hip",
                   "bf16_mfma32_256x256x64_w2x2_a8b8_lines": "gemm_bf16_lines.hip",
                   "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines": "gemm_bf16_lines.hip",
+                  "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines": "gemm_bf16_lines.hip",
                   "fp8_mfma32_256x256x128_w2x2_nt_lines": "gemm_fp8_lines.hip",
                   "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip",
                   "bf16_skinny": "gemm_bf16_skinny.hip", "f32_skinny_nt": "gemm_skinny_nt.hip",
