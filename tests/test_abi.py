@@ -243,6 +243,28 @@ def test_bf16_tile_choice():
     assert (p["tile_m"], p["tile_n"], p["grid"], p["vec_a"], p["vec_b"]) == (256, 256, 1024, 8, 8)
 
 
+def test_bf16_mid_size_choice():
+    """bf16 problems with 256 to 1023 tiles of 128^2 take the 128 x 128
+    whole-line kernel; with a workspace it is still preferred, unsplit, over
+    256^2 tiles split over K (the split's workspace round trip costs more
+    than the smaller tile gives up).  fp32 keeps the split 256^2 ring there."""
+    L128 = "bf16_mfma32_128x128x64_w2x2_a8b8_lines"
+    for M, N, K in [(2048, 2048, 2048), (2048, 4096, 4096), (2048, 2048, 8192), (1536, 1536, 4096)]:
+        for ws in (0, 1 << 34):
+            st, p = plan(BF16, M, N, K, ws=ws)
+            assert st == OK and kname(p) == L128 and p["splits"] == 1, (M, N, K, ws, p)
+    st, p = plan(BF16, 4096, 4096, 4096, ws=1 << 34)
+    assert kname(p) == "bf16_mfma32_256x256x64_w2x2_a8b8_lines" and p["splits"] == 1
+    # Too few 128^2 tiles to fill the compute units: the split 256^2 tiles.
+    st, p = plan(BF16, 1024, 1024, 16384, ws=1 << 34)
+    assert p["tile_m"] == 256 and p["splits"] == 16, p
+    st, p = plan(F32, 2048, 4096, 4096, ws=1 << 34)
+    assert p["tile_m"] == 256 and p["splits"] == 2, p
+    # Below its minimum K the generic 128^2 kernel runs.
+    st, p = plan(BF16, 2048, 2048, 128)
+    assert st == OK and p["tile_m"] == 128 and kname(p) != L128, p
+
+
 def test_vector_width_follows_alignment():
     # K = 777: rows of A are not 16-byte aligned -> element loads for A only.
     st, p = plan(F32, 1000, 3000, 777)
@@ -755,7 +777,7 @@ def test_output_types_of_the_kernels():
     assert all(v & 1 for v in outs.values())
     for name in ("f32_mfma32_256x256x16_w2x2_a4b4_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
                  "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
-                 "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines",
+                 "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines", "bf16_mfma32_128x128x64_w2x2_a8b8_lines",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "fp8_mfma32_256x256x128_w2x2_nt_lines",

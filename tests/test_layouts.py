@@ -369,12 +369,55 @@ def test_fp8_lines_epilogue_padded(gpu_available):
     check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "fp8f32", bias=bias, act="gelu")
 
 
-@pytest.mark.parametrize("op_b", ["N", "T"])
-def test_lines_kernels_padded_operands(gpu_available, op_b):
+NN_LINES = "bf16_mfma32_256x256x64_w2x2_a8b8_lines"
+NN_LINES128 = "bf16_mfma32_128x128x64_w2x2_a8b8_lines"
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 256), (1000, 1000, 1040), (40, 2048, 4096), (2048, 40, 2048),
+                                   (2100, 2056, 1096), (264, 136, 48), (136, 264, 32), (130, 136, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_lines128_kernel(gpu_available, shape):
+    """The 128 x 128 whole-line bf16 kernel, forced: exact on integer data
+    (K of 8, 32 and 48: part of a slice, one slice, a slice and a half), and
+    on random data the same bits as the 256 x 256 whole-line kernel (the same
+    k pairing and summation order per lane)."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    small, big = ids[NN_LINES128], ids[NN_LINES]
+    ok, _ = runnable("bf16f32", "N", "N", M, N, K, small)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=760, dtype="bf16f32")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[lines128] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=760")
+        C, _, _ = run_gemm(A, B, C0, alpha, beta, kernel=small)
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(A, B, C0, alpha, beta, "N", "N"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=761, dist="normal", dtype="bf16f32")
+    say(f"[lines128] random M={M} N={N} K={K} seed=761, against the 256 x 256 kernel")
+    C1, _, _ = run_gemm(A, B, C0, 0.5, 0.25, kernel=small)
+    C2, _, _ = run_gemm(A, B, C0, 0.5, 0.25, kernel=big)
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, A, B, C0, 0.5, 0.25, "N", "N", "bf16f32")
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+@pytest.mark.parametrize("c_offset", [0, 1])
+def test_lines128_epilogue_and_c_alignment(gpu_available, act, c_offset):
+    M, N, K = 520, 776, 1024
+    A, B, C0 = make_random_inputs(M, N, K, seed=762, dist="normal", dtype="bf16f32")
+    bias = make_bias(N, seed=763)
+    kid = [k["id"] for k in tg.kernels() if k["name"] == NN_LINES128][0]
+    say(f"[lines128] epilogue act={act} M={M} N={N} K={K} c_offset={c_offset}")
+    C, _, _ = run_gemm(A, B, C0, 1.0 / np.sqrt(K), -0.5, kernel=kid, offset=(0, 0, c_offset), bias=bias,
+                       activation=act)
+    check(C, A, B, C0, 1.0 / np.sqrt(K), -0.5, "N", "N", "bf16f32", bias=bias, act=act)
+
+
+@pytest.mark.parametrize("name", [NN_LINES, NT_LINES, NN_LINES128])
+def test_lines_kernels_padded_operands(gpu_available, name):
     """The whole-line kernels on operands inside wider buffers: A, B and C
     padded by 8, 24 and 5 elements per row, the padding NaN (it must never
     reach C), ragged M, N and K; integer data, so the result is exact."""
-    name = NT_LINES if op_b == "T" else "bf16_mfma32_256x256x64_w2x2_a8b8_lines"
+    op_b = "T" if name == NT_LINES else "N"
     kid = [k["id"] for k in tg.kernels() if k["name"] == name][0]
     for M, N, K in [(300, 520 if op_b == "N" else 517, 1096), (1030, 264, 2056)]:
         A, B, C0 = make_integer_inputs(M, N, K, seed=730 + M, dtype="bf16f32")

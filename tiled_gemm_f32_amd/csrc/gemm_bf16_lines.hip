@@ -61,8 +61,8 @@ __device__ __forceinline__ int lines_swz_b(int row) { return 4 * ((row >> 1) & 1
 // finished and stored a row run at a time.  STRADDLE: N is free, and runs
 // of 4 columns that straddle it are read and stored element by element
 // (otherwise N is a multiple of 8).
-template <int OUT, bool STRADDLE, typename RowPtr>
-__device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16 (&acc)[4][4], RowPtr stage_row,
+template <int OUT, bool STRADDLE, typename RowPtr, int FM = 4, int FN = 4>
+__device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16 (&acc)[FM][FN], RowPtr stage_row,
                                                int m0, int n0, int wm, int wn, int lane) {
     const int h = lane >> 5, l32 = lane & 31;
     const int M = p.M, N = p.N;
@@ -71,12 +71,12 @@ __device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16
     const bool vec_o = out_vec4<OUT>(p);
     const int act = p.act;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < FN / 2; ++pass) {
 #pragma unroll
         for (int fl = 0; fl < 2; ++fl) {
             const int fn = 2 * pass + fl;
 #pragma unroll
-            for (int fm = 0; fm < 4; ++fm) {
+            for (int fm = 0; fm < FM; ++fm) {
                 const int row = 32 * fm + l32;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -88,7 +88,7 @@ __device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16
             }
         }
         const int cc = lane & 15;
-        const int col = n0 + wn * 128 + 64 * pass + 4 * cc;
+        const int col = n0 + wn * 32 * FN + 64 * pass + 4 * cc;
         float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -100,7 +100,7 @@ __device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16
         // below, whose per-run steps and uniform branches the compiler
         // keeps in order).
         if (alpha == 1.0f && beta == 0.0f && p.bias == nullptr && act == GEMM_ACT_NONE) {
-            for (int i0 = 0; i0 < 32; i0 += 8) {
+            for (int i0 = 0; i0 < 8 * FM; i0 += 8) {
                 f32x4 vv[8];
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) {
@@ -109,7 +109,7 @@ __device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16
                 }
 #pragma unroll
                 for (int ii = 0; ii < 8; ++ii) {
-                    const int grow = m0 + wm * 128 + 4 * (i0 + ii) + (lane >> 4);
+                    const int grow = m0 + wm * 32 * FM + 4 * (i0 + ii) + (lane >> 4);
                     if (grow >= M || col >= N) continue;
                     if (whole)
                         store_out4<OUT>(p, grow, col, vv[ii], vec_o);
@@ -120,10 +120,10 @@ __device__ __forceinline__ void lines_epilogue(const GemmParams &p, const f32x16
             continue;
         }
 #pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
+        for (int i = 0; i < 8 * FM; ++i) {
             const int row = 4 * i + (lane >> 4);
             f32x4 v = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
-            const int grow = m0 + wm * 128 + row;
+            const int grow = m0 + wm * 32 * FM + row;
             if (grow >= M || col >= N) continue;
 #pragma unroll
             for (int t = 0; t < 4; ++t) v[t] *= alpha;
@@ -414,6 +414,220 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }, m0, n0, wm, wn, lane);
 }
 
+// The same ring at a quarter of the tile: 128 x 128 outputs per workgroup,
+// each wave 64 x 64 (2 x 2 fragments), for problems with too few 256 x 256
+// tiles to fill the compute units.  NA = 3 A-pair stages of 16 KB (128 rows
+// x 64 k) and NB = 4 B-slice stages of 8 KB (two 64-column blocks of 32 k
+// rows), 80 KB in all, so that two workgroups fit a compute unit.  Every
+// block of 4 matrix instructions per wave issues one A and one B load; the
+// LDS layouts, the swizzles and the per-lane order of accumulation are those
+// of the 256 x 256 kernel.  B is stored K x N.
+//
+// Deeper rings (4 + 6, 4 + 8 and 5 + 10 stages, up to the whole 160 KB of
+// LDS, one workgroup per compute unit) were no faster even on a single wave
+// of tiles (2048^3: 26.2 us here, 27.4-28.6 us deeper), so load latency is
+// not what holds this kernel back; its 64 x 64 wave tile reads twice the LDS
+// bytes per matrix instruction of the 256 x 256 kernel's 128 x 128 one.
+template <int OUT>
+__global__ void __launch_bounds__(256)
+bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint16_t>(p);
+    constexpr int BM = 128, BN = 128, BK = 32;
+    constexpr int NA = 3, NB = 4;
+    constexpr int kAPair = BM * 2 * BK * 2;   // 16 KB: 128 rows x 64 k
+    constexpr int kBSlice = BK * BN * 2;      // 8 KB: 32 k rows x 128 columns
+    constexpr int UNROLL = 12;                // 2 * NA slices per A cycle, NB per B cycle
+    __shared__ __attribute__((aligned(1024))) char sa0[kAPair], sa1[kAPair], sa2[kAPair];
+    __shared__ __attribute__((aligned(1024))) char sb0[kBSlice], sb1[kBSlice], sb2[kBSlice], sb3[kBSlice];
+    auto a_stage = [&](int i) -> char * { return i == 0 ? sa0 : i == 1 ? sa1 : sa2; };
+    auto b_stage = [&](int i) -> char * { return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : sb3; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+    const int a_rows = min(BM, M - m0);
+
+    // A load j (0..3) of this wave for a pair: rows 8g .. 8g+7 with g = 4*wave
+    // + j (lane -> row 8g + lane/8, physical chunk lane%8), landing at stage +
+    // 1024 g.  B load j (0..1) of a slice: g = 2*wave + j covers block g/4
+    // (columns 64*(g/4) ..), k rows 8*(g%4) .. +7 (lane -> k row 8*(g%4) +
+    // lane/8), landing at stage + 1024 g.
+    uint32_t a_goff[4], b_goff[2];
+    int a_kc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * (4 * wave + j) + (lane >> 3);
+        const int lc = (lane & 7) ^ lines_swz_a(row);
+        a_kc[j] = 8 * lc;
+        a_goff[j] = panel_off(row, a_rows, lda, 8 * lc, 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int g = 2 * wave + j;
+        const int row = 8 * (g & 3) + (lane >> 3);
+        const int lc = (lane & 7) ^ lines_swz_b(row);
+        b_goff[j] = (uint32_t)(row * ldb + 64 * (g >> 2) + 8 * lc) * 2u;
+    }
+    // Resources: pair P of A (k 64P ..) and slice s of B (k rows 32s ..),
+    // rebased per use.  k rows past K fall outside B's extent; A chunks at or
+    // past K get 2^31 added to their offset; rows past M read row M - 1.
+    auto rsrc_a = [&](int P) {
+        const int k0 = 2 * BK * P;
+        return make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 2));
+    };
+    auto rsrc_b = [&](int s) {
+        const int k0 = BK * s;
+        return make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
+    };
+    auto dma_a = [&](int P, int si, const rsrc_t &ra, int j) {
+        const uint32_t poison = (uint32_t)(a_kc[j] >= K - 2 * BK * P) << 31;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(a_stage(si) + (4 * wave + j) * 1024), 16,
+                                                 a_goff[j] + poison, 0, 0, 0);
+    };
+    auto dma_b = [&](int si, const rsrc_t &rb, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(b_stage(si) + 1024 * (2 * wave + j)), 16,
+                                                 b_goff[j], 0, 0, 0);
+    };
+
+    // Fragment reads, as in the 256 x 256 kernel: A fragment f, k half s of a
+    // slice with pair parity par is row wm*64 + 32f + l32, logical chunk 4*par
+    // + 2s + h; B fragment f (columns wn*64 + 32f ..: block wn, bytes 64f ..)
+    // is read with two transposing reads per k half.
+    const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int a_sw = lines_swz_a(l32);
+    const uint32_t fa_row = (uint32_t)((wm * 64 + l32) * 128);
+    const int q = lane >> 4, j16 = lane & 15;
+    const int brow = 8 * (q >> 1) + (j16 >> 2);
+    const int bx = 2 * (q & 1) + ((j16 & 3) >> 1);
+    const int bsw = (j16 >> 3) & 1;
+    uint32_t fb_off[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+        fb_off[f] = (uint32_t)(wn * 4096 + brow * 128 + 16 * (bx + 4 * (f ^ bsw)) + 8 * (j16 & 1));
+
+    bf16x8 fa[2][2], fb[2][2];
+    // Read slot r (0..3) in the order the next block consumes them: A0, B0,
+    // B1, A1.
+    auto read_slot = [&](int asi, int par, int bsi, int s, int set, int r) {
+        if (r == 0 || r == 3) {
+            const int f = r == 0 ? 0 : 1;
+            const int c = (4 * par + 2 * s + h) ^ a_sw;
+            fa[set][f] = *reinterpret_cast<const bf16x8 *>(a_stage(asi) + fa_row + 4096 * f + 16 * c);
+        } else {
+            const int f = r - 1;
+            const char *bp = b_stage(bsi) + fb_off[f] + 2048 * s;
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)bp);
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(bp + 512));
+            fb[set][f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto mma = [&](int set, int t) {
+        const int i = t >> 1, j = t & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+    };
+
+    // Load plan (per wave), the 256 x 256 kernel's with one load where that
+    // kernel issues two:
+    //   B slice s (loads 0, 1) into stage s % NB: load 0 in block 2 of slice
+    //     s - NB, load 1 in block 1 of slice s - NB + 1 (the stage is free
+    //     from the barrier of slice s - NB, the last that reads it).
+    //   A pair P (loads 0..3) into stage P % NA: load 0 in block 2 of slice
+    //     2P - 2NA + 1, loads 1 and 2 in blocks 1 and 2 of the next slice,
+    //     load 3 in block 1 of the one after (free from the barrier of slice
+    //     2P - 2NA + 1, the last that reads pair P - NA).
+    // The last load that slice kt + 1 needs is issued in block 1 of slice kt -
+    // 2 or earlier, and 8 loads per lane follow it by the barrier of slice kt.
+    // The prologue issues, in order, pair i then B slices 2i and 2i + 1 for i
+    // = 0 .. NA - 1, each as far as the plan has it issued before slice 0;
+    // slice 0 needs pair 0 and B slice 0, the first six loads.
+    constexpr int kWait = 8;
+    constexpr int kPrologue = 4 * (NA - 1) + 1 + 2 * (NB - 1) + 1;
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const rsrc_t ra = rsrc_a(i);
+#pragma unroll
+        for (int j = 0; j < (i < NA - 1 ? 4 : 1); ++j) dma_a(i, i, ra, j);
+#pragma unroll
+        for (int s2 = 2 * i; s2 < 2 * i + 2; ++s2) {
+            if (s2 >= NB) continue;
+            const rsrc_t rb = rsrc_b(s2);
+            dma_b(s2, rb, 0);
+            if (s2 < NB - 1) dma_b(s2, rb, 1);
+        }
+    }
+    rsrc_t rb_pend = rsrc_b(NB - 1), ra_pend = rsrc_a(NA - 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kPrologue - 6));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) read_slot(0, 0, 0, 0, 0, r);
+    // Slice kt, with u = kt % UNROLL a compile-time constant in every call.
+    auto slice = [&](int u, int kt) {
+        const int as = (u >> 1) % NA, bs = u % NB;
+        const int a1 = ((u + 2 * NA - 2) >> 1) % NA, b1 = (u + NB - 1) % NB;
+        const int q1 = (u & 1) ? 3 : 1;
+        const int P1 = (kt + 2 * NA - 2) >> 1, P2 = (kt + 2 * NA - 1) >> 1;
+        rsrc_t ra_next, rb_next;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            mma(0, t);
+            read_slot(as, u & 1, bs, 1, 1, t);
+            if (t == 0) ra_next = rsrc_a(P2);
+            else if (t == 1) dma_a(P1, a1, ra_pend, q1);
+            else if (t == 2) rb_next = rsrc_b(kt + NB);
+            else dma_b(b1, rb_pend, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWait));
+        __builtin_amdgcn_s_barrier();
+        const int a2 = ((u + 2 * NA - 1) >> 1) % NA, b2 = u % NB;
+        const int as_n = ((u + 1) >> 1) % NA, bs_n = (u + 1) % NB;
+        const int q2 = (u & 1) ? 0 : 2;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            mma(1, t);
+            read_slot(as_n, (u + 1) & 1, bs_n, 0, 0, t);
+            if (t == 0) dma_a(P2, a2, ra_next, q2);
+            else if (t == 2) dma_b(b2, rb_next, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rb_pend = rb_next;
+        ra_pend = ra_next;
+    };
+    const int nfull = nk / UNROLL;
+    int kb = 0;
+    for (int it = 0; it < nfull; ++it, kb += UNROLL) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) slice(u, kb + u);
+    }
+    const int rem = nk - kb;
+#pragma unroll
+    for (int u = 0; u < UNROLL - 1; ++u)
+        if (u < rem) slice(u, kb + u);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    // Epilogue in one pass of 64 columns per wave: 16 KB of staging each, a
+    // pair stage for waves 0-2 and two B slices for wave 3.
+    char *stg = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : nullptr;
+    lines_epilogue<OUT, false>(p, acc, [&](int row) -> char * {
+        return stg != nullptr ? stg + row * 256 : (row < 32 ? sb0 : sb1) + (row & 31) * 256;
+    }, m0, n0, wm, wn, lane);
+}
+
 // A stored K x M (m contiguous; the weight-gradient product X^T dY) times an
 // untransposed B.  A's 32-deep slice then has the shape of B's (32 k rows of
 // 256 columns), so both operands take the B machinery of the kernel above:
@@ -632,12 +846,27 @@ hipError_t launch_bf16_lines(const GemmParams &p, hipStream_t stream) {
                            stream);
 }
 
+hipError_t launch_bf16_lines128(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 127) / 128, tiles_n = (p.N + 127) / 128;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_BF16>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_FP8>)
+                                           : reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
+}
+
 template __global__ void bf16_lines_kernel<GEMM_OUT_F32, false>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_BF16, false>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, false>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_F32, true>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_BF16, true>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, true>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_F32>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
@@ -652,6 +881,8 @@ const KernelDesc kBf16LinesKernels[] = {
      &launch_bf16_lines<true>, 1024, nullptr, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines",
      &launch_bf16_lines_tn, 1024, nullptr, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 128, 128, 64, 256, 8, 8, "bf16_mfma32_128x128x64_w2x2_a8b8_lines",
+     &launch_bf16_lines128, 256, nullptr, kLayoutNN, false, kOutAll},
 };
 const int kBf16LinesKernelCount = sizeof(kBf16LinesKernels) / sizeof(kBf16LinesKernels[0]);
 #endif
