@@ -399,6 +399,50 @@ def test_lines128_kernel(gpu_available, shape):
     check(C1, A, B, C0, 0.5, 0.25, "N", "N", "bf16f32")
 
 
+NT_LINES128 = "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines"
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 256), (1000, 1001, 1040), (40, 2048, 4096), (2048, 41, 2048),
+                                   (2100, 2059, 1096), (264, 133, 48), (136, 264, 32), (130, 131, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_nt_lines128_kernel(gpu_available, shape):
+    """The 128 x 128 whole-line kernel with B stored N x K, forced: exact on
+    integer data (ragged N: runs of 4 columns straddle it; K of 8, 32 and
+    48), and on random data the same bits as the 256 x 256 one."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    small, big = ids[NT_LINES128], ids[NT_LINES]
+    ok, _ = runnable("bf16f32", "N", "T", M, N, K, small)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=764, dtype="bf16f32")
+    As, Bs = stored(A, B, "N", "T")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[nt lines128] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=764")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=small, op_a="N", op_b="T")
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, "N", "T"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=765, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "N", "T")
+    say(f"[nt lines128] random M={M} N={N} K={K} seed=765, against the 256 x 256 kernel")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=small, op_a="N", op_b="T")
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=big, op_a="N", op_b="T")
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, "N", "T", "bf16f32")
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu"])
+@pytest.mark.parametrize("c_offset", [0, 1])
+def test_nt_lines128_epilogue_and_c_alignment(gpu_available, act, c_offset):
+    M, N, K = 520, 777, 1024
+    A, B, C0 = make_random_inputs(M, N, K, seed=766, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "N", "T")
+    bias = make_bias(N, seed=767)
+    kid = [k["id"] for k in tg.kernels() if k["name"] == NT_LINES128][0]
+    say(f"[nt lines128] epilogue act={act} M={M} N={N} K={K} c_offset={c_offset}")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0 / np.sqrt(K), -0.5, kernel=kid, offset=(0, 0, c_offset), bias=bias,
+                       activation=act, op_a="N", op_b="T")
+    check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "bf16f32", bias=bias, act=act)
+
+
 @pytest.mark.parametrize("act", ["relu", "gelu"])
 @pytest.mark.parametrize("c_offset", [0, 1])
 def test_lines128_epilogue_and_c_alignment(gpu_available, act, c_offset):
@@ -412,12 +456,12 @@ def test_lines128_epilogue_and_c_alignment(gpu_available, act, c_offset):
     check(C, A, B, C0, 1.0 / np.sqrt(K), -0.5, "N", "N", "bf16f32", bias=bias, act=act)
 
 
-@pytest.mark.parametrize("name", [NN_LINES, NT_LINES, NN_LINES128])
+@pytest.mark.parametrize("name", [NN_LINES, NT_LINES, NN_LINES128, NT_LINES128])
 def test_lines_kernels_padded_operands(gpu_available, name):
     """The whole-line kernels on operands inside wider buffers: A, B and C
     padded by 8, 24 and 5 elements per row, the padding NaN (it must never
     reach C), ragged M, N and K; integer data, so the result is exact."""
-    op_b = "T" if name == NT_LINES else "N"
+    op_b = "T" if name in (NT_LINES, NT_LINES128) else "N"
     kid = [k["id"] for k in tg.kernels() if k["name"] == name][0]
     for M, N, K in [(300, 520 if op_b == "N" else 517, 1096), (1030, 264, 2056)]:
         A, B, C0 = make_integer_inputs(M, N, K, seed=730 + M, dtype="bf16f32")

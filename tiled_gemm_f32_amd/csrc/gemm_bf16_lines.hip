@@ -421,14 +421,15 @@ bf16_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
 // rows), 80 KB in all, so that two workgroups fit a compute unit.  Every
 // block of 4 matrix instructions per wave issues one A and one B load; the
 // LDS layouts, the swizzles and the per-lane order of accumulation are those
-// of the 256 x 256 kernel.  B is stored K x N.
+// of the 256 x 256 kernel.  BT: B stored N x K (its slices take that
+// kernel's B-transposed layout and reads, and N is free); otherwise K x N.
 //
 // Deeper rings (4 + 6, 4 + 8 and 5 + 10 stages, up to the whole 160 KB of
 // LDS, one workgroup per compute unit) were no faster even on a single wave
 // of tiles (2048^3: 26.2 us here, 27.4-28.6 us deeper), so load latency is
 // not what holds this kernel back; its 64 x 64 wave tile reads twice the LDS
 // bytes per matrix instruction of the 256 x 256 kernel's 128 x 128 one.
-template <int OUT>
+template <int OUT, bool BT>
 __global__ void __launch_bounds__(256)
 bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<uint16_t>(p);
@@ -450,15 +451,17 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B);
-    const int a_rows = min(BM, M - m0);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
 
     // A load j (0..3) of this wave for a pair: rows 8g .. 8g+7 with g = 4*wave
     // + j (lane -> row 8g + lane/8, physical chunk lane%8), landing at stage +
     // 1024 g.  B load j (0..1) of a slice: g = 2*wave + j covers block g/4
     // (columns 64*(g/4) ..), k rows 8*(g%4) .. +7 (lane -> k row 8*(g%4) +
-    // lane/8), landing at stage + 1024 g.
+    // lane/8), landing at stage + 1024 g.  B stored N x K: a slice is 128 rows
+    // (columns of C) of 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3), and
+    // load j fills rows 16g .. 16g+15 (lane -> row 16g + lane/4).
     uint32_t a_goff[4], b_goff[2];
-    int a_kc[4];
+    int a_kc[4], b_kc[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int row = 8 * (4 * wave + j) + (lane >> 3);
@@ -469,9 +472,17 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int g = 2 * wave + j;
-        const int row = 8 * (g & 3) + (lane >> 3);
-        const int lc = (lane & 7) ^ lines_swz_b(row);
-        b_goff[j] = (uint32_t)(row * ldb + 64 * (g >> 2) + 8 * lc) * 2u;
+        if (BT) {
+            const int row = 16 * g + (lane >> 2);
+            const int lc = (lane & 3) ^ ((row >> 2) & 3);
+            b_kc[j] = 8 * lc;
+            b_goff[j] = panel_off(row, b_rows, ldb, 8 * lc, 2);
+        } else {
+            const int row = 8 * (g & 3) + (lane >> 3);
+            const int lc = (lane & 7) ^ lines_swz_b(row);
+            b_kc[j] = 0;
+            b_goff[j] = (uint32_t)(row * ldb + 64 * (g >> 2) + 8 * lc) * 2u;
+        }
     }
     // Resources: pair P of A (k 64P ..) and slice s of B (k rows 32s ..),
     // rebased per use.  k rows past K fall outside B's extent; A chunks at or
@@ -482,6 +493,8 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
     };
     auto rsrc_b = [&](int s) {
         const int k0 = BK * s;
+        if (BT)
+            return make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 2));
         return make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
     };
     auto dma_a = [&](int P, int si, const rsrc_t &ra, int j) {
@@ -489,9 +502,12 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(a_stage(si) + (4 * wave + j) * 1024), 16,
                                                  a_goff[j] + poison, 0, 0, 0);
     };
-    auto dma_b = [&](int si, const rsrc_t &rb, int j) {
+    auto dma_b = [&](int s, int si, const rsrc_t &rb, int j) {
+        // B stored N x K: a chunk at or past K in a valid row would read the
+        // next row.
+        const uint32_t poison = BT ? (uint32_t)(b_kc[j] >= K - BK * s) << 31 : 0u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(b_stage(si) + 1024 * (2 * wave + j)), 16,
-                                                 b_goff[j], 0, 0, 0);
+                                                 b_goff[j] + poison, 0, 0, 0);
     };
 
     // Fragment reads, as in the 256 x 256 kernel: A fragment f, k half s of a
@@ -510,6 +526,12 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int f = 0; f < 2; ++f)
         fb_off[f] = (uint32_t)(wn * 4096 + brow * 128 + 16 * (bx + 4 * (f ^ bsw)) + 8 * (j16 & 1));
+    // B stored N x K: fragment f, k half s is row wn*64 + 32f + l32 of the
+    // slice, logical chunk 2s + h.
+    uint32_t fbt_off[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+        fbt_off[s2] = (uint32_t)((wn * 64 + l32) * 64 + 16 * ((2 * s2 + h) ^ ((l32 >> 2) & 3)));
 
     bf16x8 fa[2][2], fb[2][2];
     // Read slot r (0..3) in the order the next block consumes them: A0, B0,
@@ -519,6 +541,8 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
             const int f = r == 0 ? 0 : 1;
             const int c = (4 * par + 2 * s + h) ^ a_sw;
             fa[set][f] = *reinterpret_cast<const bf16x8 *>(a_stage(asi) + fa_row + 4096 * f + 16 * c);
+        } else if (BT) {
+            fb[set][r - 1] = *reinterpret_cast<const bf16x8 *>(b_stage(bsi) + fbt_off[s] + 2048 * (r - 1));
         } else {
             const int f = r - 1;
             const char *bp = b_stage(bsi) + fb_off[f] + 2048 * s;
@@ -563,8 +587,8 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
         for (int s2 = 2 * i; s2 < 2 * i + 2; ++s2) {
             if (s2 >= NB) continue;
             const rsrc_t rb = rsrc_b(s2);
-            dma_b(s2, rb, 0);
-            if (s2 < NB - 1) dma_b(s2, rb, 1);
+            dma_b(s2, s2, rb, 0);
+            if (s2 < NB - 1) dma_b(s2, s2, rb, 1);
         }
     }
     rsrc_t rb_pend = rsrc_b(NB - 1), ra_pend = rsrc_a(NA - 1);
@@ -587,7 +611,7 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
             if (t == 0) ra_next = rsrc_a(P2);
             else if (t == 1) dma_a(P1, a1, ra_pend, q1);
             else if (t == 2) rb_next = rsrc_b(kt + NB);
-            else dma_b(b1, rb_pend, 1);
+            else dma_b(kt + NB - 1, b1, rb_pend, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWait));
@@ -601,7 +625,7 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
             mma(1, t);
             read_slot(as_n, (u + 1) & 1, bs_n, 0, 0, t);
             if (t == 0) dma_a(P2, a2, ra_next, q2);
-            else if (t == 2) dma_b(b2, rb_next, 0);
+            else if (t == 2) dma_b(kt + NB, b2, rb_next, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         rb_pend = rb_next;
@@ -623,7 +647,7 @@ bf16_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // Epilogue in one pass of 64 columns per wave: 16 KB of staging each, a
     // pair stage for waves 0-2 and two B slices for wave 3.
     char *stg = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : nullptr;
-    lines_epilogue<OUT, false>(p, acc, [&](int row) -> char * {
+    lines_epilogue<OUT, BT>(p, acc, [&](int row) -> char * {
         return stg != nullptr ? stg + row * 256 : (row < 32 ? sb0 : sb1) + (row & 31) * 256;
     }, m0, n0, wm, wn, lane);
 }
@@ -846,14 +870,15 @@ hipError_t launch_bf16_lines(const GemmParams &p, hipStream_t stream) {
                            stream);
 }
 
+template <bool BT>
 hipError_t launch_bf16_lines128(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 127) / 128, tiles_n = (p.N + 127) / 128;
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
     const int out = launch_out_type(p);
-    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_BF16>)
-                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_FP8>)
-                                           : reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_F32>);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_BF16, BT>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_FP8, BT>)
+                                           : reinterpret_cast<const void *>(&bf16_lines128_kernel<GEMM_OUT_F32, BT>);
     return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
                            stream);
 }
@@ -864,9 +889,12 @@ template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, false>(GemmParams, int,
 template __global__ void bf16_lines_kernel<GEMM_OUT_F32, true>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_BF16, true>(GemmParams, int, int);
 template __global__ void bf16_lines_kernel<GEMM_OUT_FP8, true>(GemmParams, int, int);
-template __global__ void bf16_lines128_kernel<GEMM_OUT_F32>(GemmParams, int, int);
-template __global__ void bf16_lines128_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
-template __global__ void bf16_lines128_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_F32, false>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_BF16, false>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_FP8, false>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_F32, true>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_BF16, true>(GemmParams, int, int);
+template __global__ void bf16_lines128_kernel<GEMM_OUT_FP8, true>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_F32>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
@@ -882,7 +910,9 @@ const KernelDesc kBf16LinesKernels[] = {
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 256, 256, 32, 256, 8, 8, "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines",
      &launch_bf16_lines_tn, 1024, nullptr, kLayoutTN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 128, 128, 64, 256, 8, 8, "bf16_mfma32_128x128x64_w2x2_a8b8_lines",
-     &launch_bf16_lines128, 256, nullptr, kLayoutNN, false, kOutAll},
+     &launch_bf16_lines128<false>, 256, nullptr, kLayoutNN, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 128, 128, 64, 256, 8, 8, "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines",
+     &launch_bf16_lines128<true>, 256, nullptr, kLayoutNT, false, kOutAll},
 };
 const int kBf16LinesKernelCount = sizeof(kBf16LinesKernels) / sizeof(kBf16LinesKernels[0]);
 #endif
