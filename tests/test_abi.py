@@ -260,11 +260,14 @@ def test_bf16_mid_size_choice():
     assert p["tile_m"] == 256 and p["splits"] == 16, p
     st, p = plan(F32, 2048, 4096, 4096, ws=1 << 34)
     assert p["tile_m"] == 256 and p["splits"] == 2, p
-    # B stored N x K (a linear layer's weights): the same choice in that layout.
+    # B stored N x K (a linear layer's weights) and A stored K x M (its
+    # weight gradient): the same choice in those layouts.
     for M, N, K in [(2048, 2048, 2048), (2048, 4096, 4096)]:
         for ws in (0, 1 << 34):
             st, p = gplan(BF16, N_, T_, M, N, K, ws=ws)
             assert st == OK and kname(p) == "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines" and p["splits"] == 1, p
+            st, p = gplan(BF16, T_, N_, M, N, K, ws=ws)
+            assert st == OK and kname(p) == "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines" and p["splits"] == 1, p
     # Below its minimum K the generic 128^2 kernel runs.
     st, p = plan(BF16, 2048, 2048, 128)
     assert st == OK and p["tile_m"] == 128 and kname(p) != L128, p
@@ -556,11 +559,15 @@ def test_nt_takes_the_ring_kernels():
     # bf16 with B stored N x K: the whole-line kernel from K = 1024, the ring below.
     st, pl = gplan(BF16, N_, T_, 8192, 8192, 8192)
     assert st == OK and kname(pl) == "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines", pl
-    # Both need only 16-byte rows of B^T: N is free.
-    st, pl = gplan(BF16, N_, T_, 1000, 1001, 1040)
+    # Both need only 16-byte rows of B^T: N is free.  Fewer 256^2 tiles than
+    # compute units: the 128^2 whole-line kernel (from K = 256).
+    st, pl = gplan(BF16, N_, T_, 4000, 4001, 1040)
     assert st == OK and kname(pl) == "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines", pl
-    st, pl = gplan(BF16, N_, T_, 1000, 1001, 1000)
+    st, pl = gplan(BF16, N_, T_, 4000, 4001, 1000)
     assert st == OK and kname(pl) == "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", pl
+    for K in (1040, 1000):
+        st, pl = gplan(BF16, N_, T_, 1000, 1001, K)
+        assert st == OK and kname(pl) == "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines", pl
     st, pl = gplan(BF16, N_, T_, 1000, 1001, 1044)
     assert st == OK and kname(pl) == "bf16_general_128x128x16", pl
 
@@ -783,7 +790,7 @@ def test_output_types_of_the_kernels():
     for name in ("f32_mfma32_256x256x16_w2x2_a4b4_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_ring4",
                  "bf16_mfma32_256x256x64_w2x2_a8b8_lines", "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines", "bf16_mfma32_128x128x64_w2x2_a8b8_lines",
-                 "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines",
+                 "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines", "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "fp8_mfma32_256x256x128_w2x2_nt_lines",

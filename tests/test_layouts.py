@@ -326,6 +326,50 @@ def test_tn_lines_epilogue_padded(gpu_available):
     check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "T", "N", "bf16f32", bias=bias, act="gelu")
 
 
+TN_LINES128 = "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines"
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 256), (1000, 1000, 1040), (40, 2048, 4096), (2048, 40, 2048),
+                                   (2104, 2056, 1096), (264, 136, 48), (136, 264, 32), (136, 128, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_tn_lines128_kernel(gpu_available, shape):
+    """The 128 x 128 whole-line kernel with A stored K x M, forced: exact on
+    integer data (K of 8, 32 and 48), and on random data the same bits as
+    the 256 x 256 one."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    small, big = ids[TN_LINES128], ids[TN_LINES]
+    ok, _ = runnable("bf16f32", "T", "N", M, N, K, small)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=768, dtype="bf16f32")
+    As, Bs = stored(A, B, "T", "N")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[tn lines128] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=768")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=small, op_a="T", op_b="N")
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, "T", "N"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=769, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "T", "N")
+    say(f"[tn lines128] random M={M} N={N} K={K} seed=769, against the 256 x 256 kernel")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=small, op_a="T", op_b="N")
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=big, op_a="T", op_b="N")
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, "T", "N", "bf16f32")
+
+
+def test_tn_lines128_epilogue_padded(gpu_available):
+    """Bias and GELU with A^T, B and C inside NaN-padded rows (padding 8, 24
+    and 3 elements)."""
+    M, N, K = 520, 776, 1024
+    A, B, C0 = make_random_inputs(M, N, K, seed=770, dist="normal", dtype="bf16f32")
+    As, Bs = stored(A, B, "T", "N")
+    bias = make_bias(N, seed=771)
+    kid = [k["id"] for k in tg.kernels() if k["name"] == TN_LINES128][0]
+    say(f"[tn lines128] epilogue gelu, padded, M={M} N={N} K={K}")
+    C, _, _ = run_gemm(As, Bs, C0, 1.0 / np.sqrt(K), -0.5, kernel=kid, pad=(8, 24, 3), bias=bias,
+                       activation="gelu", op_a="T", op_b="N")
+    check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "T", "N", "bf16f32", bias=bias, act="gelu")
+
+
 FP8_LINES = "fp8_mfma32_256x256x128_w2x2_nt_lines"
 
 

@@ -845,6 +845,178 @@ bf16_lines_tn_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }, m0, n0, wm, wn, lane);
 }
 
+// The kernel above at 128 x 128 (each wave 64 x 64): four 8 KB single-slice
+// stages per operand (two 64-column blocks of 32 k rows), 64 KB in all.
+// Every block of 4 matrix instructions issues one load of A and one of B:
+// slice s's load 0 in block 2 of slice s - 4, load 1 in block 1 of slice s
+// - 3, so 8 loads per lane follow the last one slice kt + 1 needs by the
+// barrier of slice kt.  Same bits as the 256 x 256 kernel.
+template <int OUT>
+__global__ void __launch_bounds__(256)
+bf16_lines128_tn_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint16_t>(p);
+    constexpr int BM = 128, BN = 128, BK = 32;
+    constexpr int kSlice = BK * 128 * 2;      // 8 KB: 32 k rows x 128 columns
+    constexpr int UNROLL = 4;
+    __shared__ __attribute__((aligned(1024))) char sa0[kSlice], sa1[kSlice], sa2[kSlice], sa3[kSlice];
+    __shared__ __attribute__((aligned(1024))) char sb0[kSlice], sb1[kSlice], sb2[kSlice], sb3[kSlice];
+    auto a_stage = [&](int i) -> char * { return i == 0 ? sa0 : i == 1 ? sa1 : i == 2 ? sa2 : sa3; };
+    auto b_stage = [&](int i) -> char * { return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : sb3; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint16_t *A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *B = static_cast<const uint16_t *>(p.B);
+
+    // Load j (0..1) of a slice, for either operand: g = 2*wave + j covers
+    // block g/4 (columns 64*(g/4) ..), k rows 8*(g%4) .. +7 (lane -> k row
+    // 8*(g%4) + lane/8, physical chunk lane%8), landing at stage + 1024 g.
+    uint32_t a_goff[2], b_goff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int g = 2 * wave + j;
+        const int row = 8 * (g & 3) + (lane >> 3);
+        const int lc = (lane & 7) ^ lines_swz_b(row);
+        a_goff[j] = (uint32_t)(row * lda + 64 * (g >> 2) + 8 * lc) * 2u;
+        b_goff[j] = (uint32_t)(row * ldb + 64 * (g >> 2) + 8 * lc) * 2u;
+    }
+    auto rsrc_a = [&](int s) {
+        const int k0 = BK * s;
+        return make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent(((int64_t)(K - k0 - 1) * lda + (M - m0)) * 2));
+    };
+    auto rsrc_b = [&](int s) {
+        const int k0 = BK * s;
+        return make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 2));
+    };
+    auto dma_a = [&](int si, const rsrc_t &ra, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(a_stage(si) + 1024 * (2 * wave + j)), 16,
+                                                 a_goff[j], 0, 0, 0);
+    };
+    auto dma_b = [&](int si, const rsrc_t &rb, int j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(b_stage(si) + 1024 * (2 * wave + j)), 16,
+                                                 b_goff[j], 0, 0, 0);
+    };
+
+    // Fragment f, k half s of the wave's 64-column block (m for A, n for B):
+    // the transposing reads of the kernel above.
+    const int wm = wave >> 1, wn = wave & 1;
+    const int q = lane >> 4, j16 = lane & 15;
+    const int brow = 8 * (q >> 1) + (j16 >> 2);
+    const int bx = 2 * (q & 1) + ((j16 & 3) >> 1);
+    const int bsw = (j16 >> 3) & 1;
+    uint32_t fa_off[2], fb_off[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const uint32_t in_block = (uint32_t)(brow * 128 + 16 * (bx + 4 * (f ^ bsw)) + 8 * (j16 & 1));
+        fa_off[f] = (uint32_t)(wm * 4096) + in_block;
+        fb_off[f] = (uint32_t)(wn * 4096) + in_block;
+    }
+    auto tr_read = [&](const char *stage, uint32_t off) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(stage + off));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(stage + off + 512));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 fa[2][2], fb[2][2];
+    // Read slot r (0..3): A0, B0, B1, A1.
+    auto read_slot = [&](int si, int s, int set, int r) {
+        if (r == 0 || r == 3) {
+            const int f = r == 0 ? 0 : 1;
+            fa[set][f] = tr_read(a_stage(si), fa_off[f] + 2048 * s);
+        } else {
+            fb[set][r - 1] = tr_read(b_stage(si), fb_off[r - 1] + 2048 * s);
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto mma = [&](int set, int t) {
+        const int i = t >> 1, j = t & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+    };
+
+    // Prologue: slices 0..2 whole and load 0 of slice 3, A before B in each;
+    // slice 0 is followed by 10 loads.
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+        const rsrc_t ra = rsrc_a(s2), rb = rsrc_b(s2);
+#pragma unroll
+        for (int j = 0; j < (s2 < 3 ? 2 : 1); ++j) dma_a(s2, ra, j);
+#pragma unroll
+        for (int j = 0; j < (s2 < 3 ? 2 : 1); ++j) dma_b(s2, rb, j);
+    }
+    rsrc_t ra_pend = rsrc_a(3), rb_pend = rsrc_b(3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(10));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) read_slot(0, 0, 0, r);
+    auto slice = [&](int u, int kt) {
+        const int st = u % 4, st3 = (u + 3) % 4, st_n = (u + 1) % 4;
+        rsrc_t ra_next, rb_next;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            mma(0, t);
+            read_slot(st, 1, 1, t);
+            if (t == 0) ra_next = rsrc_a(kt + 4);
+            else if (t == 1) dma_a(st3, ra_pend, 1);
+            else if (t == 2) rb_next = rsrc_b(kt + 4);
+            else dma_b(st3, rb_pend, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            mma(1, t);
+            read_slot(st_n, 0, 0, t);
+            if (t == 0) dma_a(st, ra_next, 0);
+            else if (t == 2) dma_b(st, rb_next, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        ra_pend = ra_next;
+        rb_pend = rb_next;
+    };
+    const int nfull = nk / UNROLL;
+    int kb = 0;
+    for (int it = 0; it < nfull; ++it, kb += UNROLL) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) slice(u, kb + u);
+    }
+    const int rem = nk - kb;
+#pragma unroll
+    for (int u = 0; u < UNROLL - 1; ++u)
+        if (u < rem) slice(u, kb + u);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    // Each wave's 16 KB of staging: two consecutive stages.
+    char *lo = wave == 0 ? sa0 : wave == 1 ? sa2 : wave == 2 ? sb0 : sb2;
+    char *hi = wave == 0 ? sa1 : wave == 1 ? sa3 : wave == 2 ? sb1 : sb3;
+    lines_epilogue<OUT, false>(p, acc, [&](int row) -> char * {
+        return (row < 32 ? lo : hi) + (row & 31) * 256;
+    }, m0, n0, wm, wn, lane);
+}
+
+hipError_t launch_bf16_lines128_tn(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 127) / 128, tiles_n = (p.N + 127) / 128;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&bf16_lines128_tn_kernel<GEMM_OUT_BF16>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&bf16_lines128_tn_kernel<GEMM_OUT_FP8>)
+                                           : reinterpret_cast<const void *>(&bf16_lines128_tn_kernel<GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
+}
+
 hipError_t launch_bf16_lines_tn(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 255) / 256, tiles_n = (p.N + 255) / 256;
     GemmParams args = p;
@@ -896,6 +1068,9 @@ template __global__ void bf16_lines128_kernel<GEMM_OUT_F32, true>(GemmParams, in
 template __global__ void bf16_lines128_kernel<GEMM_OUT_BF16, true>(GemmParams, int, int);
 template __global__ void bf16_lines128_kernel<GEMM_OUT_FP8, true>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_lines128_tn_kernel<GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void bf16_lines128_tn_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void bf16_lines128_tn_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
 template __global__ void bf16_lines_tn_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 
@@ -913,6 +1088,8 @@ const KernelDesc kBf16LinesKernels[] = {
      &launch_bf16_lines128<false>, 256, nullptr, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 128, 128, 64, 256, 8, 8, "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines",
      &launch_bf16_lines128<true>, 256, nullptr, kLayoutNT, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_TILED, 128, 128, 32, 256, 8, 8, "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines",
+     &launch_bf16_lines128_tn, 256, nullptr, kLayoutTN, false, kOutAll},
 };
 const int kBf16LinesKernelCount = sizeof(kBf16LinesKernels) / sizeof(kBf16LinesKernels[0]);
 #endif
