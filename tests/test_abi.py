@@ -244,10 +244,11 @@ def test_bf16_tile_choice():
 
 
 def test_bf16_mid_size_choice():
-    """bf16 problems with 256 to 1023 tiles of 128^2 take the 128 x 128
-    whole-line kernel; with a workspace it is still preferred, unsplit, over
-    256^2 tiles split over K (the split's workspace round trip costs more
-    than the smaller tile gives up).  fp32 keeps the split 256^2 ring there."""
+    """bf16 (and fp8) problems with 256 to 1023 tiles of 128^2 take a 128 x
+    128 whole-line kernel; with a workspace it is still preferred, unsplit,
+    over 256^2 tiles split over K (the split's workspace round trip costs
+    more than the smaller tile gives up).  fp32 keeps the split 256^2 ring
+    there."""
     L128 = "bf16_mfma32_128x128x64_w2x2_a8b8_lines"
     for M, N, K in [(2048, 2048, 2048), (2048, 4096, 4096), (2048, 2048, 8192), (1536, 1536, 4096)]:
         for ws in (0, 1 << 34):
@@ -268,6 +269,10 @@ def test_bf16_mid_size_choice():
             assert st == OK and kname(p) == "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines" and p["splits"] == 1, p
             st, p = gplan(BF16, T_, N_, M, N, K, ws=ws)
             assert st == OK and kname(p) == "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines" and p["splits"] == 1, p
+    # fp8 with B stored N x K likewise.
+    for ws in (0, 1 << 34):
+        st, p = gplan(FP8, N_, T_, 2048, 4096, 4096, ws=ws)
+        assert st == OK and kname(p) == "fp8_mfma32_128x128x128_w2x2_nt_lines" and p["splits"] == 1, p
     # Below its minimum K the generic 128^2 kernel runs.
     st, p = plan(BF16, 2048, 2048, 128)
     assert st == OK and p["tile_m"] == 128 and kname(p) != L128, p
@@ -793,7 +798,7 @@ def test_output_types_of_the_kernels():
                  "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines", "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
-                 "fp8_mfma32_256x256x128_w2x2_nt_lines",
+                 "fp8_mfma32_256x256x128_w2x2_nt_lines", "fp8_mfma32_128x128x128_w2x2_nt_lines",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
                  "fp8_skinny_nt_splitk_n32_w8_u2"):

@@ -399,15 +399,46 @@ def test_fp8_lines_kernel(gpu_available, shape):
     check(C1, As, Bs, C0, 0.5, 0.25, "N", "T", "fp8f32")
 
 
-def test_fp8_lines_epilogue_padded(gpu_available):
+FP8_LINES128 = "fp8_mfma32_128x128x128_w2x2_nt_lines"
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 256), (1000, 1001, 1040), (33, 2048, 4096), (2048, 40, 2048),
+                                   (2100, 2059, 1088), (300, 264, 80), (136, 130, 64), (130, 136, 16)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_lines128_kernel(gpu_available, shape):
+    """The 128 x 128 whole-line fp8 kernel, forced: exact on integer data
+    (K of 16, 64 and 80: part of a slice, one slice, a pair and a part), and
+    on random data the same bits as the 256 x 256 one."""
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    small, big = ids[FP8_LINES128], ids[FP8_LINES]
+    ok, _ = runnable("fp8f32", "N", "T", M, N, K, small)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=772, dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[fp8 lines128] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=772")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=small, op_a="N", op_b="T")
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, "N", "T"))
+    A, B, C0 = make_random_inputs(M, N, K, seed=773, dist="normal", dtype="fp8f32")
+    As, Bs = stored(A, B, "N", "T")
+    say(f"[fp8 lines128] random M={M} N={N} K={K} seed=773, against the 256 x 256 kernel")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=small, op_a="N", op_b="T")
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=big, op_a="N", op_b="T")
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, "N", "T", "fp8f32")
+
+
+@pytest.mark.parametrize("name", [FP8_LINES, FP8_LINES128])
+def test_fp8_lines_epilogue_padded(gpu_available, name):
     """Bias and GELU with A, B and C inside NaN-padded rows (padding 16, 48
     and 3 elements), ragged N."""
     M, N, K = 520, 777, 1024
     A, B, C0 = make_random_inputs(M, N, K, seed=742, dist="normal", dtype="fp8f32")
     As, Bs = stored(A, B, "N", "T")
     bias = make_bias(N, seed=743)
-    lines = [k["id"] for k in tg.kernels() if k["name"] == FP8_LINES][0]
-    say(f"[fp8 lines] epilogue gelu, padded, M={M} N={N} K={K}")
+    lines = [k["id"] for k in tg.kernels() if k["name"] == name][0]
+    say(f"[fp8 lines] {name} epilogue gelu, padded, M={M} N={N} K={K}")
     C, _, _ = run_gemm(As, Bs, C0, 1.0 / np.sqrt(K), -0.5, kernel=lines, pad=(16, 48, 3), bias=bias,
                        activation="gelu", op_a="N", op_b="T")
     check(C, As, Bs, C0, 1.0 / np.sqrt(K), -0.5, "N", "T", "fp8f32", bias=bias, act="gelu")

@@ -383,13 +383,14 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand) {
             const KSplit ks = call_ksplit(c, kd);
             const int64_t groups = (pm / tile) * (pn / tile) * ks.splits;
             const bool fills = ks.splits > 1 ? 4 * groups >= 3 * kComputeUnits : groups >= kComputeUnits;
-            // bf16: a split sends every partial product through the
+            // bf16 and fp8: a split sends every partial product through the
             // workspace and back (2048 x 4096 x 4096 in two: 160 MB), which
             // costs more than the smaller tile gives up, so a smaller tile
             // that fills the compute units unsplit goes first (there: 68 us
-            // for 128^2 tiles against 87 us for 256^2 tiles in two slices).
-            // The fp32 kernels' matrix work is 8x longer and the split wins.
-            if (ks.splits > 1 && c.dtype == GEMM_DTYPE_BF16F32 && tile > 64 &&
+            // for 128^2 tiles against 87 us for 256^2 tiles in two slices in
+            // bf16, 41 against 63 us in fp8).  The fp32 kernels' matrix work
+            // is 8x longer and the split wins.
+            if (ks.splits > 1 && c.dtype != GEMM_DTYPE_F32 && tile > 64 &&
                 ceil_div(c.M, tile / 2) * ceil_div(c.N, tile / 2) >= kComputeUnits &&
                 first_candidate(cand, c, tile / 2) != nullptr)
                 continue;

@@ -40,6 +40,7 @@
 // B slice kt + 1 and both halves of the A pair holding it.
 #include "gemm_device.hpp"
 #include "gemm_kernels.hpp"
+#include "gemm_lines.hpp"
 #include "gemm.h"
 
 namespace gemm {
@@ -220,99 +221,186 @@ fp8_lines_kernel(GemmParams p, int tiles_m, int tiles_n) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __builtin_amdgcn_s_barrier();
 
-    // Epilogue, in two passes of 64 columns per wave, through LDS as in the
-    // whole-line bf16 kernel: the wave's 128 x 64 accumulators are written to
-    // its 32 KB of LDS in their register layout (register 4g + t of lane (h,
-    // l32) in fragment (fm, fn) is row 32fm + l32, column 32*(fn%2) + 8g + 4h
-    // + t of the pass; 16-byte chunk c of a row at c ^ (row & 15)), then read
-    // back 4 rows x 64 columns per instruction.  N is free: runs of 4 columns
-    // that straddle N are read and stored element by element.
+    // Epilogue, in two passes of 64 columns per wave (lines_epilogue; N is
+    // free): the wave's 32 KB of LDS is a pair stage for waves 0-2 and two B
+    // stages for wave 3.
     char *stg = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : nullptr;
-    auto stage_row = [&](int row) -> char * {
+    lines_epilogue<OUT, true>(p, acc, [&](int row) -> char * {
         return stg != nullptr ? stg + row * 256 : (row < 64 ? sb0 : sb1) + (row & 63) * 256;
-    };
-    const float alpha = p.alpha, beta = p.beta;
-    const bool vec_c = ((reinterpret_cast<uintptr_t>(p.C) & 15) == 0) && (p.ldc % 4 == 0);
-    const bool vec_o = out_vec4<OUT>(p);
-    const int act = p.act;
+    }, m0, n0, wm, wn, lane);
+}
+
+// The same ring at a quarter of the tile: 128 x 128 outputs per workgroup,
+// each wave 64 x 64 (2 x 2 fragments), for problems with too few 256 x 256
+// tiles to fill the compute units.  Three A pair stages of 16 KB (128 rows x
+// 128 k) and four B stages of 8 KB (128 rows x 64 k), 80 KB in all, so that
+// two workgroups fit a compute unit.  Per slice, 4 matrix instructions per
+// wave, each paired with two of the 8 fragment reads of the next slice and
+// one of the slice's 4 loads: B slice kt + 4 (loads 0, 1), then A pair
+// (kt + 5) / 2 loads 0, 1 when kt is odd or pair (kt + 4) / 2 loads 2, 3 when
+// kt is even.  At the barrier of slice kt every load of slice kt - 3 or
+// earlier has landed (vmcnt(8)), which covers slice kt + 1.  Layouts,
+// swizzles and the per-lane order of the sums are the 256 x 256 kernel's, so
+// the two give identical bits.
+template <int OUT>
+__global__ void __launch_bounds__(256)
+fp8_lines128_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint8_t>(p);
+    constexpr int BM = 128, BN = 128, BK = 64;
+    constexpr int kAPair = BM * 2 * BK;       // 16 KB: 128 rows x 128 k
+    constexpr int kBSlice = BN * BK;          // 8 KB: 128 rows x 64 k
+    constexpr int UNROLL = 12;
+    __shared__ __attribute__((aligned(1024))) char sa0[kAPair], sa1[kAPair], sa2[kAPair];
+    __shared__ __attribute__((aligned(1024))) char sb0[kBSlice], sb1[kBSlice], sb2[kBSlice], sb3[kBSlice];
+    auto a_stage = [&](int i) -> char * { return i == 0 ? sa0 : i == 1 ? sa1 : sa2; };
+    auto b_stage = [&](int i) -> char * { return i == 0 ? sb0 : i == 1 ? sb1 : i == 2 ? sb2 : sb3; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint8_t *A = static_cast<const uint8_t *>(p.A);
+    const uint8_t *B = static_cast<const uint8_t *>(p.B);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+
+    // A load j (0..3) for a pair: rows 8g .. 8g+7 with g = 4*wave + j (lane ->
+    // row 8g + lane/8, physical chunk lane%8), landing at stage + 1024 g.  B
+    // load j (0..1) of a slice: rows 16g .. 16g+15 with g = 2*wave + j (lane
+    // -> row 16g + lane/4, physical chunk lane%4), landing at stage + 1024 g.
+    uint32_t a_goff[4], b_goff[2];
+    int a_kc[4], b_kc[2];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int fl = 0; fl < 2; ++fl) {
-            const int fn = 2 * pass + fl;
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) {
-                const int row = 32 * fm + l32;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int c = (8 * fl + 2 * g + h) ^ (row & 15);
-                    const f32x4 v = {acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
-                                     acc[fm][fn][4 * g + 3]};
-                    *reinterpret_cast<f32x4 *>(stage_row(row) + 16 * c) = v;
-                }
-            }
-        }
-        const int cc = lane & 15;
-        const int col = n0 + wn * 128 + 64 * pass + 4 * cc;
-        const bool whole = col + 4 <= N;
-        float b[4];   // -0.0 is the identity of IEEE addition, signed zeros included
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = (p.bias != nullptr && col + t < N) ? p.bias[col + t] : -0.0f;
-        if (alpha == 1.0f && beta == 0.0f && p.bias == nullptr && act == GEMM_ACT_NONE) {
-            for (int i0 = 0; i0 < 32; i0 += 8) {
-                f32x4 vv[8];
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
-                    const int row = 4 * (i0 + ii) + (lane >> 4);
-                    vv[ii] = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
-                }
-#pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
-                    const int grow = m0 + wm * 128 + 4 * (i0 + ii) + (lane >> 4);
-                    if (grow >= M || col >= N) continue;
-                    if (whole)
-                        store_out4<OUT>(p, grow, col, vv[ii], vec_o);
-                    else
-                        store_out_first<OUT>(p, grow, col, vv[ii], N - col);
-                }
-            }
-            continue;
-        }
-#pragma unroll 4
-        for (int i = 0; i < 32; ++i) {
-            const int row = 4 * i + (lane >> 4);
-            f32x4 v = *reinterpret_cast<const f32x4 *>(stage_row(row) + 16 * (cc ^ (row & 15)));
-            const int grow = m0 + wm * 128 + row;
-            if (grow >= M || col >= N) continue;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] *= alpha;
-            if (beta != 0.0f) {
-                const float *cp = p.C + (int64_t)grow * p.ldc + col;
-                f32x4 c0;
-                if (whole && vec_c) {
-                    c0 = *reinterpret_cast<const f32x4 *>(cp);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) c0[t] = col + t < N ? cp[t] : 0.0f;
-                }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = fmaf(beta, c0[t], v[t]);
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] += b[t];
-            if (act == GEMM_ACT_GELU) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = ActGelu::apply(v[t]);
-            } else if (act == GEMM_ACT_RELU) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = ActRelu::apply(v[t]);
-            }
-            if (whole)
-                store_out4<OUT>(p, grow, col, v, vec_o);
-            else
-                store_out_first<OUT>(p, grow, col, v, N - col);
-        }
+    for (int j = 0; j < 4; ++j) {
+        const int row = 8 * (4 * wave + j) + (lane >> 3);
+        const int lc = (lane & 7) ^ fl_swz_a(row);
+        a_kc[j] = 16 * lc;
+        a_goff[j] = panel_off(row, a_rows, lda, 16 * lc, 1);
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * (2 * wave + j) + (lane >> 2);
+        const int lc = (lane & 3) ^ fl_swz_b(row);
+        b_kc[j] = 16 * lc;
+        b_goff[j] = panel_off(row, b_rows, ldb, 16 * lc, 1);
+    }
+    auto rsrc_a = [&](int P) {
+        const int k0 = 2 * BK * P;
+        return make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent((int64_t)(a_rows - 1) * lda + (K - k0)));
+    };
+    auto rsrc_b = [&](int s) {
+        const int k0 = BK * s;
+        return make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent((int64_t)(b_rows - 1) * ldb + (K - k0)));
+    };
+    auto dma_a = [&](int P, int si, const rsrc_t &ra, int j) {
+        const uint32_t poison = (uint32_t)(a_kc[j] >= K - 2 * BK * P) << 31;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(a_stage(si) + (4 * wave + j) * 1024), 16,
+                                                 a_goff[j] + poison, 0, 0, 0);
+    };
+    auto dma_b = [&](int s, int si, const rsrc_t &rb, int j) {
+        const uint32_t poison = (uint32_t)(b_kc[j] >= K - BK * s) << 31;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(b_stage(si) + (2 * wave + j) * 1024), 16,
+                                                 b_goff[j] + poison, 0, 0, 0);
+    };
+
+    // Fragment reads.  Slot r (0..7) of a slice: r < 4 reads A fragment r / 2,
+    // half r % 2; r >= 4 reads B fragment (r - 4) / 2, half r % 2.
+    const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int sa = fl_swz_a(l32), sb = fl_swz_b(l32);
+    const uint32_t fa_row = (uint32_t)((wm * 64 + l32) * 2 * BK);
+    const uint32_t fb_row = (uint32_t)((wn * 64 + l32) * BK);
+    i32x8 fa[2][2], fb[2][2];
+    auto read_slot = [&](int asi, int par, int bsi, int set, int r) {
+        const int f = (r >> 1) & 1, hf = r & 1;
+        u32x4 v;
+        if (r < 4) {
+            const int c = (4 * par + 2 * h + hf) ^ sa;
+            v = *reinterpret_cast<const u32x4 *>(a_stage(asi) + fa_row + 32 * 2 * BK * f + 16 * c);
+        } else {
+            const int c = (2 * h + hf) ^ sb;
+            v = *reinterpret_cast<const u32x4 *>(b_stage(bsi) + fb_row + 32 * BK * f + 16 * c);
+        }
+        i32x8 *frags = r < 4 ? fa[set] : fb[set];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) frags[f][4 * hf + e] = (int)v[e];
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto mma = [&](int set, int t) {
+        const int i = t >> 1, j = t & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0, 0,
+                                                                     0, 0);
+    };
+
+    // Prologue: A pairs 0 and 1, B slices 0..3, and A pair 2's loads 0, 1 (the
+    // share of "slice -1"); slice 0 (A pair 0, B slice 0) is followed by 12.
+    const int nk = (K + BK - 1) / BK;
+    {
+        const rsrc_t ra0 = rsrc_a(0), ra1 = rsrc_a(1), ra2 = rsrc_a(2);
+        const rsrc_t rb0 = rsrc_b(0), rb1 = rsrc_b(1), rb2 = rsrc_b(2), rb3 = rsrc_b(3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_a(0, 0, ra0, j);
+        dma_b(0, 0, rb0, 0);
+        dma_b(0, 0, rb0, 1);
+        dma_b(1, 1, rb1, 0);
+        dma_b(1, 1, rb1, 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_a(1, 1, ra1, j);
+        dma_b(2, 2, rb2, 0);
+        dma_b(2, 2, rb2, 1);
+        dma_b(3, 3, rb3, 0);
+        dma_b(3, 3, rb3, 1);
+        dma_a(2, 2, ra2, 0);
+        dma_a(2, 2, ra2, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(12));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < 8; ++r) read_slot(0, 0, 0, 0, r);
+
+    auto slice = [&](int u, int kt) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(8));
+        __builtin_amdgcn_s_barrier();
+        const int as_n = ((u + 1) >> 1) % 3, bs_n = (u + 1) % 4;
+        const int PA = (u & 1) ? (kt + 5) >> 1 : (kt + 4) >> 1;
+        const int pa_st = ((u & 1) ? (u + 5) >> 1 : (u + 4) >> 1) % 3;
+        const int ja = (u & 1) ? 0 : 2;
+        const rsrc_t ra = rsrc_a(PA), rb = rsrc_b(kt + 4);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            mma(u & 1, t);
+            read_slot(as_n, (u + 1) & 1, bs_n, (u + 1) & 1, 2 * t);
+            read_slot(as_n, (u + 1) & 1, bs_n, (u + 1) & 1, 2 * t + 1);
+            if (t < 2) dma_b(kt + 4, u % 4, rb, t);
+            else dma_a(PA, pa_st, ra, ja + t - 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    const int nfull = nk / UNROLL;
+    int kb = 0;
+    for (int it = 0; it < nfull; ++it, kb += UNROLL) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) slice(u, kb + u);
+    }
+    const int rem = nk - kb;
+#pragma unroll
+    for (int u = 0; u < UNROLL - 1; ++u)
+        if (u < rem) slice(u, kb + u);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+
+    // Epilogue in one pass of 64 columns per wave: 16 KB of staging each, a
+    // pair stage for waves 0-2 and two B stages for wave 3.
+    char *stg = wave == 0 ? sa0 : wave == 1 ? sa1 : wave == 2 ? sa2 : nullptr;
+    lines_epilogue<OUT, true>(p, acc, [&](int row) -> char * {
+        return stg != nullptr ? stg + row * 256 : (row < 32 ? sb0 : sb1) + (row & 31) * 256;
+    }, m0, n0, wm, wn, lane);
 }
 
 hipError_t launch_fp8_lines(const GemmParams &p, hipStream_t stream) {
@@ -327,7 +415,22 @@ hipError_t launch_fp8_lines(const GemmParams &p, hipStream_t stream) {
                            stream);
 }
 
+hipError_t launch_fp8_lines128(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 127) / 128, tiles_n = (p.N + 127) / 128;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&fp8_lines128_kernel<GEMM_OUT_BF16>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&fp8_lines128_kernel<GEMM_OUT_FP8>)
+                                           : reinterpret_cast<const void *>(&fp8_lines128_kernel<GEMM_OUT_F32>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
+}
+
 template __global__ void fp8_lines_kernel<GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void fp8_lines128_kernel<GEMM_OUT_F32>(GemmParams, int, int);
+template __global__ void fp8_lines128_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
+template __global__ void fp8_lines128_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 template __global__ void fp8_lines_kernel<GEMM_OUT_BF16>(GemmParams, int, int);
 template __global__ void fp8_lines_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 
@@ -338,6 +441,8 @@ template __global__ void fp8_lines_kernel<GEMM_OUT_FP8>(GemmParams, int, int);
 const KernelDesc kFp8LinesKernels[] = {
     {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 128, 256, 16, 16, "fp8_mfma32_256x256x128_w2x2_nt_lines",
      &launch_fp8_lines, 1024, nullptr, kLayoutNT, false, kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 128, 128, 128, 256, 16, 16, "fp8_mfma32_128x128x128_w2x2_nt_lines",
+     &launch_fp8_lines128, 256, nullptr, kLayoutNT, false, kOutAll},
 };
 const int kFp8LinesKernelCount = sizeof(kFp8LinesKernels) / sizeof(kFp8LinesKernels[0]);
 #endif
