@@ -47,10 +47,11 @@ PEAK_HBM_GBS = 8000.0
 # right after the bf16 GEMM, whose 256 MB of freshly written C would still be
 # draining from the last-level cache to HBM while the skinny kernel streams B.
 STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
-# Timed on their own with --only (not part of the step): fp8 operands, B stored N x K.
+# Timed on their own with --only (not part of the step): other operand types,
+# layouts and shapes.
 EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x8192x8192", "bf16f32_16x8192x8192_nt",
          "f32_16x8192x8192_nt", "fp8f32_16x8192x8192_nt", "f32_4096_nt", "f32_4096_tn",
-         "fp8f32_8192_nn", "fp8f32_8192_tn"]
+         "fp8f32_8192_nn", "fp8f32_8192_tn", "bf16f32_2048x4096x4096", "bf16f32_2048x4096x4096_nt"]
 # The other configurations of the workload set, timed call by call after the
 # step (they do not enter ``value``): (workload, whether a workspace is passed).
 # The M = 16 shape is timed here through the plain call as well, which has no
@@ -92,12 +93,18 @@ KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_
                   "bf16_mfma32_256x256x64_w2x2_a8b8_lines": "gemm_bf16_lines.hip",
                   "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines": "gemm_bf16_lines.hip",
                   "bf16_mfma32_256x256x32_w2x2_a8b8_tn_lines": "gemm_bf16_lines.hip",
+                  "bf16_mfma32_128x128x64_w2x2_a8b8_lines": "gemm_bf16_lines.hip",
+                  "bf16_mfma32_128x128x64_w2x2_a8b8_nt_lines": "gemm_bf16_lines.hip",
+                  "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines": "gemm_bf16_lines.hip",
                   "fp8_mfma32_256x256x128_w2x2_nt_lines": "gemm_fp8_lines.hip",
+                  "fp8_mfma32_128x128x128_w2x2_nt_lines": "gemm_fp8_lines.hip",
                   "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip",
                   "bf16_skinny": "gemm_bf16_skinny.hip", "f32_skinny_nt": "gemm_skinny_nt.hip",
                   "bf16_skinny_nt": "gemm_skinny_nt.hip", "fp8_skinny_nt": "gemm_skinny_nt.hip"}
 
 
+# Headers that only some kernel sources include (the whole-line epilogue).
+OWN_HEADERS = ["gemm_lines.hpp"]
 # Headers every kernel source includes: a change there changes the kernels too.
 KERNEL_HEADERS = [os.path.join("tiled_gemm_f32_amd", "csrc", "gemm_device.hpp"),
                   os.path.join("tiled_gemm_f32_amd", "csrc", "gemm_kernels.hpp"),
@@ -105,14 +112,20 @@ KERNEL_HEADERS = [os.path.join("tiled_gemm_f32_amd", "csrc", "gemm_device.hpp"),
 
 
 def kernel_source_sha(kernel_name: str):
-    """sha256 over the source file a kernel is built from and the shared
-    headers it includes (to spot stale counter data)."""
+    """sha256 over the source file a kernel is built from, the shared headers
+    every source includes and the headers of its own that the source
+    includes (to spot stale counter data)."""
     import hashlib
     # The longest matching prefix names the source.
     for prefix, src in sorted(KERNEL_SOURCES.items(), key=lambda kv: -len(kv[0])):
         if kernel_name.startswith(prefix):
+            src_path = os.path.join("tiled_gemm_f32_amd", "csrc", src)
+            with open(os.path.join(ROOT, src_path), "rb") as f:
+                text = f.read()
+            own = [os.path.join("tiled_gemm_f32_amd", "csrc", hdr) for hdr in OWN_HEADERS
+                   if b'#include "' + hdr.encode() + b'"' in text]
             h = hashlib.sha256()
-            for path in [os.path.join("tiled_gemm_f32_amd", "csrc", src)] + KERNEL_HEADERS:
+            for path in [src_path] + KERNEL_HEADERS + own:
                 with open(os.path.join(ROOT, path), "rb") as f:
                     h.update(f.read())
             return h.hexdigest()

@@ -80,6 +80,9 @@ WORKLOADS = {
         Workload("f32_4096_tn", "f32", 4096, 4096, 4096, 1.0, 0.0, "normal", 13, "N", "T"),
         Workload("fp8f32_8192_nn", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 14),
         Workload("fp8f32_8192_tn", "fp8f32", 8192, 8192, 8192, 1.0, 0.0, "normal", 15, "N", "T"),
+        # Mid-size: 512 tiles of 128^2 (two workgroups per compute unit), 128 of 256^2.
+        Workload("bf16f32_2048x4096x4096", "bf16f32", 2048, 4096, 4096, 1.0, 0.0, "normal", 16),
+        Workload("bf16f32_2048x4096x4096_nt", "bf16f32", 2048, 4096, 4096, 1.0, 0.0, "normal", 17, "T"),
     ]
 }
 
