@@ -895,3 +895,13 @@ def test_noalloc_rejects_problems_beyond_the_static_scratch():
     # The decode and small-tile splits fit.
     for dt, M, N, K in [(F32, 16, 8192, 8192), (BF16, 16, 8192, 8192), (BF16, 512, 512, 8192), (F32, 16, 16384, 65536)]:
         assert 0 < tg.gemm_workspace_size(dt, M, N, K) <= tg.GEMM_STATIC_SCRATCH_BYTES, (dt, M, N, K)
+
+
+def test_f32_ring64_is_the_choice_for_config_4a():
+    """fp32 1000 x 3000 x 777 (rows of A 4-byte aligned only) takes the 64 x 64
+    ring with 4-byte A loads, with or without a workspace."""
+    for ws in (0, 1 << 30):
+        st, pl = tg.gemm_plan_query(F32, 1000, 3000, 777, 2.0, 0x1000, 777, 0x1000, 3000, -1.0,
+                                    0x1000, 3000, 0, ws)
+        assert st == OK and kname(pl) == \
+            "f32_mfma32_64x64x16_w2x2_a1b4_ring6", pl
