@@ -286,31 +286,33 @@ def test_split_k_skinny_deterministic(gpu_available):
     assert all(torch.equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("tile", [64, 128])
 @pytest.mark.parametrize("va", [1, 4])
-def test_f32_ring64_matches_register_staged(gpu_available, va):
-    """The 64 x 64 fp32 ring (A loaded 4 or 16 bytes per lane) pairs the same
-    k in the same order as the register-staged 64 x 64 kernel: on random data
-    the two give the same bits, on integer data both equal the oracle.  K of
-    777 and 255 make A's rows unaligned (4-byte loads); K of 16, 17 and 3
-    are one slice, one slice and a bit, and part of one."""
+def test_f32_ring_small_tiles_match_register_staged(gpu_available, va, tile):
+    """The 64 x 64 and 128 x 128 fp32 rings (A loaded 4 or 16 bytes per lane)
+    pair the same k in the same order as the register-staged kernels of
+    their tile: on random data the two give the same bits, on integer data
+    both equal the oracle.  K of 777, 255 and 1001 make A's rows unaligned
+    (4-byte loads); K of 16, 17 and 3 are one slice, one slice and a bit, and
+    part of one."""
     ids = {k["name"]: k["id"] for k in tg.kernels()}
-    ring = ids[f"f32_mfma32_64x64x16_w2x2_a{va}b4_ring6"]
-    staged = ids[f"f32_mfma32_64x64x16_w2x2_a{va}b4"]
+    ns = 6 if tile == 64 else 4
+    ring = ids[f"f32_mfma32_{tile}x{tile}x16_w2x2_a{va}b4_ring{ns}"]
+    staged = ids[f"f32_mfma32_{tile}x{tile}x16_w2x2_a{va}b4"]
     shapes = ([(1000, 3000, 777), (257, 264, 255), (65, 68, 17), (64, 64, 3), (130, 1028, 1001)] if va == 1 else
               [(1024, 1024, 1024), (256, 256, 256), (65, 68, 16), (300, 520, 1032), (64, 4, 4)])
     for M, N, K in shapes:
         st, _ = tg.gemm_plan_query(tg.GEMM_DTYPE_F32, M, N, K, 1.0, 0x1000, K, 0x1000, N, 0.0, 0x1000, N, ring, 0)
         assert st == tg.GEMM_OK, (M, N, K)
         A, B, C0 = make_random_inputs(M, N, K, seed=M + 3 * N + K, dist="uniform")
-        say(f"[f32 ring64 a{va}] random M={M} N={N} K={K}")
+        say(f"[f32 ring {tile} a{va}] random M={M} N={N} K={K}")
         C1, _, _ = run_gemm(A, B, C0, 2.0, -1.0, kernel=ring)
         C2, _, _ = run_gemm(A, B, C0, 2.0, -1.0, kernel=staged)
         np.testing.assert_array_equal(C1, C2, err_msg=f"{M}x{N}x{K}")
         assert ratio(C1, A, B, C0, 2.0, -1.0) <= TOL["f32"]
         Ai, Bi, Ci = make_integer_inputs(M, N, K, seed=M * 5 + K)
-        say(f"[f32 ring64 a{va}] exact M={M} N={N} K={K}")
+        say(f"[f32 ring {tile} a{va}] exact M={M} N={N} K={K}")
         for alpha, beta in [(2.0, -1.0), (1.0, 0.0)]:
             C, _, _ = run_gemm(Ai, Bi, Ci, alpha, beta, kernel=ring)
             np.testing.assert_array_equal(C.astype(np.float64), _exact(Ai, Bi, Ci, alpha, beta),
                                           err_msg=f"{M}x{N}x{K}")
-

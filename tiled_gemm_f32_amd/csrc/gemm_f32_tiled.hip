@@ -531,38 +531,40 @@ hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
                            stream);
 }
 
-// 64 x 64 tiles on a direct-to-LDS ring of NS stages, for problems whose
-// 64 x 64 tiles are the ones that fill the compute units.  The register-staged
-// kernel above holds one slice in flight, so every 16-deep slice (8 matrix
-// instructions per wave, about 500 cycles) waits out a whole global-load
-// latency; here slice kt + NS - 1 is requested as slice kt starts ("A GEMM
-// Kernel, Step by Step", "What is left": asynchronous copies and
-// multi-buffering), and three workgroups of NS = 6 stages (49 KB) share a
-// compute unit.
-//   A slice: [64 rows][4 chunks of 16 B] (k contiguous), logical chunk c of
-//     row r at c ^ ((r >> 2) & 3), as in the 256 x 256 ring.  VA = 4: one
-//     16-byte load per lane.  VA = 1 (rows of A not 16-byte aligned, such as
-//     an odd K): four 4-byte loads per lane, lane i of a wave instruction
-//     landing at 4i bytes, so each lane fetches the element that belongs at
-//     its LDS position under the swizzle.
-//   B slice: [16 k rows][64 columns] as in HBM, k rows 8 .. 15 starting 128
+// 64 x 64 (F = 1) and 128 x 128 (F = 2) tiles on a direct-to-LDS ring of NS
+// stages, each of the 4 waves owning F x F fragments of 32 x 32.  The
+// register-staged kernel above holds one slice in flight, so every 16-deep
+// slice waits out a whole global-load latency; here slice kt + NS - 1 is
+// requested as slice kt starts ("A GEMM Kernel, Step by Step", "What is
+// left": asynchronous copies and multi-buffering).  64 x 64: six stages of
+// 8 KB, three workgroups per compute unit; 128 x 128: four of 16 KB, two.
+//   A slice: [BM rows][4 chunks of 16 B] (k contiguous), logical chunk c of
+//     row r at c ^ ((r >> 2) & 3), as in the 256 x 256 ring.  VA = 4: 16-byte
+//     loads (16 rows per wave instruction).  VA = 1 (rows of A not 16-byte
+//     aligned, such as an odd K): 4-byte loads (4 rows per wave instruction),
+//     lane i landing at 4i bytes, so each lane fetches the element that
+//     belongs at its LDS position under the swizzle.
+//   B slice: [16 k rows][BN columns] as in HBM, k rows 8 .. 15 starting 128
 //     bytes later so that the two lane halves' reads (k rows s and 8 + s)
 //     fall in different banks.
-// Each wave owns one 32 x 32 fragment: lane (h, l32) holds row l32 of the
-// wave's A block at k = 8h .. 8h+7 of the slice and reads column l32 of B at
-// k row 8h + s for step s, so the k order is that of the kernel above.
-template <int VA, int NS>
+// Lane (h, l32) holds row l32 of each of its A fragments at k = 8h .. 8h+7
+// of the slice and reads column l32 of each B fragment at k row 8h + s for
+// step s, so every accumulator sums k in the order of the kernel above.
+template <int VA, int NS, int F>
 __global__ void __launch_bounds__(256)
 f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<float>(p);
     static_assert(VA == 1 || VA == 4, "A loads of 4 or 16 bytes");
     static_assert(NS >= 3 && NS <= 6, "six stage arrays");
-    constexpr int BM = 64, BN = 64, BK = 16;
-    constexpr int kA = BM * BK * 4;             // 4 KB
+    static_assert(F == 1 || F == 2, "64 x 64 or 128 x 128 tiles");
+    constexpr int BM = 64 * F, BN = 64 * F, BK = 16;
+    constexpr int kA = BM * BK * 4;
+    constexpr int kBRow = BN * 4;                // bytes per k row of B
     constexpr int kBPad = 128;
-    constexpr int kStage = kA + BK * BN * 4 + kBPad;
-    constexpr int kALoads = VA == 4 ? 1 : 4;    // A loads per wave per slice
-    constexpr int kLoads = kALoads + 1;
+    constexpr int kStage = kA + BK * kBRow + kBPad;
+    constexpr int kALoads = VA == 4 ? F : 4 * F;     // A loads per wave per slice
+    constexpr int kBRowsPerLoad = 1024 / kBRow;      // k rows of B per wave instruction
+    constexpr int kLoads = kALoads + F;
     __shared__ __attribute__((aligned(256))) char st0[kStage], st1[kStage], st2[kStage], st3[kStage], st4[kStage],
         st5[kStage];
     auto stage_base = [&](int st) -> char * {
@@ -579,32 +581,40 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const float *B = static_cast<const float *>(p.B);
     const int a_rows = min(BM, M - m0);
 
-    // A load j of this wave.  VA = 4: rows 16*wave .. +15 (lane -> row
-    // 16*wave + lane/4, physical chunk lane%4), landing at stage + 1024*wave.
-    // VA = 1: wave instruction i = 4*wave + j covers rows 4i .. 4i+3 (lane ->
-    // row 4i + lane/16, physical float lane%16), landing at stage + 256 i.
-    // (Sized 4, not kALoads: hipcc's host pass rejects the LDS-load builtin
+    // A load j of this wave: instruction i = kALoads*wave + j.  VA = 4: rows
+    // 16i .. +15 (lane -> row 16i + lane/4, physical chunk lane%4), landing
+    // at stage + 1024 i.  VA = 1: rows 4i .. 4i+3 (lane -> row 4i + lane/16,
+    // physical float lane%16), landing at stage + 256 i.
+    // (Sized 8, not kALoads: hipcc's host pass rejects the LDS-load builtin
     // when its offset comes from an array whose size depends on VA.)
-    uint32_t a_goff[4];
-    int a_k[4];
+    uint32_t a_goff[8];
+    int a_k[8];
 #pragma unroll
     for (int j = 0; j < kALoads; ++j) {
+        const int i = kALoads * wave + j;
         int row, k;
         if (VA == 4) {
-            row = 16 * wave + (lane >> 2);
+            row = 16 * i + (lane >> 2);
             k = 4 * ((lane & 3) ^ ((row >> 2) & 3));
         } else {
-            row = 4 * (4 * wave + j) + (lane >> 4);
+            row = 4 * i + (lane >> 4);
             const int pf = lane & 15;
             k = 4 * ((pf >> 2) ^ ((row >> 2) & 3)) + (pf & 3);
         }
         a_k[j] = k;
         a_goff[j] = panel_off(row, a_rows, lda, k, 4);
     }
-    // B: k rows 4*wave .. +3 (lane -> k row 4*wave + lane/16, columns
-    // 4*(lane%16) .. +3).
-    const uint32_t b_goff = (uint32_t)((4 * wave + (lane >> 4)) * ldb + 4 * (lane & 15)) * 4u;
-    const uint32_t b_dst = (uint32_t)(kA + 1024 * wave + (wave >= 2 ? kBPad : 0));
+    // B load j: instruction i = F*wave + j covers k rows kBRowsPerLoad*i ..
+    // (lane -> k row kBRowsPerLoad*i + lane/(BN/4), columns 4*(lane%(BN/4)) ..
+    // +3), landing at stage + kA + 1024 i (+ 128 from k row 8 on).
+    uint32_t b_goff[2], b_dst[2];
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+        const int i = F * wave + j;
+        const int krow = kBRowsPerLoad * i + lane / (BN / 4);
+        b_goff[j] = (uint32_t)(krow * ldb + 4 * (lane % (BN / 4))) * 4u;
+        b_dst[j] = (uint32_t)(kA + 1024 * i + (kBRowsPerLoad * i >= 8 ? kBPad : 0));
+    }
 
     // Slice kt's loads into stage si, through resources rebased at the
     // slice: rows past M read row M - 1, k past K gets 2^31 added to the
@@ -619,22 +629,33 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
         for (int j = 0; j < kALoads; ++j) {
             const uint32_t poison = (uint32_t)(a_k[j] >= K - k0) << 31;
+            const int i = kALoads * wave + j;
             if constexpr (VA == 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 1024 * wave), 16, a_goff[j] + poison, 0,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 1024 * i), 16, a_goff[j] + poison, 0,
                                                          0, 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 256 * (4 * wave + j)), 4,
-                                                         a_goff[j] + poison, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 256 * i), 4, a_goff[j] + poison, 0,
+                                                         0, 0);
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(base + b_dst), 16, b_goff, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(base + b_dst[j]), 16, b_goff[j], 0, 0, 0);
     };
 
     const int h = lane >> 5, l32 = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
-    const uint32_t fa_off0 = (uint32_t)((wm * 32 + l32) * 64 + 16 * ((2 * h) ^ ((l32 >> 2) & 3)));
-    const uint32_t fa_off1 = (uint32_t)((wm * 32 + l32) * 64 + 16 * ((2 * h + 1) ^ ((l32 >> 2) & 3)));
-    const uint32_t fb_off = (uint32_t)(kA + 8 * h * 256 + (h ? kBPad : 0) + (wn * 32 + l32) * 4);
-    f32x16 acc = f32x16{};
+    uint32_t fa_off[F][2];
+#pragma unroll
+    for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            fa_off[fm][q] = (uint32_t)((wm * 32 * F + 32 * fm + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
+    const uint32_t fb_off = (uint32_t)(kA + 8 * h * kBRow + (h ? kBPad : 0) + (wn * 32 * F + l32) * 4);
+    f32x16 acc[F][F];
+#pragma unroll
+    for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < F; ++fn) acc[fm][fn] = f32x16{};
 
     // Slice kt: wait until it has landed (the loads of the NS - 2 slices after
     // it may still be in flight) and every wave has read the previous stage;
@@ -644,14 +665,25 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
         __builtin_amdgcn_s_barrier();
         issue(kt + NS - 1, (u + NS - 1) % NS);
         const char *base = stage_base(u);
-        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(base + fa_off0);
-        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(base + fa_off1);
-        float bv[8];
+        f32x4 a[F][2];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) bv[s] = *reinterpret_cast<const float *>(base + fb_off + 256 * s);
+        for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) a[fm][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[fm][q]);
+        float bv[8][F];
 #pragma unroll
         for (int s = 0; s < 8; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(s < 4 ? a0[s] : a1[s - 4], bv[s], acc, 0, 0, 0);
+#pragma unroll
+            for (int fn = 0; fn < F; ++fn)
+                bv[s][fn] = *reinterpret_cast<const float *>(base + fb_off + kBRow * s + 128 * fn);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int fm = 0; fm < F; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < F; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][s >> 2][s & 3], bv[s][fn], acc[fm][fn],
+                                                                        0, 0, 0);
     };
 
     const int nk = (K + BK - 1) / BK;
@@ -670,27 +702,33 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
     // No load may still be writing LDS when the workgroup ends.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
-    // Register r of lane (h, l32) is row 8*(r/4) + 4h + r%4, column l32 of
-    // the wave's fragment.
-    const int col = n0 + wn * 32 + l32;
-    if (col >= N) return;
+    // Register r of lane (h, l32) in fragment (fm, fn) is row 8*(r/4) + 4h +
+    // r%4, column l32 of that fragment.
     const float alpha = p.alpha, beta = p.beta;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row >= M) continue;
-        float v = alpha * acc[r];
-        if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)row * p.ldc + col], v);
-        store_out_any(p, row, col, epilogue_value(v, col, p.bias, p.act));
+    for (int fn = 0; fn < F; ++fn) {
+        const int col = n0 + wn * 32 * F + 32 * fn + l32;
+        if (col >= N) continue;
+#pragma unroll
+        for (int fm = 0; fm < F; ++fm) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 32 * F + 32 * fm + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row >= M) continue;
+                float v = alpha * acc[fm][fn][r];
+                if (beta != 0.0f) v = fmaf(beta, p.C[(int64_t)row * p.ldc + col], v);
+                store_out_any(p, row, col, epilogue_value(v, col, p.bias, p.act));
+            }
+        }
     }
 }
 
-template <int VA, int NS>
+template <int VA, int NS, int F>
 hipError_t launch_f32_ring64(const GemmParams &p, hipStream_t stream) {
-    int tiles_m = (p.M + 63) / 64, tiles_n = (p.N + 63) / 64;
+    int tiles_m = (p.M + 64 * F - 1) / (64 * F), tiles_n = (p.N + 64 * F - 1) / (64 * F);
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring64_kernel<VA, NS>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring64_kernel<VA, NS, F>),
                            dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
@@ -719,8 +757,10 @@ F32_RING_INSTANCES(false, false)
 F32_RING_INSTANCES(true, false)
 F32_RING_INSTANCES(false, true)
 F32_RING_INSTANCES(true, true)
-template __global__ void f32_ring64_kernel<4, 6>(GemmParams, int, int);
-template __global__ void f32_ring64_kernel<1, 6>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 6, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<1, 6, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 4, 2>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<1, 4, 2>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 1, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 1, 4, 4>(GemmParams, int, int);
@@ -756,6 +796,12 @@ const KernelDesc kF32TiledKernels[] = {
     F32_TILED(256, 256, 16, 2, 2, 4, 1, 4),
     F32_TILED(256, 256, 16, 2, 2, 1, 4, 4),
     F32_TILED(256, 256, 16, 2, 2, 1, 1, 4),
+    // 128 x 128 with B rows of whole 16-byte chunks: the ring, then the
+    // register-staged kernels.
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 128, 128, 16, 256, 4, 4, "f32_mfma32_128x128x16_w2x2_a4b4_ring4",
+     &launch_f32_ring64<4, 4, 2>, 0, nullptr, kLayoutNN, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 128, 128, 16, 256, 1, 4, "f32_mfma32_128x128x16_w2x2_a1b4_ring4",
+     &launch_f32_ring64<1, 4, 2>, 0, nullptr, kLayoutNN, false, kOutAll},
     F32_TILED(128, 128, 16, 2, 2, 4, 4, 8),
     F32_TILED(128, 128, 16, 2, 2, 4, 1, 8),
     F32_TILED(128, 128, 16, 2, 2, 1, 4, 8),
@@ -763,9 +809,9 @@ const KernelDesc kF32TiledKernels[] = {
     // 64 x 64 with B rows of whole 16-byte chunks: the ring (A loaded 16 or 4
     // bytes per lane), then the register-staged kernels.
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, 64, 64, 16, 256, 4, 4, "f32_mfma32_64x64x16_w2x2_a4b4_ring6",
-     &launch_f32_ring64<4, 6>, 0, nullptr, kLayoutNN, false, kOutAll},
+     &launch_f32_ring64<4, 6, 1>, 0, nullptr, kLayoutNN, false, kOutAll},
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, 64, 64, 16, 256, 1, 4, "f32_mfma32_64x64x16_w2x2_a1b4_ring6",
-     &launch_f32_ring64<1, 6>, 0, nullptr, kLayoutNN, false, kOutAll},
+     &launch_f32_ring64<1, 6, 1>, 0, nullptr, kLayoutNN, false, kOutAll},
     F32_TILED(64, 64, 16, 2, 2, 4, 4, 8),
     F32_TILED(64, 64, 16, 2, 2, 4, 1, 8),
     F32_TILED(64, 64, 16, 2, 2, 1, 4, 8),
