@@ -51,7 +51,8 @@ STEP = ["bf16f32_8192", "f32_4096", "f32_16x8192x8192"]
 # layouts and shapes.
 EXTRA = ["fp8f32_8192_nt", "bf16f32_8192_nt", "bf16f32_8192_tn", "bf16f32_16x8192x8192", "bf16f32_16x8192x8192_nt",
          "f32_16x8192x8192_nt", "fp8f32_16x8192x8192_nt", "f32_4096_nt", "f32_4096_tn",
-         "fp8f32_8192_nn", "fp8f32_8192_tn", "bf16f32_2048x4096x4096", "bf16f32_2048x4096x4096_nt"]
+         "fp8f32_8192_nn", "fp8f32_8192_tn", "bf16f32_2048x4096x4096", "bf16f32_2048x4096x4096_nt",
+         "f32_2048x4096x4096"]
 # The other configurations of the workload set, timed call by call after the
 # step (they do not enter ``value``): (workload, whether a workspace is passed).
 # The M = 16 shape is timed here through the plain call as well, which has no

@@ -247,8 +247,8 @@ def test_bf16_mid_size_choice():
     """bf16 (and fp8) problems with 256 to 1023 tiles of 128^2 take a 128 x
     128 whole-line kernel; with a workspace it is still preferred, unsplit,
     over 256^2 tiles split over K (the split's workspace round trip costs
-    more than the smaller tile gives up).  fp32 keeps the split 256^2 ring
-    there."""
+    more than the smaller tile gives up), and fp32 takes its 128^2 ring the
+    same way."""
     L128 = "bf16_mfma32_128x128x64_w2x2_a8b8_lines"
     for M, N, K in [(2048, 2048, 2048), (2048, 4096, 4096), (2048, 2048, 8192), (1536, 1536, 4096)]:
         for ws in (0, 1 << 34):
@@ -259,8 +259,9 @@ def test_bf16_mid_size_choice():
     # Too few 128^2 tiles to fill the compute units: the split 256^2 tiles.
     st, p = plan(BF16, 1024, 1024, 16384, ws=1 << 34)
     assert p["tile_m"] == 256 and p["splits"] == 16, p
+    # fp32 likewise, on the 128^2 ring.
     st, p = plan(F32, 2048, 4096, 4096, ws=1 << 34)
-    assert p["tile_m"] == 256 and p["splits"] == 2, p
+    assert kname(p) == "f32_mfma32_128x128x16_w2x2_a4b4_ring4" and p["splits"] == 1, p
     # B stored N x K (a linear layer's weights) and A stored K x M (its
     # weight gradient): the same choice in those layouts.
     for M, N, K in [(2048, 2048, 2048), (2048, 4096, 4096)]:

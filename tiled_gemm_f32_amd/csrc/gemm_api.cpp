@@ -383,14 +383,15 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand) {
             const KSplit ks = call_ksplit(c, kd);
             const int64_t groups = (pm / tile) * (pn / tile) * ks.splits;
             const bool fills = ks.splits > 1 ? 4 * groups >= 3 * kComputeUnits : groups >= kComputeUnits;
-            // bf16 and fp8: a split sends every partial product through the
-            // workspace and back (2048 x 4096 x 4096 in two: 160 MB), which
-            // costs more than the smaller tile gives up, so a smaller tile
-            // that fills the compute units unsplit goes first (there: 68 us
-            // for 128^2 tiles against 87 us for 256^2 tiles in two slices in
-            // bf16, 41 against 63 us in fp8).  The fp32 kernels' matrix work
-            // is 8x longer and the split wins.
-            if (ks.splits > 1 && c.dtype != GEMM_DTYPE_F32 && tile > 64 &&
+            // A split sends every partial product through the workspace and
+            // back (2048 x 4096 x 4096 in two: 160 MB), which costs more than
+            // 128^2 tiles give up against 256^2 ones, so 128^2 tiles that
+            // fill the compute units unsplit go first (there: 68 us against
+            // 87 us for 256^2 tiles in two slices in bf16, 41 against 63 us
+            // in fp8, 496 against 507-549 us in fp32).  64^2 tiles lose more
+            // than that to 128^2 ones, so a split 128^2 tile stays, and so
+            // does a last-wave split, whose partials cover one tile row.
+            if (ks.splits > 1 && ks.m_top == 0 && tile == 256 &&
                 ceil_div(c.M, tile / 2) * ceil_div(c.N, tile / 2) >= kComputeUnits &&
                 first_candidate(cand, c, tile / 2) != nullptr)
                 continue;

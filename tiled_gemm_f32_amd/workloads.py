@@ -83,6 +83,7 @@ WORKLOADS = {
         # Mid-size: 512 tiles of 128^2 (two workgroups per compute unit), 128 of 256^2.
         Workload("bf16f32_2048x4096x4096", "bf16f32", 2048, 4096, 4096, 1.0, 0.0, "normal", 16),
         Workload("bf16f32_2048x4096x4096_nt", "bf16f32", 2048, 4096, 4096, 1.0, 0.0, "normal", 17, "T"),
+        Workload("f32_2048x4096x4096", "f32", 2048, 4096, 4096, 1.0, 0.0, "normal", 18),
     ]
 }
 
