@@ -316,3 +316,37 @@ def test_f32_ring_small_tiles_match_register_staged(gpu_available, va, tile):
             C, _, _ = run_gemm(Ai, Bi, Ci, alpha, beta, kernel=ring)
             np.testing.assert_array_equal(C.astype(np.float64), _exact(Ai, Bi, Ci, alpha, beta),
                                           err_msg=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("tile", [64, 128])
+@pytest.mark.parametrize("layout", ["nt", "tn", "tt"])
+def test_f32_ring_small_tiles_transposed_layouts(gpu_available, layout, tile):
+    """The 64 x 64 and 128 x 128 fp32 rings with A stored K x M and/or B stored
+    N x K: on random data the same bits as the register-staged untransposed
+    kernel of the tile on the untransposed operands (same operand order and
+    k order per lane), on integer data the oracle's bits.  N is free when B
+    is stored N x K (ragged N below)."""
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    ns = 6 if tile == 64 else 4
+    ring = ids[f"f32_mfma32_{tile}x{tile}x16_w2x2_a4b4_{layout}_ring{ns}"]
+    staged = ids[f"f32_mfma32_{tile}x{tile}x16_w2x2_a4b4"]
+    op_a, op_b = layout[0].upper(), layout[1].upper()
+    for M, N, K, n_free in [(1024, 1024, 1024, 0), (260, 264, 68, 3), (64, 68, 4, 0), (300, 520, 1032, 1),
+                            (132, 8, 16, 1)]:
+        if op_b == "T":
+            N += n_free                                 # B stored N x K leaves N free
+        A, B, C0 = make_random_inputs(M, N, K, seed=M + 5 * N + K, dist="uniform")
+        As = A.t().contiguous() if op_a == "T" else A
+        Bs = B.t().contiguous() if op_b == "T" else B
+        say(f"[f32 ring {tile} {layout}] random M={M} N={N} K={K}")
+        C1, _, _ = run_gemm(As, Bs, C0, 2.0, -1.0, kernel=ring, op_a=op_a, op_b=op_b)
+        if N % 4 == 0:
+            C2, _, _ = run_gemm(A, B, C0, 2.0, -1.0, kernel=staged)
+            np.testing.assert_array_equal(C1, C2, err_msg=f"{M}x{N}x{K}")
+        assert ratio(C1, A, B, C0, 2.0, -1.0) <= TOL["f32"]
+        Ai, Bi, Ci = make_integer_inputs(M, N, K, seed=M * 3 + K)
+        Ais = Ai.t().contiguous() if op_a == "T" else Ai
+        Bis = Bi.t().contiguous() if op_b == "T" else Bi
+        say(f"[f32 ring {tile} {layout}] exact M={M} N={N} K={K}")
+        C, _, _ = run_gemm(Ais, Bis, Ci, 2.0, -1.0, kernel=ring, op_a=op_a, op_b=op_b)
+        np.testing.assert_array_equal(C.astype(np.float64), _exact(Ai, Bi, Ci, 2.0, -1.0), err_msg=f"{M}x{N}x{K}")

@@ -547,24 +547,36 @@ hipError_t launch_f32_ring(const GemmParams &p, hipStream_t stream) {
 //   B slice: [16 k rows][BN columns] as in HBM, k rows 8 .. 15 starting 128
 //     bytes later so that the two lane halves' reads (k rows s and 8 + s)
 //     fall in different banks.
-// Lane (h, l32) holds row l32 of each of its A fragments at k = 8h .. 8h+7
-// of the slice and reads column l32 of each B fragment at k row 8h + s for
-// step s, so every accumulator sums k in the order of the kernel above.
-template <int VA, int NS, int F>
+// BT (B stored N x K): B's slice takes A's layout and 16-byte loads, and its
+// fragments are read as A's are; N is free.  AT (A stored K x M): A's slice
+// takes B's layout and loads, and its values are read per step as B's are.
+// Lane (h, l32) holds row l32 of each A fragment and column l32 of each B
+// fragment at k = 8h + s for step s, so every accumulator sums k in the
+// order of the kernel above, whatever the layout.
+// A stage holds SUB 16-deep sub-slices, so one barrier serves 8*F*F*SUB
+// matrix instructions.  Two (three stages of 16 KB for 64 x 64 tiles) were
+// no faster than one; the table uses one, but the code shape with the
+// per-sub-slice loop measured 4-12% faster on 64 x 64 tiles than the same
+// kernel written without it (the compiler then starts the matrix
+// instructions before the last fragment reads return).
+template <int VA, int NS, int F, bool BT, bool AT, int SUB>
 __global__ void __launch_bounds__(256)
 f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
     apply_k_split<float>(p);
     static_assert(VA == 1 || VA == 4, "A loads of 4 or 16 bytes");
+    static_assert(VA == 4 || !AT, "A stored K x M is loaded 16 bytes per lane");
     static_assert(NS >= 3 && NS <= 6, "six stage arrays");
     static_assert(F == 1 || F == 2, "64 x 64 or 128 x 128 tiles");
+    static_assert(SUB == 1 || SUB == 2, "one or two 16-deep sub-slices per stage");
     constexpr int BM = 64 * F, BN = 64 * F, BK = 16;
-    constexpr int kA = BM * BK * 4;
-    constexpr int kBRow = BN * 4;                // bytes per k row of B
-    constexpr int kBPad = 128;
-    constexpr int kStage = kA + BK * kBRow + kBPad;
-    constexpr int kALoads = VA == 4 ? F : 4 * F;     // A loads per wave per slice
-    constexpr int kBRowsPerLoad = 1024 / kBRow;      // k rows of B per wave instruction
-    constexpr int kLoads = kALoads + F;
+    constexpr int kPad = 128;                    // k rows 8 .. 15 of a k-row slice start this much later
+    constexpr int kRow = BN * 4;                 // bytes per k row of a k-row slice (BM == BN)
+    constexpr int kKRowsPerLoad = 1024 / kRow;   // k rows per wave instruction of a k-row slice
+    constexpr int kA = AT ? BK * kRow + kPad : BM * BK * 4;
+    constexpr int kSub = kA + (BT ? BN * BK * 4 : BK * kRow + kPad);     // one 16-deep sub-slice
+    constexpr int kStage = SUB * kSub;
+    constexpr int kALoads = (VA == 4 || AT) ? F : 4 * F;     // A loads per wave per sub-slice
+    constexpr int kLoads = SUB * (kALoads + F);
     __shared__ __attribute__((aligned(256))) char st0[kStage], st1[kStage], st2[kStage], st3[kStage], st4[kStage],
         st5[kStage];
     auto stage_base = [&](int st) -> char * {
@@ -579,78 +591,113 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
     const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const float *A = static_cast<const float *>(p.A);
     const float *B = static_cast<const float *>(p.B);
-    const int a_rows = min(BM, M - m0);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
 
-    // A load j of this wave: instruction i = kALoads*wave + j.  VA = 4: rows
-    // 16i .. +15 (lane -> row 16i + lane/4, physical chunk lane%4), landing
-    // at stage + 1024 i.  VA = 1: rows 4i .. 4i+3 (lane -> row 4i + lane/16,
-    // physical float lane%16), landing at stage + 256 i.
-    // (Sized 8, not kALoads: hipcc's host pass rejects the LDS-load builtin
-    // when its offset comes from an array whose size depends on VA.)
-    uint32_t a_goff[8];
-    int a_k[8];
-#pragma unroll
-    for (int j = 0; j < kALoads; ++j) {
-        const int i = kALoads * wave + j;
-        int row, k;
-        if (VA == 4) {
-            row = 16 * i + (lane >> 2);
-            k = 4 * ((lane & 3) ^ ((row >> 2) & 3));
-        } else {
+    // Loads of a k-contiguous slice (A, or B with BT): 16-byte instruction i
+    // covers rows 16i .. +15 (lane -> row 16i + lane/4, physical chunk
+    // lane%4) and lands at 1024 i; 4-byte instruction i covers rows 4i ..
+    // 4i+3 (lane -> row 4i + lane/16, physical float lane%16) and lands at
+    // 256 i.  Loads of a k-row slice (B, or A with AT): instruction i covers
+    // k rows kKRowsPerLoad*i .. (lane -> k row kKRowsPerLoad*i + lane/(BN/4),
+    // columns 4*(lane%(BN/4)) .. +3) and lands at 1024 i (+ kPad from k row
+    // 8 on).  Load j of this wave is instruction kALoads*wave + j of A, F*wave
+    // + j of B.
+    // (Sized 8: hipcc's host pass rejects the LDS-load builtin when its offset
+    // comes from an array whose size depends on a template parameter.)
+    uint32_t a_goff[8], b_goff[2];
+    int a_k[8], b_k[2];
+    auto k_contig = [&](int i, int rows, int ld, bool narrow, uint32_t &goff, int &k) {
+        int row;
+        if (narrow) {
             row = 4 * i + (lane >> 4);
             const int pf = lane & 15;
             k = 4 * ((pf >> 2) ^ ((row >> 2) & 3)) + (pf & 3);
+        } else {
+            row = 16 * i + (lane >> 2);
+            k = 4 * ((lane & 3) ^ ((row >> 2) & 3));
         }
-        a_k[j] = k;
-        a_goff[j] = panel_off(row, a_rows, lda, k, 4);
+        goff = panel_off(row, rows, ld, k, 4);
+    };
+    auto k_rows = [&](int i, int ld, uint32_t &goff) {
+        const int krow = kKRowsPerLoad * i + lane / (BN / 4);
+        goff = (uint32_t)(krow * ld + 4 * (lane % (BN / 4))) * 4u;
+    };
+    // LDS destinations of the loads (uniform across the wave).
+    auto a_dst = [&](int j) {
+        const int i = kALoads * wave + j;
+        return AT ? 1024 * i + (kKRowsPerLoad * i >= 8 ? kPad : 0) : (VA == 4 ? 1024 * i : 256 * i);
+    };
+    auto b_dst = [&](int j) {
+        const int i = F * wave + j;
+        return kA + (BT ? 1024 * i : 1024 * i + (kKRowsPerLoad * i >= 8 ? kPad : 0));
+    };
+#pragma unroll
+    for (int j = 0; j < kALoads; ++j) {
+        a_k[j] = 0;
+        if (AT)
+            k_rows(kALoads * wave + j, lda, a_goff[j]);
+        else
+            k_contig(kALoads * wave + j, a_rows, lda, VA == 1, a_goff[j], a_k[j]);
     }
-    // B load j: instruction i = F*wave + j covers k rows kBRowsPerLoad*i ..
-    // (lane -> k row kBRowsPerLoad*i + lane/(BN/4), columns 4*(lane%(BN/4)) ..
-    // +3), landing at stage + kA + 1024 i (+ 128 from k row 8 on).
-    uint32_t b_goff[2], b_dst[2];
 #pragma unroll
     for (int j = 0; j < F; ++j) {
-        const int i = F * wave + j;
-        const int krow = kBRowsPerLoad * i + lane / (BN / 4);
-        b_goff[j] = (uint32_t)(krow * ldb + 4 * (lane % (BN / 4))) * 4u;
-        b_dst[j] = (uint32_t)(kA + 1024 * i + (kBRowsPerLoad * i >= 8 ? kBPad : 0));
+        b_k[j] = 0;
+        if (BT)
+            k_contig(F * wave + j, b_rows, ldb, false, b_goff[j], b_k[j]);
+        else
+            k_rows(F * wave + j, ldb, b_goff[j]);
     }
 
     // Slice kt's loads into stage si, through resources rebased at the
-    // slice: rows past M read row M - 1, k past K gets 2^31 added to the
-    // offset (A) or falls outside the extent (B).
-    auto issue = [&](int kt, int si) {
-        const int k0 = BK * kt;
+    // slice: rows past M (N) read the last valid one, k past K gets 2^31
+    // added to the offset (k-contiguous slices) or falls outside the extent
+    // (k-row slices).
+    auto issue_sub = [&](int ks, char *base) {
+        const int k0 = BK * ks;
         const rsrc_t ra =
-            make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 4));
+            AT ? make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent(((int64_t)(K - k0 - 1) * lda + (M - m0)) * 4))
+               : make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent(((int64_t)(a_rows - 1) * lda + (K - k0)) * 4));
         const rsrc_t rb =
-            make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
-        char *base = stage_base(si);
+            BT ? make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent(((int64_t)(b_rows - 1) * ldb + (K - k0)) * 4))
+               : make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent(((int64_t)(K - k0 - 1) * ldb + (N - n0)) * 4));
 #pragma unroll
         for (int j = 0; j < kALoads; ++j) {
-            const uint32_t poison = (uint32_t)(a_k[j] >= K - k0) << 31;
-            const int i = kALoads * wave + j;
+            const uint32_t poison = AT ? 0u : (uint32_t)(a_k[j] >= K - k0) << 31;
             if constexpr (VA == 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 1024 * i), 16, a_goff[j] + poison, 0,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + a_dst(j)), 16, a_goff[j] + poison, 0,
                                                          0, 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + 256 * i), 4, a_goff[j] + poison, 0,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(base + a_dst(j)), 4, a_goff[j] + poison, 0,
                                                          0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < F; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(base + b_dst[j]), 16, b_goff[j], 0, 0, 0);
+        for (int j = 0; j < F; ++j) {
+            const uint32_t poison = BT ? (uint32_t)(b_k[j] >= K - k0) << 31 : 0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(base + b_dst(j)), 16, b_goff[j] + poison, 0, 0,
+                                                     0);
+        }
+    };
+    auto issue = [&](int kt, int si) {
+#pragma unroll
+        for (int t = 0; t < SUB; ++t) issue_sub(SUB * kt + t, stage_base(si) + kSub * t);
     };
 
+    // Fragment reads: a k-contiguous fragment f of the wave's block is two
+    // 16-byte reads (k = 8h .. 8h+7 of row l32); a k-row fragment gives one
+    // float per step (k row 8h + s, column l32).
     const int h = lane >> 5, l32 = lane & 31;
     const int wm = wave >> 1, wn = wave & 1;
-    uint32_t fa_off[F][2];
+    uint32_t fa_off[F][2], fbt_off[F][2];
 #pragma unroll
-    for (int fm = 0; fm < F; ++fm)
+    for (int f = 0; f < F; ++f)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-            fa_off[fm][q] = (uint32_t)((wm * 32 * F + 32 * fm + l32) * 64 + 16 * ((2 * h + q) ^ ((l32 >> 2) & 3)));
-    const uint32_t fb_off = (uint32_t)(kA + 8 * h * kBRow + (h ? kBPad : 0) + (wn * 32 * F + l32) * 4);
+        for (int q = 0; q < 2; ++q) {
+            const int chunk = 16 * ((2 * h + q) ^ ((l32 >> 2) & 3));
+            fa_off[f][q] = (uint32_t)((wm * 32 * F + 32 * f + l32) * 64 + chunk);
+            fbt_off[f][q] = (uint32_t)(kA + (wn * 32 * F + 32 * f + l32) * 64 + chunk);
+        }
+    const uint32_t arow_off = (uint32_t)(8 * h * kRow + (h ? kPad : 0) + (wm * 32 * F + l32) * 4);
+    const uint32_t brow_off = (uint32_t)(kA + 8 * h * kRow + (h ? kPad : 0) + (wn * 32 * F + l32) * 4);
     f32x16 acc[F][F];
 #pragma unroll
     for (int fm = 0; fm < F; ++fm)
@@ -664,29 +711,39 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kLoads * (NS - 2)));
         __builtin_amdgcn_s_barrier();
         issue(kt + NS - 1, (u + NS - 1) % NS);
-        const char *base = stage_base(u);
-        f32x4 a[F][2];
 #pragma unroll
-        for (int fm = 0; fm < F; ++fm)
+        for (int t = 0; t < SUB; ++t) {
+        const char *base = stage_base(u) + kSub * t;
+        f32x4 a[F][2], b[F][2];
+        float av[8][F], bv[8][F];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) a[fm][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[fm][q]);
-        float bv[8][F];
+        for (int f = 0; f < F; ++f)
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
+            for (int q = 0; q < 2; ++q) {
+                if (!AT) a[f][q] = *reinterpret_cast<const f32x4 *>(base + fa_off[f][q]);
+                if (BT) b[f][q] = *reinterpret_cast<const f32x4 *>(base + fbt_off[f][q]);
+            }
 #pragma unroll
-            for (int fn = 0; fn < F; ++fn)
-                bv[s][fn] = *reinterpret_cast<const float *>(base + fb_off + kBRow * s + 128 * fn);
+        for (int st = 0; st < 8; ++st)
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
+            for (int f = 0; f < F; ++f) {
+                if (AT) av[st][f] = *reinterpret_cast<const float *>(base + arow_off + kRow * st + 128 * f);
+                if (!BT) bv[st][f] = *reinterpret_cast<const float *>(base + brow_off + kRow * st + 128 * f);
+            }
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
 #pragma unroll
             for (int fm = 0; fm < F; ++fm)
 #pragma unroll
-                for (int fn = 0; fn < F; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][s >> 2][s & 3], bv[s][fn], acc[fm][fn],
-                                                                        0, 0, 0);
+                for (int fn = 0; fn < F; ++fn) {
+                    const float x = AT ? av[st][fm] : a[fm][st >> 2][st & 3];
+                    const float y = BT ? b[fn][st >> 2][st & 3] : bv[st][fn];
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, acc[fm][fn], 0, 0, 0);
+                }
+        }
     };
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (K + BK * SUB - 1) / (BK * SUB);
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue(st, st);
     const int nfull = nk / NS;
@@ -723,12 +780,12 @@ f32_ring64_kernel(GemmParams p, int tiles_m, int tiles_n) {
     }
 }
 
-template <int VA, int NS, int F>
+template <int VA, int NS, int F, bool BT = false, bool AT = false, int SUB = 1>
 hipError_t launch_f32_ring64(const GemmParams &p, hipStream_t stream) {
     int tiles_m = (p.M + 64 * F - 1) / (64 * F), tiles_n = (p.N + 64 * F - 1) / (64 * F);
     GemmParams args = p;
     void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring64_kernel<VA, NS, F>),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&f32_ring64_kernel<VA, NS, F, BT, AT, SUB>),
                            dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0, stream);
 }
 
@@ -757,10 +814,16 @@ F32_RING_INSTANCES(false, false)
 F32_RING_INSTANCES(true, false)
 F32_RING_INSTANCES(false, true)
 F32_RING_INSTANCES(true, true)
-template __global__ void f32_ring64_kernel<4, 6, 1>(GemmParams, int, int);
-template __global__ void f32_ring64_kernel<1, 6, 1>(GemmParams, int, int);
-template __global__ void f32_ring64_kernel<4, 4, 2>(GemmParams, int, int);
-template __global__ void f32_ring64_kernel<1, 4, 2>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 6, 1, false, false, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<1, 6, 1, false, false, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 6, 1, true, false, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 6, 1, false, true, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 6, 1, true, true, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 4, 2, false, false, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<1, 4, 2, false, false, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 4, 2, true, false, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 4, 2, false, true, 1>(GemmParams, int, int);
+template __global__ void f32_ring64_kernel<4, 4, 2, true, true, 1>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 4, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 4, 1, 4>(GemmParams, int, int);
 template __global__ void f32_tiled_kernel<256, 256, 16, 2, 2, 1, 4, 4>(GemmParams, int, int);
@@ -806,6 +869,20 @@ const KernelDesc kF32TiledKernels[] = {
     F32_TILED(128, 128, 16, 2, 2, 4, 1, 8),
     F32_TILED(128, 128, 16, 2, 2, 1, 4, 8),
     F32_TILED(128, 128, 16, 2, 2, 1, 1, 8),
+    // 128 x 128 and 64 x 64 rings with A or B stored transposed (the only
+    // kernels of those tile sizes for those layouts).
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 128, 128, 16, 256, 4, 4, "f32_mfma32_128x128x16_w2x2_a4b4_nt_ring4",
+     &launch_f32_ring64<4, 4, 2, true, false>, 0, nullptr, kLayoutNT, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 128, 128, 16, 256, 4, 4, "f32_mfma32_128x128x16_w2x2_a4b4_tn_ring4",
+     &launch_f32_ring64<4, 4, 2, false, true>, 0, nullptr, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 128, 128, 16, 256, 4, 4, "f32_mfma32_128x128x16_w2x2_a4b4_tt_ring4",
+     &launch_f32_ring64<4, 4, 2, true, true>, 0, nullptr, kLayoutTT, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 64, 64, 16, 256, 4, 4, "f32_mfma32_64x64x16_w2x2_a4b4_nt_ring6",
+     &launch_f32_ring64<4, 6, 1, true, false>, 0, nullptr, kLayoutNT, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 64, 64, 16, 256, 4, 4, "f32_mfma32_64x64x16_w2x2_a4b4_tn_ring6",
+     &launch_f32_ring64<4, 6, 1, false, true>, 0, nullptr, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_TILED, 64, 64, 16, 256, 4, 4, "f32_mfma32_64x64x16_w2x2_a4b4_tt_ring6",
+     &launch_f32_ring64<4, 6, 1, true, true>, 0, nullptr, kLayoutTT, false, kOutAll},
     // 64 x 64 with B rows of whole 16-byte chunks: the ring (A loaded 16 or 4
     // bytes per lane), then the register-staged kernels.
     {GEMM_DTYPE_F32, GEMM_PATH_TILED, 64, 64, 16, 256, 4, 4, "f32_mfma32_64x64x16_w2x2_a4b4_ring6",
