@@ -644,12 +644,13 @@ BF16_AT_SKINNY = ["bf16_skinny_lds_n128_at_w4_s4", "bf16_skinny_lds_n128_at_w4_s
 
 
 @pytest.mark.parametrize("M", [8, 16])
-@pytest.mark.parametrize("NK", [(8192, 4096), (1000, 3008)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("NK", [(8192, 4096), (1000, 3008), (1000, 777)], ids=lambda s: f"{s[0]}x{s[1]}")
 def test_bf16_skinny_a_transposed_exact(gpu_available, M, NK):
     """bf16, M of 8 or 16, A stored K x M with its rows padded to 16 elements
     by NaN (which must never reach C): both streaming kernels forced, and the
     library's choice with and without a workspace, bit-exact on integer data
-    with bias and ReLU."""
+    with bias and ReLU.  K = 777 ends in a partial 32-row block of A, whose
+    rows past K must read as zero."""
     N, K = NK
     A, B, C0 = make_integer_inputs(M, N, K, seed=780 + M, dtype="bf16f32")
     As = A.t().contiguous()
