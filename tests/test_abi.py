@@ -800,6 +800,8 @@ def test_output_types_of_the_kernels():
                  "bf16_mfma32_256x256x32_w2x2_a8b8_nt_ring4", "bf16_mfma32_256x256x32_w2x2_a8b8_tn_ring4",
                  "bf16_mfma32_256x256x32_w2x2_a8b8_tt_ring4", "fp8_mfma32_256x256x64_w2x2_nt_ring4",
                  "fp8_mfma32_256x256x128_w2x2_nt_lines", "fp8_mfma32_128x128x128_w2x2_nt_lines",
+                 "fp8_mfma32_128x128x64_w2x2_nn_ring4", "fp8_mfma32_128x128x64_w2x2_tn_ring4",
+                 "fp8_mfma32_128x128x64_w2x2_tt_ring4",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
                  "fp8_skinny_nt_splitk_n32_w8_u2"):

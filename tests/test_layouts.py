@@ -429,6 +429,41 @@ def test_fp8_lines128_kernel(gpu_available, shape):
     check(C1, As, Bs, C0, 0.5, 0.25, "N", "T", "fp8f32")
 
 
+FP8_RING128 = {("N", "N"): ("fp8_mfma32_128x128x64_w2x2_nn_ring4", FP8_NN_RING),
+               ("T", "N"): ("fp8_mfma32_128x128x64_w2x2_tn_ring4", FP8_TN_RING),
+               ("T", "T"): ("fp8_mfma32_128x128x64_w2x2_tt_ring4", FP8_TT_RING)}
+
+
+@pytest.mark.parametrize("ops", list(FP8_RING128), ids=lambda o: o[0] + o[1])
+@pytest.mark.parametrize("shape", [(128, 128, 256), (1008, 1024, 1040), (48, 2048, 4096), (2048, 48, 2048),
+                                   (2096, 2064, 1088), (304, 272, 80), (144, 128, 64), (128, 144, 16)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_ring128(gpu_available, ops, shape):
+    """The 128 x 128 fp8 rings (A stored K x M and/or B stored K x N), forced:
+    exact on integer data (K of 16, 64 and 80), and on random data the same
+    bits as the 256 x 256 ring of the layout (the same byte pairing and slice
+    order)."""
+    op_a, op_b = ops
+    M, N, K = shape
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    small, big = (ids[n] for n in FP8_RING128[ops])
+    ok, _ = runnable("fp8f32", op_a, op_b, M, N, K, small)
+    assert ok
+    A, B, C0 = make_integer_inputs(M, N, K, seed=774, dtype="fp8f32")
+    As, Bs = stored(A, B, op_a, op_b)
+    for alpha, beta in [(-1.0, 2.0), (1.0, 0.0)]:
+        say(f"[fp8 ring128 {op_a}{op_b}] exact M={M} N={N} K={K} alpha={alpha} beta={beta} seed=774")
+        C, _, _ = run_gemm(As, Bs, C0, alpha, beta, kernel=small, op_a=op_a, op_b=op_b)
+        np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, alpha, beta, op_a, op_b))
+    A, B, C0 = make_random_inputs(M, N, K, seed=775, dist="normal", dtype="fp8f32")
+    As, Bs = stored(A, B, op_a, op_b)
+    say(f"[fp8 ring128 {op_a}{op_b}] random M={M} N={N} K={K} seed=775, against the 256 x 256 ring")
+    C1, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=small, op_a=op_a, op_b=op_b)
+    C2, _, _ = run_gemm(As, Bs, C0, 0.5, 0.25, kernel=big, op_a=op_a, op_b=op_b)
+    np.testing.assert_array_equal(C1, C2)
+    check(C1, As, Bs, C0, 0.5, 0.25, op_a, op_b, "fp8f32")
+
+
 @pytest.mark.parametrize("name", [FP8_LINES, FP8_LINES128])
 def test_fp8_lines_epilogue_padded(gpu_available, name):
     """Bias and GELU with A, B and C inside NaN-padded rows (padding 16, 48

@@ -41,6 +41,7 @@
 // slice kt + NS.  The pairs are pinned with sched_barrier.
 #include "gemm_device.hpp"
 #include "gemm_kernels.hpp"
+#include "gemm_lines.hpp"
 #include "gemm.h"
 
 namespace gemm {
@@ -309,6 +310,182 @@ hipError_t launch_fp8_ring(const GemmParams &p, hipStream_t stream) {
                            stream);
 }
 
+// The same ring at 128 x 128 (each wave 64 x 64, 2 x 2 fragments), for the
+// layouts without a 128 x 128 whole-line kernel: four 16 KB stages (two
+// workgroups per compute unit), per slice 4 matrix instructions per wave,
+// each paired with a quarter of the next slice's fragment reads and one of
+// the slice's 4 loads.  A K x (M or N) slice is [64 k rows][128 columns];
+// its 16-byte chunk c of row k sits at c ^ (k % 8), which gives the eight
+// rows of a transposing read eight different chunk columns.  Byte pairing,
+// slice order and the extra zero slices past K are the 256 x 256 ring's, so
+// the two give the same bits.  The epilogue is the whole-line kernels'.
+template <int OUT, bool AKN, bool BKN>
+__global__ void __launch_bounds__(256)
+fp8_ring128_kernel(GemmParams p, int tiles_m, int tiles_n) {
+    apply_k_split<uint8_t>(p);
+    constexpr int NS = 4, BM = 128, BN = 128, BK = 64;
+    constexpr int kA = BM * BK;          // 8 KB of A per slice
+    constexpr int kB = BN * BK;          // 8 KB of B per slice
+    constexpr int kStage = kA + kB;
+    __shared__ __attribute__((aligned(1024))) char st0[kStage], st1[kStage], st2[kStage], st3[kStage];
+    auto stage_base = [&](int st) -> char * { return st == 0 ? st0 : st == 1 ? st1 : st == 2 ? st2 : st3; };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_coords_square(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint8_t *A = static_cast<const uint8_t *>(p.A);
+    const uint8_t *B = static_cast<const uint8_t *>(p.B);
+    const int a_rows = min(BM, M - m0), b_rows = min(BN, N - n0);
+
+    // Load j (0..1) of this wave fills 1 KB block i = 2*wave + j of a panel:
+    // k-contiguous, rows 16i .. +15 (lane -> row 16i + lane/4, physical chunk
+    // lane%4 holding logical chunk (lane%4) ^ swizzle(row)); K x (M or N), k
+    // rows 8i .. 8i+7 (lane -> k row 8i + lane/8, physical chunk lane%8
+    // holding logical chunk (lane%8) ^ (k % 8)).
+    uint32_t goff_a[2], goff_b[2];
+    int kc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int i = 2 * wave + j;
+        const int row = 16 * i + (lane >> 2);
+        const int lc = (lane & 3) ^ fp8_swz(row);
+        kc[j] = 16 * lc;
+        const int kr = 8 * i + (lane >> 3);
+        const int cc = (lane & 7) ^ (kr & 7);
+        goff_a[j] = AKN ? (uint32_t)(kr * lda + 16 * cc) : panel_off(row, a_rows, lda, 16 * lc, 1);
+        goff_b[j] = BKN ? (uint32_t)(kr * ldb + 16 * cc) : panel_off(row, b_rows, ldb, 16 * lc, 1);
+    }
+    // Resources of slice kt, rebased per slice, as in the 256 x 256 ring.
+    auto slice_rsrc = [&](int kt, rsrc_t &ra, rsrc_t &rb) {
+        const int k0 = kt * BK;
+        if (AKN)
+            ra = make_rsrc(A + (int64_t)k0 * lda + m0, clamp_extent((int64_t)(K - k0 - 1) * lda + (M - m0)));
+        else
+            ra = make_rsrc(A + (int64_t)m0 * lda + k0, clamp_extent((int64_t)(a_rows - 1) * lda + (K - k0)));
+        if (BKN)
+            rb = make_rsrc(B + (int64_t)k0 * ldb + n0, clamp_extent((int64_t)(K - k0 - 1) * ldb + (N - n0)));
+        else
+            rb = make_rsrc(B + (int64_t)n0 * ldb + k0, clamp_extent((int64_t)(b_rows - 1) * ldb + (K - k0)));
+    };
+    // Load j (0..3) of slice kt into `stage`: j < 2 fills A block 2*wave + j,
+    // j >= 2 B block 2*wave + j - 2.
+    auto dma = [&](int kt, int stage, const rsrc_t &ra, const rsrc_t &rb, int j) {
+        const int jj = j & 1;
+        const bool kn = j < 2 ? AKN : BKN;     // k rows past K already fall outside the extent
+        const uint32_t poison = kn ? 0u : (uint32_t)(kc[jj] >= K - kt * BK) << 31;
+        char *dst = stage_base(stage) + (j < 2 ? 0 : kA) + (2 * wave + jj) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 2 ? ra : rb, (lds_void *)dst, 16,
+                                                 (j < 2 ? goff_a[jj] : goff_b[jj]) + poison, 0, 0, 0);
+    };
+    // Fragment reads: lane (h, l32) of fragment f reads row 32*f + l32 of the
+    // wave's 64-row block, logical chunks 2h and 2h+1 (k-contiguous); with a
+    // K x (M or N) panel, lane s of each 16-lane group points at k row 32h +
+    // 8q + e(s) and the half 8*(s%2) of the chunk holding the group's 16
+    // columns (the 256 x 256 ring's transposing reads on 128-byte rows).
+    const int h = lane >> 5, l32 = lane & 31;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int sw = fp8_swz(l32);
+    const uint32_t ch0 = 16 * ((2 * h) ^ sw), ch1 = 16 * ((2 * h + 1) ^ sw);
+    const uint32_t fa_row = (uint32_t)((wm * 64 + l32) * BK);
+    const uint32_t fb_row = (uint32_t)(kA + (wn * 64 + l32) * BK);
+    const int s16 = lane & 15;
+    const int e_src = ((s16 >> 1) & 3) + 4 * (s16 >> 3);
+    auto kn_off = [&](uint32_t region, int wcol, int f, int q) -> uint32_t {
+        const int kr = 32 * h + 8 * q + e_src;
+        const int c = wcol / 16 + 2 * f + (l32 >> 4);
+        return region + (uint32_t)(kr * 128 + 16 * (c ^ (kr & 7)) + 8 * (s16 & 1));
+    };
+
+    i32x8 fa[2][2], fb[2][2];
+    constexpr int NRA = AKN ? 8 : 4, NRB = BKN ? 8 : 4, NR = NRA + NRB;
+    auto read_slot = [&](int stage, int set, int r) {
+        const char *base = stage_base(stage);
+        const bool is_a = r < NRA;
+        const bool kn = is_a ? AKN : BKN;
+        const int rr = is_a ? r : r - NRA;
+        i32x8 *frags = is_a ? fa[set] : fb[set];
+        if (kn) {
+            const int f = rr >> 2, q = rr & 3;
+            const uint32_t off = is_a ? kn_off(0, wm * 64, f, q) : kn_off(kA, wn * 64, f, q);
+            const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(base + off));
+            frags[f][2 * q] = v[0];
+            frags[f][2 * q + 1] = v[1];
+        } else {
+            const int f = (rr >> 1) & 1;
+            const uint32_t off = (is_a ? fa_row : fb_row) + 32 * BK * f + ((rr & 1) ? ch1 : ch0);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(base + off);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) frags[f][4 * (rr & 1) + e] = (int)v[e];
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto mma = [&](int set, int t) {
+        const int i = t >> 1, j = t & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0, 0,
+                                                                     0, 0);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    {
+        rsrc_t ra, rb;
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            slice_rsrc(st, ra, rb);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dma(st, st, ra, rb, j);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * (NS - 1)));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_slot(0, 0, r);
+    for (int kb = 0; kb < nk; kb += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int kt = kb + u;
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * (NS - 2)));
+            __builtin_amdgcn_s_barrier();
+            rsrc_t ra, rb;
+            slice_rsrc(kt + NS, ra, rb);      // zeros past the end
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                mma(u & 1, t);
+#pragma unroll
+                for (int r = t * NR / 4; r < (t + 1) * NR / 4; ++r) read_slot((u + 1) % NS, (u + 1) & 1, r);
+                dma(kt + NS, u, ra, rb, t);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    // Every load has landed and every wave is done with the stages before the
+    // epilogue reuses them: 16 KB of staging per wave, stage `wave`.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    char *stg = stage_base(wave);
+    lines_epilogue<OUT, true>(p, acc, [&](int row) -> char * { return stg + row * 256; }, m0, n0, wm, wn, lane);
+}
+
+template <bool AKN, bool BKN>
+hipError_t launch_fp8_ring128(const GemmParams &p, hipStream_t stream) {
+    int tiles_m = (p.M + 127) / 128, tiles_n = (p.N + 127) / 128;
+    GemmParams args = p;
+    void *argv[] = {&args, (void *)&tiles_m, (void *)&tiles_n};
+    const int out = launch_out_type(p);
+    const void *fn = out == GEMM_OUT_BF16  ? reinterpret_cast<const void *>(&fp8_ring128_kernel<GEMM_OUT_BF16, AKN, BKN>)
+                     : out == GEMM_OUT_FP8 ? reinterpret_cast<const void *>(&fp8_ring128_kernel<GEMM_OUT_FP8, AKN, BKN>)
+                                           : reinterpret_cast<const void *>(&fp8_ring128_kernel<GEMM_OUT_F32, AKN, BKN>);
+    return hipLaunchKernel(fn, dim3((unsigned)(tiles_m * tiles_n), (unsigned)k_splits(p)), dim3(256), argv, 0,
+                           stream);
+}
+
 #define FP8_RING_INSTANCES(AKN, BKN)                                                             \
     template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_F32, AKN, BKN>(GemmParams, int, int);  \
     template __global__ void fp8_ring_kernel<4, 4, GEMM_OUT_BF16, AKN, BKN>(GemmParams, int, int); \
@@ -317,6 +494,15 @@ FP8_RING_INSTANCES(false, false)
 FP8_RING_INSTANCES(false, true)
 FP8_RING_INSTANCES(true, true)
 FP8_RING_INSTANCES(true, false)
+template __global__ void fp8_ring128_kernel<GEMM_OUT_F32, false, true>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_BF16, false, true>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_FP8, false, true>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_F32, true, true>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_BF16, true, true>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_FP8, true, true>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_F32, true, false>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_BF16, true, false>(GemmParams, int, int);
+template __global__ void fp8_ring128_kernel<GEMM_OUT_FP8, true, false>(GemmParams, int, int);
 
 }  // namespace
 
@@ -333,6 +519,13 @@ const KernelDesc kFp8TiledKernels[] = {
      &launch_fp8_ring<4, 4, true, true>, 0, nullptr, kLayoutTN, false, kOutAll},
     {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 256, 256, 64, 256, 16, 16, "fp8_mfma32_256x256x64_w2x2_tt_ring4",
      &launch_fp8_ring<4, 4, true, false>, 0, nullptr, kLayoutTT, false, kOutAll},
+    // 128 x 128 for the layouts without a whole-line kernel of that tile.
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 128, 128, 64, 256, 16, 16, "fp8_mfma32_128x128x64_w2x2_nn_ring4",
+     &launch_fp8_ring128<false, true>, 0, nullptr, kLayoutNN, false, kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 128, 128, 64, 256, 16, 16, "fp8_mfma32_128x128x64_w2x2_tn_ring4",
+     &launch_fp8_ring128<true, true>, 0, nullptr, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_TILED, 128, 128, 64, 256, 16, 16, "fp8_mfma32_128x128x64_w2x2_tt_ring4",
+     &launch_fp8_ring128<true, false>, 0, nullptr, kLayoutTT, false, kOutAll},
 };
 const int kFp8TiledKernelCount = sizeof(kFp8TiledKernels) / sizeof(kFp8TiledKernels[0]);
 #endif
