@@ -632,34 +632,79 @@ def test_fp8_workspace_size():
 
 # ----------------------------------------------------------------------------- last-wave split
 
+F32_RING256 = "f32_mfma32_256x256x16_w2x2_a4b4_ring4"
+
+
 def test_wave_tail_plan():
     """272 tiles of 256 = one full wave + 16: the top 4096 rows run as one
-    wave and the last tile row runs K-split."""
-    ws = tg.gemm_workspace_size(F32, 4352, 4096, 4096)
-    st, pl = plan(F32, 4352, 4096, 4096, ws=ws)
-    assert st == OK and pl["tile_m"] == 256 and pl["split_row"] == 4096 and pl["splits"] >= 2, pl
-    assert pl["grid"] == 256 + 16 * pl["splits"]
-    assert ws >= pl["splits"] * 256 * 4096 * 4
-    # No workspace, or one too small: the plain plan.
-    assert plan(F32, 4352, 4096, 4096)[1]["split_row"] == 0
-    assert plan(F32, 4352, 4096, 4096, ws=1024)[1]["split_row"] == 0
+    wave and the last tile row runs K-split (bf16 by choice, fp32 on the
+    forced 256 x 256 ring, whose own choice is 128 x 128 tiles)."""
+    for dtype, force in [(BF16, 0), (F32, kernel_ids(name=F32_RING256)[0])]:
+        ws = tg.gemm_workspace_size(dtype, 4352, 4096, 4096)
+        st, pl = plan(dtype, 4352, 4096, 4096, ws=ws, force=force)
+        assert st == OK and pl["tile_m"] == 256 and pl["split_row"] == 4096 and pl["splits"] >= 2, pl
+        assert pl["grid"] == 256 + 16 * pl["splits"]
+        assert ws >= pl["splits"] * 256 * 4096 * 4
+        # No workspace, or one too small: the plain plan.
+        assert plan(dtype, 4352, 4096, 4096, force=force)[1]["split_row"] == 0
+        assert plan(dtype, 4352, 4096, 4096, ws=1024, force=force)[1]["split_row"] == 0
 
 
 def test_wave_tail_only_for_a_mostly_empty_last_wave():
     ws = 1 << 32
+    ring = kernel_ids(name=F32_RING256)[0]
     assert plan(F32, 4096, 4096, 4096, ws=ws)[1]["split_row"] == 0           # exactly one wave
     assert plan(F32, 4096 + 256 * 13, 4096, 4096, ws=ws)[1]["split_row"] == 0  # 464 tiles: last wave 81% full
-    assert plan(F32, 4352, 4096, 1024, ws=ws)[1]["split_row"] == 0           # K too shallow to split
+    assert plan(F32, 4352, 4096, 1024, ws=ws, force=ring)[1]["split_row"] == 0  # K too shallow to split
     st, pl = plan(BF16, 8448, 8192, 8192, ws=ws)
     assert st == OK and pl["split_row"] == 8192 and pl["splits"] >= 2, pl
+    # 128 x 128 tiles run two to a compute unit: no last-wave split for them.
+    for name in ["f32_mfma32_128x128x16_w2x2_a4b4_ring4", "bf16_mfma32_128x128x64_w2x2_a8b8_lines"]:
+        st, pl = plan(F32 if name[0] == "f" else BF16, 4352, 4096, 4096, ws=ws, force=kernel_ids(name=name)[0])
+        assert st == OK and pl["split_row"] == 0 and pl["splits"] == 1, pl
 
 
-@pytest.mark.parametrize("dtype,ops", [(F32, (T_, N_)), (BF16, (N_, T_)), (FP8, (N_, T_))])
-def test_wave_tail_other_layouts(dtype, ops):
+@pytest.mark.parametrize("dtype,ops,force", [(F32, (T_, N_), "f32_mfma32_256x256x16_w2x2_a4b4_tn_ring4"),
+                                             (BF16, (N_, T_), ""),
+                                             (FP8, (N_, T_), "fp8_mfma32_256x256x128_w2x2_nt_lines")])
+def test_wave_tail_other_layouts(dtype, ops, force):
     M, N = 4352, 4096                           # 17 x 16 tiles of 256: one wave + 16
     ws = tg.gemm_workspace_size(dtype, M, N, 4096)
-    st, pl = gplan(dtype, ops[0], ops[1], M, N, 4096, ws=ws)
+    st, pl = gplan(dtype, ops[0], ops[1], M, N, 4096, ws=ws, force=kernel_ids(name=force)[0] if force else 0)
     assert st == OK and pl["split_row"] > 0 and pl["splits"] >= 2, pl
+
+
+@pytest.mark.parametrize("dtype,ops,shape,ws,expect", [
+    # fp32: 128^2 tiles once a quarter of the last 256^2 wave is empty, with or without a workspace.
+    (F32, (N_, N_), (4352, 4096, 4096), False, "f32_mfma32_128x128x16_w2x2_a4b4_ring4"),
+    (F32, (N_, N_), (4352, 4096, 4096), True, "f32_mfma32_128x128x16_w2x2_a4b4_ring4"),
+    (F32, (N_, N_), (2048, 11008, 4096), False, "f32_mfma32_128x128x16_w2x2_a4b4_ring4"),
+    (F32, (N_, T_), (3072, 6144, 4096), True, "f32_mfma32_128x128x16_w2x2_a4b4_nt_ring4"),
+    (F32, (N_, N_), (4096, 7168, 4096), False, "f32_mfma32_128x128x16_w2x2_a4b4_ring4"),     # 448 tiles
+    (F32, (N_, N_), (4096 + 256 * 13, 4096, 4096), False, F32_RING256),                     # 464: 81% full
+    (F32, (N_, N_), (4096, 4096, 4096), True, F32_RING256),                                 # whole wave
+    # bf16 and the fp8 whole-line kernel: only between one and two waves, the second at most a quarter used.
+    (BF16, (N_, N_), (3072, 6144, 4096), False, "bf16_mfma32_128x128x64_w2x2_a8b8_lines"),
+    (BF16, (T_, N_), (4096, 5120, 4096), False, "bf16_mfma32_128x128x32_w2x2_a8b8_tn_lines"),
+    (BF16, (N_, N_), (2048, 11008, 4096), False, "bf16_mfma32_256x256x64_w2x2_a8b8_lines"),  # 344 tiles
+    (BF16, (N_, T_), (6144, 6144, 4096), False, "bf16_mfma32_256x256x64_w2x2_a8b8_nt_lines"),  # 576 tiles
+    (BF16, (N_, N_), (3072, 6144, 4096), True, "bf16_mfma32_256x256x64_w2x2_a8b8_lines"),   # the split stays
+    (BF16, (N_, N_), (8192, 8192, 8192), False, "bf16_mfma32_256x256x64_w2x2_a8b8_lines"),
+    (FP8, (N_, T_), (4096, 5120, 4096), True, "fp8_mfma32_128x128x128_w2x2_nt_lines"),
+    (FP8, (N_, T_), (2048, 11008, 4096), False, "fp8_mfma32_256x256x128_w2x2_nt_lines"),
+    # the fp8 rings: as fp32, and on whole waves with K <= 2048.
+    (FP8, (N_, N_), (6144, 6144, 4096), True, "fp8_mfma32_128x128x64_w2x2_nn_ring4"),
+    (FP8, (T_, T_), (2048, 11008, 4096), False, "fp8_mfma32_128x128x64_w2x2_tt_ring4"),
+    (FP8, (T_, N_), (4096, 4096, 1024), False, "fp8_mfma32_128x128x64_w2x2_tn_ring4"),
+    (FP8, (N_, N_), (4096, 4096, 4096), False, "fp8_mfma32_256x256x64_w2x2_nn_ring4"),
+])
+def test_last_wave_takes_128_tiles(dtype, ops, shape, ws, expect):
+    M, N, K = shape
+    wsb = tg.gemm_workspace_size(dtype, M, N, K) if ws else 0
+    st, pl = gplan(dtype, ops[0], ops[1], M, N, K, ws=wsb)
+    assert st == OK and kname(pl) == expect, (kname(pl), pl)
+    if expect != "bf16_mfma32_256x256x64_w2x2_a8b8_lines" or not ws:
+        assert pl["split_row"] == 0
 
 
 @pytest.mark.parametrize("ops,name", [((N_, T_), "nt"), ((T_, N_), "tn"), ((T_, T_), "tt")])
@@ -824,10 +869,10 @@ def test_output_quantisation_choice(out_type):
     assert st == OK and kname(pl) == "bf16_skinny_nt_n32_w8_u2"
     # Short K: the 256-tile kernels preferred there write fp32 only, so a
     # regular kernel that writes the type runs, never the general fallback.
-    st, pl = eplan(BF16, N_, N_, 4352, 4096, 512, out_type, C=0)
+    st, pl = eplan(BF16, N_, N_, 4096, 4096, 512, out_type, C=0)
     info = tg.gemm_kernel_query(pl["kernel_id"])
     assert st == OK and "general" not in info["name"] and (info["outputs"] >> out_type) & 1, pl
-    assert kname(gplan(BF16, N_, N_, 4352, 4096, 512)[1]) == "bf16_mfma32_256x256x64_w2x2_a8b8_pipe"
+    assert kname(gplan(BF16, N_, N_, 4096, 4096, 512)[1]) == "bf16_mfma32_256x256x64_w2x2_a8b8_pipe"
     # fp32 M <= 16 without a workspace: the one-pass skinny kernel.
     st, pl = eplan(F32, N_, N_, 16, 8192, 8192, out_type)
     assert st == OK and pl["path"] == tg.GEMM_PATH_SKINNY, pl

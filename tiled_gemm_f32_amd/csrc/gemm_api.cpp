@@ -251,9 +251,12 @@ KSplit tiled_ksplit(const Call &c, int tile_m, int tile_n) {
 // run as usual and the few tile rows left over run as a separate K-split
 // problem, whose slices spread their multiply-adds over the compute units
 // that would otherwise idle.  Estimated in full-tile times: taken when it
-// saves at least half of one.
+// saves at least half of one.  Only for 256^2 tiles, one workgroup per
+// compute unit: smaller tiles run two or more to a compute unit, so a wave
+// holds more of them than this count assumes.
 KSplit wave_tail(const Call &c, int tile) {
     const KSplit none{1, 0, 0};
+    if (tile != 256) return none;
     const int64_t tiles_m = ceil_div(c.M, tile), tiles_n = ceil_div(c.N, tile);
     const int64_t T = tiles_m * tiles_n, waves = T / kComputeUnits, r = T % kComputeUnits;
     if (waves == 0 || r == 0 || 2 * r > kComputeUnits) return none;
@@ -316,8 +319,32 @@ const KernelDesc *first_candidate(const Candidates &cand, const Call &c, int til
 // Tile choice among kernels of one class (see below).
 const KernelDesc *choose_tiled(const Call &c, const Candidates &cand);
 
+// 128^2 tiles in place of 256^2 ones whose last wave is mostly empty ("A
+// GEMM Kernel, Step by Step", "The fringe and the last wave").  Two 128^2
+// workgroups share a compute unit and each holds a quarter of the work, so
+// their last wave is eight times finer.  What the small tile gives up per
+// multiply-add decides how empty the 256^2 wave must be (measured against
+// 256^2 tiles unsplit):
+// - the fp32 rings and the fp8 rings lose little: 128^2 tiles win once a
+//   quarter of the last wave is empty (fp32 0.65-0.90 of the time, fp8
+//   0.74-0.98), and the fp8 rings also win on whole waves with K <= 2048
+//   (0.77-0.92), where the 256^2 ring's fill and drain weigh more;
+// - the bf16 and fp8 whole-line kernels lose more: 128^2 tiles win only
+//   between one and two waves with at most a quarter of the second used
+//   (0.84-0.89).
+bool last_wave_prefers_128(const Call &c) {
+    const int64_t T = ceil_div(c.M, 256) * ceil_div(c.N, 256);
+    if (T < kComputeUnits) return false;
+    const int64_t empty = ceil_div(T, kComputeUnits) * kComputeUnits - T;
+    const bool fp8 = c.dtype == GEMM_DTYPE_FP8F32;
+    const bool lines = c.dtype == GEMM_DTYPE_BF16F32 || (fp8 && c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_T);
+    if (lines) return T < 2 * kComputeUnits && 4 * empty >= 3 * kComputeUnits;
+    return 4 * empty >= kComputeUnits || (fp8 && c.K <= 2048);
+}
+
 // Tile choice: the largest square tile whose tile count covers every compute
-// unit at least once; small problems fall through to the smallest tile.  The
+// unit at least once, unless 256^2 tiles leave a mostly empty last wave
+// (last_wave_prefers_128); small problems fall through to the smallest tile.  The
 // rule compares kernels of like speed, so it runs over the regular kernels
 // first and over the fallback (general) kernels only when none of those runs
 // the call.
@@ -395,6 +422,13 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand) {
                 ceil_div(c.M, tile / 2) * ceil_div(c.N, tile / 2) >= kComputeUnits &&
                 first_candidate(cand, c, tile / 2) != nullptr)
                 continue;
+            // A mostly empty last wave (above) goes to 128^2 tiles too when
+            // its tile rows would run as a last-wave split, except in bf16:
+            // 128^2 tiles took 0.74-0.97 of the split's time in fp8 and
+            // 0.85-1.01 in fp32, but 0.91-1.10 in bf16.
+            if (tile == 256 && (ks.splits == 1 || (ks.m_top > 0 && c.dtype != GEMM_DTYPE_BF16F32)) &&
+                last_wave_prefers_128(c) && first_candidate(cand, c, 128) != nullptr)
+                continue;
             if (4 * c.M * c.N >= 3 * pm * pn && fills) return kd;
         }
     }
@@ -404,6 +438,7 @@ const KernelDesc *choose_tiled(const Call &c, const Candidates &cand) {
         if (kernel_runs(cand.k[i], c) && cand.k[i]->tile_m < smallest) smallest = cand.k[i]->tile_m;
     for (int tile : {256, 128, 64}) {
         const int64_t tiles = ceil_div(c.M, tile) * ceil_div(c.N, tile);
+        if (tile == 256 && last_wave_prefers_128(c) && first_candidate(cand, c, 128) != nullptr) continue;
         if (tiles >= kComputeUnits || tile == smallest) {
             if (const KernelDesc *kd = first_candidate(cand, c, tile)) return kd;
         }
