@@ -101,7 +101,8 @@ KERNEL_SOURCES = {"f32_mfma32": "gemm_f32_tiled.hip", "bf16_mfma32": "gemm_bf16_
                   "fp8_mfma32_128x128x128_w2x2_nt_lines": "gemm_fp8_lines.hip",
                   "f32_skinny": "gemm_f32_skinny.hip", "fp8_mfma32": "gemm_fp8_tiled.hip",
                   "bf16_skinny": "gemm_bf16_skinny.hip", "f32_skinny_nt": "gemm_skinny_nt.hip",
-                  "bf16_skinny_nt": "gemm_skinny_nt.hip", "fp8_skinny_nt": "gemm_skinny_nt.hip"}
+                  "bf16_skinny_nt": "gemm_skinny_nt.hip", "fp8_skinny_nt": "gemm_skinny_nt.hip",
+                  "fp8_skinny_kn": "gemm_fp8_skinny.hip"}
 
 
 # Headers that only some kernel sources include (the whole-line epilogue).

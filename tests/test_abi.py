@@ -849,7 +849,7 @@ def test_output_types_of_the_kernels():
                  "fp8_mfma32_128x128x64_w2x2_tt_ring4",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
-                 "fp8_skinny_nt_splitk_n32_w8_u2"):
+                 "fp8_skinny_nt_splitk_n32_w8_u2", "fp8_skinny_kn_n128_w4_s4", "fp8_skinny_kn_n128_w4_s4_whole_k"):
         assert outs[name] == 7, name
     assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 7 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 7
     # Register-staged kernels holding 256 accumulators per lane write fp32 only.
@@ -953,3 +953,32 @@ def test_f32_ring64_is_the_choice_for_config_4a():
                                     0x1000, 3000, 0, ws)
         assert st == OK and kname(pl) == \
             "f32_mfma32_64x64x16_w2x2_a1b4_ring6", pl
+
+
+# ----------------------------------------------------------------------------- fp8 skinny, B stored K x N
+
+def test_fp8_kn_skinny_choice_and_workspace():
+    """M <= 16 with fp8 weights stored K x N: without a workspace and with at
+    most 128 strips of 128 columns, the streaming kernel over the whole of K;
+    otherwise the 128^2 ring (split over K with a workspace).  The split form
+    runs when forced and the workspace query covers it."""
+    split = kernel_ids(name="fp8_skinny_kn_n128_w4_s4")[0]
+    for M in (1, 7, 16):
+        ws = tg.gemm_workspace_size(FP8, M, 8192, 8192)
+        assert ws >= 4 * M * 8192 * 4               # 64 strips x 4 splits
+        st, pl = gplan(FP8, N_, N_, M, 8192, 8192, ws=ws, force=split)
+        assert st == OK and kname(pl) == "fp8_skinny_kn_n128_w4_s4" and pl["grid"] == 64 * 4, pl
+        assert pl["path"] == tg.GEMM_PATH_SKINNY_SPLITK
+        st, pl = gplan(FP8, N_, N_, M, 8192, 8192)
+        assert st == OK and kname(pl) == "fp8_skinny_kn_n128_w4_s4_whole_k" and pl["grid"] == 64, pl
+        st, pl = gplan(FP8, N_, N_, M, 8192, 8192, ws=ws)
+        assert st == OK and kname(pl) == "fp8_mfma32_128x128x64_w2x2_nn_ring4" and pl["splits"] > 1, pl
+    assert kname(gplan(FP8, N_, N_, 16, 16384, 4096)[1]) == "fp8_skinny_kn_n128_w4_s4_whole_k"   # 128 strips
+    assert kname(gplan(FP8, N_, N_, 16, 16512, 4096)[1]) == "fp8_mfma32_128x128x64_w2x2_nn_ring4"  # 129
+    # Rows of B must be whole 16-byte chunks, M at most 16, A stored M x K.
+    assert "skinny" not in kname(gplan(FP8, N_, N_, 16, 8200, 8192)[1])
+    assert gplan(FP8, N_, N_, 17, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
+    assert gplan(FP8, T_, N_, 16, 8192, 8192)[1]["path"] == tg.GEMM_PATH_TILED
+    # K too short for two 512-deep slices: one split, which needs no workspace.
+    st, pl = gplan(FP8, N_, N_, 16, 8192, 1008, force=split)
+    assert st == OK and kname(pl) == "fp8_skinny_kn_n128_w4_s4" and pl["splits"] == 1, pl

@@ -34,7 +34,7 @@ LIB_PATH = os.path.join(HERE, "libgemm.so")
 
 SOURCES = ["gemm_api.cpp", "gemm_f32_tiled.hip", "gemm_bf16_tiled.hip", "gemm_f32_skinny.hip", "gemm_fp8_tiled.hip",
            "gemm_general.hip", "gemm_bf16_skinny.hip", "gemm_skinny_nt.hip", "gemm_scratch.hip",
-           "gemm_bf16_lines.hip", "gemm_fp8_lines.hip"]
+           "gemm_bf16_lines.hip", "gemm_fp8_lines.hip", "gemm_fp8_skinny.hip"]
 HEADERS = ["gemm_device.hpp", "gemm_kernels.hpp", "gemm_lines.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

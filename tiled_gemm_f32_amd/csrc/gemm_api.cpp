@@ -32,7 +32,7 @@ int table_size() {
     return gemm::kF32TiledKernelCount + gemm::kBf16TiledKernelCount + gemm::kF32SkinnyKernelCount +
            gemm::kF32SplitKernelCount + gemm::kFp8TiledKernelCount + gemm::kGeneralKernelCount +
            gemm::kBf16SplitKernelCount + gemm::kSkinnyNtKernelCount + gemm::kBf16LinesKernelCount +
-           gemm::kFp8LinesKernelCount;
+           gemm::kFp8LinesKernelCount + gemm::kFp8SkinnyKernelCount;
 }
 
 const KernelDesc *kernel_by_id(int32_t id) {
@@ -60,6 +60,8 @@ const KernelDesc *kernel_by_id(int32_t id) {
     if (i < gemm::kBf16SplitKernelCount) return &gemm::kBf16SplitKernels[i];
     i -= gemm::kBf16SplitKernelCount;
     if (i < gemm::kSkinnyNtKernelCount) return &gemm::kSkinnyNtKernels[i];
+    i -= gemm::kSkinnyNtKernelCount;
+    if (i < gemm::kFp8SkinnyKernelCount) return &gemm::kFp8SkinnyKernels[i];
     return nullptr;
 }
 
@@ -365,6 +367,19 @@ const KernelDesc *choose(const Call &c) {
     // caller's workspace allows (it needs one only when it splits).
     if (b_kn && c.dtype == GEMM_DTYPE_BF16F32 && skinny_fits(c)) {
         if (const KernelDesc *kd = first_match(gemm::kBf16SplitKernels, gemm::kBf16SplitKernelCount, c, 0))
+            return kd;
+    }
+    // fp8 weights stored K x N with M <= 16: the same kernel through
+    // byte-transposing reads, but only without a workspace and with at most
+    // half as many 128-column strips as compute units.  With a workspace the
+    // 128^2 ring split over K is as fast or faster (16 x 8192 x 8192: 18.8
+    // against 19.2 us; 16 x 28672 x 4096: 22.0 against 29.9 us), and so is the
+    // unsplit 128^2 ring once the strips would fill the compute units at one
+    // workgroup each (16 x 28672 x 4096: 21.8 against 24.7 us).  The split
+    // form stays a candidate for forced calls and the autotuner.
+    if (b_kn && c.op_a == GEMM_OP_N && c.dtype == GEMM_DTYPE_FP8F32 && skinny_fits(c) && c.ws == nullptr &&
+        2 * ceil_div(c.N, gemm::kFp8SkinnyKernels[0].tile_n) <= kComputeUnits) {
+        if (const KernelDesc *kd = first_match(gemm::kFp8SkinnyKernels, gemm::kFp8SkinnyKernelCount, c, 0))
             return kd;
     }
     // M <= 16 with B stored N x K (a linear layer's weights): the streaming
@@ -813,10 +828,12 @@ GEMM_API int64_t gemm_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_
         need = tail.bytes > need ? tail.bytes : need;
     }
     if (M > 16) return need;
-    const gemm::KernelDesc *skinny = dtype == GEMM_DTYPE_F32 ? gemm::kF32SplitKernels : gemm::kBf16SplitKernels;
-    const int count = dtype == GEMM_DTYPE_F32   ? gemm::kF32SplitKernelCount
+    const gemm::KernelDesc *skinny = dtype == GEMM_DTYPE_F32       ? gemm::kF32SplitKernels
+                                     : dtype == GEMM_DTYPE_BF16F32 ? gemm::kBf16SplitKernels
+                                                                   : gemm::kFp8SkinnyKernels;
+    const int count = dtype == GEMM_DTYPE_F32       ? gemm::kF32SplitKernelCount
                       : dtype == GEMM_DTYPE_BF16F32 ? gemm::kBf16SplitKernelCount
-                                                  : 0;
+                                                    : gemm::kFp8SkinnyKernelCount;
     for (int i = 0; i < count; ++i) {
         const int64_t strips = ceil_div(N, skinny[i].tile_n);
         const int64_t b = gemm::skinny_workspace_bytes((int)strips, (int)M, (int)N, (int)K);

@@ -116,6 +116,8 @@ extern const KernelDesc kBf16LinesKernels[];
 extern const int kBf16LinesKernelCount;
 extern const KernelDesc kFp8LinesKernels[];
 extern const int kFp8LinesKernelCount;
+extern const KernelDesc kFp8SkinnyKernels[];
+extern const int kFp8SkinnyKernelCount;
 
 // Size of the library's static device scratch (gemm_scratch.hip), the
 // workspace of gemm_general_noalloc.
