@@ -776,7 +776,7 @@ def test_skinny_a_transposed_choice():
     A transposed, split over K when a workspace is passed; never for other
     layouts, M = 17, or K rows of A beyond 2^31 bytes."""
     for M in (1, 16):
-        st, pl = gplan(F32, T_, N_, M, 8192, 8192)
+        st, pl = gplan(F32, T_, N_, M, 8192, 8192, lda=16)      # (lda = 1 at M = 1 runs untransposed)
         assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4" and pl["grid"] == 256, pl
     st, pl = gplan(F32, T_, N_, 16, 8192, 8192, ws=tg.gemm_workspace_size(F32, 16, 8192, 8192))
     assert st == OK and kname(pl) == "f32_skinny_splitk_n128_at_w8_u1" and pl["grid"] == 256, pl
@@ -789,10 +789,16 @@ def test_skinny_a_transposed_choice():
     assert st == OK and kname(pl) == "bf16_skinny_lds_n128_at_w4_s4_whole_k" and pl["grid"] == 64, pl
     st, pl = gplan(BF16, T_, N_, 8, 8192, 8192, lda=8, ws=tg.gemm_workspace_size(BF16, 8, 8192, 8192))
     assert st == OK and kname(pl) == "bf16_skinny_lds_n128_at_w4_s4" and pl["grid"] == 256, pl
-    assert "_at_" not in kname(gplan(BF16, T_, N_, 5, 8192, 8192, lda=8)[1])      # rows of 5: not whole chunks
-    assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=20)[1])
-    assert "_at_" not in kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=16, A=PA + 2)[1])
-    assert "_at_" not in kname(gplan(BF16, N_, N_, 16, 8192, 8192)[1])
+    # Otherwise (rows of A not whole 16-byte chunks): the same kernel loading
+    # A 2 bytes a lane.
+    at1 = "bf16_skinny_lds_n128_at1_w4_s4"
+    assert kname(gplan(BF16, T_, N_, 5, 8192, 8192, lda=8)[1]) == at1 + "_whole_k"   # rows of 5
+    assert kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=20)[1]) == at1 + "_whole_k"
+    assert kname(gplan(BF16, T_, N_, 16, 8192, 8192, lda=16, A=PA + 2)[1]) == at1 + "_whole_k"
+    st, pl = gplan(BF16, T_, N_, 12, 8192, 8192, lda=13, ws=tg.gemm_workspace_size(BF16, 12, 8192, 8192))
+    assert st == OK and kname(pl) == at1 and pl["grid"] == 256, pl
+    assert "_at" not in kname(gplan(BF16, N_, N_, 16, 8192, 8192)[1])
+    assert "_at" not in kname(gplan(BF16, T_, N_, 17, 8192, 8192, lda=17)[1])
     K = 1 << 20
     st, pl = gplan(F32, T_, N_, 16, 64, K, lda=1 << 9)             # ((K - 1) * lda + M) * 4 < 2^31
     assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4", pl
@@ -982,3 +988,23 @@ def test_fp8_kn_skinny_choice_and_workspace():
     # K too short for two 512-deep slices: one split, which needs no workspace.
     st, pl = gplan(FP8, N_, N_, 16, 8192, 1008, force=split)
     assert st == OK and kname(pl) == "fp8_skinny_kn_n128_w4_s4" and pl["splits"] == 1, pl
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, FP8])
+def test_single_row_a_stored_transposed_runs_untransposed(dtype):
+    """M = 1 with A stored K x 1 and lda = 1 is the same memory as a 1 x K
+    row: it takes the untransposed layout's kernels (the streaming ones for
+    B stored K x N and N x K); with lda > 1 it stays transposed."""
+    for op_b in (N_, T_):
+        st, pl = gplan(dtype, T_, op_b, 1, 8192, 8192, lda=1)
+        st2, pl2 = gplan(dtype, N_, op_b, 1, 8192, 8192)
+        assert st == st2 == OK and kname(pl) == kname(pl2) and pl["grid"] == pl2["grid"], (kname(pl), kname(pl2))
+        if dtype != FP8 or op_b == T_:
+            assert "skinny" in kname(pl), kname(pl)
+        st, pl = gplan(dtype, T_, op_b, 1, 8192, 8192, lda=2)
+        assert st == OK and ((tg.gemm_kernel_query(pl["kernel_id"])["layouts"] >> (2 + op_b)) & 1), kname(pl)
+    # A forced kernel keeps the layout as passed.
+    if dtype == F32:
+        at = kernel_ids(name="f32_skinny_mfma16_n2_at_w8_u4")[0]
+        st, pl = gplan(F32, T_, N_, 1, 8192, 8192, lda=1, force=at)
+        assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4", pl

@@ -649,8 +649,9 @@ def test_skinny_a_transposed_exact(gpu_available, M, NK):
         C, _, _ = run_gemm(As, B, C0, 2.0, -1.0, kernel=kid, ws=w, bias=bias, activation="relu", op_a="T",
                            pad=pad)
         np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
-    st, pl = tg.gemm_plan_query_general(tg.GEMM_DTYPE_F32, 1, 0, M, N, K, 1.0, 0x1000, M, 0x1000, N, 0.0, 0x1000, N,
-                                        0, 0)
+    # (M = 1 with lda = 1 is the same memory as A stored 1 x K, and runs as that.)
+    st, pl = tg.gemm_plan_query_general(tg.GEMM_DTYPE_F32, 1, 0, M, N, K, 1.0, 0x1000, max(M, 2), 0x1000, N, 0.0,
+                                        0x1000, N, 0, 0)
     assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] in F32_AT_SKINNY
 
 
@@ -702,6 +703,69 @@ def test_bf16_skinny_a_transposed_exact(gpu_available, M, NK):
     st, pl = tg.gemm_plan_query_general(tg.GEMM_DTYPE_BF16F32, 1, 0, M, N, K, 1.0, 0x1000, 16, 0x1000, N, 0.0,
                                         0x1000, N, 0, 0)
     assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] in BF16_AT_SKINNY
+
+
+BF16_AT1_SKINNY = ["bf16_skinny_lds_n128_at1_w4_s4", "bf16_skinny_lds_n128_at1_w4_s4_whole_k"]
+
+
+@pytest.mark.parametrize("M", [1, 5, 12, 13])
+@pytest.mark.parametrize("NK", [(8192, 4096), (1000, 777), (1008, 3008)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_bf16_skinny_a_transposed_any_m_exact(gpu_available, M, NK):
+    """bf16 with A stored K x M whose rows are not whole 16-byte chunks (M of
+    1, 5, 12 or 13; rows padded by 3 NaN elements, and A one element off
+    4-byte alignment): both forms of the kernel that loads A 2 bytes a lane,
+    forced, and the library's choice with and without a workspace, bit-exact
+    on integer data with bias and ReLU.  Columns past M (the NaN padding and
+    the next row) must never reach C; rows past K must read as zero."""
+    N, K = NK
+    A, B, C0 = make_integer_inputs(M, N, K, seed=790 + M, dtype="bf16f32")
+    As = A.t().contiguous()
+    bias = make_bias(N, seed=791, integer=True)
+    ref = oracle.gemm_epilogue_ref(host_view(As), host_view(B), 2.0, -1.0, C0.numpy(), bias.numpy(), "relu", "T", "N")
+    ws = tg.workspace(M, N, K, dtype=tg.GEMM_DTYPE_BF16F32)
+    ids = {k["name"]: k["id"] for k in tg.kernels()}
+    runs = [(n, ids[n], ws) for n in BF16_AT1_SKINNY] + [("auto", 0, None), ("auto ws", 0, ws)]
+    for name, kid, w in runs:
+        say(f"[bf16 A^T skinny, 2-byte A] {name} M={M} N={N} K={K} lda={M + 3} offset=1 seed={790 + M}")
+        C, _, _ = run_gemm(As, B, C0, 2.0, -1.0, kernel=kid, ws=w, bias=bias, activation="relu", op_a="T",
+                           pad=(3, 0, 0), offset=(1, 0, 0))
+        np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
+    st, pl = tg.gemm_plan_query_general(tg.GEMM_DTYPE_BF16F32, 1, 0, M, N, K, 1.0, 0x1002, M + 3, 0x1000, N, 0.0,
+                                        0x1000, N, 0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] in BF16_AT1_SKINNY
+
+
+def test_bf16_skinny_a_transposed_any_m_random(gpu_available):
+    """12 x 8192 x 8192, A stored K x 12, N(0,1) data, with and without a
+    workspace: within the bf16 bound, and the same bits as the untransposed
+    call (the same matrix-instruction inputs in the same order)."""
+    M, N, K = 12, 8192, 8192
+    A, B, C0 = make_random_inputs(M, N, K, seed=792, dist="normal", dtype="bf16f32")
+    As = A.t().contiguous()
+    ws = tg.workspace(M, N, K, dtype=tg.GEMM_DTYPE_BF16F32)
+    a, b = host_view(As), host_view(B)
+    for w in (ws, None):
+        say(f"[bf16 A^T skinny, 2-byte A] auto M={M} N={N} K={K} normal seed=792 ws={w is not None}")
+        C, _, _ = run_gemm(As, B, C0, 1.0, 0.5, ws=w, op_a="T")
+        r = oracle.error_ratio(C, oracle.gemm_ref(a, b, 1.0, 0.5, C0.numpy(), "T", "N"),
+                               oracle.gemm_absbound(a, b, 1.0, 0.5, C0.numpy(), "T", "N"))
+        say(f"[bf16 A^T skinny, 2-byte A] ratio {r:.3e}")
+        assert r <= TOL["bf16f32"]
+        C2, _, _ = run_gemm(A, B, C0, 1.0, 0.5, ws=w)
+        np.testing.assert_array_equal(C, C2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16f32", "fp8f32"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_single_row_a_stored_transposed(gpu_available, dtype, op_b):
+    """M = 1, A stored K x 1 (lda = 1): the untransposed layout's kernels,
+    exact on integer data against the oracle's transposed product."""
+    M, N, K = 1, 4096, 3008
+    A, B, C0 = make_integer_inputs(M, N, K, seed=793, dtype=dtype)
+    As, Bs = stored(A, B, "T", op_b)
+    say(f"[single row A^T] {dtype} op_b={op_b} M={M} N={N} K={K} seed=793")
+    C, _, _ = run_gemm(As, Bs, C0, 2.0, -1.0, op_a="T", op_b=op_b)
+    np.testing.assert_array_equal(C.astype(np.float64), ref_of(As, Bs, C0, 2.0, -1.0, "T", op_b))
 
 
 def test_bf16_skinny_a_transposed_random_full_size(gpu_available):

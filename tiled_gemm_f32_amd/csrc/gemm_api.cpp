@@ -731,6 +731,20 @@ Call make_call(int32_t dtype, int64_t M, int64_t N, int64_t K, float alpha, cons
     return c;
 }
 
+// The operand layouts of a call.  A single row of A stored transposed (K x 1)
+// with unit leading dimension is the same memory as that row stored M x K, so
+// unless a kernel is forced it runs as one: the M <= 16 streaming kernels
+// then take it, whatever its alignment along M (which is what keeps them from
+// A stored K x M).
+void set_ops(Call &c, int32_t op_a, int32_t op_b, int32_t force_kernel = 0) {
+    c.op_a = op_a;
+    c.op_b = op_b;
+    if (force_kernel == 0 && op_a == GEMM_OP_T && c.M == 1 && c.lda == 1) {
+        c.op_a = GEMM_OP_N;
+        c.lda = c.K > 1 ? c.K : 1;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -863,8 +877,7 @@ GEMM_API gemm_status gemm_general(int32_t dtype, int32_t op_a, int32_t op_b, int
                                   float *C, int64_t ldc, int32_t force_kernel, const gemm_epilogue *epilogue,
                                   void *workspace, int64_t workspace_bytes, gemm_stream_t stream) {
     Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes);
-    c.op_a = op_a;
-    c.op_b = op_b;
+    set_ops(c, op_a, op_b, force_kernel);
     return run_epi(c, epilogue, force_kernel, stream);
 }
 
@@ -874,8 +887,7 @@ GEMM_API gemm_status gemm_general_noalloc(int32_t dtype, int32_t op_a, int32_t o
                                           const gemm_epilogue *epilogue, gemm_stream_t stream) {
     static_assert(gemm::kStaticScratchBytes == GEMM_STATIC_SCRATCH_BYTES, "header and library disagree");
     Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    c.op_a = op_a;
-    c.op_b = op_b;
+    set_ops(c, op_a, op_b, force_kernel);
     apply_epilogue(c, epilogue);
     // Argument errors first, with no HIP call, exactly as gemm_general.
     {
@@ -903,8 +915,7 @@ GEMM_API gemm_status gemm_plan_query_epi(int32_t dtype, int32_t op_a, int32_t op
     const KernelDesc *kd = nullptr;
     void *ws = workspace_bytes > 0 ? reinterpret_cast<void *>(uintptr_t(256)) : nullptr;
     Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, ws, workspace_bytes);
-    c.op_a = op_a;
-    c.op_b = op_b;
+    set_ops(c, op_a, op_b, force_kernel);
     apply_epilogue(c, epilogue);
     KSplit ks;
     return plan(c, force_kernel, out, &kd, &ks);
@@ -946,8 +957,7 @@ GEMM_API gemm_status gemm_autotune_general(int32_t dtype, int32_t op_a, int32_t 
                                            int64_t workspace_bytes, int32_t reps, gemm_stream_t stream,
                                            gemm_plan *out) {
     Call c = make_call(dtype, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes);
-    c.op_a = op_a;
-    c.op_b = op_b;
+    set_ops(c, op_a, op_b);
     return autotune(c, reps, static_cast<hipStream_t>(stream), out);
 }
 

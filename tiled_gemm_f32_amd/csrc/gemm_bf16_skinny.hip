@@ -52,15 +52,27 @@ __device__ __forceinline__ int sk_swz(int row) { return 2 * ((row & 3) | (((row 
 // the A operand comes out of the same transposing reads as B's (one
 // 16-column block: lane s gets column m = s).  Columns of the stored block
 // at or past M only reach rows of C that are never written.
-template <int WAVES, int NSLOT, bool AT = false>
+//
+// AV = 1 (with AT): A stored K x M with any M <= 16 and lda, loaded 2 bytes
+// a lane.  Such a direct-to-LDS load places lane i's element in the low half
+// of dword i (probed), so the block takes 8 loads and 2 KB of dwords (and the
+// ring the whole 160 KB of LDS).  Load j, lane l holds k row 4j + (l/16 ^
+// (j/2 % 4)), column l % 16 of the block: each load reads 16 consecutive
+// columns of four rows, and the A fragment (lane (q, s): column s, k 8q ..
+// 8q+7) is read back as 8 dwords whose banks differ across the four q.
+template <int WAVES, int NSLOT, bool AT = false, int AV = 8>
 __global__ void __launch_bounds__(64 * WAVES)
 bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     static_assert(NSLOT == 4, "four slot arrays");
+    static_assert(AV == 8 || (AT && AV == 1), "A loaded 16 bytes a lane, or 2 bytes when stored K x M");
+    constexpr bool kA2 = AV == 1;
+    constexpr int kSlot = kA2 ? kSkB + 2048 : kSkSlot;
+    constexpr int kLoads = kA2 ? 16 : 9;       // loads per block: 8 of B, then A's
     // One array per slot: with distinct objects the compiler can tell that a
     // read of one slot does not depend on loads still landing in another, and
     // does not wait for the whole ring.
-    __shared__ __attribute__((aligned(1024))) char sl0[WAVES][kSkSlot], sl1[WAVES][kSkSlot], sl2[WAVES][kSkSlot],
-        sl3[WAVES][kSkSlot];
+    __shared__ __attribute__((aligned(1024))) char sl0[WAVES][kSlot], sl1[WAVES][kSlot], sl2[WAVES][kSlot],
+        sl3[WAVES][kSlot];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,6 +134,15 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     uint32_t at_off[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) at_off[h] = (uint32_t)(kSkB + (8 * q + (s >> 2) + 4 * h) * 32 + 8 * (s & 3));
+    // AV = 1: load j reads k rows 4j .. 4j+3, lane l row 4j + (l/16 ^ c) with
+    // c = j/2 % 4 (offset a2_goff[c] + j * a2_step).  Fragment element i
+    // (k = 8q + i) then sits in dword 64 (2q + i/4) + 16 ((i%4) ^ q) + s of
+    // the block.
+    uint32_t a2_goff[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a2_goff[c] = (uint32_t)((((lane >> 4) ^ c) * lda + (lane & 15)) * 2);
+    const uint32_t a2_step = (uint32_t)(8 * lda);
+    const uint32_t a2_read = (uint32_t)(kSkB + 512 * q + 4 * s);
 
     const int nb = (kspan + kSkKB - 1) / kSkKB;
     f32x4 acc[8];
@@ -129,7 +150,7 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     for (int cb = 0; cb < 8; ++cb) acc[cb] = f32x4{};
 
     // Block t of this wave is block wave + t*WAVES of the range; it goes to
-    // slot t % NSLOT.  Nine loads per block: 8 of B, then A's.
+    // slot t % NSLOT.  kLoads loads per block: 8 of B, then A's.
     auto issue = [&](int t, int slot) {
         const int k0 = (wave + t * WAVES) * kSkKB;
         const rsrc_t rb = make_rsrc(b_range + (int64_t)k0 * ldb, clamp_extent(((int64_t)(kspan - k0 - 1) * ldb + (N - n0)) * 2));
@@ -137,7 +158,13 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
         for (int i = 0; i < 8; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(slot_base(slot) + 1024 * i), 16, b_goff[i], 0, 0,
                                                      0);
-        if constexpr (AT) {
+        if constexpr (kA2) {
+            const rsrc_t ra = make_rsrc(a_range + (int64_t)k0 * lda, clamp_extent(((int64_t)(kspan - k0 - 1) * lda + M) * 2));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_base(slot) + kSkB + 256 * j), 2,
+                                                         a2_goff[(j >> 1) & 3] + (uint32_t)j * a2_step, 0, 0, 0);
+        } else if constexpr (AT) {
             const rsrc_t ra = make_rsrc(a_range + (int64_t)k0 * lda, clamp_extent(((int64_t)(kspan - k0 - 1) * lda + M) * 2));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)(slot_base(slot) + kSkB), 16, a_goff, 0, 0, 0);
         } else {
@@ -148,7 +175,14 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     auto consume = [&](int slot) {
         const char *base = slot_base(slot);
         bf16x8 afrag;
-        if constexpr (AT) {
+        if constexpr (kA2) {
+            typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+            u16x8 e;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                e[i] = *reinterpret_cast<const uint16_t *>(base + a2_read + 256 * (i >> 2) + 64 * ((i & 3) ^ q));
+            afrag = __builtin_bit_cast(bf16x8, e);
+        } else if constexpr (AT) {
             const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + at_off[0]));
             const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(base + at_off[1]));
             afrag = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -170,11 +204,11 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     for (int t0 = 0; t0 < my_blocks; t0 += NSLOT) {
 #pragma unroll
         for (int u = 0; u < NSLOT; ++u) {
-            // Block t0+u has landed once at most the 9 loads of each later
-            // block are outstanding; then its slot is read and refilled.
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(9 * (NSLOT - 1)));
+            // Block t0+u has landed once at most the kLoads loads of each
+            // later block are outstanding; then its slot is read and refilled.
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kLoads * (NSLOT - 1)));
             if (t0 + u < my_blocks) consume(u);
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(9 * (NSLOT - 1)));   // reads done before the refill
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kLoads * (NSLOT - 1)));   // reads done before the refill
             issue(t0 + u + NSLOT, u);
         }
     }
@@ -221,7 +255,7 @@ bf16_skinny_kernel(GemmParams p, float *partials, int splits, int kchunk) {
 
 // SPLIT: cut K over workgroups as skinny_splits() suggests (which needs the
 // workspace); otherwise every workgroup covers the whole of K and finishes C.
-template <int WAVES, int NSLOT, bool SPLIT = true, bool AT = false>
+template <int WAVES, int NSLOT, bool SPLIT = true, bool AT = false, int AV = 8>
 hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t stream) {
     const int strips = (p.N + kSkNW - 1) / kSkNW;
     const int want = SPLIT ? skinny_splits(strips, p.K) : 1;
@@ -230,7 +264,7 @@ hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t 
     GemmParams args = p;
     float *partials = static_cast<float *>(workspace);
     void *argv[] = {&args, &partials, &splits, &kchunk};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&bf16_skinny_kernel<WAVES, NSLOT, AT>),
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&bf16_skinny_kernel<WAVES, NSLOT, AT, AV>),
                                      dim3((unsigned)strips, (unsigned)splits), dim3(64 * WAVES), argv, 0, stream);
     if (err != hipSuccess || splits == 1) return err;
     GemmParams red = p;
@@ -239,13 +273,14 @@ hipError_t launch_bf16_skinny(const GemmParams &p, void *workspace, hipStream_t 
     return launch_splitk_reduce(red, stream);
 }
 
-template <int WAVES, int NSLOT, bool AT = false>
+template <int WAVES, int NSLOT, bool AT = false, int AV = 8>
 hipError_t launch_bf16_skinny_whole_k(const GemmParams &p, hipStream_t stream) {
-    return launch_bf16_skinny<WAVES, NSLOT, false, AT>(p, nullptr, stream);
+    return launch_bf16_skinny<WAVES, NSLOT, false, AT, AV>(p, nullptr, stream);
 }
 
 template __global__ void bf16_skinny_kernel<4, 4, false>(GemmParams, float *, int, int);
 template __global__ void bf16_skinny_kernel<4, 4, true>(GemmParams, float *, int, int);
+template __global__ void bf16_skinny_kernel<4, 4, true, 1>(GemmParams, float *, int, int);
 
 }  // namespace
 
@@ -268,6 +303,12 @@ const KernelDesc kBf16SplitKernels[] = {
      nullptr, 0, &launch_bf16_skinny<4, 4, true, true>, kLayoutTN, false, kOutAll},
     {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kSkNW, kSkKB, 256, 8, 8, "bf16_skinny_lds_n128_at_w4_s4_whole_k",
      &launch_bf16_skinny_whole_k<4, 4, true>, 0, nullptr, kLayoutTN, false, kOutAll},
+    // A stored K x M otherwise (any M <= 16, lda or alignment): loaded 2
+    // bytes a lane.
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY_SPLITK, 16, kSkNW, kSkKB, 256, 1, 8, "bf16_skinny_lds_n128_at1_w4_s4",
+     nullptr, 0, &launch_bf16_skinny<4, 4, true, true, 1>, kLayoutTN, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kSkNW, kSkKB, 256, 1, 8, "bf16_skinny_lds_n128_at1_w4_s4_whole_k",
+     &launch_bf16_skinny_whole_k<4, 4, true, 1>, 0, nullptr, kLayoutTN, false, kOutAll},
 };
 const int kBf16SplitKernelCount = sizeof(kBf16SplitKernels) / sizeof(kBf16SplitKernels[0]);
 #endif
