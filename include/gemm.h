@@ -312,10 +312,18 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  *     type, takes a streaming kernel that loads each weight row straight
  *     into the matrix instruction, when the rows of A and B are whole
  *     16-byte chunks (aligned bases, K, lda and ldb);
- *   - fp32 with M <= 16, A transposed and B untransposed (A stored K x M)
- *     takes the fp32 skinny kernels of gemm_f32, which then gather A's
- *     values from the rows of its stored transpose; bf16 does the same when
- *     M and lda are multiples of 8 and A is 16-byte aligned;
+ *   - fp32 and bf16 with M <= 16, A transposed and B untransposed (A
+ *     stored K x M) take the streaming kernels of gemm_f32 and
+ *     gemm_bf16f32, which then gather A's values from the rows of its
+ *     stored transpose (bf16 with 16-byte loads when M and lda are
+ *     multiples of 8 and A is 16-byte aligned, else 2-byte loads);
+ *   - fp8 with M <= 16, both operands untransposed and no workspace takes a
+ *     streaming kernel through byte-transposing LDS reads when N is at most
+ *     128 * 128 (with a workspace the fp8 kernel below, split over K, is
+ *     as fast);
+ *   - M == 1 with A transposed and lda == 1 (A stored K x 1, the same
+ *     memory as a 1 x K row) runs as A untransposed unless a kernel is
+ *     forced;
  *   - fp32 and bf16 with either operand transposed take the matrix-core
  *     kernel for that layout when the stored rows of A and B are whole
  *     16-byte chunks;
