@@ -855,7 +855,8 @@ def test_output_types_of_the_kernels():
                  "fp8_mfma32_128x128x64_w2x2_tt_ring4",
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
-                 "fp8_skinny_nt_splitk_n32_w8_u2", "fp8_skinny_kn_n128_w4_s4", "fp8_skinny_kn_n128_w4_s4_whole_k"):
+                 "fp8_skinny_nt_splitk_n32_w8_u2", "fp8_skinny_kn_n128_w4_s4", "fp8_skinny_kn_n128_w4_s4_whole_k",
+                 "fp8_skinny_kn_at1_n128_w4_s3", "fp8_skinny_kn_at1_n128_w4_s3_whole_k"):
         assert outs[name] == 7, name
     assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 7 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 7
     # Register-staged kernels holding 256 accumulators per lane write fp32 only.
@@ -988,6 +989,17 @@ def test_fp8_kn_skinny_choice_and_workspace():
     # K too short for two 512-deep slices: one split, which needs no workspace.
     st, pl = gplan(FP8, N_, N_, 16, 8192, 1008, force=split)
     assert st == OK and kname(pl) == "fp8_skinny_kn_n128_w4_s4" and pl["splits"] == 1, pl
+    # A stored K x M: the byte-loading form where the 128^2 ring cannot run
+    # (A's K rows not whole 16-byte chunks), split with a workspace.
+    at1 = "fp8_skinny_kn_at1_n128_w4_s3"
+    for M, lda in [(12, 12), (13, 13), (5, 16), (1, 3)]:
+        assert kname(gplan(FP8, T_, N_, M, 8192, 8192, lda=lda)[1]) == at1 + "_whole_k"
+        ws = tg.gemm_workspace_size(FP8, M, 8192, 8192)
+        st, pl = gplan(FP8, T_, N_, M, 8192, 8192, lda=lda, ws=ws)
+        assert st == OK and kname(pl) == at1 and pl["grid"] == 256, pl
+    assert kname(gplan(FP8, T_, N_, 16, 8192, 8192, lda=16)[1]) == "fp8_mfma32_128x128x64_w2x2_tn_ring4"
+    assert kname(gplan(FP8, T_, N_, 16, 8192, 8192, lda=16, A=PA + 1)[1]) == at1 + "_whole_k"
+    assert "skinny" not in kname(gplan(FP8, T_, T_, 12, 8192, 8192, lda=12)[1])
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16, FP8])

@@ -135,3 +135,54 @@ def test_fp8_kn_skinny_quantised_output(gpu_available, kind):
         say(f"[fp8 kn skinny] {name} -> {kind} M={M} N={N} K={K} seed=1313")
         got = run_quant(A, B, C0, 2.0, -1.0, kind, 0.25, kernel=kid, ws=ws, bias=bias, act="relu")
         np.testing.assert_array_equal(got, oracle.quantize(z, kind, 0.25), err_msg=name)
+
+
+AT_SPLIT = "fp8_skinny_kn_at1_n128_w4_s3"
+AT_WHOLE = "fp8_skinny_kn_at1_n128_w4_s3_whole_k"
+
+
+def _at_ids():
+    return {k["name"]: k["id"] for k in tg.kernels() if k["name"] in (AT_SPLIT, AT_WHOLE)}
+
+
+@pytest.mark.parametrize("M", [1, 5, 12, 16])
+@pytest.mark.parametrize("NK", [(8192, 4096), (1008, 3008), (4112, 8208)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_fp8_kn_skinny_a_transposed_exact(gpu_available, M, NK):
+    """A stored K x M, loaded a byte a lane (any M): both forms forced and
+    the library's choice with and without a workspace, with A's rows padded
+    by 3 NaN bytes and A one byte off alignment (so the 128^2 ring cannot
+    run), bit-exact on integer data with bias and ReLU.  Columns past M must
+    never reach C; rows past K must read as zero."""
+    N, K = NK
+    A, B, C0 = make_integer_inputs(M, N, K, seed=1320 + M, dtype="fp8f32")
+    As = A.t().contiguous()
+    bias = make_bias(N, seed=1321, integer=True)
+    ref = oracle.gemm_epilogue_ref(host_view(As), host_view(B), 2.0, -1.0, C0.numpy(), bias.numpy(), "relu", "T", "N")
+    ws = _ws(M, N, K)
+    runs = [(n, kid, ws) for n, kid in _at_ids().items()] + [("auto", 0, None), ("auto ws", 0, ws)]
+    for name, kid, w in runs:
+        say(f"[fp8 kn skinny A^T] {name} M={M} N={N} K={K} lda={M + 3} offset=1 seed={1320 + M}")
+        C, _, _ = run_gemm(As, B, C0, 2.0, -1.0, kernel=kid, ws=w, bias=bias, activation="relu", op_a="T",
+                           pad=(3, 0, 0), offset=(1, 0, 0))
+        np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
+    st, pl = tg.gemm_plan_query_general(FP8, 1, 0, M, N, K, 1.0, 0x1001, M + 3, 0x1000, N, 0.0, 0x1000, N, 0, 0)
+    assert st == tg.GEMM_OK and tg.gemm_kernel_query(pl["kernel_id"])["name"] == AT_WHOLE, pl
+
+
+def test_fp8_kn_skinny_a_transposed_random(gpu_available):
+    """12 x 8192 x 8192, A stored K x 12 (N(0,1) bytes), with and without a
+    workspace: within the run-truncation bound, and the same bits as the
+    untransposed kernel of the same form (the same instruction inputs in the
+    same order)."""
+    M, N, K = 12, 8192, 8192
+    A, B, C0 = make_random_inputs(M, N, K, seed=1322, dist="normal", dtype="fp8f32")
+    As = A.t().contiguous()
+    ws = _ws(M, N, K)
+    at, nn = _at_ids(), _ids()
+    for w, at_name, nn_name in [(ws, AT_SPLIT, SPLIT), (None, AT_WHOLE, WHOLE)]:
+        say(f"[fp8 kn skinny A^T] {at_name} M={M} N={N} K={K} normal seed=1322")
+        C, _, _ = run_gemm(As, B, C0, 1.0, 0.5, ws=w, op_a="T", kernel=at[at_name])
+        r = layout_check(C, As, B, C0, 1.0, 0.5, "T", "N", "fp8f32")
+        say(f"[fp8 kn skinny A^T] worst err/allowance {r:.3e}")
+        C2, _, _ = run_gemm(A, B, C0, 1.0, 0.5, ws=w, kernel=nn[nn_name])
+        np.testing.assert_array_equal(C, C2)

@@ -376,11 +376,17 @@ const KernelDesc *choose(const Call &c) {
     // against 19.2 us; 16 x 28672 x 4096: 22.0 against 29.9 us), and so is the
     // unsplit 128^2 ring once the strips would fill the compute units at one
     // workgroup each (16 x 28672 x 4096: 21.8 against 24.7 us).  The split
-    // form stays a candidate for forced calls and the autotuner.
-    if (b_kn && c.op_a == GEMM_OP_N && c.dtype == GEMM_DTYPE_FP8F32 && skinny_fits(c) && c.ws == nullptr &&
-        2 * ceil_div(c.N, gemm::kFp8SkinnyKernels[0].tile_n) <= kComputeUnits) {
-        if (const KernelDesc *kd = first_match(gemm::kFp8SkinnyKernels, gemm::kFp8SkinnyKernelCount, c, 0))
-            return kd;
+    // form stays a candidate for forced calls and the autotuner.  With A
+    // stored K x M the kernel loads A a byte a lane, and runs where the
+    // 128^2 ring cannot (A's K rows not whole 16-byte chunks), which left
+    // only the general kernel.
+    if (b_kn && c.dtype == GEMM_DTYPE_FP8F32 && skinny_fits(c)) {
+        const bool ring_runs = c.op_a == GEMM_OP_N || max_vec_a(c) >= 16;
+        const bool few_strips = 2 * ceil_div(c.N, gemm::kFp8SkinnyKernels[0].tile_n) <= kComputeUnits;
+        if (!ring_runs || (c.op_a == GEMM_OP_N && c.ws == nullptr && few_strips)) {
+            if (const KernelDesc *kd = first_match(gemm::kFp8SkinnyKernels, gemm::kFp8SkinnyKernelCount, c, 0))
+                return kd;
+        }
     }
     // M <= 16 with B stored N x K (a linear layer's weights): the streaming
     // kernel that reads weight rows straight into the matrix instruction,
