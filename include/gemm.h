@@ -320,7 +320,8 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  *   - fp8 with M <= 16, both operands untransposed and no workspace takes a
  *     streaming kernel through byte-transposing LDS reads when N is at most
  *     128 * 128 (with a workspace the fp8 kernel below, split over K, is
- *     as fast);
+ *     as fast); with A stored K x M it takes that kernel, loading A a byte
+ *     a lane, whenever A's rows are not whole 16-byte chunks;
  *   - M == 1 with A transposed and lda == 1 (A stored K x 1, the same
  *     memory as a 1 x K row) runs as A untransposed unless a kernel is
  *     forced;
