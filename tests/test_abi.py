@@ -856,7 +856,8 @@ def test_output_types_of_the_kernels():
                  "f32_general_128x128x16", "bf16_general_128x128x16", "fp8_general_128x128x16",
                  "f32_skinny_splitk_n128_a4_w8_u1", "bf16_skinny_lds_n128_w4_s4", "bf16_skinny_lds_n128_w4_s4_whole_k", "bf16_skinny_nt_n32_w8_u2",
                  "fp8_skinny_nt_splitk_n32_w8_u2", "fp8_skinny_kn_n128_w4_s4", "fp8_skinny_kn_n128_w4_s4_whole_k",
-                 "fp8_skinny_kn_at1_n128_w4_s3", "fp8_skinny_kn_at1_n128_w4_s3_whole_k"):
+                 "fp8_skinny_kn_at1_n128_w4_s3", "fp8_skinny_kn_at1_n128_w4_s3_whole_k",
+                 "f32_skinny_tt_n32_w8_u2", "bf16_skinny_tt_splitk_n32_w8_u2", "fp8_skinny_tt_n32_w8_u2"):
         assert outs[name] == 7, name
     assert outs["f32_skinny_mfma16_n2_a4_w8_u4"] == 7 and outs["f32_mfma32_128x128x16_w2x2_a4b4"] == 7
     # Register-staged kernels holding 256 accumulators per lane write fp32 only.
@@ -999,7 +1000,7 @@ def test_fp8_kn_skinny_choice_and_workspace():
         assert st == OK and kname(pl) == at1 and pl["grid"] == 256, pl
     assert kname(gplan(FP8, T_, N_, 16, 8192, 8192, lda=16)[1]) == "fp8_mfma32_128x128x64_w2x2_tn_ring4"
     assert kname(gplan(FP8, T_, N_, 16, 8192, 8192, lda=16, A=PA + 1)[1]) == at1 + "_whole_k"
-    assert "skinny" not in kname(gplan(FP8, T_, T_, 12, 8192, 8192, lda=12)[1])
+    assert kname(gplan(FP8, T_, T_, 12, 8192, 8192, lda=12)[1]) == "fp8_skinny_tt_n32_w8_u2"
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16, FP8])
@@ -1020,3 +1021,19 @@ def test_single_row_a_stored_transposed_runs_untransposed(dtype):
         at = kernel_ids(name="f32_skinny_mfma16_n2_at_w8_u4")[0]
         st, pl = gplan(F32, T_, N_, 1, 8192, 8192, lda=1, force=at)
         assert st == OK and kname(pl) == "f32_skinny_mfma16_n2_at_w8_u4", pl
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, FP8])
+def test_skinny_tt_choice(dtype):
+    """M <= 16 with A stored K x M and B stored N x K: the N x K streaming
+    kernel gathering A, split over K with a workspace; fp8 with a workspace
+    keeps the 128^2 ring split over K where A's rows allow it."""
+    pre = {F32: "f32", BF16: "bf16", FP8: "fp8"}[dtype]
+    for M, lda in [(16, 16), (12, 12), (5, 8), (1, 3)]:
+        assert kname(gplan(dtype, T_, T_, M, 8192, 8192, lda=lda)[1]) == pre + "_skinny_tt_n32_w8_u2"
+        ws = tg.gemm_workspace_size(dtype, M, 4096, 8192)        # 128 strips of 32 columns: split in two
+        st, pl = gplan(dtype, T_, T_, M, 4096, 8192, lda=lda, ws=ws)
+        ring = dtype == FP8 and (lda * M) % 16 == 0 and M % 16 == 0
+        want = "fp8_mfma32_128x128x64_w2x2_tt_ring4" if ring else pre + "_skinny_tt_splitk_n32_w8_u2"
+        assert st == OK and kname(pl) == want, (M, lda, kname(pl))
+    assert "skinny" not in kname(gplan(dtype, T_, T_, 17, 8192, 8192, lda=17)[1])

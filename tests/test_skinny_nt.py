@@ -193,3 +193,52 @@ def test_fp8_adversarial_runs_within_bound(gpu_available):
         C, _, _ = run_gemm(A8, W8, C0, 1.0, 1.0, kernel=ids[name], op_b="T")
         r = layout_check(C, A8, W8, C0, 1.0, 1.0, "N", "T", "fp8f32")
         say(f"[fp8 adversarial] {name} worst err/allowance {r:.3e}")
+
+
+# ----------------------------------------------------------------------------- both operands transposed
+
+def tt_kernels(dtype):
+    return {k["name"]: k for k in tg.kernels() if k["dtype"] == DT[dtype] and "skinny_tt" in k["name"]}
+
+
+@pytest.mark.parametrize("dtype", ALL)
+@pytest.mark.parametrize("M", [1, 5, 12, 16])
+@pytest.mark.parametrize("NK", [(8192, 4096), (1000, 3008), (33, 64)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_skinny_tt_exact(gpu_available, dtype, M, NK):
+    """A stored K x M and B stored N x K: both forms forced and the library's
+    choice with and without a workspace, with A's rows padded by 3 NaN
+    elements (lda = M + 3) and A one element off alignment, bit-exact on
+    integer data with bias and ReLU.  Columns past M must never reach C."""
+    N, K = NK
+    A, B, C0 = make_integer_inputs(M, N, K, seed=1160 + M, dtype=dtype)
+    As, Bt = A.t().contiguous(), B.t().contiguous()
+    bias = make_bias(N, seed=1161, integer=True)
+    ref = oracle.gemm_epilogue_ref(host_view(As), host_view(Bt), 2.0, -1.0, C0.numpy(), bias.numpy(), "relu",
+                                   "T", "T")
+    ws = nan_ws(M, N, K, dtype)
+    runs = [(n, k["id"], ws) for n, k in tt_kernels(dtype).items()] + [("auto", 0, None), ("auto ws", 0, ws)]
+    for name, kid, w in runs:
+        say(f"[skinny tt] {dtype} {name} M={M} N={N} K={K} lda={M + 3} offset=1 seed={1160 + M}")
+        C, _, _ = run_gemm(As, Bt, C0, 2.0, -1.0, kernel=kid, ws=w, bias=bias, activation="relu", op_a="T",
+                           op_b="T", pad=(3, 0, 0), offset=(1, 0, 0))
+        np.testing.assert_array_equal(C.astype(np.float64), ref, err_msg=name)
+
+
+@pytest.mark.parametrize("dtype", ALL)
+@pytest.mark.parametrize("with_ws", [False, True], ids=["no_ws", "ws"])
+def test_skinny_tt_random_matches_nt(gpu_available, dtype, with_ws):
+    """12 x 8192 x 8192 on N(0,1) data through the forced both-transposed
+    form: within the bound, and the same bits as the N x K kernel of the same
+    form on A stored M x K (the same instruction inputs in the same order)."""
+    M, N, K = 12, 8192, 8192
+    A, B, C0 = make_random_inputs(M, N, K, seed=1170, dist="normal", dtype=dtype)
+    As, Bt = A.t().contiguous(), B.t().contiguous()
+    ws = nan_ws(M, N, K, dtype) if with_ws else None
+    tt = {("splitk" in n): k["id"] for n, k in tt_kernels(dtype).items()}
+    nt = {("splitk" in n): k["id"] for n, k in nt_kernels(dtype).items()}
+    say(f"[skinny tt] {dtype} M={M} N={N} K={K} random seed=1170 ws={with_ws}")
+    C, _, _ = run_gemm(As, Bt, C0, 0.75, 0.5, ws=ws, op_a="T", op_b="T", kernel=tt[with_ws])
+    r = layout_check(C, As, Bt, C0, 0.75, 0.5, "T", "T", dtype)
+    say(f"[skinny tt] worst err/allowance {r:.3e}")
+    C2, _, _ = run_gemm(A, Bt, C0, 0.75, 0.5, ws=ws, op_b="T", kernel=nt[with_ws])
+    np.testing.assert_array_equal(C, C2)

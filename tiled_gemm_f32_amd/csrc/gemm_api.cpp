@@ -172,7 +172,9 @@ bool operands_fit(const KernelDesc *kd, const Call &c) {
     const int64_t esz = elem_size(c.dtype);
     const bool a_n = c.op_a == GEMM_OP_N, b_n = c.op_b == GEMM_OP_N;
     if (kd->path == GEMM_PATH_SKINNY || kd->path == GEMM_PATH_SKINNY_SPLITK) {
-        if (!b_n) return panel_fits(32, c.ldb, c.K, esz) && panel_fits(16, c.lda, c.K, esz);
+        if (!b_n)   // A gathered from its K x M storage when transposed: one resource over all of it
+            return panel_fits(32, c.ldb, c.K, esz) && (a_n ? panel_fits(16, c.lda, c.K, esz)
+                                                           : panel_fits(c.K, c.lda, c.M, esz));
         const bool b_ok = panel_fits(kd->tile_k, c.ldb, kd->tile_n, esz);
         if (a_n) return b_ok && panel_fits(c.M, c.lda, c.K, esz);
         const int64_t a_rows = c.dtype == GEMM_DTYPE_F32 ? c.K : kd->tile_k;
@@ -391,7 +393,13 @@ const KernelDesc *choose(const Call &c) {
     // M <= 16 with B stored N x K (a linear layer's weights): the streaming
     // kernel that reads weight rows straight into the matrix instruction,
     // split over K only where the workspace lets it cover the compute units.
-    if (c.op_a == GEMM_OP_N && c.op_b == GEMM_OP_T && skinny_fits(c)) {
+    // With A stored K x M as well, the same kernel gathers A element by
+    // element (16 x 8192 x 8192: fp32 60 us against 98-168 us on the rings,
+    // bf16 37 against 41-148 us), except fp8 with a workspace where the 128^2
+    // ring can run: split over K it takes 18.3 us against 26.0 us.
+    const bool fp8_tt_ring = c.op_a == GEMM_OP_T && c.dtype == GEMM_DTYPE_FP8F32 && c.ws != nullptr &&
+                             max_vec_a(c) >= 16;
+    if (c.op_b == GEMM_OP_T && skinny_fits(c) && !fp8_tt_ring) {   // A stored either way (the layouts pick)
         for (int i = 0; i < gemm::kSkinnyNtKernelCount; ++i) {
             const KernelDesc *kd = &gemm::kSkinnyNtKernels[i];
             if (kd->path == GEMM_PATH_SKINNY_SPLITK && c.ws != nullptr && split_workspace_bytes(c, kd) > 0 &&

@@ -43,6 +43,12 @@
 // weight row two lanes instead of four, so each load touches 32 rows; it
 // streamed at 2.4 TB/s against 4.2.)
 //
+// With A stored K x M (AT: both operands transposed), a lane's chunk of A (the
+// 16 bytes' worth of consecutive k of its row) is gathered element by
+// element from the column of the stored matrix: A is at most 16 x K and
+// stays in the L2s, and B still streams the same way.  Its columns at or
+// past M only reach rows of C that are never written.
+//
 // Rows of A at or past M and rows of B at or past N lie beyond their buffer
 // extents and read as zero; k blocks at or past the end of the split get an
 // offset that is always out of range.  The dispatcher requires 16-byte
@@ -97,7 +103,38 @@ template <> struct NtType<GEMM_DTYPE_FP8F32> {
     }
 };
 
-template <int DT, int WAVES, int UNROLL>
+// AT: the lane's 16 bytes of A holding k = kk .. kk + 16/esz - 1 of column
+// col, gathered from A stored K x M (element k at (k * lda + col) * esz of
+// the resource); an offset outside the extent reads zero.
+template <int DT>
+__device__ __forceinline__ u32x4 gather_at(rsrc_t r, bool in, uint32_t kk, uint32_t col, uint32_t lda) {
+    u32x4 v;
+    if constexpr (DT == GEMM_DTYPE_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = load_b32(r, in ? ((kk + e) * lda + col) * 4u : kOutOfRange);
+    } else if constexpr (DT == GEMM_DTYPE_BF16F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, in ? ((kk + 2 * e) * lda + col) * 2u : kOutOfRange, 0, 0);
+            const uint32_t hi =
+                __builtin_amdgcn_raw_buffer_load_b16(r, in ? ((kk + 2 * e + 1) * lda + col) * 2u : kOutOfRange, 0, 0);
+            v[e] = lo | (hi << 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, in ? (kk + 4 * e + j) * lda + col : kOutOfRange, 0, 0)
+                     << (8 * j);
+            v[e] = w;
+        }
+    }
+    return v;
+}
+
+template <int DT, int WAVES, int UNROLL, bool AT = false>
 __global__ void __launch_bounds__(64 * WAVES)
 skinny_nt_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     typedef NtType<DT> E;
@@ -116,9 +153,9 @@ skinny_nt_kernel(GemmParams p, float *partials, int splits, int kchunk) {
     const int lc = lane & 15, g = lane >> 4;
     const int rows_here = min(kNtCols, N - n0);
 
-    const char *A = static_cast<const char *>(p.A) + (int64_t)kbeg * esz;
+    const char *A = static_cast<const char *>(p.A) + (AT ? (int64_t)kbeg * lda : (int64_t)kbeg) * esz;
     const char *W = static_cast<const char *>(p.B) + ((int64_t)n0 * ldb + kbeg) * esz;
-    const rsrc_t ra = make_rsrc(A, clamp_extent(((int64_t)(M - 1) * lda + kspan) * esz));
+    const rsrc_t ra = make_rsrc(A, clamp_extent((AT ? (int64_t)(kspan - 1) * lda + M : (int64_t)(M - 1) * lda + kspan) * esz));
     const rsrc_t rw = make_rsrc(W, clamp_extent(((int64_t)(rows_here - 1) * ldb + kspan) * esz));
     const uint32_t a_base = (uint32_t)(lc * lda + 2 * g * chunk) * esz;
     const uint32_t w_base0 = (uint32_t)(lc * ldb + 2 * g * chunk) * esz;
@@ -138,7 +175,11 @@ skinny_nt_kernel(GemmParams p, float *partials, int splits, int kchunk) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool in = live && b * kb_elems + (2 * g + h) * chunk < kspan;
-                av[set][u][h] = load_b128(ra, in ? a_base + koff + 16u * h : kOutOfRange);
+                if constexpr (AT)
+                    av[set][u][h] = gather_at<DT>(ra, in, (uint32_t)(b * kb_elems + (2 * g + h) * chunk), (uint32_t)lc,
+                                                  (uint32_t)lda);
+                else
+                    av[set][u][h] = load_b128(ra, in ? a_base + koff + 16u * h : kOutOfRange);
                 wv0[set][u][h] = load_b128_nt(rw, in ? w_base0 + koff + 16u * h : kOutOfRange);
                 wv1[set][u][h] = load_b128_nt(rw, in ? w_base1 + koff + 16u * h : kOutOfRange);
             }
@@ -206,7 +247,7 @@ void nt_split(const GemmParams &p, bool with_ws, int *splits, int *kchunk) {
     *splits = (p.K + *kchunk - 1) / *kchunk;
 }
 
-template <int DT, int WAVES, int UNROLL>
+template <int DT, int WAVES, int UNROLL, bool AT = false>
 hipError_t launch_nt(const GemmParams &p, void *workspace, bool with_ws, hipStream_t stream) {
     const int strips = (p.N + kNtCols - 1) / kNtCols;
     int splits, kchunk;
@@ -214,7 +255,7 @@ hipError_t launch_nt(const GemmParams &p, void *workspace, bool with_ws, hipStre
     float *partials = static_cast<float *>(workspace);
     GemmParams args = p;
     void *argv[] = {&args, &partials, &splits, &kchunk};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&skinny_nt_kernel<DT, WAVES, UNROLL>),
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&skinny_nt_kernel<DT, WAVES, UNROLL, AT>),
                                      dim3((unsigned)strips, (unsigned)splits), dim3(64 * WAVES), argv, 0, stream);
     if (err != hipSuccess || splits == 1) return err;
     GemmParams red = p;
@@ -223,18 +264,21 @@ hipError_t launch_nt(const GemmParams &p, void *workspace, bool with_ws, hipStre
     return launch_splitk_reduce(red, stream);
 }
 
-template <int DT, int WAVES, int UNROLL>
+template <int DT, int WAVES, int UNROLL, bool AT = false>
 hipError_t launch_nt_plain(const GemmParams &p, hipStream_t stream) {
-    return launch_nt<DT, WAVES, UNROLL>(p, nullptr, false, stream);
+    return launch_nt<DT, WAVES, UNROLL, AT>(p, nullptr, false, stream);
 }
-template <int DT, int WAVES, int UNROLL>
+template <int DT, int WAVES, int UNROLL, bool AT = false>
 hipError_t launch_nt_ws(const GemmParams &p, void *workspace, hipStream_t stream) {
-    return launch_nt<DT, WAVES, UNROLL>(p, workspace, true, stream);
+    return launch_nt<DT, WAVES, UNROLL, AT>(p, workspace, true, stream);
 }
 
 template __global__ void skinny_nt_kernel<GEMM_DTYPE_F32, 8, 2>(GemmParams, float *, int, int);
 template __global__ void skinny_nt_kernel<GEMM_DTYPE_BF16F32, 8, 2>(GemmParams, float *, int, int);
 template __global__ void skinny_nt_kernel<GEMM_DTYPE_FP8F32, 8, 2>(GemmParams, float *, int, int);
+template __global__ void skinny_nt_kernel<GEMM_DTYPE_F32, 8, 2, true>(GemmParams, float *, int, int);
+template __global__ void skinny_nt_kernel<GEMM_DTYPE_BF16F32, 8, 2, true>(GemmParams, float *, int, int);
+template __global__ void skinny_nt_kernel<GEMM_DTYPE_FP8F32, 8, 2, true>(GemmParams, float *, int, int);
 
 }  // namespace
 
@@ -256,6 +300,22 @@ const KernelDesc kSkinnyNtKernels[] = {
      &launch_nt_plain<GEMM_DTYPE_FP8F32, 8, 2>, 0, nullptr, kLayoutNT, false, kOutAll},
     {GEMM_DTYPE_FP8F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 128 * 8 * 2, 512, 16, 16,
      "fp8_skinny_nt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_FP8F32, 8, 2>, kLayoutNT, false, kOutAll},
+    // A stored K x M as well (both operands transposed): A gathered element
+    // by element, any M <= 16 and lda.
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY, 16, kNtCols, 32 * 8 * 2, 512, 1, 4, "f32_skinny_tt_n32_w8_u2",
+     &launch_nt_plain<GEMM_DTYPE_F32, 8, 2, true>, 0, nullptr, kLayoutTT, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY, 16, kNtCols, 64 * 8 * 2, 512, 1, 8, "bf16_skinny_tt_n32_w8_u2",
+     &launch_nt_plain<GEMM_DTYPE_BF16F32, 8, 2, true>, 0, nullptr, kLayoutTT, false, kOutAll},
+    {GEMM_DTYPE_F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 32 * 8 * 2, 512, 1, 4, "f32_skinny_tt_splitk_n32_w8_u2",
+     nullptr, 0, &launch_nt_ws<GEMM_DTYPE_F32, 8, 2, true>, kLayoutTT, false, kOutAll},
+    {GEMM_DTYPE_BF16F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 64 * 8 * 2, 512, 1, 8,
+     "bf16_skinny_tt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_BF16F32, 8, 2, true>, kLayoutTT, false,
+     kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_SKINNY, 16, kNtCols, 128 * 8 * 2, 512, 1, 16, "fp8_skinny_tt_n32_w8_u2",
+     &launch_nt_plain<GEMM_DTYPE_FP8F32, 8, 2, true>, 0, nullptr, kLayoutTT, false, kOutAll},
+    {GEMM_DTYPE_FP8F32, GEMM_PATH_SKINNY_SPLITK, 16, kNtCols, 128 * 8 * 2, 512, 1, 16,
+     "fp8_skinny_tt_splitk_n32_w8_u2", nullptr, 0, &launch_nt_ws<GEMM_DTYPE_FP8F32, 8, 2, true>, kLayoutTT, false,
+     kOutAll},
 };
 const int kSkinnyNtKernelCount = sizeof(kSkinnyNtKernels) / sizeof(kSkinnyNtKernels[0]);
 #endif
