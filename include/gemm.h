@@ -307,11 +307,13 @@ GEMM_API gemm_status gemm_bf16f32_ex(int64_t M, int64_t N, int64_t K, float alph
  * kernel of gemm_f32_ex.  A and B point to fp32, bf16 (uint16_t) or fp8
  * E4M3 (uint8_t) elements as dtype says; C is fp32.  Every combination runs:
  *   - untransposed fp32 and bf16 take the kernels above;
- *   - M <= 16 with A untransposed and B transposed (GEMM_OP_N, GEMM_OP_T:
- *     B stored N x K, the layout of a linear layer's weights), any operand
- *     type, takes a streaming kernel that loads each weight row straight
- *     into the matrix instruction, when the rows of A and B are whole
- *     16-byte chunks (aligned bases, K, lda and ldb);
+ *   - M <= 16 with B transposed (GEMM_OP_T: B stored N x K, the layout of
+ *     a linear layer's weights), any operand type, takes a streaming kernel
+ *     that loads each weight row straight into the matrix instruction, when
+ *     the rows of B are whole 16-byte chunks (aligned base, K and ldb) and,
+ *     with A untransposed, so are A's; A stored K x M is gathered element
+ *     by element (fp8 with a workspace takes the fp8 kernel below, split
+ *     over K, where A's rows are whole 16-byte chunks);
  *   - fp32 and bf16 with M <= 16, A transposed and B untransposed (A
  *     stored K x M) take the streaming kernels of gemm_f32 and
  *     gemm_bf16f32, which then gather A's values from the rows of its
