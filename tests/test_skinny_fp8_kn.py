@@ -186,3 +186,20 @@ def test_fp8_kn_skinny_a_transposed_random(gpu_available):
         say(f"[fp8 kn skinny A^T] worst err/allowance {r:.3e}")
         C2, _, _ = run_gemm(A, B, C0, 1.0, 0.5, ws=w, kernel=nn[nn_name])
         np.testing.assert_array_equal(C, C2)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_fp8_kn_skinny_a_transposed_quantised_output(gpu_available, kind):
+    """A stored K x 13 (rows of 13 bytes, which only the byte-loading form
+    runs): bf16 and E4M3 outputs (scale 1/4, output rows padded by 3) with
+    beta, bias and ReLU, exact on integer data, through both forms."""
+    M, N, K = 13, 1008, 3008
+    A, B, C0 = make_integer_inputs(M, N, K, seed=1323, dtype="fp8f32")
+    As = A.t().contiguous()
+    bias = make_bias(N, seed=1324, integer=True)
+    z = oracle.gemm_epilogue_ref(host_view(As), host_view(B), 2.0, -1.0, C0.numpy(), bias.numpy(), "relu", "T", "N")
+    ws = _ws(M, N, K)
+    for name, kid in _at_ids().items():
+        say(f"[fp8 kn skinny A^T] {name} -> {kind} M={M} N={N} K={K} seed=1323")
+        got = run_quant(As, B, C0, 2.0, -1.0, kind, 0.25, kernel=kid, ws=ws, bias=bias, act="relu", op_a="T", pad=3)
+        np.testing.assert_array_equal(got, oracle.quantize(z, kind, 0.25), err_msg=name)
